@@ -1,0 +1,241 @@
+"""fp64 CPU oracle of the hybrid compressed-attention layer (CSA + HCA + SWA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this package: only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library and imports
+nothing from it; the only thing both sides share is the seeded input generator
+(``synth``), which holds none of the method's arithmetic.
+
+Every function is the plain definition, in NumPy fp64, with no blocking, fusion or
+reordering beyond what the definition states.  Sources (cited by page title and
+section; the pages fix the structure, the layer configuration fixes the choices
+they leave open):
+
+* [QbitAI] "DeepSeek V4报告太详尽了！484天换代之路全公开", section 混合注意力机制:
+  CSA step 1 (every m tokens' KV entries are merged into one by learned,
+  attention-like weights), step 2 (a light indexer scores every compressed block
+  per query token, top-k kept), step 3 (multi-query attention over the selected
+  blocks); HCA (m' = 128, no overlap, dense attention over every compressed entry);
+  the sliding-window branch over the most recent 128 uncompressed tokens, added
+  because compressed attention is strictly causal; the learnable sink logit in the
+  softmax denominator.
+* [yage] yage.ai essay on V4's agentic workload, section on the three tiers: HCA,
+  CSA with k = 1024 (Pro) / 512 (Flash), and a 128-token window, read together.
+* [wiki] aperture-daq wiki "DeepSeek-V4 Preview", section on the CSA/HCA dual track:
+  4:1 and 128:1 compression, shared-KV MQA.
+
+Readings taken where the pages are silent (each one is listed in the design doc):
+pooling = softmax-weighted sum inside each non-overlapping block with one fp32
+logit per raw token per branch, shared by K and V; a block is visible to a query at
+p iff it is complete, (j+1)*r - 1 <= p; indexer score = sum_h w_h*ReLU(qi_h . ki_j)
+with no scale; top-k ties go to the lower block id, k_eff = min(k, n_vis), ids
+sorted ascending and padded with -1; the window is positions [p-W+1, p], the query's
+own token included; the three branches share one softmax with scale 1/sqrt(d); no
+de-duplication between branches.
+
+Every function here is pinned by tests under ``tests/`` against brute force,
+closed forms and library routines; nothing in it is "parity unpinned" except the
+absolute output values a trained V4 layer would give, which need weights that do
+not exist here.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
+    "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible",
+]
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the 16 stored bits are the high half of an
+    IEEE binary32 word whose low half is zero."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def as_f64(arr, dtype: str) -> np.ndarray:
+    """fp64 value of a stored tensor; dtype is "bf16" (uint16 bits) or "f32"."""
+    if dtype == "bf16":
+        return bf16_to_f64(arr)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def n_visible(p: int, r: int) -> int:
+    """Number of compressed entries of ratio r a query at position p may use.
+    [QbitAI] 混合注意力机制, sliding-window paragraph: compressed attention is
+    strictly causal, so only complete blocks count: block j is visible iff
+    (j+1)*r - 1 <= p."""
+    return (p + 1) // r
+
+
+def compress(x_raw: np.ndarray, logits: np.ndarray, raw_start: int, t0: int, n: int,
+             r: int) -> tuple[np.ndarray, np.ndarray]:
+    """Pool the complete blocks of ratio r inside [t0, t0+n) of one sequence.
+
+    [QbitAI] 混合注意力机制, CSA step 1 and the HCA paragraph (no overlap): block j
+    covers positions [j*r, (j+1)*r); its weights are the softmax of the block's
+    pooling logits and the compressed entry is the weighted sum of its rows.
+
+    x_raw: [T_raw, d] fp64, row t - raw_start holds position t; logits: [T_raw].
+    Returns (block ids [nb], rows [nb, d]) for the floor(n/r) complete blocks.
+    """
+    if t0 % r != 0:
+        raise ValueError("t0 must start a block")
+    nb = n // r
+    ids = np.arange(t0 // r, t0 // r + nb, dtype=np.int64)
+    out = np.zeros((nb, x_raw.shape[1]), dtype=np.float64)
+    for bi, j in enumerate(ids):
+        lo = j * r - raw_start
+        z = np.asarray(logits[lo:lo + r], dtype=np.float64)
+        e = np.exp(z - z.max())
+        w = e / e.sum()
+        out[bi] = w @ x_raw[lo:lo + r]
+    return ids, out
+
+
+def index_scores(qi: np.ndarray, wi: np.ndarray, ki: np.ndarray) -> np.ndarray:
+    """Indexer score of every given compressed block for one query token.
+
+    [QbitAI] 混合注意力机制, CSA step 2: a lightweight indexer relates the query to
+    each compressed block.  The configuration fixes the form: a ReLU-weighted sum
+    over indexer heads, s_j = sum_h w_h * max(0, qi_h . ki_j).
+
+    qi: [H_I, d_I], wi: [H_I], ki: [n, d_I] -> s: [n].
+    """
+    dots = ki @ qi.T                     # [n, H_I]
+    return np.maximum(dots, 0.0) @ np.asarray(wi, dtype=np.float64)
+
+
+def topk_select(s: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the k largest scores, ties to the lower id, sorted ascending, padded
+    with -1 to length k when fewer than k blocks are visible.
+
+    [QbitAI] 混合注意力机制, CSA step 2 (top-k of the indexer scores); [yage] three
+    tiers (k = 1024 Pro, 512 Flash).
+    """
+    n = s.shape[0]
+    k_eff = min(k, n)
+    order = np.lexsort((np.arange(n), -s))      # primary: score descending; then id
+    sel = np.sort(order[:k_eff]).astype(np.int64)
+    return np.concatenate([sel, np.full(k - k_eff, -1, dtype=np.int64)])
+
+
+def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
+           sink: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """One softmax per head over a key multiset; returns (o [H, d], lse [H]).
+
+    [QbitAI] 混合注意力机制: core attention is multi-query attention (one shared KV
+    head); the sink paragraph adds a learnable logit to the denominator only.
+    With no key and no sink: o = 0, lse = -inf.
+
+    q: [H, d], keys/values: [n, d], sink: [H] or None.
+    """
+    H, d = q.shape
+    if keys.shape[0] == 0:
+        o = np.zeros((H, values.shape[1] if values.ndim == 2 else d))
+        lse = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64).copy()
+        return o, lse
+    logits = scale * (q @ keys.T)                # [H, n]
+    M = logits.max(axis=1)
+    if sink is not None:
+        M = np.maximum(M, np.asarray(sink, dtype=np.float64))
+    e = np.exp(logits - M[:, None])
+    Z = e.sum(axis=1)
+    if sink is not None:
+        Z = Z + np.exp(np.asarray(sink, dtype=np.float64) - M)
+    o = (e @ values) / Z[:, None]
+    return o, M + np.log(Z)
+
+
+def decode_keyset(p: int, *, branches: int, m: int, m_hca: int, window: int,
+                  idx=None, kc=None, vc=None, kh=None, vh=None,
+                  k_raw=None, v_raw=None, raw_start: int = 0):
+    """Keys and values one query at position p attends to, per branch.
+
+    CSA: the compressed rows named by the selected ids (only ids >= 0);
+    HCA: every visible compressed entry 0..e_vis-1 ([QbitAI] HCA paragraph);
+    SWA: raw positions max(0, p-W+1)..p ([QbitAI] sliding-window paragraph;
+    [yage] the 128-token window).  Returns {"csa": (K, V), "hca": ..., "swa": ...}
+    with only the enabled branches.
+    """
+    out = {}
+    if branches & 1:
+        sel = np.asarray(idx, dtype=np.int64)
+        sel = sel[sel >= 0]
+        if sel.size and sel.max() >= n_visible(p, m):
+            raise ValueError("selected block not visible to the query")
+        out["csa"] = (kc[sel], vc[sel])
+    if branches & 2:
+        e_vis = n_visible(p, m_hca)
+        out["hca"] = (kh[:e_vis], vh[:e_vis])
+    if branches & 4:
+        lo = max(0, p - window + 1)
+        out["swa"] = (k_raw[lo - raw_start:p + 1 - raw_start], v_raw[lo - raw_start:p + 1 - raw_start])
+    return out
+
+
+def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, **ks):
+    """Attention output of one query token: every enabled branch feeds one softmax.
+
+    The configuration fixes the single softmax across CSA, HCA and SWA; [yage]
+    three tiers describe the three views (far coarse, relevant blocks fine, recent
+    tokens in full) of one query.
+    """
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None or scale == 0.0 else scale
+    parts = decode_keyset(p, **ks)
+    if parts:
+        K = np.concatenate([kv[0] for kv in parts.values()], axis=0)
+        V = np.concatenate([kv[1] for kv in parts.values()], axis=0)
+    else:
+        K = np.zeros((0, d))
+        V = np.zeros((0, d))
+    return attend(q, K, V, scale, sink)
+
+
+def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, **caches):
+    """Batched decode: q [B, H, d], pos [B], idx [B, k]; caches batched on axis 0.
+    Returns (o [B, H, d], lse [B, H])."""
+    B = q.shape[0]
+    os_, ls_ = [], []
+    for b in range(B):
+        kb = {k: (v[b] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in caches.items()}
+        o, lse = decode_query(q[b], int(pos[b]), scale=scale, sink=sink,
+                              idx=None if idx is None else idx[b],
+                              raw_start=0 if raw_start is None else int(raw_start[b]), **kb)
+        os_.append(o)
+        ls_.append(lse)
+    return np.stack(os_), np.stack(ls_)
+
+
+def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: int = 0, **caches):
+    """Chunked prefill of one sequence: row i is the query at p = pos0 + i and is the
+    decode of that query over the caches after the chunk has been compressed.
+    q [Tq, H, d], idx [Tq, k]; ``rows`` restricts the rows computed."""
+    rows = range(q.shape[0]) if rows is None else rows
+    os_, ls_ = [], []
+    for i in rows:
+        o, lse = decode_query(q[i], pos0 + i, scale=scale, sink=sink,
+                              idx=None if idx is None else idx[i], raw_start=raw_start, **caches)
+        os_.append(o)
+        ls_.append(lse)
+    return np.stack(os_), np.stack(ls_)
+
+
+def lse_merge(parts):
+    """Merge softmax results over disjoint key sets: parts is a list of (o, lse) of
+    equal shapes.  A part with lse = -inf contributes nothing."""
+    lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])
+    M = lses.max(axis=0)
+    Mf = np.where(np.isfinite(M), M, 0.0)
+    w = np.exp(lses - Mf)
+    Z = w.sum(axis=0)
+    o = sum(w[i][..., None] * parts[i][0] for i in range(len(parts)))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(Z[..., None] > 0, o / np.where(Z > 0, Z, 1.0)[..., None], 0.0)
+        lse = np.where(Z > 0, Mf + np.log(np.where(Z > 0, Z, 1.0)), -np.inf)
+    return o, lse

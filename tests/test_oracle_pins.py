@@ -1,0 +1,430 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+* hand-derived worked examples (tests/golden/worked_examples.json),
+* the pages' structural constants (tests/golden/pages_constants.json),
+* closed forms (identity pooling, plain means, one-hot pooling, one key, constant
+  values, the sink's effect on the weight sum),
+* special cases that reduce to a library routine (full causal attention via
+  torch's scaled_dot_product_attention in float64, a stable argsort, np.dot),
+* exhaustive brute force on tiny inputs (tests/bruteforce.py, pure Python),
+* invariants (shift invariance of pooling, permutation invariance of the selected
+  ids, LSE decomposition across branches, incremental compression).
+A planted mistake in the oracle (dropped term, wrong sign or index, transposed
+operand) fails at least one of them; test_planted_mistakes checks that claim for a
+few such mistakes.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests import bruteforce as BF
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- worked examples
+def test_worked_compress():
+    g = _gold("worked_examples.json")["compress"]
+    rows = np.array(g["rows"])
+    ids, out = O.compress(rows, np.array(g["logits"]), 0, 0, 4, g["ratio"])
+    assert list(ids) == [0]
+    np.testing.assert_allclose(out[0], g["expected"], rtol=0, atol=1e-14)
+
+
+def test_worked_score_topk():
+    g = _gold("worked_examples.json")["score_topk"]
+    s = O.index_scores(np.array(g["qi"]), np.array(g["wi"]), np.array(g["ki"]))
+    np.testing.assert_allclose(s, g["expected_scores"], rtol=0, atol=1e-15)
+    assert list(O.topk_select(s, g["k"])) == g["expected_idx"]
+
+
+def test_worked_attend_and_sink():
+    g = _gold("worked_examples.json")["attend"]
+    q, K, V = (np.array(g[x]) for x in ("q", "keys", "values"))
+    o, lse = O.attend(q, K, V, g["scale"])
+    np.testing.assert_allclose(o, g["expected_o"], atol=1e-14)
+    np.testing.assert_allclose(lse, g["expected_lse"], atol=1e-14)
+    o, lse = O.attend(q, K, V, g["scale"], sink=np.array([g["sink"]]))
+    np.testing.assert_allclose(o, g["expected_o_sink"], atol=1e-14)
+    np.testing.assert_allclose(lse, g["expected_lse_sink"], atol=1e-14)
+
+
+def test_worked_layer():
+    g = _gold("worked_examples.json")["layer"]
+    p, m, mh, W, k = g["p"], g["m"], g["m_hca"], g["window"], g["k"]
+    kr, vr, lg = np.array(g["k_raw"]), np.array(g["v_raw"]), np.array(g["pool_logits"])
+    _, kc = O.compress(kr, lg, 0, 0, p + 1, m)
+    _, vc = O.compress(vr, lg, 0, 0, p + 1, m)
+    _, kh = O.compress(kr, lg, 0, 0, p + 1, mh)
+    _, vh = O.compress(vr, lg, 0, 0, p + 1, mh)
+    s = O.index_scores(np.array(g["qi"]), np.array(g["wi"]), np.array(g["ki"])[:O.n_visible(p, m)])
+    idx = O.topk_select(s, k)
+    assert list(idx) == g["expected_idx"]
+    o, lse = O.decode_query(np.array(g["q"]), p, scale=g["scale"], branches=7, m=m, m_hca=mh,
+                            window=W, idx=idx, kc=kc, vc=vc, kh=kh, vh=vh, k_raw=kr, v_raw=vr)
+    np.testing.assert_allclose(o, g["expected_o"], atol=1e-14)
+    np.testing.assert_allclose(lse, g["expected_lse"], atol=1e-14)
+
+
+def test_pages_constants():
+    c = _gold("pages_constants.json")
+    ctx = c["csa_blocks_attended_at_1m"]["context"]
+    m = c["csa_ratio"]["value"]
+    # a query right after a 1M-token context sees ctx/m complete CSA blocks and
+    # attends top-k of them: 1024 for the Pro setting
+    n_vis = O.n_visible(ctx, m)
+    assert n_vis == ctx // m
+    s = np.arange(n_vis, dtype=np.float64)
+    sel = O.topk_select(s, c["topk_pro"]["value"])
+    assert (sel >= 0).sum() == c["csa_blocks_attended_at_1m"]["value"]
+    # the window holds the W most recent raw tokens
+    W = c["window"]["value"]
+    ks = O.decode_keyset(ctx, branches=4, m=m, m_hca=c["hca_ratio"]["value"], window=W,
+                         k_raw=np.zeros((W, 1)), v_raw=np.zeros((W, 1)), raw_start=ctx - W + 1)
+    assert ks["swa"][0].shape[0] == W
+    assert O.n_visible(ctx, c["hca_ratio"]["value"]) == ctx // 128
+
+
+# ----------------------------------------------------------------- compress
+def test_compress_ratio1_identity():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((9, 5))
+    ids, out = O.compress(x, rng.standard_normal(9), 0, 0, 9, 1)
+    assert np.array_equal(out, x) and list(ids) == list(range(9))
+
+
+def test_compress_equal_logits_is_mean():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((12, 3))
+    _, out = O.compress(x, np.full(12, 0.7), 0, 0, 12, 4)
+    np.testing.assert_allclose(out, x.reshape(3, 4, 3).mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_compress_dominant_logit_returns_row():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((8, 4))
+    z = np.zeros(8)
+    z[2] = 100.0
+    z[7] = 100.0
+    _, out = O.compress(x, z, 0, 0, 8, 4)
+    np.testing.assert_allclose(out[0], x[2], atol=1e-40)
+    np.testing.assert_allclose(out[1], x[7], atol=1e-40)
+
+
+def test_compress_weights_sum_to_one_and_shift_invariance():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal(16)
+    _, ones = O.compress(np.ones((16, 2)), z, 0, 0, 16, 8)
+    np.testing.assert_allclose(ones, 1.0, atol=1e-15)
+    x = rng.standard_normal((16, 3))
+    _, a = O.compress(x, z, 0, 0, 16, 8)
+    _, b = O.compress(x, z + np.repeat([3.5, -7.25], 8), 0, 0, 16, 8)
+    np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-15)
+
+
+def test_compress_offsets_and_incremental():
+    rng = np.random.default_rng(5)
+    T, r, start = 40, 4, 100          # raw row 0 is position 100
+    x = rng.standard_normal((T, 3))
+    z = rng.standard_normal(T)
+    ids, full = O.compress(x, z, start, 100, 38, r)  # 9 complete blocks, tail of 2 stays raw
+    assert list(ids) == list(range(25, 34))
+    ids1, a = O.compress(x, z, start, 100, 16, r)
+    ids2, b = O.compress(x, z, start, 116, 22, r)
+    assert list(np.concatenate([ids1, ids2])) == list(ids)
+    assert np.array_equal(np.concatenate([a, b]), full)
+    # block 27 pools positions 108..111 = raw rows 8..11
+    w = np.exp(z[8:12] - z[8:12].max())
+    np.testing.assert_allclose(full[2], (w / w.sum()) @ x[8:12], atol=1e-15)
+    with pytest.raises(ValueError):
+        O.compress(x, z, start, 102, 8, r)
+
+
+# ----------------------------------------------------------------- indexer score
+def test_score_single_head_is_relu_dot():
+    rng = np.random.default_rng(6)
+    qi = rng.standard_normal((1, 7))
+    ki = rng.standard_normal((30, 7))
+    s = O.index_scores(qi, np.ones(1), ki)
+    ref = np.array([max(0.0, float(np.dot(qi[0], k))) for k in ki])
+    np.testing.assert_allclose(s, ref, rtol=1e-15, atol=1e-15)
+    assert (s == 0).any() and (s > 0).any()
+
+
+def test_score_weight_scaling():
+    rng = np.random.default_rng(7)
+    qi, ki, w = rng.standard_normal((3, 5)), rng.standard_normal((20, 5)), rng.uniform(0, 1, 3)
+    s = O.index_scores(qi, w, ki)
+    np.testing.assert_allclose(O.index_scores(qi, 2.5 * w, ki), 2.5 * s, rtol=1e-14)
+    assert np.array_equal(O.topk_select(s, 6), O.topk_select(2.5 * s, 6))
+
+
+def test_score_bruteforce():
+    rng = np.random.default_rng(8)
+    for HI, dI, n in [(1, 1, 3), (2, 3, 5), (4, 2, 9), (3, 4, 1)]:
+        qi, ki, w = rng.standard_normal((HI, dI)), rng.standard_normal((n, dI)), rng.uniform(0, 1, HI)
+        s = O.index_scores(qi, w, ki)
+        ref = [BF.bf_score(qi.tolist(), w.tolist(), ki[j].tolist()) for j in range(n)]
+        np.testing.assert_allclose(s, ref, rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------- top-k
+def test_topk_exhaustive_distinct():
+    rng = np.random.default_rng(9)
+    for n in range(1, 11):
+        s = rng.standard_normal(n)
+        for k in range(1, n + 2):
+            got = O.topk_select(s, k)
+            assert list(got) == BF.bf_topk(s.tolist(), k)
+            ke = min(k, n)
+            # the chosen set maximises the score sum among all sets of its size
+            best = max(itertools.combinations(range(n), ke), key=lambda c: sum(s[list(c)]))
+            assert sorted(best) == [int(i) for i in got[:ke]]
+
+
+def test_topk_ties_go_to_lower_id():
+    rng = np.random.default_rng(10)
+    for _ in range(200):
+        n = int(rng.integers(1, 12))
+        s = rng.integers(0, 3, n).astype(np.float64)
+        k = int(rng.integers(1, n + 2))
+        got = [int(i) for i in O.topk_select(s, k) if i >= 0]
+        assert got == BF.bf_topk(s.tolist(), k)[:len(got)]
+        rest = [j for j in range(n) if j not in got]
+        for i in got:      # characterisation of the selected set under the tie rule
+            for j in rest:
+                assert s[i] > s[j] or (s[i] == s[j] and i < j)
+
+
+def test_topk_matches_stable_argsort_and_pads():
+    rng = np.random.default_rng(11)
+    s = np.round(rng.standard_normal(5000), 2)       # many ties
+    got = O.topk_select(s, 777)
+    ref = np.sort(np.argsort(-s, kind="stable")[:777])
+    assert np.array_equal(got, ref)
+    pad = O.topk_select(s[:10], 16)
+    assert list(pad[10:]) == [-1] * 6 and list(pad[:10]) == list(range(10))
+
+
+# ----------------------------------------------------------------- attention
+def test_attend_one_key():
+    q = np.array([[0.3, -1.2], [2.0, 0.5]])
+    k = np.array([[1.5, 0.25]])
+    v = np.array([[-4.0, 9.0]])
+    o, lse = O.attend(q, k, v, 0.7)
+    np.testing.assert_allclose(o, np.repeat(v, 2, axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse, 0.7 * (q @ k[0]), atol=1e-15)
+
+
+def test_attend_constant_values_and_weight_sum():
+    rng = np.random.default_rng(12)
+    q, K = rng.standard_normal((3, 4)), rng.standard_normal((17, 4))
+    o, _ = O.attend(q, K, np.full((17, 5), -2.25), 0.5)
+    np.testing.assert_allclose(o, -2.25, atol=1e-14)
+    # one-hot values make o the weight vector: sums to 1, equals scipy's softmax
+    from scipy.special import softmax
+    o, lse = O.attend(q, K, np.eye(17), 0.5)
+    np.testing.assert_allclose(o.sum(axis=1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(o, softmax(0.5 * q @ K.T, axis=1), atol=1e-15)
+    # with a sink the weights sum to 1 - exp(z - lse)
+    z = np.array([0.3, 2.0, -1.0])
+    o, lse = O.attend(q, K, np.eye(17), 0.5, sink=z)
+    np.testing.assert_allclose(o.sum(axis=1), 1.0 - np.exp(z - lse), atol=1e-14)
+
+
+def test_attend_empty():
+    o, lse = O.attend(np.ones((2, 3)), np.zeros((0, 3)), np.zeros((0, 3)), 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def _sdpa_causal_last(q, K, V, scale):
+    """Full causal attention of the last position via torch's library routine (fp64, CPU)."""
+    qt = torch.from_numpy(q)[None, :, None, :]           # [1, H, 1, d]
+    Kt = torch.from_numpy(K)[None, None].expand(1, q.shape[0], -1, -1)
+    Vt = torch.from_numpy(V)[None, None].expand(1, q.shape[0], -1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("which", ["csa_m1", "hca_m1", "swa_full"])
+def test_reduces_to_full_causal_attention(which):
+    rng = np.random.default_rng(13)
+    p, H, d, dI, HI = 37, 3, 8, 4, 2
+    Kr, Vr = rng.standard_normal((p + 1, d)), rng.standard_normal((p + 1, d))
+    z = rng.standard_normal(p + 1)
+    q = rng.standard_normal((H, d))
+    scale = 1 / math.sqrt(d)
+    ref = _sdpa_causal_last(q, Kr, Vr, scale)
+    kw = dict(m=1, m_hca=1, window=128, k_raw=Kr, v_raw=Vr)
+    if which == "csa_m1":
+        _, kc = O.compress(Kr, z, 0, 0, p + 1, 1)
+        _, vc = O.compress(Vr, z, 0, 0, p + 1, 1)
+        s = O.index_scores(rng.standard_normal((HI, dI)), rng.uniform(0, 1, HI), rng.standard_normal((p + 1, dI)))
+        idx = O.topk_select(s, p + 5)
+        o, _ = O.decode_query(q, p, branches=1, idx=idx, kc=kc, vc=vc, **kw)
+    elif which == "hca_m1":
+        _, kh = O.compress(Kr, z, 0, 0, p + 1, 1)
+        _, vh = O.compress(Vr, z, 0, 0, p + 1, 1)
+        o, _ = O.decode_query(q, p, branches=2, kh=kh, vh=vh, **kw)
+    else:
+        kw["window"] = p + 1
+        o, _ = O.decode_query(q, p, branches=4, **kw)
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def _random_layer(rng, p=29, H=2, d=6, HI=2, dI=3, m=2, mh=4, W=5, k=4, start=0):
+    T = p + 1 - start
+    Kr, Vr = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    n, e = O.n_visible(p, m), O.n_visible(p, mh)
+    return dict(q=rng.standard_normal((H, d)), p=p, kc=rng.standard_normal((n, d)),
+                vc=rng.standard_normal((n, d)), kh=rng.standard_normal((e, d)),
+                vh=rng.standard_normal((e, d)), k_raw=Kr, v_raw=Vr, raw_start=start,
+                idx=np.sort(rng.choice(n, k, replace=False)), m=m, m_hca=mh, window=W)
+
+
+def test_idx_permutation_invariance():
+    rng = np.random.default_rng(14)
+    L = _random_layer(rng)
+    q, p = L.pop("q"), L.pop("p")
+    o1, l1 = O.decode_query(q, p, branches=7, **L)
+    L["idx"] = L["idx"][::-1].copy()
+    o2, l2 = O.decode_query(q, p, branches=7, **L)
+    np.testing.assert_allclose(o1, o2, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+
+
+def test_lse_decomposition_across_branches_and_splits():
+    rng = np.random.default_rng(15)
+    L = _random_layer(rng, p=61, W=9, k=6)
+    q, p = L.pop("q"), L.pop("p")
+    full = O.decode_query(q, p, branches=7, **L)
+    parts = [O.decode_query(q, p, branches=b, **L) for b in (1, 2, 4)]
+    o, lse = O.lse_merge(parts)
+    np.testing.assert_allclose(o, full[0], atol=1e-13)
+    np.testing.assert_allclose(lse, full[1], atol=1e-13)
+    # an arbitrary split of one key set merges back
+    ks = O.decode_keyset(p, branches=7, **L)
+    K = np.concatenate([v[0] for v in ks.values()])
+    V = np.concatenate([v[1] for v in ks.values()])
+    cuts = [0, 3, 4, 11, K.shape[0]]
+    sub = [O.attend(q, K[a:b], V[a:b], 1 / math.sqrt(q.shape[1])) for a, b in zip(cuts, cuts[1:])]
+    sub.append(O.attend(q, K[:0], V[:0], 1.0))       # an empty split contributes nothing
+    o, lse = O.lse_merge(sub)
+    np.testing.assert_allclose(o, full[0], atol=1e-13)
+    np.testing.assert_allclose(lse, full[1], atol=1e-13)
+
+
+def test_window_before_context_start_and_raw_offset():
+    rng = np.random.default_rng(16)
+    L = _random_layer(rng, p=3, W=128, k=2, m=2, mh=4)     # p < W: window is 0..p
+    q, p = L.pop("q"), L.pop("p")
+    ks = O.decode_keyset(p, branches=4, **L)
+    assert ks["swa"][0].shape[0] == 4
+    L2 = _random_layer(rng, p=50, W=7, start=40)
+    q2, p2 = L2.pop("q"), L2.pop("p")
+    ks = O.decode_keyset(p2, branches=4, **L2)
+    assert np.array_equal(ks["swa"][0], L2["k_raw"][44 - 40:51 - 40])
+
+
+def test_prefill_rows_equal_decode():
+    rng = np.random.default_rng(17)
+    p0, Tq, H, d = 20, 6, 2, 4
+    L = _random_layer(rng, p=p0 + Tq - 1, H=H, d=d, start=10)
+    Q = rng.standard_normal((Tq, H, d))
+    idx = np.stack([O.topk_select(rng.standard_normal(O.n_visible(p0 + i, 2)), 3) for i in range(Tq)])
+    kw = {k: L[k] for k in ("kc", "vc", "kh", "vh", "k_raw", "v_raw", "m", "m_hca", "window")}
+    o, lse = O.prefill(Q, p0, idx, branches=7, raw_start=10, **kw)
+    for i in range(Tq):
+        od, ld = O.decode_query(Q[i], p0 + i, branches=7, idx=idx[i], raw_start=10, **kw)
+        assert np.array_equal(o[i], od) and np.array_equal(lse[i], ld)
+
+
+# ----------------------------------------------------------------- brute force, exhaustive on tiny shapes
+def _bf_case(rng, T, m, mh, W, k, branches, d=2, H=2, HI=2, dI=2, sink=False):
+    p = T - 1
+    Kr = rng.standard_normal((T, d)).round(3)
+    Vr = rng.standard_normal((T, d)).round(3)
+    lc, lh = rng.standard_normal(T), rng.standard_normal(T)
+    q = rng.standard_normal((H, d))
+    qi, wi = rng.standard_normal((HI, dI)), rng.uniform(0, 1, HI)
+    n = O.n_visible(p, m)
+    ki = rng.standard_normal((max(n, 1), dI))
+    sk = rng.standard_normal(H) if sink else None
+    scale = 1 / math.sqrt(d)
+    bo, bl, bsel = BF.bf_layer(p, q.tolist(), Kr.tolist(), Vr.tolist(), lc.tolist(), lh.tolist(),
+                               qi.tolist(), wi.tolist(), ki.tolist(), m=m, m_hca=mh, k=k, window=W,
+                               branches=branches, scale=scale, sink=None if sk is None else sk.tolist())
+    kw = dict(m=m, m_hca=mh, window=W, k_raw=Kr, v_raw=Vr)
+    idx = None
+    if branches & 1:
+        _, kc = O.compress(Kr, lc, 0, 0, T, m)
+        _, vc = O.compress(Vr, lc, 0, 0, T, m)
+        idx = O.topk_select(O.index_scores(qi, wi, ki[:n]), k)
+        assert [int(i) for i in idx] == bsel
+        kw.update(kc=kc, vc=vc, idx=idx)
+    if branches & 2:
+        _, kh = O.compress(Kr, lh, 0, 0, T, mh)
+        _, vh = O.compress(Vr, lh, 0, 0, T, mh)
+        kw.update(kh=kh, vh=vh)
+    o, lse = O.decode_query(q, p, branches=branches, sink=sk, **kw)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-12)
+
+
+def test_bruteforce_exhaustive_tiny():
+    rng = np.random.default_rng(18)
+    count = 0
+    for T in (1, 2, 5, 9, 16):
+        for m in (1, 2, 4):
+            for mh in (1, 2, 4, 8):
+                n = T // m
+                for W in sorted({1, 3, T}):
+                    for k in sorted({1, 2, max(n, 1), n + 1}):
+                        if n > 10 and k > 2:
+                            k = min(k, 3)      # keep the subset enumeration small
+                        for br in range(1, 8):
+                            _bf_case(rng, T, m, mh, W, k, br)
+                            count += 1
+    assert count > 1000
+
+
+def test_bruteforce_with_sink_and_empty():
+    rng = np.random.default_rng(19)
+    for T in (1, 3, 8):
+        for br in (1, 2, 3, 7):
+            _bf_case(rng, T, 4, 8, 2, 2, br, sink=True)   # T < m: CSA/HCA may be empty
+
+
+# ----------------------------------------------------------------- planted mistakes
+def test_planted_mistakes_are_caught():
+    """A few plausible mistakes, planted in copies of oracle functions, must fail a pin."""
+    rng = np.random.default_rng(20)
+    qi, ki, w = rng.standard_normal((3, 4)), rng.standard_normal((9, 4)), rng.uniform(0, 1, 3)
+    good = O.index_scores(qi, w, ki)
+    bad_sign = np.maximum(-(ki @ qi.T), 0.0) @ w
+    bad_noreluw = (ki @ qi.T) @ w
+    ref = [BF.bf_score(qi.tolist(), w.tolist(), k.tolist()) for k in ki]
+    assert np.allclose(good, ref) and not np.allclose(bad_sign, ref) and not np.allclose(bad_noreluw, ref)
+    # window off by one (excluding the query's own token) breaks the full-causal pin
+    p, d = 12, 4
+    Kr, Vr, q = rng.standard_normal((p + 1, d)), rng.standard_normal((p + 1, d)), rng.standard_normal((2, d))
+    ref = _sdpa_causal_last(q, Kr, Vr, 0.5)
+    o_bad, _ = O.attend(q, Kr[:p], Vr[:p], 0.5)
+    o_good, _ = O.attend(q, Kr, Vr, 0.5)
+    assert np.allclose(o_good, ref) and not np.allclose(o_bad, ref)
+    # pooling weights taken from the wrong block fail the worked example
+    g = _gold("worked_examples.json")["compress"]
+    rows, z = np.array(g["rows"]), np.array(g["logits"])
+    e = np.exp(z[::-1] - z.max())
+    assert not np.allclose((e / e.sum()) @ rows, g["expected"])
