@@ -1,0 +1,247 @@
+"""Python binding of libv4attn (hybrid CSA + HCA + sliding-window attention, gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libv4attn.so``; PyTorch supplies device memory and the current stream.  The
+functions mirror the C entry points of ``include/v4attn.h`` by name:
+
+    compress        -> v4attn_compress
+    index_topk      -> v4attn_index_topk
+    decode          -> v4attn_decode
+    prefill_chunk   -> v4attn_prefill_chunk
+
+Tensor layouts (torch tensors on the GPU, innermost dimension contiguous):
+    raw K/V       [B, T_raw, d]      row t holds position raw_start[b] + t
+    pool logits   [B, T_raw]         fp32
+    caches        [B, rows, d]       row = absolute block / entry id
+    qi            [B, Tq, H_I, d_I]; wi [B, Tq, H_I] fp32; ki [B, N_cap, d_I]
+    idx           [B, Tq, k] int32 (decode: [B, 1, k])
+    q, o          [B, Tq, H, d] (o fp32);  lse [B, Tq, H] fp32
+    pos0, raw_start  [B] int64
+There is no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
+
+F32, BF16 = 0, 1
+CSA, HCA, SWA = 1, 2, 4
+ABI_VERSION = 1
+KERNELS = {"compress": 0, "index_score": 1, "topk_filter": 2, "topk_final": 3, "attn": 4,
+           "merge": 5, "prefill": 6}
+
+
+class V4AttnError(RuntimeError):
+    pass
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("batch_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
+
+
+class CompressArgs(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("ratio", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("t0", ctypes.c_int64), ("n", ctypes.c_int64), ("raw_start", ctypes.c_void_p),
+                ("k_raw", Tensor), ("v_raw", Tensor), ("logits", Tensor), ("k_out", Tensor),
+                ("v_out", Tensor)]
+
+
+class IndexArgs(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("tq", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("ratio", ctypes.c_int32), ("topk", ctypes.c_int32), ("pos0", ctypes.c_void_p),
+                ("pos_max", ctypes.c_int64), ("qi", Tensor), ("wi", Tensor), ("ki", Tensor),
+                ("idx", Tensor), ("sel_scores", Tensor)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("tq", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("branch_mask", ctypes.c_uint32), ("csa_ratio", ctypes.c_int32),
+                ("hca_ratio", ctypes.c_int32), ("window", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("reserved0", ctypes.c_int32), ("pos0", ctypes.c_void_p),
+                ("pos_max", ctypes.c_int64), ("q", Tensor), ("idx", Tensor), ("kc", Tensor),
+                ("vc", Tensor), ("kh", Tensor), ("vh", Tensor), ("k_raw", Tensor), ("v_raw", Tensor),
+                ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libv4attn.so (built by ``compressed_attention_02_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise V4AttnError(f"{LIB_PATH} is missing: build it with `python -m compressed_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.v4attn_compress.argtypes = [ctypes.POINTER(CompressArgs), ctypes.c_void_p]
+        L.v4attn_index_topk.argtypes = [ctypes.POINTER(IndexArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.v4attn_index_topk_workspace.argtypes = [ctypes.POINTER(IndexArgs)]
+        L.v4attn_index_topk_workspace.restype = ctypes.c_size_t
+        for name in ("v4attn_decode", "v4attn_prefill_chunk"):
+            getattr(L, name).argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        for name in ("v4attn_decode_workspace", "v4attn_prefill_chunk_workspace"):
+            getattr(L, name).argtypes = [ctypes.POINTER(AttnArgs)]
+            getattr(L, name).restype = ctypes.c_size_t
+        for name in ("v4attn_compress", "v4attn_index_topk", "v4attn_decode", "v4attn_prefill_chunk",
+                     "v4attn_timing_enable"):
+            getattr(L, name).restype = ctypes.c_int
+        L.v4attn_status_string.argtypes = [ctypes.c_int]
+        L.v4attn_status_string.restype = ctypes.c_char_p
+        L.v4attn_last_error.restype = ctypes.c_char_p
+        L.v4attn_abi_version.restype = ctypes.c_uint32
+        L.v4attn_kernel_name.argtypes = [ctypes.c_int]
+        L.v4attn_kernel_name.restype = ctypes.c_char_p
+        L.v4attn_timing_enable.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.v4attn_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.v4attn_timing_read.restype = ctypes.c_int
+        L.v4attn_timing_reset.restype = None
+        if L.v4attn_abi_version() != ABI_VERSION:
+            raise V4AttnError("libv4attn ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise V4AttnError(f"{L.v4attn_status_string(status).decode()}: {L.v4attn_last_error().decode()}")
+
+
+# ---------------------------------------------------------------- marshalling helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise V4AttnError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t, rows_dim: int = 1) -> Tensor:
+    """Descriptor of a [B, rows, ...] tensor: strides of dims 0 and rows_dim; the dims
+    after rows_dim must be packed."""
+    if t is None:
+        return Tensor(None, 0, 0)
+    shape, st = t.shape, t.stride()
+    packed = 1
+    for dim in range(t.dim() - 1, rows_dim, -1):
+        if st[dim] != packed:
+            raise V4AttnError(f"tensor of shape {tuple(shape)} is not packed after dim {rows_dim}")
+        packed *= shape[dim]
+    return Tensor(t.data_ptr(), st[0], st[rows_dim] if t.dim() > rows_dim else 0)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _alloc_ws(nbytes: int, device):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws):
+    if ws is None:
+        return None, 0
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return p + off, ws.numel() - off
+
+
+# ---------------------------------------------------------------- entry points
+def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None):
+    """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out."""
+    a = CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
+                     _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
+                     _tensor(v_out))
+    _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
+
+
+def index_args(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max, sel_scores=None) -> IndexArgs:
+    B, Tq, HI, dI = qi.shape
+    return IndexArgs(ABI_VERSION, _dtype_code(qi), B, Tq, HI, dI, ratio, topk, _ptr(pos0), pos_max,
+                     _tensor(qi), _tensor(wi), _tensor(ki), _tensor(idx), _tensor(sel_scores))
+
+
+def index_topk_workspace(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max) -> int:
+    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max)
+    return int(lib().v4attn_index_topk_workspace(ctypes.byref(a)))
+
+
+def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, sel_scores=None,
+               workspace=None, stream=None):
+    """v4attn_index_topk: indexer scores and per-query top-k ids into idx [B, Tq, k]."""
+    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max, sel_scores=sel_scores)
+    if workspace is None:
+        workspace = _alloc_ws(int(lib().v4attn_index_topk_workspace(ctypes.byref(a))), qi.device)
+    p, n = _ws_ptr(workspace)
+    _check(lib().v4attn_index_topk(ctypes.byref(a), p, n, _stream(stream)))
+    return workspace
+
+
+def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=None, k_raw=None,
+              v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
+              window=128, topk=1, pos_max=None, scale=0.0, sink=None) -> AttnArgs:
+    B, Tq, H, d = q.shape
+    if pos_max is None:
+        raise V4AttnError("pos_max (host upper bound of the query positions) is required")
+    return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
+                    window, topk, scale, 0, _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
+                    _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
+                    _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse))
+
+
+def _run_attn(fn, wsfn, q, pos0, o, workspace, stream, kw):
+    a = attn_args(q, pos0, o, **kw)
+    if workspace is None:
+        workspace = _alloc_ws(int(getattr(lib(), wsfn)(ctypes.byref(a))), q.device)
+    p, n = _ws_ptr(workspace)
+    _check(getattr(lib(), fn)(ctypes.byref(a), p, n, _stream(stream)))
+    return workspace
+
+
+def decode_workspace(q, pos0, o, **kw) -> int:
+    return int(lib().v4attn_decode_workspace(ctypes.byref(attn_args(q, pos0, o, **kw))))
+
+
+def decode(q, pos0, o, *, workspace=None, stream=None, **kw):
+    """v4attn_decode: one query token per sequence (q [B, 1, H, d]); fills o and lse."""
+    return _run_attn("v4attn_decode", "v4attn_decode_workspace", q, pos0, o, workspace, stream, kw)
+
+
+def prefill_chunk(q, pos0, o, *, workspace=None, stream=None, **kw):
+    """v4attn_prefill_chunk: Tq causal queries per sequence at pos0[b] + i."""
+    return _run_attn("v4attn_prefill_chunk", "v4attn_prefill_chunk_workspace", q, pos0, o, workspace, stream, kw)
+
+
+# ---------------------------------------------------------------- kernel timing
+def timing_enable(kernel: str, max_launches: int) -> None:
+    _check(lib().v4attn_timing_enable(KERNELS[kernel], max_launches))
+
+
+def timing_read(kernel: str, cap: int = 1 << 16) -> list:
+    buf = (ctypes.c_float * cap)()
+    n = lib().v4attn_timing_read(KERNELS[kernel], buf, cap)
+    if n < 0:
+        raise V4AttnError("v4attn_timing_read failed")
+    return [buf[i] for i in range(n)]
+
+
+def timing_reset() -> None:
+    lib().v4attn_timing_reset()

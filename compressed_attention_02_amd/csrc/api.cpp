@@ -1,0 +1,498 @@
+// C-ABI entry points of libv4attn: host-side validation, launch planning,
+// workspace layout and kernel-timing hooks.  Every argument is checked before the
+// first HIP call so that errors are reported synchronously and nothing is enqueued
+// on failure.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/v4attn.h"
+#include "kernels.hpp"
+
+using namespace v4a;
+
+namespace {
+
+thread_local std::string g_err;
+
+v4a_status fail(v4a_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+v4a_status ok() {
+  g_err.clear();
+  return V4A_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t esize(int dtype) { return dtype == V4A_BF16 ? 2 : 4; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Compute-unit count of the current device; 256 (MI355X) if it cannot be queried.
+int cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return 256; }
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Checks a tensor: non-NULL, 16-byte aligned, strides multiples of 16 bytes and row
+// stride >= min_row elements.  batch_stride is only used when batch > 1.
+v4a_status check_tensor(const char* name, const v4a_tensor& t, int dtype, int64_t min_row, int batch,
+                        size_t align = 16) {
+  const int64_t es = (int64_t)esize(dtype);
+  if (!t.ptr) return fail(V4A_EINVAL, "%s: NULL pointer", name);
+  if (!aligned(t.ptr, align)) return fail(V4A_EINVAL, "%s: pointer not %zu-byte aligned", name, align);
+  if (t.row_stride < min_row) return fail(V4A_EINVAL, "%s: row_stride %lld < %lld", name, (long long)t.row_stride, (long long)min_row);
+  if (align >= 16 && (t.row_stride * es) % 16 != 0) return fail(V4A_EINVAL, "%s: row_stride not a multiple of 16 bytes", name);
+  if (batch > 1) {
+    if (t.batch_stride <= 0) return fail(V4A_EINVAL, "%s: batch_stride must be positive", name);
+    if (align >= 16 && (t.batch_stride * es) % 16 != 0) return fail(V4A_EINVAL, "%s: batch_stride not a multiple of 16 bytes", name);
+  }
+  return V4A_OK;
+}
+
+#define V4A_TRY(expr)              \
+  do {                             \
+    const v4a_status _s = (expr);  \
+    if (_s != V4A_OK) return _s;   \
+  } while (0)
+
+v4a_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(V4A_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return V4A_OK;
+}
+
+// ---------------------------------------------------------------- timing hooks
+struct Timing {
+  std::vector<hipEvent_t> start, stop;
+  int cap = 0, used = 0;
+};
+std::mutex g_tmu;
+Timing g_timing[V4A_K_COUNT];
+
+const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_filter", "topk_final",
+                                          "attn", "merge", "prefill"};
+
+// ---------------------------------------------------------------- plans
+struct IndexPlan {
+  int64_t rows, n_cap, sc_rs, chunk_rows, tile, ntiles, nslices;
+  size_t row_bytes, ws_bytes;
+  size_t off_scores, off_hist, off_sure, off_cand, off_counts;  // per-row byte offsets inside a row record
+};
+
+IndexPlan plan_index(const v4a_index_args* a) {
+  IndexPlan P{};
+  P.rows = (int64_t)a->batch * a->tq;
+  P.n_cap = (a->pos_max + 1) / a->ratio;
+  P.sc_rs = round_up(std::max<int64_t>(P.n_cap, 1), 64);
+  // region layout (each region holds chunk_rows rows)
+  const int64_t budget = (int64_t)1 << 30;  // scores of one chunk of rows
+  P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, budget / (P.sc_rs * 4)));
+  const int64_t R = P.chunk_rows;
+  P.off_scores = 0;
+  P.off_hist = (size_t)round_up(R * P.sc_rs * 4, 256);
+  P.off_sure = P.off_hist + (size_t)round_up(R * kHistBins * 4, 256);
+  P.off_cand = P.off_sure + (size_t)round_up(R * kMaxTopk * 4, 256);
+  P.off_counts = P.off_cand + (size_t)round_up(R * kCandCap * 8, 256);
+  P.ws_bytes = P.off_counts + (size_t)round_up(R * 16, 256);
+  const int64_t cus = cu_count();
+  const int64_t want = std::max<int64_t>(1, 4 * cus / std::max<int64_t>(1, std::min(P.rows, R)));
+  P.tile = std::min<int64_t>(8192, std::max<int64_t>(256, round_up(cdiv(P.n_cap, want), 256)));
+  P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, P.tile));
+  P.nslices = std::max<int64_t>(1, cdiv(P.n_cap, 4096));
+  return P;
+}
+
+struct AttnPlan {
+  int64_t rows, n_keys, splits, kps;
+  size_t ws_bytes;
+};
+
+AttnPlan plan_attn(const v4a_attn_args* a) {
+  AttnPlan P{};
+  P.rows = (int64_t)a->batch * a->tq;
+  const int64_t pmax = a->pos_max;
+  P.n_keys = ((a->branch_mask & V4A_CSA) ? a->topk : 0) + ((a->branch_mask & V4A_HCA) ? (pmax + 1) / a->hca_ratio : 0) +
+             ((a->branch_mask & V4A_SWA) ? std::min<int64_t>(a->window, pmax + 1) : 0);
+  const int64_t cus = cu_count();
+  const int64_t target = 2 * cus;
+  if (P.rows >= target || P.n_keys <= 4 * kAttnChunk) {
+    P.splits = 1;
+    P.kps = std::max<int64_t>(P.n_keys, 1);
+  } else {
+    const int64_t per_row = cdiv(target, P.rows);
+    P.kps = std::max<int64_t>(4 * kAttnChunk, round_up(cdiv(P.n_keys, per_row), kAttnChunk));
+    P.splits = cdiv(P.n_keys, P.kps);
+  }
+  if (P.splits <= 1) {
+    P.splits = 1;
+    P.kps = round_up(std::max<int64_t>(P.n_keys, 1), kAttnChunk);
+    P.ws_bytes = 0;
+  } else {
+    P.ws_bytes = (size_t)(P.rows * P.splits * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
+  }
+  return P;
+}
+
+// ---------------------------------------------------------------- validation
+v4a_status validate_compress(const v4a_compress_args* a) {
+  if (!a) return fail(V4A_EINVAL, "args is NULL");
+  if (a->abi_version != V4ATTN_ABI_VERSION) return fail(V4A_EINVAL, "abi_version %u != %u", a->abi_version, V4ATTN_ABI_VERSION);
+  if (a->dtype != V4A_F32 && a->dtype != V4A_BF16) return fail(V4A_EINVAL, "dtype %d unknown", a->dtype);
+  if (a->batch < 0) return fail(V4A_EINVAL, "batch < 0");
+  if (a->ratio < 1) return fail(V4A_EINVAL, "ratio must be >= 1");
+  if (a->t0 < 0 || a->n < 0) return fail(V4A_EINVAL, "t0 and n must be >= 0");
+  if (a->t0 % a->ratio != 0) return fail(V4A_EINVAL, "t0 (%lld) must be a multiple of ratio (%d)", (long long)a->t0, a->ratio);
+  if (a->dim < 1) return fail(V4A_EINVAL, "dim must be >= 1");
+  if ((a->dim * esize(a->dtype)) % 16 != 0 || a->dim > 512)
+    return fail(V4A_ENOTSUP, "dim %d: rows must be a multiple of 16 bytes and dim <= 512", a->dim);
+  if (a->batch == 0 || a->n / a->ratio == 0) return V4A_OK;
+  if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
+  V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, a->batch));
+  V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, a->batch));
+  V4A_TRY(check_tensor("k_out", a->k_out, a->dtype, a->dim, a->batch));
+  V4A_TRY(check_tensor("v_out", a->v_out, a->dtype, a->dim, a->batch));
+  if (!a->logits.ptr) return fail(V4A_EINVAL, "logits: NULL pointer");
+  if (!aligned(a->logits.ptr, 4)) return fail(V4A_EINVAL, "logits: pointer not 4-byte aligned");
+  if (a->logits.row_stride != 1) return fail(V4A_EINVAL, "logits: row_stride must be 1");
+  if (a->batch > 1 && a->logits.batch_stride <= 0) return fail(V4A_EINVAL, "logits: batch_stride must be positive");
+  return V4A_OK;
+}
+
+v4a_status validate_index(const v4a_index_args* a) {
+  if (!a) return fail(V4A_EINVAL, "args is NULL");
+  if (a->abi_version != V4ATTN_ABI_VERSION) return fail(V4A_EINVAL, "abi_version %u != %u", a->abi_version, V4ATTN_ABI_VERSION);
+  if (a->dtype != V4A_F32 && a->dtype != V4A_BF16) return fail(V4A_EINVAL, "dtype %d unknown", a->dtype);
+  if (a->batch < 0) return fail(V4A_EINVAL, "batch < 0");
+  if (a->tq < 1) return fail(V4A_EINVAL, "tq must be >= 1");
+  if (a->heads < 1 || a->dim < 1) return fail(V4A_EINVAL, "heads and dim must be >= 1");
+  if (a->ratio < 1) return fail(V4A_EINVAL, "ratio must be >= 1");
+  if (a->topk < 1) return fail(V4A_EINVAL, "topk must be >= 1");
+  if (a->topk > kMaxTopk) return fail(V4A_ENOTSUP, "topk %d > %d", a->topk, kMaxTopk);
+  if (a->pos_max < 0) return fail(V4A_EINVAL, "pos_max must be >= 0");
+  if (a->pos_max < (int64_t)a->tq - 1) return fail(V4A_EINVAL, "pos_max must be >= tq - 1");
+  if ((a->pos_max + 1) / a->ratio >= ((int64_t)1 << 31) - 1) return fail(V4A_ENOTSUP, "more than 2^31 - 2 blocks");
+  if (a->dtype == V4A_BF16) {
+    if (!(a->heads == 16 || a->heads == 32 || a->heads == 64 || a->heads == 128))
+      return fail(V4A_ENOTSUP, "bf16 indexer: heads must be 16, 32, 64 or 128");
+    if (!(a->dim == 32 || a->dim == 64 || a->dim == 128)) return fail(V4A_ENOTSUP, "bf16 indexer: dim must be 32, 64 or 128");
+  } else {
+    if (a->dim % 4 != 0) return fail(V4A_ENOTSUP, "fp32 indexer: dim must be a multiple of 4");
+    if ((int64_t)a->heads * a->dim + a->heads > 16384) return fail(V4A_ENOTSUP, "fp32 indexer: heads*dim too large");
+  }
+  if (a->batch == 0) return V4A_OK;
+  if (!a->pos0) return fail(V4A_EINVAL, "pos0 is NULL");
+  V4A_TRY(check_tensor("qi", a->qi, a->dtype, (int64_t)a->heads * a->dim, a->batch));
+  V4A_TRY(check_tensor("ki", a->ki, a->dtype, a->dim, a->batch));
+  if (!a->wi.ptr || !aligned(a->wi.ptr, 4)) return fail(V4A_EINVAL, "wi: NULL or not 4-byte aligned");
+  if (a->wi.row_stride < a->heads) return fail(V4A_EINVAL, "wi: row_stride < heads");
+  if (a->batch > 1 && a->wi.batch_stride <= 0) return fail(V4A_EINVAL, "wi: batch_stride must be positive");
+  if (!a->idx.ptr || !aligned(a->idx.ptr, 4)) return fail(V4A_EINVAL, "idx: NULL or not 4-byte aligned");
+  if (a->idx.row_stride < a->topk) return fail(V4A_EINVAL, "idx: row_stride < topk");
+  if (a->sel_scores.ptr) {
+    if (!aligned(a->sel_scores.ptr, 4)) return fail(V4A_EINVAL, "sel_scores: not 4-byte aligned");
+    if (a->sel_scores.row_stride < a->topk) return fail(V4A_EINVAL, "sel_scores: row_stride < topk");
+  }
+  return V4A_OK;
+}
+
+v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
+  if (!a) return fail(V4A_EINVAL, "args is NULL");
+  if (a->abi_version != V4ATTN_ABI_VERSION) return fail(V4A_EINVAL, "abi_version %u != %u", a->abi_version, V4ATTN_ABI_VERSION);
+  if (a->dtype != V4A_F32 && a->dtype != V4A_BF16) return fail(V4A_EINVAL, "dtype %d unknown", a->dtype);
+  if (a->out_dtype != V4A_F32) return fail(V4A_ENOTSUP, "out_dtype must be F32");
+  if (a->batch < 0) return fail(V4A_EINVAL, "batch < 0");
+  if (prefill ? a->tq < 1 : a->tq != 1) return fail(V4A_EINVAL, prefill ? "tq must be >= 1" : "decode needs tq == 1");
+  if (a->heads < 1 || a->heads > 128) return fail(V4A_ENOTSUP, "heads must be in 1..128");
+  if (a->dtype == V4A_BF16 && a->heads % 16 != 0) return fail(V4A_ENOTSUP, "bf16 attention: heads must be a multiple of 16");
+  if (a->dim != 64 && a->dim != 128) return fail(V4A_ENOTSUP, "dim must be 64 or 128");
+  if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
+  if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
+  if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
+  if (a->branch_mask & V4A_CSA) {
+    if (a->topk < 1) return fail(V4A_EINVAL, "topk must be >= 1");
+    if (a->topk > kMaxTopk) return fail(V4A_ENOTSUP, "topk %d > %d", a->topk, kMaxTopk);
+  }
+  if (!std::isfinite(a->scale)) return fail(V4A_EINVAL, "scale must be finite");
+  if (a->pos_max < 0 || a->pos_max < (int64_t)a->tq - 1) return fail(V4A_EINVAL, "pos_max must be >= tq - 1 >= 0");
+  if (a->batch == 0) return V4A_OK;
+  if (!a->pos0) return fail(V4A_EINVAL, "pos0 is NULL");
+  const int64_t hd = (int64_t)a->heads * a->dim;
+  const int bq = a->batch;
+  V4A_TRY(check_tensor("q", a->q, a->dtype, hd, bq));
+  V4A_TRY(check_tensor("o", a->o, V4A_F32, hd, bq));
+  if (a->lse.ptr) {
+    if (!aligned(a->lse.ptr, 4)) return fail(V4A_EINVAL, "lse: not 4-byte aligned");
+    if (a->lse.row_stride < a->heads) return fail(V4A_EINVAL, "lse: row_stride < heads");
+  }
+  if (a->branch_mask & V4A_CSA) {
+    if (!a->idx.ptr || !aligned(a->idx.ptr, 4)) return fail(V4A_EINVAL, "idx: NULL or not 4-byte aligned");
+    if (a->idx.row_stride < a->topk) return fail(V4A_EINVAL, "idx: row_stride < topk");
+    V4A_TRY(check_tensor("kc", a->kc, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("vc", a->vc, a->dtype, a->dim, bq));
+  }
+  if (a->branch_mask & V4A_HCA) {
+    V4A_TRY(check_tensor("kh", a->kh, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("vh", a->vh, a->dtype, a->dim, bq));
+  }
+  if ((a->branch_mask & V4A_SWA) && a->window > 0) {
+    V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, bq));
+    if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
+  }
+  if (a->sink && !aligned(a->sink, 4)) return fail(V4A_EINVAL, "sink: not 4-byte aligned");
+  return V4A_OK;
+}
+
+v4a_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return V4A_OK;
+  if (!ws) return fail(V4A_EWORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (!aligned(ws, 256)) return fail(V4A_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(V4A_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return V4A_OK;
+}
+
+AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
+  AttnP p{};
+  p.q = a->q.ptr; p.q_bs = a->q.batch_stride; p.q_rs = a->q.row_stride;
+  p.idx = (const int32_t*)a->idx.ptr; p.idx_bs = a->idx.batch_stride; p.idx_rs = a->idx.row_stride;
+  p.kc = a->kc.ptr; p.kc_bs = a->kc.batch_stride; p.kc_rs = a->kc.row_stride;
+  p.vc = a->vc.ptr; p.vc_bs = a->vc.batch_stride; p.vc_rs = a->vc.row_stride;
+  p.kh = a->kh.ptr; p.kh_bs = a->kh.batch_stride; p.kh_rs = a->kh.row_stride;
+  p.vh = a->vh.ptr; p.vh_bs = a->vh.batch_stride; p.vh_rs = a->vh.row_stride;
+  p.kr = a->k_raw.ptr; p.kr_bs = a->k_raw.batch_stride; p.kr_rs = a->k_raw.row_stride;
+  p.vr = a->v_raw.ptr; p.vr_bs = a->v_raw.batch_stride; p.vr_rs = a->v_raw.row_stride;
+  p.raw_start = a->raw_start; p.pos0 = a->pos0; p.sink = a->sink;
+  p.o = (float*)a->o.ptr; p.o_bs = a->o.batch_stride; p.o_rs = a->o.row_stride;
+  p.lse = (float*)a->lse.ptr; p.lse_bs = a->lse.batch_stride; p.lse_rs = a->lse.row_stride;
+  p.tq = a->tq; p.heads = a->heads; p.dim = a->dim;
+  p.mask = a->branch_mask;
+  if (!(a->window > 0)) p.mask &= ~V4A_SWA;
+  p.m = a->csa_ratio; p.mh = a->hca_ratio; p.W = a->window; p.topk = a->topk;
+  p.scale = a->scale != 0.f ? a->scale : 1.0f / std::sqrt((float)a->dim);
+  p.splits = (int)P.splits; p.keys_per_split = (int)P.kps;
+  if (P.splits > 1) {
+    p.part_o = (float*)ws;
+    p.part_ml = p.part_o + (size_t)P.rows * P.splits * a->heads * a->dim;
+  }
+  return p;
+}
+
+v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t s, bool prefill) {
+  V4A_TRY(validate_attn(a, prefill));
+  if (a->batch == 0) return ok();
+  const AttnPlan P = plan_attn(a);
+  if (P.splits > INT32_MAX || P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
+  V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
+  const AttnP p = make_attn_params(a, P, ws);
+  const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
+  timing_before(kid, s);
+  V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s), "attention launch"));
+  timing_after(kid, s);
+  if (P.splits > 1) {
+    timing_before(V4A_K_MERGE, s);
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s), "merge launch"));
+    timing_after(V4A_K_MERGE, s);
+  }
+  return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- timing (namespace v4a)
+namespace v4a {
+void timing_before(int k, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  Timing& t = g_timing[k];
+  if (t.used < t.cap) (void)hipEventRecord(t.start[t.used], s);
+}
+void timing_after(int k, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  Timing& t = g_timing[k];
+  if (t.used < t.cap) (void)hipEventRecord(t.stop[t.used++], s);
+}
+}  // namespace v4a
+
+// ---------------------------------------------------------------- C ABI
+extern "C" {
+
+uint32_t v4attn_abi_version(void) { return V4ATTN_ABI_VERSION; }
+
+const char* v4attn_status_string(v4a_status s) {
+  switch (s) {
+    case V4A_OK: return "ok";
+    case V4A_EINVAL: return "invalid argument";
+    case V4A_ENOTSUP: return "unsupported shape or combination";
+    case V4A_EWORKSPACE: return "workspace missing or too small";
+    case V4A_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* v4attn_last_error(void) { return g_err.c_str(); }
+
+const char* v4attn_kernel_name(int kernel) {
+  return (kernel >= 0 && kernel < V4A_K_COUNT) ? kKernelNames[kernel] : "";
+}
+
+v4a_status v4attn_compress(const v4a_compress_args* a, hipStream_t stream) {
+  V4A_TRY(validate_compress(a));
+  const int64_t nb = a->n / a->ratio;
+  if (a->batch == 0 || nb == 0) return ok();
+  CompressP p{};
+  p.k_raw = a->k_raw.ptr; p.v_raw = a->v_raw.ptr; p.logits = (const float*)a->logits.ptr;
+  p.k_out = a->k_out.ptr; p.v_out = a->v_out.ptr; p.raw_start = a->raw_start;
+  p.kr_bs = a->k_raw.batch_stride; p.kr_rs = a->k_raw.row_stride;
+  p.vr_bs = a->v_raw.batch_stride; p.vr_rs = a->v_raw.row_stride;
+  p.lg_bs = a->logits.batch_stride;
+  p.ko_bs = a->k_out.batch_stride; p.ko_rs = a->k_out.row_stride;
+  p.vo_bs = a->v_out.batch_stride; p.vo_rs = a->v_out.row_stride;
+  p.t0 = a->t0; p.nb = nb; p.r = a->ratio; p.d = a->dim;
+  p.ch = (int)(a->dim * esize(a->dtype) / 16);
+  p.g = std::max(1, std::min(a->ratio, 256 / p.ch));
+  p.bpw = std::max(1, 256 / (p.ch * p.g));
+  if (cdiv(nb, p.bpw) > INT32_MAX || a->batch > 65535) return fail(V4A_ENOTSUP, "launch too large");
+  timing_before(V4A_K_COMPRESS, stream);
+  V4A_TRY(hip_check(launch_compress(a->dtype, p, a->batch, stream), "compress launch"));
+  timing_after(V4A_K_COMPRESS, stream);
+  return ok();
+}
+
+size_t v4attn_index_topk_workspace(const v4a_index_args* a) {
+  if (validate_index(a) != V4A_OK || a->batch == 0) return 0;
+  return plan_index(a).ws_bytes;
+}
+
+v4a_status v4attn_index_topk(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  V4A_TRY(validate_index(a));
+  if (a->batch == 0) return ok();
+  const IndexPlan P = plan_index(a);
+  V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
+  char* base = (char*)ws;
+  ScoreP sp{};
+  sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
+  sp.scores = (float*)(base + P.off_scores);
+  sp.hist = (uint32_t*)(base + P.off_hist);
+  sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
+  sp.wi_bs = a->wi.batch_stride; sp.wi_rs = a->wi.row_stride;
+  sp.ki_bs = a->ki.batch_stride; sp.ki_rs = a->ki.row_stride;
+  sp.sc_rs = P.sc_rs;
+  sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio; sp.topk = a->topk;
+  sp.tile = (int)P.tile;
+  TopkP tp{};
+  tp.scores = sp.scores; tp.hist = sp.hist;
+  tp.sure = (uint32_t*)(base + P.off_sure);
+  tp.cand = (uint2*)(base + P.off_cand);
+  tp.counts = (uint32_t*)(base + P.off_counts);
+  tp.pos0 = a->pos0;
+  tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
+  tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
+  tp.sc_rs = P.sc_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
+  tp.slice = 4096;
+  for (int64_t r0 = 0; r0 < P.rows; r0 += P.chunk_rows) {
+    const int nr = (int)std::min<int64_t>(P.chunk_rows, P.rows - r0);
+    sp.row0 = (int)r0;
+    tp.row0 = (int)r0;
+    V4A_TRY(hip_check(launch_topk_clear(tp, nr, stream), "topk clear launch"));
+    timing_before(V4A_K_INDEX_SCORE, stream);
+    V4A_TRY(hip_check(launch_score(a->dtype, sp, nr, (int)P.ntiles, stream), "index score launch"));
+    timing_after(V4A_K_INDEX_SCORE, stream);
+    timing_before(V4A_K_TOPK_FILTER, stream);
+    V4A_TRY(hip_check(launch_topk_filter(tp, nr, (int)P.nslices, stream), "topk filter launch"));
+    timing_after(V4A_K_TOPK_FILTER, stream);
+    timing_before(V4A_K_TOPK_FINAL, stream);
+    V4A_TRY(hip_check(launch_topk_final(tp, nr, stream), "topk final launch"));
+    timing_after(V4A_K_TOPK_FINAL, stream);
+  }
+  return ok();
+}
+
+size_t v4attn_decode_workspace(const v4a_attn_args* a) {
+  if (validate_attn(a, false) != V4A_OK || a->batch == 0) return 0;
+  return plan_attn(a).ws_bytes;
+}
+
+v4a_status v4attn_decode(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_attn(a, ws, ws_bytes, stream, false);
+}
+
+size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* a) {
+  if (validate_attn(a, true) != V4A_OK || a->batch == 0) return 0;
+  return plan_attn(a).ws_bytes;
+}
+
+v4a_status v4attn_prefill_chunk(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_attn(a, ws, ws_bytes, stream, true);
+}
+
+v4a_status v4attn_timing_enable(int kernel, int max_launches) {
+  if (kernel < 0 || kernel >= V4A_K_COUNT) return fail(V4A_EINVAL, "unknown kernel id %d", kernel);
+  if (max_launches < 0 || max_launches > (1 << 20)) return fail(V4A_EINVAL, "max_launches out of range");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  Timing& t = g_timing[kernel];
+  for (hipEvent_t e : t.start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t.stop) (void)hipEventDestroy(e);
+  t.start.assign(max_launches, nullptr);
+  t.stop.assign(max_launches, nullptr);
+  t.cap = 0;
+  t.used = 0;
+  for (int n = 0; n < max_launches; ++n) {
+    if (hipEventCreate(&t.start[n]) != hipSuccess || hipEventCreate(&t.stop[n]) != hipSuccess)
+      return fail(V4A_EHIP, "hipEventCreate failed");
+    t.cap = n + 1;
+  }
+  return ok();
+}
+
+int v4attn_timing_read(int kernel, float* ms, int cap) {
+  if (kernel < 0 || kernel >= V4A_K_COUNT || (cap > 0 && !ms)) return -1;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  Timing& t = g_timing[kernel];
+  const int n = std::min(t.used, cap);
+  for (int k = 0; k < n; ++k) {
+    if (hipEventSynchronize(t.stop[k]) != hipSuccess) return -1;
+    float v = 0.f;
+    if (hipEventElapsedTime(&v, t.start[k], t.stop[k]) != hipSuccess) return -1;
+    ms[k] = v;
+  }
+  return n;
+}
+
+void v4attn_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (Timing& t : g_timing) {
+    for (hipEvent_t e : t.start) (void)hipEventDestroy(e);
+    for (hipEvent_t e : t.stop) (void)hipEventDestroy(e);
+    t.start.clear();
+    t.stop.clear();
+    t.cap = t.used = 0;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// kv_compress: pool every complete block of r raw tokens into one entry.
+//
+// QbitAI article "DeepSeek V4报告太详尽了！484天换代之路全公开", section 混合注意力机制:
+// CSA step 1 merges every m tokens' KV entries into one with learned, attention-like
+// weights; HCA does the same with m' = 128 and no overlap.  The weights are the
+// softmax of one fp32 logit per raw token over its block, shared by K and V.
+//
+// Pure HBM streaming: each raw K/V row is read once, each output row written once.
+// Thread layout: a row of d elements is CH 16-byte chunks; G threads ("row groups")
+// share one block's r rows (rows g, g+G, ...), so a ratio-128 block keeps 256
+// threads busy and a ratio-4 block 64.  Row groups are combined in LDS.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace v4a {
+
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void store(float* p, const float* o) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+template <> struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* o) { unpack8(*reinterpret_cast<const uint4*>(p), o); }
+  __device__ static void store(uint16_t* p, const float* o) { *reinterpret_cast<uint4*>(p) = pack8(o); }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
+  constexpr int N = Chunk<T>::N;
+  __shared__ float s_max[256];
+  __shared__ float s_acc[256][2 * N + 1];
+
+  const int tid = threadIdx.x;
+  const int per_block = p.ch * p.g;
+  const int slot = tid / per_block;
+  const int rem = tid - slot * per_block;
+  const int g = rem / p.ch;
+  const int c = rem - g * p.ch;
+  const int b = blockIdx.y;
+  const int64_t jb = (int64_t)blockIdx.x * p.bpw + slot;
+  const bool active = slot < p.bpw && jb < p.nb;
+  const int64_t j = p.t0 / p.r + jb;                       // absolute block id
+  const int64_t row0 = j * p.r - p.raw_start[b];           // raw row of its first token
+
+  const float* lg = p.logits + (int64_t)b * p.lg_bs + row0;
+  float mx = -INFINITY;
+  if (active)
+    for (int u = g; u < p.r; u += p.g) mx = fmaxf(mx, lg[u]);
+  s_max[tid] = mx;
+  __syncthreads();
+  if (active)
+    for (int gg = 0; gg < p.g; ++gg) mx = fmaxf(mx, s_max[slot * per_block + gg * p.ch + c]);
+
+  float ak[N], av[N], ws = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) { ak[e] = 0.f; av[e] = 0.f; }
+  if (active) {
+    const T* kr = reinterpret_cast<const T*>(p.k_raw) + (int64_t)b * p.kr_bs + row0 * p.kr_rs + c * N;
+    const T* vr = reinterpret_cast<const T*>(p.v_raw) + (int64_t)b * p.vr_bs + row0 * p.vr_rs + c * N;
+#pragma unroll 4
+    for (int u = g; u < p.r; u += p.g) {
+      const float w = __expf(lg[u] - mx);
+      float xk[N], xv[N];
+      Chunk<T>::load(kr + (int64_t)u * p.kr_rs, xk);
+      Chunk<T>::load(vr + (int64_t)u * p.vr_rs, xv);
+      ws += w;
+#pragma unroll
+      for (int e = 0; e < N; ++e) { ak[e] = fmaf(w, xk[e], ak[e]); av[e] = fmaf(w, xv[e], av[e]); }
+    }
+  }
+  if (p.g > 1) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) { s_acc[tid][e] = ak[e]; s_acc[tid][N + e] = av[e]; }
+    s_acc[tid][2 * N] = ws;
+    __syncthreads();
+    if (active && g == 0) {
+      for (int gg = 1; gg < p.g; ++gg) {
+        const float* o = s_acc[slot * per_block + gg * p.ch + c];
+#pragma unroll
+        for (int e = 0; e < N; ++e) { ak[e] += o[e]; av[e] += o[N + e]; }
+        ws += o[2 * N];
+      }
+    }
+  }
+  if (active && g == 0) {
+    const float inv = 1.0f / ws;
+#pragma unroll
+    for (int e = 0; e < N; ++e) { ak[e] *= inv; av[e] *= inv; }
+    T* ko = reinterpret_cast<T*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
+    T* vo = reinterpret_cast<T*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
+    Chunk<T>::store(ko, ak);
+    Chunk<T>::store(vo, av);
+  }
+}
+
+hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s) {
+  const dim3 grid((unsigned)((p.nb + p.bpw - 1) / p.bpw), (unsigned)batch);
+  if (dtype == 0)
+    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace v4a

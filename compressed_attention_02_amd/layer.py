@@ -1,0 +1,110 @@
+"""One step of the hybrid compressed-attention layer on device-resident tensors.
+
+``LayerStep`` strings the four C entry points together in the order a decode or
+prefill step needs them (compress the newly complete blocks, score and select CSA
+blocks, attend) and keeps the workspaces between calls.  It adds no arithmetic:
+everything runs in libv4attn's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import CSA, HCA, SWA, compress, decode, index_topk, prefill_chunk
+
+
+def to_device(arrays: dict, device="cuda") -> dict:
+    """Upload numpy inputs: uint16 arrays are bf16 bit patterns, float32 stays fp32,
+    int64 stays int64."""
+    import torch
+    out = {}
+    for k, v in arrays.items():
+        if not isinstance(v, np.ndarray):
+            continue
+        if v.dtype == np.uint16:
+            t = torch.from_numpy(v.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        out[k] = t
+    return out
+
+
+@dataclass
+class LayerShape:
+    heads: int
+    dim: int
+    idx_heads: int
+    idx_dim: int
+    m: int
+    m_hca: int
+    window: int
+    topk: int
+    branches: int
+    compress: str          # "all", "hca_newest", "chunk" or "none"
+    compress_t0: int
+    pos: int               # position of the first query of the step
+    tq: int
+
+    @classmethod
+    def of(cls, cfg) -> "LayerShape":
+        return cls(cfg.heads, cfg.dim, cfg.idx_heads, cfg.idx_dim, cfg.m, cfg.m_hca, cfg.window,
+                   max(cfg.topk, 1), cfg.branches, cfg.compress, cfg.compress_t0, cfg.pos, cfg.tq)
+
+
+class LayerStep:
+    """Buffers of one step: ``t`` holds the device tensors (inputs and caches, as
+    produced by ``to_device``); outputs ``o``/``lse``/``idx`` are allocated here."""
+
+    def __init__(self, shape: LayerShape, t: dict):
+        import torch
+        self.s = shape
+        self.t = t
+        B = t["q"].shape[0]
+        dev = t["q"].device
+        self.B = B
+        self.pos_max = shape.pos + shape.tq - 1
+        self.o = torch.empty((B, shape.tq, shape.heads, shape.dim), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, shape.tq, shape.heads), dtype=torch.float32, device=dev)
+        self.idx = torch.full((B, shape.tq, shape.topk), -1, dtype=torch.int32, device=dev)
+        self.ws_index = None
+        self.ws_attn = None
+
+    # -- stages -------------------------------------------------------------
+    def run_compress(self, stream=None):
+        s, t = self.s, self.t
+        if s.compress == "none":
+            return
+        n = self.pos_max + 1 - s.compress_t0
+        if s.branches & CSA and s.compress in ("all", "chunk"):
+            compress(t["k_raw"], t["v_raw"], t["logit_csa"], t["raw_start"], t["kc"], t["vc"],
+                     t0=s.compress_t0, n=n, ratio=s.m, stream=stream)
+        if s.branches & HCA:
+            compress(t["k_raw"], t["v_raw"], t["logit_hca"], t["raw_start"], t["kh"], t["vh"],
+                     t0=s.compress_t0, n=n, ratio=s.m_hca, stream=stream)
+
+    def run_index(self, stream=None):
+        s, t = self.s, self.t
+        if not s.branches & CSA:
+            return
+        self.ws_index = index_topk(t["qi"], t["wi"], t["ki"], t["pos"], self.idx, ratio=s.m, topk=s.topk,
+                                   pos_max=self.pos_max, workspace=self.ws_index, stream=stream)
+
+    def attn_kwargs(self):
+        s, t = self.s, self.t
+        return dict(lse=self.lse, idx=self.idx if s.branches & CSA else None, kc=t.get("kc"), vc=t.get("vc"),
+                    kh=t.get("kh"), vh=t.get("vh"), k_raw=t.get("k_raw"), v_raw=t.get("v_raw"),
+                    raw_start=t.get("raw_start"), branch_mask=s.branches, csa_ratio=s.m,
+                    hca_ratio=s.m_hca, window=s.window, topk=s.topk, pos_max=self.pos_max)
+
+    def run_attn(self, stream=None):
+        fn = decode if self.s.tq == 1 else prefill_chunk
+        self.ws_attn = fn(self.t["q"], self.t["pos"], self.o, workspace=self.ws_attn, stream=stream,
+                          **self.attn_kwargs())
+
+    def step(self, stream=None):
+        """The whole hot path of one step: compress (if the step compresses),
+        index_topk (if CSA is on), attention."""
+        self.run_compress(stream)
+        self.run_index(stream)
+        self.run_attn(stream)

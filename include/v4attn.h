@@ -1,0 +1,259 @@
+/*
+ * v4attn — hybrid compressed attention (CSA + HCA + sliding window) for AMD
+ * MI355X (gfx950).  C ABI.
+ *
+ * The layer, as the source pages describe it:
+ *   [QbitAI]  "DeepSeek V4报告太详尽了！484天换代之路全公开", section 混合注意力机制:
+ *             CSA merges every m tokens' KV entries into one with learned,
+ *             attention-like weights (step 1), scores every compressed block per
+ *             query token with a light indexer and keeps the top-k (step 2), runs
+ *             multi-query attention over the kept blocks (step 3); HCA merges every
+ *             m' = 128 tokens without overlap and attends densely to all entries;
+ *             a sliding-window branch over the most recent 128 raw tokens makes up
+ *             for the strict causality of compressed blocks; a learnable sink
+ *             logit may sit in the softmax denominator.
+ *   [yage]    yage.ai essay on V4's agentic workload, section on the three tiers:
+ *             k = 1024 (Pro) / 512 (Flash), window 128, all three views per query.
+ *   [wiki]    aperture-daq wiki "DeepSeek-V4 Preview", CSA/HCA dual-track section:
+ *             4:1 and 128:1 compression, MQA with one shared KV head.
+ * The choices the pages leave open are fixed as follows (one softmax over all
+ * three branches, scale 1/sqrt(d) by default; pooling = softmax over one fp32 logit
+ * per raw token inside each non-overlapping block, shared by K and V; a block is
+ * visible to a query at p iff it is complete, (j+1)*r-1 <= p; indexer score
+ * s_j = sum_h w_h * ReLU(qi_h . ki_j); top-k ties go to the lower block id; the
+ * window is positions [p-W+1, p], the query's own token included).
+ *
+ * Conventions for every call
+ * --------------------------
+ *  * Positions are absolute token positions, 0-based.  Compressed rows are
+ *    indexed by absolute block id (row j of a ratio-r cache pools positions
+ *    [j*r, (j+1)*r)).  Raw K/V rows are indexed by position - raw_start[b].
+ *  * A v4a_tensor is a device pointer plus element strides between sequences
+ *    (batch_stride) and between rows (row_stride); the innermost dimension is
+ *    contiguous.  Pointers must be 16-byte aligned and strides multiples of 16
+ *    bytes (8 bf16 / 4 fp32 elements) except where a field says otherwise.
+ *  * All pointers are device pointers unless the field says "host".
+ *  * Ownership: the caller owns every buffer, including the workspace whose
+ *    size the matching *_workspace() function returns.  The library allocates
+ *    no device memory, keeps no pointer after a call returns, and holds no state
+ *    between calls except a per-device property cache and the optional kernel
+ *    timing events (v4attn_timing_*).
+ *  * Calls are asynchronous and ordered on the given stream.  Every argument is
+ *    validated on the host before any HIP call; on error nothing is launched and
+ *    v4attn_last_error() (thread-local) describes the problem.  Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  * Preconditions that are not checked (device data): selected ids are unique
+ *    and < n_vis of their query, or -1; caches hold every row a query may read;
+ *    raw rows cover the window and the compressed span.
+ */
+#ifndef V4ATTN_H
+#define V4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define V4ATTN_ABI_VERSION 1u
+
+typedef enum v4a_status {
+  V4A_OK = 0,
+  V4A_EINVAL = 1,      /* bad argument (NULL, range, alignment, stride, dtype)   */
+  V4A_ENOTSUP = 2,     /* valid but unsupported shape or combination            */
+  V4A_EWORKSPACE = 3,  /* workspace missing or smaller than *_workspace()      */
+  V4A_EHIP = 4         /* a HIP runtime call failed at enqueue                  */
+} v4a_status;
+
+typedef enum v4a_dtype { V4A_F32 = 0, V4A_BF16 = 1 } v4a_dtype;
+
+/* branch_mask bits */
+#define V4A_CSA 1u
+#define V4A_HCA 2u
+#define V4A_SWA 4u
+
+typedef struct v4a_tensor {
+  void* ptr;
+  int64_t batch_stride; /* elements */
+  int64_t row_stride;   /* elements */
+} v4a_tensor;
+
+/* ---------------------------------------------------------------------------
+ * v4attn_compress — pool raw K and V into compressed entries.
+ * [QbitAI] 混合注意力机制, CSA step 1 and the HCA paragraph (no overlap).
+ * For every complete block j of ratio r inside [t0, t0+n):
+ *   w_t = softmax over the block of logits[t];  out_j = sum_t w_t * x_t
+ * for x = k_raw and x = v_raw with the same weights.  floor(n/r) blocks
+ * (ids t0/r .. t0/r + floor(n/r) - 1) are written to k_out / v_out; a partial
+ * tail of fewer than r tokens is left alone (it is the "state" a later call
+ * compresses once its block is complete).  Accumulation is fp32; a bf16 store
+ * rounds to nearest even.
+ *   dtype        F32 or BF16: type of k_raw, v_raw, k_out, v_out
+ *   dim          d, a multiple of 16 up to 256 (row size a multiple of 16 bytes)
+ *   ratio        r >= 1
+ *   t0, n        host; t0 >= 0 is a multiple of r, n >= 0; the same for all sequences
+ *   raw_start    [batch] int64: position of raw row 0 of each sequence
+ *   k_raw/v_raw  [batch][T_raw][d]
+ *   logits       fp32 [batch][T_raw], row_stride must be 1, no alignment needed
+ *   k_out/v_out  [batch][N_cap][d] indexed by absolute block id
+ * ------------------------------------------------------------------------- */
+typedef struct v4a_compress_args {
+  uint32_t abi_version;
+  int32_t dtype;
+  int32_t batch;
+  int32_t dim;
+  int32_t ratio;
+  int32_t reserved0;
+  int64_t t0;
+  int64_t n;
+  const int64_t* raw_start;
+  v4a_tensor k_raw, v_raw;
+  v4a_tensor logits;
+  v4a_tensor k_out, v_out;
+} v4a_compress_args;
+
+v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * v4attn_index_topk — lightning-indexer scores and per-query top-k.
+ * [QbitAI] 混合注意力机制, CSA step 2; [yage] three tiers (k = 1024 / 512).
+ * For query token i of sequence b at position p = pos0[b] + i and every
+ * visible block j < n_vis = floor((p+1)/m):
+ *   s_j = sum_h wi[h] * max(0, qi[h] . ki[j])          (fp32 accumulation)
+ * idx[b][i] receives the k_eff = min(k, n_vis) ids with the largest s_j (ties
+ * to the lower id), sorted ascending, then -1 up to k.  sel_scores (optional)
+ * receives s of each written id (0 for padding).
+ *   dtype        F32 or BF16: type of qi and ki
+ *   heads, dim   H_I and d_I; BF16 needs heads % 16 == 0 and dim % 32 == 0
+ *   ratio        m >= 1
+ *   topk         1 <= k <= 2048
+ *   pos0         [batch] int64; pos_max (host) >= pos0[b] + tq - 1 for all b
+ *   qi           [batch][tq][H_I][d_I] (row = query token, heads contiguous)
+ *   wi           fp32 [batch][tq][H_I] (row = query token); weights should be
+ *                >= 0 (the ReLU form assumes it; not checked)
+ *   ki           [batch][N_cap][d_I] (row = block id)
+ *   idx          int32 out [batch][tq][k] (row = query token), row_stride >= k
+ *   sel_scores   fp32 out, same layout as idx, or ptr == NULL
+ * Workspace: v4attn_index_topk_workspace(args) bytes.
+ * ------------------------------------------------------------------------- */
+typedef struct v4a_index_args {
+  uint32_t abi_version;
+  int32_t dtype;
+  int32_t batch;
+  int32_t tq;
+  int32_t heads;
+  int32_t dim;
+  int32_t ratio;
+  int32_t topk;
+  const int64_t* pos0;
+  int64_t pos_max;
+  v4a_tensor qi, wi, ki;
+  v4a_tensor idx;
+  v4a_tensor sel_scores;
+} v4a_index_args;
+
+size_t v4attn_index_topk_workspace(const v4a_index_args* args);
+v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * v4attn_decode / v4attn_prefill_chunk — one softmax per query and head over
+ *   CSA: rows idx[b][i][*] >= 0 of kc/vc            [QbitAI] CSA step 3
+ *   HCA: rows 0 .. floor((p+1)/m')-1 of kh/vh       [QbitAI] HCA paragraph
+ *   SWA: raw positions max(0, p-W+1) .. p           [QbitAI] window paragraph
+ * with p = pos0[b] + i.  All query heads share the one KV head (MQA).
+ *   l = scale * q_h . k ;  o_h = sum e^(l-M) v / Z ;  lse_h = M + ln Z,
+ *   Z = sum e^(l-M) (+ e^(sink_h - M) when sink != NULL).
+ * A query with no key and no sink gets o = 0, lse = -inf.  Disabled branches
+ * (branch_mask) contribute nothing and their pointers may be NULL.
+ *   dtype        F32 or BF16: q and every cache; BF16 needs heads % 16 == 0
+ *   out_dtype    must be F32 (o and lse are fp32)
+ *   tq           query tokens per sequence: 1 for v4attn_decode, >= 1 for
+ *                v4attn_prefill_chunk
+ *   heads, dim   H <= 128; d = 64 or 128
+ *   csa_ratio, hca_ratio, window   m, m' >= 1; W >= 0
+ *   topk         k, the row length of idx (CSA only), 1..2048
+ *   scale        softmax scale; 0 selects 1/sqrt(d)
+ *   pos0         [batch] int64; pos_max (host) >= pos0[b] + tq - 1 for all b
+ *   q            [batch][tq][H][d] (row = query token, heads contiguous)
+ *   idx          int32 [batch][tq][k], as written by v4attn_index_topk
+ *   kc, vc       [batch][N_cap][d]; kh, vh [batch][E_cap][d]
+ *   k_raw, v_raw [batch][T_raw][d]; raw_start [batch] int64
+ *   sink         fp32 [H] or NULL
+ *   o            fp32 out [batch][tq][H][d] (row = query token)
+ *   lse          fp32 out [batch][tq][H] (row = query token) or ptr == NULL
+ * The caller appends the query's own K/V to the raw buffers, and for a prefill
+ * chunk runs v4attn_compress over the chunk first.
+ * Workspace: v4attn_decode_workspace / v4attn_prefill_chunk_workspace.
+ * ------------------------------------------------------------------------- */
+typedef struct v4a_attn_args {
+  uint32_t abi_version;
+  int32_t dtype;
+  int32_t out_dtype;
+  int32_t batch;
+  int32_t tq;
+  int32_t heads;
+  int32_t dim;
+  uint32_t branch_mask;
+  int32_t csa_ratio;
+  int32_t hca_ratio;
+  int32_t window;
+  int32_t topk;
+  float scale;
+  int32_t reserved0;
+  const int64_t* pos0;
+  int64_t pos_max;
+  v4a_tensor q;
+  v4a_tensor idx;
+  v4a_tensor kc, vc, kh, vh, k_raw, v_raw;
+  const int64_t* raw_start;
+  const float* sink;
+  v4a_tensor o;
+  v4a_tensor lse;
+} v4a_attn_args;
+
+size_t v4attn_decode_workspace(const v4a_attn_args* args);
+v4a_status v4attn_decode(const v4a_attn_args* args, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* args);
+v4a_status v4attn_prefill_chunk(const v4a_attn_args* args, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Status, version, diagnostics.
+ * ------------------------------------------------------------------------- */
+const char* v4attn_status_string(v4a_status s);
+/* Thread-local text of the last error raised by this thread ("" if none). */
+const char* v4attn_last_error(void);
+uint32_t v4attn_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing for benchmarks.  v4attn_timing_enable(kernel, n) makes the
+ * library bracket each of the next n launches of that kernel with a pair of
+ * hipEventRecord calls on the launch stream (events created here, kept until
+ * v4attn_timing_reset).  v4attn_timing_read waits for the recorded events and
+ * writes up to cap per-launch durations in milliseconds; it returns the count,
+ * or -1 on error.  kernel: one of the V4A_K_* ids.
+ * ------------------------------------------------------------------------- */
+enum {
+  V4A_K_COMPRESS = 0,
+  V4A_K_INDEX_SCORE = 1,
+  V4A_K_TOPK_FILTER = 2,
+  V4A_K_TOPK_FINAL = 3,
+  V4A_K_ATTN = 4,
+  V4A_K_MERGE = 5,
+  V4A_K_PREFILL = 6,
+  V4A_K_COUNT = 7
+};
+v4a_status v4attn_timing_enable(int kernel, int max_launches);
+int v4attn_timing_read(int kernel, float* ms, int cap);
+void v4attn_timing_reset(void);
+const char* v4attn_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* V4ATTN_H */

@@ -21,7 +21,7 @@ Recipe (the same for every configuration):
     s_h shared across the chunk, which keeps every marginal N(0,1);
   * raw K/V exist only for the positions the step touches (window + compressed
     span); the 1M-token history is never materialised, its compressed caches are
-    drawn directly.
+    drawn directly.  Caches hold at least one row even when no entry is visible.
 """
 from __future__ import annotations
 
@@ -84,7 +84,7 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
             qi64 = rngs["qi"].standard_normal((B, Tq, HI, dI))
         out["qi"] = _store(qi64, cfg.dtype)
         out["wi"] = rngs["wi"].uniform(0.0, 1.0, (B, Tq, HI)).astype(np.float32)
-        ki = rngs["ki"].standard_normal((B, cfg.n_cap, dI))
+        ki = rngs["ki"].standard_normal((B, max(cfg.n_cap, 1), dI))
         needles = np.zeros((B, cfg.needles), dtype=np.int64)
         # needles are planted among the blocks every query of the step can see
         first_vis = (cfg.pos + 1) // cfg.m
@@ -101,8 +101,8 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
             ki[b, needles[b]] += 3.0 * np.sqrt(dI) * u
         out["ki"] = _store(ki, cfg.dtype)
         out["needles"] = needles
-        kc = rngs["kc"].standard_normal((B, cfg.n_cap, d))
-        vc = rngs["vc"].standard_normal((B, cfg.n_cap, d))
+        kc = rngs["kc"].standard_normal((B, max(cfg.n_cap, 1), d))
+        vc = rngs["vc"].standard_normal((B, max(cfg.n_cap, 1), d))
         if cfg.compress == "none" and cfg.needles:
             for b in range(B):
                 qm = _load(out["q"][b, 0], cfg.dtype).mean(axis=0)
@@ -110,8 +110,8 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
         out["kc"] = _store(kc, cfg.dtype)
         out["vc"] = _store(vc, cfg.dtype)
     if use_hca:
-        out["kh"] = _normal(rngs["kh"], (B, cfg.e_cap, d), cfg.dtype)
-        out["vh"] = _normal(rngs["vh"], (B, cfg.e_cap, d), cfg.dtype)
+        out["kh"] = _normal(rngs["kh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
+        out["vh"] = _normal(rngs["vh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
     out["k_raw"] = _normal(rngs["k_raw"], (B, cfg.raw_rows, d), cfg.dtype)
     out["v_raw"] = _normal(rngs["v_raw"], (B, cfg.raw_rows, d), cfg.dtype)
     if cfg.compress != "none":

@@ -1,0 +1,187 @@
+"""Runs the HIP path on seeded inputs and compares each stage with the fp64 oracle.
+
+Comparison rules (per stage, stages compared in isolation):
+  * compress: the oracle pools the same raw rows; fp32 configs max-abs <= 1e-5,
+    bf16 configs max-abs <= 1e-2 and mean-relative (sum|diff| / sum|ref|) <= 2e-3;
+  * top-k: with the oracle's fp64 scores and s_k its k-th largest, ids whose score
+    lies within 1e-6*|s_k| of s_k are ties; outside that band the GPU set must equal
+    the oracle set, and both hold k_eff = min(k, n_vis) ids, ascending, -1 padded;
+  * attention: the oracle attends with the GPU's compressed rows and the GPU's ids
+    (so a tie-swapped block cannot fail the output check); same tolerances as above.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+from compressed_attention_02_amd.layer import LayerShape, LayerStep, to_device
+
+TOL = {"f32": dict(max_abs=1e-5, mean_rel=None), "bf16": dict(max_abs=1e-2, mean_rel=2e-3)}
+
+
+def dev_to_np(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy with the stored bits (bf16 as uint16)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def assert_close(got, ref, dtype: str, what: str):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    ninf_g, ninf_r = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(ninf_g, ninf_r), f"{what}: -inf pattern differs"
+    g, r = got[~ninf_r], ref[~ninf_r]
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    tol = TOL[dtype]
+    err = np.abs(g - r)
+    mx = float(err.max()) if err.size else 0.0
+    assert mx <= tol["max_abs"], f"{what}: max-abs {mx:.3e} > {tol['max_abs']}"
+    if tol["mean_rel"] is not None and err.size:
+        mr = float(err.sum() / max(np.abs(r).sum(), 1e-300))
+        assert mr <= tol["mean_rel"], f"{what}: mean-relative {mr:.3e} > {tol['mean_rel']}"
+    return mx
+
+
+def check_topk_row(gpu_ids: np.ndarray, scores: np.ndarray, k: int, what: str):
+    n = scores.shape[0]
+    ke = min(k, n)
+    sel = gpu_ids[gpu_ids >= 0]
+    assert sel.size == ke, f"{what}: {sel.size} ids, expected {ke}"
+    assert np.all(gpu_ids[ke:] == -1), f"{what}: padding"
+    assert np.all(np.diff(sel) > 0), f"{what}: ids not strictly ascending"
+    assert sel.size == 0 or (sel[0] >= 0 and sel[-1] < n), f"{what}: id out of range"
+    ref = O.topk_select(scores, k)
+    ref = ref[ref >= 0]
+    if ke == 0:
+        return
+    sk = np.sort(scores)[::-1][ke - 1]
+    band = set(np.nonzero(np.abs(scores - sk) <= 1e-6 * abs(sk))[0].tolist())
+    a = set(sel.tolist()) - band
+    b = set(ref.tolist()) - band
+    assert a == b, f"{what}: sets differ outside the tie band: gpu-only {sorted(a - b)[:8]}, oracle-only {sorted(b - a)[:8]}"
+
+
+class Run:
+    """Inputs, device tensors, step and host copies of the results for one config."""
+
+    def __init__(self, cfg, seed=None, gen=None):
+        self.cfg = cfg
+        self.g = synth.generate(cfg, seed) if gen is None else gen
+        self.t = to_device(self.g)
+        self.step = LayerStep(LayerShape.of(cfg), self.t)
+
+    def run(self):
+        st = self.step
+        st.run_compress()
+        torch.cuda.synchronize()
+        st.run_index()
+        torch.cuda.synchronize()
+        st.run_attn()
+        torch.cuda.synchronize()
+        return self
+
+    # ---- host views of the device state
+    def host(self, name):
+        return dev_to_np(self.t[name])
+
+    def f64(self, name):
+        return O.as_f64(self.host(name), self.cfg.dtype)
+
+    # ---- per-stage checks
+    def check_compress(self):
+        cfg = self.cfg
+        if cfg.compress == "none":
+            return
+        kr, vr = O.as_f64(self.g["k_raw"], cfg.dtype), O.as_f64(self.g["v_raw"], cfg.dtype)
+        t0 = cfg.compress_t0
+        n = cfg.last_pos + 1 - t0
+        todo = []
+        if cfg.branches & 1 and cfg.compress in ("all", "chunk"):
+            todo.append(("logit_csa", cfg.m, "kc", "vc"))
+        if cfg.branches & 2:
+            todo.append(("logit_hca", cfg.m_hca, "kh", "vh"))
+        for lg, r, kn, vn in todo:
+            gk, gv = self.f64(kn), self.f64(vn)
+            for b in range(cfg.batch):
+                rs = int(self.g["raw_start"][b])
+                ids, ck = O.compress(kr[b], self.g[lg][b], rs, t0, n, r)
+                _, cv = O.compress(vr[b], self.g[lg][b], rs, t0, n, r)
+                assert_close(gk[b, ids], ck, cfg.dtype, f"compress {kn} b={b}")
+                assert_close(gv[b, ids], cv, cfg.dtype, f"compress {vn} b={b}")
+
+    def oracle_scores(self, b, i):
+        cfg = self.cfg
+        p = int(self.g["pos"][b]) + i
+        n = O.n_visible(p, cfg.m)
+        qi = O.as_f64(self.g["qi"][b, i], cfg.dtype)
+        ki = O.as_f64(self.g["ki"][b, :n], cfg.dtype)
+        return O.index_scores(qi, self.g["wi"][b, i].astype(np.float64), ki)
+
+    def check_topk(self, rows=None):
+        cfg = self.cfg
+        if not cfg.branches & 1:
+            return
+        idx = dev_to_np(self.step.idx)
+        rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.tq)] if rows is None else rows
+        for b, i in rows:
+            check_topk_row(idx[b, i], self.oracle_scores(b, i), cfg.topk, f"topk b={b} i={i}")
+
+    def oracle_attn(self, rows=None, sink=None):
+        cfg = self.cfg
+        idx = dev_to_np(self.step.idx)
+        caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
+        for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):
+            if nm in self.t:
+                caches[nm] = self.f64(nm)
+        q = O.as_f64(self.g["q"], cfg.dtype)
+        rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.tq)] if rows is None else rows
+        out_o, out_l = [], []
+        for b, i in rows:
+            kw = {k: (v[b] if isinstance(v, np.ndarray) else v) for k, v in caches.items()}
+            o, l = O.decode_query(q[b, i], int(self.g["pos"][b]) + i, sink=sink,
+                                  idx=idx[b, i] if cfg.branches & 1 else None,
+                                  raw_start=int(self.g["raw_start"][b]), **kw)
+            out_o.append(o)
+            out_l.append(l)
+        return np.stack(out_o), np.stack(out_l)
+
+    def check_attn(self, rows=None):
+        cfg = self.cfg
+        rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.tq)] if rows is None else rows
+        ro, rl = self.oracle_attn(rows)
+        o = dev_to_np(self.step.o)
+        l = dev_to_np(self.step.lse)
+        go = np.stack([o[b, i] for b, i in rows])
+        gl = np.stack([l[b, i] for b, i in rows])
+        assert_close(go, ro, cfg.dtype, "attention o")
+        assert_close(gl, rl, cfg.dtype, "attention lse")
+
+    def check_all(self, rows=None):
+        self.check_compress()
+        self.check_topk(rows)
+        self.check_attn(rows)
+        return self
+
+
+def sample_rows(cfg, n_random=8, seed=0):
+    """Rows of a prefill chunk the oracle checks one by one: first, last, the rows
+    where a CSA block or an HCA entry completes, and random ones."""
+    rng = np.random.default_rng(seed)
+    rows = {0, cfg.tq - 1}
+    for i in range(cfg.tq):
+        p = cfg.pos + i
+        if (p + 1) % cfg.m_hca == 0 or i < 4:
+            rows.add(i)
+    rows |= set(rng.choice(cfg.tq, min(n_random, cfg.tq), replace=False).tolist())
+    return [(b, i) for b in range(cfg.batch) for i in sorted(rows)]
+
+
+def scale_of(cfg):
+    return 1.0 / math.sqrt(cfg.dim)

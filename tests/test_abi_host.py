@@ -1,0 +1,174 @@
+"""C-ABI library: loads, exports every declared symbol, validates on the host.
+
+No GPU needed.  Validation-failure calls use fake, aligned, never-dereferenced
+pointers: the library must reject them before any HIP call.  Calls with valid
+arguments are only made when no GPU is visible (they must then fail with EHIP).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_attention_02_amd as V
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "v4attn.h")
+EINVAL, ENOTSUP, EWORKSPACE, EHIP = 1, 2, 3, 4
+FAKE = 0x7f0000000000          # 256-byte aligned, never dereferenced
+
+
+def _declared():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(v4attn_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = V.lib()
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.v4attn_abi_version() == 1
+    assert L.v4attn_status_string(0) == b"ok"
+    assert L.v4attn_kernel_name(1) == b"index_score"
+
+
+def _T(p=FAKE, bs=0, rs=0):
+    return V.Tensor(p, bs, rs)
+
+
+def good_compress(**kw):
+    a = V.CompressArgs(1, V.BF16, 2, 128, 4, 0, 0, 4096, FAKE,
+                       _T(rs=128, bs=128 * 5000), _T(rs=128, bs=128 * 5000), _T(rs=1, bs=5000),
+                       _T(rs=128, bs=128 * 1024), _T(rs=128, bs=128 * 1024))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def good_index(**kw):
+    a = V.IndexArgs(1, V.BF16, 2, 1, 64, 64, 4, 512, FAKE, 131072,
+                    _T(bs=4096, rs=4096), _T(bs=64, rs=64), _T(bs=64 * 32768, rs=64),
+                    _T(bs=512, rs=512), _T(None))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def good_attn(**kw):
+    T = _T
+    a = V.AttnArgs(1, V.BF16, V.F32, 2, 1, 64, 128, 7, 4, 128, 128, 512, 0.0, 0, FAKE, 131072,
+                   T(bs=8192, rs=8192), T(bs=512, rs=512), T(bs=128 * 32768, rs=128),
+                   T(bs=128 * 32768, rs=128), T(bs=128 * 1024, rs=128), T(bs=128 * 1024, rs=128),
+                   T(bs=128 * 128, rs=128), T(bs=128 * 128, rs=128), FAKE, None,
+                   T(bs=8192, rs=8192), T(bs=64, rs=64))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _st(fn, a, *extra):
+    r = fn(ctypes.byref(a), *extra)
+    return r, V.lib().v4attn_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 2, EINVAL), ("dtype", 7, EINVAL), ("ratio", 0, EINVAL), ("t0", 6, EINVAL),
+    ("n", -1, EINVAL), ("dim", 100, ENOTSUP), ("raw_start", None, EINVAL),
+])
+def test_compress_rejects(field, value, code):
+    r, msg = _st(V.lib().v4attn_compress, good_compress(**{field: value}), None)
+    assert r == code and msg
+
+
+def test_compress_rejects_tensors():
+    L = V.lib()
+    assert _st(L.v4attn_compress, good_compress(k_raw=_T(None, 640000, 128)), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(v_out=_T(FAKE + 8, 131072, 128)), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(k_out=_T(FAKE, 131072, 100)), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(logits=_T(FAKE, 5000, 2)), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(k_raw=_T(FAKE, 0, 128)), None)[0] == EINVAL
+    # nothing to do is not an error, even with NULL buffers
+    assert _st(L.v4attn_compress, good_compress(n=3, k_raw=_T(None)), None)[0] == 0
+    assert _st(L.v4attn_compress, good_compress(batch=0), None)[0] == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 0, EINVAL), ("tq", 0, EINVAL), ("topk", 0, EINVAL), ("topk", 4096, ENOTSUP),
+    ("heads", 48, ENOTSUP), ("dim", 48, ENOTSUP), ("ratio", 0, EINVAL), ("pos_max", -1, EINVAL),
+    ("pos0", None, EINVAL),
+])
+def test_index_rejects(field, value, code):
+    L = V.lib()
+    r, msg = _st(L.v4attn_index_topk, good_index(**{field: value}), None, 0, None)
+    assert r == code and msg
+
+
+def test_index_rejects_tensors_and_workspace():
+    L = V.lib()
+    f = L.v4attn_index_topk
+    assert _st(f, good_index(idx=_T(FAKE, 512, 100)), None, 0, None)[0] == EINVAL
+    assert _st(f, good_index(qi=_T(FAKE + 4, 4096, 4096)), None, 0, None)[0] == EINVAL
+    assert _st(f, good_index(ki=_T(FAKE, 64 * 32768, 32)), None, 0, None)[0] == EINVAL
+    a = good_index()
+    need = L.v4attn_index_topk_workspace(ctypes.byref(a))
+    assert need > 2 * 32768 * 4
+    assert _st(f, a, None, 0, None)[0] == EWORKSPACE
+    assert _st(f, a, FAKE, need - 1, None)[0] == EWORKSPACE
+    assert _st(f, a, FAKE + 16, need, None)[0] == EWORKSPACE
+    # f32 indexer shapes: any head count, dim a multiple of 4
+    a = good_index(dtype=V.F32, heads=4, dim=32, qi=_T(bs=128, rs=128), ki=_T(bs=32 * 32768, rs=32))
+    assert L.v4attn_index_topk_workspace(ctypes.byref(a)) > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("out_dtype", 1, ENOTSUP), ("tq", 2, EINVAL), ("heads", 40, ENOTSUP), ("dim", 96, ENOTSUP),
+    ("branch_mask", 0, EINVAL), ("branch_mask", 9, EINVAL), ("csa_ratio", 0, EINVAL),
+    ("window", -1, EINVAL), ("topk", 0, EINVAL), ("topk", 3000, ENOTSUP), ("scale", float("nan"), EINVAL),
+    ("pos0", None, EINVAL), ("raw_start", None, EINVAL), ("sink", FAKE + 2, EINVAL),
+])
+def test_decode_rejects(field, value, code):
+    L = V.lib()
+    r, msg = _st(L.v4attn_decode, good_attn(**{field: value}), None, 0, None)
+    assert r == code and msg
+
+
+def test_decode_rejects_branch_pointers():
+    L = V.lib()
+    f = L.v4attn_decode
+    assert _st(f, good_attn(kc=_T(None)), None, 0, None)[0] == EINVAL
+    assert _st(f, good_attn(kh=_T(None)), None, 0, None)[0] == EINVAL
+    assert _st(f, good_attn(idx=_T(None)), None, 0, None)[0] == EINVAL
+    assert _st(f, good_attn(o=_T(FAKE, 8192, 8000)), None, 0, None)[0] == EINVAL
+    # disabled branches may be NULL: HCA+SWA only
+    a = good_attn(branch_mask=6, kc=_T(None), vc=_T(None), idx=_T(None))
+    assert V.lib().v4attn_decode_workspace(ctypes.byref(a)) >= 0
+    # prefill accepts tq > 1, decode does not
+    a = good_attn(tq=16, q=_T(bs=16 * 8192, rs=8192), o=_T(bs=16 * 8192, rs=8192))
+    assert _st(L.v4attn_decode, a, None, 0, None)[0] == EINVAL
+    assert _st(L.v4attn_prefill_chunk, good_attn(tq=0), None, 0, None)[0] == EINVAL
+
+
+def test_decode_workspace_and_split_plan():
+    L = V.lib()
+    a = good_attn()
+    need = L.v4attn_decode_workspace(ctypes.byref(a))
+    # two sequences, 512 + 1024 + 128 keys each: the keys are split across workgroups
+    assert need > 0
+    assert _st(L.v4attn_decode, a, None, 0, None)[0] == EWORKSPACE
+
+
+def test_timing_api_validates():
+    L = V.lib()
+    assert L.v4attn_timing_enable(99, 1) == EINVAL
+    assert L.v4attn_timing_read(99, None, 0) == -1
+    L.v4attn_timing_reset()
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this checks the no-device path only")
+    r, msg = _st(V.lib().v4attn_compress, good_compress(), None)
+    assert r == EHIP and msg

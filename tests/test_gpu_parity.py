@@ -1,0 +1,126 @@
+"""Parity of the HIP path with the fp64 oracle, stage by stage (GPU).
+
+Small configurations span several tiles and ragged tails and finish in seconds in
+the oracle; the full configurations run in the launch configuration bench.py times
+and are checked on every row (decode) or on sampled rows (prefill).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import configs as C
+from tests.gpu_harness import Run, assert_close, dev_to_np, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# reduced versions of the configurations: same head shapes, shorter contexts,
+# positions that are not block aligned, several sequences
+SMALL = {
+    "c1_tiny_f32": C.C1,
+    "c2_small": C.C2.small(name="c2_small", batch=3, pos=16389, needles=8),
+    "c3_small": C.C3.small(name="c3_small", pos=65539, needles=16),
+    "c4_small": C.C4.small(name="c4_small", batch=4, pos=16384 + 77, compress_tokens=1024 + 77),
+    "c5_small": C.C5.small(name="c5_small", pos=8192, tq=320, needles=8),
+}
+
+
+def _hca_newest_ok(cfg):
+    return cfg.compress != "hca_newest" or cfg.compress_t0 % cfg.m_hca == 0
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs(name):
+    cfg = SMALL[name]
+    if name == "c4_small":
+        cfg = cfg.small(compress_tokens=1024 + (cfg.pos % cfg.m_hca))
+    assert _hca_newest_ok(cfg)
+    print(f"[case] {name}", flush=True)
+    Run(cfg).run().check_all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_short_context_k_exceeds_visible(dtype):
+    # p < W, n_vis < k: padding with -1, window shorter than W, HCA nearly empty
+    base = C.C1 if dtype == "f32" else C.C2
+    cfg = base.small(name=f"short_{dtype}", batch=2, pos=37, needles=0, topk=64 if dtype == "f32" else 512,
+                     compress="all", compress_tokens=38)
+    print(f"[case] short {dtype}", flush=True)
+    r = Run(cfg).run().check_all()
+    idx = dev_to_np(r.step.idx)
+    assert (idx[:, 0, :9] >= 0).all() and (idx[:, 0, 9:] == -1).all()
+
+
+@pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
+def test_branch_subsets_bf16(mask):
+    cfg = C.C2.small(name=f"mask{mask}", batch=2, pos=4097, branches=mask, needles=4)
+    print(f"[case] mask {mask}", flush=True)
+    Run(cfg).run().check_all()
+
+
+def test_f32_odd_heads_d128_and_bf16_h16_d64():
+    a = C.C1.small(name="f32_h5_d128", heads=5, dim=128, batch=2, pos=999, needles=2, compress_tokens=1000)
+    print("[case] f32 H=5 d=128", flush=True)
+    Run(a).run().check_all()
+    b = C.C2.small(name="bf16_h16_d64", heads=16, dim=64, idx_heads=16, idx_dim=32, batch=2, pos=3001,
+                   topk=64, needles=4)
+    print("[case] bf16 H=16 d=64", flush=True)
+    Run(b).run().check_all()
+
+
+def test_sink_and_explicit_scale():
+    cfg = C.C2.small(name="sink", batch=2, pos=2050, needles=2)
+    r = Run(cfg).run()
+    sink = torch.linspace(-2.0, 3.0, cfg.heads, device="cuda", dtype=torch.float32)
+    import compressed_attention_02_amd as V
+    kw = r.step.attn_kwargs()
+    kw["scale"] = 0.05
+    V.decode(r.t["q"], r.t["pos"], r.step.o, sink=sink, **kw)
+    torch.cuda.synchronize()
+    rows = [(b, 0) for b in range(cfg.batch)]
+    idx = dev_to_np(r.step.idx)
+    caches = {n: r.f64(n) for n in ("kc", "vc", "kh", "vh", "k_raw", "v_raw")}
+    q = O.as_f64(r.g["q"], cfg.dtype)
+    for b, i in rows:
+        o, l = O.decode_query(q[b, 0], cfg.pos, scale=0.05, sink=sink.cpu().numpy().astype(np.float64),
+                              branches=7, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window, idx=idx[b, 0],
+                              raw_start=int(r.g["raw_start"][b]), **{k: v[b] for k, v in caches.items()})
+        assert_close(dev_to_np(r.step.o)[b, 0], o, "bf16", "sink o")
+        assert_close(dev_to_np(r.step.lse)[b, 0], l, "bf16", "sink lse")
+
+
+def test_determinism_and_idx_permutation():
+    cfg = SMALL["c3_small"]
+    r = Run(cfg).run()
+    o1, l1, i1 = (dev_to_np(x).copy() for x in (r.step.o, r.step.lse, r.step.idx))
+    r.step.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, dev_to_np(r.step.o))
+    assert np.array_equal(l1, dev_to_np(r.step.lse))
+    assert np.array_equal(i1, dev_to_np(r.step.idx))
+    # the selected blocks in reverse order give the same output up to rounding order
+    rev = torch.flip(r.step.idx, dims=[2]).contiguous()
+    r.step.idx.copy_(rev)
+    r.step.run_attn()
+    torch.cuda.synchronize()
+    o2 = dev_to_np(r.step.o)
+    assert np.max(np.abs(o2 - o1)) <= 1e-6 * max(1.0, np.abs(o1).max())
+
+
+def test_incremental_compress_bitwise():
+    import compressed_attention_02_amd as V
+    cfg = C.C5.small(name="incr", pos=4096, tq=512, needles=0)
+    r = Run(cfg)
+    t = r.t
+    for ratio, lg, kn, vn in ((4, "logit_csa", "kc", "vc"), (128, "logit_hca", "kh", "vh")):
+        V.compress(t["k_raw"], t["v_raw"], t[lg], t["raw_start"], t[kn], t[vn], t0=4096, n=512, ratio=ratio)
+        torch.cuda.synchronize()
+        one_k, one_v = t[kn].clone(), t[vn].clone()
+        t[kn].zero_()
+        t[vn].zero_()
+        V.compress(t["k_raw"], t["v_raw"], t[lg], t["raw_start"], t[kn], t[vn], t0=4096, n=256, ratio=ratio)
+        V.compress(t["k_raw"], t["v_raw"], t[lg], t["raw_start"], t[kn], t[vn], t0=4352, n=256 + 3, ratio=ratio)
+        torch.cuda.synchronize()
+        lo, hi = 4096 // ratio, (4096 + 512) // ratio
+        assert torch.equal(one_k[:, lo:hi], t[kn][:, lo:hi])
+        assert torch.equal(one_v[:, lo:hi], t[vn][:, lo:hi])
