@@ -31,8 +31,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
 ABI_VERSION = 1
-KERNELS = {"compress": 0, "index_score": 1, "topk_filter": 2, "topk_final": 3, "attn": 4,
-           "merge": 5, "prefill": 6}
+KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5}
 
 
 class V4AttnError(RuntimeError):

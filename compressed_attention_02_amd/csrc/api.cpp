@@ -96,14 +96,13 @@ struct Timing {
 std::mutex g_tmu;
 Timing g_timing[V4A_K_COUNT];
 
-const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_filter", "topk_final",
-                                          "attn", "merge", "prefill"};
+const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select", "attn", "merge",
+                                          "prefill"};
 
 // ---------------------------------------------------------------- plans
 struct IndexPlan {
-  int64_t rows, n_cap, sc_rs, chunk_rows, tile, ntiles, nslices;
-  size_t row_bytes, ws_bytes;
-  size_t off_scores, off_hist, off_sure, off_cand, off_counts;  // per-row byte offsets inside a row record
+  int64_t rows, n_cap, sc_rs, ntiles, sum_rs, chunk_rows;
+  size_t off_summary, ws_bytes;
 };
 
 IndexPlan plan_index(const v4a_index_args* a) {
@@ -111,21 +110,13 @@ IndexPlan plan_index(const v4a_index_args* a) {
   P.rows = (int64_t)a->batch * a->tq;
   P.n_cap = (a->pos_max + 1) / a->ratio;
   P.sc_rs = round_up(std::max<int64_t>(P.n_cap, 1), 64);
-  // region layout (each region holds chunk_rows rows)
-  const int64_t budget = (int64_t)1 << 30;  // scores of one chunk of rows
-  P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, budget / (P.sc_rs * 4)));
-  const int64_t R = P.chunk_rows;
-  P.off_scores = 0;
-  P.off_hist = (size_t)round_up(R * P.sc_rs * 4, 256);
-  P.off_sure = P.off_hist + (size_t)round_up(R * kHistBins * 4, 256);
-  P.off_cand = P.off_sure + (size_t)round_up(R * kMaxTopk * 4, 256);
-  P.off_counts = P.off_cand + (size_t)round_up(R * kCandCap * 8, 256);
-  P.ws_bytes = P.off_counts + (size_t)round_up(R * 16, 256);
-  const int64_t cus = cu_count();
-  const int64_t want = std::max<int64_t>(1, 4 * cus / std::max<int64_t>(1, std::min(P.rows, R)));
-  P.tile = std::min<int64_t>(8192, std::max<int64_t>(256, round_up(cdiv(P.n_cap, want), 256)));
-  P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, P.tile));
-  P.nslices = std::max<int64_t>(1, cdiv(P.n_cap, 4096));
+  P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, kTile));
+  P.sum_rs = round_up(P.ntiles * kTileTop, 32);
+  // rows are processed in chunks whose scores fit in 1 GiB
+  const int64_t row_bytes = P.sc_rs * 4 + P.sum_rs * 8;
+  P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
+  P.off_summary = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
+  P.ws_bytes = P.off_summary + (size_t)round_up(P.chunk_rows * P.sum_rs * 8, 256);
   return P;
 }
 
@@ -142,12 +133,11 @@ AttnPlan plan_attn(const v4a_attn_args* a) {
              ((a->branch_mask & V4A_SWA) ? std::min<int64_t>(a->window, pmax + 1) : 0);
   const int64_t cus = cu_count();
   const int64_t target = 2 * cus;
-  if (P.rows >= target || P.n_keys <= 4 * kAttnChunk) {
-    P.splits = 1;
-    P.kps = std::max<int64_t>(P.n_keys, 1);
-  } else {
+  P.splits = 1;
+  if (P.rows < target && P.n_keys > kAttnChunk) {
     const int64_t per_row = cdiv(target, P.rows);
-    P.kps = std::max<int64_t>(4 * kAttnChunk, round_up(cdiv(P.n_keys, per_row), kAttnChunk));
+    P.kps = std::max<int64_t>(kAttnChunk, round_up(cdiv(P.n_keys, per_row), kAttnChunk));
+    P.kps = std::max<int64_t>(P.kps, round_up(cdiv(P.n_keys, kAttnMaxSplits), kAttnChunk));
     P.splits = cdiv(P.n_keys, P.kps);
   }
   if (P.splits <= 1) {
@@ -397,38 +387,28 @@ v4a_status v4attn_index_topk(const v4a_index_args* a, void* ws, size_t ws_bytes,
   char* base = (char*)ws;
   ScoreP sp{};
   sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
-  sp.scores = (float*)(base + P.off_scores);
-  sp.hist = (uint32_t*)(base + P.off_hist);
+  sp.scores = (float*)base;
+  sp.summary = (uint2*)(base + P.off_summary);
   sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
   sp.wi_bs = a->wi.batch_stride; sp.wi_rs = a->wi.row_stride;
   sp.ki_bs = a->ki.batch_stride; sp.ki_rs = a->ki.row_stride;
-  sp.sc_rs = P.sc_rs;
-  sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio; sp.topk = a->topk;
-  sp.tile = (int)P.tile;
-  TopkP tp{};
-  tp.scores = sp.scores; tp.hist = sp.hist;
-  tp.sure = (uint32_t*)(base + P.off_sure);
-  tp.cand = (uint2*)(base + P.off_cand);
-  tp.counts = (uint32_t*)(base + P.off_counts);
-  tp.pos0 = a->pos0;
+  sp.sc_rs = P.sc_rs; sp.sum_rs = P.sum_rs;
+  sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio;
+  SelectP tp{};
+  tp.scores = sp.scores; tp.summary = sp.summary; tp.pos0 = a->pos0;
   tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
   tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
-  tp.sc_rs = P.sc_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
-  tp.slice = 4096;
+  tp.sc_rs = P.sc_rs; tp.sum_rs = P.sum_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
   for (int64_t r0 = 0; r0 < P.rows; r0 += P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(P.chunk_rows, P.rows - r0);
     sp.row0 = (int)r0;
     tp.row0 = (int)r0;
-    V4A_TRY(hip_check(launch_topk_clear(tp, nr, stream), "topk clear launch"));
     timing_before(V4A_K_INDEX_SCORE, stream);
     V4A_TRY(hip_check(launch_score(a->dtype, sp, nr, (int)P.ntiles, stream), "index score launch"));
     timing_after(V4A_K_INDEX_SCORE, stream);
-    timing_before(V4A_K_TOPK_FILTER, stream);
-    V4A_TRY(hip_check(launch_topk_filter(tp, nr, (int)P.nslices, stream), "topk filter launch"));
-    timing_after(V4A_K_TOPK_FILTER, stream);
-    timing_before(V4A_K_TOPK_FINAL, stream);
-    V4A_TRY(hip_check(launch_topk_final(tp, nr, stream), "topk final launch"));
-    timing_after(V4A_K_TOPK_FINAL, stream);
+    timing_before(V4A_K_TOPK_SELECT, stream);
+    V4A_TRY(hip_check(launch_select(tp, nr, stream), "top-k select launch"));
+    timing_after(V4A_K_TOPK_SELECT, stream);
   }
   return ok();
 }

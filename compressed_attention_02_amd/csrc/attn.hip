@@ -8,12 +8,12 @@
 //
 // Each query (row) sees a virtual key list: [CSA picks | HCA entries 0..e_vis-1 |
 // raw positions max(0,p-W+1)..p].  The list is cut into splits of keys_per_split
-// keys; a workgroup owns one (split, row), walks its keys in chunks of 32 and keeps
+// keys; a workgroup owns one (split, row), walks its keys in chunks of 64 and keeps
 // an online softmax per head.  With one split the workgroup writes o and lse
 // directly; otherwise it writes (U, m, l) partials that merge_kernel combines in a
 // fixed split order (no float atomics: results do not depend on timing).
 //
-// bf16 path, per chunk (one KV head shared by all H query heads, MQA):
+// bf16 path, per chunk of 64 keys (one KV head shared by all H query heads, MQA):
 //   * K rows of the chunk go to LDS row-major, V rows transposed (V^T[d][key]);
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: keys on M, 16 heads per wave on N,
 //     so a lane ends up with 8 keys of one head and the row statistics need only
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   constexpr int KROW = D + 8;      // bf16 per K row in LDS (+16 B keeps ds_read_b128 conflict-free)
   constexpr int VROW = CH + 8;     // bf16 per V^T row in LDS
   constexpr int C8 = D / 8;        // 16-byte chunks per row
-  constexpr int LPT = (CH * C8 + NT - 1) / NT;
+  constexpr int ITEMS = (CH / 2) * C8;          // (key pair, chunk) staging items
+  constexpr int LPT = (ITEMS + NT - 1) / NT;
   __shared__ __align__(16) uint16_t sK[CH * KROW];
   __shared__ __align__(16) uint16_t sV[D * VROW];
   __shared__ int sOK[CH];
@@ -109,6 +110,57 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   const int head = wave * 16 + col;
   const float sl2 = p.scale * kLog2e;
 
+  uint4 pk[LPT][2], pv[LPT][2];
+  int pok[LPT][2];
+  auto fetch = [&](int64_t kc0) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int e = tid + u * NT;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pk[u][h] = make_uint4(0, 0, 0, 0);
+        pv[u][h] = make_uint4(0, 0, 0, 0);
+        pok[u][h] = 0;
+      }
+      if (e < ITEMS) {
+        const int kp2 = e / C8, c8 = e - kp2 * C8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t t = kc0 + 2 * kp2 + h;
+          const uint16_t *kp, *vp;
+          if (t < k_end && key_rows<uint16_t>(p, L, b, i, t, kp, vp)) {
+            pk[u][h] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
+            pv[u][h] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
+            pok[u][h] = 1;
+          }
+        }
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int e = tid + u * NT;
+      if (e < ITEMS) {
+        const int kp2 = e / C8, c8 = e - kp2 * C8;
+        const int key = 2 * kp2;
+        *reinterpret_cast<uint4*>(&sK[key * KROW + c8 * 8]) = pk[u][0];
+        *reinterpret_cast<uint4*>(&sK[(key + 1) * KROW + c8 * 8]) = pk[u][1];
+        // V^T[d][key..key+1]: one 32-bit word per dim holds the pair
+        const uint32_t a[4] = {pv[u][0].x, pv[u][0].y, pv[u][0].z, pv[u][0].w};
+        const uint32_t c[4] = {pv[u][1].x, pv[u][1].y, pv[u][1].z, pv[u][1].w};
+        uint32_t* vt = reinterpret_cast<uint32_t*>(&sV[(c8 * 8) * VROW + key]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          vt[(2 * q) * (VROW / 2)] = (a[q] & 0xffffu) | (c[q] << 16);
+          vt[(2 * q + 1) * (VROW / 2)] = (a[q] >> 16) | (c[q] & 0xffff0000u);
+        }
+        if (c8 == 0) { sOK[key] = pok[u][0]; sOK[key + 1] = pok[u][1]; }
+      }
+    }
+  };
+
+  if (k_begin < k_end) fetch(k_begin);
   bf16x8_t Qb[KS];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs +
@@ -122,107 +174,73 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pk[LPT], pv[LPT];
-  int pok[LPT];
-  auto fetch = [&](int64_t kc0) {
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = tid + u * NT;
-      pk[u] = make_uint4(0, 0, 0, 0);
-      pv[u] = make_uint4(0, 0, 0, 0);
-      pok[u] = 0;
-      if (e < CH * C8) {
-        const int key = e / C8, c8 = e - key * C8;
-        const int64_t t = kc0 + key;
-        const uint16_t *kp, *vp;
-        if (t < k_end && key_rows<uint16_t>(p, L, b, i, t, kp, vp)) {
-          pk[u] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
-          pv[u] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
-          pok[u] = 1;
-        }
-      }
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = tid + u * NT;
-      if (e < CH * C8) {
-        const int key = e / C8, c8 = e - key * C8;
-        *reinterpret_cast<uint4*>(&sK[key * KROW + c8 * 8]) = pk[u];
-        uint16_t* vt = &sV[(c8 * 8) * VROW + key];
-        vt[0 * VROW] = (uint16_t)(pv[u].x & 0xffffu);
-        vt[1 * VROW] = (uint16_t)(pv[u].x >> 16);
-        vt[2 * VROW] = (uint16_t)(pv[u].y & 0xffffu);
-        vt[3 * VROW] = (uint16_t)(pv[u].y >> 16);
-        vt[4 * VROW] = (uint16_t)(pv[u].z & 0xffffu);
-        vt[5 * VROW] = (uint16_t)(pv[u].z >> 16);
-        vt[6 * VROW] = (uint16_t)(pv[u].w & 0xffffu);
-        vt[7 * VROW] = (uint16_t)(pv[u].w >> 16);
-        if (c8 == 0) sOK[key] = pok[u];
-      }
-    }
-  };
-
-  if (k_begin < k_end) fetch(k_begin);
   for (int64_t kc0 = k_begin; kc0 < k_end; kc0 += CH) {
     __syncthreads();
     stash();
     __syncthreads();
     if (kc0 + CH < k_end) fetch(kc0 + CH);
 
-    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    // S^T for 4 tiles of 16 keys: lane holds head col, keys 16*kt + 4*grp + e
+    f32x4 S[4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&sK[col * KROW + s * 32 + grp * 8]));
-      const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&sK[(16 + col) * KROW + s * 32 + grp * 8]));
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Qb[s], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Qb[s], S1, 0, 0, 0);
-    }
-    float x[8];
+    for (int kt = 0; kt < 4; ++kt) {
+      S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = sOK[4 * grp + e] ? S0[e] * sl2 : -INFINITY;
-      x[4 + e] = sOK[16 + 4 * grp + e] ? S1[e] * sl2 : -INFINITY;
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t A = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&sK[(16 * kt + col) * KROW + s * 32 + grp * 8]));
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qb[s], S[kt], 0, 0, 0);
+      }
     }
+    float x[16];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * kt + e] = sOK[16 * kt + 4 * grp + e] ? S[kt][e] * sl2 : -INFINITY;
     float cm = x[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
+    for (int e = 1; e < 16; ++e) cm = fmaxf(cm, x[e]);
     cm = fmaxf(cm, __shfl_xor(cm, 16));
     cm = fmaxf(cm, __shfl_xor(cm, 32));
     const float m_new = fmaxf(m_run, cm);
-    float alpha = 1.f, pe[8];
+    float alpha = 1.f, pe[16];
     if (m_new == -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = 0.f;
+      for (int e = 0; e < 16; ++e) pe[e] = 0.f;
     } else {
       alpha = exp2f(m_run - m_new);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = exp2f(x[e] - m_new);
+      for (int e = 0; e < 16; ++e) pe[e] = exp2f(x[e] - m_new);
     }
     m_run = m_new;
     float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ps += pe[e];
+    for (int e = 0; e < 16; ++e) ps += pe[e];
     l_run = l_run * alpha + ps;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
-    float hi[8], lo[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hi[e] = bf2f(f2bf(pe[e]));
-      lo[e] = pe[e] - hi[e];
-    }
-    const bf16x8_t Bhi = __builtin_bit_cast(bf16x8_t, pack8(hi));
-    const bf16x8_t Blo = __builtin_bit_cast(bf16x8_t, pack8(lo));
+    for (int kk = 0; kk < 2; ++kk) {
+      // P^T operand of keys 32kk + {4grp+e, 16+4grp+e}: tiles 2kk and 2kk+1
+      float hi[8], lo[8];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vr = &sV[(dt * 16 + col) * VROW];
-      const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 4 * grp);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * grp);
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, O[dt], 0, 0, 0);
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, O[dt], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = bf2f(f2bf(pe[8 * kk + e]));
+        hi[4 + e] = bf2f(f2bf(pe[8 * kk + 4 + e]));
+        lo[e] = pe[8 * kk + e] - hi[e];
+        lo[4 + e] = pe[8 * kk + 4 + e] - hi[4 + e];
+      }
+      const bf16x8_t Bhi = __builtin_bit_cast(bf16x8_t, pack8(hi));
+      const bf16x8_t Blo = __builtin_bit_cast(bf16x8_t, pack8(lo));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vr = &sV[(dt * 16 + col) * VROW + 32 * kk];
+        const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 4 * grp);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * grp);
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, O[dt], 0, 0, 0);
+      }
     }
   }
   l_run += __shfl_xor(l_run, 16);
@@ -327,30 +345,60 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 }
 
 // ------------------------------------------------------------------ merge
-// One workgroup per (row, head), one thread per output column; splits are merged
-// in index order.
-__global__ void merge_kernel(AttnP p) {
-  const int row = blockIdx.x, head = blockIdx.y, c = threadIdx.x;
+// One 256-thread workgroup per (row, head).  Split weights go to LDS; the weighted
+// sum over splits is spread over 256/D thread groups and combined in LDS, always in
+// the same order, so the result does not depend on timing.
+constexpr int kMergeThreads = 256;
+constexpr int kMaxSplits = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kMergeThreads];
+  const int row = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int b = row / p.tq, i = row - b * p.tq;
-  const int S = p.splits;
+  const int S = p.splits, D = p.dim;
   const float* ml = p.part_ml + ((int64_t)row * S * p.heads + head) * 2;
-  const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * p.dim + c;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(int64_t)s * p.heads * 2]);
-  float l = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float ms = ml[(int64_t)s * p.heads * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      l = fmaf(w, ml[(int64_t)s * p.heads * 2 + 1], l);
-      acc = fmaf(w, po[(int64_t)s * p.heads * p.dim], acc);
-    }
+  const int64_t ml_step = (int64_t)p.heads * 2;
+  // 1) global max of the split maxima
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, ml[s * ml_step]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  float M = s_red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
+  // 2) split weights and the total sum
+  float part = 0.f;
+  for (int s = tid; s < S; s += kMergeThreads) {
+    const float ms = ml[s * ml_step];
+    const float w = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    s_w[s] = w;
+    part = fmaf(w, ml[s * ml_step + 1], part);
   }
-  float lse;
-  const float f = finish_head(M, l, p.sink, head, &lse);
-  p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * p.dim + c] = acc * f;
-  if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+  part = wave_sum(part);
+  if ((tid & 63) == 0) s_red[tid >> 6] = part;
+  __syncthreads();
+  float l = 0.f;
+  for (int w = 0; w < kMergeThreads / 64; ++w) l += s_red[w];
+  __syncthreads();
+  // 3) weighted sum of the partial outputs: thread (g, c) takes splits g, g+G, ...
+  const int G = kMergeThreads / D;
+  const int c = tid % D, g = tid / D;
+  const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * D + c;
+  const int64_t po_step = (int64_t)p.heads * D;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int s = g; s < S; s += G) acc = fmaf(s_w[s], po[s * po_step], acc);
+  s_red[tid] = acc;
+  __syncthreads();
+  if (g == 0) {
+    for (int gg = 1; gg < G; ++gg) acc += s_red[gg * D + c];
+    float lse;
+    const float f = finish_head(M, l, p.sink, head, &lse);
+    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + c] = acc * f;
+    if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+  }
 }
 
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s) {
@@ -374,7 +422,8 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s) {
 }
 
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3((unsigned)p.dim), 0, s, p);
+  if (p.splits > kMaxSplits) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -6,25 +6,29 @@
 // section: k = 1024 for Pro, 512 for Flash).  Score form fixed by the layer
 // configuration: s_j = sum_h w_h * ReLU(qi_h . ki_j).
 //
-// Pipeline per launch (rows = query tokens):
-//   clear   zero the per-row radix histograms and list counters
-//   score   one workgroup per (tile of blocks, row): bf16 MFMA 16x16x32 with the
-//           indexer heads on M and the blocks on N, or fp32 VALU; writes fp32 scores
-//           and adds the tile's histogram of the top 12 key bits into the row's one
-//   filter  every workgroup re-derives the threshold bin from the histogram, then
-//           compacts its slice: ids above the bin ("sure") and (key, id) pairs inside
-//           the bin ("candidates")
-//   final   one workgroup per row: two more radix levels over the candidates fix
-//           the exact k-th key; ties at that key go to the lowest ids (radix on the
-//           id); the k ids are bitonic-sorted ascending and written with -1 padding
-// Keys are the order-preserving uint32 image of the fp32 scores, so "larger key"
-// is "larger score"; the selection is exact and independent of launch shape.
+// Two launches per group of query rows, with no global atomics and no state that
+// has to be cleared between calls:
+//   score   one workgroup per (tile of 256 blocks, row): bf16 MFMA 16x16x32 (indexer
+//           heads on M, blocks on N) or fp32 VALU.  Writes the fp32 scores and the
+//           tile's 8 best (key, id) pairs.
+//   select  one 1024-thread workgroup per row.  The k-th largest key among all tile
+//           summaries is a lower bound tau of the row's true k-th key (any subset's
+//           k-th largest is).  A tile whose 8th best key is below tau has no other
+//           element >= tau; tiles that fail this test are rescanned.  The pool of
+//           every element with key >= tau (LDS) therefore holds the top-k, which a
+//           rank search over power-of-two slices of the live key range (then of the
+//           ids, for ties: the lower id wins) extracts exactly.  Tiles report their 8
+//           in id order and the pool is built by order-preserving compaction, so the
+//           k ids come out ascending without a sort.  If the pool would overflow LDS
+//           (or a row has more than 2048 tiles), the same search and compaction run
+//           over the whole row instead.  Rows with n_vis < k are padded with -1.
+// Keys are the order-preserving uint32 image of the fp32 scores, so "larger key" is
+// "larger score"; the result does not depend on launch shape or timing.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace v4a {
 
-// ------------------------------------------------------------------ helpers
 __device__ __forceinline__ void row_coords(int row, int tq, const int64_t* pos0, int& b, int& i,
                                            int64_t& pos) {
   b = row / tq;
@@ -32,11 +36,53 @@ __device__ __forceinline__ void row_coords(int row, int tq, const int64_t* pos0,
   pos = pos0[b] + i;
 }
 
-// Flush a workgroup's LDS histogram into the row's global histogram.
-__device__ __forceinline__ void flush_hist(const uint32_t* s_hist, uint32_t* gh) {
-  for (int t = threadIdx.x; t < kHistBins; t += blockDim.x) {
-    const uint32_t c = s_hist[t];
-    if (c) atomicAdd(&gh[t], c);
+// (key, id) packed so that the larger value is the better element: higher key, then
+// lower id.  0 marks "no element".
+__device__ __forceinline__ uint64_t pack_kid(uint32_t key, uint32_t id) {
+  return ((uint64_t)key << 32) | (uint64_t)(~id);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// The 8 best of a tile's 256 packed values (s_v, one per thread of a 256-thread
+// workgroup) to out[0..7] as (key, id), in ascending id order (missing entries, for
+// tiles with fewer than 8 elements, are (0, 0xffffffff) and come last).
+__device__ void tile_top8(const uint64_t* s_v, uint64_t* s_w, uint2* out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t v = s_v[threadIdx.x];
+#pragma unroll
+  for (int r = 0; r < kTileTop; ++r) {
+    const uint64_t m = wave_max_u64(v);
+    if (v == m) v = 0;
+    if (lane == 0) s_w[wave * kTileTop + r] = m;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t u = lane < 4 * kTileTop ? s_w[lane] : 0;
+    uint64_t mine = 0;
+#pragma unroll
+    for (int r = 0; r < kTileTop; ++r) {
+      const uint64_t m = wave_max_u64(u);
+      if (u == m) u = 0;
+      if (lane == r) mine = m;
+    }
+    const uint32_t id = ~(uint32_t)mine;
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < kTileTop; ++q) {
+      const uint32_t oid = (uint32_t)__shfl((int)id, q);
+      rank += (oid < id || (oid == id && q < lane)) ? 1 : 0;
+    }
+    if (lane < kTileTop) out[rank] = make_uint2((uint32_t)(mine >> 32), id);
   }
 }
 
@@ -48,19 +94,33 @@ __device__ __forceinline__ void flush_hist(const uint32_t* s_hist, uint32_t* gh)
 // The dims a lane group carries only have to agree between A and B.
 template <int MT, int KS>
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
-  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint64_t s_v[kTile];
+  __shared__ uint64_t s_w[4 * kTileTop];
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = (pos + 1) / p.ratio;
-  const int64_t tile0 = (int64_t)blockIdx.x * p.tile;
+  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
   if (tile0 >= nvis) return;
-  for (int t = threadIdx.x; t < kHistBins; t += 256) s_hist[t] = 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   constexpr int DI = KS * 32;
+  const uint16_t* ki = reinterpret_cast<const uint16_t*>(p.ki) + (int64_t)b * p.ki_bs;
+  // blocks of this wave: tile0 + wave*16 + u*64 + col, u = 0..3
+  constexpr int U = kTile / 64;
+  bf16x8_t Bv[U][KS];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = tile0 + wave * 16 + u * 64 + col;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j < nvis) v = *reinterpret_cast<const uint4*>(ki + j * p.ki_rs + s * 32 + grp * 8);
+      Bv[u][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
   const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
   bf16x8_t A[MT][KS];
 #pragma unroll
@@ -75,73 +135,57 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[mt][e] = wi[mt * 16 + grp * 4 + e];
-  __syncthreads();
 
-  const uint16_t* ki = reinterpret_cast<const uint16_t*>(p.ki) + (int64_t)b * p.ki_bs;
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
-  const int64_t tile_end = min(tile0 + (int64_t)p.tile, nvis);
-  constexpr int U = 4;  // 16-block groups in flight per wave
-  for (int64_t j0 = tile0 + wave * 16; j0 < tile_end; j0 += 4 * 16 * U) {
-    bf16x8_t Bv[U][KS];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + u * 64 + col;
-      const bool ok = j < tile_end;
+  for (int u = 0; u < U; ++u) {
+    float part = 0.f;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (ok) v = *reinterpret_cast<const uint4*>(ki + j * p.ki_rs + s * 32 + grp * 8);
-        Bv[u][s] = __builtin_bit_cast(bf16x8_t, v);
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[u][s], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(acc[e], 0.f), part);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float part = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[u][s], acc, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(acc[e], 0.f), part);
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      const int64_t j = j0 + u * 64 + col;
-      if (grp == 0 && j < tile_end) {
-        sc[j] = part;
-        atomicAdd(&s_hist[score_key(part) >> (32 - kHistBits)], 1u);
-      }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    const int t = wave * 16 + u * 64 + col;
+    const int64_t j = tile0 + t;
+    if (grp == 0) {
+      if (j < nvis) sc[j] = part;
+      s_v[t] = j < nvis ? pack_kid(score_key(part), (uint32_t)j) : 0ull;
     }
   }
   __syncthreads();
-  flush_hist(s_hist, p.hist + (int64_t)lr * kHistBins);
+  tile_top8(s_v, s_w, p.summary + (int64_t)lr * p.sum_rs + (int64_t)blockIdx.x * kTileTop);
 }
 
 // ------------------------------------------------------------------ score, fp32 VALU
-// One thread per block; the row's indexer queries and weights sit in LDS.
+// One thread per block of the tile; the row's indexer queries and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
-  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ uint64_t s_v[kTile];
+  __shared__ uint64_t s_w[4 * kTileTop];
   extern __shared__ float s_q[];  // [heads*dim] then [heads]
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = (pos + 1) / p.ratio;
-  const int64_t tile0 = (int64_t)blockIdx.x * p.tile;
+  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
   if (tile0 >= nvis) return;
   const int HD = p.heads * p.dim;
   const float* qi = reinterpret_cast<const float*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
   const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
-  for (int t = threadIdx.x; t < kHistBins; t += 256) s_hist[t] = 0;
   for (int t = threadIdx.x; t < HD; t += 256) s_q[t] = qi[t];
   for (int t = threadIdx.x; t < p.heads; t += 256) s_q[HD + t] = wi[t];
   __syncthreads();
   const float* ki = reinterpret_cast<const float*>(p.ki) + (int64_t)b * p.ki_bs;
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
-  const int64_t tile_end = min(tile0 + (int64_t)p.tile, nvis);
-  for (int64_t j = tile0 + threadIdx.x; j < tile_end; j += 256) {
+  const int64_t j = tile0 + threadIdx.x;
+  uint64_t v = 0;
+  if (j < nvis) {
     const float* kj = ki + j * p.ki_rs;
     float s = 0.f;
     for (int h = 0; h < p.heads; ++h) {
@@ -157,10 +201,11 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
       s = fmaf(s_q[HD + h], fmaxf(dot, 0.f), s);
     }
     sc[j] = s;
-    atomicAdd(&s_hist[score_key(s) >> (32 - kHistBits)], 1u);
+    v = pack_kid(score_key(s), (uint32_t)j);
   }
+  s_v[threadIdx.x] = v;
   __syncthreads();
-  flush_hist(s_hist, p.hist + (int64_t)lr * kHistBins);
+  tile_top8(s_v, s_w, p.summary + (int64_t)lr * p.sum_rs + (int64_t)blockIdx.x * kTileTop);
 }
 
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s) {
@@ -181,256 +226,356 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
   return hipErrorInvalidValue;
 }
 
-// ------------------------------------------------------------------ radix helpers
-// Given an LDS histogram of nb bins (nb a multiple of 256) and a rank r >= 1, find
-// the bin holding the r-th element counted from the top (descending == true) or
-// from the bottom; returns the bin and the count strictly before it in that order.
-// All 256 threads must call it.
-struct RankHit { int bin; uint32_t before; };
+// ------------------------------------------------------------------ selection
+constexpr int kNW = kSelThreads / 64;
+constexpr int kBins = 4096;
 
-__device__ RankHit find_rank(const uint32_t* hist, int nb, uint32_t r, bool descending,
-                             uint32_t* s_scan /*[256]*/, RankHit* s_hit) {
+struct SelShared {
+  uint32_t hist[kBins];
+  uint32_t wtot[kNW];
+  uint32_t wmin[kNW], wmax[kNW];
+  uint32_t pool_key[kPoolCap];
+  uint32_t pool_id[kPoolCap];
+  uint32_t fail[256], fcount[256], fbase[256];
+  uint32_t n_pool, n_fail, flag;
+  uint32_t hit_bin, hit_before;
+};
+
+// inclusive prefix sum over the workgroup (one value per thread)
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) sh.wtot[wave] = v;
+  __syncthreads();
+  uint32_t add = 0;
+  for (int w = 0; w < wave; ++w) add += sh.wtot[w];
+  __syncthreads();
+  return v + add;
+}
+
+// min and max over the workgroup
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t& omn, uint32_t& omx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  if (lane == 0) { sh.wmin[wave] = mn; sh.wmax[wave] = mx; }
+  __syncthreads();
+  omn = sh.wmin[0];
+  omx = sh.wmax[0];
+  for (int w = 1; w < kNW; ++w) { omn = min(omn, sh.wmin[w]); omx = max(omx, sh.wmax[w]); }
+  __syncthreads();
+}
+
+// Bin of sh.hist[0..nb) holding the r-th element (1-based) counted from the top
+// (descending) or from the bottom, and the count strictly before it.
+__device__ void find_rank(SelShared& sh, int nb, uint32_t r, bool descending, uint32_t& bin,
+                          uint32_t& before) {
   const int t = threadIdx.x;
-  const int per = nb / 256;
+  const int per = (nb + kSelThreads - 1) / kSelThreads;
   uint32_t sum = 0;
   for (int e = 0; e < per; ++e) {
     const int o = t * per + e;
-    sum += hist[descending ? nb - 1 - o : o];
+    if (o < nb) sum += sh.hist[descending ? nb - 1 - o : o];
   }
-  s_scan[t] = sum;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over 256 partial sums
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = t >= off ? s_scan[t - off] : 0u;
-    __syncthreads();
-    s_scan[t] += v;
-    __syncthreads();
-  }
-  const uint32_t incl = s_scan[t];
+  const uint32_t incl = block_scan(sum, sh);
   const uint32_t excl = incl - sum;
   if (excl < r && r <= incl) {
     uint32_t run = excl;
     for (int e = 0; e < per; ++e) {
       const int o = t * per + e;
-      const int bin = descending ? nb - 1 - o : o;
-      const uint32_t c = hist[bin];
-      if (run + c >= r) { s_hit->bin = bin; s_hit->before = run; break; }
+      if (o >= nb) break;
+      const int bb = descending ? nb - 1 - o : o;
+      const uint32_t c = sh.hist[bb];
+      if (run + c >= r) { sh.hit_bin = (uint32_t)bb; sh.hit_before = run; break; }
       run += c;
     }
   }
   __syncthreads();
-  const RankHit h = *s_hit;
+  bin = sh.hit_bin;
+  before = sh.hit_before;
   __syncthreads();
-  return h;
 }
 
-// ------------------------------------------------------------------ clear
-__global__ void topk_clear_kernel(uint32_t* hist, uint32_t* counts, int64_t nh, int64_t nc) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nh; t += stride) hist[t] = 0;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nc; t += stride) counts[t] = 0;
-}
-
-hipError_t launch_topk_clear(const TopkP& p, int nrows, hipStream_t s) {
-  const int64_t nh = (int64_t)nrows * kHistBins, nc = (int64_t)nrows * 4;
-  const int64_t want = (nh + 255) / 256;
-  const int blocks = (int)(want < 1024 ? want : 1024);
-  hipLaunchKernelGGL(topk_clear_kernel, dim3(blocks), dim3(256), 0, s, const_cast<uint32_t*>(p.hist),
-                     p.counts, nh, nc);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ filter
-constexpr int kFilterSlice = 4096;
-
-__global__ __launch_bounds__(256) void topk_filter_kernel(TopkP p) {
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ uint32_t s_scan[256];
-  __shared__ RankHit s_hit;
-  __shared__ uint32_t s_sure[kMaxTopk];
-  __shared__ uint2 s_cand[kFilterSlice];
-  __shared__ uint32_t s_ns, s_nc, s_bs, s_bc;
-  const int lr = blockIdx.y;
-  int b, i;
-  int64_t pos;
-  row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
-  const int64_t nvis = (pos + 1) / p.ratio;
-  if (nvis <= p.topk) return;                      // everything is selected
-  const int64_t start = (int64_t)blockIdx.x * p.slice;
-  if (start >= nvis) return;
-  const uint32_t* gh = p.hist + (int64_t)lr * kHistBins;
-  for (int t = threadIdx.x; t < kHistBins; t += 256) s_hist[t] = gh[t];
-  if (threadIdx.x == 0) { s_ns = 0; s_nc = 0; }
-  __syncthreads();
-  const RankHit h1 = find_rank(s_hist, kHistBins, (uint32_t)p.topk, true, s_scan, &s_hit);
-  const uint32_t b1 = (uint32_t)h1.bin;
-  const bool overflow = s_hist[b1] > (uint32_t)kCandCap;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    p.counts[(int64_t)lr * 4 + 2] = b1;
-    p.counts[(int64_t)lr * 4 + 3] = h1.before;
-  }
-  const float* sc = p.scores + (int64_t)lr * p.sc_rs;
-  const int64_t end = min(start + (int64_t)p.slice, nvis);
-  for (int64_t j = start + threadIdx.x; j < end; j += 256) {
-    const uint32_t key = score_key(sc[j]);
-    const uint32_t bin = key >> (32 - kHistBits);
-    if (bin > b1) {
-      s_sure[atomicAdd(&s_ns, 1u)] = (uint32_t)j;
-    } else if (bin == b1 && !overflow) {
-      s_cand[atomicAdd(&s_nc, 1u)] = make_uint2(key, (uint32_t)j);
+// Rank search over the values `val(key, id)` of the elements that `each` visits and
+// `keep(key, id)` accepts: returns the value v* holding the r-th element counted
+// from the top (descending) or the bottom, and through r the rank of the wanted
+// element among those equal to v*.  Bins are power-of-two slices of the live
+// [lo, hi] range, so keys that sit close together spread over many bins and the
+// LDS atomics stay free of contention; at most 3 levels narrow 32 bits to one value.
+template <class Each, class Keep, class Val>
+__device__ uint32_t rank_search(Each each, Keep keep, Val val, uint32_t& r, bool descending, SelShared& sh,
+                                uint32_t& n_equal) {
+  uint32_t mn = 0xffffffffu, mx = 0;
+  each([&](uint32_t key, uint32_t id) {
+    if (keep(key, id)) { const uint32_t v = val(key, id); mn = min(mn, v); mx = max(mx, v); }
+  });
+  uint32_t lo, hi;
+  block_minmax(mn, mx, sh, lo, hi);
+  n_equal = 0;
+  if (lo > hi) return lo;   // nothing accepted (callers never ask for that)
+  while (true) {
+    const uint64_t range = (uint64_t)hi - lo + 1;
+    int shift = 0;
+    while ((range >> shift) > (uint64_t)kBins) ++shift;
+    const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+    for (int t = threadIdx.x; t < nb; t += kSelThreads) sh.hist[t] = 0;
+    __syncthreads();
+    each([&](uint32_t key, uint32_t id) {
+      if (keep(key, id)) {
+        const uint32_t v = val(key, id);
+        if (v >= lo && v <= hi) atomicAdd(&sh.hist[(v - lo) >> shift], 1u);
+      }
+    });
+    __syncthreads();
+    uint32_t bin, before;
+    find_rank(sh, nb, r, descending, bin, before);
+    r -= before;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint32_t nhi = (uint32_t)min<uint64_t>((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
+    if (shift == 0) {
+      n_equal = sh.hist[bin];
+      __syncthreads();
+      return nlo;
     }
+    lo = nlo;
+    hi = nhi;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    s_bs = s_ns ? atomicAdd(&p.counts[(int64_t)lr * 4 + 0], s_ns) : 0u;
-    s_bc = s_nc ? atomicAdd(&p.counts[(int64_t)lr * 4 + 1], s_nc) : 0u;
-  }
-  __syncthreads();
-  uint32_t* gs = p.sure + (int64_t)lr * kMaxTopk;
-  uint2* gc = p.cand + (int64_t)lr * kCandCap;
-  for (uint32_t t = threadIdx.x; t < s_ns; t += 256) gs[s_bs + t] = s_sure[t];
-  for (uint32_t t = threadIdx.x; t < s_nc; t += 256) gc[s_bc + t] = s_cand[t];
 }
 
-hipError_t launch_topk_filter(const TopkP& p, int nrows, int nslices, hipStream_t s) {
-  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nslices, (unsigned)nrows), dim3(256), 0, s, p);
-  return hipGetLastError();
+// The key threshold T and the largest tie id of the exact top-k over the visited
+// elements: an element is selected iff key > T, or key == T and id <= id_max.
+template <class Each>
+__device__ void topk_threshold(Each each, uint32_t k, SelShared& sh, uint32_t& T, uint32_t& id_max) {
+  uint32_t r = k, n_tie;
+  T = rank_search(each, [](uint32_t, uint32_t) { return true; },
+                  [](uint32_t key, uint32_t) { return key; }, r, true, sh, n_tie);
+  id_max = 0xffffffffu;
+  if (r < n_tie) {      // ties at T: the r lowest ids among them
+    uint32_t n_eq;
+    id_max = rank_search(each, [T](uint32_t key, uint32_t) { return key == T; },
+                         [](uint32_t, uint32_t id) { return id; }, r, false, sh, n_eq);
+  }
 }
 
-// ------------------------------------------------------------------ final
-// Candidates of the threshold bin come from the row's candidate list, or, when the
-// bin held more than kCandCap elements, from a rescan of the row's scores.
-struct CandSrc {
-  const uint2* list; const float* sc; uint32_t n; int64_t nvis; uint32_t b1; bool from_list;
-  __device__ __forceinline__ int64_t size() const { return from_list ? (int64_t)n : nvis; }
-  // returns false when element t is not in the threshold bin
-  __device__ __forceinline__ bool get(int64_t t, uint32_t& key, uint32_t& id) const {
-    if (from_list) { const uint2 v = list[t]; key = v.x; id = v.y; return true; }
-    key = score_key(sc[t]);
-    id = (uint32_t)t;
-    return (key >> (32 - kHistBits)) == b1;
-  }
-};
+__device__ __forceinline__ bool picked(uint32_t key, uint32_t id, uint32_t T, uint32_t id_max) {
+  return key > T || (key == T && id <= id_max);
+}
 
-__global__ __launch_bounds__(256) void topk_final_kernel(TopkP p) {
-  __shared__ uint32_t s_h[2048];
-  __shared__ uint32_t s_scan[256];
-  __shared__ RankHit s_hit;
-  __shared__ uint32_t s_sel[kMaxTopk];
-  __shared__ uint32_t s_n;
+constexpr int kMaxTilesPerThread = 2;
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectP p) {
+  __shared__ SelShared sh;
   const int lr = blockIdx.x;
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = (pos + 1) / p.ratio;
   const int k = p.topk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* out = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs;
-  float* sel = p.sel ? p.sel + (int64_t)b * p.sel_bs + (int64_t)i * p.sel_rs : nullptr;
+  float* selp = p.sel ? p.sel + (int64_t)b * p.sel_bs + (int64_t)i * p.sel_rs : nullptr;
   const float* sc = p.scores + (int64_t)lr * p.sc_rs;
   if (nvis <= k) {
-    for (int t = threadIdx.x; t < k; t += 256) {
+    for (int t = tid; t < k; t += kSelThreads) {
       out[t] = t < nvis ? t : -1;
-      if (sel) sel[t] = t < nvis ? sc[t] : 0.f;
+      if (selp) selp[t] = t < nvis ? sc[t] : 0.f;
     }
     return;
   }
-  const uint32_t* cnt = p.counts + (int64_t)lr * 4;
-  const uint32_t n_sure = cnt[0], n_list = cnt[1], b1 = cnt[2], above1 = cnt[3];
-  const uint32_t bin1_total = p.hist[(int64_t)lr * kHistBins + b1];
-  CandSrc src{p.cand + (int64_t)lr * kCandCap, sc, n_list, nvis, b1, bin1_total <= (uint32_t)kCandCap};
-  const uint32_t r = (uint32_t)k - above1;       // 1 <= r <= bin1_total
-  const int64_t ns = src.size();
+  const uint2* U = p.summary + (int64_t)lr * p.sum_rs;
+  const int64_t ntiles = (nvis + kTile - 1) / kTile;
+  const int tpt = ntiles <= kSelThreads ? 1 : kMaxTilesPerThread;   // tiles per thread
+  bool fast = ntiles <= (int64_t)kSelThreads * kMaxTilesPerThread;
 
-  // level 2: key bits [19:10]
-  for (int t = threadIdx.x; t < 1024; t += 256) s_h[t] = 0;
-  __syncthreads();
-  for (int64_t t = threadIdx.x; t < ns; t += 256) {
-    uint32_t key, id;
-    if (src.get(t, key, id)) atomicAdd(&s_h[(key >> 10) & 1023u], 1u);
+  // thread t owns tiles [t*tpt, t*tpt + tpt): their summaries (id order) in registers
+  uint32_t uk[kMaxTilesPerThread][kTileTop], ui[kMaxTilesPerThread][kTileTop];
+#pragma unroll
+  for (int q = 0; q < kMaxTilesPerThread; ++q) {
+    const int64_t t = (int64_t)tid * tpt + q;
+    const bool own = fast && q < tpt && t < ntiles;
+    const uint4* src = reinterpret_cast<const uint4*>(U + t * kTileTop);
+#pragma unroll
+    for (int j = 0; j < kTileTop / 2; ++j) {
+      uint4 e = make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
+      if (own) e = src[j];
+      uk[q][2 * j] = e.x; ui[q][2 * j] = e.y; uk[q][2 * j + 1] = e.z; ui[q][2 * j + 1] = e.w;
+    }
   }
-  __syncthreads();
-  const RankHit h2 = find_rank(s_h, 1024, r, true, s_scan, &s_hit);
-  const uint32_t r2 = r - h2.before;
-  // level 3: key bits [9:0] among keys matching b1:b2
-  const uint32_t hi22 = (b1 << 10) | (uint32_t)h2.bin;
-  for (int t = threadIdx.x; t < 1024; t += 256) s_h[t] = 0;
-  __syncthreads();
-  for (int64_t t = threadIdx.x; t < ns; t += 256) {
-    uint32_t key, id;
-    if (src.get(t, key, id) && (key >> 10) == hi22) atomicAdd(&s_h[key & 1023u], 1u);
-  }
-  __syncthreads();
-  const RankHit h3 = find_rank(s_h, 1024, r2, true, s_scan, &s_hit);
-  const uint32_t r3 = r2 - h3.before;             // how many of the ties at T to take
-  const uint32_t T = (hi22 << 10) | (uint32_t)h3.bin;
-  const uint32_t ties = s_h[h3.bin];
-  // ties at T: take the r3 lowest ids -> threshold id by radix on the id, ascending,
-  // over bits [31:21], [20:10], [9:0]
-  uint32_t id_max = 0xffffffffu;
-  if (r3 < ties) {
-    uint32_t rr = r3, prefix = 0;
-    for (int lvl = 0; lvl < 3; ++lvl) {
-      const int shift = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
-      const int nbins = lvl == 2 ? 1024 : 2048;
-      for (int t = threadIdx.x; t < nbins; t += 256) s_h[t] = 0;
-      __syncthreads();
-      for (int64_t t = threadIdx.x; t < ns; t += 256) {
-        uint32_t key, id;
-        if (!src.get(t, key, id) || key != T) continue;
-        if (lvl > 0 && (id >> (lvl == 1 ? 21 : 10)) != prefix) continue;
-        atomicAdd(&s_h[(id >> shift) & (uint32_t)(nbins - 1)], 1u);
+  uint32_t T = 0, id_max = 0xffffffffu;
+  uint32_t np = 0;
+  if (fast) {
+    // tau: the k-th largest summary key, a lower bound of the row's k-th key (0 when the
+    // summaries hold fewer than k elements)
+    uint32_t tau = 0;
+    if (ntiles * kTileTop >= k) {
+      uint32_t r = (uint32_t)k, n_eq;
+      tau = rank_search(
+          [&](auto&& f) {
+#pragma unroll
+            for (int q = 0; q < kMaxTilesPerThread; ++q)
+#pragma unroll
+              for (int j = 0; j < kTileTop; ++j)
+                if ((int64_t)tid * tpt + q < ntiles && q < tpt) f(uk[q][j], ui[q][j]);
+          },
+          [](uint32_t, uint32_t) { return true; }, [](uint32_t key, uint32_t) { return key; }, r, true, sh,
+          n_eq);
+    }
+    // per owned tile: count of elements >= tau, or a rescan slot when the tile may hold
+    // more of them than its summary shows
+    if (tid == 0) { sh.n_fail = 0; sh.flag = 0; }
+    __syncthreads();
+    int fslot[kMaxTilesPerThread];
+    uint32_t cnt[kMaxTilesPerThread];
+#pragma unroll
+    for (int q = 0; q < kMaxTilesPerThread; ++q) {
+      fslot[q] = -1;
+      cnt[q] = 0;
+      const int64_t t = (int64_t)tid * tpt + q;
+      if (q >= tpt || t >= ntiles) continue;
+      const int64_t valid = min<int64_t>(kTile, nvis - t * kTile);
+      uint32_t kmin = 0xffffffffu;
+#pragma unroll
+      for (int j = 0; j < kTileTop; ++j) {
+        if (ui[q][j] != 0xffffffffu) {
+          cnt[q] += uk[q][j] >= tau ? 1u : 0u;
+          kmin = min(kmin, uk[q][j]);
+        }
+      }
+      if (valid > kTileTop && kmin >= tau) {
+        const uint32_t slot = atomicAdd(&sh.n_fail, 1u);
+        if (slot < 256u) { fslot[q] = (int)slot; sh.fail[slot] = (uint32_t)t; }
+        else sh.flag = 1;
+      }
+    }
+    __syncthreads();
+    const uint32_t nf = sh.n_fail;
+    if (sh.flag) fast = false;
+    if (fast && nf) {
+      // a wave counts the elements >= tau of each failing tile
+      for (uint32_t f = wave; f < nf; f += kNW) {
+        const int64_t base = (int64_t)sh.fail[f] * kTile;
+        uint32_t c = 0;
+        for (int r = 0; r < kTile / 64; ++r) {
+          const int64_t j = base + r * 64 + lane;
+          const bool hit = j < nvis && score_key(sc[j]) >= tau;
+          c += __popcll(__ballot(hit));
+        }
+        if (lane == 0) sh.fcount[f] = c;
       }
       __syncthreads();
-      const RankHit hh = find_rank(s_h, nbins, rr, false, s_scan, &s_hit);
-      rr -= hh.before;
-      prefix = (prefix << (lvl == 0 ? 0 : (lvl == 1 ? 11 : 10))) | (uint32_t)hh.bin;
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q)
+        if (fslot[q] >= 0) cnt[q] = sh.fcount[fslot[q]];
     }
-    id_max = prefix;  // the r3-th lowest id among the ties
-  }
-  // gather: sure ids + candidates above T + ties at T with id <= id_max
-  if (threadIdx.x == 0) s_n = 0;
-  __syncthreads();
-  const uint32_t* gs = p.sure + (int64_t)lr * kMaxTopk;
-  for (uint32_t t = threadIdx.x; t < n_sure && t < (uint32_t)kMaxTopk; t += 256) {
-    const uint32_t slot = atomicAdd(&s_n, 1u);
-    if (slot < (uint32_t)kMaxTopk) s_sel[slot] = gs[t];
-  }
-  for (int64_t t = threadIdx.x; t < ns; t += 256) {
-    uint32_t key, id;
-    if (!src.get(t, key, id)) continue;
-    if (key > T || (key == T && id <= id_max)) {
-      const uint32_t slot = atomicAdd(&s_n, 1u);
-      if (slot < (uint32_t)kMaxTopk) s_sel[slot] = id;
-    }
-  }
-  __syncthreads();
-  // bitonic sort of k ids ascending (padding with UINT_MAX up to a power of two)
-  int npow = 1;
-  while (npow < k) npow <<= 1;
-  for (int t = k + threadIdx.x; t < npow; t += 256) s_sel[t] = 0xffffffffu;
-  __syncthreads();
-  for (int size = 2; size <= npow; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < npow / 2; t += 256) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint32_t a = s_sel[lo], c = s_sel[hi];
-        if ((a > c) == up) { s_sel[lo] = c; s_sel[hi] = a; }
-      }
+    if (fast) {
+      // order-preserving compaction: tiles in order, ids ascending inside a tile
+      uint32_t mine = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q) mine += cnt[q];
+      const uint32_t incl = block_scan(mine, sh);
+      if (tid == kSelThreads - 1) sh.n_pool = incl;
+      uint32_t off = incl - mine;
       __syncthreads();
+      np = sh.n_pool;
+      if (np > (uint32_t)kPoolCap) {
+        fast = false;
+      } else {
+#pragma unroll
+        for (int q = 0; q < kMaxTilesPerThread; ++q) {
+          if (fslot[q] >= 0) {
+            sh.fbase[fslot[q]] = off;
+          } else {
+#pragma unroll
+            for (int j = 0; j < kTileTop; ++j)
+              if (ui[q][j] != 0xffffffffu && uk[q][j] >= tau) {
+                sh.pool_key[off] = uk[q][j];
+                sh.pool_id[off] = ui[q][j];
+                ++off;
+              }
+          }
+          off += fslot[q] >= 0 ? cnt[q] : 0;
+        }
+        __syncthreads();
+        for (uint32_t f = wave; f < nf; f += kNW) {
+          const int64_t base = (int64_t)sh.fail[f] * kTile;
+          uint32_t o = sh.fbase[f];
+          for (int r = 0; r < kTile / 64; ++r) {
+            const int64_t j = base + r * 64 + lane;
+            const uint32_t key = j < nvis ? score_key(sc[j]) : 0u;
+            const bool hit = j < nvis && key >= tau;
+            const uint64_t m = __ballot(hit);
+            if (hit) {
+              const uint32_t at = o + __popcll(m & ((1ull << lane) - 1));
+              sh.pool_key[at] = key;
+              sh.pool_id[at] = (uint32_t)j;
+            }
+            o += __popcll(m);
+          }
+        }
+        __syncthreads();
+      }
     }
   }
-  for (int t = threadIdx.x; t < k; t += 256) {
-    const uint32_t id = s_sel[t];
-    const bool valid = (int64_t)id < nvis;   // always true unless the lists disagree
-    out[t] = valid ? (int32_t)id : -1;
-    if (sel) sel[t] = valid ? sc[id] : 0.f;
+
+  if (fast) {
+    // the pool holds every element >= tau in id order, and at least k of them
+    if (np > (uint32_t)k) {
+      topk_threshold([&](auto&& f) { for (uint32_t t = tid; t < np; t += kSelThreads) f(sh.pool_key[t], sh.pool_id[t]); },
+                     (uint32_t)k, sh, T, id_max);
+    } else {
+      T = 0;
+      id_max = 0xffffffffu;
+    }
+    // order-preserving compaction of the picked pool entries (contiguous ranges per thread)
+    const uint32_t per = (np + kSelThreads - 1) / kSelThreads;
+    const uint32_t lo = min(np, tid * per), hi = min(np, lo + per);
+    uint32_t c = 0;
+    for (uint32_t t = lo; t < hi; ++t) c += picked(sh.pool_key[t], sh.pool_id[t], T, id_max) ? 1u : 0u;
+    uint32_t o = block_scan(c, sh) - c;
+    for (uint32_t t = lo; t < hi; ++t) {
+      const uint32_t id = sh.pool_id[t];
+      if (picked(sh.pool_key[t], id, T, id_max)) {
+        if (o < (uint32_t)k) {
+          out[o] = (int32_t)id;
+          if (selp) selp[o] = sc[id];
+        }
+        ++o;
+      }
+    }
+    return;
+  }
+
+  // slow path: the whole row (ties everywhere, or a pool too large for LDS)
+  auto eachR = [&](auto&& f) {
+    for (int64_t t = tid; t < nvis; t += kSelThreads) f(score_key(sc[t]), (uint32_t)t);
+  };
+  topk_threshold(eachR, (uint32_t)k, sh, T, id_max);
+  const int64_t per = (nvis + kSelThreads - 1) / kSelThreads;
+  const int64_t lo = min<int64_t>(nvis, (int64_t)tid * per), hi = min<int64_t>(nvis, lo + per);
+  uint32_t c = 0;
+  for (int64_t t = lo; t < hi; ++t) c += picked(score_key(sc[t]), (uint32_t)t, T, id_max) ? 1u : 0u;
+  uint32_t o = block_scan(c, sh) - c;
+  for (int64_t t = lo; t < hi; ++t) {
+    const float v = sc[t];
+    if (picked(score_key(v), (uint32_t)t, T, id_max)) {
+      if (o < (uint32_t)k) {
+        out[o] = (int32_t)t;
+        if (selp) selp[o] = v;
+      }
+      ++o;
+    }
   }
 }
 
-hipError_t launch_topk_final(const TopkP& p, int nrows, hipStream_t s) {
-  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)nrows), dim3(256), 0, s, p);
+hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)nrows), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
 

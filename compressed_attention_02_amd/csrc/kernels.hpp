@@ -22,41 +22,36 @@ struct CompressP {
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s);
 
 // ---------------------------------------------------------------- indexer
-constexpr int kHistBits = 12;                 // first radix level: top 12 key bits
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kCandCap = 16384;               // per-row candidate list capacity
+constexpr int kTile = 256;        // blocks per score tile
+constexpr int kTileTop = 8;       // (key, id) pairs each tile reports to the selection
+constexpr int kPoolCap = 4096;    // candidate pool of the per-row selection (LDS)
 constexpr int kMaxTopk = 2048;
+constexpr int kSelThreads = 1024;
 
 struct ScoreP {
   const void* qi; const float* wi; const void* ki;
   const int64_t* pos0;
   float* scores;      // [rows][sc_rs]
-  uint32_t* hist;     // [rows][kHistBins]
-  int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs;
+  uint2* summary;     // [rows][sum_rs]: kTileTop (key, id) per tile, best first
+  int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs, sum_rs;
   int tq, row0;       // launch covers global rows row0 + blockIdx.y; row = b*tq + i
-  int heads, dim, ratio, topk;
-  int tile;           // blocks per workgroup
+  int heads, dim, ratio;
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s);
 
-struct TopkP {
-  const float* scores; const uint32_t* hist;
-  uint32_t* sure;     // [rows][kMaxTopk] ids above the threshold bin
-  uint2* cand;        // [rows][kCandCap] (key, id) in the threshold bin
-  uint32_t* counts;   // [rows][4]: n_sure, n_cand
+struct SelectP {
+  const float* scores; const uint2* summary;
   const int64_t* pos0;
   int32_t* idx; int64_t idx_bs, idx_rs;
   float* sel; int64_t sel_bs, sel_rs;
-  int64_t sc_rs;
+  int64_t sc_rs, sum_rs;
   int tq, row0, ratio, topk;
-  int slice;          // scores per filter workgroup
 };
-hipError_t launch_topk_clear(const TopkP& p, int nrows, hipStream_t s);
-hipError_t launch_topk_filter(const TopkP& p, int nrows, int nslices, hipStream_t s);
-hipError_t launch_topk_final(const TopkP& p, int nrows, hipStream_t s);
+hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
-constexpr int kAttnChunk = 32;  // keys per inner chunk of the attention kernels
+constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels
+constexpr int kAttnMaxSplits = 1024;
 
 struct AttnP {
   const void* q; int64_t q_bs, q_rs;

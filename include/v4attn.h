@@ -241,12 +241,11 @@ uint32_t v4attn_abi_version(void);
 enum {
   V4A_K_COMPRESS = 0,
   V4A_K_INDEX_SCORE = 1,
-  V4A_K_TOPK_FILTER = 2,
-  V4A_K_TOPK_FINAL = 3,
-  V4A_K_ATTN = 4,
-  V4A_K_MERGE = 5,
-  V4A_K_PREFILL = 6,
-  V4A_K_COUNT = 7
+  V4A_K_TOPK_SELECT = 2,
+  V4A_K_ATTN = 3,
+  V4A_K_MERGE = 4,
+  V4A_K_PREFILL = 5,
+  V4A_K_COUNT = 6
 };
 v4a_status v4attn_timing_enable(int kernel, int max_launches);
 int v4attn_timing_read(int kernel, float* ms, int cap);

@@ -1,0 +1,41 @@
+"""Parity at the full configurations, in the launch configuration bench.py uses.
+
+Decode configurations are checked on every sequence; the 4096-query prefill chunk
+on sampled rows (first, last, rows where an HCA entry completes, random rows),
+which the oracle computes one by one.
+"""
+import pytest
+
+from synth import configs as C
+from tests.gpu_harness import Run, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c2_flash_decode_b8_128k", "c3_pro_decode_b1_1m", "c4_hca_decode_b16_1m"])
+def test_full_decode_configs(name):
+    cfg = C.CONFIGS[name]
+    print(f"[case] full {name}", flush=True)
+    r = Run(cfg).run().check_all()
+    # planted needles are selected (structural: they carry +3 sigma of relevance)
+    if cfg.needles:
+        import numpy as np
+        from tests.gpu_harness import dev_to_np
+        idx = dev_to_np(r.step.idx)
+        for b in range(cfg.batch):
+            assert set(r.g["needles"][b].tolist()) <= set(idx[b, 0].tolist())
+
+
+def test_full_c1():
+    print("[case] full c1", flush=True)
+    Run(C.C1).run().check_all()
+
+
+def test_full_prefill_sampled():
+    cfg = C.C5
+    print("[case] full c5 prefill", flush=True)
+    r = Run(cfg).run()
+    r.check_compress()
+    rows = sample_rows(cfg, n_random=10)
+    r.check_topk(rows)
+    r.check_attn(rows)
