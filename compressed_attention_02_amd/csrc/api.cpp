@@ -101,8 +101,8 @@ const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select
 
 // ---------------------------------------------------------------- plans
 struct IndexPlan {
-  int64_t rows, n_cap, sc_rs, ntiles, sum_rs, chunk_rows;
-  size_t off_summary, ws_bytes;
+  int64_t rows, n_cap, sc_rs, ntiles, key_rs, info_rs, chunk_rows;
+  size_t off_keys, off_info, ws_bytes;
 };
 
 IndexPlan plan_index(const v4a_index_args* a) {
@@ -111,12 +111,14 @@ IndexPlan plan_index(const v4a_index_args* a) {
   P.n_cap = (a->pos_max + 1) / a->ratio;
   P.sc_rs = round_up(std::max<int64_t>(P.n_cap, 1), 64);
   P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, kTile));
-  P.sum_rs = round_up(P.ntiles * kTileTop, 32);
+  P.key_rs = round_up(P.ntiles * kTileTop, 64);
+  P.info_rs = round_up(P.ntiles * 4, 32);
   // rows are processed in chunks whose scores fit in 1 GiB
-  const int64_t row_bytes = P.sc_rs * 4 + P.sum_rs * 8;
+  const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 8;
   P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
-  P.off_summary = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
-  P.ws_bytes = P.off_summary + (size_t)round_up(P.chunk_rows * P.sum_rs * 8, 256);
+  P.off_keys = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
+  P.off_info = P.off_keys + (size_t)round_up(P.chunk_rows * P.key_rs * 4, 256);
+  P.ws_bytes = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 8, 256);
   return P;
 }
 
@@ -191,7 +193,7 @@ v4a_status validate_index(const v4a_index_args* a) {
   if (a->dtype == V4A_BF16) {
     if (!(a->heads == 16 || a->heads == 32 || a->heads == 64 || a->heads == 128))
       return fail(V4A_ENOTSUP, "bf16 indexer: heads must be 16, 32, 64 or 128");
-    if (!(a->dim == 32 || a->dim == 64 || a->dim == 128)) return fail(V4A_ENOTSUP, "bf16 indexer: dim must be 32, 64 or 128");
+    if (!(a->dim == 32 || a->dim == 64)) return fail(V4A_ENOTSUP, "bf16 indexer: dim must be 32 or 64");
   } else {
     if (a->dim % 4 != 0) return fail(V4A_ENOTSUP, "fp32 indexer: dim must be a multiple of 4");
     if ((int64_t)a->heads * a->dim + a->heads > 16384) return fail(V4A_ENOTSUP, "fp32 indexer: heads*dim too large");
@@ -286,7 +288,9 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   if (!(a->window > 0)) p.mask &= ~V4A_SWA;
   p.m = a->csa_ratio; p.mh = a->hca_ratio; p.W = a->window; p.topk = a->topk;
   p.scale = a->scale != 0.f ? a->scale : 1.0f / std::sqrt((float)a->dim);
+  p.key_lo = 0; p.key_hi = INT64_MAX;
   p.splits = (int)P.splits; p.keys_per_split = (int)P.kps;
+  p.split_base = 0; p.splits_total = (int)P.splits;
   if (P.splits > 1) {
     p.part_o = (float*)ws;
     p.part_ml = p.part_o + (size_t)P.rows * P.splits * a->heads * a->dim;
@@ -388,17 +392,27 @@ v4a_status v4attn_index_topk(const v4a_index_args* a, void* ws, size_t ws_bytes,
   ScoreP sp{};
   sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
   sp.scores = (float*)base;
-  sp.summary = (uint2*)(base + P.off_summary);
+  sp.rep_key = (uint32_t*)(base + P.off_keys);
+  sp.rep_info = (uint2*)(base + P.off_info);
+  sp.key_rs = P.key_rs;
+  sp.info_rs = P.info_rs;
   sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
   sp.wi_bs = a->wi.batch_stride; sp.wi_rs = a->wi.row_stride;
   sp.ki_bs = a->ki.batch_stride; sp.ki_rs = a->ki.row_stride;
-  sp.sc_rs = P.sc_rs; sp.sum_rs = P.sum_rs;
+  sp.sc_rs = P.sc_rs;
   sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio;
+  {
+    // enough workgroups to fill the chip about twice, each walking several tiles
+    // one tile per workgroup while that fills the chip a few times over; long rows
+    // batches walk several tiles per workgroup
+    const int64_t per_row = cdiv(8 * (int64_t)cu_count(), std::min<int64_t>(P.rows, P.chunk_rows));
+    sp.wgs_per_row = (int)std::max<int64_t>(1, std::min<int64_t>(P.ntiles, per_row));
+  }
   SelectP tp{};
-  tp.scores = sp.scores; tp.summary = sp.summary; tp.pos0 = a->pos0;
+  tp.scores = sp.scores; tp.rep_key = sp.rep_key; tp.rep_info = sp.rep_info; tp.pos0 = a->pos0;
   tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
   tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
-  tp.sc_rs = P.sc_rs; tp.sum_rs = P.sum_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
+  tp.sc_rs = P.sc_rs; tp.key_rs = P.key_rs; tp.info_rs = P.info_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
   for (int64_t r0 = 0; r0 < P.rows; r0 += P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(P.chunk_rows, P.rows - r0);
     sp.row0 = (int)r0;

@@ -103,8 +103,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   const int b = row / p.tq, i = row - b * p.tq;
   const int64_t pos = p.pos0[b] + i;
   const KeyList L = key_list(p, pos);
-  const int64_t k_begin = (int64_t)split * p.keys_per_split;
-  const int64_t k_end = min(L.n_keys, k_begin + (int64_t)p.keys_per_split);
+  const int64_t k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
+  const int64_t k_end = min(min(L.n_keys, p.key_hi), k_begin + (int64_t)p.keys_per_split);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int head = wave * 16 + col;
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  if (p.splits == 1) {
+  if (p.splits_total == 1) {
     float lse;
     const float f = finish_head(m_run, l_run, p.sink, head, &lse);
     float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnP p) {
           make_float4(O[dt][0] * f, O[dt][1] * f, O[dt][2] * f, O[dt][3] * f);
     if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
   } else {
-    const int64_t slot = ((int64_t)row * p.splits + split) * p.heads + head;
+    const int64_t slot = ((int64_t)row * p.splits_total + p.split_base + split) * p.heads + head;
     float* po = p.part_o + slot * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
   const int b = row / p.tq, i = row - b * p.tq;
   const int64_t pos = p.pos0[b] + i;
   const KeyList L = key_list(p, pos);
-  const int64_t k_begin = (int64_t)split * p.keys_per_split;
-  const int64_t k_end = min(L.n_keys, k_begin + (int64_t)p.keys_per_split);
+  const int64_t k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
+  const int64_t k_end = min(min(L.n_keys, p.key_hi), k_begin + (int64_t)p.keys_per_split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float sl2 = p.scale * kLog2e;
 
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
         }
       }
     }
-    if (p.splits == 1) {
+    if (p.splits_total == 1) {
       float lse;
       const float f = finish_head(m_run, l_run, p.sink, head, &lse);
       float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
       for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = acc[e] * f;
       if (lane == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
-      const int64_t slot = ((int64_t)row * p.splits + split) * p.heads + head;
+      const int64_t slot = ((int64_t)row * p.splits_total + p.split_base + split) * p.heads + head;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) p.part_o[slot * D + lane + 64 * e] = acc[e];
       if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_run);
@@ -345,10 +345,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 256-thread workgroup per (row, head).  Split weights go to LDS; the weighted
-// sum over splits is spread over 256/D thread groups and combined in LDS, always in
-// the same order, so the result does not depend on timing.
-constexpr int kMergeThreads = 256;
+// One 1024-thread workgroup per (row, head).  Split weights go to LDS; the weighted
+// sum over splits is spread over 1024/D thread groups, each with four independent
+// accumulators so that its loads are in flight together, and combined in LDS in a
+// fixed order, so the result does not depend on timing.
+constexpr int kMergeThreads = 1024;
 constexpr int kMaxSplits = 1024;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
@@ -356,27 +357,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   __shared__ float s_red[kMergeThreads];
   const int row = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int b = row / p.tq, i = row - b * p.tq;
-  const int S = p.splits, D = p.dim;
+  const int S = p.splits_total, D = p.dim;
   const float* ml = p.part_ml + ((int64_t)row * S * p.heads + head) * 2;
   const int64_t ml_step = (int64_t)p.heads * 2;
-  // 1) global max of the split maxima
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, ml[s * ml_step]);
-  mx = wave_max(mx);
+  float ms = -INFINITY, ls = 0.f;
+  if (tid < S) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + tid * ml_step);
+    ms = v.x;
+    ls = v.y;
+  }
+  // 1) global max of the split maxima (S <= kMergeThreads: one split per thread)
+  float mx = wave_max(ms);
   if ((tid & 63) == 0) s_red[tid >> 6] = mx;
   __syncthreads();
   float M = s_red[0];
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
   __syncthreads();
   // 2) split weights and the total sum
-  float part = 0.f;
-  for (int s = tid; s < S; s += kMergeThreads) {
-    const float ms = ml[s * ml_step];
-    const float w = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    s_w[s] = w;
-    part = fmaf(w, ml[s * ml_step + 1], part);
-  }
-  part = wave_sum(part);
+  const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+  if (tid < S) s_w[tid] = wgt;
+  float part = wave_sum(wgt * ls);
   if ((tid & 63) == 0) s_red[tid >> 6] = part;
   __syncthreads();
   float l = 0.f;
@@ -387,12 +387,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   const int c = tid % D, g = tid / D;
   const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * D + c;
   const int64_t po_step = (int64_t)p.heads * D;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int s = g; s < S; s += G) acc = fmaf(s_w[s], po[s * po_step], acc);
-  s_red[tid] = acc;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = g;
+  for (; s + 3 * G < S; s += 4 * G) {
+    a0 = fmaf(s_w[s], po[s * po_step], a0);
+    a1 = fmaf(s_w[s + G], po[(s + G) * po_step], a1);
+    a2 = fmaf(s_w[s + 2 * G], po[(s + 2 * G) * po_step], a2);
+    a3 = fmaf(s_w[s + 3 * G], po[(s + 3 * G) * po_step], a3);
+  }
+  for (; s < S; s += G) a0 = fmaf(s_w[s], po[s * po_step], a0);
+  s_red[tid] = (a0 + a1) + (a2 + a3);
   __syncthreads();
   if (g == 0) {
+    float acc = s_red[c];
     for (int gg = 1; gg < G; ++gg) acc += s_red[gg * D + c];
     float lse;
     const float f = finish_head(M, l, p.sink, head, &lse);
@@ -422,7 +429,7 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s) {
 }
 
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s) {
-  if (p.splits > kMaxSplits) return hipErrorInvalidValue;
+  if (p.splits_total > kMaxSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }

@@ -51,16 +51,56 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// ---- wave reductions -------------------------------------------------------
+// ---- wave-level scans and reductions on DPP ---------------------------------
+// All cross-lane steps below are DPP moves (quad swaps, row shifts, row mirrors,
+// row_bcast15/31) plus one readlane: no LDS round trips, and a fixed combination
+// order, so every lane of every run sees the same bits.
+template <int CTRL, int ROWMASK = 0xF, int BANKMASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROWMASK, BANKMASK, BOUND_ZERO);
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  uint32_t s = v + dpp_u32<0x111, 0xF, 0xF, true>(0, v);   // row_shr:1
+  s += dpp_u32<0x112, 0xF, 0xF, true>(0, v);                // row_shr:2
+  s += dpp_u32<0x113, 0xF, 0xF, true>(0, v);                // row_shr:3
+  s += dpp_u32<0x114, 0xF, 0xE, true>(0, s);                // row_shr:4 into banks 1-3
+  s += dpp_u32<0x118, 0xF, 0xC, true>(0, s);                // row_shr:8 into banks 2-3
+  s += dpp_u32<0x142, 0xA>(0, s);                           // row_bcast:15 into rows 1, 3
+  s += dpp_u32<0x143, 0xC>(0, s);                           // row_bcast:31 into rows 2, 3
+  return s;
+}
+
+// Reduction with an associative, commutative op whose identity is `id` (rows the
+// row_bcast steps leave out contribute `id`); the result is wave-uniform.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op, uint32_t id) {
+  v = op(v, dpp_u32<0xB1>(id, v));        // quad_perm [1,0,3,2]
+  v = op(v, dpp_u32<0x4E>(id, v));        // quad_perm [2,3,0,1]
+  v = op(v, dpp_u32<0x141>(id, v));       // row_half_mirror
+  v = op(v, dpp_u32<0x140>(id, v));       // row_mirror
+  v = op(v, dpp_u32<0x142, 0xA>(id, v));  // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_u32<0x143, 0xC>(id, v));  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __uint_as_float(wave_reduce_u32(
+      __float_as_uint(v),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); },
+      0xff800000u));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return __uint_as_float(wave_reduce_u32(
+      __float_as_uint(v),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); }, 0u));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; }, 0xffffffffu);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }, 0u);
 }
 
 // exp(x) with -inf -> 0

@@ -8,20 +8,22 @@
 //
 // Two launches per group of query rows, with no global atomics and no state that
 // has to be cleared between calls:
-//   score   one workgroup per (tile of 256 blocks, row): bf16 MFMA 16x16x32 (indexer
-//           heads on M, blocks on N) or fp32 VALU.  Writes the fp32 scores and the
-//           tile's 8 best (key, id) pairs.
-//   select  one 1024-thread workgroup per row.  The k-th largest key among all tile
-//           summaries is a lower bound tau of the row's true k-th key (any subset's
-//           k-th largest is).  A tile whose 8th best key is below tau has no other
-//           element >= tau; tiles that fail this test are rescanned.  The pool of
-//           every element with key >= tau (LDS) therefore holds the top-k, which a
-//           rank search over power-of-two slices of the live key range (then of the
-//           ids, for ties: the lower id wins) extracts exactly.  Tiles report their 8
-//           in id order and the pool is built by order-preserving compaction, so the
-//           k ids come out ascending without a sort.  If the pool would overflow LDS
-//           (or a row has more than 2048 tiles), the same search and compaction run
-//           over the whole row instead.  Rows with n_vis < k are padded with -1.
+//   score   bf16 MFMA 16x16x32 (indexer heads on M, blocks on N) or fp32 VALU over
+//           tiles of 256 blocks.  Writes the fp32 scores; each wave (64 consecutive
+//           blocks) also reports its 4 best (key, id) pairs and the key of its 5th
+//           best, which bounds every key it leaves out.
+//   select  one 512-thread workgroup per row.  The k-th largest of the wave maxima
+//           bounds the row's k-th key from below (the k-th largest of any subset
+//           does), so the reports at or above it (an LDS pool, about k entries)
+//           contain the reports' top-k, whose exact k-th key T a rank search over
+//           power-of-two slices of the live key range finds (then over the ids, for
+//           ties: the lower id wins).  If no wave's bound reaches T, nothing left
+//           unreported can beat T and the pool's top-k is the row's.  Otherwise the
+//           waves that may hide elements >= T are rescanned into the pool first.
+//           Reports come in id order and pools are built by order-preserving
+//           compaction, so the k ids come out ascending without a sort.  Too many
+//           rescans, an LDS overflow or more than 2048 tiles send the row to the same
+//           search over all of its scores.  Rows with n_vis < k are padded with -1.
 // Keys are the order-preserving uint32 image of the fp32 scores, so "larger key" is
 // "larger score"; the result does not depend on launch shape or timing.
 #include "common.hpp"
@@ -42,47 +44,72 @@ __device__ __forceinline__ uint64_t pack_kid(uint32_t key, uint32_t id) {
   return ((uint64_t)key << 32) | (uint64_t)(~id);
 }
 
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp32<CTRL, ROWMASK>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL, ROWMASK>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wave, returned to every lane, with DPP moves only (quad swaps,
+// half-row and row mirrors, then the row_bcast15/31 steps that leave the total in
+// lane 63) and a readlane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = v > w ? v : w;
-  }
-  return v;
+  v = umax64(v, dpp64<0xB1>(v));        // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));        // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));       // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));       // row_mirror
+  v = umax64(v, dpp64<0x142, 0xA>(v));  // row_bcast15 into rows 1 and 3
+  v = umax64(v, dpp64<0x143, 0xC>(v));  // row_bcast31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// The 8 best of a tile's 256 packed values (s_v, one per thread of a 256-thread
-// workgroup) to out[0..7] as (key, id), in ascending id order (missing entries, for
-// tiles with fewer than 8 elements, are (0, 0xffffffff) and come last).
-__device__ void tile_top8(const uint64_t* s_v, uint64_t* s_w, uint2* out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t v = s_v[threadIdx.x];
+// Sum of x over the four 16-lane rows of the wave at the same column, in every lane
+// (gfx950 row swaps; the two partial sums are formed in the same order in all lanes).
+__device__ __forceinline__ float col_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// A wave's report on its 64 packed values (one per lane, 0 = no element; lane L
+// holds block wave_base + L): the keys of its kWaveTop best in ascending id order,
+// their ids as 8-bit offsets from wave_base (0xff = no element) packed in one word,
+// and the key of the next best, an upper bound on every key it leaves out (0 if
+// none).
+__device__ __forceinline__ void wave_top(uint64_t v, uint32_t wave_base, uint32_t* keys, uint2* info) {
+  static_assert(kWaveTop == 4, "four offsets per info word");
+  uint64_t m[kWaveTop + 1];
 #pragma unroll
-  for (int r = 0; r < kTileTop; ++r) {
-    const uint64_t m = wave_max_u64(v);
-    if (v == m) v = 0;
-    if (lane == 0) s_w[wave * kTileTop + r] = m;
+  for (int r = 0; r <= kWaveTop; ++r) {
+    m[r] = wave_max_u64(v);
+    if (v == m[r]) v = 0;
   }
-  __syncthreads();
-  if (wave == 0) {
-    uint64_t u = lane < 4 * kTileTop ? s_w[lane] : 0;
-    uint64_t mine = 0;
+  if ((threadIdx.x & 63) == 0) {
+    uint32_t key[kWaveTop], id[kWaveTop];
 #pragma unroll
-    for (int r = 0; r < kTileTop; ++r) {
-      const uint64_t m = wave_max_u64(u);
-      if (u == m) u = 0;
-      if (lane == r) mine = m;
-    }
-    const uint32_t id = ~(uint32_t)mine;
-    int rank = 0;
+    for (int r = 0; r < kWaveTop; ++r) { key[r] = (uint32_t)(m[r] >> 32); id[r] = ~(uint32_t)m[r]; }
 #pragma unroll
-    for (int q = 0; q < kTileTop; ++q) {
-      const uint32_t oid = (uint32_t)__shfl((int)id, q);
-      rank += (oid < id || (oid == id && q < lane)) ? 1 : 0;
-    }
-    if (lane < kTileTop) out[rank] = make_uint2((uint32_t)(mine >> 32), id);
+    for (int a = 0; a < kWaveTop; ++a)
+#pragma unroll
+      for (int c = 0; c + 1 < kWaveTop - a; ++c)
+        if (id[c + 1] < id[c]) {
+          const uint32_t tk = key[c], ti = id[c];
+          key[c] = key[c + 1]; id[c] = id[c + 1];
+          key[c + 1] = tk; id[c + 1] = ti;
+        }
+    uint32_t offs = 0;
+#pragma unroll
+    for (int r = 0; r < kWaveTop; ++r)
+      offs |= (id[r] == 0xffffffffu ? 0xffu : ((id[r] - wave_base) & 0x3fu)) << (8 * r);
+    *reinterpret_cast<uint4*>(keys) = make_uint4(key[0], key[1], key[2], key[3]);
+    *info = make_uint2(offs, (uint32_t)(m[kWaveTop] >> 32));
   }
 }
 
@@ -92,81 +119,109 @@ __device__ void tile_top8(const uint64_t* s_v, uint64_t* s_w, uint2* out) {
 // head col, 8 dims of group grp; B (32 dims x 16 blocks): lane holds block col, the
 // same 8 dims; C (16 heads x 16 blocks): lane holds block col, heads 4*grp + e.
 // The dims a lane group carries only have to agree between A and B.
+//
+// A workgroup walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of its row.
+// Tile loads are fully coalesced (each wave instruction reads 1 KiB of consecutive
+// block rows) into registers one tile ahead, then land in a padded LDS tile from
+// which the MFMA operands are read; the indexer queries are staged in LDS once.
 template <int MT, int KS>
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
-  __shared__ uint64_t s_v[kTile];
-  __shared__ uint64_t s_w[4 * kTileTop];
+  constexpr int DI = KS * 32;
+  constexpr int ROWB = DI * 2 + 16;          // LDS bytes per block row (+16: conflict-free reads)
+  constexpr int CPR = DI * 2 / 16;           // 16-byte chunks per block row
+  constexpr int LPT = kTile * CPR / 256;     // 16-byte loads per thread per tile
+  __shared__ __align__(16) unsigned char sK[kTile * ROWB];
+  __shared__ __align__(16) uint16_t sA[MT * 16 * DI];
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = (pos + 1) / p.ratio;
-  const int64_t tile0 = (int64_t)blockIdx.x * kTile;
-  if (tile0 >= nvis) return;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ntile_row = (nvis + kTile - 1) / kTile;
+  int64_t tile = blockIdx.x;
+  if (tile >= ntile_row) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  constexpr int DI = KS * 32;
   const uint16_t* ki = reinterpret_cast<const uint16_t*>(p.ki) + (int64_t)b * p.ki_bs;
-  // blocks of this wave: tile0 + wave*16 + u*64 + col, u = 0..3
-  constexpr int U = kTile / 64;
-  bf16x8_t Bv[U][KS];
+
+  uint4 pre[LPT];
+  auto fetch = [&](int64_t t) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t j = tile0 + wave * 16 + u * 64 + col;
+    for (int u = 0; u < LPT; ++u) {
+      const int e = tid + u * 256;
+      const int r = e / CPR, c = e - r * CPR;
+      const int64_t j = t * kTile + r;
+      pre[u] = make_uint4(0, 0, 0, 0);
+      if (j < nvis) pre[u] = *reinterpret_cast<const uint4*>(ki + j * p.ki_rs + c * 8);
+    }
+  };
+  fetch(tile);
+  {
+    const uint4* qi = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.qi) +
+                                                     (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs);
+    for (int e = tid; e < MT * 16 * DI / 8; e += 256) reinterpret_cast<uint4*>(sA)[e] = qi[e];
+  }
+  float w[MT][4];
+  {
+    const float4* wi = reinterpret_cast<const float4*>(p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < nvis) v = *reinterpret_cast<const uint4*>(ki + j * p.ki_rs + s * 32 + grp * 8);
-      Bv[u][s] = __builtin_bit_cast(bf16x8_t, v);
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4 v = wi[mt * 4 + grp];
+      w[mt][0] = v.x; w[mt][1] = v.y; w[mt][2] = v.z; w[mt][3] = v.w;
     }
   }
-  const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
+  __syncthreads();
   bf16x8_t A[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      A[mt][s] = __builtin_bit_cast(bf16x8_t,
-                   *reinterpret_cast<const uint4*>(qi + (mt * 16 + col) * DI + s * 32 + grp * 8));
-  float w[MT][4];
-  const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[mt][e] = wi[mt * 16 + grp * 4 + e];
+      A[mt][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&sA[(mt * 16 + col) * DI + s * 32 + grp * 8]));
 
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
+  for (; tile < ntile_row; tile += gridDim.x) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float part = 0.f;
+    for (int u = 0; u < LPT; ++u) {
+      const int e = tid + u * 256;
+      const int r = e / CPR, c = e - r * CPR;
+      *reinterpret_cast<uint4*>(sK + r * ROWB + c * 16) = pre[u];
+    }
+    __syncthreads();
+    if (tile + gridDim.x < ntile_row) fetch(tile + gridDim.x);
+    const int64_t tile0 = tile * kTile;
+    float mine = 0.f;       // score of block tile0 + 64*wave + lane after the loop
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 64 + u * 16 + col;     // block of this lane's column
+      float part = 0.f;
+      bf16x8_t Bv[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[u][s], acc, 0, 0, 0);
+        Bv[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sK + t * ROWB + (s * 4 + grp) * 16));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(acc[e], 0.f), part);
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(acc[e], 0.f), part);
+      }
+      part = col_sum4(part);
+      if (grp == u) mine = part;
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    const int t = wave * 16 + u * 64 + col;
-    const int64_t j = tile0 + t;
-    if (grp == 0) {
-      if (j < nvis) sc[j] = part;
-      s_v[t] = j < nvis ? pack_kid(score_key(part), (uint32_t)j) : 0ull;
-    }
+    const int64_t j = tile0 + wave * 64 + lane;
+    if (j < nvis) sc[j] = mine;
+    wave_top(j < nvis ? pack_kid(score_key(mine), (uint32_t)j) : 0ull, (uint32_t)(tile0 + wave * 64),
+             p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
+             p.rep_info + (int64_t)lr * p.info_rs + tile * 4 + wave);
+    __syncthreads();       // sK is rewritten by the next tile
   }
-  __syncthreads();
-  tile_top8(s_v, s_w, p.summary + (int64_t)lr * p.sum_rs + (int64_t)blockIdx.x * kTileTop);
 }
 
 // ------------------------------------------------------------------ score, fp32 VALU
 // One thread per block of the tile; the row's indexer queries and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
-  __shared__ uint64_t s_v[kTile];
-  __shared__ uint64_t s_w[4 * kTileTop];
   extern __shared__ float s_q[];  // [heads*dim] then [heads]
   const int lr = blockIdx.y;
   int b, i;
@@ -203,9 +258,9 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
     sc[j] = s;
     v = pack_kid(score_key(s), (uint32_t)j);
   }
-  s_v[threadIdx.x] = v;
-  __syncthreads();
-  tile_top8(s_v, s_w, p.summary + (int64_t)lr * p.sum_rs + (int64_t)blockIdx.x * kTileTop);
+  wave_top(v, (uint32_t)(tile0 + (threadIdx.x & ~63)),
+           p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop + (threadIdx.x >> 6) * kWaveTop,
+           p.rep_info + (int64_t)lr * p.info_rs + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s) {
@@ -216,12 +271,13 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
     return hipGetLastError();
   }
   const int mt = p.heads / 16, ks = p.dim / 32;
+  const dim3 pgrid((unsigned)p.wgs_per_row, (unsigned)nrows);
 #define V4A_SCORE_CASE(M, K) \
-  if (mt == M && ks == K) { hipLaunchKernelGGL((score_bf16_kernel<M, K>), grid, dim3(256), 0, s, p); return hipGetLastError(); }
-  V4A_SCORE_CASE(1, 1) V4A_SCORE_CASE(1, 2) V4A_SCORE_CASE(1, 4)
-  V4A_SCORE_CASE(2, 1) V4A_SCORE_CASE(2, 2) V4A_SCORE_CASE(2, 4)
-  V4A_SCORE_CASE(4, 1) V4A_SCORE_CASE(4, 2) V4A_SCORE_CASE(4, 4)
-  V4A_SCORE_CASE(8, 1) V4A_SCORE_CASE(8, 2) V4A_SCORE_CASE(8, 4)
+  if (mt == M && ks == K) { hipLaunchKernelGGL((score_bf16_kernel<M, K>), pgrid, dim3(256), 0, s, p); return hipGetLastError(); }
+  V4A_SCORE_CASE(1, 1) V4A_SCORE_CASE(1, 2)
+  V4A_SCORE_CASE(2, 1) V4A_SCORE_CASE(2, 2)
+  V4A_SCORE_CASE(4, 1) V4A_SCORE_CASE(4, 2)
+  V4A_SCORE_CASE(8, 1) V4A_SCORE_CASE(8, 2)
 #undef V4A_SCORE_CASE
   return hipErrorInvalidValue;
 }
@@ -244,15 +300,15 @@ struct SelShared {
 // inclusive prefix sum over the workgroup (one value per thread)
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = (uint32_t)__shfl_up((int)v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_scan_u32(v);
   if (lane == 63) sh.wtot[wave] = v;
   __syncthreads();
+  uint32_t tot[kNW];
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) tot[w] = sh.wtot[w];
   uint32_t add = 0;
-  for (int w = 0; w < wave; ++w) add += sh.wtot[w];
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) add += w < wave ? tot[w] : 0u;
   __syncthreads();
   return v + add;
 }
@@ -260,11 +316,8 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, SelShared& sh) {
 // min and max over the workgroup
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared& sh, uint32_t& omn, uint32_t& omx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   if (lane == 0) { sh.wmin[wave] = mn; sh.wmax[wave] = mx; }
   __syncthreads();
   omn = sh.wmin[0];
@@ -275,27 +328,33 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared
 
 // Bin of sh.hist[0..nb) holding the r-th element (1-based) counted from the top
 // (descending) or from the bottom, and the count strictly before it.
-__device__ void find_rank(SelShared& sh, int nb, uint32_t r, bool descending, uint32_t& bin,
+__device__ __forceinline__ void find_rank(SelShared& sh, int nb, uint32_t r, bool descending, uint32_t& bin,
                           uint32_t& before) {
+  constexpr int kMaxPer = kBins / kSelThreads;
   const int t = threadIdx.x;
   const int per = (nb + kSelThreads - 1) / kSelThreads;
+  uint32_t c[kMaxPer];
   uint32_t sum = 0;
-  for (int e = 0; e < per; ++e) {
+#pragma unroll
+  for (int e = 0; e < kMaxPer; ++e) {
     const int o = t * per + e;
-    if (o < nb) sum += sh.hist[descending ? nb - 1 - o : o];
+    c[e] = (e < per && o < nb) ? sh.hist[descending ? nb - 1 - o : o] : 0u;
+    sum += c[e];
   }
   const uint32_t incl = block_scan(sum, sh);
   const uint32_t excl = incl - sum;
   if (excl < r && r <= incl) {
     uint32_t run = excl;
-    for (int e = 0; e < per; ++e) {
-      const int o = t * per + e;
-      if (o >= nb) break;
-      const int bb = descending ? nb - 1 - o : o;
-      const uint32_t c = sh.hist[bb];
-      if (run + c >= r) { sh.hit_bin = (uint32_t)bb; sh.hit_before = run; break; }
-      run += c;
+    int hit = 0;
+    bool found = false;
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e) {
+      if (!found && run + c[e] >= r) { hit = e; found = true; }
+      if (!found) run += c[e];
     }
+    const int o = t * per + hit;
+    sh.hit_bin = (uint32_t)(descending ? nb - 1 - o : o);
+    sh.hit_before = run;
   }
   __syncthreads();
   bin = sh.hit_bin;
@@ -304,13 +363,15 @@ __device__ void find_rank(SelShared& sh, int nb, uint32_t r, bool descending, ui
 }
 
 // Rank search over the values `val(key, id)` of the elements that `each` visits and
-// `keep(key, id)` accepts: returns the value v* holding the r-th element counted
-// from the top (descending) or the bottom, and through r the rank of the wanted
-// element among those equal to v*.  Bins are power-of-two slices of the live
+// `keep(key, id)` accepts: returns a value v* such that the elements at or above it
+// (descending; at or below it, ascending) are the r first ones plus, when r ends
+// inside a run of equal values, part of that run; through r it returns how many of
+// the elements equal to v* are wanted and through n_equal how many there are (both
+// equal when the search stops early at a bin that is taken whole).  Bins are power-of-two slices of the live
 // [lo, hi] range, so keys that sit close together spread over many bins and the
 // LDS atomics stay free of contention; at most 3 levels narrow 32 bits to one value.
 template <class Each, class Keep, class Val>
-__device__ uint32_t rank_search(Each each, Keep keep, Val val, uint32_t& r, bool descending, SelShared& sh,
+__device__ __forceinline__ uint32_t rank_search(Each each, Keep keep, Val val, uint32_t& r, bool descending, SelShared& sh,
                                 uint32_t& n_equal) {
   uint32_t mn = 0xffffffffu, mx = 0;
   each([&](uint32_t key, uint32_t id) {
@@ -339,20 +400,64 @@ __device__ uint32_t rank_search(Each each, Keep keep, Val val, uint32_t& r, bool
     r -= before;
     const uint32_t nlo = lo + (bin << shift);
     const uint32_t nhi = (uint32_t)min<uint64_t>((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
+    const uint32_t in_bin = sh.hist[bin];
+    __syncthreads();
     if (shift == 0) {
-      n_equal = sh.hist[bin];
-      __syncthreads();
+      n_equal = in_bin;
       return nlo;
+    }
+    if (r == in_bin) {
+      // the wanted rank closes the bin: every element of the bin is taken, so the
+      // bin edge on the far side is an exact threshold
+      n_equal = in_bin;
+      return descending ? nlo : nhi;
     }
     lo = nlo;
     hi = nhi;
   }
 }
 
+// A lower bound of the r-th largest key over the visited elements from one level
+// of power-of-two bins over the live key range: the lower edge of the bin that
+// holds the r-th element.
+template <class Each>
+__device__ __forceinline__ uint32_t kth_key_floor(Each each, uint32_t r, SelShared& sh) {
+  uint32_t mn = 0xffffffffu, mx = 0;
+  each([&](uint32_t key, uint32_t) { mn = min(mn, key); mx = max(mx, key); });
+  uint32_t lo, hi;
+  block_minmax(mn, mx, sh, lo, hi);
+  if (lo > hi) return 0;
+  const uint64_t range = (uint64_t)hi - lo + 1;
+  int shift = 0;
+  while ((range >> shift) > (uint64_t)kBins) ++shift;
+  const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+  for (int t = threadIdx.x; t < nb; t += kSelThreads) sh.hist[t] = 0;
+  __syncthreads();
+  each([&](uint32_t key, uint32_t) { atomicAdd(&sh.hist[(key - lo) >> shift], 1u); });
+  __syncthreads();
+  uint32_t bin, before;
+  find_rank(sh, nb, r, true, bin, before);
+  return lo + (bin << shift);
+}
+
+// 64-bit minimum over the wave (DPP), wave-uniform
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  auto umin64 = [](uint64_t a, uint64_t b) { return a < b ? a : b; };
+  v = umin64(v, dpp64<0xB1>(v));
+  v = umin64(v, dpp64<0x4E>(v));
+  v = umin64(v, dpp64<0x141>(v));
+  v = umin64(v, dpp64<0x140>(v));
+  v = umin64(v, dpp64<0x142, 0xA>(v));
+  v = umin64(v, dpp64<0x143, 0xC>(v));
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // The key threshold T and the largest tie id of the exact top-k over the visited
 // elements: an element is selected iff key > T, or key == T and id <= id_max.
 template <class Each>
-__device__ void topk_threshold(Each each, uint32_t k, SelShared& sh, uint32_t& T, uint32_t& id_max) {
+__device__ __forceinline__ void topk_threshold(Each each, uint32_t k, SelShared& sh, uint32_t& T, uint32_t& id_max) {
   uint32_t r = k, n_tie;
   T = rank_search(each, [](uint32_t, uint32_t) { return true; },
                   [](uint32_t key, uint32_t) { return key; }, r, true, sh, n_tie);
@@ -368,7 +473,28 @@ __device__ __forceinline__ bool picked(uint32_t key, uint32_t id, uint32_t T, ui
   return key > T || (key == T && id <= id_max);
 }
 
-constexpr int kMaxTilesPerThread = 2;
+constexpr int kMaxTilesPerThread = 3;
+
+// Emits out[0..k) from the LDS pool (ascending ids) by an order-preserving
+// compaction of the picked entries; every thread owns a contiguous pool range.
+__device__ __forceinline__ void emit_pool(SelShared& sh, uint32_t np, uint32_t k, uint32_t T, uint32_t id_max,
+                                          int32_t* out, float* selp, const float* sc) {
+  const uint32_t per = (np + kSelThreads - 1) / kSelThreads;
+  const uint32_t lo = min(np, threadIdx.x * per), hi = min(np, lo + per);
+  uint32_t c = 0;
+  for (uint32_t t = lo; t < hi; ++t) c += picked(sh.pool_key[t], sh.pool_id[t], T, id_max) ? 1u : 0u;
+  uint32_t o = block_scan(c, sh) - c;
+  for (uint32_t t = lo; t < hi; ++t) {
+    const uint32_t id = sh.pool_id[t];
+    if (picked(sh.pool_key[t], id, T, id_max)) {
+      if (o < k) {
+        out[o] = (int32_t)id;
+        if (selp) selp[o] = sc[id];
+      }
+      ++o;
+    }
+  }
+}
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectP p) {
   __shared__ SelShared sh;
@@ -389,170 +515,220 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectP p) {
     }
     return;
   }
-  const uint2* U = p.summary + (int64_t)lr * p.sum_rs;
+  const uint32_t* RK = p.rep_key + (int64_t)lr * p.key_rs;
+  const uint2* RI = p.rep_info + (int64_t)lr * p.info_rs;
   const int64_t ntiles = (nvis + kTile - 1) / kTile;
-  const int tpt = ntiles <= kSelThreads ? 1 : kMaxTilesPerThread;   // tiles per thread
-  bool fast = ntiles <= (int64_t)kSelThreads * kMaxTilesPerThread;
+  const int tpt = (int)min<int64_t>(kMaxTilesPerThread + 1, (ntiles + kSelThreads - 1) / kSelThreads);
+  bool ok = tpt <= kMaxTilesPerThread;
 
-  // thread t owns tiles [t*tpt, t*tpt + tpt): their summaries (id order) in registers
-  uint32_t uk[kMaxTilesPerThread][kTileTop], ui[kMaxTilesPerThread][kTileTop];
+  // thread t owns tiles [t*tpt, t*tpt + tpt): report keys, packed id offsets (the id of
+  // entry j of tile t is t*256 + (j/4)*64 + offset) and the largest wave bound
+  uint32_t uk[kMaxTilesPerThread][kTileTop], uo[kMaxTilesPerThread][kTileTop / 4], ub[kMaxTilesPerThread];
+  bool own[kMaxTilesPerThread];
+  int64_t tbase[kMaxTilesPerThread];
+  {
+    // every load in flight before any of them is used: loads come from a valid tile
+    // (tpt is uniform, the tile clamp keeps them unconditional per lane); ownership is
+    // applied when unpacking
+    uint4 rk[kMaxTilesPerThread][kTileTop / 4], ri[kMaxTilesPerThread][2];
 #pragma unroll
-  for (int q = 0; q < kMaxTilesPerThread; ++q) {
-    const int64_t t = (int64_t)tid * tpt + q;
-    const bool own = fast && q < tpt && t < ntiles;
-    const uint4* src = reinterpret_cast<const uint4*>(U + t * kTileTop);
+    for (int q = 0; q < kMaxTilesPerThread; ++q) {
+      const int64_t t = (int64_t)tid * tpt + q;
+      own[q] = ok && q < tpt && t < ntiles;
+      tbase[q] = t * kTile;
+      if (ok && q < tpt) {
+        const int64_t tl = min<int64_t>(t, ntiles - 1);
+        const uint4* ks = reinterpret_cast<const uint4*>(RK + tl * kTileTop);
+        const uint4* is = reinterpret_cast<const uint4*>(RI + tl * 4);
 #pragma unroll
-    for (int j = 0; j < kTileTop / 2; ++j) {
-      uint4 e = make_uint4(0u, 0xffffffffu, 0u, 0xffffffffu);
-      if (own) e = src[j];
-      uk[q][2 * j] = e.x; ui[q][2 * j] = e.y; uk[q][2 * j + 1] = e.z; ui[q][2 * j + 1] = e.w;
+        for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = ks[j];
+        ri[q][0] = is[0];
+        ri[q][1] = is[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = make_uint4(0u, 0u, 0u, 0u);
+        ri[q][0] = ri[q][1] = make_uint4(0xffffffffu, 0u, 0xffffffffu, 0u);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxTilesPerThread; ++q) {
+#pragma unroll
+      for (int w = 0; w < kTileTop / 4; ++w) {
+        uk[q][4 * w] = rk[q][w].x; uk[q][4 * w + 1] = rk[q][w].y;
+        uk[q][4 * w + 2] = rk[q][w].z; uk[q][4 * w + 3] = rk[q][w].w;
+      }
+      uo[q][0] = own[q] ? ri[q][0].x : 0xffffffffu;
+      uo[q][1] = own[q] ? ri[q][0].z : 0xffffffffu;
+      uo[q][2] = own[q] ? ri[q][1].x : 0xffffffffu;
+      uo[q][3] = own[q] ? ri[q][1].z : 0xffffffffu;
+      ub[q] = own[q] ? max(max(ri[q][0].y, ri[q][0].w), max(ri[q][1].y, ri[q][1].w)) : 0u;
     }
   }
-  uint32_t T = 0, id_max = 0xffffffffu;
-  uint32_t np = 0;
-  if (fast) {
-    // tau: the k-th largest summary key, a lower bound of the row's k-th key (0 when the
-    // summaries hold fewer than k elements)
-    uint32_t tau = 0;
-    if (ntiles * kTileTop >= k) {
-      uint32_t r = (uint32_t)k, n_eq;
-      tau = rank_search(
+  auto eachOwn = [&](auto&& f) {
+#pragma unroll
+    for (int q = 0; q < kMaxTilesPerThread; ++q)
+#pragma unroll
+      for (int j = 0; j < kTileTop; ++j) {
+        const uint32_t off = (uo[q][j / 4] >> (8 * (j % 4))) & 0xffu;
+        if (own[q] && off != 0xffu) f(uk[q][j], (uint32_t)tbase[q] + 64u * (j / 4) + off);
+      }
+  };
+  // order-preserving copy of the reported elements that pass `keep` into the pool
+  auto pool_reports = [&](auto&& keep) -> uint32_t {
+    uint32_t c = 0;
+    eachOwn([&](uint32_t key, uint32_t id) { c += keep(key) ? 1u : 0u; });
+    const uint32_t incl = block_scan(c, sh);
+    if (tid == kSelThreads - 1) sh.n_pool = incl;
+    uint32_t o = incl - c;
+    eachOwn([&](uint32_t key, uint32_t id) {
+      if (keep(key)) {
+        if (o < (uint32_t)kPoolCap) { sh.pool_key[o] = key; sh.pool_id[o] = id; }
+        ++o;
+      }
+    });
+    __syncthreads();
+    return sh.n_pool;
+  };
+
+  if (ok) {
+    // 1. a lower bound from the wave maxima (the k-th largest of any subset bounds the
+    //    row's k-th key from below)
+    uint32_t tau1 = 0;
+    if (ntiles * 4 >= k) {
+      tau1 = kth_key_floor(
           [&](auto&& f) {
 #pragma unroll
             for (int q = 0; q < kMaxTilesPerThread; ++q)
 #pragma unroll
-              for (int j = 0; j < kTileTop; ++j)
-                if ((int64_t)tid * tpt + q < ntiles && q < tpt) f(uk[q][j], ui[q][j]);
-          },
-          [](uint32_t, uint32_t) { return true; }, [](uint32_t key, uint32_t) { return key; }, r, true, sh,
-          n_eq);
-    }
-    // per owned tile: count of elements >= tau, or a rescan slot when the tile may hold
-    // more of them than its summary shows
-    if (tid == 0) { sh.n_fail = 0; sh.flag = 0; }
-    __syncthreads();
-    int fslot[kMaxTilesPerThread];
-    uint32_t cnt[kMaxTilesPerThread];
+              for (int w = 0; w < 4; ++w) {
+                uint32_t m = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxTilesPerThread; ++q) {
-      fslot[q] = -1;
-      cnt[q] = 0;
-      const int64_t t = (int64_t)tid * tpt + q;
-      if (q >= tpt || t >= ntiles) continue;
-      const int64_t valid = min<int64_t>(kTile, nvis - t * kTile);
-      uint32_t kmin = 0xffffffffu;
-#pragma unroll
-      for (int j = 0; j < kTileTop; ++j) {
-        if (ui[q][j] != 0xffffffffu) {
-          cnt[q] += uk[q][j] >= tau ? 1u : 0u;
-          kmin = min(kmin, uk[q][j]);
-        }
-      }
-      if (valid > kTileTop && kmin >= tau) {
-        const uint32_t slot = atomicAdd(&sh.n_fail, 1u);
-        if (slot < 256u) { fslot[q] = (int)slot; sh.fail[slot] = (uint32_t)t; }
-        else sh.flag = 1;
-      }
-    }
-    __syncthreads();
-    const uint32_t nf = sh.n_fail;
-    if (sh.flag) fast = false;
-    if (fast && nf) {
-      // a wave counts the elements >= tau of each failing tile
-      for (uint32_t f = wave; f < nf; f += kNW) {
-        const int64_t base = (int64_t)sh.fail[f] * kTile;
-        uint32_t c = 0;
-        for (int r = 0; r < kTile / 64; ++r) {
-          const int64_t j = base + r * 64 + lane;
-          const bool hit = j < nvis && score_key(sc[j]) >= tau;
-          c += __popcll(__ballot(hit));
-        }
-        if (lane == 0) sh.fcount[f] = c;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kMaxTilesPerThread; ++q)
-        if (fslot[q] >= 0) cnt[q] = sh.fcount[fslot[q]];
-    }
-    if (fast) {
-      // order-preserving compaction: tiles in order, ids ascending inside a tile
-      uint32_t mine = 0;
-#pragma unroll
-      for (int q = 0; q < kMaxTilesPerThread; ++q) mine += cnt[q];
-      const uint32_t incl = block_scan(mine, sh);
-      if (tid == kSelThreads - 1) sh.n_pool = incl;
-      uint32_t off = incl - mine;
-      __syncthreads();
-      np = sh.n_pool;
-      if (np > (uint32_t)kPoolCap) {
-        fast = false;
-      } else {
-#pragma unroll
-        for (int q = 0; q < kMaxTilesPerThread; ++q) {
-          if (fslot[q] >= 0) {
-            sh.fbase[fslot[q]] = off;
-          } else {
-#pragma unroll
-            for (int j = 0; j < kTileTop; ++j)
-              if (ui[q][j] != 0xffffffffu && uk[q][j] >= tau) {
-                sh.pool_key[off] = uk[q][j];
-                sh.pool_id[off] = ui[q][j];
-                ++off;
+                for (int e = 0; e < kWaveTop; ++e) m = max(m, uk[q][w * kWaveTop + e]);
+                if (own[q]) f(m, 0u);
               }
-          }
-          off += fslot[q] >= 0 ? cnt[q] : 0;
+          },
+          (uint32_t)k, sh);
+    }
+    // 2. the reported elements >= tau1, in id order
+    const uint32_t np = pool_reports([tau1](uint32_t key) { return key >= tau1; });
+    if (np <= (uint32_t)kPoolCap && np >= (uint32_t)k) {
+      // 3. the exact k-th key T of the reports
+      uint32_t r = (uint32_t)k, n_tie;
+      auto eachP = [&](auto&& f) { for (uint32_t t = tid; t < np; t += kSelThreads) f(sh.pool_key[t], sh.pool_id[t]); };
+      const uint32_t T = rank_search(eachP, [](uint32_t, uint32_t) { return true; },
+                                     [](uint32_t key, uint32_t) { return key; }, r, true, sh, n_tie);
+      // 4. no tile hides a key >= T: the reports hold every element >= T and their top-k
+      //    is the row's
+      bool hides = false;
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q) hides |= own[q] && ub[q] >= T;
+      if (!__syncthreads_or(hides)) {
+        uint32_t id_max = 0xffffffffu;
+        if (r < n_tie)
+          id_max = rank_search(eachP, [T](uint32_t key, uint32_t) { return key == T; },
+                               [](uint32_t, uint32_t id) { return id; }, r, false, sh, n_tie);
+        emit_pool(sh, np, (uint32_t)k, T, id_max, out, selp, sc);
+        return;
+      }
+      // 5. some tiles may hide elements >= T: pool = reports >= T of the other tiles
+      //    plus every element >= T of those tiles (rescanned), in id order
+      if (tid == 0) sh.n_fail = 0;
+      __syncthreads();
+      int fslot[kMaxTilesPerThread];
+      uint32_t cnt[kMaxTilesPerThread];
+      bool over = false;
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q) {
+        fslot[q] = -1;
+        cnt[q] = 0;
+        if (!own[q]) continue;
+#pragma unroll
+        for (int j = 0; j < kTileTop; ++j)
+          if (((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu) != 0xffu) cnt[q] += uk[q][j] >= T ? 1u : 0u;
+        if (ub[q] >= T) {
+          const uint32_t slot = atomicAdd(&sh.n_fail, 1u);
+          if (slot < 256u) { fslot[q] = (int)slot; sh.fail[slot] = (uint32_t)((int64_t)tid * tpt + q); }
+          else over = true;
         }
-        __syncthreads();
+      }
+      over = __syncthreads_or(over);
+      const uint32_t nf = min(sh.n_fail, 256u);
+      if (!over) {
+        // a wave counts the elements >= T of its failing tiles, all loads in flight
         for (uint32_t f = wave; f < nf; f += kNW) {
           const int64_t base = (int64_t)sh.fail[f] * kTile;
-          uint32_t o = sh.fbase[f];
-          for (int r = 0; r < kTile / 64; ++r) {
-            const int64_t j = base + r * 64 + lane;
-            const uint32_t key = j < nvis ? score_key(sc[j]) : 0u;
-            const bool hit = j < nvis && key >= tau;
-            const uint64_t m = __ballot(hit);
-            if (hit) {
-              const uint32_t at = o + __popcll(m & ((1ull << lane) - 1));
-              sh.pool_key[at] = key;
-              sh.pool_id[at] = (uint32_t)j;
-            }
-            o += __popcll(m);
+          uint32_t kk[kTile / 64];
+#pragma unroll
+          for (int rr = 0; rr < kTile / 64; ++rr) {
+            const int64_t j = base + rr * 64 + lane;
+            kk[rr] = j < nvis ? score_key(sc[j]) : 0u;
           }
+          uint32_t c = 0;
+#pragma unroll
+          for (int rr = 0; rr < kTile / 64; ++rr) c += __popcll(__ballot(base + rr * 64 + lane < nvis && kk[rr] >= T));
+          if (lane == 0) sh.fcount[f] = c;
         }
         __syncthreads();
-      }
-    }
-  }
-
-  if (fast) {
-    // the pool holds every element >= tau in id order, and at least k of them
-    if (np > (uint32_t)k) {
-      topk_threshold([&](auto&& f) { for (uint32_t t = tid; t < np; t += kSelThreads) f(sh.pool_key[t], sh.pool_id[t]); },
-                     (uint32_t)k, sh, T, id_max);
-    } else {
-      T = 0;
-      id_max = 0xffffffffu;
-    }
-    // order-preserving compaction of the picked pool entries (contiguous ranges per thread)
-    const uint32_t per = (np + kSelThreads - 1) / kSelThreads;
-    const uint32_t lo = min(np, tid * per), hi = min(np, lo + per);
-    uint32_t c = 0;
-    for (uint32_t t = lo; t < hi; ++t) c += picked(sh.pool_key[t], sh.pool_id[t], T, id_max) ? 1u : 0u;
-    uint32_t o = block_scan(c, sh) - c;
-    for (uint32_t t = lo; t < hi; ++t) {
-      const uint32_t id = sh.pool_id[t];
-      if (picked(sh.pool_key[t], id, T, id_max)) {
-        if (o < (uint32_t)k) {
-          out[o] = (int32_t)id;
-          if (selp) selp[o] = sc[id];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int q = 0; q < kMaxTilesPerThread; ++q) {
+          if (fslot[q] >= 0) cnt[q] = sh.fcount[fslot[q]];
+          mine += cnt[q];
         }
-        ++o;
+        const uint32_t incl = block_scan(mine, sh);
+        if (tid == kSelThreads - 1) sh.n_pool = incl;
+        __syncthreads();
+        const uint32_t np2 = sh.n_pool;
+        if (np2 <= (uint32_t)kPoolCap) {
+          uint32_t off = incl - mine;
+#pragma unroll
+          for (int q = 0; q < kMaxTilesPerThread; ++q) {
+            if (fslot[q] >= 0) {
+              sh.fbase[fslot[q]] = off;
+              off += cnt[q];
+            } else if (own[q]) {
+#pragma unroll
+              for (int j = 0; j < kTileTop; ++j) {
+                const uint32_t wo = (uo[q][j / 4] >> (8 * (j % 4))) & 0xffu;
+                if (wo != 0xffu && uk[q][j] >= T) {
+                  sh.pool_key[off] = uk[q][j];
+                  sh.pool_id[off] = (uint32_t)tbase[q] + 64u * (j / 4) + wo;
+                  ++off;
+                }
+              }
+            }
+          }
+          __syncthreads();
+          for (uint32_t f = wave; f < nf; f += kNW) {
+            const int64_t base = (int64_t)sh.fail[f] * kTile;
+            uint32_t o = sh.fbase[f];
+#pragma unroll
+            for (int rr = 0; rr < kTile / 64; ++rr) {
+              const int64_t j = base + rr * 64 + lane;
+              const uint32_t key = j < nvis ? score_key(sc[j]) : 0u;
+              const bool hit = j < nvis && key >= T;
+              const uint64_t m = __ballot(hit);
+              if (hit) {
+                const uint32_t at = o + __popcll(m & ((1ull << lane) - 1));
+                sh.pool_key[at] = key;
+                sh.pool_id[at] = (uint32_t)j;
+              }
+              o += __popcll(m);
+            }
+          }
+          __syncthreads();
+          uint32_t T2, id2;
+          auto eachP2 = [&](auto&& f) { for (uint32_t t = tid; t < np2; t += kSelThreads) f(sh.pool_key[t], sh.pool_id[t]); };
+          topk_threshold(eachP2, (uint32_t)k, sh, T2, id2);
+          emit_pool(sh, np2, (uint32_t)k, T2, id2, out, selp, sc);
+          return;
+        }
       }
     }
-    return;
   }
 
-  // slow path: the whole row (ties everywhere, or a pool too large for LDS)
+  // whole-row path (ties everywhere, too many rescans, or more tiles than registers hold)
+  uint32_t T, id_max;
   auto eachR = [&](auto&& f) {
     for (int64_t t = tid; t < nvis; t += kSelThreads) f(score_key(sc[t]), (uint32_t)t);
   };

@@ -23,28 +23,31 @@ hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t
 
 // ---------------------------------------------------------------- indexer
 constexpr int kTile = 256;        // blocks per score tile
-constexpr int kTileTop = 8;       // (key, id) pairs each tile reports to the selection
+constexpr int kWaveTop = 4;       // (key, id) pairs each 64-block wave reports
+constexpr int kTileTop = 4 * kWaveTop;  // pairs per tile
 constexpr int kPoolCap = 4096;    // candidate pool of the per-row selection (LDS)
 constexpr int kMaxTopk = 2048;
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 
 struct ScoreP {
   const void* qi; const float* wi; const void* ki;
   const int64_t* pos0;
   float* scores;      // [rows][sc_rs]
-  uint2* summary;     // [rows][sum_rs]: kTileTop (key, id) per tile, best first
-  int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs, sum_rs;
+  uint32_t* rep_key;  // [rows][key_rs]: per wave, the keys of its kWaveTop best, in id order
+  uint2* rep_info;    // [rows][info_rs]: per wave, (4 packed 8-bit id offsets, bound key)
+  int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs, key_rs, info_rs;
   int tq, row0;       // launch covers global rows row0 + blockIdx.y; row = b*tq + i
   int heads, dim, ratio;
+  int wgs_per_row;    // bf16 kernel: workgroups per row, each walking tiles with that stride
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s);
 
 struct SelectP {
-  const float* scores; const uint2* summary;
+  const float* scores; const uint32_t* rep_key; const uint2* rep_info;
   const int64_t* pos0;
   int32_t* idx; int64_t idx_bs, idx_rs;
   float* sel; int64_t sel_bs, sel_rs;
-  int64_t sc_rs, sum_rs;
+  int64_t sc_rs, key_rs, info_rs;
   int tq, row0, ratio, topk;
 };
 hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s);
@@ -68,7 +71,12 @@ struct AttnP {
   uint32_t mask;
   int m, mh, W, topk;
   float scale;     // already resolved (never 0)
-  int splits, keys_per_split;
+  // this launch covers the virtual keys [key_lo, key_hi) of every row, cut into
+  // `splits` splits of keys_per_split keys; its partials go to slots
+  // split_base .. split_base + splits - 1 of splits_total per row.  With
+  // splits_total == 1 the launch writes o and lse directly.
+  int64_t key_lo, key_hi;
+  int splits, keys_per_split, split_base, splits_total;
 };
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s);
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s);

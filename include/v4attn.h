@@ -126,7 +126,8 @@ v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
  * to the lower id), sorted ascending, then -1 up to k.  sel_scores (optional)
  * receives s of each written id (0 for padding).
  *   dtype        F32 or BF16: type of qi and ki
- *   heads, dim   H_I and d_I; BF16 needs heads % 16 == 0 and dim % 32 == 0
+ *   heads, dim   H_I and d_I; BF16 needs heads in {16, 32, 64, 128} and
+ *                d_I in {32, 64}; F32 needs d_I % 4 == 0 and H_I*(d_I+1) <= 16384
  *   ratio        m >= 1
  *   topk         1 <= k <= 2048
  *   pos0         [batch] int64; pos_max (host) >= pos0[b] + tq - 1 for all b
