@@ -127,18 +127,23 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
+// Splits of the virtual key list: enough (split, row) workgroups to cover the
+// chip twice, but at least kMinKeysPerSplit keys each, since every split writes a
+// partial of heads * (dim + 2) floats that the merge reads back.
+constexpr int64_t kMinKeysPerSplit = 256;
+
 AttnPlan plan_attn(const v4a_attn_args* a) {
   AttnPlan P{};
   P.rows = (int64_t)a->batch * a->tq;
   const int64_t pmax = a->pos_max;
   P.n_keys = ((a->branch_mask & V4A_CSA) ? a->topk : 0) + ((a->branch_mask & V4A_HCA) ? (pmax + 1) / a->hca_ratio : 0) +
              ((a->branch_mask & V4A_SWA) ? std::min<int64_t>(a->window, pmax + 1) : 0);
-  const int64_t cus = cu_count();
-  const int64_t target = 2 * cus;
+  const int64_t target = 2 * (int64_t)cu_count();
   P.splits = 1;
-  if (P.rows < target && P.n_keys > kAttnChunk) {
+  if (P.rows < target && P.n_keys > kMinKeysPerSplit) {
     const int64_t per_row = cdiv(target, P.rows);
-    P.kps = std::max<int64_t>(kAttnChunk, round_up(cdiv(P.n_keys, per_row), kAttnChunk));
+    P.kps = round_up(cdiv(P.n_keys, per_row), kAttnChunk);
+    P.kps = std::max<int64_t>(P.kps, kMinKeysPerSplit);
     P.kps = std::max<int64_t>(P.kps, round_up(cdiv(P.n_keys, kAttnMaxSplits), kAttnChunk));
     P.splits = cdiv(P.n_keys, P.kps);
   }

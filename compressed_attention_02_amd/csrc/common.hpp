@@ -7,6 +7,7 @@ namespace v4a {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte load unit (a native vector, not HIP's uint4 struct, so copies stay in registers)
 
 constexpr int kWave = 64;
 
@@ -101,6 +102,31 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }, 0u);
+}
+
+// Reductions over the four lanes that share lane % 16 (the four 16-lane rows of a
+// wave), e.g. the four row groups of one MFMA output column; every lane gets the
+// result.  Two row-swap steps (permlane16 and permlane32 swaps), no LDS.
+__device__ __forceinline__ float col_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float col_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// A value every lane holds the same copy of, moved to scalar registers so that the
+// compiler treats what derives from it as uniform (scalar branches and address
+// arithmetic instead of per-lane ones).
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // exp(x) with -inf -> 0

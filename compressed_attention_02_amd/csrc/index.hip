@@ -69,15 +69,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Sum of x over the four 16-lane rows of the wave at the same column, in every lane
-// (gfx950 row swaps; the two partial sums are formed in the same order in all lanes).
-__device__ __forceinline__ float col_sum4(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // A wave's report on its 64 packed values (one per lane, 0 = no element; lane L
 // holds block wave_base + L): the keys of its kWaveTop best in ascending id order,
 // their ids as 8-bit offsets from wave_base (0xff = no element) packed in one word,
