@@ -151,6 +151,7 @@ def main():
     steps[0].step(stream)          # allocates the workspaces, which all sets share
     for st in steps[1:]:           # (one stream: steps never overlap)
         st.ws_index, st.ws_attn = steps[0].ws_index, steps[0].ws_attn
+        st.ws_step = getattr(steps[0], "ws_step", None)
 
     def one(k):
         steps[k % R].step(stream)

@@ -31,7 +31,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
 ABI_VERSION = 1
-KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5}
+KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
+           "select_attn": 6}
 
 
 class V4AttnError(RuntimeError):
@@ -88,8 +89,12 @@ def lib() -> ctypes.CDLL:
         for name in ("v4attn_decode_workspace", "v4attn_prefill_chunk_workspace"):
             getattr(L, name).argtypes = [ctypes.POINTER(AttnArgs)]
             getattr(L, name).restype = ctypes.c_size_t
+        L.v4attn_decode_step.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+        L.v4attn_decode_step_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs)]
+        L.v4attn_decode_step_workspace.restype = ctypes.c_size_t
         for name in ("v4attn_compress", "v4attn_index_topk", "v4attn_decode", "v4attn_prefill_chunk",
-                     "v4attn_timing_enable"):
+                     "v4attn_decode_step", "v4attn_timing_enable"):
             getattr(L, name).restype = ctypes.c_int
         L.v4attn_status_string.argtypes = [ctypes.c_int]
         L.v4attn_status_string.restype = ctypes.c_char_p
@@ -227,6 +232,31 @@ def decode(q, pos0, o, *, workspace=None, stream=None, **kw):
 def prefill_chunk(q, pos0, o, *, workspace=None, stream=None, **kw):
     """v4attn_prefill_chunk: Tq causal queries per sequence at pos0[b] + i."""
     return _run_attn("v4attn_prefill_chunk", "v4attn_prefill_chunk_workspace", q, pos0, o, workspace, stream, kw)
+
+
+def _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw):
+    ia = None
+    if qi is not None:
+        ia = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max)
+    aa = attn_args(q, pos0, o, idx=idx, csa_ratio=ratio, topk=topk, pos_max=pos_max, **attn_kw)
+    return (ctypes.byref(ia) if ia is not None else None), ctypes.byref(aa)
+
+
+def decode_step_workspace(qi, wi, ki, q, pos0, o, idx, *, ratio, topk, pos_max, **attn_kw) -> int:
+    ia, aa = _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw)
+    return int(lib().v4attn_decode_step_workspace(ia, aa))
+
+
+def decode_step(qi, wi, ki, q, pos0, o, idx, *, ratio: int, topk: int, pos_max: int, workspace=None,
+                stream=None, **attn_kw):
+    """v4attn_decode_step: index_topk (into idx) and decode in one call; the HCA and window
+    attention overlaps the indexer.  qi/wi/ki may be None when branch_mask has no CSA."""
+    ia, aa = _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw)
+    if workspace is None:
+        workspace = _alloc_ws(int(lib().v4attn_decode_step_workspace(ia, aa)), q.device)
+    p, n = _ws_ptr(workspace)
+    _check(lib().v4attn_decode_step(ia, aa, p, n, _stream(stream)))
+    return workspace
 
 
 # ---------------------------------------------------------------- kernel timing

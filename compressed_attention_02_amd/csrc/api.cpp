@@ -97,7 +97,7 @@ std::mutex g_tmu;
 Timing g_timing[V4A_K_COUNT];
 
 const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select", "attn", "merge",
-                                          "prefill"};
+                                          "prefill", "select_attn"};
 
 // ---------------------------------------------------------------- plans
 struct IndexPlan {
@@ -130,7 +130,7 @@ struct AttnPlan {
 // Splits of the virtual key list: enough (split, row) workgroups to cover the
 // chip twice, but at least kMinKeysPerSplit keys each, since every split writes a
 // partial of heads * (dim + 2) floats that the merge reads back.
-constexpr int64_t kMinKeysPerSplit = 256;
+constexpr int64_t kMinKeysPerSplit = 128;
 
 AttnPlan plan_attn(const v4a_attn_args* a) {
   AttnPlan P{};
@@ -264,6 +264,10 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
     if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
   }
   if (a->sink && !aligned(a->sink, 4)) return fail(V4A_EINVAL, "sink: not 4-byte aligned");
+  // the kernels form cache row offsets from 32-bit row strides
+  const v4a_tensor* caches[] = {&a->kc, &a->vc, &a->kh, &a->vh, &a->k_raw, &a->v_raw};
+  for (const v4a_tensor* t : caches)
+    if (t->ptr && t->row_stride > INT32_MAX) return fail(V4A_ENOTSUP, "cache row strides must be < 2^31 elements");
   return V4A_OK;
 }
 
@@ -315,6 +319,178 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s), "attention launch"));
   timing_after(kid, s);
   if (P.splits > 1) {
+    timing_before(V4A_K_MERGE, s);
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s), "merge launch"));
+    timing_after(V4A_K_MERGE, s);
+  }
+  return ok();
+}
+
+// Launch parameters of v4attn_index_topk (arguments validated, workspace checked).
+struct IndexLaunch {
+  IndexPlan P;
+  ScoreP sp;
+  SelectP tp;
+};
+
+IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
+  IndexLaunch L{};
+  const IndexPlan& P = L.P = plan_index(a);
+  char* base = (char*)ws;
+  ScoreP& sp = L.sp;
+  sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
+  sp.scores = (float*)base;
+  sp.rep_key = (uint32_t*)(base + P.off_keys);
+  sp.rep_info = (uint2*)(base + P.off_info);
+  sp.key_rs = P.key_rs;
+  sp.info_rs = P.info_rs;
+  sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
+  sp.wi_bs = a->wi.batch_stride; sp.wi_rs = a->wi.row_stride;
+  sp.ki_bs = a->ki.batch_stride; sp.ki_rs = a->ki.row_stride;
+  sp.sc_rs = P.sc_rs;
+  sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio;
+  // enough workgroups to cover the chip about eight times; a row with more tiles
+  // than its share has each workgroup walk several of them
+  const int64_t per_row = cdiv(8 * (int64_t)cu_count(), std::min<int64_t>(P.rows, P.chunk_rows));
+  sp.wgs_per_row = (int)std::max<int64_t>(1, std::min<int64_t>(P.ntiles, per_row));
+  SelectP& tp = L.tp;
+  tp.scores = sp.scores; tp.rep_key = sp.rep_key; tp.rep_info = sp.rep_info; tp.pos0 = a->pos0;
+  tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
+  tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
+  tp.sc_rs = P.sc_rs; tp.key_rs = P.key_rs; tp.info_rs = P.info_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
+  return L;
+}
+
+v4a_status launch_score_rows(const v4a_index_args* a, IndexLaunch& L, int64_t r0, int nr, hipStream_t stream) {
+  L.sp.row0 = (int)r0;
+  L.tp.row0 = (int)r0;
+  timing_before(V4A_K_INDEX_SCORE, stream);
+  V4A_TRY(hip_check(launch_score(a->dtype, L.sp, nr, (int)L.P.ntiles, stream), "index score launch"));
+  timing_after(V4A_K_INDEX_SCORE, stream);
+  return V4A_OK;
+}
+
+// Scores and selection of v4attn_index_topk on stream (arguments validated).
+v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  IndexLaunch L = index_launch(a, ws);
+  V4A_TRY(check_ws(ws, ws_bytes, L.P.ws_bytes));
+  for (int64_t r0 = 0; r0 < L.P.rows; r0 += L.P.chunk_rows) {
+    const int nr = (int)std::min<int64_t>(L.P.chunk_rows, L.P.rows - r0);
+    V4A_TRY(launch_score_rows(a, L, r0, nr, stream));
+    timing_before(V4A_K_TOPK_SELECT, stream);
+    V4A_TRY(hip_check(launch_select(L.tp, nr, stream), "top-k select launch"));
+    timing_after(V4A_K_TOPK_SELECT, stream);
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------- fused decode step
+// Key list of a decode row = [CSA picks | HCA entries + window].  The second part
+// does not depend on the selection: it is attended on the side stream while the
+// indexer runs, in splits of kps_rest keys; the CSA picks are attended afterwards
+// in one-chunk splits (they sit on the critical path).  Both write partials into
+// one [rows][s_rest + s_csa] table, merged once.
+struct StepPlan {
+  bool csa;
+  IndexPlan ix;
+  int64_t rows, n_rest, kps_rest, s_rest, s_csa, s_total;
+  size_t off_attn, ws_bytes;
+};
+
+StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
+  StepPlan P{};
+  P.csa = (a->branch_mask & V4A_CSA) != 0;
+  P.rows = a->batch;
+  const int64_t pmax = a->pos_max;
+  P.n_rest = ((a->branch_mask & V4A_HCA) ? (pmax + 1) / a->hca_ratio : 0) +
+             ((a->branch_mask & V4A_SWA) && a->window > 0 ? std::min<int64_t>(a->window, pmax + 1) : 0);
+  P.s_csa = P.csa ? cdiv(a->topk, kAttnChunk) : 0;
+  if (P.n_rest > 0) {
+    const int64_t per_row = cdiv(2 * (int64_t)cu_count(), P.rows);
+    P.kps_rest = std::max<int64_t>(round_up(cdiv(P.n_rest, per_row), kAttnChunk), kMinKeysPerSplit);
+    P.kps_rest = std::max<int64_t>(P.kps_rest, round_up(cdiv(P.n_rest, kAttnMaxSplits - P.s_csa), kAttnChunk));
+    P.s_rest = cdiv(P.n_rest, P.kps_rest);
+  }
+  if (P.s_rest + P.s_csa == 0) {  // no key at all: one empty split writes o = 0 (or the sink alone)
+    P.s_rest = 1;
+    P.kps_rest = kAttnChunk;
+  }
+  P.s_total = P.s_rest + P.s_csa;
+  if (P.csa) P.ix = plan_index(ix);
+  P.off_attn = P.csa ? (size_t)round_up((int64_t)P.ix.ws_bytes, 256) : 0;
+  P.ws_bytes = P.off_attn;
+  if (P.s_total > 1) P.ws_bytes += (size_t)(P.rows * P.s_total * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
+  return P;
+}
+
+v4a_status validate_step(const v4a_index_args* ix, const v4a_attn_args* a) {
+  V4A_TRY(validate_attn(a, false));
+  if (!(a->branch_mask & V4A_CSA)) return V4A_OK;
+  if (!ix) return fail(V4A_EINVAL, "index arguments are NULL but the CSA branch is on");
+  V4A_TRY(validate_index(ix));
+  if (ix->tq != 1) return fail(V4A_EINVAL, "index: tq must be 1 for a decode step");
+  if (ix->batch != a->batch || ix->pos0 != a->pos0 || ix->pos_max != a->pos_max)
+    return fail(V4A_EINVAL, "index and attention disagree on batch, pos0 or pos_max");
+  if (ix->topk != a->topk || ix->ratio != a->csa_ratio)
+    return fail(V4A_EINVAL, "index and attention disagree on topk or the CSA ratio");
+  if (ix->idx.ptr != a->idx.ptr || ix->idx.row_stride != a->idx.row_stride ||
+      (a->batch > 1 && ix->idx.batch_stride != a->idx.batch_stride))
+    return fail(V4A_EINVAL, "index and attention must name the same idx buffer with the same strides");
+  return V4A_OK;
+}
+
+v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t s) {
+  V4A_TRY(validate_step(ix, a));
+  if (a->batch == 0) return ok();
+  const StepPlan P = plan_step(ix, a);
+  if (P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
+  V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
+  AttnPlan AP{};
+  AP.rows = P.rows;
+  AP.splits = P.s_total;
+  AttnP p = make_attn_params(a, AP, nullptr);
+  p.splits_total = (int)P.s_total;
+  if (P.s_total > 1) {
+    p.part_o = (float*)((char*)ws + P.off_attn);
+    p.part_ml = p.part_o + (size_t)P.rows * P.s_total * a->heads * a->dim;
+  }
+  AttnP rest = p, csa = p;
+  rest.key_lo = P.csa ? a->topk : 0;
+  rest.key_hi = INT64_MAX;
+  rest.splits = (int)P.s_rest;
+  rest.keys_per_split = (int)P.kps_rest;
+  rest.split_base = 0;
+  csa.key_lo = 0;
+  csa.key_hi = a->topk;
+  csa.splits = (int)P.s_csa;
+  csa.keys_per_split = kAttnChunk;
+  csa.split_base = (int)P.s_rest;
+
+  auto attend = [&](const AttnP& ap) -> v4a_status {
+    timing_before(V4A_K_ATTN, s);
+    V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s), "attention launch"));
+    timing_after(V4A_K_ATTN, s);
+    return V4A_OK;
+  };
+  if (P.csa) {
+    IndexLaunch IL = index_launch(ix, ws);
+    // selection and the selection-independent attention share one launch when the
+    // rows fit one score pass and the attention is bf16
+    const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
+    if (combined) {
+      V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
+      timing_before(V4A_K_SELECT_ATTN, s);
+      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s), "select+attention launch"));
+      timing_after(V4A_K_SELECT_ATTN, s);
+    } else {
+      V4A_TRY(run_index(ix, ws, P.ix.ws_bytes, s));
+      if (P.s_rest > 0) V4A_TRY(attend(rest));
+    }
+    V4A_TRY(attend(csa));
+  } else {
+    V4A_TRY(attend(rest));
+  }
+  if (P.s_total > 1) {
     timing_before(V4A_K_MERGE, s);
     V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s), "merge launch"));
     timing_after(V4A_K_MERGE, s);
@@ -390,46 +566,7 @@ size_t v4attn_index_topk_workspace(const v4a_index_args* a) {
 
 v4a_status v4attn_index_topk(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   V4A_TRY(validate_index(a));
-  if (a->batch == 0) return ok();
-  const IndexPlan P = plan_index(a);
-  V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
-  char* base = (char*)ws;
-  ScoreP sp{};
-  sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
-  sp.scores = (float*)base;
-  sp.rep_key = (uint32_t*)(base + P.off_keys);
-  sp.rep_info = (uint2*)(base + P.off_info);
-  sp.key_rs = P.key_rs;
-  sp.info_rs = P.info_rs;
-  sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
-  sp.wi_bs = a->wi.batch_stride; sp.wi_rs = a->wi.row_stride;
-  sp.ki_bs = a->ki.batch_stride; sp.ki_rs = a->ki.row_stride;
-  sp.sc_rs = P.sc_rs;
-  sp.tq = a->tq; sp.heads = a->heads; sp.dim = a->dim; sp.ratio = a->ratio;
-  {
-    // enough workgroups to fill the chip about twice, each walking several tiles
-    // one tile per workgroup while that fills the chip a few times over; long rows
-    // batches walk several tiles per workgroup
-    const int64_t per_row = cdiv(8 * (int64_t)cu_count(), std::min<int64_t>(P.rows, P.chunk_rows));
-    sp.wgs_per_row = (int)std::max<int64_t>(1, std::min<int64_t>(P.ntiles, per_row));
-  }
-  SelectP tp{};
-  tp.scores = sp.scores; tp.rep_key = sp.rep_key; tp.rep_info = sp.rep_info; tp.pos0 = a->pos0;
-  tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
-  tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
-  tp.sc_rs = P.sc_rs; tp.key_rs = P.key_rs; tp.info_rs = P.info_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
-  for (int64_t r0 = 0; r0 < P.rows; r0 += P.chunk_rows) {
-    const int nr = (int)std::min<int64_t>(P.chunk_rows, P.rows - r0);
-    sp.row0 = (int)r0;
-    tp.row0 = (int)r0;
-    timing_before(V4A_K_INDEX_SCORE, stream);
-    V4A_TRY(hip_check(launch_score(a->dtype, sp, nr, (int)P.ntiles, stream), "index score launch"));
-    timing_after(V4A_K_INDEX_SCORE, stream);
-    timing_before(V4A_K_TOPK_SELECT, stream);
-    V4A_TRY(hip_check(launch_select(tp, nr, stream), "top-k select launch"));
-    timing_after(V4A_K_TOPK_SELECT, stream);
-  }
-  return ok();
+  return run_index(a, ws, ws_bytes, stream);
 }
 
 size_t v4attn_decode_workspace(const v4a_attn_args* a) {
@@ -439,6 +576,16 @@ size_t v4attn_decode_workspace(const v4a_attn_args* a) {
 
 v4a_status v4attn_decode(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_attn(a, ws, ws_bytes, stream, false);
+}
+
+size_t v4attn_decode_step_workspace(const v4a_index_args* ix, const v4a_attn_args* a) {
+  if (validate_step(ix, a) != V4A_OK || a->batch == 0) return 0;
+  return plan_step(ix, a).ws_bytes;
+}
+
+v4a_status v4attn_decode_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  return run_step(ix, a, ws, ws_bytes, stream);
 }
 
 size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* a) {

@@ -23,420 +23,15 @@
 //     free); the keys a lane holds in P^T are exactly the keys it holds in S^T.
 // Softmax runs in base 2: logits are pre-multiplied by scale*log2(e); partial m is
 // kept in that unit and converted back to natural log for lse.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "attn_impl.hpp"
 
 namespace v4a {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-struct KeyList {
-  int n_csa;
-  int64_t e_vis, w_lo, n_keys;
-};
-
-__device__ __forceinline__ KeyList key_list(const AttnP& p, int64_t pos) {
-  KeyList L;
-  L.n_csa = (p.mask & 1u) ? p.topk : 0;
-  L.e_vis = (p.mask & 2u) ? (pos + 1) / p.mh : 0;
-  L.w_lo = pos - p.W + 1 > 0 ? pos - p.W + 1 : 0;
-  const int64_t n_swa = ((p.mask & 4u) && p.W > 0) ? pos - L.w_lo + 1 : 0;
-  L.n_keys = L.n_csa + L.e_vis + n_swa;
-  return L;
-}
-
-// Row pointers of virtual key t; false for a CSA slot padded with -1.
-template <typename T>
-__device__ __forceinline__ bool key_rows(const AttnP& p, const KeyList& L, int b, int i, int64_t t,
-                                         const T*& kp, const T*& vp) {
-  if (t < L.n_csa) {
-    const int32_t id = p.idx[(int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs + t];
-    if (id < 0) return false;
-    kp = reinterpret_cast<const T*>(p.kc) + (int64_t)b * p.kc_bs + (int64_t)id * p.kc_rs;
-    vp = reinterpret_cast<const T*>(p.vc) + (int64_t)b * p.vc_bs + (int64_t)id * p.vc_rs;
-    return true;
-  }
-  t -= L.n_csa;
-  if (t < L.e_vis) {
-    kp = reinterpret_cast<const T*>(p.kh) + (int64_t)b * p.kh_bs + t * p.kh_rs;
-    vp = reinterpret_cast<const T*>(p.vh) + (int64_t)b * p.vh_bs + t * p.vh_rs;
-    return true;
-  }
-  t -= L.e_vis;
-  const int64_t r = L.w_lo + t - p.raw_start[b];
-  kp = reinterpret_cast<const T*>(p.kr) + (int64_t)b * p.kr_bs + r * p.kr_rs;
-  vp = reinterpret_cast<const T*>(p.vr) + (int64_t)b * p.vr_bs + r * p.vr_rs;
-  return true;
-}
-
-// Final normalisation of one head (base-2 running max m, sum l, unnormalised o).
-// Returns the factor for o and writes lse (natural log) through *lse_out.
-__device__ __forceinline__ float finish_head(float m, float l, const float* sink, int head, float* lse_out) {
-  float scale_o = 1.f;
-  if (sink) {
-    const float z = sink[head] * kLog2e;
-    const float mn = fmaxf(m, z);
-    const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-    l = l * a + exp2f(z - mn);
-    scale_o = a;
-    m = mn;
-  }
-  *lse_out = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-  return l > 0.f ? scale_o / l : 0.f;
-}
-
-// ------------------------------------------------------------------ bf16 MFMA
-// Where the keys of one row come from.  Virtual key t < n_csa is CSA pick t (its
-// id read from the split's copy of the idx row in LDS), t < hca_end is HCA entry
-// t - n_csa, anything later is raw row t + raw_off.  Keys the row does not have
-// (past the split's end, padded CSA slots) read the row's query instead, which is
-// always valid memory, and are masked out, so every load is unconditional and no
-// load waits on another.
-struct RowKeys {
-  const uint16_t *kc, *vc, *kh, *vh, *kr, *vr, *fallback;  // the row's sequence
-  int64_t kc_rs, vc_rs, kh_rs, vh_rs, kr_rs, vr_rs;        // row strides (elements)
-  int64_t n_csa, hca_end, raw_off, k_begin, k_end;
-};
-
-constexpr float kLazyRescale = 8.f; // running max moves only when exceeded by 2^8
-
-// Source rows of key t in the general case (a chunk that straddles branches or
-// the end of the split): selects only.
-__device__ __forceinline__ void key_src_any(const RowKeys& R, const int* s_idx, int64_t t, const uint16_t*& kp,
-                                            const uint16_t*& vp, bool& ok) {
-  const bool in = t < R.k_end;
-  const bool csa = t < R.n_csa, hca = t < R.hca_end;
-  const int64_t j = t - R.k_begin;
-  const int id = s_idx[j < 0 ? 0 : (j >= kMaxTopk ? kMaxTopk - 1 : j)];
-  ok = in && (!csa || id >= 0);
-  const int64_t rc = id, rh = t - R.n_csa, rr = t + R.raw_off;
-  const int64_t r = ok ? (csa ? rc : (hca ? rh : rr)) : 0;
-  const int64_t kcs = R.kc_rs, khs = R.kh_rs, krs = R.kr_rs, vcs = R.vc_rs, vhs = R.vh_rs, vrs = R.vr_rs;
-  const int64_t ks = csa ? kcs : (hca ? khs : krs);
-  const int64_t vs = csa ? vcs : (hca ? vhs : vrs);
-  const uint16_t *kc = R.kc, *kh = R.kh, *kr = R.kr, *vc = R.vc, *vh = R.vh, *vr = R.vr, *fb = R.fallback;
-  const uint16_t* kb = ok ? (csa ? kc : (hca ? kh : kr)) : fb;
-  const uint16_t* vb = ok ? (csa ? vc : (hca ? vh : vr)) : fb;
-  kp = kb + r * ks;
-  vp = vb + r * vs;
-}
-
-// LDS layout of a chunk: K and V rows of D bf16 each, unpadded, with the 16-byte
-// pieces of row r permuted by XOR with swz_k(r) / swz_v(r).  The permutations make
-// the three access patterns free of bank conflicts: the direct global->LDS loads
-// (a wave writes 1 KB contiguously), the K fragment reads (16 rows, one piece
-// column) and the transposing V reads (4 rows x 2 pieces per 16 lanes).
-template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
-
-// One 16-byte-per-lane load from global memory straight into LDS: lane l's bytes
-// land at LDS address lds + 16 l (lds wave-uniform).  Written as inline asm so that
-// the compiler's wait insertion does not treat every later LDS read as depending
-// on it; the code that consumes the data waits for it explicitly (s_waitcnt on
-// the vector-memory counter, then a workgroup barrier).  The instruction has no
-// register result, and the compiler's own waits can only get stricter for not
-// counting it, since vector-memory loads complete in issue order.
-__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// row r of a table at base with row stride rs (elements): 32 x 32 -> 64-bit product
-__device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_t r, int64_t rs) {
-  return base + (uint64_t)r * (uint32_t)rs;
-}
-
-// Issues the loads of the chunk at virtual key kc0 straight into LDS (sK, sV) and
-// writes its mask (sBias[key] = 0 or -inf).  Each wave moves rows of 64 lanes x
-// 16 bytes per instruction; lane l's piece lands at LDS base + 16 l, so the lane
-// loads the global piece that the XOR layout puts there.  wave is uniform.
-template <int NW, int D>
-__device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, int64_t kc0, uint16_t* sK,
-                                            uint16_t* sV, float* sBias, int wave, int lane) {
-  constexpr int PIECES = D / 8;               // 16-byte pieces per row
-  constexpr int RPI = 64 / PIECES;            // rows per wave instruction
-  constexpr int IPW = kAttnChunk / RPI / NW;  // instructions per wave, for K and for V
-  static_assert(IPW * RPI * NW == kAttnChunk, "rows must divide over the waves");
-  const int prow = lane / PIECES, ppiece = lane % PIECES;
-  // chunks wholly inside one branch (the common case) take a plain address
-  const bool whole = kc0 + kAttnChunk <= R.k_end;
-  const bool all_h = whole && kc0 >= R.n_csa && kc0 + kAttnChunk <= R.hca_end;
-  const bool all_r = whole && kc0 >= R.hca_end;
-  const bool all_c = whole && kc0 + kAttnChunk <= R.n_csa;
-  const uint16_t *kb = R.kh, *vb = R.vh;
-  int64_t ks = R.kh_rs, vs = R.vh_rs;
-  if (all_r) { kb = R.kr + (kc0 + R.raw_off) * R.kr_rs; vb = R.vr + (kc0 + R.raw_off) * R.vr_rs; ks = R.kr_rs; vs = R.vr_rs; }
-  else if (all_h) { kb = R.kh + (kc0 - R.n_csa) * R.kh_rs; vb = R.vh + (kc0 - R.n_csa) * R.vh_rs; }
-#pragma unroll
-  for (int u = 0; u < IPW; ++u) {
-    const int r0 = (wave * IPW + u) * RPI;    // first row of this instruction (uniform)
-    const int r = r0 + prow;
-    const uint16_t *kp, *vp;
-    bool ok = true;
-    if (all_h || all_r) {
-      kp = row_ptr(kb, r, ks);
-      vp = row_ptr(vb, r, vs);
-    } else if (all_c) {
-      const int id = s_idx[kc0 - R.k_begin + r];
-      ok = id >= 0;
-      kp = row_ptr(ok ? R.kc : R.fallback, ok ? id : 0, R.kc_rs);
-      vp = row_ptr(ok ? R.vc : R.fallback, ok ? id : 0, R.vc_rs);
-    } else {
-      key_src_any(R, s_idx, kc0 + r, kp, vp, ok);
-    }
-    lds_load16(kp + (ppiece ^ swz_k<D>(r)) * 8, lds_addr(sK + r0 * D));
-    lds_load16(vp + (ppiece ^ swz_v<D>(r)) * 8, lds_addr(sV + r0 * D));
-    if (ppiece == 0) sBias[r] = ok ? 0.f : -INFINITY;
-  }
-}
-
-// S^T = K Q^T, online softmax and O^T += V^T P^T for one chunk of kAttnChunk keys
-// in LDS, for HT tiles of 16 heads.
-//   * S^T: keys on M, heads on N; lane (col, grp) ends up with head col and keys
-//     16*kt + 4*grp + e of the chunk; each K fragment feeds all HT tiles.
-//   * P^T operand of 32 keys holds keys {4grp+e, 16+4grp+e}; the matching V^T
-//     fragment comes from two transposing LDS reads (ds_read_b64_tr_b16), each of
-//     which hands lane j of a 16-lane group V[key0+e][d0+j], e = 0..3, when lane s
-//     of the group points at V[key0 + s/4][d0 + 4*(s%4)].
-//   * P is split into bf16 hi + lo parts (hardware round-to-nearest conversion),
-//     so P keeps ~16 significant bits.
-//   * The running max m only moves when a chunk max exceeds it by more than
-//     kLazyRescale (base 2); until then exp2(x - m) <= 2^8 and O, l need no
-//     rescaling.  (m, l, O) stay consistent, which is all that finishing and
-//     merging need.
-template <int D, int HT>
-__device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t* sV, const float* sBias,
-                                             const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
-                                             float (&m_run)[HT], float (&l_run)[HT], float sl2, int col, int grp) {
-  constexpr int KS = D / 32, DT = D / 16;
-  f32x4 S[HT][4];
-  // K fragment: row 16kt + col, piece 4s + grp; the row's XOR does not depend on kt
-  const uint16_t* kb = sK + col * D;
-  const int kx = swz_k<D>(col);
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int t = 0; t < HT; ++t) S[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(kb + 16 * kt * D + ((4 * s + grp) ^ kx) * 8);
-#pragma unroll
-      for (int t = 0; t < HT; ++t) S[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qb[t][s], S[t][kt], 0, 0, 0);
-    }
-  }
-  // logits in base 2 (masked keys -inf), in place
-  float cm[HT];
-  bool need = false;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * kt + 4 * grp]);
-#pragma unroll
-    for (int t = 0; t < HT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][kt][e] = fmaf(S[t][kt][e], sl2, bias[e]);
-  }
-#pragma unroll
-  for (int t = 0; t < HT; ++t) {
-    float c = fmaxf(fmaxf(S[t][0][0], S[t][0][1]), fmaxf(S[t][0][2], S[t][0][3]));
-#pragma unroll
-    for (int kt = 1; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c = fmaxf(c, S[t][kt][e]);
-    cm[t] = col_max4(c);
-    need = need || (cm[t] > m_run[t] + kLazyRescale);
-  }
-  if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      const bool up = cm[t] > m_run[t] + kLazyRescale;
-      const float alpha = up ? __builtin_amdgcn_exp2f(m_run[t] - cm[t]) : 1.f;
-      m_run[t] = up ? cm[t] : m_run[t];
-      l_run[t] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[t][dt] *= alpha;
-    }
-  }
-  float mu[HT];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) mu[t] = m_run[t] == -INFINITY ? 0.f : m_run[t];
-
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  // V^T fragment: rows 32kk + 4grp + col/4 (+16), piece 2dt + (col%4)/2, half col%2;
-  // the rows' XOR does not depend on kk
-  const int vr = 4 * grp + (col >> 2);
-  const int vx = swz_v<D>(vr);
-  const uint16_t* vb = sV + vr * D + (col & 1) * 4;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    // P^T of keys 32kk + {4grp+e, 16+4grp+e} (tiles 2kk, 2kk+1) as bf16 hi + lo
-    bf16x8_t Bhi[HT], Blo[HT];
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_exp2f(S[t][2 * kk + (e >> 2)][e & 3] - mu[t]);
-        ps += v;
-        const __bf16 h = (__bf16)v;
-        Bhi[t][e] = h;
-        Blo[t][e] = (__bf16)(v - (float)h);
-      }
-      l_run[t] += ps;
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* v0 = vb + 32 * kk * D + ((2 * dt + ((col & 3) >> 1)) ^ vx) * 8;
-      const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0));
-      const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0 + 16 * D));
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        O[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi[t], O[t][dt], 0, 0, 0);
-        O[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo[t], O[t][dt], 0, 0, 0);
-      }
-    }
-  }
-}
-
-// The chunk pipeline of one split, double-buffered in LDS: the loads of chunk c + 1
-// are in flight while chunk c is computed.  Every iteration keeps the same loads in
-// flight in the same order (chunks past the end read the fallback row and are
-// never used), so waiting until only the newest chunk's 2 * IPW loads are
-// outstanding settles the current chunk (and, the first time, the q loads).
-template <int NW, int D, int HT>
-__device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, uint16_t* K0, uint16_t* V0, float* B0,
-                                           uint16_t* K1, uint16_t* V1, float* B1, int64_t nch, bool active,
-                                           const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
-                                           float (&m_run)[HT], float (&l_run)[HT], float sl2, int wave, int lane) {
-  constexpr int CH = kAttnChunk;
-  constexpr int IPW = CH / (64 / (D / 8)) / NW;  // direct loads per wave per chunk, for K and for V
-  const int col = lane & 15, grp = lane >> 4;
-  if (nch > 0) {
-    issue_chunk<NW, D>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
-    issue_chunk<NW, D>(R, s_idx, R.k_begin + CH, K1, V1, B1, wave, lane);
-  }
-  for (int64_t c = 0; c < nch; c += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // vmcnt(2 * IPW)
-    __syncthreads();
-    if (active) attend_chunk<D, HT>(K0, V0, B0, Qb, O, m_run, l_run, sl2, col, grp);
-    __syncthreads();
-    issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 2) * CH, K0, V0, B0, wave, lane);
-    const bool more = c + 1 < nch;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // vmcnt(2 * IPW)
-    __syncthreads();
-    if (active && more) attend_chunk<D, HT>(K1, V1, B1, Qb, O, m_run, l_run, sl2, col, grp);
-    __syncthreads();
-    issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 3) * CH, K1, V1, B1, wave, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the workgroup
-}
-
-// One workgroup of NW waves per (split, row).  Wave w computes head tiles w, w + NW,
-// ... (HT of them); a tile past the head count is computed on a copy of tile 0's
-// queries and not written.  All waves load.  Chunks are double-buffered in LDS:
-// the loads of chunk c + 1 are in flight while chunk c is computed.
+// One workgroup of NW waves per (split, row), two workgroups per CU when NW <= 4.
 template <int NW, int HT, int D>
 __global__ __launch_bounds__(NW * 64, NW * HT <= 4 ? 2 : 1) void attn_bf16_kernel(AttnP p) {
-  constexpr int NT = NW * 64, CH = kAttnChunk, KS = D / 32, DT = D / 16;
-  // two buffers as separate arrays: reads of one are then known not to alias the
-  // direct loads in flight into the other, so they need not wait for them
-  __shared__ __align__(16) uint16_t sK0[CH * D], sK1[CH * D];
-  __shared__ __align__(16) uint16_t sV0[CH * D], sV1[CH * D];
-  __shared__ __align__(16) float sB0[CH], sB1[CH];
-  __shared__ int s_idx[kMaxTopk];
-
-  const int row = blockIdx.y, split = blockIdx.x;
-  const int b = row / p.tq, i = row - b * p.tq;
-  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ntile = p.heads / 16;
-  const float sl2 = p.scale * kLog2e;
-
-  const int64_t pos = uniform_i64(p.pos0[b] + i);
-  const int64_t raw0 = uniform_i64((p.mask & 4u) ? p.raw_start[b] : 0);
-  const KeyList L = key_list(p, pos);
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs;
-  RowKeys R;
-  R.k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
-  R.k_end = min(min(L.n_keys, p.key_hi), R.k_begin + (int64_t)p.keys_per_split);
-  R.n_csa = L.n_csa;
-  R.hca_end = L.n_csa + L.e_vis;
-  R.raw_off = L.w_lo - R.hca_end - raw0;
-  R.fallback = qrow;
-  R.kc = (p.mask & 1u) ? reinterpret_cast<const uint16_t*>(p.kc) + (int64_t)b * p.kc_bs : qrow;
-  R.vc = (p.mask & 1u) ? reinterpret_cast<const uint16_t*>(p.vc) + (int64_t)b * p.vc_bs : qrow;
-  R.kh = (p.mask & 2u) ? reinterpret_cast<const uint16_t*>(p.kh) + (int64_t)b * p.kh_bs : qrow;
-  R.vh = (p.mask & 2u) ? reinterpret_cast<const uint16_t*>(p.vh) + (int64_t)b * p.vh_bs : qrow;
-  R.kr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.kr) + (int64_t)b * p.kr_bs : qrow;
-  R.vr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.vr) + (int64_t)b * p.vr_bs : qrow;
-  R.kc_rs = p.kc_rs; R.vc_rs = p.vc_rs; R.kh_rs = p.kh_rs; R.vh_rs = p.vh_rs; R.kr_rs = p.kr_rs; R.vr_rs = p.vr_rs;
-
-  int tile[HT];
-  bf16x8_t Qb[HT][KS];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) {
-    tile[t] = wave + NW * t;
-    const int tq = tile[t] < ntile ? tile[t] : 0;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      Qb[t][s] = *reinterpret_cast<const bf16x8_t*>(qrow + (tq * 16 + col) * D + s * 32 + grp * 8);
-  }
-
-  // the split's CSA ids (at most topk of them) go to LDS once
-  const int64_t n_idx = min(R.k_end, R.n_csa) - R.k_begin;
-  if (n_idx > 0) {
-    const int32_t* ip = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs + R.k_begin;
-    for (int64_t j0 = 0; j0 < n_idx; j0 += 4 * NT) {
-      int v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ip[min(j0 + u * NT + tid, n_idx - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (j0 + u * NT + tid < n_idx) s_idx[j0 + u * NT + tid] = v[u];
-    }
-    __syncthreads();
-  }
-
-  float m_run[HT], l_run[HT];
-  f32x4 O[HT][DT];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  run_chunks<NW, D, HT>(R, s_idx, sK0, sV0, sB0, sK1, sV1, sB1, nch, tile[0] < ntile, Qb, O, m_run, l_run, sl2, wave,
-                    lane);
-
-#pragma unroll
-  for (int t = 0; t < HT; ++t) {
-    if (tile[t] >= ntile) continue;
-    const int head = tile[t] * 16 + col;
-    const float l = col_sum4(l_run[t]);
-    if (p.splits_total == 1) {
-      float lse;
-      const float f = finish_head(m_run[t], l, p.sink, head, &lse);
-      float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(orow + dt * 16 + 4 * grp) =
-            make_float4(O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f);
-      if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
-    } else {
-      const int64_t slot = ((int64_t)row * p.splits_total + p.split_base + split) * p.heads + head;
-      float* po = p.part_o + slot * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + dt * 16 + 4 * grp) =
-            make_float4(O[t][dt][0], O[t][dt][1], O[t][dt][2], O[t][dt][3]);
-      if (grp == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[t], l);
-    }
-  }
+  __shared__ __align__(16) AttnSmem<D> sm;
+  attn_block<NW, HT, D>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -535,11 +130,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   const int S = p.splits_total, D = p.dim;
   const float* ml = p.part_ml + ((int64_t)row * S * p.heads + head) * 2;
   const int64_t ml_step = (int64_t)p.heads * 2;
+  // thread (g, c) sums output column c over splits g, g+G, ... in ascending order;
+  // its first kMergeBatch partial values load together with the split statistics
+  const int G = kMergeThreads / D;
+  const int c = tid % D, g = tid / D;
+  const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * D + c;
+  const int64_t po_step = (int64_t)p.heads * D;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(g + u * G, S - 1) * po_step];
   float ms = -INFINITY, ls = 0.f;
   if (tid < S) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + tid * ml_step);
-    ms = v.x;
-    ls = v.y;
+    const float2 m2 = *reinterpret_cast<const float2*>(ml + tid * ml_step);
+    ms = m2.x;
+    ls = m2.y;
   }
   // 1) global max of the split maxima (S <= kMergeThreads: one split per thread)
   float mx = wave_max(ms);
@@ -557,16 +161,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   float l = 0.f;
   for (int w = 0; w < kMergeThreads / 64; ++w) l += s_red[w];
   __syncthreads();
-  // 3) weighted sum of the partial outputs: thread (g, c) takes splits g, g+G, ...
-  //    in ascending order, loading kMergeBatch of them at a time so that their
-  //    loads are in flight together
-  const int G = kMergeThreads / D;
-  const int c = tid % D, g = tid / D;
-  const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * D + c;
-  const int64_t po_step = (int64_t)p.heads * D;
+  // 3) weighted sum of the partial outputs
   float acc = 0.f;
-  for (int s0 = g; s0 < S; s0 += G * kMergeBatch) {
-    float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    if (g + u * G < S) acc = fmaf(s_w[g + u * G], v[u], acc);
+  for (int s0 = g + G * kMergeBatch; s0 < S; s0 += G * kMergeBatch) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(s0 + u * G, S - 1) * po_step];
 #pragma unroll

@@ -81,6 +81,10 @@ struct AttnP {
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s);
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s);
 
+// selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
+// workgroups) in one launch
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s);
+
 // ---------------------------------------------------------------- timing hooks
 void timing_before(int kernel, hipStream_t s);
 void timing_after(int kernel, hipStream_t s);

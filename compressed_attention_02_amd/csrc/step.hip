@@ -1,0 +1,46 @@
+// The decode step's top-k selection and its selection-independent attention in
+// one launch.
+//
+// QbitAI article "DeepSeek V4报告太详尽了！484天换代之路全公开", section 混合注意力机制:
+// the HCA entries and the sliding window do not depend on which compressed blocks
+// the indexer picks.  The selection needs one workgroup per query row for several
+// microseconds, so the rest of the chip attends those keys meanwhile: workgroups
+// [0, n_sel) of the launch select (as select_kernel), the others attend a split of
+// the key range after the CSA picks (as attn_bf16_kernel with 8 waves).  One
+// launch on one stream: no cross-queue synchronisation.
+#include "attn_impl.hpp"
+#include "select_impl.hpp"
+
+namespace v4a {
+
+template <int D>
+union StepSmem {
+  AttnSmem<D> attn;
+  SelShared sel;
+};
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, AttnP ap, int n_sel) {
+  static_assert(kSelThreads == 8 * 64, "the attention workgroups run 8 waves");
+  __shared__ __align__(16) StepSmem<D> sm;
+  const int blk = blockIdx.x;
+  if (blk < n_sel) {
+    select_row(sp, blk, sm.sel);
+    return;
+  }
+  const int a = blk - n_sel;
+  attn_block<8, 1, D>(ap, a % ap.splits, a / ap.splits, sm.attn);
+}
+
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s) {
+  const int64_t n = (int64_t)n_sel + (int64_t)ap.splits * n_rows;
+  if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0)
+    return hipErrorInvalidValue;
+  if (ap.dim == 64)
+    hipLaunchKernelGGL(select_attn_kernel<64>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
+  else
+    hipLaunchKernelGGL(select_attn_kernel<128>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
+  return hipGetLastError();
+}
+
+}  // namespace v4a

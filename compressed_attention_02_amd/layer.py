@@ -11,7 +11,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import CSA, HCA, SWA, compress, decode, index_topk, prefill_chunk
+from . import CSA, HCA, SWA, compress, decode, decode_step, index_topk, prefill_chunk
 
 
 def to_device(arrays: dict, device="cuda") -> dict:
@@ -102,9 +102,24 @@ class LayerStep:
         self.ws_attn = fn(self.t["q"], self.t["pos"], self.o, workspace=self.ws_attn, stream=stream,
                           **self.attn_kwargs())
 
-    def step(self, stream=None):
+    def run_decode_step(self, stream=None):
+        """index_topk + decode as one v4attn_decode_step (decode only)."""
+        s, t = self.s, self.t
+        kw = self.attn_kwargs()
+        for k in ("idx", "csa_ratio", "topk", "pos_max"):
+            kw.pop(k)
+        csa = bool(s.branches & CSA)
+        self.ws_step = decode_step(t["qi"] if csa else None, t.get("wi"), t.get("ki"), t["q"], t["pos"], self.o,
+                                   self.idx, ratio=s.m, topk=s.topk, pos_max=self.pos_max,
+                                   workspace=getattr(self, "ws_step", None), stream=stream, **kw)
+
+    def step(self, stream=None, fused=True):
         """The whole hot path of one step: compress (if the step compresses),
-        index_topk (if CSA is on), attention."""
+        index_topk (if CSA is on), attention.  A decode step with fused=True runs
+        the last two as one v4attn_decode_step."""
         self.run_compress(stream)
+        if fused and self.s.tq == 1:
+            self.run_decode_step(stream)
+            return
         self.run_index(stream)
         self.run_attn(stream)

@@ -224,6 +224,31 @@ v4a_status v4attn_prefill_chunk(const v4a_attn_args* args, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * v4attn_decode_step — one decode step of the layer: v4attn_index_topk then
+ * v4attn_decode, with the same results (idx bit for bit; o and lse up to
+ * rounding, as the key list is split differently).
+ * [QbitAI] 混合注意力机制: the HCA and window branches do not depend on the
+ * CSA selection, so with a bf16 attention they are attended by the other
+ * workgroups of the launch that runs the top-k selection (which needs one
+ * workgroup per query row); the CSA keys are attended once the selection is
+ * done, and one merge combines both.  Everything runs on `stream`, in order.
+ *   index   arguments of v4attn_index_topk with tq == 1; its idx is read by
+ *           the attention.  Ignored (may be NULL) when attn has no CSA branch.
+ *   attn    arguments of v4attn_decode.  With CSA: batch, pos0 and pos_max
+ *           equal index's, topk == index->topk, csa_ratio == index->ratio,
+ *           and idx names the same buffer with the same strides.
+ * Errors: as the two calls, plus V4A_EINVAL when index and attn disagree.
+ * Workspace: v4attn_decode_step_workspace(index, attn) bytes (0 when the
+ * arguments are invalid), 256-byte aligned, owned by the caller and not used
+ * after the work enqueued on stream completes.
+ * ------------------------------------------------------------------------- */
+size_t v4attn_decode_step_workspace(const v4a_index_args* index,
+                                    const v4a_attn_args* attn);
+v4a_status v4attn_decode_step(const v4a_index_args* index,
+                              const v4a_attn_args* attn, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Status, version, diagnostics.
  * ------------------------------------------------------------------------- */
 const char* v4attn_status_string(v4a_status s);
@@ -246,7 +271,8 @@ enum {
   V4A_K_ATTN = 3,
   V4A_K_MERGE = 4,
   V4A_K_PREFILL = 5,
-  V4A_K_COUNT = 6
+  V4A_K_SELECT_ATTN = 6, /* v4attn_decode_step: selection + HCA/window attention */
+  V4A_K_COUNT = 7
 };
 v4a_status v4attn_timing_enable(int kernel, int max_launches);
 int v4attn_timing_read(int kernel, float* ms, int cap);

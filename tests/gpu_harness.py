@@ -77,10 +77,16 @@ class Run:
         self.t = to_device(self.g)
         self.step = LayerStep(LayerShape.of(cfg), self.t)
 
-    def run(self):
+    def run(self, fused=False):
+        """Stages one by one (synchronising after each), or, with fused=True and a
+        decode configuration, compress then one v4attn_decode_step."""
         st = self.step
         st.run_compress()
         torch.cuda.synchronize()
+        if fused and self.cfg.tq == 1:
+            st.run_decode_step()
+            torch.cuda.synchronize()
+            return self
         st.run_index()
         torch.cuda.synchronize()
         st.run_attn()

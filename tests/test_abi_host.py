@@ -172,3 +172,42 @@ def test_valid_call_without_gpu_reports_hip_error():
         pytest.skip("a GPU is visible; this checks the no-device path only")
     r, msg = _st(V.lib().v4attn_compress, good_compress(), None)
     assert r == EHIP and msg
+
+
+def _step(ix, a, ws=None, n=0):
+    L = V.lib()
+    r = L.v4attn_decode_step(ctypes.byref(ix) if ix is not None else None, ctypes.byref(a), ws, n, None)
+    return r, L.v4attn_last_error().decode()
+
+
+@pytest.mark.parametrize("ix_kw,a_kw", [
+    (dict(topk=256), {}), (dict(ratio=8), {}), (dict(pos_max=131073), {}), (dict(tq=2), {}),
+    (dict(idx=_T(FAKE + 256, 512, 512)), {}), (dict(idx=_T(FAKE, 512, 1024)), {}), (dict(batch=1), {}),
+    ({}, dict(tq=2)), ({}, dict(topk=0)),
+])
+def test_decode_step_rejects_mismatch(ix_kw, a_kw):
+    r, msg = _step(good_index(**ix_kw), good_attn(**a_kw))
+    assert r == EINVAL and msg
+
+
+def test_decode_step_workspace_and_null_index():
+    L = V.lib()
+    ix, a = good_index(), good_attn()
+    need = L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a))
+    # the indexer's workspace plus the attention partials of both launches
+    assert need > L.v4attn_index_topk_workspace(ctypes.byref(ix))
+    assert _step(ix, a)[0] == EWORKSPACE
+    assert _step(ix, a, FAKE + 16, need)[0] == EWORKSPACE
+    # the CSA branch needs the indexer's arguments; without it they may be NULL
+    assert _step(None, a)[0] == EINVAL
+    assert L.v4attn_decode_step_workspace(None, ctypes.byref(a)) == 0
+    b = good_attn(branch_mask=6, kc=_T(None), vc=_T(None), idx=_T(None))
+    assert L.v4attn_decode_step_workspace(None, ctypes.byref(b)) > 0
+    # invalid arguments report no workspace
+    assert L.v4attn_decode_step_workspace(ctypes.byref(good_index(topk=256)), ctypes.byref(a)) == 0
+
+
+def test_attention_rejects_huge_row_strides():
+    big = 1 << 31
+    r, msg = _st(V.lib().v4attn_decode, good_attn(kh=_T(FAKE, big * 4, big)), None, 0, None)
+    assert r == ENOTSUP and msg

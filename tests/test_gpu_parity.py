@@ -93,10 +93,18 @@ def test_determinism_and_idx_permutation():
     cfg = SMALL["c3_small"]
     r = Run(cfg).run()
     o1, l1, i1 = (dev_to_np(x).copy() for x in (r.step.o, r.step.lse, r.step.idx))
-    r.step.step()
+    r.step.step(fused=False)
     torch.cuda.synchronize()
     assert np.array_equal(o1, dev_to_np(r.step.o))
     assert np.array_equal(l1, dev_to_np(r.step.lse))
+    assert np.array_equal(i1, dev_to_np(r.step.idx))
+    # the fused step is deterministic too (its split of the key list differs)
+    r.step.step()
+    torch.cuda.synchronize()
+    of, lf = dev_to_np(r.step.o).copy(), dev_to_np(r.step.lse).copy()
+    r.step.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(of, dev_to_np(r.step.o)) and np.array_equal(lf, dev_to_np(r.step.lse))
     assert np.array_equal(i1, dev_to_np(r.step.idx))
     # the selected blocks in reverse order give the same output up to rounding order
     rev = torch.flip(r.step.idx, dims=[2]).contiguous()
@@ -124,3 +132,34 @@ def test_incremental_compress_bitwise():
         lo, hi = 4096 // ratio, (4096 + 512) // ratio
         assert torch.equal(one_k[:, lo:hi], t[kn][:, lo:hi])
         assert torch.equal(one_v[:, lo:hi], t[vn][:, lo:hi])
+
+
+@pytest.mark.parametrize("name", ["c1_tiny_f32", "c2_small", "c3_small", "c4_small"])
+def test_fused_decode_step(name):
+    # v4attn_decode_step: the HCA + window attention overlaps the indexer on the
+    # side stream; idx must equal the separate index_topk's bit for bit
+    cfg = SMALL[name]
+    if name == "c4_small":
+        cfg = cfg.small(compress_tokens=1024 + (cfg.pos % cfg.m_hca))
+    print(f"[case] fused {name}", flush=True)
+    r = Run(cfg).run(fused=True).check_all()
+    idx_fused = dev_to_np(r.step.idx).copy()
+    o_fused = dev_to_np(r.step.o).copy()
+    r.run(fused=False)
+    assert np.array_equal(dev_to_np(r.step.idx), idx_fused)
+    assert_close(o_fused, dev_to_np(r.step.o), cfg.dtype, "fused vs separate o")
+
+
+@pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
+def test_fused_branch_subsets(mask):
+    cfg = C.C2.small(name=f"fmask{mask}", batch=2, pos=4097, branches=mask, needles=4)
+    print(f"[case] fused mask {mask}", flush=True)
+    Run(cfg).run(fused=True).check_all()
+
+
+def test_fused_short_context_and_small_topk():
+    # a row with no HCA entry yet and fewer visible blocks than k; k = 32 is a
+    # single partial chunk
+    cfg = C.C2.small(name="fshort", batch=2, pos=37, needles=0, topk=32, compress="all", compress_tokens=38)
+    print("[case] fused short", flush=True)
+    Run(cfg).run(fused=True).check_all()
