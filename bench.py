@@ -11,7 +11,8 @@ launch stream between two synchronisations.  Inputs are resident in HBM; the ste
 cycles through R copies of the input set at distinct addresses (R * bytes touched
 per step >= 2.5x the 256 MB Infinity Cache) so that steps are not served from it.
 The dominant kernel (the indexer score kernel, which streams the indexer keys) is
-bracketed by HIP events inside the library on its own stream for every timed launch.
+timed on every timed launch by a pair of HIP events that its dispatch records at the
+kernel's start and end (the library's timing hooks, hipExtLaunchKernel).
 
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
 """
@@ -30,6 +31,66 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn tokens/s + achieved HBM GB/s, CSA+HCA+SWA layer at 1M ctx"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+# HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of this script, calibrated on a plain device copy of known size made in
+# the same runs (--calibration-copy).  The file records a hash of the kernel's sources;
+# once they change the figure no longer describes the kernel and is not reported.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_bf16_c3.json")
+SCORE_SOURCES = ("index.hip", "select_impl.hpp", "common.hpp", "kernels.hpp")
+
+
+def score_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "compressed_attention_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != score_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def _pmc_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = []
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            out.append((int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0), r["Kernel_Name"],
+                        float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def parse_pmc(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
+    """HBM bytes per launch of score_bf16_kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes / counter of the calibration copy (the last
+    three device copies of the run, copy_bytes each)."""
+    res = {}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _pmc_rows(path)
+        score = [v for _, k, v in rows if "score_bf16_kernel" in k]
+        copies = [v for _, k, v in rows if "copyBuffer" in k][-3:]
+        if not score or len(copies) < 3:
+            raise SystemExit(f"{path}: no score or calibration-copy dispatches")
+        per_kib = copy_bytes / (sum(copies) / len(copies) * 1024.0)
+        res[name] = {"score_kib_per_dispatch": sum(score) / len(score), "dispatches": len(score),
+                     "copy_kib_per_dispatch": sum(copies) / len(copies), "bytes_per_counter_kib": per_kib * 1024.0,
+                     "bytes_per_launch": sum(score) / len(score) * 1024.0 * per_kib}
+    return {"kernel": "score_bf16_kernel", "workload": "c3_pro_decode_b1_1m", "calibration_copy_bytes": copy_bytes,
+            "fetch": res["fetch"], "write": res["write"],
+            "traffic_bytes_per_launch": round(res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]),
+            "source_hash": score_source_hash()}
 
 
 def step_bytes(cfg) -> dict:
@@ -121,7 +182,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="BYTES",
+                    help="after the timed region, three plain device copies of BYTES each "
+                         "(reference dispatches for rocprofv3 --pmc byte counters)")
+    ap.add_argument("--parse-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
+                    help="turn the counter files of two --pmc runs into the traffic record")
     args = ap.parse_args()
+    if args.parse_pmc:
+        rec = parse_pmc(args.parse_pmc[0], args.parse_pmc[1], int(args.parse_pmc[2]))
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -198,7 +270,9 @@ def main():
         avg = sum(kern_ms) / len(kern_ms)
         ach = dom_bytes / (avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom_name,
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic() if dom == "index_score" and cfg.name == "c3_pro_decode_b1_1m" else None,
+                "kernel": dom_name,
                 "avg_launch_us": round(avg * 1e3, 3), "launches": len(kern_ms),
                 "algorithmic_bytes_per_launch": dom_bytes}
     tok_s = cfg.batch / (ms * 1e-3)
@@ -217,6 +291,14 @@ def main():
         "warm_ms_per_step_no_rotation": round(ms_warm, 5),
         "roofline": roof,
     }
+    if args.calibration_copy:
+        src = torch.empty(args.calibration_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, g, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -259,6 +259,24 @@ def decode_step(qi, wi, ki, q, pos0, o, idx, *, ratio: int, topk: int, pos_max: 
     return workspace
 
 
+class DecodeStepCall:
+    """A v4attn_decode_step call whose arguments are marshalled once: repeated calls on
+    the same tensors (a serving loop, a benchmark) pay only the C call."""
+
+    def __init__(self, qi, wi, ki, q, pos0, o, idx, *, ratio: int, topk: int, pos_max: int, workspace=None,
+                 **attn_kw):
+        ia, aa = _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw)
+        self._keep = (ia, aa)
+        if workspace is None:
+            workspace = _alloc_ws(int(lib().v4attn_decode_step_workspace(ia, aa)), q.device)
+        self.workspace = workspace
+        self._ws = _ws_ptr(workspace)
+        self._fn = lib().v4attn_decode_step
+
+    def __call__(self, stream=None):
+        _check(self._fn(self._keep[0], self._keep[1], self._ws[0], self._ws[1], _stream(stream)))
+
+
 # ---------------------------------------------------------------- kernel timing
 def timing_enable(kernel: str, max_launches: int) -> None:
     _check(lib().v4attn_timing_enable(KERNELS[kernel], max_launches))

@@ -315,13 +315,9 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
   const AttnP p = make_attn_params(a, P, ws);
   const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
-  timing_before(kid, s);
-  V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s), "attention launch"));
-  timing_after(kid, s);
+  V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
   if (P.splits > 1) {
-    timing_before(V4A_K_MERGE, s);
-    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s), "merge launch"));
-    timing_after(V4A_K_MERGE, s);
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s, V4A_K_MERGE), "merge launch"));
   }
   return ok();
 }
@@ -364,9 +360,7 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
 v4a_status launch_score_rows(const v4a_index_args* a, IndexLaunch& L, int64_t r0, int nr, hipStream_t stream) {
   L.sp.row0 = (int)r0;
   L.tp.row0 = (int)r0;
-  timing_before(V4A_K_INDEX_SCORE, stream);
-  V4A_TRY(hip_check(launch_score(a->dtype, L.sp, nr, (int)L.P.ntiles, stream), "index score launch"));
-  timing_after(V4A_K_INDEX_SCORE, stream);
+  V4A_TRY(hip_check(launch_score(a->dtype, L.sp, nr, (int)L.P.ntiles, stream, V4A_K_INDEX_SCORE), "index score launch"));
   return V4A_OK;
 }
 
@@ -377,9 +371,7 @@ v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStre
   for (int64_t r0 = 0; r0 < L.P.rows; r0 += L.P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(L.P.chunk_rows, L.P.rows - r0);
     V4A_TRY(launch_score_rows(a, L, r0, nr, stream));
-    timing_before(V4A_K_TOPK_SELECT, stream);
-    V4A_TRY(hip_check(launch_select(L.tp, nr, stream), "top-k select launch"));
-    timing_after(V4A_K_TOPK_SELECT, stream);
+    V4A_TRY(hip_check(launch_select(L.tp, nr, stream, V4A_K_TOPK_SELECT), "top-k select launch"));
   }
   return ok();
 }
@@ -467,9 +459,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   csa.split_base = (int)P.s_rest;
 
   auto attend = [&](const AttnP& ap) -> v4a_status {
-    timing_before(V4A_K_ATTN, s);
-    V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s), "attention launch"));
-    timing_after(V4A_K_ATTN, s);
+    V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s, V4A_K_ATTN), "attention launch"));
     return V4A_OK;
   };
   if (P.csa) {
@@ -479,9 +469,8 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
       V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
-      timing_before(V4A_K_SELECT_ATTN, s);
-      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s), "select+attention launch"));
-      timing_after(V4A_K_SELECT_ATTN, s);
+      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s, V4A_K_SELECT_ATTN),
+                        "select+attention launch"));
     } else {
       V4A_TRY(run_index(ix, ws, P.ix.ws_bytes, s));
       if (P.s_rest > 0) V4A_TRY(attend(rest));
@@ -491,9 +480,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     V4A_TRY(attend(rest));
   }
   if (P.s_total > 1) {
-    timing_before(V4A_K_MERGE, s);
-    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s), "merge launch"));
-    timing_after(V4A_K_MERGE, s);
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s, V4A_K_MERGE), "merge launch"));
   }
   return ok();
 }
@@ -502,15 +489,15 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
 
 // ---------------------------------------------------------------- timing (namespace v4a)
 namespace v4a {
-void timing_before(int k, hipStream_t s) {
+void timing_events(int k, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (k < 0 || k >= V4A_K_COUNT) return;
   std::lock_guard<std::mutex> lk(g_tmu);
   Timing& t = g_timing[k];
-  if (t.used < t.cap) (void)hipEventRecord(t.start[t.used], s);
-}
-void timing_after(int k, hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  Timing& t = g_timing[k];
-  if (t.used < t.cap) (void)hipEventRecord(t.stop[t.used++], s);
+  if (t.used < t.cap) {
+    *start = t.start[t.used];
+    *stop = t.stop[t.used++];
+  }
 }
 }  // namespace v4a
 
@@ -553,9 +540,7 @@ v4a_status v4attn_compress(const v4a_compress_args* a, hipStream_t stream) {
   p.g = std::max(1, std::min(a->ratio, 256 / p.ch));
   p.bpw = std::max(1, 256 / (p.ch * p.g));
   if (cdiv(nb, p.bpw) > INT32_MAX || a->batch > 65535) return fail(V4A_ENOTSUP, "launch too large");
-  timing_before(V4A_K_COMPRESS, stream);
-  V4A_TRY(hip_check(launch_compress(a->dtype, p, a->batch, stream), "compress launch"));
-  timing_after(V4A_K_COMPRESS, stream);
+  V4A_TRY(hip_check(launch_compress(a->dtype, p, a->batch, stream, V4A_K_COMPRESS), "compress launch"));
   return ok();
 }
 

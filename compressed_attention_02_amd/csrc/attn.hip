@@ -185,29 +185,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   }
 }
 
-hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s) {
+hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid) {
   const dim3 grid((unsigned)p.splits, (unsigned)nrows);
   if (dtype == 0) {
-    if (p.dim == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, s, p);
+    if (p.dim == 64) V4A_LAUNCH(tid, attn_f32_kernel<64>, grid, dim3(256), 0, s, p);
+    else V4A_LAUNCH(tid, attn_f32_kernel<128>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
   const int ntile = p.heads / 16;
   if (p.heads % 16 != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
   // 16 heads per wave up to 8 waves (128 heads); two waves per SIMD
   if (ntile <= 4) {
-    if (p.dim == 64) hipLaunchKernelGGL((attn_bf16_kernel<4, 1, 64>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<4, 1, 128>), grid, dim3(256), 0, s, p);
+    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<4, 1, 64>), grid, dim3(256), 0, s, p);
+    else V4A_LAUNCH(tid, (attn_bf16_kernel<4, 1, 128>), grid, dim3(256), 0, s, p);
   } else {
-    if (p.dim == 64) hipLaunchKernelGGL((attn_bf16_kernel<8, 1, 64>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<8, 1, 128>), grid, dim3(512), 0, s, p);
+    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64>), grid, dim3(512), 0, s, p);
+    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128>), grid, dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s) {
+hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid) {
   if (p.splits_total > kMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3(kMergeThreads), 0, s, p);
+  V4A_LAUNCH(tid, merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

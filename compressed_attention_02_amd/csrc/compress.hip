@@ -100,12 +100,12 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   }
 }
 
-hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s) {
+hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid) {
   const dim3 grid((unsigned)((p.nb + p.bpw - 1) / p.bpw), (unsigned)batch);
   if (dtype == 0)
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(256), 0, s, p);
+    V4A_LAUNCH(tid, compress_kernel<float>, grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    V4A_LAUNCH(tid, compress_kernel<uint16_t>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

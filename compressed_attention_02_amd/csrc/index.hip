@@ -180,17 +180,17 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
            p.rep_info + (int64_t)lr * p.info_rs + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
-hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s) {
+hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid) {
   const dim3 grid((unsigned)ntiles, (unsigned)nrows);
   if (dtype == 0) {
     const size_t lds = (size_t)(p.heads * p.dim + p.heads) * sizeof(float);
-    hipLaunchKernelGGL(score_f32_kernel, grid, dim3(256), lds, s, p);
+    V4A_LAUNCH(tid, score_f32_kernel, grid, dim3(256), lds, s, p);
     return hipGetLastError();
   }
   const int mt = p.heads / 16, ks = p.dim / 32;
   const dim3 pgrid((unsigned)p.wgs_per_row, (unsigned)nrows);
 #define V4A_SCORE_CASE(M, K) \
-  if (mt == M && ks == K) { hipLaunchKernelGGL((score_bf16_kernel<M, K>), pgrid, dim3(256), 0, s, p); return hipGetLastError(); }
+  if (mt == M && ks == K) { V4A_LAUNCH(tid, (score_bf16_kernel<M, K>), pgrid, dim3(256), 0, s, p); return hipGetLastError(); }
   V4A_SCORE_CASE(1, 1) V4A_SCORE_CASE(1, 2)
   V4A_SCORE_CASE(2, 1) V4A_SCORE_CASE(2, 2)
   V4A_SCORE_CASE(4, 1) V4A_SCORE_CASE(4, 2)
@@ -205,8 +205,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectP p) {
   select_row(p, blockIdx.x, sh);
 }
 
-hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)nrows), dim3(kSelThreads), 0, s, p);
+hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid) {
+  V4A_LAUNCH(tid, select_kernel, dim3((unsigned)nrows), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
 

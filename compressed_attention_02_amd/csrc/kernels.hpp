@@ -1,5 +1,6 @@
 // Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,7 +20,7 @@ struct CompressP {
   int g;          // row groups per block (threads sharing one block's rows)
   int bpw;        // blocks per workgroup
 };
-hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s);
+hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- indexer
 constexpr int kTile = 256;        // blocks per score tile
@@ -40,7 +41,7 @@ struct ScoreP {
   int heads, dim, ratio;
   int wgs_per_row;    // bf16 kernel: workgroups per row, each walking tiles with that stride
 };
-hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s);
+hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
 struct SelectP {
   const float* scores; const uint32_t* rep_key; const uint2* rep_info;
@@ -50,7 +51,7 @@ struct SelectP {
   int64_t sc_rs, key_rs, info_rs;
   int tq, row0, ratio, topk;
 };
-hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s);
+hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels
@@ -78,15 +79,24 @@ struct AttnP {
   int64_t key_lo, key_hi;
   int splits, keys_per_split, split_base, splits_total;
 };
-hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s);
-hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s);
+hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
+hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
 
 // selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
 // workgroups) in one launch
-hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s);
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- timing hooks
-void timing_before(int kernel, hipStream_t s);
-void timing_after(int kernel, hipStream_t s);
+// The next (start, stop) event pair of kernel id `tid` while timing is enabled for
+// it, else two nulls.  The launch records them itself (hipExtLaunchKernel), so they
+// bracket the kernel's execution and not the queue around it.
+void timing_events(int tid, hipEvent_t* start, hipEvent_t* stop);
+
+#define V4A_LAUNCH(TID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                               \
+  do {                                                                                        \
+    hipEvent_t v4a_e0_, v4a_e1_;                                                              \
+    ::v4a::timing_events(TID, &v4a_e0_, &v4a_e1_);                                            \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, v4a_e0_, v4a_e1_, 0, __VA_ARGS__); \
+  } while (0)
 
 }  // namespace v4a

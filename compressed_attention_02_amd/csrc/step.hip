@@ -32,14 +32,15 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   attn_block<8, 1, D>(ap, a % ap.splits, a / ap.splits, sm.attn);
 }
 
-hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s) {
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s,
+                              int tid) {
   const int64_t n = (int64_t)n_sel + (int64_t)ap.splits * n_rows;
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0)
     return hipErrorInvalidValue;
   if (ap.dim == 64)
-    hipLaunchKernelGGL(select_attn_kernel<64>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
+    V4A_LAUNCH(tid, select_attn_kernel<64>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
   else
-    hipLaunchKernelGGL(select_attn_kernel<128>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
+    V4A_LAUNCH(tid, select_attn_kernel<128>, dim3((unsigned)n), dim3(kSelThreads), 0, s, sp, ap, n_sel);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import CSA, HCA, SWA, compress, decode, decode_step, index_topk, prefill_chunk
+from . import CSA, HCA, SWA, DecodeStepCall, compress, decode, index_topk, prefill_chunk
 
 
 def to_device(arrays: dict, device="cuda") -> dict:
@@ -103,15 +103,19 @@ class LayerStep:
                           **self.attn_kwargs())
 
     def run_decode_step(self, stream=None):
-        """index_topk + decode as one v4attn_decode_step (decode only)."""
-        s, t = self.s, self.t
-        kw = self.attn_kwargs()
-        for k in ("idx", "csa_ratio", "topk", "pos_max"):
-            kw.pop(k)
-        csa = bool(s.branches & CSA)
-        self.ws_step = decode_step(t["qi"] if csa else None, t.get("wi"), t.get("ki"), t["q"], t["pos"], self.o,
-                                   self.idx, ratio=s.m, topk=s.topk, pos_max=self.pos_max,
-                                   workspace=getattr(self, "ws_step", None), stream=stream, **kw)
+        """index_topk + decode as one v4attn_decode_step (decode only); the call's
+        arguments are marshalled on first use and reused."""
+        if getattr(self, "_step_call", None) is None:
+            s, t = self.s, self.t
+            kw = self.attn_kwargs()
+            for k in ("idx", "csa_ratio", "topk", "pos_max"):
+                kw.pop(k)
+            csa = bool(s.branches & CSA)
+            self._step_call = DecodeStepCall(t["qi"] if csa else None, t.get("wi"), t.get("ki"), t["q"], t["pos"],
+                                             self.o, self.idx, ratio=s.m, topk=s.topk, pos_max=self.pos_max,
+                                             workspace=getattr(self, "ws_step", None), **kw)
+            self.ws_step = self._step_call.workspace
+        self._step_call(stream)
 
     def step(self, stream=None, fused=True):
         """The whole hot path of one step: compress (if the step compresses),
