@@ -172,6 +172,68 @@ def cpu_baseline(cfg, g, budget_s: float) -> dict:
                       f"input, fp64 NumPy oracle, {el:.1f} s"}
 
 
+def prefill_flops(cfg) -> dict:
+    """Algorithmic MFMA FLOPs of one prefill chunk: the indexer's QI.KI^T over every
+    visible block of every query, and QK^T + PV over every key of every query."""
+    B, T, p0 = cfg.batch, cfg.tq, cfg.pos
+    n_vis = sum((p0 + i + 1) // cfg.m for i in range(T))
+    keys = 0
+    for i in range(T):
+        p = p0 + i
+        keys += (min(cfg.topk, (p + 1) // cfg.m) if cfg.branches & 1 else 0) + \
+                ((p + 1) // cfg.m_hca if cfg.branches & 2 else 0) + (min(cfg.window, p + 1) if cfg.branches & 4 else 0)
+    return {"indexer": 2 * B * cfg.idx_heads * cfg.idx_dim * n_vis, "attention": 4 * B * cfg.heads * cfg.dim * keys}
+
+
+def bench_prefill(cfg, args):
+    """One step = compress the chunk + index_topk over its queries + prefill_chunk."""
+    import torch
+    import synth
+    import compressed_attention_02_amd as V
+    from compressed_attention_02_amd.layer import LayerShape, LayerStep, to_device
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = to_device(synth.generate(cfg), dev)
+    sets = [base, {k: v.clone() for k, v in base.items()}]   # two sets of ~0.45 GB each
+    steps = [LayerStep(LayerShape.of(cfg), t) for t in sets]
+    stream = torch.cuda.current_stream()
+    steps[0].step(stream)
+    steps[1].ws_index, steps[1].ws_attn = steps[0].ws_index, steps[0].ws_attn
+    K, W = min(args.steps, 10), min(args.warmup, 2)
+    for k in range(W):
+        steps[k % 2].step(stream)
+    torch.cuda.synchronize()
+    V.timing_reset()
+    for name in ("index_score", "topk_select", "prefill", "compress", "merge"):
+        V.timing_enable(name, 4 * K)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(K):
+        steps[k % 2].step(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    kern = {n: sum(V.timing_read(n)) / K for n in ("index_score", "topk_select", "prefill", "compress", "merge")}
+    V.timing_reset()
+    fl = prefill_flops(cfg)
+    sc = fl["indexer"] / (kern["index_score"] * 1e-3) / 1e12
+    line = {
+        "metric": "prefill tokens/s, 4096-token chunk at 1M ctx (compress + index_topk + prefill_chunk)",
+        "value": round(cfg.batch * cfg.tq / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) bf16 inputs, planted needles)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "chunk": cfg.tq, "context": cfg.pos,
+                   "heads": cfg.heads, "head_dim": cfg.dim, "topk": cfg.topk, "rotating_input_sets": 2},
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in kern.items()},
+        "mfma_flops_per_step": fl,
+        "step_mfma_frac": round((fl["indexer"] + fl["attention"]) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(sc, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(sc / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "score_bf16_kernel (indexer QI.KI^T over the chunk's queries)"},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,7 +269,8 @@ def main():
 
     cfg = synth.CONFIGS[args.config]
     if cfg.tq != 1:
-        raise SystemExit("bench.py times decode configurations")
+        bench_prefill(cfg, args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = synth.generate(cfg)
