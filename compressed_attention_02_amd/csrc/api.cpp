@@ -116,6 +116,7 @@ IndexPlan plan_index(const v4a_index_args* a) {
   // rows are processed in chunks whose scores fit in 1 GiB
   const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 8;
   P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
+
   P.off_keys = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
   P.off_info = P.off_keys + (size_t)round_up(P.chunk_rows * P.key_rs * 4, 256);
   P.ws_bytes = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 8, 256);

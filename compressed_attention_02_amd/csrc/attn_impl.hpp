@@ -109,19 +109,6 @@ __device__ __forceinline__ void key_src_any(const RowKeys& R, const int* s_idx, 
 template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
-// One 16-byte-per-lane load from global memory straight into LDS: lane l's bytes
-// land at LDS address lds + 16 l (lds wave-uniform).  Written as inline asm so that
-// the compiler's wait insertion does not treat every later LDS read as depending
-// on it; the code that consumes the data waits for it explicitly (s_waitcnt on
-// the vector-memory counter, then a workgroup barrier).  The instruction has no
-// register result, and the compiler's own waits can only get stricter for not
-// counting it, since vector-memory loads complete in issue order.
-__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 // row r of a table at base with row stride rs (elements): 32 x 32 -> 64-bit product
 __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_t r, int64_t rs) {
   return base + (uint64_t)r * (uint32_t)rs;

@@ -129,6 +129,19 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's bytes
+// land at LDS address lds + 16 l (lds wave-uniform).  Written as inline asm so that
+// the compiler's wait insertion does not treat every later LDS read as depending
+// on it; the code that consumes the data waits for it explicitly (s_waitcnt on
+// the vector-memory counter, then a workgroup barrier).  The instruction has no
+// register result, and the compiler's own waits can only get stricter for not
+// counting it, since vector-memory loads complete in issue order.
+__device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 // exp(x) with -inf -> 0
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
 

@@ -37,84 +37,82 @@ namespace v4a {
 // same 8 dims; C (16 heads x 16 blocks): lane holds block col, heads 4*grp + e.
 // The dims a lane group carries only have to agree between A and B.
 //
-// A workgroup walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of its row.
-// Tile loads are fully coalesced (each wave instruction reads 1 KiB of consecutive
-// block rows) into registers one tile ahead, then land in a padded LDS tile from
-// which the MFMA operands are read; the indexer queries are staged in LDS once.
-template <int MT, int KS>
+// A workgroup (4 waves) walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
+// its row.  A tile of 256 indexer keys goes from HBM straight into LDS (16 bytes per
+// lane per load; lane l's piece lands at base + 16 l), unpadded, with the 16-byte
+// pieces of row r permuted by XOR with swz_ki(r) so that both the loads and the
+// B-fragment reads (16 rows, one piece column) are free of bank conflicts.  QI and
+// the head weights stay in registers.  With NB = 2 the next tile loads while the
+// current one is scored.  Each wave scores 64 keys: ReLU, w-weighted head sum (row
+// swaps across the 4 lane groups), then its top-4 report.
+template <int DI> __device__ __forceinline__ int swz_ki(int r) { return DI == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+
+template <int MT, int KS, int NB>
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   constexpr int DI = KS * 32;
-  constexpr int ROWB = DI * 2 + 16;          // LDS bytes per block row (+16: conflict-free reads)
-  constexpr int CPR = DI * 2 / 16;           // 16-byte chunks per block row
-  constexpr int LPT = kTile * CPR / 256;     // 16-byte loads per thread per tile
-  __shared__ __align__(16) unsigned char sK[kTile * ROWB];
-  __shared__ __align__(16) uint16_t sA[MT * 16 * DI];
+  constexpr int ROWB = DI * 2;               // LDS bytes per key row
+  constexpr int CPR = DI * 2 / 16;           // 16-byte pieces per key row
+  constexpr int RPI = 64 / CPR;              // key rows per wave load
+  constexpr int IPW = kTile / RPI / 4;       // loads per wave per tile
+  __shared__ __align__(16) unsigned char sK[NB][kTile * ROWB];
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
-  const int64_t nvis = (pos + 1) / p.ratio;
+  const int64_t nvis = uniform_i64((pos + 1) / p.ratio);
   const int64_t ntile_row = (nvis + kTile - 1) / kTile;
   int64_t tile = blockIdx.x;
   if (tile >= ntile_row) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* ki = reinterpret_cast<const uint16_t*>(p.ki) + (int64_t)b * p.ki_bs;
 
-  uint4 pre[LPT];
-  auto fetch = [&](int64_t t) {
+  // rows past n_vis re-read the last visible row; their scores are dropped
+  auto issue = [&](int64_t t, unsigned char* buf) {
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = tid + u * 256;
-      const int r = e / CPR, c = e - r * CPR;
-      const int64_t j = t * kTile + r;
-      pre[u] = make_uint4(0, 0, 0, 0);
-      if (j < nvis) pre[u] = *reinterpret_cast<const uint4*>(ki + j * p.ki_rs + c * 8);
+    for (int u = 0; u < IPW; ++u) {
+      const int r0 = (wave * IPW + u) * RPI;
+      const int r = r0 + lane / CPR;
+      const int64_t j = min(t * kTile + r, nvis - 1);
+      lds_load16(ki + j * p.ki_rs + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(buf + r0 * ROWB));
     }
   };
-  fetch(tile);
-  {
-    const uint4* qi = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.qi) +
-                                                     (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs);
-    for (int e = tid; e < MT * 16 * DI / 8; e += 256) reinterpret_cast<uint4*>(sA)[e] = qi[e];
-  }
+  issue(tile, sK[0]);
+  if (NB == 2 && tile + gridDim.x < ntile_row) issue(tile + gridDim.x, sK[NB - 1]);
+
+  bf16x8_t A[MT][KS];
   float w[MT][4];
   {
-    const float4* wi = reinterpret_cast<const float4*>(p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs);
+    const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
+    const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float4 v = wi[mt * 4 + grp];
-      w[mt][0] = v.x; w[mt][1] = v.y; w[mt][2] = v.z; w[mt][3] = v.w;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        A[mt][s] = *reinterpret_cast<const bf16x8_t*>(qi + (mt * 16 + col) * DI + s * 32 + grp * 8);
+      const f32x4 wq = *reinterpret_cast<const f32x4*>(wi + mt * 16 + 4 * grp);
+      w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
     }
   }
-  __syncthreads();
-  bf16x8_t A[MT][KS];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      A[mt][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&sA[(mt * 16 + col) * DI + s * 32 + grp * 8]));
 
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
-  for (; tile < ntile_row; tile += gridDim.x) {
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int e = tid + u * 256;
-      const int r = e / CPR, c = e - r * CPR;
-      *reinterpret_cast<uint4*>(sK + r * ROWB + c * 16) = pre[u];
-    }
+  const int kx = swz_ki<DI>(col);          // rows 16u + col of a wave share col's XOR
+  for (int c = 0; tile < ntile_row; tile += gridDim.x, ++c) {
+    const unsigned char* buf = sK[NB == 2 ? (c & 1) : 0];
+    const bool next = NB == 2 && tile + gridDim.x < ntile_row;
+    if (next) __builtin_amdgcn_s_waitcnt(0x0F70 | IPW);  // vmcnt(IPW): the next tile may stay in flight
+    else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
     __syncthreads();
-    if (tile + gridDim.x < ntile_row) fetch(tile + gridDim.x);
     const int64_t tile0 = tile * kTile;
-    float mine = 0.f;       // score of block tile0 + 64*wave + lane after the loop
+    float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = wave * 64 + u * 16 + col;     // block of this lane's column
+      const int t = wave * 64 + u * 16 + col;     // key row of this lane's column
       float part = 0.f;
       bf16x8_t Bv[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        Bv[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sK + t * ROWB + (s * 4 + grp) * 16));
+        Bv[s] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s * 4 + grp) ^ kx) * 16));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -132,7 +130,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     wave_top(j < nvis ? pack_kid(score_key(mine), (uint32_t)j) : 0ull, (uint32_t)(tile0 + wave * 64),
              p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
              p.rep_info + (int64_t)lr * p.info_rs + tile * 4 + wave);
-    __syncthreads();       // sK is rewritten by the next tile
+    __syncthreads();       // the buffer is reloaded next
+    if (NB == 2 && tile + 2 * (int64_t)gridDim.x < ntile_row)
+      issue(tile + 2 * (int64_t)gridDim.x, sK[NB == 2 ? (c & 1) : 0]);
   }
 }
 
@@ -188,9 +188,17 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
     return hipGetLastError();
   }
   const int mt = p.heads / 16, ks = p.dim / 32;
+  ScoreP q = p;
+  q.nrows = nrows;
   const dim3 pgrid((unsigned)p.wgs_per_row, (unsigned)nrows);
-#define V4A_SCORE_CASE(M, K) \
-  if (mt == M && ks == K) { V4A_LAUNCH(tid, (score_bf16_kernel<M, K>), pgrid, dim3(256), 0, s, p); return hipGetLastError(); }
+  // a second tile buffer only when workgroups walk several tiles
+  const bool two = (int64_t)p.wgs_per_row < ntiles;
+#define V4A_SCORE_CASE(M, K)                                                                             \
+  if (mt == M && ks == K) {                                                                              \
+    if (two) V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 2>), pgrid, dim3(256), 0, s, q);                  \
+    else V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 1>), pgrid, dim3(256), 0, s, q);                      \
+    return hipGetLastError();                                                                            \
+  }
   V4A_SCORE_CASE(1, 1) V4A_SCORE_CASE(1, 2)
   V4A_SCORE_CASE(2, 1) V4A_SCORE_CASE(2, 2)
   V4A_SCORE_CASE(4, 1) V4A_SCORE_CASE(4, 2)

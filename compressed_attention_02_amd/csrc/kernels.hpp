@@ -39,7 +39,8 @@ struct ScoreP {
   int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs, key_rs, info_rs;
   int tq, row0;       // launch covers global rows row0 + blockIdx.y; row = b*tq + i
   int heads, dim, ratio;
-  int wgs_per_row;    // bf16 kernel: workgroups per row, each walking tiles with that stride
+  int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
+  int nrows;          // rows of the launch (set by launch_score)
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
