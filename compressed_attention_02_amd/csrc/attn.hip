@@ -27,11 +27,12 @@
 
 namespace v4a {
 
-// One workgroup of NW waves per (split, row), two workgroups per CU when NW <= 4.
-template <int NW, int HT, int D>
-__global__ __launch_bounds__(NW * 64, NW * HT <= 4 ? 2 : 1) void attn_bf16_kernel(AttnP p) {
+// One workgroup of NW waves per (split, row); two workgroups per CU when each wave
+// computes one head tile over half the keys (KP = 2) or NW <= 4.
+template <int NW, int HT, int D, int KP>
+__global__ __launch_bounds__(NW * 64, KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1) void attn_bf16_kernel(AttnP p) {
   __shared__ __align__(16) AttnSmem<D> sm;
-  attn_block<NW, HT, D>(p, blockIdx.x, blockIdx.y, sm);
+  attn_block<NW, HT, D, KP>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -194,13 +195,14 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   }
   const int ntile = p.heads / 16;
   if (p.heads % 16 != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
-  // 16 heads per wave up to 8 waves (128 heads); two waves per SIMD
+  // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
+  // chunk's keys in half (four waves per SIMD); above, one wave per head tile
   if (ntile <= 4) {
-    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<4, 1, 64>), grid, dim3(256), 0, s, p);
-    else V4A_LAUNCH(tid, (attn_bf16_kernel<4, 1, 128>), grid, dim3(256), 0, s, p);
+    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64, 2>), grid, dim3(512), 0, s, p);
+    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128, 2>), grid, dim3(512), 0, s, p);
   } else {
-    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64>), grid, dim3(512), 0, s, p);
-    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128>), grid, dim3(512), 0, s, p);
+    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64, 1>), grid, dim3(512), 0, s, p);
+    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128, 1>), grid, dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }

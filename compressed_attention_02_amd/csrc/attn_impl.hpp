@@ -172,17 +172,19 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
 //     kLazyRescale (base 2); until then exp2(x - m) <= 2^8 and O, l need no
 //     rescaling.  (m, l, O) stay consistent, which is all that finishing and
 //     merging need.
-template <int D, int HT>
+template <int D, int HT, int KP>
 __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t* sV, const float* sBias,
                                              const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
-                                             float (&m_run)[HT], float (&l_run)[HT], float sl2, int col, int grp) {
+                                             float (&m_run)[HT], float (&l_run)[HT], float sl2, int col, int grp,
+                                             int kh) {
   constexpr int KS = D / 32, DT = D / 16;
-  f32x4 S[HT][4];
+  constexpr int NKT = 4 / KP;     // tiles of 16 keys of this wave: its part kh of the chunk
+  f32x4 S[HT][NKT];
   // K fragment: row 16kt + col, piece 4s + grp; the row's XOR does not depend on kt
-  const uint16_t* kb = sK + col * D;
+  const uint16_t* kb = sK + col * D + 16 * NKT * kh * D;
   const int kx = swz_k<D>(col);
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
     for (int t = 0; t < HT; ++t) S[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -196,8 +198,8 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   float cm[HT];
   bool need = false;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * kt + 4 * grp]);
+  for (int kt = 0; kt < NKT; ++kt) {
+    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * (NKT * kh + kt) + 4 * grp]);
 #pragma unroll
     for (int t = 0; t < HT; ++t)
 #pragma unroll
@@ -207,7 +209,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   for (int t = 0; t < HT; ++t) {
     float c = fmaxf(fmaxf(S[t][0][0], S[t][0][1]), fmaxf(S[t][0][2], S[t][0][3]));
 #pragma unroll
-    for (int kt = 1; kt < 4; ++kt)
+    for (int kt = 1; kt < NKT; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) c = fmaxf(c, S[t][kt][e]);
     cm[t] = col_max4(c);
@@ -235,7 +237,8 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   const int vx = swz_v<D>(vr);
   const uint16_t* vb = sV + vr * D + (col & 1) * 4;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int k2 = 0; k2 < 2 / KP; ++k2) {
+    const int kk = (2 / KP) * kh + k2;   // 32-key half of the chunk
     // P^T of keys 32kk + {4grp+e, 16+4grp+e} (tiles 2kk, 2kk+1) as bf16 hi + lo
     bf16x8_t Bhi[HT], Blo[HT];
 #pragma unroll
@@ -243,7 +246,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_exp2f(S[t][2 * kk + (e >> 2)][e & 3] - mu[t]);
+        const float v = __builtin_amdgcn_exp2f(S[t][2 * k2 + (e >> 2)][e & 3] - mu[t]);
         ps += v;
         const __bf16 h = (__bf16)v;
         Bhi[t][e] = h;
@@ -270,33 +273,32 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
 // are in flight while chunk c is computed.  The waits count the direct loads (2 *
 // IPW per lane per chunk) that may stay outstanding; everything issued before the
 // first chunk (q, ids) is older and therefore settled by the first wait.
-template <int NW, int D, int HT>
+template <int NW, int D, int HT, int KP>
 __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, uint16_t* K0, uint16_t* V0, float* B0,
                                            uint16_t* K1, uint16_t* V1, float* B1, int64_t nch, bool active,
                                            const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
-                                           float (&m_run)[HT], float (&l_run)[HT], float sl2, int wave, int lane) {
+                                           float (&m_run)[HT], float (&l_run)[HT], float sl2, int wave, int lane,
+                                           int kh) {
   constexpr int CH = kAttnChunk;
   constexpr int IPW = CH / (64 / (D / 8)) / NW;  // direct loads per wave per chunk, for K and for V
   const int col = lane & 15, grp = lane >> 4;
   if (nch > 0) issue_chunk<NW, D>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
   if (nch > 1) issue_chunk<NW, D>(R, s_idx, R.k_begin + CH, K1, V1, B1, wave, lane);
   // chunk c is computed while chunk c + 1 (if any) loads; the wait before chunk c
-  // leaves only chunk c + 1's loads outstanding, so the last chunk waits for all
-  for (int64_t c = 0; c < nch; c += 2) {
+  // leaves only chunk c + 1's loads outstanding, so the last chunk waits for all.
+  // One body for both buffers (the buffer is a uniform base): the per-lane LDS
+  // offsets are kept once, not once per buffer.
+  for (int64_t c = 0; c < nch; ++c) {
     if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // vmcnt(2 * IPW)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
     __syncthreads();
-    if (active) attend_chunk<D, HT>(K0, V0, B0, Qb, O, m_run, l_run, sl2, col, grp);
+    const bool odd = (c & 1) != 0;
+    uint16_t* Kc = odd ? K1 : K0;
+    uint16_t* Vc = odd ? V1 : V0;
+    float* Bc = odd ? B1 : B0;
+    if (active) attend_chunk<D, HT, KP>(Kc, Vc, Bc, Qb, O, m_run, l_run, sl2, col, grp, kh);
     __syncthreads();
-    if (c + 2 < nch) issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 2) * CH, K0, V0, B0, wave, lane);
-    if (c + 1 < nch) {
-      if (c + 2 < nch) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // vmcnt(2 * IPW)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
-      __syncthreads();
-      if (active) attend_chunk<D, HT>(K1, V1, B1, Qb, O, m_run, l_run, sl2, col, grp);
-      __syncthreads();
-      if (c + 3 < nch) issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 3) * CH, K1, V1, B1, wave, lane);
-    }
+    if (c + 2 < nch) issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
   }
 }
 
@@ -304,18 +306,30 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
 // CSA ids.
 template <int D>
 struct AttnSmem {
-  uint16_t K0[kAttnChunk * D], K1[kAttnChunk * D];
-  uint16_t V0[kAttnChunk * D], V1[kAttnChunk * D];
+  union {
+    struct {
+      uint16_t K0[kAttnChunk * D], K1[kAttnChunk * D];
+      uint16_t V0[kAttnChunk * D], V1[kAttnChunk * D];
+    };
+    // after the last chunk: the state (O, m, l) one key half hands to the other,
+    // per lane of 4 waves
+    float C[4 * 64 * (D / 4 + 2)];
+  };
   float B0[kAttnChunk], B1[kAttnChunk];
   int idx[kMaxTopk];
 };
 
-// The work of one workgroup of NW waves on (split, row).  Wave w computes head tiles w, w + NW,
-// ... (HT of them); a tile past the head count is computed on a copy of tile 0's
-// queries and not written.  All waves load.  Chunks are double-buffered in LDS:
-// the loads of chunk c + 1 are in flight while chunk c is computed.
-template <int NW, int HT, int D>
+// The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
+// head tiles w, w + NW, ... (HT of them); with KP = 2 (HT = 1), waves w and
+// w + NW/2 share head tile w and take one half of every chunk's keys each, and
+// combine their softmax states through LDS at the end.  A tile past the head count
+// is computed on a copy of tile 0's queries and not written.  All waves load.
+// Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
+// chunk c is computed.
+template <int NW, int HT, int D, int KP>
 __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, AttnSmem<D>& sm) {
+  static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
+  constexpr int TW = NW / KP;   // waves per key part: head tiles of one pass
   constexpr int NT = NW * 64, CH = kAttnChunk, KS = D / 32, DT = D / 16;
   int* s_idx = sm.idx;
   const int b = row / p.tq, i = row - b * p.tq;
@@ -332,9 +346,10 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs;
   int tile[HT];
   bf16x8_t Qb[HT][KS];
+  const int kh = KP == 2 ? wave / TW : 0;
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    tile[t] = wave + NW * t;
+    tile[t] = wave % TW + TW * t;
     const int tq = tile[t] < ntile ? tile[t] : 0;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -386,12 +401,38 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  run_chunks<NW, D, HT>(R, s_idx, sm.K0, sm.V0, sm.B0, sm.K1, sm.V1, sm.B1, nch, tile[0] < ntile, Qb, O, m_run, l_run, sl2, wave,
-                    lane);
+  run_chunks<NW, D, HT, KP>(R, s_idx, sm.K0, sm.V0, sm.B0, sm.K1, sm.V1, sm.B1, nch, tile[0] < ntile, Qb, O, m_run,
+                            l_run, sl2, wave, lane, kh);
+
+  if constexpr (KP == 2) {
+    // the second key half hands (O, m, l) to the first through LDS; the chunk
+    // buffers are free (every chunk's reads ended at a barrier, no load in flight)
+    static_assert(TW <= 4, "combine buffer holds 4 waves");
+    f32x4* sO = reinterpret_cast<f32x4*>(sm.C);
+    float* sM = sm.C + 4 * 64 * (D / 4);
+    const int slot = (wave % TW) * 64 + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) sO[dt * TW * 64 + slot] = O[0][dt];
+      sM[slot] = m_run[0];
+      sM[TW * 64 + slot] = l_run[0];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = sM[slot], l1 = sM[TW * 64 + slot];
+      const float m = fmaxf(m_run[0], m1);
+      const float a0 = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      m_run[0] = m;
+      l_run[0] = l_run[0] * a0 + l1 * a1;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[0][dt] = O[0][dt] * a0 + sO[dt * TW * 64 + slot] * a1;
+    }
+  }
 
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    if (tile[t] >= ntile) continue;
+    if (tile[t] >= ntile || kh != 0) continue;
     const int head = tile[t] * 16 + col;
     const float l = col_sum4(l_run[t]);
     if (p.splits_total == 1) {
