@@ -93,8 +93,11 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, ctypes.c_void_p]
         L.v4attn_decode_step_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs)]
         L.v4attn_decode_step_workspace.restype = ctypes.c_size_t
+        L.v4attn_set_wait_limit_us.argtypes = [ctypes.c_int64]
+        L.v4attn_set_one_launch_step.argtypes = [ctypes.c_int]
+        L.v4attn_set_one_launch_step.restype = None
         for name in ("v4attn_compress", "v4attn_index_topk", "v4attn_decode", "v4attn_prefill_chunk",
-                     "v4attn_decode_step", "v4attn_timing_enable"):
+                     "v4attn_decode_step", "v4attn_timing_enable", "v4attn_set_wait_limit_us"):
             getattr(L, name).restype = ctypes.c_int
         L.v4attn_status_string.argtypes = [ctypes.c_int]
         L.v4attn_status_string.restype = ctypes.c_char_p
@@ -278,6 +281,16 @@ class DecodeStepCall:
 
 
 # ---------------------------------------------------------------- kernel timing
+def set_wait_limit_us(us: int) -> None:
+    """Bound of each wait between workgroups of the one-launch decode step."""
+    _check(lib().v4attn_set_wait_limit_us(int(us)))
+
+
+def set_one_launch_step(enable: bool) -> None:
+    """Let the decode step run as one launch when its grid fits the chip."""
+    lib().v4attn_set_one_launch_step(1 if enable else 0)
+
+
 def timing_enable(kernel: str, max_launches: int) -> None:
     _check(lib().v4attn_timing_enable(KERNELS[kernel], max_launches))
 

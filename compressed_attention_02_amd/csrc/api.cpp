@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -355,6 +356,7 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;
   tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
   tp.sc_rs = P.sc_rs; tp.key_rs = P.key_rs; tp.info_rs = P.info_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
+  tp.ntiles_cap = (int)P.ntiles;
   return L;
 }
 
@@ -387,8 +389,13 @@ struct StepPlan {
   bool csa;
   IndexPlan ix;
   int64_t rows, n_rest, kps_rest, s_rest, s_csa, s_total;
-  size_t off_attn, ws_bytes;
+  size_t off_attn, off_sync, ws_bytes;
 };
+
+// Bound of each wait of the one-launch step, in ticks of the 100 MHz clock.
+std::atomic<int64_t> g_wait_ticks{100 * 200000};  // 200 ms
+// Whether a decode step whose grid fits the chip runs as one launch.
+std::atomic<int> g_one_launch{0};
 
 StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   StepPlan P{};
@@ -413,6 +420,9 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   P.off_attn = P.csa ? (size_t)round_up((int64_t)P.ix.ws_bytes, 256) : 0;
   P.ws_bytes = P.off_attn;
   if (P.s_total > 1) P.ws_bytes += (size_t)(P.rows * P.s_total * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
+  // per row {selection published, splits done} for the one-launch step
+  P.off_sync = (size_t)round_up((int64_t)P.ws_bytes, 256);
+  if (P.csa) P.ws_bytes = P.off_sync + (size_t)P.rows * 2 * sizeof(int);
   return P;
 }
 
@@ -469,9 +479,26 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     // rows fit one score pass and the attention is bf16
     const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
+      // the picks' attention and the merge join the launch when its workgroups are
+      // all resident at once (one per CU at most), since they wait on each other
+      AttnP csa_in = csa;
+      csa_in.sync = (int*)((char*)ws + P.off_sync);
+      const bool one_launch = g_one_launch.load() != 0 &&
+                              select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&
+                              P.s_total <= kStepMaxSplits;
+      if (one_launch) {
+        rest.sync = csa_in.sync;
+        rest.wait_ticks = csa_in.wait_ticks = g_wait_ticks.load();
+        csa_in.wait_idx = 1;
+        IL.sp.zero = csa_in.sync;
+        IL.sp.n_zero = (int)(2 * P.rows);
+      } else {
+        csa_in.sync = nullptr;
+      }
       V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
-      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s, V4A_K_SELECT_ATTN),
+      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, csa_in, (int)P.rows, s, V4A_K_SELECT_ATTN),
                         "select+attention launch"));
+      if (one_launch) return ok();
     } else {
       V4A_TRY(run_index(ix, ws, P.ix.ws_bytes, s));
       if (P.s_rest > 0) V4A_TRY(attend(rest));
@@ -506,6 +533,14 @@ void timing_events(int k, hipEvent_t* start, hipEvent_t* stop) {
 extern "C" {
 
 uint32_t v4attn_abi_version(void) { return V4ATTN_ABI_VERSION; }
+
+void v4attn_set_one_launch_step(int enable) { g_one_launch.store(enable ? 1 : 0); }
+
+v4a_status v4attn_set_wait_limit_us(int64_t us) {
+  if (us < 0 || us > (int64_t)3600 * 1000000) return fail(V4A_EINVAL, "wait limit out of range");
+  g_wait_ticks.store(us * 100);
+  return V4A_OK;
+}
 
 const char* v4attn_status_string(v4a_status s) {
   switch (s) {

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
       for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = acc[e] * f;
       if (lane == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
-      const int64_t slot = ((int64_t)row * p.splits_total + p.split_base + split) * p.heads + head;
+      const int64_t slot = ((int64_t)row * p.heads + head) * p.splits_total + p.split_base + split;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) p.part_o[slot * D + lane + 64 * e] = acc[e];
       if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_run);
@@ -115,75 +115,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 1024-thread workgroup per (row, head).  Split weights go to LDS; the weighted
-// sum over splits is spread over 1024/D thread groups, each summing its splits in
-// ascending order, and the groups are combined in LDS in a fixed order, so the
-// result does not depend on timing.
+// One 1024-thread workgroup per (row, head); merge_head holds the arithmetic.
 constexpr int kMergeThreads = 1024;
-constexpr int kMaxSplits = 1024;
-constexpr int kMergeBatch = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kMergeThreads];
-  const int row = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
-  const int b = row / p.tq, i = row - b * p.tq;
-  const int S = p.splits_total, D = p.dim;
-  const float* ml = p.part_ml + ((int64_t)row * S * p.heads + head) * 2;
-  const int64_t ml_step = (int64_t)p.heads * 2;
-  // thread (g, c) sums output column c over splits g, g+G, ... in ascending order;
-  // its first kMergeBatch partial values load together with the split statistics
-  const int G = kMergeThreads / D;
-  const int c = tid % D, g = tid / D;
-  const float* po = p.part_o + ((int64_t)row * S * p.heads + head) * D + c;
-  const int64_t po_step = (int64_t)p.heads * D;
-  float v[kMergeBatch];
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(g + u * G, S - 1) * po_step];
-  float ms = -INFINITY, ls = 0.f;
-  if (tid < S) {
-    const float2 m2 = *reinterpret_cast<const float2*>(ml + tid * ml_step);
-    ms = m2.x;
-    ls = m2.y;
-  }
-  // 1) global max of the split maxima (S <= kMergeThreads: one split per thread)
-  float mx = wave_max(ms);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  float M = s_red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-  __syncthreads();
-  // 2) split weights and the total sum
-  const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-  if (tid < S) s_w[tid] = wgt;
-  float part = wave_sum(wgt * ls);
-  if ((tid & 63) == 0) s_red[tid >> 6] = part;
-  __syncthreads();
-  float l = 0.f;
-  for (int w = 0; w < kMergeThreads / 64; ++w) l += s_red[w];
-  __syncthreads();
-  // 3) weighted sum of the partial outputs
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u)
-    if (g + u * G < S) acc = fmaf(s_w[g + u * G], v[u], acc);
-  for (int s0 = g + G * kMergeBatch; s0 < S; s0 += G * kMergeBatch) {
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(s0 + u * G, S - 1) * po_step];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      if (s0 + u * G < S) acc = fmaf(s_w[s0 + u * G], v[u], acc);
-  }
-  s_red[tid] = acc;
-  __syncthreads();
-  if (g == 0) {
-    float acc = s_red[c];
-    for (int gg = 1; gg < G; ++gg) acc += s_red[gg * D + c];
-    float lse;
-    const float f = finish_head(M, l, p.sink, head, &lse);
-    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + c] = acc * f;
-    if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
-  }
+  merge_head<kMergeThreads>(p, blockIdx.x, blockIdx.y, s_w, s_red);
 }
 
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid) {

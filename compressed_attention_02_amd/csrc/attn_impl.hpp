@@ -65,6 +65,224 @@ __device__ __forceinline__ float finish_head(float m, float l, const float* sink
   return l > 0.f ? scale_o / l : 0.f;
 }
 
+// ------------------------------------------------------------------ merge
+// Combination of one (row, head)'s split partials (U_s, m_s, l_s), m in base 2:
+// weights exp2(m_s - max m), o = sum w_s U_s / sum w_s l_s.  NT threads; split s's
+// statistics are read by thread s (splits_total <= NT).  The weighted sum is spread
+// over NT/D thread groups, each summing its splits in ascending order, and the groups
+// are combined in LDS in a fixed order, so the result does not depend on timing.
+// s_w holds splits_total floats, s_red NT.
+constexpr int kMaxSplits = 1024;
+constexpr int kMergeBatch = 16;
+
+template <int NT>
+__device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, float* s_w, float* s_red) {
+  const int tid = threadIdx.x;
+  const int b = row / p.tq, i = row - b * p.tq;
+  const int S = p.splits_total, D = p.dim;
+  const float* ml = p.part_ml + ((int64_t)row * p.heads + head) * S * 2;
+  const int64_t ml_step = 2;
+  // thread (g, c) sums output column c over splits g, g+G, ...; its first
+  // kMergeBatch partial values load together with the split statistics
+  const int G = NT / D;
+  const int c = tid % D, g = tid / D;
+  const float* po = p.part_o + ((int64_t)row * p.heads + head) * S * D + c;
+  const int64_t po_step = D;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(g + u * G, S - 1) * po_step];
+  float ms = -INFINITY, ls = 0.f;
+  if (tid < S) {
+    const float2 m2 = *reinterpret_cast<const float2*>(ml + tid * ml_step);
+    ms = m2.x;
+    ls = m2.y;
+  }
+  // 1) global max of the split maxima
+  const float mx = wave_max(ms);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  float M = s_red[0];
+  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
+  // 2) split weights and the total sum
+  const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+  if (tid < S) s_w[tid] = wgt;
+  const float part = wave_sum(wgt * ls);
+  if ((tid & 63) == 0) s_red[tid >> 6] = part;
+  __syncthreads();
+  float l = 0.f;
+  for (int w = 0; w < NT / 64; ++w) l += s_red[w];
+  __syncthreads();
+  // 3) weighted sum of the partial outputs
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    if (g + u * G < S) acc = fmaf(s_w[g + u * G], v[u], acc);
+  for (int s0 = g + G * kMergeBatch; s0 < S; s0 += G * kMergeBatch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(s0 + u * G, S - 1) * po_step];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (s0 + u * G < S) acc = fmaf(s_w[s0 + u * G], v[u], acc);
+  }
+  s_red[tid] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float a = s_red[c];
+    for (int gg = 1; gg < G; ++gg) a += s_red[gg * D + c];
+    float lse;
+    const float f = finish_head(M, l, p.sink, head, &lse);
+    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + c] = a * f;
+    if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+  }
+  __syncthreads();
+}
+
+// Merge of heads [h0, h0 + nh) of one row by one NT-thread workgroup with every
+// load of a pass in flight at once: the workgroup's G = NT/D column groups take up
+// to G heads per pass, gph = G/heads groups per head, each summing the splits sub,
+// sub + gph, ... of its head in ascending order, combined in LDS in group order.
+// The split statistics of the pass load together with the partials; the head
+// maxima come from LDS integer maxima of order-preserving keys (independent of
+// order), the sums l from one wave per head in a fixed lane order.  `lds` holds
+// kMergeLds(NT, D, splits_total) floats; splits_total <= kStepMaxSplits.
+constexpr int kMergeLoads = 48;     // partial values in flight per thread
+
+__host__ __device__ constexpr int kMergeLds(int nt, int d, int splits) {
+  return 2 * (nt / d) + (nt / d) * splits + ((nt / d) * splits > nt ? (nt / d) * splits : nt);
+}
+
+__device__ __forceinline__ uint32_t f2key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+template <int NT>
+__device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int nh, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = row / p.tq, i = row - b * p.tq;
+  const int S = p.splits_total, D = p.dim, H = p.heads, G = NT / D;
+  const int g = tid / D, c = tid % D;
+  uint32_t* s_mk = reinterpret_cast<uint32_t*>(lds);
+  float* s_l = lds + G;
+  float* s_w = lds + 2 * G;
+  float* s_wl = s_w + G * S;   // w*l per item; later the group sums
+  const float* part_o = p.part_o + (int64_t)row * S * H * D;
+  const float* part_ml = p.part_ml + (int64_t)row * S * H * 2;
+  constexpr int kStat = kStepMaxSplits * 8 / NT;  // statistics per thread (G <= 8)
+  for (int hb = 0; hb < nh; hb += G) {
+    const int nhp = min(G, nh - hb);
+    const int gph = G / nhp;
+    const int hs = min(g / gph, nhp - 1), sub = g % gph;
+    const bool act = g / gph < nhp;
+    const int h = h0 + hb + hs;
+    const int n_it = nhp * S;
+    // 1) every load of the pass: this thread's partial values and split statistics
+    const int nmine = (S - sub + gph - 1) / gph;
+    float v[kMergeLoads];
+#pragma unroll
+    for (int u = 0; u < kMergeLoads; ++u)
+      v[u] = part_o[((int64_t)h * S + min(sub + u * gph, S - 1)) * D + c];
+    float2 ml[kStat];
+#pragma unroll
+    for (int u = 0; u < kStat; ++u) {
+      const int q = min(tid + u * NT, n_it - 1);
+      ml[u] = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(h0 + hb + q / S) * S + q % S) * 2);
+    }
+    if (tid < G) s_mk[tid] = 0u;
+    __syncthreads();
+    // 2) head maxima
+#pragma unroll
+    for (int u = 0; u < kStat; ++u) {
+      const int t = tid + u * NT;
+      if (t < n_it) atomicMax(&s_mk[t / S], f2key(ml[u].x));
+    }
+    __syncthreads();
+    // 3) split weights and w*l per item, then l per head (wave hs, fixed order)
+#pragma unroll
+    for (int u = 0; u < kStat; ++u) {
+      const int t = tid + u * NT;
+      if (t < n_it) {
+        const float M = key2f(s_mk[t / S]);
+        const float w = (M == -INFINITY || ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
+        s_w[t] = w;
+        s_wl[t] = w * ml[u].y;
+      }
+    }
+    __syncthreads();
+    if (wave < nhp) {
+      float a = 0.f;
+      for (int sp = lane; sp < S; sp += 64) a += s_wl[wave * S + sp];
+      a = wave_sum(a);
+      if (lane == 0) s_l[wave] = a;
+    }
+    // 4) weighted sum of this thread's splits, ascending
+    float acc = 0.f;
+    for (int r0 = 0; r0 < nmine; r0 += kMergeLoads) {
+      if (r0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kMergeLoads; ++u)
+          v[u] = part_o[((int64_t)h * S + min(sub + (r0 + u) * gph, S - 1)) * D + c];
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeLoads; ++u)
+        if (r0 + u < nmine) acc = fmaf(s_w[hs * S + sub + (r0 + u) * gph], v[u], acc);
+    }
+    __syncthreads();
+    s_wl[tid] = acc;
+    __syncthreads();
+    if (act && sub == 0) {
+      float a = 0.f;
+      for (int q = 0; q < gph; ++q) a += s_wl[(g + q) * D + c];
+      float lse;
+      const float f = finish_head(key2f(s_mk[hs]), s_l[hs], p.sink, h, &lse);
+      p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a * f;
+      if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + h] = lse;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ one-launch step sync
+// Thread 0 polls *w with relaxed agent-scope loads (no cache maintenance per poll)
+// until *w >= target, at most `ticks` of the 100 MHz clock, then takes one
+// agent-scope acquire; the workgroup learns the outcome through *flag.  After a
+// successful wait the workgroup's later loads see what the releasing workgroups
+// wrote before their release.
+__device__ __forceinline__ bool wg_wait_ge(const int* w, int target, int64_t ticks, int* flag) {
+  if (threadIdx.x == 0) {
+    const int64_t t0 = wall_clock64();
+    bool ok = true;
+    while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (wall_clock64() - t0 > ticks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Every wave waits for its own memory operations to complete, then thread 0
+// releases them at agent scope with its add to *w (or store of 1 when `set`).
+__device__ __forceinline__ void wg_release(int* w, bool set) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (set) __hip_atomic_store(w, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_add(w, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA
 // Where the keys of one row come from.  Virtual key t < n_csa is CSA pick t (its
 // id read from the split's copy of the idx row in LDS), t < hca_end is HCA entry
@@ -317,6 +535,7 @@ struct AttnSmem {
   };
   float B0[kAttnChunk], B1[kAttnChunk];
   int idx[kMaxTopk];
+  int flag;
 };
 
 // The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
@@ -326,7 +545,7 @@ struct AttnSmem {
 // is computed on a copy of tile 0's queries and not written.  All waves load.
 // Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
 // chunk c is computed.
-template <int NW, int HT, int D, int KP>
+template <int NW, int HT, int D, int KP, bool STEP = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, AttnSmem<D>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   constexpr int TW = NW / KP;   // waves per key part: head tiles of one pass
@@ -355,9 +574,14 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
     for (int s = 0; s < KS; ++s)
       Qb[t][s] = *reinterpret_cast<const bf16x8_t*>(qrow + (tq * 16 + col) * D + s * 32 + grp * 8);
   }
+  // one-launch step: the picks are read only once the row's selection is published;
+  // if the wait gives up, the split attends nothing and reports NaN statistics
+  bool poison = false;
+  if constexpr (STEP)
+    if (p.sync && p.wait_idx) poison = !wg_wait_ge(p.sync + 2 * row, 1, p.wait_ticks, &sm.flag);
   const int64_t k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
   const int64_t n_csa = (p.mask & 1u) ? p.topk : 0;
-  const int64_t n_idx = min(min(n_csa, p.key_hi), k_begin + (int64_t)p.keys_per_split) - k_begin;
+  const int64_t n_idx = poison ? 0 : min(min(n_csa, p.key_hi), k_begin + (int64_t)p.keys_per_split) - k_begin;
   const int32_t* ip = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs + k_begin;
   constexpr int IDX_PER = kMaxTopk / NT;  // ids per thread: n_idx <= topk <= kMaxTopk
   int ids[IDX_PER];
@@ -371,7 +595,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   const KeyList L = key_list(p, pos);
   RowKeys R;
   R.k_begin = k_begin;
-  R.k_end = min(min(L.n_keys, p.key_hi), R.k_begin + (int64_t)p.keys_per_split);
+  R.k_end = poison ? R.k_begin : min(min(L.n_keys, p.key_hi), R.k_begin + (int64_t)p.keys_per_split);
   R.n_csa = L.n_csa;
   R.hca_end = L.n_csa + L.e_vis;
   R.raw_off = L.w_lo - R.hca_end - raw0;
@@ -445,13 +669,31 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
             make_float4(O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f);
       if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
-      const int64_t slot = ((int64_t)row * p.splits_total + p.split_base + split) * p.heads + head;
+      const int64_t slot = ((int64_t)row * p.heads + head) * p.splits_total + p.split_base + split;
       float* po = p.part_o + slot * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<float4*>(po + dt * 16 + 4 * grp) =
             make_float4(O[t][dt][0], O[t][dt][1], O[t][dt][2], O[t][dt][3]);
-      if (grp == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[t], l);
+      if (grp == 0)
+        *reinterpret_cast<float2*>(p.part_ml + slot * 2) = poison ? make_float2(NAN, NAN) : make_float2(m_run[t], l);
+    }
+  }
+
+  if (STEP && p.sync) {
+    // one-launch step: count this split done, wait for all of the row's splits, then
+    // merge heads [j hp, (j + 1) hp) of the row, j = this split's slot
+    wg_release(p.sync + 2 * row + 1, false);
+    const bool ok = wg_wait_ge(p.sync + 2 * row + 1, p.splits_total, p.wait_ticks, &sm.flag);
+    const int j = p.split_base + split;
+    const int hp = (p.heads + p.splits_total - 1) / p.splits_total;
+    const int hlo = min(p.heads, j * hp), h1 = min(p.heads, (j + 1) * hp);
+    static_assert(kMergeLds(NT, D, kStepMaxSplits) <= 4 * 64 * (D / 4 + 2), "merge scratch fits the chunk buffers");
+    if (ok) {
+      merge_heads<NT>(p, row, hlo, h1 - hlo, sm.C);
+    } else {
+      for (int h = hlo; h < h1; ++h)
+        if (tid < D) p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + tid] = NAN;
     }
   }
 }

@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   constexpr int RPI = 64 / CPR;              // key rows per wave load
   constexpr int IPW = kTile / RPI / 4;       // loads per wave per tile
   __shared__ __align__(16) unsigned char sK[NB][kTile * ROWB];
+  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
@@ -140,6 +142,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
 // One thread per block of the tile; the row's indexer queries and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
   extern __shared__ float s_q[];  // [heads*dim] then [heads]
+  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;

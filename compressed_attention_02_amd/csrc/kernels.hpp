@@ -41,6 +41,7 @@ struct ScoreP {
   int heads, dim, ratio;
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
   int nrows;          // rows of the launch (set by launch_score)
+  int* zero; int n_zero;  // words workgroup (0, 0) clears before anything else (null: none)
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
@@ -51,11 +52,13 @@ struct SelectP {
   float* sel; int64_t sel_bs, sel_rs;
   int64_t sc_rs, key_rs, info_rs;
   int tq, row0, ratio, topk;
+  int ntiles_cap;     // score tiles of the longest row (pos_max): bounds the report loads
 };
 hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels
+constexpr int kStepMaxSplits = 256;  // splits per row the one-launch decode step merges in-kernel
 constexpr int kAttnMaxSplits = 1024;
 
 struct AttnP {
@@ -67,8 +70,8 @@ struct AttnP {
   const int64_t* raw_start; const int64_t* pos0; const float* sink;
   float* o; int64_t o_bs, o_rs;
   float* lse; int64_t lse_bs, lse_rs;
-  float* part_o;   // [rows][splits][H][d]
-  float* part_ml;  // [rows][splits][H][2]
+  float* part_o;   // [rows][H][splits][d]: one head's splits contiguous for the merge
+  float* part_ml;  // [rows][H][splits][2]
   int tq, heads, dim;
   uint32_t mask;
   int m, mh, W, topk;
@@ -79,13 +82,22 @@ struct AttnP {
   // splits_total == 1 the launch writes o and lse directly.
   int64_t key_lo, key_hi;
   int splits, keys_per_split, split_base, splits_total;
+  // one-launch decode step only (null elsewhere): per row {idx ready, splits done}.
+  // A launch with wait_idx waits for its row's idx before reading it; with sync, every
+  // workgroup of a row counts itself done, waits for all splits_total and merges its
+  // share of the heads.  Each wait gives up after wait_ticks of the 100 MHz clock.
+  int* sync; int64_t wait_ticks; int wait_idx;
 };
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
 
 // selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
-// workgroups) in one launch
-hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s, int tid);
+// workgroups) in one launch; with csa (splits > 0, sync set) also the attention of
+// the picks and the merge, as one grid that must fit the chip at once
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int n_rows,
+                              hipStream_t s, int tid);
+// workgroups of the one-launch step; it needs every one resident at once
+int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows);
 
 // ---------------------------------------------------------------- timing hooks
 // The next (start, stop) event pair of kernel id `tid` while timing is enabled for

@@ -82,14 +82,19 @@ __device__ __forceinline__ void wave_top(uint64_t v, uint32_t wave_base, uint32_
 
 // ------------------------------------------------------------------ selection
 constexpr int kNW = kSelThreads / 64;
-constexpr int kBins = 4096;
+constexpr int kBins = 8192;
 
 struct SelShared {
-  uint32_t hist[kBins];
+  uint32_t hist[kBins + 64];   // + one slot per lane for branch-free passes to discard into
   uint32_t wtot[kNW];
   uint32_t wmin[kNW], wmax[kNW];
-  uint32_t pool_key[kPoolCap];
-  uint32_t pool_id[kPoolCap];
+  union {
+    uint32_t hist2[kBins];     // second level of the register search (zeroed up front)
+    struct {
+      uint32_t pool_key[kPoolCap];
+      uint32_t pool_id[kPoolCap];
+    };
+  };
   uint32_t fail[256], fcount[256], fbase[256];
   uint32_t n_pool, n_fail, flag;
   uint32_t hit_bin, hit_before;
@@ -126,8 +131,8 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared
 
 // Bin of sh.hist[0..nb) holding the r-th element (1-based) counted from the top
 // (descending) or from the bottom, and the count strictly before it.
-__device__ __forceinline__ void find_rank(SelShared& sh, int nb, uint32_t r, bool descending, uint32_t& bin,
-                          uint32_t& before) {
+__device__ __forceinline__ void find_rank(const uint32_t* hist, SelShared& sh, int nb, uint32_t r, bool descending,
+                                          uint32_t& bin, uint32_t& before) {
   constexpr int kMaxPer = kBins / kSelThreads;
   const int t = threadIdx.x;
   const int per = (nb + kSelThreads - 1) / kSelThreads;
@@ -136,7 +141,7 @@ __device__ __forceinline__ void find_rank(SelShared& sh, int nb, uint32_t r, boo
 #pragma unroll
   for (int e = 0; e < kMaxPer; ++e) {
     const int o = t * per + e;
-    c[e] = (e < per && o < nb) ? sh.hist[descending ? nb - 1 - o : o] : 0u;
+    c[e] = (e < per && o < nb) ? hist[descending ? nb - 1 - o : o] : 0u;
     sum += c[e];
   }
   const uint32_t incl = block_scan(sum, sh);
@@ -194,7 +199,7 @@ __device__ __forceinline__ uint32_t rank_search(Each each, Keep keep, Val val, u
     });
     __syncthreads();
     uint32_t bin, before;
-    find_rank(sh, nb, r, descending, bin, before);
+    find_rank(sh.hist, sh, nb, r, descending, bin, before);
     r -= before;
     const uint32_t nlo = lo + (bin << shift);
     const uint32_t nhi = (uint32_t)min<uint64_t>((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
@@ -234,7 +239,7 @@ __device__ __forceinline__ uint32_t kth_key_floor(Each each, uint32_t r, SelShar
   each([&](uint32_t key, uint32_t) { atomicAdd(&sh.hist[(key - lo) >> shift], 1u); });
   __syncthreads();
   uint32_t bin, before;
-  find_rank(sh, nb, r, true, bin, before);
+  find_rank(sh.hist, sh, nb, r, true, bin, before);
   return lo + (bin << shift);
 }
 
@@ -270,8 +275,71 @@ __device__ __forceinline__ void topk_threshold(Each each, uint32_t k, SelShared&
 __device__ __forceinline__ bool picked(uint32_t key, uint32_t id, uint32_t T, uint32_t id_max) {
   return key > T || (key == T && id <= id_max);
 }
+// the same as 0 / 1, without short-circuit branches
+__device__ __forceinline__ uint32_t picked_bits(uint32_t key, uint32_t id, uint32_t T, uint32_t id_max) {
+  return (uint32_t)(key > T) | ((uint32_t)(key == T) & (uint32_t)(id <= id_max));
+}
 
 constexpr int kMaxTilesPerThread = 3;
+
+// Rank search (descending) over the report keys held in registers, keys[q][j] for
+// q < tpt (0 = no element): as rank_search, but every pass is branch-free (an
+// element outside the live range adds into its lane's discard slot).
+__device__ __forceinline__ uint32_t reg_rank_search(const uint32_t (&keys)[kMaxTilesPerThread][kTileTop], int tpt,
+                                                    uint32_t& r, SelShared& sh, uint32_t& n_equal) {
+  const int lane = threadIdx.x & 63;
+  uint32_t mn = 0xffffffffu, mx = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxTilesPerThread; ++q) {
+    if (q >= tpt) break;
+#pragma unroll
+    for (int j = 0; j < kTileTop; ++j) {
+      const uint32_t v = keys[q][j];
+      mx = max(mx, v);
+      mn = min(mn, v ? v : 0xffffffffu);
+    }
+  }
+  uint32_t lo, hi;
+  block_minmax(mn, mx, sh, lo, hi);
+  n_equal = 0;
+  if (lo > hi) return lo;
+  for (int level = 0;; ++level) {
+    const uint64_t range = (uint64_t)hi - lo + 1;
+    int shift = 0;
+    while ((range >> shift) > (uint64_t)kBins) ++shift;
+    const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+    // levels 0 and 1 count into sh.hist and sh.hist2, which the caller zeroed
+    uint32_t* h = (level & 1) ? sh.hist2 : sh.hist;
+    if (level >= 2) {
+      for (int t = threadIdx.x; t < nb; t += kSelThreads) h[t] = 0;
+      __syncthreads();
+    }
+    const uint32_t span = hi - lo;
+#pragma unroll
+    for (int q = 0; q < kMaxTilesPerThread; ++q) {
+      if (q >= tpt) break;
+#pragma unroll
+      for (int j = 0; j < kTileTop; ++j) {
+        const uint32_t d = keys[q][j] - lo;   // wraps for keys below lo (and for 0)
+        atomicAdd(d <= span ? &h[d >> shift] : &sh.hist[kBins + lane], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t bin, before;
+    find_rank(h, sh, nb, r, true, bin, before);
+    r -= before;
+    const uint32_t nlo = lo + (bin << shift);
+    const uint32_t nhi = (uint32_t)min<uint64_t>((uint64_t)hi, (uint64_t)nlo + ((uint64_t)1 << shift) - 1);
+    const uint32_t in_bin = h[bin];
+    __syncthreads();
+    if (shift == 0 || r == in_bin) {   // one value left, or the bin is taken whole
+      n_equal = in_bin;
+      return nlo;
+    }
+    lo = nlo;
+    hi = nhi;
+  }
+}
 
 // Emits out[0..k) from the LDS pool (ascending ids) by an order-preserving
 // compaction of the picked entries; every thread owns a contiguous pool range.
@@ -296,12 +364,46 @@ __device__ __forceinline__ void emit_pool(SelShared& sh, uint32_t np, uint32_t k
 
 // The selection of row lr of the launch (one kSelThreads-thread workgroup).
 __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* RK = p.rep_key + (int64_t)lr * p.key_rs;
+  const uint2* RI = p.rep_info + (int64_t)lr * p.info_rs;
+  // thread t owns tiles [t*tpt, t*tpt + tpt) of the longest row; the report loads do
+  // not wait for the row's position (tiles past the row's own end are dropped below)
+  const int64_t ntc = p.ntiles_cap;
+  const int tpt = (int)min<int64_t>(kMaxTilesPerThread + 1, (ntc + kSelThreads - 1) / kSelThreads);
+  bool ok = tpt <= kMaxTilesPerThread;
+  uint4 rk[kMaxTilesPerThread][kTileTop / 4], ri[kMaxTilesPerThread][2];
+#pragma unroll
+  for (int q = 0; q < kMaxTilesPerThread; ++q) {
+    if (ok && q < tpt) {
+      const int64_t tl = min<int64_t>((int64_t)tid * tpt + q, ntc - 1);
+      const uint4* ks = reinterpret_cast<const uint4*>(RK + tl * kTileTop);
+      const uint4* is = reinterpret_cast<const uint4*>(RI + tl * 4);
+#pragma unroll
+      for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = ks[j];
+      ri[q][0] = is[0];
+      ri[q][1] = is[1];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = make_uint4(0u, 0u, 0u, 0u);
+      ri[q][0] = ri[q][1] = make_uint4(0xffffffffu, 0u, 0xffffffffu, 0u);
+    }
+  }
+  // the two histogram levels of the register search start at zero (cleared while
+  // the reports load; the search's first barrier orders this before any count)
+  {
+    u32x4* h1 = reinterpret_cast<u32x4*>(sh.hist);
+    u32x4* h2 = reinterpret_cast<u32x4*>(sh.hist2);
+    for (int t = tid; t < kBins / 4; t += kSelThreads) {
+      h1[t] = u32x4{0u, 0u, 0u, 0u};
+      h2[t] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   int b, i;
   int64_t pos;
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = (pos + 1) / p.ratio;
   const int k = p.topk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* out = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs;
   float* selp = p.sel ? p.sel + (int64_t)b * p.sel_bs + (int64_t)i * p.sel_rs : nullptr;
   const float* sc = p.scores + (int64_t)lr * p.sc_rs;
@@ -312,55 +414,37 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
     }
     return;
   }
-  const uint32_t* RK = p.rep_key + (int64_t)lr * p.key_rs;
-  const uint2* RI = p.rep_info + (int64_t)lr * p.info_rs;
   const int64_t ntiles = (nvis + kTile - 1) / kTile;
-  const int tpt = (int)min<int64_t>(kMaxTilesPerThread + 1, (ntiles + kSelThreads - 1) / kSelThreads);
-  bool ok = tpt <= kMaxTilesPerThread;
+  ok = ok && ntiles <= ntc;
 
-  // thread t owns tiles [t*tpt, t*tpt + tpt): report keys, packed id offsets (the id of
-  // entry j of tile t is t*256 + (j/4)*64 + offset) and the largest wave bound
+  // report keys, packed id offsets (the id of entry j of tile t is t*256 + (j/4)*64 +
+  // offset) and the largest wave bound of each owned tile
   uint32_t uk[kMaxTilesPerThread][kTileTop], uo[kMaxTilesPerThread][kTileTop / 4], ub[kMaxTilesPerThread];
   bool own[kMaxTilesPerThread];
   int64_t tbase[kMaxTilesPerThread];
-  {
-    // every load in flight before any of them is used: loads come from a valid tile
-    // (tpt is uniform, the tile clamp keeps them unconditional per lane); ownership is
-    // applied when unpacking
-    uint4 rk[kMaxTilesPerThread][kTileTop / 4], ri[kMaxTilesPerThread][2];
 #pragma unroll
-    for (int q = 0; q < kMaxTilesPerThread; ++q) {
-      const int64_t t = (int64_t)tid * tpt + q;
-      own[q] = ok && q < tpt && t < ntiles;
-      tbase[q] = t * kTile;
-      if (ok && q < tpt) {
-        const int64_t tl = min<int64_t>(t, ntiles - 1);
-        const uint4* ks = reinterpret_cast<const uint4*>(RK + tl * kTileTop);
-        const uint4* is = reinterpret_cast<const uint4*>(RI + tl * 4);
+  for (int q = 0; q < kMaxTilesPerThread; ++q) {
+    const int64_t t = (int64_t)tid * tpt + q;
+    own[q] = ok && q < tpt && t < ntiles;
+    tbase[q] = t * kTile;
 #pragma unroll
-        for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = ks[j];
-        ri[q][0] = is[0];
-        ri[q][1] = is[1];
-      } else {
-#pragma unroll
-        for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = make_uint4(0u, 0u, 0u, 0u);
-        ri[q][0] = ri[q][1] = make_uint4(0xffffffffu, 0u, 0xffffffffu, 0u);
-      }
+    for (int w = 0; w < kTileTop / 4; ++w) {
+      uk[q][4 * w] = rk[q][w].x; uk[q][4 * w + 1] = rk[q][w].y;
+      uk[q][4 * w + 2] = rk[q][w].z; uk[q][4 * w + 3] = rk[q][w].w;
     }
+    uo[q][0] = own[q] ? ri[q][0].x : 0xffffffffu;
+    uo[q][1] = own[q] ? ri[q][0].z : 0xffffffffu;
+    uo[q][2] = own[q] ? ri[q][1].x : 0xffffffffu;
+    uo[q][3] = own[q] ? ri[q][1].z : 0xffffffffu;
+    ub[q] = own[q] ? max(max(ri[q][0].y, ri[q][0].w), max(ri[q][1].y, ri[q][1].w)) : 0u;
+    // key 0 marks no element from here on
 #pragma unroll
-    for (int q = 0; q < kMaxTilesPerThread; ++q) {
-#pragma unroll
-      for (int w = 0; w < kTileTop / 4; ++w) {
-        uk[q][4 * w] = rk[q][w].x; uk[q][4 * w + 1] = rk[q][w].y;
-        uk[q][4 * w + 2] = rk[q][w].z; uk[q][4 * w + 3] = rk[q][w].w;
-      }
-      uo[q][0] = own[q] ? ri[q][0].x : 0xffffffffu;
-      uo[q][1] = own[q] ? ri[q][0].z : 0xffffffffu;
-      uo[q][2] = own[q] ? ri[q][1].x : 0xffffffffu;
-      uo[q][3] = own[q] ? ri[q][1].z : 0xffffffffu;
-      ub[q] = own[q] ? max(max(ri[q][0].y, ri[q][0].w), max(ri[q][1].y, ri[q][1].w)) : 0u;
-    }
+    for (int j = 0; j < kTileTop; ++j)
+      if (((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu) == 0xffu) uk[q][j] = 0u;
   }
+  auto rep_id = [&](int q, int j) -> uint32_t {
+    return (uint32_t)tbase[q] + 64u * (j / 4) + ((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu);
+  };
   auto eachOwn = [&](auto&& f) {
 #pragma unroll
     for (int q = 0; q < kMaxTilesPerThread; ++q)
@@ -370,63 +454,54 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
         if (own[q] && off != 0xffu) f(uk[q][j], (uint32_t)tbase[q] + 64u * (j / 4) + off);
       }
   };
-  // order-preserving copy of the reported elements that pass `keep` into the pool
-  auto pool_reports = [&](auto&& keep) -> uint32_t {
-    uint32_t c = 0;
-    eachOwn([&](uint32_t key, uint32_t id) { c += keep(key) ? 1u : 0u; });
-    const uint32_t incl = block_scan(c, sh);
-    if (tid == kSelThreads - 1) sh.n_pool = incl;
-    uint32_t o = incl - c;
-    eachOwn([&](uint32_t key, uint32_t id) {
-      if (keep(key)) {
-        if (o < (uint32_t)kPoolCap) { sh.pool_key[o] = key; sh.pool_id[o] = id; }
-        ++o;
-      }
-    });
-    __syncthreads();
-    return sh.n_pool;
-  };
+  // every wave of 64 visible blocks reports kWaveTop of them, a partial last wave
+  // as many as it has
+  const int64_t n_rep = kWaveTop * (nvis / 64) + min<int64_t>(kWaveTop, nvis % 64);
 
-  if (ok) {
-    // 1. a lower bound from the wave maxima (the k-th largest of any subset bounds the
-    //    row's k-th key from below)
-    uint32_t tau1 = 0;
-    if (ntiles * 4 >= k) {
-      tau1 = kth_key_floor(
-          [&](auto&& f) {
+  if (ok && n_rep >= k) {
+    // 1. the exact k-th key T of all the reports
+    uint32_t r = (uint32_t)k, n_tie;
+    const uint32_t T = reg_rank_search(uk, tpt, r, sh, n_tie);
+    // 2. no tile hides a key >= T: the reports hold every element >= T and their top-k
+    //    is the row's; compacted in id order from the registers through LDS
+    bool hides = false;
 #pragma unroll
-            for (int q = 0; q < kMaxTilesPerThread; ++q)
+    for (int q = 0; q < kMaxTilesPerThread; ++q) hides |= own[q] && ub[q] >= T;
+    if (!__syncthreads_or(hides) && T != 0u) {
+      uint32_t id_max = 0xffffffffu;
+      if (r < n_tie)
+        id_max = rank_search(eachOwn, [T](uint32_t key, uint32_t) { return key == T; },
+                             [](uint32_t, uint32_t id) { return id; }, r, false, sh, n_tie);
+      // branch-free per entry (id_max = ~0 when no cut falls inside the ties at T);
+      // keys of no element are 0 < T
+      uint32_t c = 0;
 #pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                uint32_t m = 0;
+      for (int q = 0; q < kMaxTilesPerThread; ++q) {
+        if (q >= tpt) break;
 #pragma unroll
-                for (int e = 0; e < kWaveTop; ++e) m = max(m, uk[q][w * kWaveTop + e]);
-                if (own[q]) f(m, 0u);
-              }
-          },
-          (uint32_t)k, sh);
-    }
-    // 2. the reported elements >= tau1, in id order
-    const uint32_t np = pool_reports([tau1](uint32_t key) { return key >= tau1; });
-    if (np <= (uint32_t)kPoolCap && np >= (uint32_t)k) {
-      // 3. the exact k-th key T of the reports
-      uint32_t r = (uint32_t)k, n_tie;
-      auto eachP = [&](auto&& f) { for (uint32_t t = tid; t < np; t += kSelThreads) f(sh.pool_key[t], sh.pool_id[t]); };
-      const uint32_t T = rank_search(eachP, [](uint32_t, uint32_t) { return true; },
-                                     [](uint32_t key, uint32_t) { return key; }, r, true, sh, n_tie);
-      // 4. no tile hides a key >= T: the reports hold every element >= T and their top-k
-      //    is the row's
-      bool hides = false;
-#pragma unroll
-      for (int q = 0; q < kMaxTilesPerThread; ++q) hides |= own[q] && ub[q] >= T;
-      if (!__syncthreads_or(hides)) {
-        uint32_t id_max = 0xffffffffu;
-        if (r < n_tie)
-          id_max = rank_search(eachP, [T](uint32_t key, uint32_t) { return key == T; },
-                               [](uint32_t, uint32_t id) { return id; }, r, false, sh, n_tie);
-        emit_pool(sh, np, (uint32_t)k, T, id_max, out, selp, sc);
-        return;
+        for (int j = 0; j < kTileTop; ++j) c += picked_bits(uk[q][j], rep_id(q, j), T, id_max);
       }
+      uint32_t o = block_scan(c, sh) - c;
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q) {
+        if (q >= tpt) break;
+#pragma unroll
+        for (int j = 0; j < kTileTop; ++j) {
+          const uint32_t id = rep_id(q, j);
+          const uint32_t pk = picked_bits(uk[q][j], id, T, id_max);
+          *(pk & (o < (uint32_t)k) ? &sh.pool_id[o] : &sh.hist[kBins + lane]) = id;
+          o += pk;
+        }
+      }
+      __syncthreads();
+      for (int t = tid; t < k; t += kSelThreads) {
+        const uint32_t id = sh.pool_id[t];
+        out[t] = (int32_t)id;
+        if (selp) selp[t] = sc[id];
+      }
+      return;
+    }
+    {
       // 5. some tiles may hide elements >= T: pool = reports >= T of the other tiles
       //    plus every element >= T of those tiles (rescanned), in id order
       if (tid == 0) sh.n_fail = 0;

@@ -6,8 +6,15 @@
 // the indexer picks.  The selection needs one workgroup per query row for several
 // microseconds, so the rest of the chip attends those keys meanwhile: workgroups
 // [0, n_sel) of the launch select (as select_kernel), the others attend a split of
-// the key range after the CSA picks (as attn_bf16_kernel).  One
-// launch on one stream: no cross-queue synchronisation.
+// the key range after the CSA picks (as attn_bf16_kernel).  One launch on one
+// stream: no cross-queue synchronisation.
+//
+// When the whole grid fits the chip at once, the launch also attends the picks and
+// merges: the selecting workgroup publishes its row (agent-scope release of a row
+// word), the workgroups of the picks wait for it before reading idx, and every
+// attention workgroup of the row counts itself done, waits for the row's last
+// split and merges a share of the heads.  Waits are bounded in time; a wait that
+// gives up leaves NaN in the outputs it owns rather than hang.
 #include "attn_impl.hpp"
 #include "select_impl.hpp"
 
@@ -20,31 +27,50 @@ union StepSmem {
 };
 
 template <int D, int KP>
-__global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, AttnP ap, int n_sel) {
+__global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, AttnP ap, AttnP csa, int n_sel,
+                                                                  int n_rest) {
   static_assert(kSelThreads == 8 * 64, "the attention workgroups run 8 waves");
   __shared__ __align__(16) StepSmem<D> sm;
   const int blk = blockIdx.x;
   if (blk < n_sel) {
     select_row(sp, blk, sm.sel);
+    if (ap.sync) wg_release(ap.sync + 2 * blk, true);  // publish the row's picks
     return;
   }
   const int a = blk - n_sel;
-  attn_block<8, 1, D, KP>(ap, a % ap.splits, a / ap.splits, sm.attn);
+  if (a < n_rest) {
+    attn_block<8, 1, D, KP, true>(ap, a % ap.splits, a / ap.splits, sm.attn);
+  } else {
+    const int c = a - n_rest;
+    attn_block<8, 1, D, KP, true>(csa, c % csa.splits, c / csa.splits, sm.attn);
+  }
 }
 
-hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s,
-                              int tid) {
-  const int64_t n = (int64_t)n_sel + (int64_t)ap.splits * n_rows;
+int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows) {
+  return (int64_t)n_sel + ((int64_t)ap.splits + (csa.sync ? csa.splits : 0)) * n_rows;
+}
+
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int n_rows,
+                              hipStream_t s, int tid) {
+  const int64_t n = select_attn_grid(n_sel, ap, csa, n_rows);
+  const int64_t n_rest = (int64_t)ap.splits * n_rows;
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0)
+    return hipErrorInvalidValue;
+  // with the picks attended in the same launch both parts carry the row words, the
+  // picks' part waits for the selection, and every split joins the merge
+  if ((ap.sync || csa.sync) && (csa.splits < 1 || ap.sync != csa.sync || !csa.wait_idx || ap.wait_idx ||
+                   ap.splits_total != ap.splits + csa.splits || csa.splits_total != ap.splits_total ||
+                   ap.splits_total > kStepMaxSplits))
     return hipErrorInvalidValue;
   // up to 64 heads, two waves per head tile take half of every chunk's keys each
   const dim3 g((unsigned)n), blk(kSelThreads);
+  const int nr = (int)n_rest;
   if (ap.heads <= 64) {
-    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 2>), g, blk, 0, s, sp, ap, n_sel);
-    else V4A_LAUNCH(tid, (select_attn_kernel<128, 2>), g, blk, 0, s, sp, ap, n_sel);
+    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 2>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    else V4A_LAUNCH(tid, (select_attn_kernel<128, 2>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
   } else {
-    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 1>), g, blk, 0, s, sp, ap, n_sel);
-    else V4A_LAUNCH(tid, (select_attn_kernel<128, 1>), g, blk, 0, s, sp, ap, n_sel);
+    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 1>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    else V4A_LAUNCH(tid, (select_attn_kernel<128, 1>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
   }
   return hipGetLastError();
 }

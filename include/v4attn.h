@@ -232,6 +232,13 @@ v4a_status v4attn_prefill_chunk(const v4a_attn_args* args, void* workspace,
  * workgroups of the launch that runs the top-k selection (which needs one
  * workgroup per query row); the CSA keys are attended once the selection is
  * done, and one merge combines both.  Everything runs on `stream`, in order.
+ * With v4attn_set_one_launch_step(1), when that launch, with one workgroup
+ * per split of the CSA keys added, has no more workgroups than the device has
+ * compute units, the CSA attention and the merge run inside it too: the
+ * workgroups wait for each other on per-row words in the workspace (cleared
+ * by the step's first kernel).  Each such wait is bounded
+ * (v4attn_set_wait_limit_us); one that gives up leaves NaN in the o values
+ * that depended on it instead of blocking the device.
  *   index   arguments of v4attn_index_topk with tq == 1; its idx is read by
  *           the attention.  Ignored (may be NULL) when attn has no CSA branch.
  *   attn    arguments of v4attn_decode.  With CSA: batch, pos0 and pos_max
@@ -252,6 +259,15 @@ v4a_status v4attn_decode_step(const v4a_index_args* index,
  * Status, version, diagnostics.
  * ------------------------------------------------------------------------- */
 const char* v4attn_status_string(v4a_status s);
+/* Whether v4attn_decode_step may run as one launch whose workgroups wait for
+ * each other (default 0: two launches).  It needs every workgroup of the
+ * launch resident at once, so leave it off where other work shares the GPU. */
+void v4attn_set_one_launch_step(int enable);
+/* Bound, in microseconds, of each wait between the workgroups of the one-launch
+ * decode step (default 200000); applies to steps enqueued after the call.
+ * V4A_EINVAL outside [0, 3600 s].  With 0, any wait not already satisfied gives
+ * up, which is how the failure path is tested. */
+v4a_status v4attn_set_wait_limit_us(int64_t us);
 /* Thread-local text of the last error raised by this thread ("" if none). */
 const char* v4attn_last_error(void);
 uint32_t v4attn_abi_version(void);

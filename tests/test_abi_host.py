@@ -211,3 +211,22 @@ def test_attention_rejects_huge_row_strides():
     big = 1 << 31
     r, msg = _st(V.lib().v4attn_decode, good_attn(kh=_T(FAKE, big * 4, big)), None, 0, None)
     assert r == ENOTSUP and msg
+
+
+def test_wait_limit_range():
+    L = V.lib()
+    assert L.v4attn_set_wait_limit_us(-1) == EINVAL
+    assert L.v4attn_set_wait_limit_us(3600 * 1000000 + 1) == EINVAL
+    assert L.v4attn_set_wait_limit_us(0) == 0
+    assert L.v4attn_set_wait_limit_us(200000) == 0
+    L.v4attn_set_one_launch_step(1)
+    L.v4attn_set_one_launch_step(0)
+
+
+def test_decode_step_workspace_holds_row_words():
+    # with CSA the step's workspace ends with two 32-bit words per row (selection
+    # published, splits done) after the 256-byte aligned partials
+    L = V.lib()
+    ix, a = good_index(), good_attn()
+    need = L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a))
+    assert need % 256 == a.batch * 8 % 256

@@ -12,13 +12,19 @@ from tests.gpu_harness import Run, sample_rows
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["stages", "decode_step"])
+@pytest.mark.parametrize("fused", [False, True, "one_launch"], ids=["stages", "decode_step", "one_launch"])
 @pytest.mark.parametrize("name", ["c2_flash_decode_b8_128k", "c3_pro_decode_b1_1m", "c4_hca_decode_b16_1m"])
 def test_full_decode_configs(name, fused):
-    # fused=True is the launch configuration bench.py times (v4attn_decode_step)
+    # fused=True is the launch configuration bench.py times (v4attn_decode_step);
+    # "one_launch" is the same step with the one-launch form switched on
+    import compressed_attention_02_amd as V
     cfg = C.CONFIGS[name]
     print(f"[case] full {name} fused={fused}", flush=True)
-    r = Run(cfg).run(fused=fused).check_all()
+    V.set_one_launch_step(fused == "one_launch")
+    try:
+        r = Run(cfg).run(fused=bool(fused)).check_all()
+    finally:
+        V.set_one_launch_step(False)
     # planted needles are selected (structural: they carry +3 sigma of relevance)
     if cfg.needles:
         import numpy as np
