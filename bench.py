@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="let the decode step run as one launch (workgroups wait for each other)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="BYTES",
                     help="after the timed region, three plain device copies of BYTES each "
                          "(reference dispatches for rocprofv3 --pmc byte counters)")
@@ -271,6 +273,7 @@ def main():
     if cfg.tq != 1:
         bench_prefill(cfg, args)
         return
+    V.set_one_launch_step(args.one_launch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = synth.generate(cfg)
@@ -347,7 +350,8 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "context": cfg.pos, "heads": cfg.heads,
                    "head_dim": cfg.dim, "csa_ratio": cfg.m, "topk": cfg.topk, "hca_ratio": cfg.m_hca,
                    "window": cfg.window, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim}",
-                   "step": cfg.timed, "rotating_input_sets": R},
+                   "step": cfg.timed, "rotating_input_sets": R,
+                   "step_form": "one_launch" if args.one_launch else "two_launch"},
         "hbm_gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,

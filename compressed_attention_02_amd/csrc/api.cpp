@@ -422,7 +422,7 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   if (P.s_total > 1) P.ws_bytes += (size_t)(P.rows * P.s_total * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
   // per row {selection published, splits done} for the one-launch step
   P.off_sync = (size_t)round_up((int64_t)P.ws_bytes, 256);
-  if (P.csa) P.ws_bytes = P.off_sync + (size_t)P.rows * 2 * sizeof(int);
+  if (P.csa) P.ws_bytes = P.off_sync + (size_t)P.rows * kRowWords * sizeof(int);
   return P;
 }
 
@@ -479,21 +479,31 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     // rows fit one score pass and the attention is bf16
     const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
-      // the picks' attention and the merge join the launch when its workgroups are
-      // all resident at once (one per CU at most), since they wait on each other
+      // in the one-launch form (the whole grid resident at once, at most one
+      // workgroup per CU) the picks' attention and the merge join the launch; the
+      // rest of each row, done early, pre-merges in-kernel meanwhile
+      int* words = (int*)((char*)ws + P.off_sync);
       AttnP csa_in = csa;
-      csa_in.sync = (int*)((char*)ws + P.off_sync);
-      const bool one_launch = g_one_launch.load() != 0 &&
+      csa_in.sync = words;
+      const bool one_launch = g_one_launch.load() != 0 && P.s_rest >= 2 &&
                               select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&
                               P.s_total <= kStepMaxSplits;
-      if (one_launch) {
-        rest.sync = csa_in.sync;
-        rest.wait_ticks = csa_in.wait_ticks = g_wait_ticks.load();
-        csa_in.wait_idx = 1;
-        IL.sp.zero = csa_in.sync;
-        IL.sp.n_zero = (int)(2 * P.rows);
-      } else {
-        csa_in.sync = nullptr;
+      const bool premerge = one_launch;
+      csa_in.sync = nullptr;
+      if (premerge) {
+        const int64_t ticks = g_wait_ticks.load();
+        rest.sync = words;
+        rest.wait_ticks = ticks;
+        rest.premerge = 1;
+        p.merge_lo = rest.merge_lo = csa.merge_lo = csa_in.merge_lo = (int)P.s_rest - 1;
+        IL.sp.zero = words;
+        IL.sp.n_zero = (int)(kRowWords * P.rows);
+        if (one_launch) {
+          csa_in.sync = words;
+          csa_in.wait_ticks = ticks;
+          csa_in.wait_idx = 1;
+          rest.final_merge = csa_in.final_merge = 1;
+        }
       }
       V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
       V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, csa_in, (int)P.rows, s, V4A_K_SELECT_ATTN),

@@ -115,13 +115,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 1024-thread workgroup per (row, head); merge_head holds the arithmetic.
-constexpr int kMergeThreads = 1024;
+// One 256-thread workgroup per (row, head, 32 output columns): the merge reads every
+// partial once, so it is spread over as many workgroups as there are column
+// slices to keep all CUs loading; merge_head holds the arithmetic.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeCols = 32;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kMergeThreads];
-  merge_head<kMergeThreads>(p, blockIdx.x, blockIdx.y, s_w, s_red);
+  merge_head<kMergeThreads, kMergeCols>(p, blockIdx.x, blockIdx.y, blockIdx.z * kMergeCols, s_w, s_red);
 }
 
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid) {
@@ -147,7 +150,9 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
 
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid) {
   if (p.splits_total > kMaxSplits) return hipErrorInvalidValue;
-  V4A_LAUNCH(tid, merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads), dim3(kMergeThreads), 0, s, p);
+  if (p.dim % kMergeCols != 0 || p.merge_lo < 0 || p.merge_lo >= p.splits_total) return hipErrorInvalidValue;
+  V4A_LAUNCH(tid, merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads, (unsigned)(p.dim / kMergeCols)),
+             dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

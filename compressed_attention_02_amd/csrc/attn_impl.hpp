@@ -66,52 +66,63 @@ __device__ __forceinline__ float finish_head(float m, float l, const float* sink
 }
 
 // ------------------------------------------------------------------ merge
-// Combination of one (row, head)'s split partials (U_s, m_s, l_s), m in base 2:
-// weights exp2(m_s - max m), o = sum w_s U_s / sum w_s l_s.  NT threads; split s's
-// statistics are read by thread s (splits_total <= NT).  The weighted sum is spread
-// over NT/D thread groups, each summing its splits in ascending order, and the groups
-// are combined in LDS in a fixed order, so the result does not depend on timing.
-// s_w holds splits_total floats, s_red NT.
+// Combination of slots merge_lo .. splits_total - 1 of one (row, head)'s split
+// partials (U_s, m_s, l_s), m in base 2: weights exp2(m_s - max m), o = sum w_s U_s
+// / sum w_s l_s, for output columns [d0, d0 + DW).  NT threads; the statistics are
+// spread over the threads (kMaxSplits / NT each), the weighted sum over NT/DW thread
+// groups, each summing its splits in ascending order, and the groups are combined
+// in LDS in a fixed order, so the result does not depend on timing.  s_w holds
+// kMaxSplits floats, s_red NT.
 constexpr int kMaxSplits = 1024;
 constexpr int kMergeBatch = 16;
 
-template <int NT>
-__device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, float* s_w, float* s_red) {
-  const int tid = threadIdx.x;
+template <int NT, int DW>
+__device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, int d0, float* s_w, float* s_red) {
+  constexpr int G = NT / DW, NWV = NT / 64, KST = kMaxSplits / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = row / p.tq, i = row - b * p.tq;
-  const int S = p.splits_total, D = p.dim;
-  const float* ml = p.part_ml + ((int64_t)row * p.heads + head) * S * 2;
-  const int64_t ml_step = 2;
-  // thread (g, c) sums output column c over splits g, g+G, ...; its first
-  // kMergeBatch partial values load together with the split statistics
-  const int G = NT / D;
-  const int c = tid % D, g = tid / D;
-  const float* po = p.part_o + ((int64_t)row * p.heads + head) * S * D + c;
-  const int64_t po_step = D;
+  const int ST = p.splits_total, lo = p.merge_lo, S = ST - lo, D = p.dim;
+  const float* ml = p.part_ml + (((int64_t)row * p.heads + head) * ST + lo) * 2;
+  const int c = tid % DW, g = tid / DW;
+  const float* po = p.part_o + (((int64_t)row * p.heads + head) * ST + lo) * D + d0 + c;
+  // this thread's first kMergeBatch partial values load together with the statistics
   float v[kMergeBatch];
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(g + u * G, S - 1) * po_step];
-  float ms = -INFINITY, ls = 0.f;
-  if (tid < S) {
-    const float2 m2 = *reinterpret_cast<const float2*>(ml + tid * ml_step);
-    ms = m2.x;
-    ls = m2.y;
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(g + u * G, S - 1) * D];
+  float ms[KST], ls[KST];
+#pragma unroll
+  for (int u = 0; u < KST; ++u) {
+    const int t = tid + u * NT;
+    const float2 m2 = *reinterpret_cast<const float2*>(ml + (int64_t)min(t, S - 1) * 2);
+    ms[u] = t < S ? m2.x : -INFINITY;
+    ls[u] = t < S ? m2.y : 0.f;
   }
   // 1) global max of the split maxima
-  const float mx = wave_max(ms);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  float mx = ms[0];
+#pragma unroll
+  for (int u = 1; u < KST; ++u) mx = fmaxf(mx, ms[u]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   float M = s_red[0];
-  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, s_red[w]);
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_red[w]);
   __syncthreads();
-  // 2) split weights and the total sum
-  const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-  if (tid < S) s_w[tid] = wgt;
-  const float part = wave_sum(wgt * ls);
-  if ((tid & 63) == 0) s_red[tid >> 6] = part;
+  // 2) split weights and the total sum (per thread in u order, then waves in order)
+  float part = 0.f;
+#pragma unroll
+  for (int u = 0; u < KST; ++u) {
+    const int t = tid + u * NT;
+    const float wgt = (M == -INFINITY || ms[u] == -INFINITY) ? 0.f : exp2f(ms[u] - M);
+    if (t < S) s_w[t] = wgt;
+    part += wgt * ls[u];
+  }
+  part = wave_sum(part);
+  if (lane == 0) s_red[wave] = part;
   __syncthreads();
   float l = 0.f;
-  for (int w = 0; w < NT / 64; ++w) l += s_red[w];
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) l += s_red[w];
   __syncthreads();
   // 3) weighted sum of the partial outputs
   float acc = 0.f;
@@ -120,7 +131,7 @@ __device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, fl
     if (g + u * G < S) acc = fmaf(s_w[g + u * G], v[u], acc);
   for (int s0 = g + G * kMergeBatch; s0 < S; s0 += G * kMergeBatch) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(s0 + u * G, S - 1) * po_step];
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(int64_t)min(s0 + u * G, S - 1) * D];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
       if (s0 + u * G < S) acc = fmaf(s_w[s0 + u * G], v[u], acc);
@@ -129,27 +140,28 @@ __device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, fl
   __syncthreads();
   if (g == 0) {
     float a = s_red[c];
-    for (int gg = 1; gg < G; ++gg) a += s_red[gg * D + c];
+    for (int gg = 1; gg < G; ++gg) a += s_red[gg * DW + c];
     float lse;
     const float f = finish_head(M, l, p.sink, head, &lse);
-    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + c] = a * f;
-    if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + d0 + c] = a * f;
+    if (c == 0 && d0 == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
   }
-  __syncthreads();
 }
 
-// Merge of heads [h0, h0 + nh) of one row by one NT-thread workgroup with every
-// load of a pass in flight at once: the workgroup's G = NT/D column groups take up
-// to G heads per pass, gph = G/heads groups per head, each summing the splits sub,
-// sub + gph, ... of its head in ascending order, combined in LDS in group order.
-// The split statistics of the pass load together with the partials; the head
-// maxima come from LDS integer maxima of order-preserving keys (independent of
-// order), the sums l from one wave per head in a fixed lane order.  `lds` holds
-// kMergeLds(NT, D, splits_total) floats; splits_total <= kStepMaxSplits.
+// Merge of slots [lo, lo + n) of heads [h0, h0 + nh) of one row by one NT-thread
+// workgroup, with every load of a pass in flight at once: the workgroup's G = NT/D
+// column groups take up to G heads per pass, gph = G/heads groups per head, each
+// summing the slots lo + sub, lo + sub + gph, ... of its head in ascending order,
+// combined in LDS in group order.  The slot statistics of the pass load together
+// with the partials; the head maxima come from LDS integer maxima of
+// order-preserving keys (independent of order), the sums l from one wave per head
+// in a fixed lane order.  out_slot < 0 writes o and lse; otherwise the combination
+// (U relative to the new maximum, m, l) goes to slot out_slot.  With ok false
+// nothing is read and the outputs get NaN.  `lds` holds kMergeLds(NT, D, n) floats.
 constexpr int kMergeLoads = 48;     // partial values in flight per thread
 
-__host__ __device__ constexpr int kMergeLds(int nt, int d, int splits) {
-  return 2 * (nt / d) + (nt / d) * splits + ((nt / d) * splits > nt ? (nt / d) * splits : nt);
+__host__ __device__ constexpr int kMergeLds(int nt, int d, int n) {
+  return 2 * (nt / d) + (nt / d) * n + ((nt / d) * n > nt ? (nt / d) * n : nt);
 }
 
 __device__ __forceinline__ uint32_t f2key(float f) {
@@ -161,17 +173,28 @@ __device__ __forceinline__ float key2f(uint32_t k) {
 }
 
 template <int NT>
-__device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int nh, float* lds) {
+__device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int nh, int lo, int n, int out_slot,
+                                            bool ok, float* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = row / p.tq, i = row - b * p.tq;
-  const int S = p.splits_total, D = p.dim, H = p.heads, G = NT / D;
+  const int ST = p.splits_total, D = p.dim, H = p.heads, G = NT / D;
   const int g = tid / D, c = tid % D;
+  float* part_o = p.part_o + (int64_t)row * H * ST * D;
+  float* part_ml = p.part_ml + (int64_t)row * H * ST * 2;
+  if (!ok) {
+    for (int h = h0; h < h0 + nh; ++h) {
+      if (out_slot >= 0) {
+        if (tid == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)h * ST + out_slot) * 2) = make_float2(NAN, NAN);
+      } else if (tid < D) {
+        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + tid] = NAN;
+      }
+    }
+    return;
+  }
   uint32_t* s_mk = reinterpret_cast<uint32_t*>(lds);
   float* s_l = lds + G;
   float* s_w = lds + 2 * G;
-  float* s_wl = s_w + G * S;   // w*l per item; later the group sums
-  const float* part_o = p.part_o + (int64_t)row * S * H * D;
-  const float* part_ml = p.part_ml + (int64_t)row * S * H * 2;
+  float* s_wl = s_w + G * n;   // w*l per item; later the group sums
   constexpr int kStat = kStepMaxSplits * 8 / NT;  // statistics per thread (G <= 8)
   for (int hb = 0; hb < nh; hb += G) {
     const int nhp = min(G, nh - hb);
@@ -179,18 +202,18 @@ __device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int
     const int hs = min(g / gph, nhp - 1), sub = g % gph;
     const bool act = g / gph < nhp;
     const int h = h0 + hb + hs;
-    const int n_it = nhp * S;
-    // 1) every load of the pass: this thread's partial values and split statistics
-    const int nmine = (S - sub + gph - 1) / gph;
+    const int n_it = nhp * n;
+    const float* ph = part_o + ((int64_t)h * ST + lo) * D + c;
+    // 1) every load of the pass: this thread's partial values and slot statistics
+    const int nmine = (n - sub + gph - 1) / gph;
     float v[kMergeLoads];
 #pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u)
-      v[u] = part_o[((int64_t)h * S + min(sub + u * gph, S - 1)) * D + c];
+    for (int u = 0; u < kMergeLoads; ++u) v[u] = ph[(int64_t)min(sub + u * gph, n - 1) * D];
     float2 ml[kStat];
 #pragma unroll
     for (int u = 0; u < kStat; ++u) {
       const int q = min(tid + u * NT, n_it - 1);
-      ml[u] = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(h0 + hb + q / S) * S + q % S) * 2);
+      ml[u] = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(h0 + hb + q / n) * ST + lo + q % n) * 2);
     }
     if (tid < G) s_mk[tid] = 0u;
     __syncthreads();
@@ -198,15 +221,15 @@ __device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int
 #pragma unroll
     for (int u = 0; u < kStat; ++u) {
       const int t = tid + u * NT;
-      if (t < n_it) atomicMax(&s_mk[t / S], f2key(ml[u].x));
+      if (t < n_it) atomicMax(&s_mk[t / n], f2key(ml[u].x));
     }
     __syncthreads();
-    // 3) split weights and w*l per item, then l per head (wave hs, fixed order)
+    // 3) slot weights and w*l per item, then l per head (wave hs, fixed order)
 #pragma unroll
     for (int u = 0; u < kStat; ++u) {
       const int t = tid + u * NT;
       if (t < n_it) {
-        const float M = key2f(s_mk[t / S]);
+        const float M = key2f(s_mk[t / n]);
         const float w = (M == -INFINITY || ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
         s_w[t] = w;
         s_wl[t] = w * ml[u].y;
@@ -215,21 +238,20 @@ __device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int
     __syncthreads();
     if (wave < nhp) {
       float a = 0.f;
-      for (int sp = lane; sp < S; sp += 64) a += s_wl[wave * S + sp];
+      for (int sp = lane; sp < n; sp += 64) a += s_wl[wave * n + sp];
       a = wave_sum(a);
       if (lane == 0) s_l[wave] = a;
     }
-    // 4) weighted sum of this thread's splits, ascending
+    // 4) weighted sum of this thread's slots, ascending
     float acc = 0.f;
     for (int r0 = 0; r0 < nmine; r0 += kMergeLoads) {
       if (r0 > 0) {
 #pragma unroll
-        for (int u = 0; u < kMergeLoads; ++u)
-          v[u] = part_o[((int64_t)h * S + min(sub + (r0 + u) * gph, S - 1)) * D + c];
+        for (int u = 0; u < kMergeLoads; ++u) v[u] = ph[(int64_t)min(sub + (r0 + u) * gph, n - 1) * D];
       }
 #pragma unroll
       for (int u = 0; u < kMergeLoads; ++u)
-        if (r0 + u < nmine) acc = fmaf(s_w[hs * S + sub + (r0 + u) * gph], v[u], acc);
+        if (r0 + u < nmine) acc = fmaf(s_w[hs * n + sub + (r0 + u) * gph], v[u], acc);
     }
     __syncthreads();
     s_wl[tid] = acc;
@@ -237,10 +259,16 @@ __device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int
     if (act && sub == 0) {
       float a = 0.f;
       for (int q = 0; q < gph; ++q) a += s_wl[(g + q) * D + c];
-      float lse;
-      const float f = finish_head(key2f(s_mk[hs]), s_l[hs], p.sink, h, &lse);
-      p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a * f;
-      if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + h] = lse;
+      const float M = key2f(s_mk[hs]), l = s_l[hs];
+      if (out_slot >= 0) {
+        part_o[((int64_t)h * ST + out_slot) * D + c] = a;
+        if (c == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)h * ST + out_slot) * 2) = make_float2(M, l);
+      } else {
+        float lse;
+        const float f = finish_head(M, l, p.sink, h, &lse);
+        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a * f;
+        if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + h] = lse;
+      }
     }
     __syncthreads();
   }
@@ -578,7 +606,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   // if the wait gives up, the split attends nothing and reports NaN statistics
   bool poison = false;
   if constexpr (STEP)
-    if (p.sync && p.wait_idx) poison = !wg_wait_ge(p.sync + 2 * row, 1, p.wait_ticks, &sm.flag);
+    if (p.sync && p.wait_idx) poison = !wg_wait_ge(p.sync + kRowWords * row, 1, p.wait_ticks, &sm.flag);
   const int64_t k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
   const int64_t n_csa = (p.mask & 1u) ? p.topk : 0;
   const int64_t n_idx = poison ? 0 : min(min(n_csa, p.key_hi), k_begin + (int64_t)p.keys_per_split) - k_begin;
@@ -681,19 +709,26 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   }
 
   if (STEP && p.sync) {
-    // one-launch step: count this split done, wait for all of the row's splits, then
-    // merge heads [j hp, (j + 1) hp) of the row, j = this split's slot
-    wg_release(p.sync + 2 * row + 1, false);
-    const bool ok = wg_wait_ge(p.sync + 2 * row + 1, p.splits_total, p.wait_ticks, &sm.flag);
-    const int j = p.split_base + split;
-    const int hp = (p.heads + p.splits_total - 1) / p.splits_total;
-    const int hlo = min(p.heads, j * hp), h1 = min(p.heads, (j + 1) * hp);
+    int* w = p.sync + kRowWords * row;
     static_assert(kMergeLds(NT, D, kStepMaxSplits) <= 4 * 64 * (D / 4 + 2), "merge scratch fits the chunk buffers");
-    if (ok) {
-      merge_heads<NT>(p, row, hlo, h1 - hlo, sm.C);
-    } else {
-      for (int h = hlo; h < h1; ++h)
-        if (tid < D) p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + tid] = NAN;
+    if (p.premerge) {
+      // the launch's splits of the row, done early, combine into its last slot
+      // while the rest of the step runs; heads are shared over the launch's splits
+      wg_release(w + 2, false);
+      const bool okr = wg_wait_ge(w + 2, p.splits, p.wait_ticks, &sm.flag);
+      const int hp = (p.heads + p.splits - 1) / p.splits;
+      const int hlo = min(p.heads, split * hp), h1 = min(p.heads, (split + 1) * hp);
+      merge_heads<NT>(p, row, hlo, h1 - hlo, p.split_base, p.splits, p.split_base + p.splits - 1, okr, sm.C);
+    }
+    if (p.final_merge) {
+      // count this split done, wait for all of the row's splits, then merge heads
+      // [j hp, (j + 1) hp) of the row from merge_lo on, j = this split's slot
+      wg_release(w + 1, false);
+      const bool ok = wg_wait_ge(w + 1, p.splits_total, p.wait_ticks, &sm.flag);
+      const int j = p.split_base + split;
+      const int hp = (p.heads + p.splits_total - 1) / p.splits_total;
+      const int hlo = min(p.heads, j * hp), h1 = min(p.heads, (j + 1) * hp);
+      merge_heads<NT>(p, row, hlo, h1 - hlo, p.merge_lo, p.splits_total - p.merge_lo, -1, ok, sm.C);
     }
   }
 }

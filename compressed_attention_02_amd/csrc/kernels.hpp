@@ -82,12 +82,18 @@ struct AttnP {
   // splits_total == 1 the launch writes o and lse directly.
   int64_t key_lo, key_hi;
   int splits, keys_per_split, split_base, splits_total;
-  // one-launch decode step only (null elsewhere): per row {idx ready, splits done}.
-  // A launch with wait_idx waits for its row's idx before reading it; with sync, every
-  // workgroup of a row counts itself done, waits for all splits_total and merges its
-  // share of the heads.  Each wait gives up after wait_ticks of the 100 MHz clock.
-  int* sync; int64_t wait_ticks; int wait_idx;
+  // the merge (kernel or in-kernel) combines slots merge_lo .. splits_total - 1
+  int merge_lo;
+  // decode step only (null elsewhere): kRowWords words per row {idx ready, splits
+  // done, rest splits done}.  wait_idx: wait for the row's idx before reading it.
+  // premerge: the launch's workgroups count themselves done, wait for each other
+  // and combine the launch's slots of the row into its last slot.  final_merge:
+  // every workgroup of the row counts itself done, waits for all splits_total and
+  // merges its share of the heads from merge_lo on.  Each wait gives up after
+  // wait_ticks of the 100 MHz clock.
+  int* sync; int64_t wait_ticks; int wait_idx, premerge, final_merge;
 };
+constexpr int kRowWords = 4;
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
 

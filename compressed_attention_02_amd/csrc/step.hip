@@ -9,12 +9,14 @@
 // the key range after the CSA picks (as attn_bf16_kernel).  One launch on one
 // stream: no cross-queue synchronisation.
 //
-// When the whole grid fits the chip at once, the launch also attends the picks and
-// merges: the selecting workgroup publishes its row (agent-scope release of a row
-// word), the workgroups of the picks wait for it before reading idx, and every
-// attention workgroup of the row counts itself done, waits for the row's last
-// split and merges a share of the heads.  Waits are bounded in time; a wait that
-// gives up leaves NaN in the outputs it owns rather than hang.
+// In the one-launch form, when the whole grid fits the chip at once, the launch
+// also attends the picks and merges: the selecting workgroup publishes its row
+// (agent-scope release of a row word), the workgroups of the picks wait for it
+// before reading idx; the other attention workgroups of a row, done long before
+// the selection, wait for each other and combine their partials into one per head;
+// then every attention workgroup of the row counts itself done, waits for the
+// row's last split and merges a share of the heads.  Waits are bounded in time; a
+// wait that gives up leaves NaN in the outputs it owns rather than hang.
 #include "attn_impl.hpp"
 #include "select_impl.hpp"
 
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   const int blk = blockIdx.x;
   if (blk < n_sel) {
     select_row(sp, blk, sm.sel);
-    if (ap.sync) wg_release(ap.sync + 2 * blk, true);  // publish the row's picks
+    if (csa.sync) wg_release(csa.sync + kRowWords * blk, true);  // publish the row's picks
     return;
   }
   const int a = blk - n_sel;
@@ -56,12 +58,18 @@ hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, con
   const int64_t n_rest = (int64_t)ap.splits * n_rows;
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0)
     return hipErrorInvalidValue;
-  // with the picks attended in the same launch both parts carry the row words, the
-  // picks' part waits for the selection, and every split joins the merge
-  if ((ap.sync || csa.sync) && (csa.splits < 1 || ap.sync != csa.sync || !csa.wait_idx || ap.wait_idx ||
-                   ap.splits_total != ap.splits + csa.splits || csa.splits_total != ap.splits_total ||
-                   ap.splits_total > kStepMaxSplits))
+  // the rest pre-merge needs the row words; with the picks attended in the same
+  // launch both parts carry them, the picks' part waits for the selection, and
+  // every split joins the final merge
+  if (ap.premerge && (!ap.sync || ap.splits < 2 || ap.splits > kStepMaxSplits ||
+                      ap.merge_lo != ap.split_base + ap.splits - 1))
     return hipErrorInvalidValue;
+  if (csa.sync && (csa.splits < 1 || ap.sync != csa.sync || !csa.wait_idx || ap.wait_idx || !ap.final_merge ||
+                   !csa.final_merge || ap.splits_total != ap.splits + csa.splits ||
+                   csa.splits_total != ap.splits_total || ap.splits_total > kStepMaxSplits ||
+                   ap.merge_lo != csa.merge_lo))
+    return hipErrorInvalidValue;
+  if (!csa.sync && ap.final_merge) return hipErrorInvalidValue;
   // up to 64 heads, two waves per head tile take half of every chunk's keys each
   const dim3 g((unsigned)n), blk(kSelThreads);
   const int nr = (int)n_rest;

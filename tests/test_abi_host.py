@@ -224,9 +224,10 @@ def test_wait_limit_range():
 
 
 def test_decode_step_workspace_holds_row_words():
-    # with CSA the step's workspace ends with two 32-bit words per row (selection
-    # published, splits done) after the 256-byte aligned partials
+    # with CSA the step's workspace ends with four 32-bit words per row (selection
+    # published, splits done, rest splits done, spare) after the 256-byte aligned
+    # partials
     L = V.lib()
     ix, a = good_index(), good_attn()
     need = L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a))
-    assert need % 256 == a.batch * 8 % 256
+    assert need % 256 == a.batch * 16 % 256
