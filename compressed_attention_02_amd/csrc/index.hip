@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   constexpr int CPR = DI * 2 / 16;           // 16-byte pieces per key row
   constexpr int RPI = 64 / CPR;              // key rows per wave load
   constexpr int IPW = kTile / RPI / 4;       // loads per wave per tile
+  constexpr int QN = MT * 16 / RPI;         // wave loads of the query rows (heads)
   __shared__ __align__(16) unsigned char sK[NB][kTile * ROWB];
+  __shared__ __align__(16) unsigned char sQ[MT * 16 * ROWB];
   if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
   const int lr = blockIdx.y;
@@ -79,23 +81,30 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
       lds_load16(ki + j * p.ki_rs + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(buf + r0 * ROWB));
     }
   };
+  // the query rows go to LDS once per workgroup (laid out like the key rows), ahead
+  // of the first tile; the waves read their fragments from there
+  {
+    const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
+#pragma unroll
+    for (int u = wave; u < QN; u += 4) {
+      const int r = u * RPI + lane / CPR;
+      lds_load16(qi + r * DI + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(sQ + u * RPI * ROWB));
+    }
+  }
   issue(tile, sK[0]);
   if (NB == 2 && tile + gridDim.x < ntile_row) issue(tile + gridDim.x, sK[NB - 1]);
 
-  bf16x8_t A[MT][KS];
   float w[MT][4];
   {
-    const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
     const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        A[mt][s] = *reinterpret_cast<const bf16x8_t*>(qi + (mt * 16 + col) * DI + s * 32 + grp * 8);
       const f32x4 wq = *reinterpret_cast<const f32x4*>(wi + mt * 16 + 4 * grp);
       w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
     }
   }
+  bf16x8_t A[MT][KS];
+  bool have_q = false;
 
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
   const int kx = swz_ki<DI>(col);          // rows 16u + col of a wave share col's XOR
@@ -105,6 +114,14 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     if (next) __builtin_amdgcn_s_waitcnt(0x0F70 | IPW);  // vmcnt(IPW): the next tile may stay in flight
     else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
     __syncthreads();
+    if (!have_q) {  // query fragments: row mt*16 + col, piece 4s + grp (the rows share col's XOR)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          A[mt][s] = *reinterpret_cast<const bf16x8_t*>(sQ + (mt * 16 + col) * ROWB + (((s * 4 + grp) ^ kx) * 16));
+      have_q = true;
+    }
     const int64_t tile0 = tile * kTile;
     float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
 #pragma unroll
