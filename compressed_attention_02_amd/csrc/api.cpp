@@ -283,6 +283,7 @@ v4a_status check_ws(void* ws, size_t have, size_t need) {
 
 AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   AttnP p{};
+  p.head_groups = 1;
   p.q = a->q.ptr; p.q_bs = a->q.batch_stride; p.q_rs = a->q.row_stride;
   p.idx = (const int32_t*)a->idx.ptr; p.idx_bs = a->idx.batch_stride; p.idx_rs = a->idx.row_stride;
   p.kc = a->kc.ptr; p.kc_bs = a->kc.batch_stride; p.kc_rs = a->kc.row_stride;
@@ -468,6 +469,9 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   csa.splits = (int)P.s_csa;
   csa.keys_per_split = kAttnChunk;
   csa.split_base = (int)P.s_rest;
+  // the picks' launch is short and on the critical path: groups of two head tiles
+  // per workgroup cut the queries each workgroup reads and the partials it writes
+  if (a->dtype == V4A_BF16) csa.head_groups = std::max(1, a->heads / 32);
 
   auto attend = [&](const AttnP& ap) -> v4a_status {
     V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s, V4A_K_ATTN), "attention launch"));
@@ -484,6 +488,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
       // rest of each row, done early, pre-merges in-kernel meanwhile
       int* words = (int*)((char*)ws + P.off_sync);
       AttnP csa_in = csa;
+      csa_in.head_groups = 1;   // the one-launch roles take every head
       csa_in.sync = words;
       const bool one_launch = g_one_launch.load() != 0 && P.s_rest >= 2 &&
                               select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&

@@ -128,14 +128,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
 }
 
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid) {
-  const dim3 grid((unsigned)p.splits, (unsigned)nrows);
+  if (p.head_groups < 1 || (dtype == 0 && p.head_groups != 1)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.splits * p.head_groups), (unsigned)nrows);
   if (dtype == 0) {
     if (p.dim == 64) V4A_LAUNCH(tid, attn_f32_kernel<64>, grid, dim3(256), 0, s, p);
     else V4A_LAUNCH(tid, attn_f32_kernel<128>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  const int ntile = p.heads / 16;
-  if (p.heads % 16 != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
+  const int ntile = p.heads / 16 / p.head_groups;   // tiles per workgroup
+  if (p.heads % (16 * p.head_groups) != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
   // chunk's keys in half (four waves per SIMD); above, one wave per head tile
   if (ntile <= 4) {

@@ -569,20 +569,25 @@ struct AttnSmem {
 // The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
 // head tiles w, w + NW, ... (HT of them); with KP = 2 (HT = 1), waves w and
 // w + NW/2 share head tile w and take one half of every chunk's keys each, and
-// combine their softmax states through LDS at the end.  A tile past the head count
-// is computed on a copy of tile 0's queries and not written.  All waves load.
+// combine their softmax states through LDS at the end.  With head_groups > 1 the
+// launch's x index is split * head_groups + group and the workgroup takes only the
+// group's head tiles (fewer queries read and partials written per workgroup).  A
+// tile past the group's is computed on a copy of the group's first tile's queries
+// and not written.  All waves load.
 // Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
 // chunk c is computed.
 template <int NW, int HT, int D, int KP, bool STEP = false>
-__device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, AttnSmem<D>& sm) {
+__device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
+  // xs = split * head_groups + group: the workgroup takes group's head tiles
+  const int hgn = p.head_groups, split = xs / hgn, hgi = xs - split * hgn;
   constexpr int TW = NW / KP;   // waves per key part: head tiles of one pass
   constexpr int NT = NW * 64, CH = kAttnChunk, KS = D / 32, DT = D / 16;
   int* s_idx = sm.idx;
   const int b = row / p.tq, i = row - b * p.tq;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ntile = p.heads / 16;
+  const int ntg = p.heads / 16 / hgn;   // head tiles of the group
   const float sl2 = p.scale * kLog2e;
 
   // Independent loads first, all in flight together: the position, the raw
@@ -592,12 +597,15 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   const int64_t raw_ld = (p.mask & 4u) ? p.raw_start[b] : 0;
   const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs;
   int tile[HT];
+  bool tv[HT];   // the wave's tile t exists in the group
   bf16x8_t Qb[HT][KS];
   const int kh = KP == 2 ? wave / TW : 0;
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    tile[t] = wave % TW + TW * t;
-    const int tq = tile[t] < ntile ? tile[t] : 0;
+    const int lt = wave % TW + TW * t;
+    tv[t] = lt < ntg;
+    tile[t] = hgi * ntg + (tv[t] ? lt : 0);
+    const int tq = tile[t];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       Qb[t][s] = *reinterpret_cast<const bf16x8_t*>(qrow + (tq * 16 + col) * D + s * 32 + grp * 8);
@@ -653,7 +661,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  run_chunks<NW, D, HT, KP>(R, s_idx, sm.K0, sm.V0, sm.B0, sm.K1, sm.V1, sm.B1, nch, tile[0] < ntile, Qb, O, m_run,
+  run_chunks<NW, D, HT, KP>(R, s_idx, sm.K0, sm.V0, sm.B0, sm.K1, sm.V1, sm.B1, nch, tv[0], Qb, O, m_run,
                             l_run, sl2, wave, lane, kh);
 
   if constexpr (KP == 2) {
@@ -684,7 +692,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int split, int row, A
 
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    if (tile[t] >= ntile || kh != 0) continue;
+    if (!tv[t] || kh != 0) continue;
     const int head = tile[t] * 16 + col;
     const float l = col_sum4(l_run[t]);
     if (p.splits_total == 1) {

@@ -82,6 +82,9 @@ struct AttnP {
   // splits_total == 1 the launch writes o and lse directly.
   int64_t key_lo, key_hi;
   int splits, keys_per_split, split_base, splits_total;
+  // bf16 launches: heads split into head_groups groups of whole 16-head tiles, one
+  // workgroup per (split, group); 1 = every workgroup takes all heads
+  int head_groups;
   // the merge (kernel or in-kernel) combines slots merge_lo .. splits_total - 1
   int merge_lo;
   // decode step only (null elsewhere): kRowWords words per row {idx ready, splits

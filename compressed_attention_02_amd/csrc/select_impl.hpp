@@ -472,25 +472,51 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
       if (r < n_tie)
         id_max = rank_search(eachOwn, [T](uint32_t key, uint32_t) { return key == T; },
                              [](uint32_t, uint32_t id) { return id; }, r, false, sh, n_tie);
-      // branch-free per entry (id_max = ~0 when no cut falls inside the ties at T);
-      // keys of no element are 0 < T
-      uint32_t c = 0;
+      if (id_max == 0xffffffffu) {
+        // no cut inside the ties at T: the picks are the keys >= T (keys of no element
+        // are 0 < T).  A bit per entry, then only the set bits are visited.
+        uint64_t mask = 0;
 #pragma unroll
-      for (int q = 0; q < kMaxTilesPerThread; ++q) {
-        if (q >= tpt) break;
+        for (int q = 0; q < kMaxTilesPerThread; ++q) {
+          if (q >= tpt) break;
 #pragma unroll
-        for (int j = 0; j < kTileTop; ++j) c += picked_bits(uk[q][j], rep_id(q, j), T, id_max);
-      }
-      uint32_t o = block_scan(c, sh) - c;
+          for (int j = 0; j < kTileTop; ++j) mask |= (uint64_t)(uk[q][j] >= T) << (q * kTileTop + j);
+        }
+        const uint32_t c = (uint32_t)__popcll(mask);
+        uint32_t o = block_scan(c, sh) - c;
+        while (mask) {
+          const int j = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const int q = j / kTileTop, wv = (j % kTileTop) / 4, e = j % 4;
+          uint32_t word = uo[0][0];
 #pragma unroll
-      for (int q = 0; q < kMaxTilesPerThread; ++q) {
-        if (q >= tpt) break;
+          for (int qq = 0; qq < kMaxTilesPerThread; ++qq)
 #pragma unroll
-        for (int j = 0; j < kTileTop; ++j) {
-          const uint32_t id = rep_id(q, j);
-          const uint32_t pk = picked_bits(uk[q][j], id, T, id_max);
-          *(pk & (o < (uint32_t)k) ? &sh.pool_id[o] : &sh.hist[kBins + lane]) = id;
-          o += pk;
+            for (int ww = 0; ww < 4; ++ww) word = (q * 4 + wv == qq * 4 + ww) ? uo[qq][ww] : word;
+          const uint32_t id = (uint32_t)(((int64_t)tid * tpt + q) * kTile) + 64u * wv + ((word >> (8 * e)) & 0xffu);
+          if (o < (uint32_t)k) sh.pool_id[o] = id;
+          ++o;
+        }
+      } else {
+        // branch-free per entry
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < kMaxTilesPerThread; ++q) {
+          if (q >= tpt) break;
+#pragma unroll
+          for (int j = 0; j < kTileTop; ++j) c += picked_bits(uk[q][j], rep_id(q, j), T, id_max);
+        }
+        uint32_t o = block_scan(c, sh) - c;
+#pragma unroll
+        for (int q = 0; q < kMaxTilesPerThread; ++q) {
+          if (q >= tpt) break;
+#pragma unroll
+          for (int j = 0; j < kTileTop; ++j) {
+            const uint32_t id = rep_id(q, j);
+            const uint32_t pk = picked_bits(uk[q][j], id, T, id_max);
+            *(pk & (o < (uint32_t)k) ? &sh.pool_id[o] : &sh.hist[kBins + lane]) = id;
+            o += pk;
+          }
         }
       }
       __syncthreads();
