@@ -469,9 +469,15 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   csa.splits = (int)P.s_csa;
   csa.keys_per_split = kAttnChunk;
   csa.split_base = (int)P.s_rest;
-  // the picks' launch is short and on the critical path: groups of two head tiles
-  // per workgroup cut the queries each workgroup reads and the partials it writes
-  if (a->dtype == V4A_BF16) csa.head_groups = std::max(1, a->heads / 32);
+  // the picks' launch is short and on the critical path: head groups cut the queries
+  // each workgroup reads and the partials it writes; the smallest groups (one 16-head
+  // tile) while the launch stays within one workgroup per CU
+  if (a->dtype == V4A_BF16 && P.s_csa > 0) {
+    const int ntile = std::max(1, a->heads / 16);
+    int hg = ntile;
+    while (hg > 1 && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
+    csa.head_groups = hg;
+  }
 
   auto attend = [&](const AttnP& ap) -> v4a_status {
     V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s, V4A_K_ATTN), "attention launch"));

@@ -196,3 +196,13 @@ def test_step_wait_limit_gives_nan_then_recovers():
         r.run(fused=True).check_all()
     finally:
         V.set_one_launch_step(False)
+
+
+@pytest.mark.parametrize("heads", [48, 80])
+def test_step_odd_head_tile_counts(heads):
+    # 3 and 5 tiles of 16 heads: the CSA launch's head groups must divide the tile
+    # count, and the attention kernels take the KP=2 (<= 4 tiles) and KP=1 forms
+    cfg = C.C2.small(name=f"h{heads}", heads=heads, batch=2, pos=4097, needles=4)
+    print(f"[case] step heads={heads}", flush=True)
+    Run(cfg).run(fused=True).check_all()
+    Run(cfg).run(fused=False).check_all()
