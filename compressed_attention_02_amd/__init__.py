@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 
 F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
+BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ABI_VERSION = 1
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6}
@@ -64,7 +65,7 @@ class AttnArgs(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("tq", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("dim", ctypes.c_int32), ("branch_mask", ctypes.c_uint32), ("csa_ratio", ctypes.c_int32),
                 ("hca_ratio", ctypes.c_int32), ("window", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("reserved0", ctypes.c_int32), ("pos0", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("flags", ctypes.c_uint32), ("pos0", ctypes.c_void_p),
                 ("pos_max", ctypes.c_int64), ("q", Tensor), ("idx", Tensor), ("kc", Tensor),
                 ("vc", Tensor), ("kh", Tensor), ("vh", Tensor), ("k_raw", Tensor), ("v_raw", Tensor),
                 ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor)]
@@ -204,12 +205,12 @@ def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, se
 
 def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=None, k_raw=None,
               v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
-              window=128, topk=1, pos_max=None, scale=0.0, sink=None) -> AttnArgs:
+              window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False) -> AttnArgs:
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
     return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
-                    window, topk, scale, 0, _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
+                    window, topk, scale, BATCH_INVARIANT if batch_invariant else 0, _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
                     _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
                     _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse))
 

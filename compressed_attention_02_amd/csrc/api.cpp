@@ -133,6 +133,8 @@ struct AttnPlan {
 // chip twice, but at least kMinKeysPerSplit keys each, since every split writes a
 // partial of heads * (dim + 2) floats that the merge reads back.
 constexpr int64_t kMinKeysPerSplit = 128;
+// keys per split of the batch-invariant plans
+constexpr int64_t kInvariantKeysPerSplit = 256;
 
 AttnPlan plan_attn(const v4a_attn_args* a) {
   AttnPlan P{};
@@ -142,7 +144,13 @@ AttnPlan plan_attn(const v4a_attn_args* a) {
              ((a->branch_mask & V4A_SWA) ? std::min<int64_t>(a->window, pmax + 1) : 0);
   const int64_t target = 2 * (int64_t)cu_count();
   P.splits = 1;
-  if (P.rows < target && P.n_keys > kMinKeysPerSplit) {
+  if (a->flags & V4A_BATCH_INVARIANT) {
+    // fixed split size: a query's splits cover the same keys whatever the batch and
+    // pos_max (splits past its keys are empty and add exact zeros in the merge)
+    P.kps = kInvariantKeysPerSplit;
+    P.splits = cdiv(std::max<int64_t>(P.n_keys, 1), P.kps);
+    if (P.splits == 1) P.splits = 2;  // the merge's rounding, not the direct write's
+  } else if (P.rows < target && P.n_keys > kMinKeysPerSplit) {
     const int64_t per_row = cdiv(target, P.rows);
     P.kps = round_up(cdiv(P.n_keys, per_row), kAttnChunk);
     P.kps = std::max<int64_t>(P.kps, kMinKeysPerSplit);
@@ -234,6 +242,7 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
   if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
   if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
+  if (a->flags & ~V4A_BATCH_INVARIANT) return fail(V4A_EINVAL, "unknown flags 0x%x", a->flags);
   if (a->branch_mask & V4A_CSA) {
     if (a->topk < 1) return fail(V4A_EINVAL, "topk must be >= 1");
     if (a->topk > kMaxTopk) return fail(V4A_ENOTSUP, "topk %d > %d", a->topk, kMaxTopk);
@@ -406,7 +415,11 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   P.n_rest = ((a->branch_mask & V4A_HCA) ? (pmax + 1) / a->hca_ratio : 0) +
              ((a->branch_mask & V4A_SWA) && a->window > 0 ? std::min<int64_t>(a->window, pmax + 1) : 0);
   P.s_csa = P.csa ? cdiv(a->topk, kAttnChunk) : 0;
-  if (P.n_rest > 0) {
+  const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;
+  if (P.n_rest > 0 && inv) {
+    P.kps_rest = kInvariantKeysPerSplit;
+    P.s_rest = cdiv(P.n_rest, P.kps_rest);
+  } else if (P.n_rest > 0) {
     const int64_t per_row = cdiv(2 * (int64_t)cu_count(), P.rows);
     P.kps_rest = std::max<int64_t>(round_up(cdiv(P.n_rest, per_row), kAttnChunk), kMinKeysPerSplit);
     P.kps_rest = std::max<int64_t>(P.kps_rest, round_up(cdiv(P.n_rest, kAttnMaxSplits - P.s_csa), kAttnChunk));
@@ -458,24 +471,27 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     p.part_o = (float*)((char*)ws + P.off_attn);
     p.part_ml = p.part_o + (size_t)P.rows * P.s_total * a->heads * a->dim;
   }
+  // batch-invariant plans put the CSA slots first, so that the rest's split count
+  // (from pos_max) only appends empty slots at the end of the merge order
+  const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;
   AttnP rest = p, csa = p;
   rest.key_lo = P.csa ? a->topk : 0;
   rest.key_hi = INT64_MAX;
   rest.splits = (int)P.s_rest;
   rest.keys_per_split = (int)P.kps_rest;
-  rest.split_base = 0;
+  rest.split_base = inv ? (int)P.s_csa : 0;
   csa.key_lo = 0;
   csa.key_hi = a->topk;
   csa.splits = (int)P.s_csa;
   csa.keys_per_split = kAttnChunk;
-  csa.split_base = (int)P.s_rest;
+  csa.split_base = inv ? 0 : (int)P.s_rest;
   // the picks' launch is short and on the critical path: head groups cut the queries
   // each workgroup reads and the partials it writes; the smallest groups (one 16-head
   // tile) while the launch stays within one workgroup per CU
   if (a->dtype == V4A_BF16 && P.s_csa > 0) {
     const int ntile = std::max(1, a->heads / 16);
     int hg = ntile;
-    while (hg > 1 && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
+    while (!inv && hg > 1 && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
     csa.head_groups = hg;
   }
 
@@ -496,7 +512,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
       AttnP csa_in = csa;
       csa_in.head_groups = 1;   // the one-launch roles take every head
       csa_in.sync = words;
-      const bool one_launch = g_one_launch.load() != 0 && P.s_rest >= 2 &&
+      const bool one_launch = !inv && g_one_launch.load() != 0 && P.s_rest >= 2 &&
                               select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&
                               P.s_total <= kStepMaxSplits;
       const bool premerge = one_launch;

@@ -185,10 +185,21 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *   sink         fp32 [H] or NULL
  *   o            fp32 out [batch][tq][H][d] (row = query token)
  *   lse          fp32 out [batch][tq][H] (row = query token) or ptr == NULL
+ *   flags        V4A_BATCH_INVARIANT: a query's o and lse (and, through
+ *                v4attn_decode_step, its idx) depend only on its own sequence's
+ *                inputs, bit for bit, not on the other sequences of the batch
+ *                nor on pos_max.  Key splits then have a fixed size (256 keys;
+ *                64 for the CSA picks of v4attn_decode_step), the CSA picks'
+ *                attention takes one 16-head tile per workgroup and the step
+ *                runs in two launches.  Other bits: V4A_EINVAL.
  * The caller appends the query's own K/V to the raw buffers, and for a prefill
  * chunk runs v4attn_compress over the chunk first.
  * Workspace: v4attn_decode_workspace / v4attn_prefill_chunk_workspace.
  * ------------------------------------------------------------------------- */
+/* [wiki] the batch-invariance material: results that must not change with
+ * the batch a request is served in. */
+#define V4A_BATCH_INVARIANT 1u
+
 typedef struct v4a_attn_args {
   uint32_t abi_version;
   int32_t dtype;
@@ -203,7 +214,7 @@ typedef struct v4a_attn_args {
   int32_t window;
   int32_t topk;
   float scale;
-  int32_t reserved0;
+  uint32_t flags;      /* V4A_BATCH_INVARIANT or 0 */
   const int64_t* pos0;
   int64_t pos_max;
   v4a_tensor q;

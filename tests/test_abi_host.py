@@ -231,3 +231,8 @@ def test_decode_step_workspace_holds_row_words():
     ix, a = good_index(), good_attn()
     need = L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a))
     assert need % 256 == a.batch * 16 % 256
+
+
+def test_attention_rejects_unknown_flags():
+    r, msg = _st(V.lib().v4attn_decode, good_attn(flags=2), None, 0, None)
+    assert r == EINVAL and "flags" in msg
