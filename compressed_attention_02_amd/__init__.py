@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
 BATCH_INVARIANT = 1   # v4a_attn_args.flags
-ABI_VERSION = 1
+ABI_VERSION = 2
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6}
 
@@ -49,7 +49,8 @@ class CompressArgs(ctypes.Structure):
                 ("dim", ctypes.c_int32), ("ratio", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("t0", ctypes.c_int64), ("n", ctypes.c_int64), ("raw_start", ctypes.c_void_p),
                 ("k_raw", Tensor), ("v_raw", Tensor), ("logits", Tensor), ("k_out", Tensor),
-                ("v_out", Tensor)]
+                ("v_out", Tensor), ("norm_k", ctypes.c_void_p), ("norm_v", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("reserved1", ctypes.c_int32)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -68,7 +69,8 @@ class AttnArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("flags", ctypes.c_uint32), ("pos0", ctypes.c_void_p),
                 ("pos_max", ctypes.c_int64), ("q", Tensor), ("idx", Tensor), ("kc", Tensor),
                 ("vc", Tensor), ("kh", Tensor), ("vh", Tensor), ("k_raw", Tensor), ("v_raw", Tensor),
-                ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor)]
+                ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor),
+                ("q_norm", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("reserved1", ctypes.c_int32)]
 
 
 _lib = None
@@ -173,11 +175,13 @@ def _ws_ptr(ws):
 
 
 # ---------------------------------------------------------------- entry points
-def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None):
-    """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out."""
+def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None,
+             norm_k=None, norm_v=None, norm_eps: float = 1e-6):
+    """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out
+    (RMS-normalised with the fp32 gains norm_k / norm_v when given)."""
     a = CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
                      _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
-                     _tensor(v_out))
+                     _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, 0)
     _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
 
 
@@ -205,14 +209,15 @@ def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, se
 
 def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=None, k_raw=None,
               v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
-              window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False) -> AttnArgs:
+              window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False,
+              q_norm=None, norm_eps=1e-6) -> AttnArgs:
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
     return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
                     window, topk, scale, BATCH_INVARIANT if batch_invariant else 0, _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
                     _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
-                    _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse))
+                    _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse), _ptr(q_norm), norm_eps, 0)
 
 
 def _run_attn(fn, wsfn, q, pos0, o, workspace, stream, kw):

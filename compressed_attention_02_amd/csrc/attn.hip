@@ -56,7 +56,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
     __syncthreads();
     if (head < p.heads) {
       const float* qrow = reinterpret_cast<const float*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs + head * D;
-      for (int c = lane; c < D; c += 64) sQ[wave][c] = qrow[c];
+      float qv[DPL], ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        qv[e] = qrow[lane + 64 * e];
+        ss = fmaf(qv[e], qv[e], ss);
+      }
+      if (p.q_norm) {  // RMSNorm of the head's query
+        const float rq = rsqrtf(wave_sum(ss) / (float)D + p.norm_eps);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) qv[e] = qv[e] * rq * p.q_norm[lane + 64 * e];
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sQ[wave][lane + 64 * e] = qv[e];
     }
     __syncthreads();
     if (head >= p.heads) continue;

@@ -650,6 +650,25 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     __syncthreads();
   }
 
+  if (p.q_norm) {
+    // RMSNorm of each head's query: lane (col, grp) holds elements s*32 + grp*8 + e
+    // of head col, and the four grp lanes of a column hold the whole head
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf((float)Qb[t][s][e], (float)Qb[t][s][e], ss);
+      const float rq = rsqrtf(col_sum4(ss) / (float)D + p.norm_eps);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          Qb[t][s][e] = (__bf16)((float)Qb[t][s][e] * rq * p.q_norm[s * 32 + grp * 8 + e]);
+    }
+  }
+
   float m_run[HT], l_run[HT];
   f32x4 O[HT][DT];
 #pragma unroll

@@ -9,6 +9,10 @@
 // Thread layout: a row of d elements is CH 16-byte chunks; G threads ("row groups")
 // share one block's r rows (rows g, g+G, ...), so a ratio-128 block keeps 256
 // threads busy and a ratio-4 block 64.  Row groups are combined in LDS.
+//
+// Optional RMSNorm of the entries ([QbitAI] 混合注意力机制, Q/KV normalization:
+// KV entries are normalised before core attention): with a gain g the stored entry
+// is g * y / sqrt(mean(y^2) + eps).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -89,10 +93,39 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
       }
     }
   }
+  float kss = 0.f, vss = 0.f;
   if (active && g == 0) {
     const float inv = 1.0f / ws;
 #pragma unroll
-    for (int e = 0; e < N; ++e) { ak[e] *= inv; av[e] *= inv; }
+    for (int e = 0; e < N; ++e) {
+      ak[e] *= inv;
+      av[e] *= inv;
+      kss = fmaf(ak[e], ak[e], kss);
+      vss = fmaf(av[e], av[e], vss);
+    }
+  }
+  if (p.gk || p.gv) {
+    // RMSNorm of the entry: the row's ch chunk threads add their squares in LDS,
+    // in chunk order
+    __syncthreads();
+    s_acc[tid][0] = kss;
+    s_acc[tid][1] = vss;
+    __syncthreads();
+    if (active && g == 0) {
+      float sk = 0.f, sv = 0.f;
+      for (int cc = 0; cc < p.ch; ++cc) {
+        sk += s_acc[slot * per_block + cc][0];
+        sv += s_acc[slot * per_block + cc][1];
+      }
+      const float rk = rsqrtf(sk / (float)p.d + p.eps), rv = rsqrtf(sv / (float)p.d + p.eps);
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        if (p.gk) ak[e] = ak[e] * rk * p.gk[c * N + e];
+        if (p.gv) av[e] = av[e] * rv * p.gv[c * N + e];
+      }
+    }
+  }
+  if (active && g == 0) {
     T* ko = reinterpret_cast<T*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
     T* vo = reinterpret_cast<T*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
     Chunk<T>::store(ko, ak);

@@ -19,6 +19,7 @@ struct CompressP {
   int ch;         // 16-byte chunks per row
   int g;          // row groups per block (threads sharing one block's rows)
   int bpw;        // blocks per workgroup
+  const float* gk; const float* gv; float eps;  // RMSNorm gains of the entries (null: none)
 };
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid);
 
@@ -76,6 +77,7 @@ struct AttnP {
   uint32_t mask;
   int m, mh, W, topk;
   float scale;     // already resolved (never 0)
+  const float* q_norm; float norm_eps;  // RMSNorm gain of the queries (null: none)
   // this launch covers the virtual keys [key_lo, key_hi) of every row, cut into
   // `splits` splits of keys_per_split keys; its partials go to slots
   // split_base .. split_base + splits - 1 of splits_total per row.  With

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 1u
+#define V4ATTN_ABI_VERSION 2u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -98,6 +98,11 @@ typedef struct v4a_tensor {
  *   k_raw/v_raw  [batch][T_raw][d]
  *   logits       fp32 [batch][T_raw], row_stride must be 1, no alignment needed
  *   k_out/v_out  [batch][N_cap][d] indexed by absolute block id
+ *   norm_k/norm_v  fp32 [d] RMSNorm gains or NULL.  [QbitAI] 混合注意力机制,
+ *                the Q/KV normalization paragraph: KV entries are RMS-normalised
+ *                before core attention; with a gain the pooled entry y is
+ *                stored as g * y / sqrt(mean(y^2) + norm_eps) (fp32, then the
+ *                store rounding).  norm_eps >= 0, finite.
  * ------------------------------------------------------------------------- */
 typedef struct v4a_compress_args {
   uint32_t abi_version;
@@ -112,6 +117,10 @@ typedef struct v4a_compress_args {
   v4a_tensor k_raw, v_raw;
   v4a_tensor logits;
   v4a_tensor k_out, v_out;
+  const float* norm_k;
+  const float* norm_v;
+  float norm_eps;
+  int32_t reserved1;
 } v4a_compress_args;
 
 v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
@@ -185,6 +194,10 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *   sink         fp32 [H] or NULL
  *   o            fp32 out [batch][tq][H][d] (row = query token)
  *   lse          fp32 out [batch][tq][H] (row = query token) or ptr == NULL
+ *   q_norm       fp32 [d] RMSNorm gain for every head's query, or NULL:
+ *                q_h is used as g * q_h / sqrt(mean(q_h^2) + norm_eps) ([QbitAI]
+ *                混合注意力机制, Q/KV normalization); the bf16 path rounds the
+ *                normalised query to bf16.  norm_eps >= 0, finite.
  *   flags        V4A_BATCH_INVARIANT: a query's o and lse (and, through
  *                v4attn_decode_step, its idx) depend only on its own sequence's
  *                inputs, bit for bit, not on the other sequences of the batch
@@ -224,6 +237,9 @@ typedef struct v4a_attn_args {
   const float* sink;
   v4a_tensor o;
   v4a_tensor lse;
+  const float* q_norm;
+  float norm_eps;
+  int32_t reserved1;
 } v4a_attn_args;
 
 size_t v4attn_decode_workspace(const v4a_attn_args* args);

@@ -46,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
-    "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible",
+    "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible", "rms_norm",
 ]
 
 
@@ -95,6 +95,18 @@ def compress(x_raw: np.ndarray, logits: np.ndarray, raw_start: int, t0: int, n: 
         w = e / e.sum()
         out[bi] = w @ x_raw[lo:lo + r]
     return ids, out
+
+
+def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
+    """RMSNorm along the last axis: x / sqrt(mean(x^2) + eps) * gain.
+
+    [QbitAI] 混合注意力机制, the Q/KV normalization paragraph: before core attention
+    both the queries and the KV entries are RMS-normalised (to keep the logits from
+    blowing up).  The gain is one value per channel of the last axis.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
 
 
 def index_scores(qi: np.ndarray, wi: np.ndarray, ki: np.ndarray) -> np.ndarray:
@@ -178,14 +190,18 @@ def decode_keyset(p: int, *, branches: int, m: int, m_hca: int, window: int,
     return out
 
 
-def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, **ks):
+def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, q_norm=None,
+                 norm_eps: float = 1e-6, **ks):
     """Attention output of one query token: every enabled branch feeds one softmax.
 
     The configuration fixes the single softmax across CSA, HCA and SWA; [yage]
     three tiers describe the three views (far coarse, relevant blocks fine, recent
-    tokens in full) of one query.
+    tokens in full) of one query.  With a gain q_norm, each head's query is
+    RMS-normalised first (``rms_norm``).
     """
     d = q.shape[1]
+    if q_norm is not None:
+        q = rms_norm(q, q_norm, norm_eps)
     scale = 1.0 / math.sqrt(d) if scale is None or scale == 0.0 else scale
     parts = decode_keyset(p, **ks)
     if parts:
@@ -197,14 +213,14 @@ def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, *
     return attend(q, K, V, scale, sink)
 
 
-def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, **caches):
+def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=None, norm_eps=1e-6, **caches):
     """Batched decode: q [B, H, d], pos [B], idx [B, k]; caches batched on axis 0.
     Returns (o [B, H, d], lse [B, H])."""
     B = q.shape[0]
     os_, ls_ = [], []
     for b in range(B):
         kb = {k: (v[b] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in caches.items()}
-        o, lse = decode_query(q[b], int(pos[b]), scale=scale, sink=sink,
+        o, lse = decode_query(q[b], int(pos[b]), scale=scale, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
                               idx=None if idx is None else idx[b],
                               raw_start=0 if raw_start is None else int(raw_start[b]), **kb)
         os_.append(o)
@@ -212,14 +228,15 @@ def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, **caches)
     return np.stack(os_), np.stack(ls_)
 
 
-def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: int = 0, **caches):
+def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: int = 0, q_norm=None,
+            norm_eps=1e-6, **caches):
     """Chunked prefill of one sequence: row i is the query at p = pos0 + i and is the
     decode of that query over the caches after the chunk has been compressed.
     q [Tq, H, d], idx [Tq, k]; ``rows`` restricts the rows computed."""
     rows = range(q.shape[0]) if rows is None else rows
     os_, ls_ = [], []
     for i in rows:
-        o, lse = decode_query(q[i], pos0 + i, scale=scale, sink=sink,
+        o, lse = decode_query(q[i], pos0 + i, scale=scale, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
                               idx=None if idx is None else idx[i], raw_start=raw_start, **caches)
         os_.append(o)
         ls_.append(lse)

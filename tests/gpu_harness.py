@@ -139,7 +139,7 @@ class Run:
         for b, i in rows:
             check_topk_row(idx[b, i], self.oracle_scores(b, i), cfg.topk, f"topk b={b} i={i}")
 
-    def oracle_attn(self, rows=None, sink=None):
+    def oracle_attn(self, rows=None, sink=None, q_norm=None, norm_eps=1e-6):
         cfg = self.cfg
         idx = dev_to_np(self.step.idx)
         caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
@@ -151,17 +151,17 @@ class Run:
         out_o, out_l = [], []
         for b, i in rows:
             kw = {k: (v[b] if isinstance(v, np.ndarray) else v) for k, v in caches.items()}
-            o, l = O.decode_query(q[b, i], int(self.g["pos"][b]) + i, sink=sink,
+            o, l = O.decode_query(q[b, i], int(self.g["pos"][b]) + i, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
                                   idx=idx[b, i] if cfg.branches & 1 else None,
                                   raw_start=int(self.g["raw_start"][b]), **kw)
             out_o.append(o)
             out_l.append(l)
         return np.stack(out_o), np.stack(out_l)
 
-    def check_attn(self, rows=None):
+    def check_attn(self, rows=None, q_norm=None, norm_eps=1e-6):
         cfg = self.cfg
         rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.tq)] if rows is None else rows
-        ro, rl = self.oracle_attn(rows)
+        ro, rl = self.oracle_attn(rows, q_norm=q_norm, norm_eps=norm_eps)
         o = dev_to_np(self.step.o)
         l = dev_to_np(self.step.lse)
         go = np.stack([o[b, i] for b, i in rows])

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 13
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == 1
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 2
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -39,7 +39,7 @@ def _T(p=FAKE, bs=0, rs=0):
 
 
 def good_compress(**kw):
-    a = V.CompressArgs(1, V.BF16, 2, 128, 4, 0, 0, 4096, FAKE,
+    a = V.CompressArgs(V.ABI_VERSION, V.BF16, 2, 128, 4, 0, 0, 4096, FAKE,
                        _T(rs=128, bs=128 * 5000), _T(rs=128, bs=128 * 5000), _T(rs=1, bs=5000),
                        _T(rs=128, bs=128 * 1024), _T(rs=128, bs=128 * 1024))
     for k, v in kw.items():
@@ -48,7 +48,7 @@ def good_compress(**kw):
 
 
 def good_index(**kw):
-    a = V.IndexArgs(1, V.BF16, 2, 1, 64, 64, 4, 512, FAKE, 131072,
+    a = V.IndexArgs(V.ABI_VERSION, V.BF16, 2, 1, 64, 64, 4, 512, FAKE, 131072,
                     _T(bs=4096, rs=4096), _T(bs=64, rs=64), _T(bs=64 * 32768, rs=64),
                     _T(bs=512, rs=512), _T(None))
     for k, v in kw.items():
@@ -58,7 +58,7 @@ def good_index(**kw):
 
 def good_attn(**kw):
     T = _T
-    a = V.AttnArgs(1, V.BF16, V.F32, 2, 1, 64, 128, 7, 4, 128, 128, 512, 0.0, 0, FAKE, 131072,
+    a = V.AttnArgs(V.ABI_VERSION, V.BF16, V.F32, 2, 1, 64, 128, 7, 4, 128, 128, 512, 0.0, 0, FAKE, 131072,
                    T(bs=8192, rs=8192), T(bs=512, rs=512), T(bs=128 * 32768, rs=128),
                    T(bs=128 * 32768, rs=128), T(bs=128 * 1024, rs=128), T(bs=128 * 1024, rs=128),
                    T(bs=128 * 128, rs=128), T(bs=128 * 128, rs=128), FAKE, None,
@@ -74,7 +74,7 @@ def _st(fn, a, *extra):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("abi_version", 2, EINVAL), ("dtype", 7, EINVAL), ("ratio", 0, EINVAL), ("t0", 6, EINVAL),
+    ("abi_version", 1, EINVAL), ("dtype", 7, EINVAL), ("ratio", 0, EINVAL), ("t0", 6, EINVAL),
     ("n", -1, EINVAL), ("dim", 100, ENOTSUP), ("raw_start", None, EINVAL),
 ])
 def test_compress_rejects(field, value, code):

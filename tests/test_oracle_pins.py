@@ -428,3 +428,54 @@ def test_planted_mistakes_are_caught():
     rows, z = np.array(g["rows"]), np.array(g["logits"])
     e = np.exp(z[::-1] - z.max())
     assert not np.allclose((e / e.sum()) @ rows, g["expected"])
+
+
+# ----------------------------------------------------------------- RMSNorm (Q/KV normalization)
+def test_rms_norm_closed_forms():
+    # a constant vector c*1 normalises to sign(c)*1 (eps = 0); [3, 4] has mean square
+    # 12.5, so it becomes [3, 4] / sqrt(12.5) = [0.848528137..., 1.131370849...]
+    for c in (2.5, -0.125, 7.0):
+        assert np.array_equal(O.rms_norm(np.full(8, c), np.ones(8), 0.0), np.full(8, math.copysign(1.0, c)))
+    got = O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0)
+    assert np.allclose(got, [0.8485281374238570, 1.1313708498984760], rtol=0, atol=1e-15)
+    # eps enters under the root: mean square 12.5 + eps 3.5 = 16 -> [0.75, 1.0]
+    assert np.allclose(O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 3.5), [0.75, 1.0], rtol=0, atol=1e-15)
+    # the zero vector stays zero for eps > 0
+    assert np.array_equal(O.rms_norm(np.zeros(4), np.ones(4), 1e-6), np.zeros(4))
+
+
+def test_rms_norm_invariants():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 16))
+    g = rng.uniform(0.5, 2.0, 16)
+    y1 = O.rms_norm(x, np.ones(16), 0.0)
+    # unit mean square per row, independent of a positive scale, gain elementwise
+    assert np.allclose(np.mean(y1 * y1, axis=-1), 1.0, rtol=0, atol=1e-13)
+    assert np.allclose(O.rms_norm(3.7 * x, np.ones(16), 0.0), y1, rtol=0, atol=1e-13)
+    assert np.allclose(O.rms_norm(x, g, 0.0), y1 * g, rtol=0, atol=1e-13)
+    # a plausible mistake (mean |x| instead of the root mean square) breaks the unit
+    # mean square
+    bad = x / np.mean(np.abs(x), axis=-1, keepdims=True)
+    assert not np.allclose(np.mean(bad * bad, axis=-1), 1.0, atol=1e-3)
+
+
+def test_query_norm_makes_attention_scale_free():
+    # with the query normalised (eps = 0) a positive rescaling of q cannot change the
+    # output; without it, it changes the softmax temperature
+    rng = np.random.default_rng(32)
+    d, p = 8, 40
+    caches = dict(branches=6, m=4, m_hca=8, window=6, kh=rng.standard_normal((8, d)),
+                  vh=rng.standard_normal((8, d)), k_raw=rng.standard_normal((p + 1, d)),
+                  v_raw=rng.standard_normal((p + 1, d)), raw_start=0)
+    q = rng.standard_normal((3, d))
+    g = rng.uniform(0.5, 1.5, d)
+    o1, l1 = O.decode_query(q, p, q_norm=g, norm_eps=0.0, **caches)
+    o2, _ = O.decode_query(5.0 * q, p, q_norm=g, norm_eps=0.0, **caches)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12)
+    o3, _ = O.decode_query(5.0 * q, p, **caches)
+    o4, _ = O.decode_query(q, p, **caches)
+    assert not np.allclose(o3, o4, atol=1e-6)
+    # and normalising is the same as feeding the normalised query
+    qn = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True)) * g
+    o5, l5 = O.decode_query(qn, p, **caches)
+    assert np.allclose(o1, o5, rtol=0, atol=1e-12) and np.allclose(l1, l5, rtol=0, atol=1e-12)
