@@ -47,6 +47,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
     "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible", "rms_norm",
+    "rope", "compress_entries",
 ]
 
 
@@ -107,6 +108,50 @@ def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+
+
+def rope(x: np.ndarray, pos, dims: int, base: float) -> np.ndarray:
+    """Partial rotary position encoding of the last ``dims`` channels at ``pos``.
+
+    [QbitAI] 混合注意力机制, the partial RoPE paragraph: only the last 64 channels of
+    the queries and KV entries are rotated, the rest are left alone.  The rotation
+    itself is the usual one (the pages name it, not its form): channel pairs
+    (2j, 2j+1) of the rotated part turn by the angle pos * base^(-2j/dims).
+    ``pos`` is a scalar or one position per row of x.
+    """
+    x = np.array(x, dtype=np.float64)
+    if dims == 0:
+        return x
+    d = x.shape[-1]
+    lo = d - dims
+    j = np.arange(dims // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / dims)
+    ang = np.multiply.outer(np.asarray(pos, dtype=np.float64), theta)
+    c, s_ = np.cos(ang), np.sin(ang)
+    a, b = x[..., lo::2].copy(), x[..., lo + 1::2].copy()
+    x[..., lo::2] = a * c - b * s_
+    x[..., lo + 1::2] = a * s_ + b * c
+    return x
+
+
+def compress_entries(x_raw, logits, raw_start, t0, n, r, *, gain=None, eps=1e-6, rope_dims=0, rope_base=1e4):
+    """Compressed entries with the layer's pre-attention operations.
+
+    Raw rows hold per-token entries already rotated at their own positions (the form
+    the window branch attends to).  An entry is pooled in the unrotated frame, then
+    RMS-normalised (``rms_norm``, with a gain) and rotated at the position of its
+    block's last token, (j+1)*r - 1 (a reading: the pages give entries a position
+    but not which one).  Returns (block ids, rows) like ``compress``.
+    """
+    x = np.asarray(x_raw, dtype=np.float64)
+    if rope_dims:
+        x = rope(x, -(raw_start + np.arange(x.shape[0])), rope_dims, rope_base)
+    ids, out = compress(x, logits, raw_start, t0, n, r)
+    if gain is not None:
+        out = rms_norm(out, gain, eps)
+    if rope_dims:
+        out = rope(out, (ids + 1) * r - 1, rope_dims, rope_base)
+    return ids, out
 
 
 def index_scores(qi: np.ndarray, wi: np.ndarray, ki: np.ndarray) -> np.ndarray:
@@ -191,17 +236,23 @@ def decode_keyset(p: int, *, branches: int, m: int, m_hca: int, window: int,
 
 
 def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, q_norm=None,
-                 norm_eps: float = 1e-6, **ks):
+                 norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4, rope_out: bool = False,
+                 **ks):
     """Attention output of one query token: every enabled branch feeds one softmax.
 
     The configuration fixes the single softmax across CSA, HCA and SWA; [yage]
     three tiers describe the three views (far coarse, relevant blocks fine, recent
     tokens in full) of one query.  With a gain q_norm, each head's query is
-    RMS-normalised first (``rms_norm``).
+    RMS-normalised first (``rms_norm``); with rope_dims it is then rotated at p
+    (``rope``).  rope_out rotates the output at -p: [QbitAI] 混合注意力机制, the
+    partial RoPE paragraph, since the KV entries are the values too, the output
+    would carry absolute positions, and the rotation at -p leaves relative ones.
     """
     d = q.shape[1]
     if q_norm is not None:
         q = rms_norm(q, q_norm, norm_eps)
+    if rope_dims:
+        q = rope(q, p, rope_dims, rope_base)
     scale = 1.0 / math.sqrt(d) if scale is None or scale == 0.0 else scale
     parts = decode_keyset(p, **ks)
     if parts:
@@ -210,10 +261,14 @@ def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, q
     else:
         K = np.zeros((0, d))
         V = np.zeros((0, d))
-    return attend(q, K, V, scale, sink)
+    o, lse = attend(q, K, V, scale, sink)
+    if rope_out and rope_dims:
+        o = rope(o, -p, rope_dims, rope_base)
+    return o, lse
 
 
-def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=None, norm_eps=1e-6, **caches):
+def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=None, norm_eps=1e-6, rope_dims=0,
+           rope_base=1e4, rope_out=False, **caches):
     """Batched decode: q [B, H, d], pos [B], idx [B, k]; caches batched on axis 0.
     Returns (o [B, H, d], lse [B, H])."""
     B = q.shape[0]
@@ -221,6 +276,7 @@ def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=No
     for b in range(B):
         kb = {k: (v[b] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in caches.items()}
         o, lse = decode_query(q[b], int(pos[b]), scale=scale, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
+                              rope_dims=rope_dims, rope_base=rope_base, rope_out=rope_out,
                               idx=None if idx is None else idx[b],
                               raw_start=0 if raw_start is None else int(raw_start[b]), **kb)
         os_.append(o)
@@ -229,7 +285,7 @@ def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=No
 
 
 def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: int = 0, q_norm=None,
-            norm_eps=1e-6, **caches):
+            norm_eps=1e-6, rope_dims=0, rope_base=1e4, rope_out=False, **caches):
     """Chunked prefill of one sequence: row i is the query at p = pos0 + i and is the
     decode of that query over the caches after the chunk has been compressed.
     q [Tq, H, d], idx [Tq, k]; ``rows`` restricts the rows computed."""
@@ -237,6 +293,7 @@ def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: i
     os_, ls_ = [], []
     for i in rows:
         o, lse = decode_query(q[i], pos0 + i, scale=scale, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
+                              rope_dims=rope_dims, rope_base=rope_base, rope_out=rope_out,
                               idx=None if idx is None else idx[i], raw_start=raw_start, **caches)
         os_.append(o)
         ls_.append(lse)

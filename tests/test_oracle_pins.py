@@ -479,3 +479,91 @@ def test_query_norm_makes_attention_scale_free():
     qn = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True)) * g
     o5, l5 = O.decode_query(qn, p, **caches)
     assert np.allclose(o1, o5, rtol=0, atol=1e-12) and np.allclose(l1, l5, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- partial RoPE
+def test_rope_closed_forms():
+    x = np.array([0.3, -1.2, 1.0, 0.0, 1.0, 0.0])
+    # dims = 0 leaves everything; only the last `dims` channels ever move
+    assert np.array_equal(O.rope(x, 7, 0, 1e4), x)
+    y = O.rope(x, 7, 4, 1e4)
+    assert np.array_equal(y[:2], x[:2])
+    # the first pair of the rotated part turns by pos radians: (1, 0) at pos 1 is
+    # (cos 1, sin 1) = (0.5403023058681398, 0.8414709848078965); at pos 0 nothing moves
+    y = O.rope(np.array([1.0, 0.0]), 1, 2, 1e4)
+    assert np.allclose(y, [0.5403023058681398, 0.8414709848078965], rtol=0, atol=1e-15)
+    assert np.array_equal(O.rope(x, 0, 4, 1e4), x)
+    # the second pair of a 4-channel part turns by pos * base^(-1/2): base 1e4 and
+    # pos 100 give 1 radian there (and 100 radians on the first pair:
+    # cos 100 = 0.8623188722876839, sin 100 = -0.5063656411097588)
+    y = O.rope(np.array([1.0, 0.0, 1.0, 0.0]), 100, 4, 1e4)
+    assert np.allclose(y, [0.8623188722876839, -0.5063656411097588, 0.5403023058681398, 0.8414709848078965],
+                       rtol=0, atol=1e-13)
+
+
+def test_rope_group_and_relative_properties():
+    rng = np.random.default_rng(41)
+    q, k = rng.standard_normal((2, 16)), rng.standard_normal((2, 16))
+    for m, n in ((5, 3), (1_000_003, 17), (0, 250)):
+        a = O.rope(q, m, 8, 1e4)
+        # norm preserved, a rotation at -m undoes one at m, angles add
+        assert np.allclose(np.linalg.norm(a, axis=-1), np.linalg.norm(q, axis=-1), rtol=0, atol=1e-12)
+        assert np.allclose(O.rope(a, -m, 8, 1e4), q, rtol=0, atol=1e-9)
+        assert np.allclose(O.rope(O.rope(q, n, 8, 1e4), m, 8, 1e4), O.rope(q, m + n, 8, 1e4), rtol=0, atol=1e-9)
+        # dot products depend on the relative position only
+        lhs = np.sum(a * O.rope(k, n, 8, 1e4), axis=-1)
+        rhs = np.sum(O.rope(q, m - n, 8, 1e4) * k, axis=-1)
+        assert np.allclose(lhs, rhs, rtol=0, atol=1e-9)
+    # a plausible mistake (pairs (j, j + dims/2) instead of (2j, 2j+1)) breaks the
+    # closed form of the second pair
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    half = x.copy()
+    ang = np.array([100.0, 1.0])
+    half[[0, 1]] = x[[0, 1]] * np.cos(ang) - x[[2, 3]] * np.sin(ang)
+    half[[2, 3]] = x[[0, 1]] * np.sin(ang) + x[[2, 3]] * np.cos(ang)
+    assert not np.allclose(half, O.rope(x, 100, 4, 1e4), atol=1e-3)
+
+
+def test_rope_entries_of_identical_tokens():
+    # tokens that are one unrotated vector u, each rotated at its own position: the
+    # pooled entry of a block is u itself (any weights), rotated at the block's last
+    # position (and normalised first when a gain is given)
+    rng = np.random.default_rng(42)
+    d, r, T = 16, 8, 40
+    u = rng.standard_normal(d)
+    raw_start = 5
+    pos = raw_start + np.arange(T)
+    x = O.rope(np.tile(u, (T, 1)), pos, 8, 1e4)
+    z = rng.standard_normal(T)
+    ids, ent = O.compress_entries(x, z, raw_start, 8, 32, r, rope_dims=8, rope_base=1e4)
+    assert list(ids) == [1, 2, 3, 4]
+    for bi, j in enumerate(ids):
+        assert np.allclose(ent[bi], O.rope(u, (j + 1) * r - 1, 8, 1e4), rtol=0, atol=1e-12)
+    g = rng.uniform(0.5, 1.5, d)
+    _, ent2 = O.compress_entries(x, z, raw_start, 8, 32, r, gain=g, eps=0.0, rope_dims=8, rope_base=1e4)
+    un = u / np.sqrt(np.mean(u * u)) * g
+    assert np.allclose(ent2[0], O.rope(un, 2 * r - 1, 8, 1e4), rtol=0, atol=1e-12)
+
+
+def test_rope_output_rotation_makes_the_layer_shift_invariant():
+    # shared K = V entries rotated at their positions, the query rotated at p and the
+    # output rotated at -p: shifting every position leaves the output unchanged (only
+    # relative positions remain), and without the output rotation it does not.  The
+    # window covers every token so that a shift adds no key (an HCA or CSA history
+    # would gain empty entries); the entries' own rotation is pinned above.
+    rng = np.random.default_rng(43)
+    d, R = 16, 8
+    p0 = 45
+    u = rng.standard_normal((p0 + 1, d))       # unrotated per-token entries
+    q = rng.standard_normal((2, d))
+    outs = {}
+    for shift in (0, 1000, 123457):
+        raw = O.rope(u, shift + np.arange(p0 + 1), R, 1e4)
+        for ro in (True, False):
+            outs[shift, ro] = O.decode_query(q, shift + p0, branches=4, m=4, m_hca=8, window=p0 + 1,
+                                             k_raw=raw, v_raw=raw, raw_start=shift, rope_dims=R, rope_base=1e4,
+                                             rope_out=ro)
+    for shift in (1000, 123457):
+        assert np.allclose(outs[0, True][0], outs[shift, True][0], rtol=0, atol=1e-9)
+        assert np.allclose(outs[0, True][1], outs[shift, True][1], rtol=0, atol=1e-9)
+        assert not np.allclose(outs[0, False][0], outs[shift, False][0], atol=1e-4)
