@@ -31,7 +31,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
 BATCH_INVARIANT = 1   # v4a_attn_args.flags
-ABI_VERSION = 2
+ROPE_OUTPUT = 2       # v4a_attn_args.flags
+ROPE_V = 1            # v4a_compress_args.rope_flags
+ABI_VERSION = 3
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6}
 
@@ -50,7 +52,8 @@ class CompressArgs(ctypes.Structure):
                 ("t0", ctypes.c_int64), ("n", ctypes.c_int64), ("raw_start", ctypes.c_void_p),
                 ("k_raw", Tensor), ("v_raw", Tensor), ("logits", Tensor), ("k_out", Tensor),
                 ("v_out", Tensor), ("norm_k", ctypes.c_void_p), ("norm_v", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+                ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("rope_flags", ctypes.c_uint32)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -70,7 +73,8 @@ class AttnArgs(ctypes.Structure):
                 ("pos_max", ctypes.c_int64), ("q", Tensor), ("idx", Tensor), ("kc", Tensor),
                 ("vc", Tensor), ("kh", Tensor), ("vh", Tensor), ("k_raw", Tensor), ("v_raw", Tensor),
                 ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor),
-                ("q_norm", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+                ("q_norm", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("reserved1", ctypes.c_int32)]
 
 
 _lib = None
@@ -176,12 +180,15 @@ def _ws_ptr(ws):
 
 # ---------------------------------------------------------------- entry points
 def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None,
-             norm_k=None, norm_v=None, norm_eps: float = 1e-6):
+             norm_k=None, norm_v=None, norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4,
+             rope_v: bool = False):
     """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out
-    (RMS-normalised with the fp32 gains norm_k / norm_v when given)."""
+    (RMS-normalised with the fp32 gains norm_k / norm_v when given; with rope_dims,
+    raw rows are rotated at their positions and entries at their block's last one)."""
     a = CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
                      _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
-                     _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, 0)
+                     _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, rope_dims, rope_base,
+                     ROPE_V if rope_v else 0)
     _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
 
 
@@ -210,14 +217,16 @@ def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, se
 def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=None, k_raw=None,
               v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
               window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False,
-              q_norm=None, norm_eps=1e-6) -> AttnArgs:
+              q_norm=None, norm_eps=1e-6, rope_dims=0, rope_base=1e4, rope_out=False) -> AttnArgs:
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
     return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
-                    window, topk, scale, BATCH_INVARIANT if batch_invariant else 0, _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
+                    window, topk, scale, (BATCH_INVARIANT if batch_invariant else 0) | (ROPE_OUTPUT if rope_out else 0),
+                    _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
                     _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
-                    _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse), _ptr(q_norm), norm_eps, 0)
+                    _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse), _ptr(q_norm), norm_eps, rope_dims,
+                    rope_base, 0)
 
 
 def _run_attn(fn, wsfn, q, pos0, o, workspace, stream, kw):

@@ -179,6 +179,13 @@ v4a_status validate_compress(const v4a_compress_args* a) {
   if (a->dim < 1) return fail(V4A_EINVAL, "dim must be >= 1");
   if ((a->dim * esize(a->dtype)) % 16 != 0 || a->dim > 512)
     return fail(V4A_ENOTSUP, "dim %d: rows must be a multiple of 16 bytes and dim <= 512", a->dim);
+  if (a->rope_dims < 0 || a->rope_dims % 2 != 0 || a->rope_dims > a->dim)
+    return fail(V4A_EINVAL, "rope_dims must be even and in [0, dim]");
+  if (a->rope_dims > 0 && !(a->rope_base > 0.f && std::isfinite(a->rope_base)))
+    return fail(V4A_EINVAL, "rope_base must be finite and > 0");
+  if (a->rope_flags & ~V4A_ROPE_V) return fail(V4A_EINVAL, "unknown rope_flags 0x%x", a->rope_flags);
+  if ((int64_t)a->ratio * (a->rope_dims / 2) > 4096)
+    return fail(V4A_ENOTSUP, "rope: ratio * rope_dims / 2 must be <= 4096");
   if ((a->norm_k || a->norm_v) && !(a->norm_eps >= 0.f && std::isfinite(a->norm_eps)))
     return fail(V4A_EINVAL, "norm_eps must be finite and >= 0");
   if ((a->norm_k && !aligned(a->norm_k, 4)) || (a->norm_v && !aligned(a->norm_v, 4)))
@@ -246,7 +253,12 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
   if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
   if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
-  if (a->flags & ~V4A_BATCH_INVARIANT) return fail(V4A_EINVAL, "unknown flags 0x%x", a->flags);
+  if (a->flags & ~(V4A_BATCH_INVARIANT | V4A_ROPE_OUTPUT)) return fail(V4A_EINVAL, "unknown flags 0x%x", a->flags);
+  if (a->rope_dims < 0 || a->rope_dims % 2 != 0 || a->rope_dims > a->dim)
+    return fail(V4A_EINVAL, "rope_dims must be even and in [0, dim]");
+  if (a->rope_dims > 0 && !(a->rope_base > 0.f && std::isfinite(a->rope_base)))
+    return fail(V4A_EINVAL, "rope_base must be finite and > 0");
+  if ((a->flags & V4A_ROPE_OUTPUT) && a->rope_dims == 0) return fail(V4A_EINVAL, "V4A_ROPE_OUTPUT needs rope_dims > 0");
   if (a->q_norm && !(a->norm_eps >= 0.f && std::isfinite(a->norm_eps)))
     return fail(V4A_EINVAL, "norm_eps must be finite and >= 0");
   if (a->q_norm && !aligned(a->q_norm, 4)) return fail(V4A_EINVAL, "q_norm must be 4-byte aligned");
@@ -317,6 +329,8 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   p.m = a->csa_ratio; p.mh = a->hca_ratio; p.W = a->window; p.topk = a->topk;
   p.scale = a->scale != 0.f ? a->scale : 1.0f / std::sqrt((float)a->dim);
   p.q_norm = a->q_norm; p.norm_eps = a->norm_eps;
+  p.rope = a->rope_dims; p.rope_out = (a->flags & V4A_ROPE_OUTPUT) != 0;
+  p.rope_lb = a->rope_dims > 0 ? std::log2((double)a->rope_base) : 0.0;
   p.key_lo = 0; p.key_hi = INT64_MAX;
   p.splits = (int)P.splits; p.keys_per_split = (int)P.kps;
   p.split_base = 0; p.splits_total = (int)P.splits;
@@ -621,6 +635,8 @@ v4a_status v4attn_compress(const v4a_compress_args* a, hipStream_t stream) {
   p.g = std::max(1, std::min(a->ratio, 256 / p.ch));
   p.bpw = std::max(1, 256 / (p.ch * p.g));
   p.gk = a->norm_k; p.gv = a->norm_v; p.eps = a->norm_eps;
+  p.rope = a->rope_dims; p.rope_v = (a->rope_flags & V4A_ROPE_V) != 0;
+  p.rope_lb = a->rope_dims > 0 ? std::log2((double)a->rope_base) : 0.0;
   if (cdiv(nb, p.bpw) > INT32_MAX || a->batch > 65535) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(hip_check(launch_compress(a->dtype, p, a->batch, stream, V4A_K_COMPRESS), "compress launch"));
   return ok();

@@ -67,6 +67,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) qv[e] = qv[e] * rq * p.q_norm[lane + 64 * e];
       }
+      if (p.rope) {  // then its rotation at pos: pair partners sit in neighbouring lanes
+        const int lo = D - p.rope;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          const float other = __shfl_xor(qv[e], 1);
+          const int ch = lane + 64 * e;
+          if (ch >= lo) {
+            float cs, sn;
+            rope_cs((double)pos, (ch - lo) / 2, p.rope, p.rope_lb, cs, sn);
+            qv[e] = (ch & 1) ? fmaf(other, sn, qv[e] * cs) : fmaf(-other, sn, qv[e] * cs);
+          }
+        }
+      }
 #pragma unroll
       for (int e = 0; e < DPL; ++e) sQ[wave][lane + 64 * e] = qv[e];
     }
@@ -115,7 +128,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
       const float f = finish_head(m_run, l_run, p.sink, head, &lse);
       float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) orow[lane + 64 * e] = acc[e] * f;
+      for (int e = 0; e < DPL; ++e) {
+        float a = acc[e] * f;
+        if (p.rope_out) a = rope_back_pair(p, a, lane + 64 * e, pos);
+        orow[lane + 64 * e] = a;
+      }
       if (lane == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
       const int64_t slot = ((int64_t)row * p.heads + head) * p.splits_total + p.split_base + split;

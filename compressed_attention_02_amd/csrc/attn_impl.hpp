@@ -65,6 +65,19 @@ __device__ __forceinline__ float finish_head(float m, float l, const float* sink
   return l > 0.f ? scale_o / l : 0.f;
 }
 
+// Output channel ch of a query at pos, turned back by -pos when it lies in the
+// rotated part: its pair partner is the neighbouring lane (ch ^ 1 sits in lane ^ 1),
+// so every lane of the wave must call this together.
+__device__ __forceinline__ float rope_back_pair(const AttnP& p, float a, int ch, int64_t pos) {
+  const float other = __shfl_xor(a, 1);
+  const int lo = p.dim - p.rope;
+  if (ch < lo) return a;
+  float cs, sn;
+  rope_cs((double)pos, (ch - lo) / 2, p.rope, p.rope_lb, cs, sn);
+  // x' = x c + y s, y' = -x s + y c (the rotation by -angle)
+  return (ch & 1) ? fmaf(-other, sn, a * cs) : fmaf(other, sn, a * cs);
+}
+
 // ------------------------------------------------------------------ merge
 // Combination of slots merge_lo .. splits_total - 1 of one (row, head)'s split
 // partials (U_s, m_s, l_s), m in base 2: weights exp2(m_s - max m), o = sum w_s U_s
@@ -143,7 +156,9 @@ __device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, in
     for (int gg = 1; gg < G; ++gg) a += s_red[gg * DW + c];
     float lse;
     const float f = finish_head(M, l, p.sink, head, &lse);
-    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + d0 + c] = a * f;
+    a *= f;
+    if (p.rope_out) a = rope_back_pair(p, a, d0 + c, p.pos0[b] + i);
+    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + d0 + c] = a;
     if (c == 0 && d0 == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
   }
 }
@@ -266,7 +281,9 @@ __device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int
       } else {
         float lse;
         const float f = finish_head(M, l, p.sink, h, &lse);
-        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a * f;
+        a *= f;
+        if (p.rope_out) a = rope_back_pair(p, a, c, p.pos0[b] + i);
+        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a;
         if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + h] = lse;
       }
     }
@@ -650,22 +667,45 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     __syncthreads();
   }
 
-  if (p.q_norm) {
-    // RMSNorm of each head's query: lane (col, grp) holds elements s*32 + grp*8 + e
-    // of head col, and the four grp lanes of a column hold the whole head
+  if (p.q_norm || p.rope) {
+    // RMSNorm of each head's query, then its rotation at pos, in fp32 and rounded
+    // once: lane (col, grp) holds elements s*32 + grp*8 + e of head col, and the
+    // four grp lanes of a column hold the whole head
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
+      float qf[KS][8];
       float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf((float)Qb[t][s][e], (float)Qb[t][s][e], ss);
-      const float rq = rsqrtf(col_sum4(ss) / (float)D + p.norm_eps);
+        for (int e = 0; e < 8; ++e) {
+          qf[s][e] = (float)Qb[t][s][e];
+          ss = fmaf(qf[s][e], qf[s][e], ss);
+        }
+      if (p.q_norm) {
+        const float rq = rsqrtf(col_sum4(ss) / (float)D + p.norm_eps);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[s][e] = qf[s][e] * rq * p.q_norm[s * 32 + grp * 8 + e];
+      }
+      if (p.rope) {
+        const int lo = D - p.rope;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            const int e0 = s * 32 + grp * 8 + 2 * k2;
+            if (e0 < lo) continue;
+            float cs, sn;
+            rope_cs((double)pos, (e0 - lo) / 2, p.rope, p.rope_lb, cs, sn);
+            rot2(qf[s][2 * k2], qf[s][2 * k2 + 1], cs, sn, false);
+          }
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Qb[t][s][e] = (__bf16)((float)Qb[t][s][e] * rq * p.q_norm[s * 32 + grp * 8 + e]);
+        for (int e = 0; e < 8; ++e) Qb[t][s][e] = (__bf16)qf[s][e];
     }
   }
 
@@ -719,9 +759,20 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
       const float f = finish_head(m_run[t], l, p.sink, head, &lse);
       float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(orow + dt * 16 + 4 * grp) =
-            make_float4(O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f);
+      for (int dt = 0; dt < DT; ++dt) {
+        float ov[4] = {O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f};
+        if (p.rope_out) {  // back at -pos: channels dt*16 + 4*grp + e, pairs inside the lane
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int e0 = dt * 16 + 4 * grp + 2 * k2;
+            if (e0 < D - p.rope) continue;
+            float cs, sn;
+            rope_cs((double)pos, (e0 - (D - p.rope)) / 2, p.rope, p.rope_lb, cs, sn);
+            rot2(ov[2 * k2], ov[2 * k2 + 1], cs, sn, true);
+          }
+        }
+        *reinterpret_cast<float4*>(orow + dt * 16 + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      }
       if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
       const int64_t slot = ((int64_t)row * p.heads + head) * p.splits_total + p.split_base + split;

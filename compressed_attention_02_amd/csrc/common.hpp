@@ -142,6 +142,23 @@ __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// Partial RoPE: cos and sin of the angle pos * 2^(-2i/R * lb) of channel pair i
+// (lb = log2 of the base).  The angle is formed and reduced to [-pi, pi] in fp64, so
+// positions in the millions keep their phase to ~1e-10 rad; the reduced angle then
+// goes through the fp32 sincos.
+__device__ __forceinline__ void rope_cs(double pos, int i, int R, double lb, float& c, float& s) {
+  const double th = exp2(-2.0 * (double)i / (double)R * lb);
+  double a = pos * th;
+  a -= 6.283185307179586 * rint(a * 0.15915494309189535);
+  sincosf((float)a, &s, &c);
+}
+// (x, y) turned by the angle whose cos and sin are (c, s); by its opposite with neg
+__device__ __forceinline__ void rot2(float& x, float& y, float c, float s, bool neg) {
+  const float sn = neg ? -s : s;
+  const float nx = x * c - y * sn, ny = x * sn + y * c;
+  x = nx;
+  y = ny;
+}
 // exp(x) with -inf -> 0
 __device__ __forceinline__ float fexp(float x) { return __expf(x); }
 

@@ -12,7 +12,10 @@
 //
 // Optional RMSNorm of the entries ([QbitAI] 混合注意力机制, Q/KV normalization:
 // KV entries are normalised before core attention): with a gain g the stored entry
-// is g * y / sqrt(mean(y^2) + eps).
+// is g * y / sqrt(mean(y^2) + eps).  Optional partial RoPE (the partial RoPE
+// paragraph of the same section): raw rows are rotated at their own positions; the
+// entry is pooled and normalised in the unrotated frame and stored rotated at the
+// position of its block's last token.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,11 +38,15 @@ template <> struct Chunk<uint16_t> {
   __device__ static void store(uint16_t* p, const float* o) { *reinterpret_cast<uint4*>(p) = pack8(o); }
 };
 
+// Partial RoPE table of the in-block offsets: (cos, sin) of u * theta_i for u < r
+constexpr int kRopeTab = 4096;
+
 template <typename T>
 __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   constexpr int N = Chunk<T>::N;
   __shared__ float s_max[256];
   __shared__ float s_acc[256][2 * N + 1];
+  __shared__ float2 s_cs[kRopeTab];
 
   const int tid = threadIdx.x;
   const int per_block = p.ch * p.g;
@@ -58,6 +65,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   if (active)
     for (int u = g; u < p.r; u += p.g) mx = fmaxf(mx, lg[u]);
   s_max[tid] = mx;
+  const int R = p.rope, hr = p.rope / 2, lo = p.d - p.rope;
+  if (R)
+    for (int t = tid; t < p.r * hr; t += 256) {
+      float cs, sn;
+      rope_cs((double)(t / hr), t % hr, R, p.rope_lb, cs, sn);
+      s_cs[t] = make_float2(cs, sn);
+    }
   __syncthreads();
   if (active)
     for (int gg = 0; gg < p.g; ++gg) mx = fmaxf(mx, s_max[slot * per_block + gg * p.ch + c]);
@@ -74,6 +88,18 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
       float xk[N], xv[N];
       Chunk<T>::load(kr + (int64_t)u * p.kr_rs, xk);
       Chunk<T>::load(vr + (int64_t)u * p.vr_rs, xv);
+      if (R) {
+        // raw rows are rotated at their positions j*r + u: undo the in-block part u
+        // here, the block part j*r once on the pooled entry
+#pragma unroll
+        for (int k2 = 0; k2 < N / 2; ++k2) {
+          const int e0 = c * N + 2 * k2;
+          if (e0 < lo) continue;
+          const float2 cs = s_cs[u * hr + (e0 - lo) / 2];
+          rot2(xk[2 * k2], xk[2 * k2 + 1], cs.x, cs.y, true);
+          if (p.rope_v) rot2(xv[2 * k2], xv[2 * k2 + 1], cs.x, cs.y, true);
+        }
+      }
       ws += w;
 #pragma unroll
       for (int e = 0; e < N; ++e) { ak[e] = fmaf(w, xk[e], ak[e]); av[e] = fmaf(w, xv[e], av[e]); }
@@ -100,6 +126,20 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
     for (int e = 0; e < N; ++e) {
       ak[e] *= inv;
       av[e] *= inv;
+    }
+    if (R) {  // into the unrotated frame: undo the block's base rotation j*r
+#pragma unroll
+      for (int k2 = 0; k2 < N / 2; ++k2) {
+        const int e0 = c * N + 2 * k2;
+        if (e0 < lo) continue;
+        float cs, sn;
+        rope_cs((double)(j * p.r), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
+        rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, true);
+        if (p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, true);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
       kss = fmaf(ak[e], ak[e], kss);
       vss = fmaf(av[e], av[e], vss);
     }
@@ -126,6 +166,17 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
     }
   }
   if (active && g == 0) {
+    if (R) {  // the entry's own rotation, at its block's last position
+#pragma unroll
+      for (int k2 = 0; k2 < N / 2; ++k2) {
+        const int e0 = c * N + 2 * k2;
+        if (e0 < lo) continue;
+        float cs, sn;
+        rope_cs((double)((j + 1) * p.r - 1), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
+        rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, false);
+        if (p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, false);
+      }
+    }
     T* ko = reinterpret_cast<T*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
     T* vo = reinterpret_cast<T*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
     Chunk<T>::store(ko, ak);

@@ -20,6 +20,9 @@ struct CompressP {
   int g;          // row groups per block (threads sharing one block's rows)
   int bpw;        // blocks per workgroup
   const float* gk; const float* gv; float eps;  // RMSNorm gains of the entries (null: none)
+  int rope;            // rotated channels R (0: off), the last R of each row
+  int rope_v;          // raw V rows are rotated too
+  double rope_lb;      // log2 of the RoPE base
 };
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid);
 
@@ -78,6 +81,7 @@ struct AttnP {
   int m, mh, W, topk;
   float scale;     // already resolved (never 0)
   const float* q_norm; float norm_eps;  // RMSNorm gain of the queries (null: none)
+  int rope; int rope_out; double rope_lb;  // query rotation (R channels), output rotation at -p
   // this launch covers the virtual keys [key_lo, key_hi) of every row, cut into
   // `splits` splits of keys_per_split keys; its partials go to slots
   // split_base .. split_base + splits - 1 of splits_total per row.  With

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 2u
+#define V4ATTN_ABI_VERSION 3u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -103,6 +103,15 @@ typedef struct v4a_tensor {
  *                before core attention; with a gain the pooled entry y is
  *                stored as g * y / sqrt(mean(y^2) + norm_eps) (fp32, then the
  *                store rounding).  norm_eps >= 0, finite.
+ *   rope_dims    R, even, 0 <= R <= d (0: off).  [QbitAI] 混合注意力机制, the
+ *                partial RoPE paragraph: the last 64 channels of the KV entries
+ *                carry a rotary position encoding.  Raw K rows (and raw V rows
+ *                when rope_flags & V4A_ROPE_V) are taken as rotated at their own
+ *                positions t: channel pairs (d-R+2i, d-R+2i+1) turned by
+ *                t * rope_base^(-2i/R).  The entry is pooled in the unrotated
+ *                frame, normalised there, and stored rotated at the position of
+ *                its block's last token, (j+1)*r - 1.  Angles are reduced in
+ *                fp64.  rope_base > 0, finite.
  * ------------------------------------------------------------------------- */
 typedef struct v4a_compress_args {
   uint32_t abi_version;
@@ -120,7 +129,9 @@ typedef struct v4a_compress_args {
   const float* norm_k;
   const float* norm_v;
   float norm_eps;
-  int32_t reserved1;
+  int32_t rope_dims;
+  float rope_base;
+  uint32_t rope_flags;  /* V4A_ROPE_V or 0 */
 } v4a_compress_args;
 
 v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
@@ -198,7 +209,13 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *                q_h is used as g * q_h / sqrt(mean(q_h^2) + norm_eps) ([QbitAI]
  *                混合注意力机制, Q/KV normalization); the bf16 path rounds the
  *                normalised query to bf16.  norm_eps >= 0, finite.
- *   flags        V4A_BATCH_INVARIANT: a query's o and lse (and, through
+ *   rope_dims    R, even, 0 <= R <= d (0: off): the query (after q_norm) is
+ *                rotated at its position p like the entries (see
+ *                v4attn_compress); rope_base > 0, finite.  The caches hold
+ *                entries already rotated (compress, and the caller's raw rows).
+ *   flags        V4A_ROPE_OUTPUT (with rope_dims): o's last R channels are
+ *                rotated at -p.
+ *                V4A_BATCH_INVARIANT: a query's o and lse (and, through
  *                v4attn_decode_step, its idx) depend only on its own sequence's
  *                inputs, bit for bit, not on the other sequences of the batch
  *                nor on pos_max.  Key splits then have a fixed size (256 keys;
@@ -212,6 +229,12 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
 /* [wiki] the batch-invariance material: results that must not change with
  * the batch a request is served in. */
 #define V4A_BATCH_INVARIANT 1u
+/* [QbitAI] 混合注意力机制, partial RoPE paragraph: the KV entries are the values
+ * too, so the output would carry absolute positions; V4A_ROPE_OUTPUT rotates o
+ * at -p (its last rope_dims channels) to keep relative ones only. */
+#define V4A_ROPE_OUTPUT 2u
+/* v4a_compress_args.rope_flags: raw V rows are rotated too (shared K = V). */
+#define V4A_ROPE_V 1u
 
 typedef struct v4a_attn_args {
   uint32_t abi_version;
@@ -239,6 +262,8 @@ typedef struct v4a_attn_args {
   v4a_tensor lse;
   const float* q_norm;
   float norm_eps;
+  int32_t rope_dims;
+  float rope_base;
   int32_t reserved1;
 } v4a_attn_args;
 

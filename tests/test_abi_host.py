@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 13
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 2
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 3
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -234,5 +234,19 @@ def test_decode_step_workspace_holds_row_words():
 
 
 def test_attention_rejects_unknown_flags():
-    r, msg = _st(V.lib().v4attn_decode, good_attn(flags=2), None, 0, None)
+    r, msg = _st(V.lib().v4attn_decode, good_attn(flags=4), None, 0, None)
     assert r == EINVAL and "flags" in msg
+
+
+@pytest.mark.parametrize("field,value", [("rope_dims", 3), ("rope_dims", 130), ("rope_dims", -2), ("rope_base", 0.0)])
+def test_rope_argument_checks(field, value):
+    kw = {field: value}
+    if field == "rope_base":
+        kw["rope_dims"] = 64
+    r, msg = _st(V.lib().v4attn_decode, good_attn(**kw), None, 0, None)
+    assert r == EINVAL and "rope" in msg
+    assert _st(V.lib().v4attn_decode, good_attn(flags=2), None, 0, None)[0] == EINVAL   # output rotation needs R
+    rc, msg = _st(V.lib().v4attn_compress, good_compress(**kw), None)
+    assert rc == EINVAL and "rope" in msg
+    assert _st(V.lib().v4attn_compress, good_compress(rope_dims=64, rope_base=1e4, rope_flags=4), None)[0] == EINVAL
+    assert _st(V.lib().v4attn_compress, good_compress(rope_dims=128, rope_base=1e4, ratio=128), None)[0] == ENOTSUP

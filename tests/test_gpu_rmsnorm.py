@@ -10,7 +10,7 @@ import oracle as O
 import synth
 from synth import configs as C
 from compressed_attention_02_amd.layer import to_device
-from tests.gpu_harness import Run, assert_close, dev_to_np, sample_rows
+from tests.gpu_harness import Run, assert_close_store, dev_to_np, sample_rows
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-5
@@ -43,8 +43,8 @@ def test_compress_entry_rmsnorm(base, ratio_name):
         rs = int(g["raw_start"][b])
         ids, ck = O.compress(kr[b], g[lg][b], rs, t0, n, r)
         _, cv = O.compress(vr[b], g[lg][b], rs, t0, n, r)
-        assert_close(gok[b, ids], O.rms_norm(ck, gk, EPS), cfg.dtype, f"compress k b={b}")
-        assert_close(gov[b, ids], O.rms_norm(cv, gv, EPS), cfg.dtype, f"compress v b={b}")
+        assert_close_store(gok[b, ids], O.rms_norm(ck, gk, EPS), cfg.dtype, f"compress k b={b}")
+        assert_close_store(gov[b, ids], O.rms_norm(cv, gv, EPS), cfg.dtype, f"compress v b={b}")
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
