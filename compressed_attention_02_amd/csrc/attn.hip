@@ -29,10 +29,20 @@ namespace v4a {
 
 // One workgroup of NW waves per (split, row); two workgroups per CU when each wave
 // computes one head tile over half the keys (KP = 2) or NW <= 4.
-template <int NW, int HT, int D, int KP>
+template <int NW, int HT, int D, int KP, bool QP>
 __global__ __launch_bounds__(NW * 64, KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1) void attn_bf16_kernel(AttnP p) {
   __shared__ __align__(16) AttnSmem<D> sm;
-  attn_block<NW, HT, D, KP>(p, blockIdx.x, blockIdx.y, sm);
+  attn_block<NW, HT, D, KP, false, QP>(p, blockIdx.x, blockIdx.y, sm);
+}
+
+template <int D, int KP, bool QP>
+static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
+  V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, D, KP, QP>), grid, dim3(512), 0, s, p);
+}
+template <int D, int KP>
+static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
+  if (p.q_norm || p.rope) launch_bf16<D, KP, true>(p, grid, s, tid);
+  else launch_bf16<D, KP, false>(p, grid, s, tid);
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -169,11 +179,11 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
   // chunk's keys in half (four waves per SIMD); above, one wave per head tile
   if (ntile <= 4) {
-    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64, 2>), grid, dim3(512), 0, s, p);
-    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128, 2>), grid, dim3(512), 0, s, p);
+    if (p.dim == 64) launch_bf16<64, 2>(p, grid, s, tid);
+    else launch_bf16<128, 2>(p, grid, s, tid);
   } else {
-    if (p.dim == 64) V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 64, 1>), grid, dim3(512), 0, s, p);
-    else V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, 128, 1>), grid, dim3(512), 0, s, p);
+    if (p.dim == 64) launch_bf16<64, 1>(p, grid, s, tid);
+    else launch_bf16<128, 1>(p, grid, s, tid);
   }
   return hipGetLastError();
 }

@@ -593,7 +593,9 @@ struct AttnSmem {
 // and not written.  All waves load.
 // Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
 // chunk c is computed.
-template <int NW, int HT, int D, int KP, bool STEP = false>
+// QP: the query is RMS-normalised and/or rotated in the block and the output may be
+// rotated back; without it the kernel carries none of that code.
+template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   // xs = split * head_groups + group: the workgroup takes group's head tiles
@@ -667,7 +669,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     __syncthreads();
   }
 
-  if (p.q_norm || p.rope) {
+  if (QP && (p.q_norm || p.rope)) {
     // RMSNorm of each head's query, then its rotation at pos, in fp32 and rounded
     // once: lane (col, grp) holds elements s*32 + grp*8 + e of head col, and the
     // four grp lanes of a column hold the whole head
@@ -761,7 +763,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         float ov[4] = {O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f};
-        if (p.rope_out) {  // back at -pos: channels dt*16 + 4*grp + e, pairs inside the lane
+        if (QP && p.rope_out) {  // back at -pos: channels dt*16 + 4*grp + e, pairs inside the lane
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
             const int e0 = dt * 16 + 4 * grp + 2 * k2;

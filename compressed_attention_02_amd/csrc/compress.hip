@@ -41,12 +41,12 @@ template <> struct Chunk<uint16_t> {
 // Partial RoPE table of the in-block offsets: (cos, sin) of u * theta_i for u < r
 constexpr int kRopeTab = 4096;
 
-template <typename T>
+template <typename T, bool ROPE>
 __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   constexpr int N = Chunk<T>::N;
   __shared__ float s_max[256];
   __shared__ float s_acc[256][2 * N + 1];
-  __shared__ float2 s_cs[kRopeTab];
+  __shared__ float2 s_cs[ROPE ? kRopeTab : 1];
 
   const int tid = threadIdx.x;
   const int per_block = p.ch * p.g;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   if (active)
     for (int u = g; u < p.r; u += p.g) mx = fmaxf(mx, lg[u]);
   s_max[tid] = mx;
-  const int R = p.rope, hr = p.rope / 2, lo = p.d - p.rope;
+  const int R = ROPE ? p.rope : 0, hr = R / 2, lo = p.d - R;
   if (R)
     for (int t = tid; t < p.r * hr; t += 256) {
       float cs, sn;
@@ -186,10 +186,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
 
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid) {
   const dim3 grid((unsigned)((p.nb + p.bpw - 1) / p.bpw), (unsigned)batch);
-  if (dtype == 0)
-    V4A_LAUNCH(tid, compress_kernel<float>, grid, dim3(256), 0, s, p);
-  else
-    V4A_LAUNCH(tid, compress_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  if (dtype == 0) {
+    if (p.rope) V4A_LAUNCH(tid, (compress_kernel<float, true>), grid, dim3(256), 0, s, p);
+    else V4A_LAUNCH(tid, (compress_kernel<float, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.rope) V4A_LAUNCH(tid, (compress_kernel<uint16_t, true>), grid, dim3(256), 0, s, p);
+    else V4A_LAUNCH(tid, (compress_kernel<uint16_t, false>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ union StepSmem {
   SelShared sel;
 };
 
-template <int D, int KP>
+template <int D, int KP, bool QP>
 __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, AttnP ap, AttnP csa, int n_sel,
                                                                   int n_rest) {
   static_assert(kSelThreads == 8 * 64, "the attention workgroups run 8 waves");
@@ -41,11 +41,19 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   }
   const int a = blk - n_sel;
   if (a < n_rest) {
-    attn_block<8, 1, D, KP, true>(ap, a % ap.splits, a / ap.splits, sm.attn);
+    attn_block<8, 1, D, KP, true, QP>(ap, a % ap.splits, a / ap.splits, sm.attn);
   } else {
     const int c = a - n_rest;
-    attn_block<8, 1, D, KP, true>(csa, c % csa.splits, c / csa.splits, sm.attn);
+    attn_block<8, 1, D, KP, true, QP>(csa, c % csa.splits, c / csa.splits, sm.attn);
   }
+}
+
+template <int D, int KP>
+static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int nr, dim3 g,
+                      hipStream_t s, int tid) {
+  const dim3 blk(kSelThreads);
+  if (ap.q_norm || ap.rope) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+  else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
 }
 
 int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows) {
@@ -72,14 +80,14 @@ hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, con
     return hipErrorInvalidValue;
   if (!csa.sync && ap.final_merge) return hipErrorInvalidValue;
   // up to 64 heads, two waves per head tile take half of every chunk's keys each
-  const dim3 g((unsigned)n), blk(kSelThreads);
+  const dim3 g((unsigned)n);
   const int nr = (int)n_rest;
   if (ap.heads <= 64) {
-    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 2>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
-    else V4A_LAUNCH(tid, (select_attn_kernel<128, 2>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    if (ap.dim == 64) launch_sa<64, 2>(sp, n_sel, ap, csa, nr, g, s, tid);
+    else launch_sa<128, 2>(sp, n_sel, ap, csa, nr, g, s, tid);
   } else {
-    if (ap.dim == 64) V4A_LAUNCH(tid, (select_attn_kernel<64, 1>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
-    else V4A_LAUNCH(tid, (select_attn_kernel<128, 1>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    if (ap.dim == 64) launch_sa<64, 1>(sp, n_sel, ap, csa, nr, g, s, tid);
+    else launch_sa<128, 1>(sp, n_sel, ap, csa, nr, g, s, tid);
   }
   return hipGetLastError();
 }
