@@ -217,8 +217,14 @@ def decode_keyset(p: int, *, branches: int, m: int, m_hca: int, window: int,
     HCA: every visible compressed entry 0..e_vis-1 ([QbitAI] HCA paragraph);
     SWA: raw positions max(0, p-W+1)..p ([QbitAI] sliding-window paragraph;
     [yage] the 128-token window).  Returns {"csa": (K, V), "hca": ..., "swa": ...}
-    with only the enabled branches.
+    with only the enabled branches.  A branch given without values (vc, vh or v_raw
+    None) has shared entries: each one is its own value ([QbitAI] 混合注意力机制, the
+    partial RoPE paragraph: the KV entries serve as keys and as values; [wiki]
+    shared-KV MQA).
     """
+    vc = kc if vc is None else vc
+    vh = kh if vh is None else vh
+    v_raw = k_raw if v_raw is None else v_raw
     out = {}
     if branches & 1:
         sel = np.asarray(idx, dtype=np.int64)

@@ -567,3 +567,68 @@ def test_rope_output_rotation_makes_the_layer_shift_invariant():
         assert np.allclose(outs[0, True][0], outs[shift, True][0], rtol=0, atol=1e-9)
         assert np.allclose(outs[0, True][1], outs[shift, True][1], rtol=0, atol=1e-9)
         assert not np.allclose(outs[0, False][0], outs[shift, False][0], atol=1e-4)
+
+
+def test_shared_kv_layer_in_relative_form():
+    # The pages' shared-KV layer at its own sizes (c = 512, RoPE on the last 64
+    # channels, m = 4, m' = 128, a 128-token window): every entry is its own value,
+    # so with the query rotated at p and the output at -p each key contributes
+    # only through its position relative to p.  The same output is rebuilt here
+    # from the unrotated token contents: entries pooled and normalised without any
+    # rotation, each one placed at its block's last position s and turned by s - p,
+    # both in the logit and as a value.
+    rng = np.random.default_rng(44)
+    d, R, H, p, W = 512, 64, 3, 300, 128
+    u = rng.standard_normal((p + 1, d))               # unrotated token contents
+    x = O.rope(u, np.arange(p + 1), R, 1e4)           # raw rows, rotated at their positions
+    zc, zh = rng.standard_normal(p + 1), rng.standard_normal(p + 1)
+    gk = rng.uniform(0.5, 1.5, d)
+    gq = rng.uniform(0.5, 1.5, d)
+    eps = 1e-6
+    ids_c, ec = O.compress_entries(x, zc, 0, 0, p + 1, 4, gain=gk, eps=eps, rope_dims=R, rope_base=1e4)
+    ids_h, eh = O.compress_entries(x, zh, 0, 0, p + 1, 128, gain=gk, eps=eps, rope_dims=R, rope_base=1e4)
+    assert len(ids_c) == 75 and len(ids_h) == 2
+    sel = np.sort(rng.choice(75, 16, replace=False))
+    q = rng.standard_normal((H, d))
+    o, lse = O.decode_query(q, p, q_norm=gq, norm_eps=eps, rope_dims=R, rope_base=1e4, rope_out=True,
+                            branches=7, m=4, m_hca=128, window=W, idx=sel, kc=ec, kh=eh, k_raw=x, raw_start=0)
+    # rebuilt: unrotated entries with their positions
+    _, pc = O.compress(u, zc, 0, 0, p + 1, 4)
+    _, ph = O.compress(u, zh, 0, 0, p + 1, 128)
+    content = [O.rms_norm(pc[j], gk, eps) for j in sel] + [O.rms_norm(ph[j], gk, eps) for j in range(2)]
+    where = [4 * (j + 1) - 1 for j in sel] + [128 * (j + 1) - 1 for j in range(2)]
+    content += [u[t] for t in range(p - W + 1, p + 1)]
+    where += list(range(p - W + 1, p + 1))
+    rel = np.stack([O.rope(c, s - p, R, 1e4) for c, s in zip(content, where)])
+    qn = O.rms_norm(q, gq, eps)
+    logits = (qn @ rel.T) / math.sqrt(d)
+    mx = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - mx)
+    ref_o = (w @ rel) / w.sum(axis=1, keepdims=True)
+    ref_lse = mx[:, 0] + np.log(w.sum(axis=1))
+    assert np.allclose(o, ref_o, rtol=0, atol=1e-9)
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-9)
+    # leaving out the output rotation, or placing entries at their block's first
+    # position, breaks it
+    o2, _ = O.decode_query(q, p, q_norm=gq, norm_eps=eps, rope_dims=R, rope_base=1e4, rope_out=False,
+                           branches=7, m=4, m_hca=128, window=W, idx=sel, kc=ec, kh=eh, k_raw=x, raw_start=0)
+    assert not np.allclose(o2, ref_o, atol=1e-3)
+    shifted = [O.rope(c, s - 3 - p, R, 1e4) if k < 18 else O.rope(c, s - p, R, 1e4)
+               for k, (c, s) in enumerate(zip(content, where))]
+    assert not np.allclose((w @ np.stack(shifted)) / w.sum(axis=1, keepdims=True), o, atol=1e-3)
+
+
+def test_shared_entries_when_values_are_omitted():
+    # a branch given without values attends with each entry as its own value
+    rng = np.random.default_rng(45)
+    d = 8
+    kc, kh, raw = rng.standard_normal((6, d)), rng.standard_normal((2, d)), rng.standard_normal((40, d))
+    q = rng.standard_normal((2, d))
+    a = O.decode_query(q, 39, branches=7, m=4, m_hca=16, window=5, idx=np.array([1, 4, -1]),
+                       kc=kc, kh=kh, k_raw=raw, raw_start=0)
+    b = O.decode_query(q, 39, branches=7, m=4, m_hca=16, window=5, idx=np.array([1, 4, -1]),
+                       kc=kc, vc=kc, kh=kh, vh=kh, k_raw=raw, v_raw=raw, raw_start=0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    keys = np.concatenate([kc[[1, 4]], kh[:2], raw[35:40]])
+    ref = O.attend(q, keys, keys, 1 / math.sqrt(d))
+    assert np.allclose(a[0], ref[0], rtol=0, atol=1e-12)
