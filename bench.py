@@ -101,16 +101,17 @@ def step_bytes(cfg) -> dict:
     n_vis = (p + 1) // cfg.m
     e_vis = (p + 1) // cfg.m_hca
     w = min(cfg.window, p + 1)
+    kv = 1 if cfg.shared_kv else 2     # shared entries are read once as key and value
     out = {}
     if cfg.branches & 1:
         out["ki"] = B * n_vis * cfg.idx_dim * es
         out["qi_wi"] = B * cfg.idx_heads * (cfg.idx_dim * es + 4)
         out["idx"] = B * cfg.topk * 4 * 2
-        out["csa_kv"] = B * min(cfg.topk, n_vis) * 2 * d * es
+        out["csa_kv"] = B * min(cfg.topk, n_vis) * kv * d * es
     if cfg.branches & 2:
-        out["hca_kv"] = B * e_vis * 2 * d * es
+        out["hca_kv"] = B * e_vis * kv * d * es
     if cfg.branches & 4:
-        out["swa_kv"] = B * w * 2 * d * es
+        out["swa_kv"] = B * w * kv * d * es
     if cfg.compress == "hca_newest":
         out["compress_rd"] = B * cfg.compress_tokens * (2 * d * es + 4)
         out["compress_wr"] = B * (cfg.compress_tokens // cfg.m_hca) * 2 * d * es
@@ -124,6 +125,11 @@ def run_oracle_step(cfg, g, arrays):
     import numpy as np
     import oracle as O
     qi, wi, ki, q, caches = arrays
+    extra = {}
+    if cfg.q_norm:
+        extra["q_norm"] = g["gq"].astype(np.float64)
+    if cfg.rope_dims:
+        extra.update(rope_dims=cfg.rope_dims, rope_base=1e4, rope_out=True)
     outs = []
     for b in range(cfg.batch):
         p = int(g["pos"][b])
@@ -133,7 +139,7 @@ def run_oracle_step(cfg, g, arrays):
             s = O.index_scores(qi[b, 0], wi[b, 0], ki[b, :n])
             idx = O.topk_select(s, cfg.topk)
         kw = {k: (v[b] if isinstance(v, np.ndarray) else v) for k, v in caches.items()}
-        outs.append(O.decode_query(q[b, 0], p, idx=idx, raw_start=int(g["raw_start"][b]), **kw))
+        outs.append(O.decode_query(q[b, 0], p, idx=idx, raw_start=int(g["raw_start"][b]), **extra, **kw))
     return outs
 
 
@@ -356,7 +362,10 @@ def main():
                    "head_dim": cfg.dim, "csa_ratio": cfg.m, "topk": cfg.topk, "hca_ratio": cfg.m_hca,
                    "window": cfg.window, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim}",
                    "step": cfg.timed, "rotating_input_sets": R,
-                   "step_form": "one_launch" if args.one_launch else "two_launch"},
+                   "step_form": "one_launch" if args.one_launch else "two_launch",
+                   **({"shared_kv": True} if cfg.shared_kv else {}),
+                   **({"rope_dims": cfg.rope_dims} if cfg.rope_dims else {}),
+                   **({"q_norm": True} if cfg.q_norm else {})},
         "hbm_gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,

@@ -32,8 +32,9 @@ F32, BF16 = 0, 1
 CSA, HCA, SWA = 1, 2, 4
 BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ROPE_OUTPUT = 2       # v4a_attn_args.flags
+SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
-ABI_VERSION = 3
+ABI_VERSION = 4
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6}
 
@@ -184,7 +185,8 @@ def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, 
              rope_v: bool = False):
     """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out
     (RMS-normalised with the fp32 gains norm_k / norm_v when given; with rope_dims,
-    raw rows are rotated at their positions and entries at their block's last one)."""
+    raw rows are rotated at their positions and entries at their block's last one).
+    v_raw and v_out None: shared K = V entries, K alone is pooled."""
     a = CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
                      _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
                      _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, rope_dims, rope_base,
@@ -217,12 +219,15 @@ def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, se
 def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=None, k_raw=None,
               v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
               window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False,
-              q_norm=None, norm_eps=1e-6, rope_dims=0, rope_base=1e4, rope_out=False) -> AttnArgs:
+              q_norm=None, norm_eps=1e-6, rope_dims=0, rope_base=1e4, rope_out=False,
+              shared_kv=False) -> AttnArgs:
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
     return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
-                    window, topk, scale, (BATCH_INVARIANT if batch_invariant else 0) | (ROPE_OUTPUT if rope_out else 0),
+                    window, topk, scale,
+                    (BATCH_INVARIANT if batch_invariant else 0) | (ROPE_OUTPUT if rope_out else 0) |
+                    (SHARED_KV if shared_kv else 0),
                     _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
                     _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
                     _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse), _ptr(q_norm), norm_eps, rope_dims,

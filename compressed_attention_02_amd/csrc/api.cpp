@@ -190,12 +190,18 @@ v4a_status validate_compress(const v4a_compress_args* a) {
     return fail(V4A_EINVAL, "norm_eps must be finite and >= 0");
   if ((a->norm_k && !aligned(a->norm_k, 4)) || (a->norm_v && !aligned(a->norm_v, 4)))
     return fail(V4A_EINVAL, "norm gains must be 4-byte aligned");
+  const bool hv = a->v_raw.ptr || a->v_out.ptr;   // else shared K = V entries: K alone
+  if (hv && !(a->v_raw.ptr && a->v_out.ptr)) return fail(V4A_EINVAL, "v_raw and v_out must both be set or both be NULL");
+  if (!hv && (a->norm_v || (a->rope_flags & V4A_ROPE_V)))
+    return fail(V4A_EINVAL, "K-only compression: norm_v must be NULL and rope_flags 0");
   if (a->batch == 0 || a->n / a->ratio == 0) return V4A_OK;
   if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
   V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, a->batch));
-  V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, a->batch));
   V4A_TRY(check_tensor("k_out", a->k_out, a->dtype, a->dim, a->batch));
-  V4A_TRY(check_tensor("v_out", a->v_out, a->dtype, a->dim, a->batch));
+  if (hv) {
+    V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, a->batch));
+    V4A_TRY(check_tensor("v_out", a->v_out, a->dtype, a->dim, a->batch));
+  }
   if (!a->logits.ptr) return fail(V4A_EINVAL, "logits: NULL pointer");
   if (!aligned(a->logits.ptr, 4)) return fail(V4A_EINVAL, "logits: pointer not 4-byte aligned");
   if (a->logits.row_stride != 1) return fail(V4A_EINVAL, "logits: row_stride must be 1");
@@ -249,11 +255,17 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (prefill ? a->tq < 1 : a->tq != 1) return fail(V4A_EINVAL, prefill ? "tq must be >= 1" : "decode needs tq == 1");
   if (a->heads < 1 || a->heads > 128) return fail(V4A_ENOTSUP, "heads must be in 1..128");
   if (a->dtype == V4A_BF16 && a->heads % 16 != 0) return fail(V4A_ENOTSUP, "bf16 attention: heads must be a multiple of 16");
-  if (a->dim != 64 && a->dim != 128) return fail(V4A_ENOTSUP, "dim must be 64 or 128");
+  const bool skv = (a->flags & V4A_SHARED_KV) != 0;
+  if (a->dim != 64 && a->dim != 128 && a->dim != 512) return fail(V4A_ENOTSUP, "dim must be 64, 128 or 512");
+  if (a->dim == 512 && a->dtype == V4A_BF16 && !skv)
+    return fail(V4A_ENOTSUP, "bf16 attention at dim 512 needs V4A_SHARED_KV");
   if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
   if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
   if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
-  if (a->flags & ~(V4A_BATCH_INVARIANT | V4A_ROPE_OUTPUT)) return fail(V4A_EINVAL, "unknown flags 0x%x", a->flags);
+  if (a->flags & ~(V4A_BATCH_INVARIANT | V4A_ROPE_OUTPUT | V4A_SHARED_KV))
+    return fail(V4A_EINVAL, "unknown flags 0x%x", a->flags);
+  if (skv && (a->vc.ptr || a->vh.ptr || a->v_raw.ptr))
+    return fail(V4A_EINVAL, "V4A_SHARED_KV: vc, vh and v_raw must be NULL (the key rows are the values)");
   if (a->rope_dims < 0 || a->rope_dims % 2 != 0 || a->rope_dims > a->dim)
     return fail(V4A_EINVAL, "rope_dims must be even and in [0, dim]");
   if (a->rope_dims > 0 && !(a->rope_base > 0.f && std::isfinite(a->rope_base)))
@@ -282,15 +294,15 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
     if (!a->idx.ptr || !aligned(a->idx.ptr, 4)) return fail(V4A_EINVAL, "idx: NULL or not 4-byte aligned");
     if (a->idx.row_stride < a->topk) return fail(V4A_EINVAL, "idx: row_stride < topk");
     V4A_TRY(check_tensor("kc", a->kc, a->dtype, a->dim, bq));
-    V4A_TRY(check_tensor("vc", a->vc, a->dtype, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("vc", a->vc, a->dtype, a->dim, bq));
   }
   if (a->branch_mask & V4A_HCA) {
     V4A_TRY(check_tensor("kh", a->kh, a->dtype, a->dim, bq));
-    V4A_TRY(check_tensor("vh", a->vh, a->dtype, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("vh", a->vh, a->dtype, a->dim, bq));
   }
   if ((a->branch_mask & V4A_SWA) && a->window > 0) {
     V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, bq));
-    V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, bq));
     if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
   }
   if (a->sink && !aligned(a->sink, 4)) return fail(V4A_EINVAL, "sink: not 4-byte aligned");
@@ -309,9 +321,19 @@ v4a_status check_ws(void* ws, size_t have, size_t need) {
   return V4A_OK;
 }
 
+// Fewest head groups the attention kernel needs: bf16 rows of 512 take one 16-head
+// tile per wave of a 4-wave workgroup, so at most 64 heads per group; otherwise one.
+int min_head_groups(const v4a_attn_args* a) {
+  if (a->dtype != V4A_BF16 || a->dim != 512) return 1;
+  const int ntile = std::max(1, a->heads / 16);
+  int hg = (ntile + 3) / 4;
+  while (ntile % hg != 0) ++hg;
+  return hg;
+}
+
 AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   AttnP p{};
-  p.head_groups = 1;
+  p.head_groups = min_head_groups(a);
   p.q = a->q.ptr; p.q_bs = a->q.batch_stride; p.q_rs = a->q.row_stride;
   p.idx = (const int32_t*)a->idx.ptr; p.idx_bs = a->idx.batch_stride; p.idx_rs = a->idx.row_stride;
   p.kc = a->kc.ptr; p.kc_bs = a->kc.batch_stride; p.kc_rs = a->kc.row_stride;
@@ -320,6 +342,12 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   p.vh = a->vh.ptr; p.vh_bs = a->vh.batch_stride; p.vh_rs = a->vh.row_stride;
   p.kr = a->k_raw.ptr; p.kr_bs = a->k_raw.batch_stride; p.kr_rs = a->k_raw.row_stride;
   p.vr = a->v_raw.ptr; p.vr_bs = a->v_raw.batch_stride; p.vr_rs = a->v_raw.row_stride;
+  p.skv = (a->flags & V4A_SHARED_KV) != 0;
+  if (p.skv) {  // every entry is its own value
+    p.vc = p.kc; p.vc_bs = p.kc_bs; p.vc_rs = p.kc_rs;
+    p.vh = p.kh; p.vh_bs = p.kh_bs; p.vh_rs = p.kh_rs;
+    p.vr = p.kr; p.vr_bs = p.kr_bs; p.vr_rs = p.kr_rs;
+  }
   p.raw_start = a->raw_start; p.pos0 = a->pos0; p.sink = a->sink;
   p.o = (float*)a->o.ptr; p.o_bs = a->o.batch_stride; p.o_rs = a->o.row_stride;
   p.lse = (float*)a->lse.ptr; p.lse_bs = a->lse.batch_stride; p.lse_rs = a->lse.row_stride;
@@ -512,8 +540,9 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   // tile) while the launch stays within one workgroup per CU
   if (a->dtype == V4A_BF16 && P.s_csa > 0) {
     const int ntile = std::max(1, a->heads / 16);
-    int hg = ntile;
-    while (!inv && hg > 1 && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
+    const int hmin = min_head_groups(a);
+    int hg = inv ? ntile : std::max(ntile, hmin);
+    while (!inv && hg > hmin && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
     csa.head_groups = hg;
   }
 
@@ -525,7 +554,9 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     IndexLaunch IL = index_launch(ix, ws);
     // selection and the selection-independent attention share one launch when the
     // rows fit one score pass and the attention is bf16
-    const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
+    // (rows of 512 attend in 4-wave workgroups, which the selection's launch cannot
+    // host)
+    const bool combined = a->dtype == V4A_BF16 && a->dim != 512 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
       // in the one-launch form (the whole grid resident at once, at most one
       // workgroup per CU) the picks' attention and the merge join the launch; the

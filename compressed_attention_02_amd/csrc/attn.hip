@@ -28,21 +28,24 @@
 namespace v4a {
 
 // One workgroup of NW waves per (split, row); two workgroups per CU when each wave
-// computes one head tile over half the keys (KP = 2) or NW <= 4.
-template <int NW, int HT, int D, int KP, bool QP>
-__global__ __launch_bounds__(NW * 64, KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1) void attn_bf16_kernel(AttnP p) {
-  __shared__ __align__(16) AttnSmem<D> sm;
-  attn_block<NW, HT, D, KP, false, QP>(p, blockIdx.x, blockIdx.y, sm);
+// computes one head tile over half the keys (KP = 2) or NW <= 4.  Shared entries of
+// D = 512 take most of the LDS (two 64 KB chunk buffers): one workgroup of 4 waves
+// per CU, one head tile per wave with the SIMD's whole register file (its O^T alone
+// is 128 registers, its queries 64); more than 64 heads come in head groups.
+template <int NW, int HT, int D, int KP>
+constexpr int attn_waves_per_eu() {
+  return D == 512 ? 1 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
+}
+template <int NW, int HT, int D, int KP, bool QP, bool SKV>
+__global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
+  __shared__ __align__(16) AttnSmem<D, SKV> sm;
+  attn_block<NW, HT, D, KP, false, QP, SKV>(p, blockIdx.x, blockIdx.y, sm);
 }
 
-template <int D, int KP, bool QP>
+template <int NW, int HT, int D, int KP, bool SKV>
 static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
-  V4A_LAUNCH(tid, (attn_bf16_kernel<8, 1, D, KP, QP>), grid, dim3(512), 0, s, p);
-}
-template <int D, int KP>
-static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
-  if (p.q_norm || p.rope) launch_bf16<D, KP, true>(p, grid, s, tid);
-  else launch_bf16<D, KP, false>(p, grid, s, tid);
+  if (p.q_norm || p.rope) V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, true, SKV>), grid, dim3(NW * 64), 0, s, p);
+  else V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, false, SKV>), grid, dim3(NW * 64), 0, s, p);
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -171,19 +174,27 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   const dim3 grid((unsigned)(p.splits * p.head_groups), (unsigned)nrows);
   if (dtype == 0) {
     if (p.dim == 64) V4A_LAUNCH(tid, attn_f32_kernel<64>, grid, dim3(256), 0, s, p);
-    else V4A_LAUNCH(tid, attn_f32_kernel<128>, grid, dim3(256), 0, s, p);
+    else if (p.dim == 128) V4A_LAUNCH(tid, attn_f32_kernel<128>, grid, dim3(256), 0, s, p);
+    else V4A_LAUNCH(tid, attn_f32_kernel<512>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
   const int ntile = p.heads / 16 / p.head_groups;   // tiles per workgroup
   if (p.heads % (16 * p.head_groups) != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
+  if (p.dim == 512) {
+    // shared entries only: 4 waves, one head tile each
+    if (!p.skv || ntile > 4) return hipErrorInvalidValue;
+    launch_bf16<4, 1, 512, 1, true>(p, grid, s, tid);
+    return hipGetLastError();
+  }
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
   // chunk's keys in half (four waves per SIMD); above, one wave per head tile
+  // (shared entries at d <= 128 arrive with the value pointers aimed at the keys)
   if (ntile <= 4) {
-    if (p.dim == 64) launch_bf16<64, 2>(p, grid, s, tid);
-    else launch_bf16<128, 2>(p, grid, s, tid);
+    if (p.dim == 64) launch_bf16<8, 1, 64, 2, false>(p, grid, s, tid);
+    else launch_bf16<8, 1, 128, 2, false>(p, grid, s, tid);
   } else {
-    if (p.dim == 64) launch_bf16<64, 1>(p, grid, s, tid);
-    else launch_bf16<128, 1>(p, grid, s, tid);
+    if (p.dim == 64) launch_bf16<8, 1, 64, 1, false>(p, grid, s, tid);
+    else launch_bf16<8, 1, 128, 1, false>(p, grid, s, tid);
   }
   return hipGetLastError();
 }

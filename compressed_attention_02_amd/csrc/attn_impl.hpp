@@ -341,7 +341,8 @@ struct RowKeys {
   int64_t n_csa, hca_end, raw_off, k_begin, k_end;
 };
 
-constexpr float kLazyRescale = 8.f; // running max moves only when exceeded by 2^8
+constexpr float kLazyRescale = 8.f;
+constexpr int kWideGroup = 4;        // LDS fragments per scheduling group at D = 512 // running max moves only when exceeded by 2^8
 
 // Source rows of key t in the general case (a chunk that straddles branches or
 // the end of the split): selects only.
@@ -368,9 +369,20 @@ __device__ __forceinline__ void key_src_any(const RowKeys& R, const int* s_idx, 
 // pieces of row r permuted by XOR with swz_k(r) / swz_v(r).  The permutations make
 // the three access patterns free of bank conflicts: the direct global->LDS loads
 // (a wave writes 1 KB contiguously), the K fragment reads (16 rows, one piece
-// column) and the transposing V reads (4 rows x 2 pieces per 16 lanes).
-template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+// column) and the transposing V reads (4 rows x 2 pieces per 16 lanes).  At
+// D = 512 the entries are shared (one buffer is read both ways), so one XOR serves
+// both: 2(r mod 8) + bit 3 of r is distinct over 16 rows (K reads) and keeps piece
+// pairs together with distinct pair slots over each 8 rows (V reads).
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+  return D == 512 ? (2 * (r & 7) | ((r >> 3) & 1)) : D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+  return D == 512 ? swz_k<512>(r) : D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+}
+
+// s_waitcnt immediate for vmcnt(n) (gfx9: low 4 bits at [3:0], high 2 at [15:14]),
+// every other counter left alone
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // row r of a table at base with row stride rs (elements): 32 x 32 -> 64-bit product
 __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_t r, int64_t rs) {
@@ -381,7 +393,7 @@ __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_
 // writes its mask (sBias[key] = 0 or -inf).  Each wave moves rows of 64 lanes x
 // 16 bytes per instruction; lane l's piece lands at LDS base + 16 l, so the lane
 // loads the global piece that the XOR layout puts there.  wave is uniform.
-template <int NW, int D>
+template <int NW, int D, bool SKV>
 __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, int64_t kc0, uint16_t* sK,
                                             uint16_t* sV, float* sBias, int wave, int lane) {
   constexpr int PIECES = D / 8;               // 16-byte pieces per row
@@ -416,7 +428,7 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
       key_src_any(R, s_idx, kc0 + r, kp, vp, ok);
     }
     lds_load16(kp + (ppiece ^ swz_k<D>(r)) * 8, lds_addr(sK + r0 * D));
-    lds_load16(vp + (ppiece ^ swz_v<D>(r)) * 8, lds_addr(sV + r0 * D));
+    if constexpr (!SKV) lds_load16(vp + (ppiece ^ swz_v<D>(r)) * 8, lds_addr(sV + r0 * D));
     if (ppiece == 0) sBias[r] = ok ? 0.f : -INFINITY;
   }
 }
@@ -455,6 +467,10 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
       const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(kb + 16 * kt * D + ((4 * s + grp) ^ kx) * 8);
 #pragma unroll
       for (int t = 0; t < HT; ++t) S[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qb[t][s], S[t][kt], 0, 0, 0);
+      // wide rows: fence every kWideGroup fragments, so that the scheduler does not
+      // hoist a whole chunk's fragment reads into registers
+      if constexpr (D > 128)
+        if (s % kWideGroup == kWideGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
   // logits in base 2 (masked keys -inf), in place
@@ -519,6 +535,8 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      if constexpr (D > 128)
+        if (dt % kWideGroup == 0) __builtin_amdgcn_sched_barrier(0);
       const uint16_t* v0 = vb + 32 * kk * D + ((2 * dt + ((col & 3) >> 1)) ^ vx) * 8;
       const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0));
       const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0 + 16 * D));
@@ -536,7 +554,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
 // are in flight while chunk c is computed.  The waits count the direct loads (2 *
 // IPW per lane per chunk) that may stay outstanding; everything issued before the
 // first chunk (q, ids) is older and therefore settled by the first wait.
-template <int NW, int D, int HT, int KP>
+template <int NW, int D, int HT, int KP, bool SKV>
 __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, uint16_t* K0, uint16_t* V0, float* B0,
                                            uint16_t* K1, uint16_t* V1, float* B1, int64_t nch, bool active,
                                            const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
@@ -544,16 +562,17 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
                                            int kh) {
   constexpr int CH = kAttnChunk;
   constexpr int IPW = CH / (64 / (D / 8)) / NW;  // direct loads per wave per chunk, for K and for V
+  constexpr int LPW = SKV ? IPW : 2 * IPW;        // all of a chunk's loads per wave
   const int col = lane & 15, grp = lane >> 4;
-  if (nch > 0) issue_chunk<NW, D>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
-  if (nch > 1) issue_chunk<NW, D>(R, s_idx, R.k_begin + CH, K1, V1, B1, wave, lane);
+  if (nch > 0) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
+  if (nch > 1) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + CH, K1, V1, B1, wave, lane);
   // chunk c is computed while chunk c + 1 (if any) loads; the wait before chunk c
   // leaves only chunk c + 1's loads outstanding, so the last chunk waits for all.
   // One body for both buffers (the buffer is a uniform base): the per-lane LDS
   // offsets are kept once, not once per buffer.
   for (int64_t c = 0; c < nch; ++c) {
-    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPW));  // vmcnt(2 * IPW)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     const bool odd = (c & 1) != 0;
     uint16_t* Kc = odd ? K1 : K0;
@@ -561,19 +580,17 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
     float* Bc = odd ? B1 : B0;
     if (active) attend_chunk<D, HT, KP>(Kc, Vc, Bc, Qb, O, m_run, l_run, sl2, col, grp, kh);
     __syncthreads();
-    if (c + 2 < nch) issue_chunk<NW, D>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
+    if (c + 2 < nch) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
   }
 }
 
-// LDS of one attention workgroup: two chunk buffers (K, V, mask) and the split's
-// CSA ids.
-template <int D>
+// LDS of one attention workgroup: two chunk buffers (K, V, mask; shared entries
+// (SKV) keep one row that serves as both) and the split's CSA ids.
+template <int D, bool SKV = false>
 struct AttnSmem {
+  static constexpr int kRows = kAttnChunk * D;
   union {
-    struct {
-      uint16_t K0[kAttnChunk * D], K1[kAttnChunk * D];
-      uint16_t V0[kAttnChunk * D], V1[kAttnChunk * D];
-    };
+    uint16_t buf[(SKV ? 2 : 4) * kRows];
     // after the last chunk: the state (O, m, l) one key half hands to the other,
     // per lane of 4 waves
     float C[4 * 64 * (D / 4 + 2)];
@@ -581,6 +598,10 @@ struct AttnSmem {
   float B0[kAttnChunk], B1[kAttnChunk];
   int idx[kMaxTopk];
   int flag;
+  __device__ uint16_t* K0() { return buf; }
+  __device__ uint16_t* K1() { return buf + kRows; }
+  __device__ uint16_t* V0() { return SKV ? buf : buf + 2 * kRows; }
+  __device__ uint16_t* V1() { return SKV ? buf + kRows : buf + 3 * kRows; }
 };
 
 // The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
@@ -594,9 +615,10 @@ struct AttnSmem {
 // Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
 // chunk c is computed.
 // QP: the query is RMS-normalised and/or rotated in the block and the output may be
-// rotated back; without it the kernel carries none of that code.
-template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false>
-__device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D>& sm) {
+// rotated back; without it the kernel carries none of that code.  SKV: every entry
+// is its own value (shared K = V rows, loaded once).
+template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false>
+__device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   // xs = split * head_groups + group: the workgroup takes group's head tiles
   const int hgn = p.head_groups, split = xs / hgn, hgi = xs - split * hgn;
@@ -722,8 +744,8 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  run_chunks<NW, D, HT, KP>(R, s_idx, sm.K0, sm.V0, sm.B0, sm.K1, sm.V1, sm.B1, nch, tv[0], Qb, O, m_run,
-                            l_run, sl2, wave, lane, kh);
+  run_chunks<NW, D, HT, KP, SKV>(R, s_idx, sm.K0(), sm.V0(), sm.B0, sm.K1(), sm.V1(), sm.B1, nch, tv[0], Qb, O,
+                                 m_run, l_run, sl2, wave, lane, kh);
 
   if constexpr (KP == 2) {
     // the second key half hands (O, m, l) to the first through LDS; the chunk

@@ -41,7 +41,8 @@ template <> struct Chunk<uint16_t> {
 // Partial RoPE table of the in-block offsets: (cos, sin) of u * theta_i for u < r
 constexpr int kRopeTab = 4096;
 
-template <typename T, bool ROPE>
+// HV: the block has V rows too (else the entries are shared K = V: K alone is pooled)
+template <typename T, bool ROPE, bool HV>
 __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   constexpr int N = Chunk<T>::N;
   __shared__ float s_max[256];
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
       const float w = __expf(lg[u] - mx);
       float xk[N], xv[N];
       Chunk<T>::load(kr + (int64_t)u * p.kr_rs, xk);
-      Chunk<T>::load(vr + (int64_t)u * p.vr_rs, xv);
+      if (HV) Chunk<T>::load(vr + (int64_t)u * p.vr_rs, xv);
       if (R) {
         // raw rows are rotated at their positions j*r + u: undo the in-block part u
         // here, the block part j*r once on the pooled entry
@@ -97,12 +98,15 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
           if (e0 < lo) continue;
           const float2 cs = s_cs[u * hr + (e0 - lo) / 2];
           rot2(xk[2 * k2], xk[2 * k2 + 1], cs.x, cs.y, true);
-          if (p.rope_v) rot2(xv[2 * k2], xv[2 * k2 + 1], cs.x, cs.y, true);
+          if (HV && p.rope_v) rot2(xv[2 * k2], xv[2 * k2 + 1], cs.x, cs.y, true);
         }
       }
       ws += w;
 #pragma unroll
-      for (int e = 0; e < N; ++e) { ak[e] = fmaf(w, xk[e], ak[e]); av[e] = fmaf(w, xv[e], av[e]); }
+      for (int e = 0; e < N; ++e) {
+        ak[e] = fmaf(w, xk[e], ak[e]);
+        if (HV) av[e] = fmaf(w, xv[e], av[e]);
+      }
     }
   }
   if (p.g > 1) {
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
         float cs, sn;
         rope_cs((double)(j * p.r), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
         rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, true);
-        if (p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, true);
+        if (HV && p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, true);
       }
     }
 #pragma unroll
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
 #pragma unroll
       for (int e = 0; e < N; ++e) {
         if (p.gk) ak[e] = ak[e] * rk * p.gk[c * N + e];
-        if (p.gv) av[e] = av[e] * rv * p.gv[c * N + e];
+        if (HV && p.gv) av[e] = av[e] * rv * p.gv[c * N + e];
       }
     }
   }
@@ -174,24 +178,31 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
         float cs, sn;
         rope_cs((double)((j + 1) * p.r - 1), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
         rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, false);
-        if (p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, false);
+        if (HV && p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, false);
       }
     }
     T* ko = reinterpret_cast<T*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
     T* vo = reinterpret_cast<T*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
     Chunk<T>::store(ko, ak);
-    Chunk<T>::store(vo, av);
+    if (HV) Chunk<T>::store(vo, av);
   }
+}
+
+template <typename T, bool HV>
+static void launch_variant(const CompressP& p, dim3 grid, hipStream_t s, int tid) {
+  if (p.rope) V4A_LAUNCH(tid, (compress_kernel<T, true, HV>), grid, dim3(256), 0, s, p);
+  else V4A_LAUNCH(tid, (compress_kernel<T, false, HV>), grid, dim3(256), 0, s, p);
 }
 
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid) {
   const dim3 grid((unsigned)((p.nb + p.bpw - 1) / p.bpw), (unsigned)batch);
+  const bool hv = p.v_raw != nullptr;
   if (dtype == 0) {
-    if (p.rope) V4A_LAUNCH(tid, (compress_kernel<float, true>), grid, dim3(256), 0, s, p);
-    else V4A_LAUNCH(tid, (compress_kernel<float, false>), grid, dim3(256), 0, s, p);
+    if (hv) launch_variant<float, true>(p, grid, s, tid);
+    else launch_variant<float, false>(p, grid, s, tid);
   } else {
-    if (p.rope) V4A_LAUNCH(tid, (compress_kernel<uint16_t, true>), grid, dim3(256), 0, s, p);
-    else V4A_LAUNCH(tid, (compress_kernel<uint16_t, false>), grid, dim3(256), 0, s, p);
+    if (hv) launch_variant<uint16_t, true>(p, grid, s, tid);
+    else launch_variant<uint16_t, false>(p, grid, s, tid);
   }
   return hipGetLastError();
 }

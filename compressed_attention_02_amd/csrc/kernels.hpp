@@ -82,6 +82,7 @@ struct AttnP {
   float scale;     // already resolved (never 0)
   const float* q_norm; float norm_eps;  // RMSNorm gain of the queries (null: none)
   int rope; int rope_out; double rope_lb;  // query rotation (R channels), output rotation at -p
+  int skv;             // shared entries: the value rows are the key rows (vc/vh/vr alias kc/kh/kr)
   // this launch covers the virtual keys [key_lo, key_hi) of every row, cut into
   // `splits` splits of keys_per_split keys; its partials go to slots
   // split_base .. split_base + splits - 1 of splits_total per row.  With

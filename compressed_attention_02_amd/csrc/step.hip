@@ -65,6 +65,7 @@ hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, con
   const int64_t n = select_attn_grid(n_sel, ap, csa, n_rows);
   const int64_t n_rest = (int64_t)ap.splits * n_rows;
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0 ||
+      (ap.dim != 64 && ap.dim != 128) ||
       ap.head_groups != 1 || (csa.sync && csa.head_groups != 1))
     return hipErrorInvalidValue;
   // the rest pre-merge needs the row words; with the picks attended in the same

@@ -45,11 +45,17 @@ class LayerShape:
     compress_t0: int
     pos: int               # position of the first query of the step
     tq: int
+    shared_kv: bool = False  # every entry is its own value (no V tensors)
+    rope_dims: int = 0       # partial RoPE of the query, output rotated back
+    rope_base: float = 1e4
+    q_norm: bool = False     # RMSNorm of the queries with the gain t["gq"]
+    norm_eps: float = 1e-6
 
     @classmethod
     def of(cls, cfg) -> "LayerShape":
         return cls(cfg.heads, cfg.dim, cfg.idx_heads, cfg.idx_dim, cfg.m, cfg.m_hca, cfg.window,
-                   max(cfg.topk, 1), cfg.branches, cfg.compress, cfg.compress_t0, cfg.pos, cfg.tq)
+                   max(cfg.topk, 1), cfg.branches, cfg.compress, cfg.compress_t0, cfg.pos, cfg.tq,
+                   shared_kv=cfg.shared_kv, rope_dims=cfg.rope_dims, q_norm=cfg.q_norm)
 
 
 class LayerStep:
@@ -76,12 +82,15 @@ class LayerStep:
         if s.compress == "none":
             return
         n = self.pos_max + 1 - s.compress_t0
+        # with RoPE, raw rows arrive rotated at their positions and entries are stored
+        # rotated at their block's last one (shared entries: the values are the keys)
+        rope = dict(rope_dims=s.rope_dims, rope_base=s.rope_base)
         if s.branches & CSA and s.compress in ("all", "chunk"):
-            compress(t["k_raw"], t["v_raw"], t["logit_csa"], t["raw_start"], t["kc"], t["vc"],
-                     t0=s.compress_t0, n=n, ratio=s.m, stream=stream)
+            compress(t["k_raw"], t.get("v_raw"), t["logit_csa"], t["raw_start"], t["kc"], t.get("vc"),
+                     t0=s.compress_t0, n=n, ratio=s.m, stream=stream, **rope)
         if s.branches & HCA:
-            compress(t["k_raw"], t["v_raw"], t["logit_hca"], t["raw_start"], t["kh"], t["vh"],
-                     t0=s.compress_t0, n=n, ratio=s.m_hca, stream=stream)
+            compress(t["k_raw"], t.get("v_raw"), t["logit_hca"], t["raw_start"], t["kh"], t.get("vh"),
+                     t0=s.compress_t0, n=n, ratio=s.m_hca, stream=stream, **rope)
 
     def run_index(self, stream=None):
         s, t = self.s, self.t
@@ -95,7 +104,9 @@ class LayerStep:
         return dict(lse=self.lse, idx=self.idx if s.branches & CSA else None, kc=t.get("kc"), vc=t.get("vc"),
                     kh=t.get("kh"), vh=t.get("vh"), k_raw=t.get("k_raw"), v_raw=t.get("v_raw"),
                     raw_start=t.get("raw_start"), branch_mask=s.branches, csa_ratio=s.m,
-                    hca_ratio=s.m_hca, window=s.window, topk=s.topk, pos_max=self.pos_max)
+                    hca_ratio=s.m_hca, window=s.window, topk=s.topk, pos_max=self.pos_max,
+                    shared_kv=s.shared_kv, rope_dims=s.rope_dims, rope_base=s.rope_base,
+                    rope_out=s.rope_dims > 0, q_norm=t.get("gq") if s.q_norm else None, norm_eps=s.norm_eps)
 
     def run_attn(self, stream=None):
         fn = decode if self.s.tq == 1 else prefill_chunk

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 3u
+#define V4ATTN_ABI_VERSION 4u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -95,7 +95,10 @@ typedef struct v4a_tensor {
  *   ratio        r >= 1
  *   t0, n        host; t0 >= 0 is a multiple of r, n >= 0; the same for all sequences
  *   raw_start    [batch] int64: position of raw row 0 of each sequence
- *   k_raw/v_raw  [batch][T_raw][d]
+ *   k_raw/v_raw  [batch][T_raw][d]; v_raw.ptr and v_out.ptr both NULL pools K
+ *                alone (shared K = V entries: [QbitAI] 混合注意力机制, the partial
+ *                RoPE paragraph, and [wiki] shared-KV MQA); norm_v must then be
+ *                NULL and rope_flags 0
  *   logits       fp32 [batch][T_raw], row_stride must be 1, no alignment needed
  *   k_out/v_out  [batch][N_cap][d] indexed by absolute block id
  *   norm_k/norm_v  fp32 [d] RMSNorm gains or NULL.  [QbitAI] 混合注意力机制,
@@ -193,14 +196,15 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *   out_dtype    must be F32 (o and lse are fp32)
  *   tq           query tokens per sequence: 1 for v4attn_decode, >= 1 for
  *                v4attn_prefill_chunk
- *   heads, dim   H <= 128; d = 64 or 128
+ *   heads, dim   H <= 128; d = 64, 128 or 512 (bf16 at 512: V4A_SHARED_KV only)
  *   csa_ratio, hca_ratio, window   m, m' >= 1; W >= 0
  *   topk         k, the row length of idx (CSA only), 1..2048
  *   scale        softmax scale; 0 selects 1/sqrt(d)
  *   pos0         [batch] int64; pos_max (host) >= pos0[b] + tq - 1 for all b
  *   q            [batch][tq][H][d] (row = query token, heads contiguous)
  *   idx          int32 [batch][tq][k], as written by v4attn_index_topk
- *   kc, vc       [batch][N_cap][d]; kh, vh [batch][E_cap][d]
+ *   kc, vc       [batch][N_cap][d]; kh, vh [batch][E_cap][d] (vc, vh, v_raw
+ *                NULL with V4A_SHARED_KV)
  *   k_raw, v_raw [batch][T_raw][d]; raw_start [batch] int64
  *   sink         fp32 [H] or NULL
  *   o            fp32 out [batch][tq][H][d] (row = query token)
@@ -221,7 +225,14 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *                nor on pos_max.  Key splits then have a fixed size (256 keys;
  *                64 for the CSA picks of v4attn_decode_step), the CSA picks'
  *                attention takes one 16-head tile per workgroup and the step
- *                runs in two launches.  Other bits: V4A_EINVAL.
+ *                runs in two launches.
+ *                V4A_SHARED_KV: every entry is its own value (v = k in the
+ *                formula above), read once; vc, vh and v_raw must be NULL.
+ *                [QbitAI] 混合注意力机制, the partial RoPE paragraph (the KV
+ *                entries serve as keys and values) and CSA step 4 (head
+ *                dimension c = 512); [wiki] shared-KV MQA.  With RoPE the values
+ *                carry the rotation too, which V4A_ROPE_OUTPUT takes back out.
+ *                Other bits: V4A_EINVAL.
  * The caller appends the query's own K/V to the raw buffers, and for a prefill
  * chunk runs v4attn_compress over the chunk first.
  * Workspace: v4attn_decode_workspace / v4attn_prefill_chunk_workspace.
@@ -233,8 +244,11 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  * too, so the output would carry absolute positions; V4A_ROPE_OUTPUT rotates o
  * at -p (its last rope_dims channels) to keep relative ones only. */
 #define V4A_ROPE_OUTPUT 2u
-/* v4a_compress_args.rope_flags: raw V rows are rotated too (shared K = V). */
+/* v4a_compress_args.rope_flags: raw V rows are rotated too. */
 #define V4A_ROPE_V 1u
+/* [QbitAI] 混合注意力机制 (the KV entries serve as keys and values; c = 512) and
+ * [wiki] shared-KV MQA: the key rows are the values, loaded once. */
+#define V4A_SHARED_KV 4u
 
 typedef struct v4a_attn_args {
   uint32_t abi_version;

@@ -21,16 +21,19 @@ Recipe (the same for every configuration):
     s_h shared across the chunk, which keeps every marginal N(0,1);
   * raw K/V exist only for the positions the step touches (window + compressed
     span); the 1M-token history is never materialised, its compressed caches are
-    drawn directly.  Caches hold at least one row even when no entry is visible.
+    drawn directly.  Caches hold at least one row even when no entry is visible;
+  * shared K = V configurations draw no V tensor (each entry is its own value);
+    with a query RMSNorm its per-channel gain is U(0.5, 1.5) fp32.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .configs import C1, C2, C3, C4, C5, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
+from .configs import C1, C2, C3, C4, C5, C6, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
 
+# appending a stream leaves the earlier ones' draws unchanged
 _STREAMS = ("q", "qi", "wi", "ki", "kc", "vc", "kh", "vh", "k_raw", "v_raw",
-            "logit_csa", "logit_hca", "needles", "shared")
+            "logit_csa", "logit_hca", "needles", "shared", "gq")
 
 
 def f32_to_bf16_bits(x) -> np.ndarray:
@@ -102,18 +105,23 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
         out["ki"] = _store(ki, cfg.dtype)
         out["needles"] = needles
         kc = rngs["kc"].standard_normal((B, max(cfg.n_cap, 1), d))
-        vc = rngs["vc"].standard_normal((B, max(cfg.n_cap, 1), d))
+        vc = None if cfg.shared_kv else rngs["vc"].standard_normal((B, max(cfg.n_cap, 1), d))
         if cfg.compress == "none" and cfg.needles:
             for b in range(B):
                 qm = _load(out["q"][b, 0], cfg.dtype).mean(axis=0)
                 kc[b, needles[b]] += 3.0 * qm / np.linalg.norm(qm)
         out["kc"] = _store(kc, cfg.dtype)
-        out["vc"] = _store(vc, cfg.dtype)
+        if not cfg.shared_kv:
+            out["vc"] = _store(vc, cfg.dtype)
     if use_hca:
         out["kh"] = _normal(rngs["kh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
-        out["vh"] = _normal(rngs["vh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
+        if not cfg.shared_kv:
+            out["vh"] = _normal(rngs["vh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
     out["k_raw"] = _normal(rngs["k_raw"], (B, cfg.raw_rows, d), cfg.dtype)
-    out["v_raw"] = _normal(rngs["v_raw"], (B, cfg.raw_rows, d), cfg.dtype)
+    if not cfg.shared_kv:
+        out["v_raw"] = _normal(rngs["v_raw"], (B, cfg.raw_rows, d), cfg.dtype)
+    if cfg.q_norm:
+        out["gq"] = rngs["gq"].uniform(0.5, 1.5, d).astype(np.float32)
     if cfg.compress != "none":
         out["logit_csa"] = rngs["logit_csa"].standard_normal((B, cfg.raw_rows)).astype(np.float32)
         out["logit_hca"] = rngs["logit_hca"].standard_normal((B, cfg.raw_rows)).astype(np.float32)

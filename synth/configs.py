@@ -44,6 +44,9 @@ class LayerConfig:
     seed: int
     timed: str            # what one timed step covers
     rho: float = 0.0      # shared-relevance mix of indexer queries (prefill only)
+    shared_kv: bool = False  # one tensor per branch: every entry is its own value
+    rope_dims: int = 0    # partial RoPE on the last rope_dims channels (0: off)
+    q_norm: bool = False  # RMSNorm of each head's query with a synthetic gain
 
     # ---- derived shape helpers (pure bookkeeping, no method arithmetic) ----
     @property
@@ -120,4 +123,13 @@ C5 = LayerConfig(
     branches=CSA | HCA | SWA, needles=64, compress="chunk", compress_tokens=4096,
     seed=20260005, timed="compress(chunk) + index_topk(4096) + prefill", rho=0.5)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+# The pages' own layer shape: shared K = V entries of c = 512 ([QbitAI] 混合注意力机制,
+# CSA step 4 and the partial RoPE paragraph; [wiki] shared-KV MQA), RoPE on the last
+# 64 channels, RMS-normalised queries, Pro's 128 heads and k = 1024 at 1M context.
+C6 = LayerConfig(
+    name="c6_shared_kv_c512_decode_b1_1m", dtype="bf16", batch=1, pos=1048576, tq=1, heads=128,
+    dim=512, idx_heads=64, idx_dim=64, m=4, topk=1024, m_hca=128, window=128,
+    branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
+    seed=20260006, timed="index_topk + decode", shared_kv=True, rope_dims=64, q_norm=True)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6)}

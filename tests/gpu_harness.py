@@ -120,7 +120,8 @@ class Run:
         cfg = self.cfg
         if cfg.compress == "none":
             return
-        kr, vr = O.as_f64(self.g["k_raw"], cfg.dtype), O.as_f64(self.g["v_raw"], cfg.dtype)
+        kr = O.as_f64(self.g["k_raw"], cfg.dtype)
+        vr = None if cfg.shared_kv else O.as_f64(self.g["v_raw"], cfg.dtype)
         t0 = cfg.compress_t0
         n = cfg.last_pos + 1 - t0
         todo = []
@@ -129,13 +130,15 @@ class Run:
         if cfg.branches & 2:
             todo.append(("logit_hca", cfg.m_hca, "kh", "vh"))
         for lg, r, kn, vn in todo:
-            gk, gv = self.f64(kn), self.f64(vn)
+            gk = self.f64(kn)
+            gv = None if cfg.shared_kv else self.f64(vn)
             for b in range(cfg.batch):
                 rs = int(self.g["raw_start"][b])
-                ids, ck = O.compress(kr[b], self.g[lg][b], rs, t0, n, r)
-                _, cv = O.compress(vr[b], self.g[lg][b], rs, t0, n, r)
+                ids, ck = O.compress_entries(kr[b], self.g[lg][b], rs, t0, n, r, rope_dims=cfg.rope_dims)
                 assert_close(gk[b, ids], ck, cfg.dtype, f"compress {kn} b={b}")
-                assert_close(gv[b, ids], cv, cfg.dtype, f"compress {vn} b={b}")
+                if gv is not None:
+                    _, cv = O.compress(vr[b], self.g[lg][b], rs, t0, n, r)
+                    assert_close(gv[b, ids], cv, cfg.dtype, f"compress {vn} b={b}")
 
     def oracle_scores(self, b, i):
         cfg = self.cfg
@@ -156,6 +159,12 @@ class Run:
 
     def oracle_attn(self, rows=None, sink=None, q_norm=None, norm_eps=1e-6, **rope):
         cfg = self.cfg
+        # a configuration's own query norm and RoPE (what LayerStep passes) unless
+        # the caller names them
+        if q_norm is None and cfg.q_norm:
+            q_norm = self.g["gq"].astype(np.float64)
+        if not rope and cfg.rope_dims:
+            rope = dict(rope_dims=cfg.rope_dims, rope_base=1e4, rope_out=True)
         idx = dev_to_np(self.step.idx)
         caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
         for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):

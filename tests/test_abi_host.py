@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 13
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 3
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 4
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -234,8 +234,32 @@ def test_decode_step_workspace_holds_row_words():
 
 
 def test_attention_rejects_unknown_flags():
-    r, msg = _st(V.lib().v4attn_decode, good_attn(flags=4), None, 0, None)
+    r, msg = _st(V.lib().v4attn_decode, good_attn(flags=8), None, 0, None)
     assert r == EINVAL and "flags" in msg
+
+
+def test_shared_kv_argument_checks():
+    L = V.lib()
+    # shared entries: the value tensors must be absent
+    r, msg = _st(L.v4attn_decode, good_attn(flags=V.SHARED_KV), None, 0, None)
+    assert r == EINVAL and "SHARED_KV" in msg
+    none = V.Tensor(None, 0, 0)
+    ok = good_attn(flags=V.SHARED_KV, vc=none, vh=none, v_raw=none)
+    assert L.v4attn_decode_workspace(ctypes.byref(ok)) > 0
+    # bf16 rows of 512 only as shared entries; 256 is no supported size
+    assert _st(L.v4attn_decode, good_attn(dim=512), None, 0, None)[0] == ENOTSUP
+    assert _st(L.v4attn_decode, good_attn(dim=256, flags=V.SHARED_KV, vc=none, vh=none, v_raw=none),
+               None, 0, None)[0] == ENOTSUP
+    wide = dict(dim=512, flags=V.SHARED_KV, vc=none, vh=none, v_raw=none, q=_T(bs=32768, rs=32768),
+                o=_T(bs=32768, rs=32768), kc=_T(bs=512 * 32768, rs=512), kh=_T(bs=512 * 1024, rs=512),
+                k_raw=_T(bs=512 * 128, rs=512))
+    assert L.v4attn_decode_workspace(ctypes.byref(good_attn(**wide))) > 0
+    assert L.v4attn_decode_workspace(ctypes.byref(good_attn(**dict(wide, dtype=V.F32)))) > 0
+    # K-only compression: v_raw and v_out both absent, and then no V gain or V rotation
+    assert _st(L.v4attn_compress, good_compress(v_out=none), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(v_raw=none, v_out=none, norm_v=FAKE), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(v_raw=none, v_out=none, rope_dims=64, rope_base=1e4,
+                                                rope_flags=V.ROPE_V), None)[0] == EINVAL
 
 
 @pytest.mark.parametrize("field,value", [("rope_dims", 3), ("rope_dims", 130), ("rope_dims", -2), ("rope_base", 0.0)])
