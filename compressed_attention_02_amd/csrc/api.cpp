@@ -321,12 +321,12 @@ v4a_status check_ws(void* ws, size_t have, size_t need) {
   return V4A_OK;
 }
 
-// Fewest head groups the attention kernel needs: bf16 rows of 512 take one 16-head
-// tile per wave of a 4-wave workgroup, so at most 64 heads per group; otherwise one.
+// Fewest head groups the attention kernel needs: bf16 rows of 512 take at most
+// kWideTiles 16-head tiles per workgroup (a wave pair each); otherwise one.
 int min_head_groups(const v4a_attn_args* a) {
-  if (a->dtype != V4A_BF16 || a->dim != 512) return 1;
+  if (a->dtype != V4A_BF16 || a->dim <= 128) return 1;
   const int ntile = std::max(1, a->heads / 16);
-  int hg = (ntile + 3) / 4;
+  int hg = (ntile + kWideTiles - 1) / kWideTiles;
   while (ntile % hg != 0) ++hg;
   return hg;
 }
@@ -541,7 +541,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   if (a->dtype == V4A_BF16 && P.s_csa > 0) {
     const int ntile = std::max(1, a->heads / 16);
     const int hmin = min_head_groups(a);
-    int hg = inv ? ntile : std::max(ntile, hmin);
+    int hg = ntile;
     while (!inv && hg > hmin && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
     csa.head_groups = hg;
   }
@@ -554,8 +554,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     IndexLaunch IL = index_launch(ix, ws);
     // selection and the selection-independent attention share one launch when the
     // rows fit one score pass and the attention is bf16
-    // (rows of 512 attend in 4-wave workgroups, which the selection's launch cannot
-    // host)
+    // (rows of 512 attend in the plain attention launches)
     const bool combined = a->dtype == V4A_BF16 && a->dim != 512 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
       // in the one-launch form (the whole grid resident at once, at most one

@@ -29,12 +29,11 @@ namespace v4a {
 
 // One workgroup of NW waves per (split, row); two workgroups per CU when each wave
 // computes one head tile over half the keys (KP = 2) or NW <= 4.  Shared entries of
-// D = 512 take most of the LDS (two 64 KB chunk buffers): one workgroup of 4 waves
-// per CU, one head tile per wave with the SIMD's whole register file (its O^T alone
-// is 128 registers, its queries 64); more than 64 heads come in head groups.
+// D = 512 take most of the LDS (two 64 KB chunk buffers): one workgroup of 8 waves
+// per CU, two waves per SIMD, a wave pair per head tile (attend_wide_*).
 template <int NW, int HT, int D, int KP>
 constexpr int attn_waves_per_eu() {
-  return D == 512 ? 1 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
+  return D == 512 ? 2 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
 }
 template <int NW, int HT, int D, int KP, bool QP, bool SKV>
 __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
@@ -181,9 +180,10 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   const int ntile = p.heads / 16 / p.head_groups;   // tiles per workgroup
   if (p.heads % (16 * p.head_groups) != 0 || ntile < 1 || ntile > 8) return hipErrorInvalidValue;
   if (p.dim == 512) {
-    // shared entries only: 4 waves, one head tile each
-    if (!p.skv || ntile > 4) return hipErrorInvalidValue;
-    launch_bf16<4, 1, 512, 1, true>(p, grid, s, tid);
+    // shared entries only: 8 waves, a wave pair per head tile, four tiles per
+    // workgroup (more heads come in head groups)
+    if (!p.skv || ntile > kWideTiles) return hipErrorInvalidValue;
+    launch_bf16<8, 1, 512, 1, true>(p, grid, s, tid);
     return hipGetLastError();
   }
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every

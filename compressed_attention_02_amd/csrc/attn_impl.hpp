@@ -341,8 +341,8 @@ struct RowKeys {
   int64_t n_csa, hca_end, raw_off, k_begin, k_end;
 };
 
-constexpr float kLazyRescale = 8.f;
-constexpr int kWideGroup = 4;        // LDS fragments per scheduling group at D = 512 // running max moves only when exceeded by 2^8
+constexpr float kLazyRescale = 8.f; // running max moves only when exceeded by 2^8
+constexpr int kWideGroup = 4;        // fragment steps per scheduling group of rows wider than 128
 
 // Source rows of key t in the general case (a chunk that straddles branches or
 // the end of the split): selects only.
@@ -380,6 +380,17 @@ template <int D> __device__ __forceinline__ int swz_v(int r) {
   return D == 512 ? swz_k<512>(r) : D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
+// Rows wider than 128 are kept as D / 128 stacked sub-buffers of 128 columns
+// (column group g of row r at (g * kAttnChunk + r) * 128), so that every sub-row is
+// 256 bytes like a d = 128 row: a load instruction then moves 4 rows of one group
+// (per-lane row addresses) and the XOR permutes 16 pieces.
+template <int D> constexpr int sub_cols() { return D > 128 ? 128 : D; }
+// element offset of 16-byte piece p of chunk row r in that layout
+template <int D> __device__ __forceinline__ int chunk_off(int r, int p, int x) {
+  constexpr int PS = sub_cols<D>() / 8;
+  return ((p / PS) * kAttnChunk + r) * sub_cols<D>() + ((p % PS) ^ x) * 8;
+}
+
 // s_waitcnt immediate for vmcnt(n) (gfx9: low 4 bits at [3:0], high 2 at [15:14]),
 // every other counter left alone
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
@@ -390,17 +401,19 @@ __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_
 }
 
 // Issues the loads of the chunk at virtual key kc0 straight into LDS (sK, sV) and
-// writes its mask (sBias[key] = 0 or -inf).  Each wave moves rows of 64 lanes x
-// 16 bytes per instruction; lane l's piece lands at LDS base + 16 l, so the lane
-// loads the global piece that the XOR layout puts there.  wave is uniform.
+// writes its mask (sBias[key] = 0 or -inf).  Each wave moves 64 lanes x 16 bytes
+// per instruction: RPI rows of one column group; lane l's piece lands at LDS base
+// + 16 l, so the lane loads the global piece that the XOR layout puts there.  A
+// lane's row address serves all column groups.  wave is uniform.
 template <int NW, int D, bool SKV>
 __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, int64_t kc0, uint16_t* sK,
                                             uint16_t* sV, float* sBias, int wave, int lane) {
-  constexpr int PIECES = D / 8;               // 16-byte pieces per row
-  constexpr int RPI = 64 / PIECES;            // rows per wave instruction
-  constexpr int IPW = kAttnChunk / RPI / NW;  // instructions per wave, for K and for V
-  static_assert(IPW * RPI * NW == kAttnChunk, "rows must divide over the waves");
-  const int prow = lane / PIECES, ppiece = lane % PIECES;
+  constexpr int SUB = sub_cols<D>(), NG = D / SUB;
+  constexpr int PS = SUB / 8;                     // 16-byte pieces per sub-row
+  constexpr int RPI = 64 / PS;                    // rows per wave instruction
+  constexpr int RBW = kAttnChunk / RPI / NW;      // row blocks per wave (NG instructions each)
+  static_assert(RBW * RPI * NW == kAttnChunk, "rows must divide over the waves");
+  const int prow = lane / PS, ppiece = lane % PS;
   // chunks wholly inside one branch (the common case) take a plain address
   const bool whole = kc0 + kAttnChunk <= R.k_end;
   const bool all_h = whole && kc0 >= R.n_csa && kc0 + kAttnChunk <= R.hca_end;
@@ -411,8 +424,8 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
   if (all_r) { kb = R.kr + (kc0 + R.raw_off) * R.kr_rs; vb = R.vr + (kc0 + R.raw_off) * R.vr_rs; ks = R.kr_rs; vs = R.vr_rs; }
   else if (all_h) { kb = R.kh + (kc0 - R.n_csa) * R.kh_rs; vb = R.vh + (kc0 - R.n_csa) * R.vh_rs; }
 #pragma unroll
-  for (int u = 0; u < IPW; ++u) {
-    const int r0 = (wave * IPW + u) * RPI;    // first row of this instruction (uniform)
+  for (int u = 0; u < RBW; ++u) {
+    const int r0 = (wave * RBW + u) * RPI;    // first row of this block (uniform)
     const int r = r0 + prow;
     const uint16_t *kp, *vp;
     bool ok = true;
@@ -427,8 +440,12 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
     } else {
       key_src_any(R, s_idx, kc0 + r, kp, vp, ok);
     }
-    lds_load16(kp + (ppiece ^ swz_k<D>(r)) * 8, lds_addr(sK + r0 * D));
-    if constexpr (!SKV) lds_load16(vp + (ppiece ^ swz_v<D>(r)) * 8, lds_addr(sV + r0 * D));
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      lds_load16(kp + (g * PS + (ppiece ^ swz_k<D>(r))) * 8, lds_addr(sK + (g * kAttnChunk + r0) * SUB));
+      if constexpr (!SKV)
+        lds_load16(vp + (g * PS + (ppiece ^ swz_v<D>(r))) * 8, lds_addr(sV + (g * kAttnChunk + r0) * SUB));
+    }
     if (ppiece == 0) sBias[r] = ok ? 0.f : -INFINITY;
   }
 }
@@ -456,23 +473,21 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   constexpr int NKT = 4 / KP;     // tiles of 16 keys of this wave: its part kh of the chunk
   f32x4 S[HT][NKT];
   // K fragment: row 16kt + col, piece 4s + grp; the row's XOR does not depend on kt
-  const uint16_t* kb = sK + col * D + 16 * NKT * kh * D;
+  const int kr0 = col + 16 * NKT * kh;
   const int kx = swz_k<D>(col);
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int t = 0; t < HT; ++t) S[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  static_assert(D <= 128, "rows wider than 128 take attend_wide_*");
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(kb + 16 * kt * D + ((4 * s + grp) ^ kx) * 8);
+      const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(sK + chunk_off<D>(kr0 + 16 * kt, 4 * s + grp, kx));
 #pragma unroll
       for (int t = 0; t < HT; ++t) S[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Qb[t][s], S[t][kt], 0, 0, 0);
-      // wide rows: fence every kWideGroup fragments, so that the scheduler does not
-      // hoist a whole chunk's fragment reads into registers
-      if constexpr (D > 128)
-        if (s % kWideGroup == kWideGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
-  }
   // logits in base 2 (masked keys -inf), in place
   float cm[HT];
   bool need = false;
@@ -514,7 +529,7 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   // the rows' XOR does not depend on kk
   const int vr = 4 * grp + (col >> 2);
   const int vx = swz_v<D>(vr);
-  const uint16_t* vb = sV + vr * D + (col & 1) * 4;
+  const uint16_t* vb = sV + (col & 1) * 4;
 #pragma unroll
   for (int k2 = 0; k2 < 2 / KP; ++k2) {
     const int kk = (2 / KP) * kh + k2;   // 32-key half of the chunk
@@ -535,11 +550,10 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      if constexpr (D > 128)
-        if (dt % kWideGroup == 0) __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* v0 = vb + 32 * kk * D + ((2 * dt + ((col & 3) >> 1)) ^ vx) * 8;
+      const uint16_t* v0 = vb + chunk_off<D>(vr + 32 * kk, 2 * dt + ((col & 3) >> 1), vx);
       const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0));
-      const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0 + 16 * D));
+      const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(v0 + 16 * sub_cols<D>()));
       const bf16x8_t A = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
@@ -561,7 +575,7 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
                                            float (&m_run)[HT], float (&l_run)[HT], float sl2, int wave, int lane,
                                            int kh) {
   constexpr int CH = kAttnChunk;
-  constexpr int IPW = CH / (64 / (D / 8)) / NW;  // direct loads per wave per chunk, for K and for V
+  constexpr int IPW = CH * (D / 8) / 64 / NW;     // direct loads per wave per chunk, for K and for V
   constexpr int LPW = SKV ? IPW : 2 * IPW;        // all of a chunk's loads per wave
   const int col = lane & 15, grp = lane >> 4;
   if (nch > 0) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
@@ -584,6 +598,160 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
   }
 }
 
+// ---- rows wider than 128 (d = 512 shared entries): one 16-head tile per wave
+// pair.  A tile's O^T alone would take 128 of a lane's registers and its queries
+// 64 more, which leaves none to keep LDS reads in flight; so the pair (lt, hh),
+// hh = 0, 1, splits the chunk: wave hh scores key tiles 2hh, 2hh+1 over all of d
+// (attend_wide_scores) and hands them to its partner through LDS; after a barrier
+// both hold the chunk's 64 logits per head, take the same softmax steps on the
+// same values, and wave hh accumulates columns [hh d/2, (hh+1) d/2) of O^T
+// (attend_wide_pv).  m and l are computed twice, identically.
+
+template <int D>
+__device__ __forceinline__ void attend_wide_scores(const uint16_t* sK, const float* sBias, float* sX,
+                                                   const bf16x8_t (&Qb)[1][D / 32], float sl2, int lt, int hh,
+                                                   int lane) {
+  constexpr int KS = D / 32;
+  const int col = lane & 15, grp = lane >> 4;
+  const int kx = swz_k<D>(col);
+  f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // two independent chains, software-pipelined by groups of kWideGroup steps: the
+  // fragment reads of group g + 1 are issued before the products of group g, and a
+  // scheduling fence closes each group, so a group's reads land while the
+  // previous group computes and no more than two groups are in registers
+  constexpr int G = kWideGroup, NGR = KS / G;
+  static_assert(KS % G == 0, "whole groups");
+  bf16x8_t A[2][G][2];
+  auto fetch = [&](int g, bf16x8_t (&buf)[G][2]) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        buf[u][j] = *reinterpret_cast<const bf16x8_t*>(sK + chunk_off<D>(16 * (2 * hh + j) + col, 4 * (g * G + u) + grp, kx));
+  };
+  fetch(0, A[0]);
+#pragma unroll
+  for (int g = 0; g < NGR; ++g) {
+    if (g + 1 < NGR) fetch(g + 1, A[(g + 1) & 1]);
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g & 1][u][j], Qb[0][g * G + u], S[j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kt = 2 * hh + j;
+    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * kt + 4 * grp]);
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = fmaf(S[j][e], sl2, bias[e]);
+    reinterpret_cast<f32x4*>(sX)[(lt * 4 + kt) * 64 + lane] = x;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void attend_wide_pv(const uint16_t* sV, const float* sX, f32x4 (&O)[1][D / 32],
+                                               float (&m_run)[1], float (&l_run)[1], int lt, int hh, int lane) {
+  constexpr int DH = D / 32;   // 16-column tiles of this wave's half
+  const int col = lane & 15, grp = lane >> 4;
+  f32x4 S[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) S[kt] = reinterpret_cast<const f32x4*>(sX)[(lt * 4 + kt) * 64 + lane];
+  float c = fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3]));
+#pragma unroll
+  for (int kt = 1; kt < 4; ++kt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = fmaxf(c, S[kt][e]);
+  const float cm = col_max4(c);
+  if (__builtin_amdgcn_ballot_w64(cm > m_run[0] + kLazyRescale)) {
+    const bool up = cm > m_run[0] + kLazyRescale;
+    const float alpha = up ? __builtin_amdgcn_exp2f(m_run[0] - cm) : 1.f;
+    m_run[0] = up ? cm : m_run[0];
+    l_run[0] *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DH; ++dt) O[0][dt] *= alpha;
+  }
+  const float mu = m_run[0] == -INFINITY ? 0.f : m_run[0];
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int vr = 4 * grp + (col >> 2);
+  const int vx = swz_v<D>(vr);
+  const uint16_t* vb = sV + (col & 1) * 4;
+  // P^T of both 32-key halves first, then the products, pipelined like the
+  // scores: the V^T fragments of group g + 1 (over (kk, dt)) are read before the
+  // products of group g
+  bf16x8_t Bhi[2], Blo[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = __builtin_amdgcn_exp2f(S[2 * kk + (e >> 2)][e & 3] - mu);
+      ps += v;
+      const __bf16 h = (__bf16)v;
+      Bhi[kk][e] = h;
+      Blo[kk][e] = (__bf16)(v - (float)h);
+    }
+    l_run[0] += ps;
+  }
+  constexpr int G = kWideGroup, NGR = 2 * DH / G;   // groups over (kk, dt), kk outer
+  static_assert(DH % G == 0, "whole groups");
+  bf16x8_t A[2][G];
+  auto fetch = [&](int g, bf16x8_t (&buf)[G]) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int kk = (g * G + u) / DH, dt = (g * G + u) % DH;
+      const uint16_t* v0 = vb + chunk_off<D>(vr + 32 * kk, 2 * (hh * DH + dt) + ((col & 3) >> 1), vx);
+      const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(v0));
+      const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(v0 + 16 * sub_cols<D>()));
+      buf[u] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  fetch(0, A[0]);
+#pragma unroll
+  for (int g = 0; g < NGR; ++g) {
+    if (g + 1 < NGR) fetch(g + 1, A[(g + 1) & 1]);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int kk = (g * G + u) / DH, dt = (g * G + u) % DH;
+      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g & 1][u], Bhi[kk], O[0][dt], 0, 0, 0);
+      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g & 1][u], Blo[kk], O[0][dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The chunk pipeline of the wide rows: as run_chunks, with the pair's hand-over
+// between the scores and the products (one more barrier per chunk).
+template <int NW, int D, bool SKV>
+__device__ __forceinline__ void run_chunks_wide(const RowKeys& R, const int* s_idx, uint16_t* K0, uint16_t* V0,
+                                                float* B0, uint16_t* K1, uint16_t* V1, float* B1, float* sX,
+                                                int64_t nch, bool active, const bf16x8_t (&Qb)[1][D / 32],
+                                                f32x4 (&O)[1][D / 32], float (&m_run)[1], float (&l_run)[1],
+                                                float sl2, int wave, int lane, int lt, int hh) {
+  constexpr int CH = kAttnChunk;
+  constexpr int IPW = CH * (D / 8) / 64 / NW;
+  constexpr int LPW = SKV ? IPW : 2 * IPW;
+  if (nch > 0) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin, K0, V0, B0, wave, lane);
+  if (nch > 1) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + CH, K1, V1, B1, wave, lane);
+  for (int64_t c = 0; c < nch; ++c) {
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    const bool odd = (c & 1) != 0;
+    uint16_t* Kc = odd ? K1 : K0;
+    uint16_t* Vc = odd ? V1 : V0;
+    float* Bc = odd ? B1 : B0;
+    if (active) attend_wide_scores<D>(Kc, Bc, sX, Qb, sl2, lt, hh, lane);
+    __syncthreads();
+    if (active) attend_wide_pv<D>(Vc, sX, O, m_run, l_run, lt, hh, lane);
+    __syncthreads();
+    if (c + 2 < nch) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
+  }
+}
+
 // LDS of one attention workgroup: two chunk buffers (K, V, mask; shared entries
 // (SKV) keep one row that serves as both) and the split's CSA ids.
 template <int D, bool SKV = false>
@@ -592,9 +760,11 @@ struct AttnSmem {
   union {
     uint16_t buf[(SKV ? 2 : 4) * kRows];
     // after the last chunk: the state (O, m, l) one key half hands to the other,
-    // per lane of 4 waves
-    float C[4 * 64 * (D / 4 + 2)];
+    // per lane of 4 waves (rows up to 128)
+    float C[D > 128 ? 1 : 4 * 64 * (D / 4 + 2)];
   };
+  // wide rows: the logits a wave pair hands over, [tile][key tile][lane] x 4
+  float X[D > 128 ? kWideTiles * 4 * 64 * 4 : 1];
   float B0[kAttnChunk], B1[kAttnChunk];
   int idx[kMaxTopk];
   int flag;
@@ -620,9 +790,11 @@ struct AttnSmem {
 template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
+  constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
+  static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1 && !STEP), "wide rows: 8 waves, one tile per pair");
   // xs = split * head_groups + group: the workgroup takes group's head tiles
   const int hgn = p.head_groups, split = xs / hgn, hgi = xs - split * hgn;
-  constexpr int TW = NW / KP;   // waves per key part: head tiles of one pass
+  constexpr int TW = WIDE ? kWideTiles : NW / KP;   // head tiles of one pass
   constexpr int NT = NW * 64, CH = kAttnChunk, KS = D / 32, DT = D / 16;
   int* s_idx = sm.idx;
   const int b = row / p.tq, i = row - b * p.tq;
@@ -640,7 +812,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   int tile[HT];
   bool tv[HT];   // the wave's tile t exists in the group
   bf16x8_t Qb[HT][KS];
-  const int kh = KP == 2 ? wave / TW : 0;
+  const int kh = (KP == 2 || WIDE) ? wave / TW : 0;   // key half, or the pair's half of a wide row
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     const int lt = wave % TW + TW * t;
@@ -694,58 +866,62 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   if (QP && (p.q_norm || p.rope)) {
     // RMSNorm of each head's query, then its rotation at pos, in fp32 and rounded
     // once: lane (col, grp) holds elements s*32 + grp*8 + e of head col, and the
-    // four grp lanes of a column hold the whole head
+    // four grp lanes of a column hold the whole head.  One 8-element slice at a
+    // time, so that no per-lane array outgrows the registers.
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
-      float qf[KS][8];
       float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf((float)Qb[t][s][e], (float)Qb[t][s][e], ss);
+      const float rq = p.q_norm ? rsqrtf(col_sum4(ss) / (float)D + p.norm_eps) : 1.f;
+      const int lo = D - p.rope;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float qf[8];
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qf[s][e] = (float)Qb[t][s][e];
-          ss = fmaf(qf[s][e], qf[s][e], ss);
+          qf[e] = (float)Qb[t][s][e];
+          if (p.q_norm) qf[e] = qf[e] * rq * p.q_norm[s * 32 + grp * 8 + e];
         }
-      if (p.q_norm) {
-        const float rq = rsqrtf(col_sum4(ss) / (float)D + p.norm_eps);
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qf[s][e] = qf[s][e] * rq * p.q_norm[s * 32 + grp * 8 + e];
-      }
-      if (p.rope) {
-        const int lo = D - p.rope;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
+        if (p.rope) {
 #pragma unroll
           for (int k2 = 0; k2 < 4; ++k2) {
             const int e0 = s * 32 + grp * 8 + 2 * k2;
             if (e0 < lo) continue;
             float cs, sn;
             rope_cs((double)pos, (e0 - lo) / 2, p.rope, p.rope_lb, cs, sn);
-            rot2(qf[s][2 * k2], qf[s][2 * k2 + 1], cs, sn, false);
+            rot2(qf[2 * k2], qf[2 * k2 + 1], cs, sn, false);
           }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Qb[t][s][e] = (__bf16)qf[e];
       }
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Qb[t][s][e] = (__bf16)qf[s][e];
     }
   }
 
+  // the 16-column tiles of O^T this wave holds (a wide row's pair splits them) and
+  // the first one's index
+  constexpr int DTW = WIDE ? DT / 2 : DT;
+  const int dt0 = WIDE ? kh * DTW : 0;
   float m_run[HT], l_run[HT];
-  f32x4 O[HT][DT];
+  f32x4 O[HT][DTW];
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DTW; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  run_chunks<NW, D, HT, KP, SKV>(R, s_idx, sm.K0(), sm.V0(), sm.B0, sm.K1(), sm.V1(), sm.B1, nch, tv[0], Qb, O,
-                                 m_run, l_run, sl2, wave, lane, kh);
+  if constexpr (WIDE)
+    run_chunks_wide<NW, D, SKV>(R, s_idx, sm.K0(), sm.V0(), sm.B0, sm.K1(), sm.V1(), sm.B1, sm.X, nch, tv[0], Qb,
+                                O, m_run, l_run, sl2, wave, lane, wave % TW, kh);
+  else
+    run_chunks<NW, D, HT, KP, SKV>(R, s_idx, sm.K0(), sm.V0(), sm.B0, sm.K1(), sm.V1(), sm.B1, nch, tv[0], Qb, O,
+                                   m_run, l_run, sl2, wave, lane, kh);
 
   if constexpr (KP == 2) {
     // the second key half hands (O, m, l) to the first through LDS; the chunk
@@ -775,7 +951,8 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
 
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
-    if (!tv[t] || kh != 0) continue;
+    if (!tv[t] || (KP == 2 && kh != 0)) continue;
+    const bool stats = !WIDE || kh == 0;   // one wave of a wide pair writes lse / (m, l)
     const int head = tile[t] * 16 + col;
     const float l = col_sum4(l_run[t]);
     if (p.splits_total == 1) {
@@ -783,29 +960,29 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
       const float f = finish_head(m_run[t], l, p.sink, head, &lse);
       float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DTW; ++dt) {
         float ov[4] = {O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f};
-        if (QP && p.rope_out) {  // back at -pos: channels dt*16 + 4*grp + e, pairs inside the lane
+        if (QP && p.rope_out) {  // back at -pos: channels (dt0+dt)*16 + 4*grp + e, pairs inside the lane
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
-            const int e0 = dt * 16 + 4 * grp + 2 * k2;
+            const int e0 = (dt0 + dt) * 16 + 4 * grp + 2 * k2;
             if (e0 < D - p.rope) continue;
             float cs, sn;
             rope_cs((double)pos, (e0 - (D - p.rope)) / 2, p.rope, p.rope_lb, cs, sn);
             rot2(ov[2 * k2], ov[2 * k2 + 1], cs, sn, true);
           }
         }
-        *reinterpret_cast<float4*>(orow + dt * 16 + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        *reinterpret_cast<float4*>(orow + (dt0 + dt) * 16 + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
       }
-      if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+      if (stats && grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
       const int64_t slot = ((int64_t)row * p.heads + head) * p.splits_total + p.split_base + split;
       float* po = p.part_o + slot * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + dt * 16 + 4 * grp) =
+      for (int dt = 0; dt < DTW; ++dt)
+        *reinterpret_cast<float4*>(po + (dt0 + dt) * 16 + 4 * grp) =
             make_float4(O[t][dt][0], O[t][dt][1], O[t][dt][2], O[t][dt][3]);
-      if (grp == 0)
+      if (stats && grp == 0)
         *reinterpret_cast<float2*>(p.part_ml + slot * 2) = poison ? make_float2(NAN, NAN) : make_float2(m_run[t], l);
     }
   }

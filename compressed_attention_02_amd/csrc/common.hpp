@@ -143,14 +143,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // Partial RoPE: cos and sin of the angle pos * 2^(-2i/R * lb) of channel pair i
-// (lb = log2 of the base).  The angle is formed and reduced to [-pi, pi] in fp64, so
-// positions in the millions keep their phase to ~1e-10 rad; the reduced angle then
-// goes through the fp32 sincos.
+// (lb = log2 of the base).  The angle is formed in fp64 and reduced there to
+// r = a - k pi/2 with |r| <= pi/4 (positions in the millions keep their phase to
+// ~1e-10 rad); sin r and cos r are their Taylor series through r^9 and r^10
+// (truncation below 2e-9 on that interval) in fp32, and the quadrant k mod 4
+// swaps and negates them.  No library sincos: its large-argument path keeps
+// per-lane arrays in scratch memory even when the argument is small.
 __device__ __forceinline__ void rope_cs(double pos, int i, int R, double lb, float& c, float& s) {
+  constexpr double kHalfPi = 1.5707963267948966, kTwoOverPi = 0.6366197723675814;
   const double th = exp2(-2.0 * (double)i / (double)R * lb);
-  double a = pos * th;
-  a -= 6.283185307179586 * rint(a * 0.15915494309189535);
-  sincosf((float)a, &s, &c);
+  const double a = pos * th;
+  const double k = rint(a * kTwoOverPi);
+  const float r = (float)(a - k * kHalfPi);
+  const float r2 = r * r;
+  const float ps = r * (1.f - r2 * (1.f / 6.f - r2 * (1.f / 120.f - r2 * (1.f / 5040.f - r2 * (1.f / 362880.f)))));
+  const float pc = 1.f - r2 * (0.5f - r2 * (1.f / 24.f - r2 * (1.f / 720.f - r2 * (1.f / 40320.f - r2 * (1.f / 3628800.f)))));
+  const int q = (int)((long long)k & 3);
+  s = q == 0 ? ps : q == 1 ? pc : q == 2 ? -ps : -pc;
+  c = q == 0 ? pc : q == 1 ? -ps : q == 2 ? -pc : ps;
 }
 // (x, y) turned by the angle whose cos and sin are (c, s); by its opposite with neg
 __device__ __forceinline__ void rot2(float& x, float& y, float c, float s, bool neg) {

@@ -62,6 +62,7 @@ hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels
+constexpr int kWideTiles = 4;   // 16-head tiles per workgroup for rows wider than 128 (a wave pair each)
 constexpr int kStepMaxSplits = 256;  // splits per row the one-launch decode step merges in-kernel
 constexpr int kAttnMaxSplits = 1024;
 

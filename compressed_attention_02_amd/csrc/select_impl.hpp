@@ -514,7 +514,7 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
           for (int j = 0; j < kTileTop; ++j) {
             const uint32_t id = rep_id(q, j);
             const uint32_t pk = picked_bits(uk[q][j], id, T, id_max);
-            *(pk & (o < (uint32_t)k) ? &sh.pool_id[o] : &sh.hist[kBins + lane]) = id;
+            *((pk & (o < (uint32_t)k)) ? &sh.pool_id[o] : &sh.hist[kBins + lane]) = id;
             o += pk;
           }
         }

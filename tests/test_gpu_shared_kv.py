@@ -3,10 +3,10 @@ values, head dimension c = 512, RoPE on the last 64 channels with the output rot
 back; [wiki] shared-KV MQA) against the fp64 oracle, through the C ABI.
 
 The oracle attends with each entry as its own value (no V tensor exists); the GPU
-reads each row once.  Rows of 512 run in 4-wave workgroups of up to 64 heads (head
-groups above), so the cases cover 16, 64, 80 (five groups) and 128 heads, every
-branch subset, the sink, prefill rows and the decode step, plus the fp32 path and
-the d = 128 aliasing path.
+reads each row once.  Rows of 512 run one 16-head tile per wave, two waves per
+tile on the halves of every chunk up to 64 heads, so the cases cover 16, 64, 80
+(idle waves) and 128 heads, every branch subset, the sink, prefill rows and the
+decode step, plus the fp32 path and the d = 128 aliasing path.
 """
 import numpy as np
 import pytest
