@@ -36,7 +36,7 @@ SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
 ABI_VERSION = 4
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
-           "select_attn": 6}
+           "select_attn": 6, "qprep": 7}
 
 
 class V4AttnError(RuntimeError):

@@ -98,7 +98,7 @@ std::mutex g_tmu;
 Timing g_timing[V4A_K_COUNT];
 
 const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select", "attn", "merge",
-                                          "prefill", "select_attn"};
+                                          "prefill", "select_attn", "qprep"};
 
 // ---------------------------------------------------------------- plans
 struct IndexPlan {
@@ -126,8 +126,30 @@ IndexPlan plan_index(const v4a_index_args* a) {
 
 struct AttnPlan {
   int64_t rows, n_keys, splits, kps;
-  size_t ws_bytes;
+  size_t off_q, ws_bytes;   // off_q: prepared bf16 queries (when qprep), after the partials
 };
+
+// bf16 queries with a norm gain or a rotation are prepared once per row
+// (launch_qprep) into the workspace: rows * heads * dim bf16
+bool needs_qprep(const v4a_attn_args* a) { return a->dtype == V4A_BF16 && (a->q_norm || a->rope_dims > 0); }
+size_t add_qprep(const v4a_attn_args* a, int64_t rows, size_t& ws_bytes) {
+  if (!needs_qprep(a)) return 0;
+  const size_t off = (size_t)round_up((int64_t)ws_bytes, 256);
+  ws_bytes = off + (size_t)rows * a->heads * a->dim * 2;
+  return off;
+}
+
+// Prepares the queries (if needed) and points p at them.
+v4a_status prep_queries(const v4a_attn_args* a, AttnP& p, int64_t rows, void* ws, size_t off_q, hipStream_t s) {
+  if (!needs_qprep(a)) return V4A_OK;
+  uint16_t* qb = (uint16_t*)((char*)ws + off_q);
+  V4A_TRY(hip_check(launch_qprep(p, (int)rows, qb, s, V4A_K_QPREP), "query prep launch"));
+  p.q = qb;
+  p.q_rs = (int64_t)a->heads * a->dim;
+  p.q_bs = (int64_t)a->tq * p.q_rs;
+  p.q_norm = nullptr;
+  return V4A_OK;
+}
 
 // Splits of the virtual key list: enough (split, row) workgroups to cover the
 // chip twice, but at least kMinKeysPerSplit keys each, since every split writes a
@@ -164,6 +186,7 @@ AttnPlan plan_attn(const v4a_attn_args* a) {
   } else {
     P.ws_bytes = (size_t)(P.rows * P.splits * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
   }
+  P.off_q = add_qprep(a, P.rows, P.ws_bytes);
   return P;
 }
 
@@ -273,7 +296,7 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if ((a->flags & V4A_ROPE_OUTPUT) && a->rope_dims == 0) return fail(V4A_EINVAL, "V4A_ROPE_OUTPUT needs rope_dims > 0");
   if (a->q_norm && !(a->norm_eps >= 0.f && std::isfinite(a->norm_eps)))
     return fail(V4A_EINVAL, "norm_eps must be finite and >= 0");
-  if (a->q_norm && !aligned(a->q_norm, 4)) return fail(V4A_EINVAL, "q_norm must be 4-byte aligned");
+  if (a->q_norm && !aligned(a->q_norm, 16)) return fail(V4A_EINVAL, "q_norm must be 16-byte aligned");
   if (a->branch_mask & V4A_CSA) {
     if (a->topk < 1) return fail(V4A_EINVAL, "topk must be >= 1");
     if (a->topk > kMaxTopk) return fail(V4A_ENOTSUP, "topk %d > %d", a->topk, kMaxTopk);
@@ -375,7 +398,8 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   const AttnPlan P = plan_attn(a);
   if (P.splits > INT32_MAX || P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
-  const AttnP p = make_attn_params(a, P, ws);
+  AttnP p = make_attn_params(a, P, ws);
+  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s));
   const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
   V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
   if (P.splits > 1) {
@@ -449,7 +473,7 @@ struct StepPlan {
   bool csa;
   IndexPlan ix;
   int64_t rows, n_rest, kps_rest, s_rest, s_csa, s_total;
-  size_t off_attn, off_sync, ws_bytes;
+  size_t off_attn, off_sync, off_q, ws_bytes;
 };
 
 // Bound of each wait of the one-launch step, in ticks of the 100 MHz clock.
@@ -487,6 +511,7 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   // per row {selection published, splits done} for the one-launch step
   P.off_sync = (size_t)round_up((int64_t)P.ws_bytes, 256);
   if (P.csa) P.ws_bytes = P.off_sync + (size_t)P.rows * kRowWords * sizeof(int);
+  P.off_q = add_qprep(a, P.rows, P.ws_bytes);
   return P;
 }
 
@@ -521,6 +546,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     p.part_o = (float*)((char*)ws + P.off_attn);
     p.part_ml = p.part_o + (size_t)P.rows * P.s_total * a->heads * a->dim;
   }
+  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s));
   // batch-invariant plans put the CSA slots first, so that the rest's split count
   // (from pos_max) only appends empty slots at the end of the merge order
   const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void
 
 template <int NW, int HT, int D, int KP, bool SKV>
 static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
-  if (p.q_norm || p.rope) V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, true, SKV>), grid, dim3(NW * 64), 0, s, p);
+  if (p.rope_out) V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, true, SKV>), grid, dim3(NW * 64), 0, s, p);
   else V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, false, SKV>), grid, dim3(NW * 64), 0, s, p);
 }
 
@@ -153,6 +153,70 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
       if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_run);
     }
   }
+}
+
+// ------------------------------------------------------------------ query prep
+// [QbitAI] 混合注意力机制, the Q/KV normalization and partial RoPE paragraphs: each
+// head's query is RMS-normalised with the gain, then its last R channels rotated at
+// the row's position, in fp32 from the bf16 input and rounded to bf16 once.  A
+// thread holds 8 consecutive channels of one head (pairs stay inside it); the D/8
+// threads of a head are neighbouring lanes and add their squares by butterfly.
+// Done once per row here rather than in every attention workgroup of the row.
+template <int D>
+__global__ __launch_bounds__(256) void qprep_kernel(AttnP p, uint16_t* qout) {
+  constexpr int GS = D / 8;   // threads per head
+  const int row = blockIdx.x;
+  const int b = row / p.tq, i = row - b * p.tq;
+  const int g = blockIdx.y * 256 + threadIdx.x;   // 8-channel group of the row
+  const bool ok = g < p.heads * GS;
+  const int part = g % GS;
+  float x[8];
+  if (ok) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs + g * 8;
+    unpack8(*reinterpret_cast<const uint4*>(src), x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  if (p.q_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int m = 1; m < GS; m <<= 1) ss += __shfl_xor(ss, m);
+    const float rq = rsqrtf(ss / (float)D + p.norm_eps);
+    if (ok) {
+      const float4 g0 = *reinterpret_cast<const float4*>(p.q_norm + part * 8);
+      const float4 g1 = *reinterpret_cast<const float4*>(p.q_norm + part * 8 + 4);
+      const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * rq * gs[e];
+    }
+  }
+  if (!ok) return;
+  if (p.rope) {
+    const int64_t pos = p.pos0[b] + i;
+    const int lo = D - p.rope;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int ch = part * 8 + 2 * k2;
+      if (ch < lo) continue;
+      float cs, sn;
+      rope_cs((double)pos, (ch - lo) / 2, p.rope, p.rope_lb, cs, sn);
+      rot2(x[2 * k2], x[2 * k2 + 1], cs, sn, false);
+    }
+  }
+  *reinterpret_cast<uint4*>(qout + (int64_t)row * p.heads * D + g * 8) = pack8(x);
+}
+
+hipError_t launch_qprep(const AttnP& p, int nrows, uint16_t* qout, hipStream_t s, int tid) {
+  const int groups = p.heads * (p.dim / 8);
+  const dim3 grid((unsigned)nrows, (unsigned)((groups + 255) / 256));
+  if (p.dim == 64) V4A_LAUNCH(tid, qprep_kernel<64>, grid, dim3(256), 0, s, p, qout);
+  else if (p.dim == 128) V4A_LAUNCH(tid, qprep_kernel<128>, grid, dim3(256), 0, s, p, qout);
+  else if (p.dim == 512) V4A_LAUNCH(tid, qprep_kernel<512>, grid, dim3(256), 0, s, p, qout);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ merge

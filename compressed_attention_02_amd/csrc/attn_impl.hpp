@@ -343,6 +343,9 @@ struct RowKeys {
 
 constexpr float kLazyRescale = 8.f; // running max moves only when exceeded by 2^8
 constexpr int kWideGroup = 4;        // fragment steps per scheduling group of rows wider than 128
+// rows wider than 128: a wave pair splits the scores and hands them over through LDS
+// (true), or each wave scores the whole chunk itself (false)
+constexpr bool kWideHandOver = true;
 
 // Source rows of key t in the general case (a chunk that straddles branches or
 // the end of the split): selects only.
@@ -607,27 +610,28 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
 // same values, and wave hh accumulates columns [hh d/2, (hh+1) d/2) of O^T
 // (attend_wide_pv).  m and l are computed twice, identically.
 
-template <int D>
-__device__ __forceinline__ void attend_wide_scores(const uint16_t* sK, const float* sBias, float* sX,
-                                                   const bf16x8_t (&Qb)[1][D / 32], float sl2, int lt, int hh,
-                                                   int lane) {
+// logits (base 2, masked) of key tiles kt0 .. kt0 + NJ - 1 of the chunk over all of d
+template <int D, int NJ>
+__device__ __forceinline__ void wide_logits(const uint16_t* sK, const float* sBias, const bf16x8_t (&Qb)[1][D / 32],
+                                            float sl2, int kt0, int lane, f32x4 (&S)[NJ]) {
   constexpr int KS = D / 32;
   const int col = lane & 15, grp = lane >> 4;
   const int kx = swz_k<D>(col);
-  f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // two independent chains, software-pipelined by groups of kWideGroup steps: the
   // fragment reads of group g + 1 are issued before the products of group g, and a
   // scheduling fence closes each group, so a group's reads land while the
   // previous group computes and no more than two groups are in registers
-  constexpr int G = kWideGroup, NGR = KS / G;
+  constexpr int G = kWideGroup * 2 / NJ, NGR = KS / G;
   static_assert(KS % G == 0, "whole groups");
-  bf16x8_t A[2][G][2];
-  auto fetch = [&](int g, bf16x8_t (&buf)[G][2]) {
+  bf16x8_t A[2][G][NJ];
+  auto fetch = [&](int g, bf16x8_t (&buf)[G][NJ]) {
 #pragma unroll
     for (int u = 0; u < G; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        buf[u][j] = *reinterpret_cast<const bf16x8_t*>(sK + chunk_off<D>(16 * (2 * hh + j) + col, 4 * (g * G + u) + grp, kx));
+      for (int j = 0; j < NJ; ++j)
+        buf[u][j] = *reinterpret_cast<const bf16x8_t*>(sK + chunk_off<D>(16 * (kt0 + j) + col, 4 * (g * G + u) + grp, kx));
   };
   fetch(0, A[0]);
 #pragma unroll
@@ -636,29 +640,35 @@ __device__ __forceinline__ void attend_wide_scores(const uint16_t* sK, const flo
 #pragma unroll
     for (int u = 0; u < G; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g & 1][u][j], Qb[0][g * G + u], S[j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int kt = 2 * hh + j;
-    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * kt + 4 * grp]);
-    f32x4 x;
+  for (int j = 0; j < NJ; ++j) {
+    const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * (kt0 + j) + 4 * grp]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = fmaf(S[j][e], sl2, bias[e]);
-    reinterpret_cast<f32x4*>(sX)[(lt * 4 + kt) * 64 + lane] = x;
+    for (int e = 0; e < 4; ++e) S[j][e] = fmaf(S[j][e], sl2, bias[e]);
   }
 }
 
+// the pair's hand-over: wave hh scores key tiles 2hh, 2hh + 1 into sX
 template <int D>
-__device__ __forceinline__ void attend_wide_pv(const uint16_t* sV, const float* sX, f32x4 (&O)[1][D / 32],
-                                               float (&m_run)[1], float (&l_run)[1], int lt, int hh, int lane) {
+__device__ __forceinline__ void attend_wide_scores(const uint16_t* sK, const float* sBias, float* sX,
+                                                   const bf16x8_t (&Qb)[1][D / 32], float sl2, int lt, int hh,
+                                                   int lane) {
+  f32x4 S[2];
+  wide_logits<D, 2>(sK, sBias, Qb, sl2, 2 * hh, lane, S);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) reinterpret_cast<f32x4*>(sX)[(lt * 4 + 2 * hh + j) * 64 + lane] = S[j];
+}
+
+// softmax of the chunk's logits S (4 key tiles) and this wave's half of O^T += V^T P^T
+template <int D>
+__device__ __forceinline__ void attend_wide_pv(const uint16_t* sV, const f32x4 (&S)[4], f32x4 (&O)[1][D / 32],
+                                               float (&m_run)[1], float (&l_run)[1], int hh, int lane) {
   constexpr int DH = D / 32;   // 16-column tiles of this wave's half
   const int col = lane & 15, grp = lane >> 4;
-  f32x4 S[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) S[kt] = reinterpret_cast<const f32x4*>(sX)[(lt * 4 + kt) * 64 + lane];
   float c = fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3]));
 #pragma unroll
   for (int kt = 1; kt < 4; ++kt)
@@ -744,9 +754,20 @@ __device__ __forceinline__ void run_chunks_wide(const RowKeys& R, const int* s_i
     uint16_t* Kc = odd ? K1 : K0;
     uint16_t* Vc = odd ? V1 : V0;
     float* Bc = odd ? B1 : B0;
-    if (active) attend_wide_scores<D>(Kc, Bc, sX, Qb, sl2, lt, hh, lane);
-    __syncthreads();
-    if (active) attend_wide_pv<D>(Vc, sX, O, m_run, l_run, lt, hh, lane);
+    if constexpr (kWideHandOver) {
+      if (active) attend_wide_scores<D>(Kc, Bc, sX, Qb, sl2, lt, hh, lane);
+      __syncthreads();
+      if (active) {
+        f32x4 S[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) S[kt] = reinterpret_cast<const f32x4*>(sX)[(lt * 4 + kt) * 64 + lane];
+        attend_wide_pv<D>(Vc, S, O, m_run, l_run, hh, lane);
+      }
+    } else if (active) {
+      f32x4 S[4];
+      wide_logits<D, 4>(Kc, Bc, Qb, sl2, 0, lane, S);
+      attend_wide_pv<D>(Vc, S, O, m_run, l_run, hh, lane);
+    }
     __syncthreads();
     if (c + 2 < nch) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
   }
@@ -784,9 +805,9 @@ struct AttnSmem {
 // and not written.  All waves load.
 // Chunks are double-buffered in LDS: the loads of chunk c + 1 are in flight while
 // chunk c is computed.
-// QP: the query is RMS-normalised and/or rotated in the block and the output may be
-// rotated back; without it the kernel carries none of that code.  SKV: every entry
-// is its own value (shared K = V rows, loaded once).
+// QP: the output is rotated back at -pos (the query arrives normalised and rotated
+// from launch_qprep); without it the kernel carries none of that code.  SKV: every
+// entry is its own value (shared K = V rows, loaded once).
 template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
@@ -861,44 +882,6 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     for (int u = 0; u < IDX_PER; ++u)
       if (u * NT + tid < n_idx) s_idx[u * NT + tid] = ids[u];
     __syncthreads();
-  }
-
-  if (QP && (p.q_norm || p.rope)) {
-    // RMSNorm of each head's query, then its rotation at pos, in fp32 and rounded
-    // once: lane (col, grp) holds elements s*32 + grp*8 + e of head col, and the
-    // four grp lanes of a column hold the whole head.  One 8-element slice at a
-    // time, so that no per-lane array outgrows the registers.
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf((float)Qb[t][s][e], (float)Qb[t][s][e], ss);
-      const float rq = p.q_norm ? rsqrtf(col_sum4(ss) / (float)D + p.norm_eps) : 1.f;
-      const int lo = D - p.rope;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        float qf[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qf[e] = (float)Qb[t][s][e];
-          if (p.q_norm) qf[e] = qf[e] * rq * p.q_norm[s * 32 + grp * 8 + e];
-        }
-        if (p.rope) {
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2) {
-            const int e0 = s * 32 + grp * 8 + 2 * k2;
-            if (e0 < lo) continue;
-            float cs, sn;
-            rope_cs((double)pos, (e0 - lo) / 2, p.rope, p.rope_lb, cs, sn);
-            rot2(qf[2 * k2], qf[2 * k2 + 1], cs, sn, false);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Qb[t][s][e] = (__bf16)qf[e];
-      }
-    }
   }
 
   // the 16-column tiles of O^T this wave holds (a wide row's pair splits them) and

@@ -106,6 +106,9 @@ struct AttnP {
 };
 constexpr int kRowWords = 4;
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
+// bf16 queries normalised (q_norm) and rotated (rope) once per row into qout
+// [rows][heads][dim] (bf16, rounded once), which the attention then reads as is
+hipError_t launch_qprep(const AttnP& p, int nrows, uint16_t* qout, hipStream_t s, int tid);
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
 
 // selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)

@@ -52,7 +52,7 @@ template <int D, int KP>
 static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int nr, dim3 g,
                       hipStream_t s, int tid) {
   const dim3 blk(kSelThreads);
-  if (ap.q_norm || ap.rope) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+  if (ap.rope_out) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
   else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
 }
 

@@ -209,7 +209,7 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *   sink         fp32 [H] or NULL
  *   o            fp32 out [batch][tq][H][d] (row = query token)
  *   lse          fp32 out [batch][tq][H] (row = query token) or ptr == NULL
- *   q_norm       fp32 [d] RMSNorm gain for every head's query, or NULL:
+ *   q_norm       fp32 [d], 16-byte aligned: RMSNorm gain for every head's query, or NULL:
  *                q_h is used as g * q_h / sqrt(mean(q_h^2) + norm_eps) ([QbitAI]
  *                混合注意力机制, Q/KV normalization); the bf16 path rounds the
  *                normalised query to bf16.  norm_eps >= 0, finite.
@@ -354,7 +354,8 @@ enum {
   V4A_K_MERGE = 4,
   V4A_K_PREFILL = 5,
   V4A_K_SELECT_ATTN = 6, /* v4attn_decode_step: selection + HCA/window attention */
-  V4A_K_COUNT = 7
+  V4A_K_QPREP = 7,       /* bf16 queries normalised / rotated once per row */
+  V4A_K_COUNT = 8
 };
 v4a_status v4attn_timing_enable(int kernel, int max_launches);
 int v4attn_timing_read(int kernel, float* ms, int cap);
