@@ -580,8 +580,8 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     IndexLaunch IL = index_launch(ix, ws);
     // selection and the selection-independent attention share one launch when the
     // rows fit one score pass and the attention is bf16
-    // (rows of 512 attend in the plain attention launches)
-    const bool combined = a->dtype == V4A_BF16 && a->dim != 512 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
+    // (rows of 512 join it too, but never in the one-launch form)
+    const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
       // in the one-launch form (the whole grid resident at once, at most one
       // workgroup per CU) the picks' attention and the merge join the launch; the
@@ -590,7 +590,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
       AttnP csa_in = csa;
       csa_in.head_groups = 1;   // the one-launch roles take every head
       csa_in.sync = words;
-      const bool one_launch = !inv && g_one_launch.load() != 0 && P.s_rest >= 2 &&
+      const bool one_launch = !inv && a->dim <= 128 && g_one_launch.load() != 0 && P.s_rest >= 2 &&
                               select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&
                               P.s_total <= kStepMaxSplits;
       const bool premerge = one_launch;

@@ -812,7 +812,7 @@ template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, boo
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
-  static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1 && !STEP), "wide rows: 8 waves, one tile per pair");
+  static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1), "wide rows: 8 waves, one tile per pair");
   // xs = split * head_groups + group: the workgroup takes group's head tiles
   const int hgn = p.head_groups, split = xs / hgn, hgi = xs - split * hgn;
   constexpr int TW = WIDE ? kWideTiles : NW / KP;   // head tiles of one pass
@@ -970,7 +970,8 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     }
   }
 
-  if (STEP && p.sync) {
+  // (wide rows have no one-launch form: the host never sets sync for them)
+  if constexpr (STEP && !WIDE) if (p.sync) {
     int* w = p.sync + kRowWords * row;
     static_assert(kMergeLds(NT, D, kStepMaxSplits) <= 4 * 64 * (D / 4 + 2), "merge scratch fits the chunk buffers");
     if (p.premerge) {

@@ -24,7 +24,7 @@ namespace v4a {
 
 template <int D>
 union StepSmem {
-  AttnSmem<D> attn;
+  AttnSmem<D, D == 512> attn;   // rows of 512 are shared entries
   SelShared sel;
 };
 
@@ -41,10 +41,11 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   }
   const int a = blk - n_sel;
   if (a < n_rest) {
-    attn_block<8, 1, D, KP, true, QP>(ap, a % ap.splits, a / ap.splits, sm.attn);
+    const int xw = ap.splits * ap.head_groups;   // (split, head group) workgroups per row
+    attn_block<8, 1, D, KP, true, QP, D == 512>(ap, a % xw, a / xw, sm.attn);
   } else {
     const int c = a - n_rest;
-    attn_block<8, 1, D, KP, true, QP>(csa, c % csa.splits, c / csa.splits, sm.attn);
+    attn_block<8, 1, D, KP, true, QP, D == 512>(csa, c % csa.splits, c / csa.splits, sm.attn);
   }
 }
 
@@ -57,16 +58,16 @@ static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP
 }
 
 int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows) {
-  return (int64_t)n_sel + ((int64_t)ap.splits + (csa.sync ? csa.splits : 0)) * n_rows;
+  return (int64_t)n_sel + ((int64_t)ap.splits * ap.head_groups + (csa.sync ? csa.splits : 0)) * n_rows;
 }
 
 hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int n_rows,
                               hipStream_t s, int tid) {
   const int64_t n = select_attn_grid(n_sel, ap, csa, n_rows);
-  const int64_t n_rest = (int64_t)ap.splits * n_rows;
+  const int64_t n_rest = (int64_t)ap.splits * ap.head_groups * n_rows;
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0 ||
-      (ap.dim != 64 && ap.dim != 128) ||
-      ap.head_groups != 1 || (csa.sync && csa.head_groups != 1))
+      (ap.dim != 64 && ap.dim != 128 && !(ap.dim == 512 && ap.skv && !ap.sync)) ||
+      (ap.dim != 512 && ap.head_groups != 1) || ap.head_groups < 1 || (csa.sync && csa.head_groups != 1))
     return hipErrorInvalidValue;
   // the rest pre-merge needs the row words; with the picks attended in the same
   // launch both parts carry them, the picks' part waits for the selection, and
@@ -83,7 +84,11 @@ hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, con
   // up to 64 heads, two waves per head tile take half of every chunk's keys each
   const dim3 g((unsigned)n);
   const int nr = (int)n_rest;
-  if (ap.heads <= 64) {
+  if (ap.dim == 512) {
+    // shared rows of 512: a wave pair per head tile, head groups of kWideTiles tiles
+    if (ap.heads / 16 / ap.head_groups > kWideTiles) return hipErrorInvalidValue;
+    launch_sa<512, 1>(sp, n_sel, ap, csa, nr, g, s, tid);
+  } else if (ap.heads <= 64) {
     if (ap.dim == 64) launch_sa<64, 2>(sp, n_sel, ap, csa, nr, g, s, tid);
     else launch_sa<128, 2>(sp, n_sel, ap, csa, nr, g, s, tid);
   } else {
