@@ -139,12 +139,24 @@ size_t add_qprep(const v4a_attn_args* a, int64_t rows, size_t& ws_bytes) {
   return off;
 }
 
-// Prepares the queries (if needed) and points p at them.
-v4a_status prep_queries(const v4a_attn_args* a, AttnP& p, int64_t rows, void* ws, size_t off_q, hipStream_t s) {
+QPrepP qprep_params(const v4a_attn_args* a, const AttnP& p, void* ws, size_t off_q) {
+  QPrepP q{};
+  q.q = a->q.ptr; q.q_bs = a->q.batch_stride; q.q_rs = a->q.row_stride;
+  q.gain = a->q_norm; q.eps = a->norm_eps;
+  q.rope = a->rope_dims; q.rope_lb = p.rope_lb;
+  q.heads = a->heads; q.dim = a->dim; q.tq = a->tq; q.pos0 = a->pos0;
+  q.out = (uint16_t*)((char*)ws + off_q);
+  return q;
+}
+
+// Points p at the prepared queries (when the queries need it); with launch, also
+// launches the prep (else a score launch of the step carries it).
+v4a_status prep_queries(const v4a_attn_args* a, AttnP& p, int64_t rows, void* ws, size_t off_q, hipStream_t s,
+                        bool launch) {
   if (!needs_qprep(a)) return V4A_OK;
-  uint16_t* qb = (uint16_t*)((char*)ws + off_q);
-  V4A_TRY(hip_check(launch_qprep(p, (int)rows, qb, s, V4A_K_QPREP), "query prep launch"));
-  p.q = qb;
+  const QPrepP q = qprep_params(a, p, ws, off_q);
+  if (launch) V4A_TRY(hip_check(launch_qprep(q, (int)rows, s, V4A_K_QPREP), "query prep launch"));
+  p.q = q.out;
   p.q_rs = (int64_t)a->heads * a->dim;
   p.q_bs = (int64_t)a->tq * p.q_rs;
   p.q_norm = nullptr;
@@ -399,7 +411,7 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   if (P.splits > INT32_MAX || P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
   AttnP p = make_attn_params(a, P, ws);
-  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s));
+  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s, true));
   const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
   V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
   if (P.splits > 1) {
@@ -546,7 +558,11 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     p.part_o = (float*)((char*)ws + P.off_attn);
     p.part_ml = p.part_o + (size_t)P.rows * P.s_total * a->heads * a->dim;
   }
-  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s));
+  // the selection's launch hosts the rest of the rows' attention when the rows fit
+  // one score pass and the attention is bf16; the score launch before it then
+  // carries the query prep too
+  const bool combined = P.csa && a->dtype == V4A_BF16 && P.s_rest > 0 && P.ix.chunk_rows >= P.ix.rows;
+  V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s, !combined));
   // batch-invariant plans put the CSA slots first, so that the rest's split count
   // (from pos_max) only appends empty slots at the end of the merge order
   const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;
@@ -581,8 +597,11 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     // selection and the selection-independent attention share one launch when the
     // rows fit one score pass and the attention is bf16
     // (rows of 512 join it too, but never in the one-launch form)
-    const bool combined = a->dtype == V4A_BF16 && P.s_rest > 0 && IL.P.chunk_rows >= IL.P.rows;
     if (combined) {
+      if (needs_qprep(a)) {
+        IL.sp.prep = qprep_params(a, p, ws, P.off_q);
+        IL.sp.prep_x = qprep_blocks(IL.sp.prep);
+      }
       // in the one-launch form (the whole grid resident at once, at most one
       // workgroup per CU) the picks' attention and the merge join the launch; the
       // rest of each row, done early, pre-merges in-kernel meanwhile

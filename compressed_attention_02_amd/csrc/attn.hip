@@ -24,6 +24,7 @@
 // Softmax runs in base 2: logits are pre-multiplied by scale*log2(e); partial m is
 // kept in that unit and converted back to natural log for lse.
 #include "attn_impl.hpp"
+#include "qprep_impl.hpp"
 
 namespace v4a {
 
@@ -156,66 +157,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
 }
 
 // ------------------------------------------------------------------ query prep
-// [QbitAI] 混合注意力机制, the Q/KV normalization and partial RoPE paragraphs: each
-// head's query is RMS-normalised with the gain, then its last R channels rotated at
-// the row's position, in fp32 from the bf16 input and rounded to bf16 once.  A
-// thread holds 8 consecutive channels of one head (pairs stay inside it); the D/8
-// threads of a head are neighbouring lanes and add their squares by butterfly.
-// Done once per row here rather than in every attention workgroup of the row.
-template <int D>
-__global__ __launch_bounds__(256) void qprep_kernel(AttnP p, uint16_t* qout) {
-  constexpr int GS = D / 8;   // threads per head
-  const int row = blockIdx.x;
-  const int b = row / p.tq, i = row - b * p.tq;
-  const int g = blockIdx.y * 256 + threadIdx.x;   // 8-channel group of the row
-  const bool ok = g < p.heads * GS;
-  const int part = g % GS;
-  float x[8];
-  if (ok) {
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs + g * 8;
-    unpack8(*reinterpret_cast<const uint4*>(src), x);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-  }
-  if (p.q_norm) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-    for (int m = 1; m < GS; m <<= 1) ss += __shfl_xor(ss, m);
-    const float rq = rsqrtf(ss / (float)D + p.norm_eps);
-    if (ok) {
-      const float4 g0 = *reinterpret_cast<const float4*>(p.q_norm + part * 8);
-      const float4 g1 = *reinterpret_cast<const float4*>(p.q_norm + part * 8 + 4);
-      const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * rq * gs[e];
-    }
-  }
-  if (!ok) return;
-  if (p.rope) {
-    const int64_t pos = p.pos0[b] + i;
-    const int lo = D - p.rope;
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int ch = part * 8 + 2 * k2;
-      if (ch < lo) continue;
-      float cs, sn;
-      rope_cs((double)pos, (ch - lo) / 2, p.rope, p.rope_lb, cs, sn);
-      rot2(x[2 * k2], x[2 * k2 + 1], cs, sn, false);
-    }
-  }
-  *reinterpret_cast<uint4*>(qout + (int64_t)row * p.heads * D + g * 8) = pack8(x);
-}
+// once per row, when no score launch of the same step carries it (qprep_impl.hpp)
+__global__ __launch_bounds__(256) void qprep_kernel(QPrepP p) { qprep_block(p, blockIdx.x, blockIdx.y); }
 
-hipError_t launch_qprep(const AttnP& p, int nrows, uint16_t* qout, hipStream_t s, int tid) {
-  const int groups = p.heads * (p.dim / 8);
-  const dim3 grid((unsigned)nrows, (unsigned)((groups + 255) / 256));
-  if (p.dim == 64) V4A_LAUNCH(tid, qprep_kernel<64>, grid, dim3(256), 0, s, p, qout);
-  else if (p.dim == 128) V4A_LAUNCH(tid, qprep_kernel<128>, grid, dim3(256), 0, s, p, qout);
-  else if (p.dim == 512) V4A_LAUNCH(tid, qprep_kernel<512>, grid, dim3(256), 0, s, p, qout);
-  else return hipErrorInvalidValue;
+hipError_t launch_qprep(const QPrepP& p, int nrows, hipStream_t s, int tid) {
+  if (p.dim != 64 && p.dim != 128 && p.dim != 512) return hipErrorInvalidValue;
+  V4A_LAUNCH(tid, qprep_kernel, dim3((unsigned)nrows, (unsigned)qprep_blocks(p)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

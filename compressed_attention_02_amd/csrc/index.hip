@@ -26,6 +26,7 @@
 //           search over all of its scores.  Rows with n_vis < k are padded with -1.
 // Keys are the order-preserving uint32 image of the fp32 scores, so "larger key" is
 // "larger score"; the result does not depend on launch shape or timing.
+#include "qprep_impl.hpp"
 #include "select_impl.hpp"
 
 namespace v4a {
@@ -59,6 +60,10 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   __shared__ __align__(16) unsigned char sQ[MT * 16 * ROWB];
   if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
+  if ((int)blockIdx.x >= p.wgs_per_row) {   // the attention queries of row y
+    qprep_block(p.prep, p.row0 + blockIdx.y, blockIdx.x - p.wgs_per_row);
+    return;
+  }
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
@@ -211,7 +216,7 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
   const int mt = p.heads / 16, ks = p.dim / 32;
   ScoreP q = p;
   q.nrows = nrows;
-  const dim3 pgrid((unsigned)p.wgs_per_row, (unsigned)nrows);
+  const dim3 pgrid((unsigned)(p.wgs_per_row + p.prep_x), (unsigned)nrows);
   // a second tile buffer only when workgroups walk several tiles
   const bool two = (int64_t)p.wgs_per_row < ntiles;
 #define V4A_SCORE_CASE(M, K)                                                                             \

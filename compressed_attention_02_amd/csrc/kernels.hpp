@@ -34,6 +34,21 @@ constexpr int kPoolCap = 4096;    // candidate pool of the per-row selection (LD
 constexpr int kMaxTopk = 2048;
 constexpr int kSelThreads = 512;
 
+// Query prep (bf16): [QbitAI] 混合注意力机制, Q/KV normalization and partial RoPE.
+// Row r = b * tq + i of q is RMS-normalised with gain (if any) and its last `rope`
+// channels rotated at pos0[b] + i; out [rows][heads][dim] bf16.
+struct QPrepP {
+  const void* q; int64_t q_bs, q_rs;
+  const float* gain; float eps;
+  int rope; double rope_lb;
+  int heads, dim, tq;
+  const int64_t* pos0;
+  uint16_t* out;
+};
+hipError_t launch_qprep(const QPrepP& p, int nrows, hipStream_t s, int tid);
+// 256-thread blocks of the query prep of one row
+inline int qprep_blocks(const QPrepP& p) { return (p.heads * (p.dim / 8) + 255) / 256; }
+
 struct ScoreP {
   const void* qi; const float* wi; const void* ki;
   const int64_t* pos0;
@@ -46,6 +61,9 @@ struct ScoreP {
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
   int nrows;          // rows of the launch (set by launch_score)
   int* zero; int n_zero;  // words workgroup (0, 0) clears before anything else (null: none)
+  // bf16 kernel: workgroups x >= wgs_per_row of row y prepare that row's attention
+  // queries instead (prep_x of them; 0: none)
+  QPrepP prep; int prep_x;
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
@@ -106,9 +124,7 @@ struct AttnP {
 };
 constexpr int kRowWords = 4;
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
-// bf16 queries normalised (q_norm) and rotated (rope) once per row into qout
-// [rows][heads][dim] (bf16, rounded once), which the attention then reads as is
-hipError_t launch_qprep(const AttnP& p, int nrows, uint16_t* qout, hipStream_t s, int tid);
+
 hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
 
 // selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
