@@ -38,8 +38,9 @@ namespace v4a {
 // same 8 dims; C (16 heads x 16 blocks): lane holds block col, heads 4*grp + e.
 // The dims a lane group carries only have to agree between A and B.
 //
-// A workgroup (4 waves) walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
-// its row.  A tile of 256 indexer keys goes from HBM straight into LDS (16 bytes per
+// A workgroup (4 waves) walks the tiles x, x + wgs_per_row, ... of its row (x its
+// index among the row's score workgroups; with the query prep hosted, the first
+// prep_x workgroups of each row prepare the attention queries instead).  A tile of 256 indexer keys goes from HBM straight into LDS (16 bytes per
 // lane per load; lane l's piece lands at base + 16 l), unpadded, with the 16-byte
 // pieces of row r permuted by XOR with swz_ki(r) so that both the loads and the
 // B-fragment reads (16 rows, one piece column) are free of bank conflicts.  QI and
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   __shared__ __align__(16) unsigned char sQ[MT * 16 * ROWB];
   if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
-  if ((int)blockIdx.x >= p.wgs_per_row) {   // the attention queries of row y
-    qprep_block(p.prep, p.row0 + blockIdx.y, blockIdx.x - p.wgs_per_row);
+  if ((int)blockIdx.x < p.prep_x) {   // first (dispatched early): the attention queries of row y
+    qprep_block(p.prep, p.row0 + blockIdx.y, blockIdx.x);
     return;
   }
   const int lr = blockIdx.y;
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
   const int64_t nvis = uniform_i64((pos + 1) / p.ratio);
   const int64_t ntile_row = (nvis + kTile - 1) / kTile;
-  int64_t tile = blockIdx.x;
+  int64_t tile = (int)blockIdx.x - p.prep_x;
+  const int64_t stride = p.wgs_per_row;   // score workgroups of the row
   if (tile >= ntile_row) return;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     }
   }
   issue(tile, sK[0]);
-  if (NB == 2 && tile + gridDim.x < ntile_row) issue(tile + gridDim.x, sK[NB - 1]);
+  if (NB == 2 && tile + stride < ntile_row) issue(tile + stride, sK[NB - 1]);
 
   float w[MT][4];
   {
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
 
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
   const int kx = swz_ki<DI>(col);          // rows 16u + col of a wave share col's XOR
-  for (int c = 0; tile < ntile_row; tile += gridDim.x, ++c) {
+  for (int c = 0; tile < ntile_row; tile += stride, ++c) {
     const unsigned char* buf = sK[NB == 2 ? (c & 1) : 0];
-    const bool next = NB == 2 && tile + gridDim.x < ntile_row;
+    const bool next = NB == 2 && tile + stride < ntile_row;
     if (next) __builtin_amdgcn_s_waitcnt(0x0F70 | IPW);  // vmcnt(IPW): the next tile may stay in flight
     else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
     __syncthreads();
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
              p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
              p.rep_info + (int64_t)lr * p.info_rs + tile * 4 + wave);
     __syncthreads();       // the buffer is reloaded next
-    if (NB == 2 && tile + 2 * (int64_t)gridDim.x < ntile_row)
-      issue(tile + 2 * (int64_t)gridDim.x, sK[NB == 2 ? (c & 1) : 0]);
+    if (NB == 2 && tile + 2 * stride < ntile_row)
+      issue(tile + 2 * stride, sK[NB == 2 ? (c & 1) : 0]);
   }
 }
 

@@ -86,3 +86,22 @@ def test_query_and_output_rope_prefill():
     V.prefill_chunk(r.t["q"], r.t["pos"], r.step.o, **kw)
     torch.cuda.synchronize()
     r.check_attn(rows=sample_rows(cfg), q_norm=gq, norm_eps=EPS, rope_dims=R, rope_base=BASE, rope_out=True)
+
+
+def test_query_prep_in_score_launch_with_walking_workgroups():
+    # the decode step hosts the query prep in its score launch; with many rows each
+    # score workgroup walks several indexer tiles (20 rows x 128 tiles here), which
+    # the prep workgroups must not disturb
+    cfg = C.C2.small(name="rq2w", batch=20, pos=131077, needles=8)
+    r = Run(cfg).run()
+    gq = _gain(cfg.dim, 9)
+    kw = r.step.attn_kwargs()
+    for k in ("idx", "csa_ratio", "topk", "pos_max"):
+        kw.pop(k)
+    kw.update(rope_dims=R, rope_base=BASE, rope_out=True, q_norm=torch.from_numpy(gq).cuda(), norm_eps=EPS)
+    print("[case] rope decode_step 20 rows", flush=True)
+    V.decode_step(r.t["qi"], r.t["wi"], r.t["ki"], r.t["q"], r.t["pos"], r.step.o, r.step.idx, ratio=cfg.m,
+                  topk=cfg.topk, pos_max=r.step.pos_max, **kw)
+    torch.cuda.synchronize()
+    r.check_topk()
+    r.check_attn(q_norm=gq, norm_eps=EPS, rope_dims=R, rope_base=BASE, rope_out=True)
