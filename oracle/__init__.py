@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
     "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible", "rms_norm",
-    "rope", "compress_entries",
+    "rope", "compress_entries", "fp8_e4m3_decode", "fp8_rows",
 ]
 
 
@@ -152,6 +152,30 @@ def compress_entries(x_raw, logits, raw_start, t0, n, r, *, gain=None, eps=1e-6,
     if rope_dims:
         out = rope(out, (ids + 1) * r - 1, rope_dims, rope_base)
     return ids, out
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of FP8 E4M3 codes (one sign bit, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent 0 is subnormal, m * 2^-9; the all-ones exponent and
+    mantissa is NaN; no infinities), exactly, in fp64.
+
+    [wiki] the quantization and deployment section: the checkpoint keeps attention
+    in FP8, and FP8 KV caches serve long contexts.  The pages name the format only
+    as FP8; E4M3 is a reading, and so is the cache layout: a row holds codes plus
+    one fp32 scale, value = scale * decode(code).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def fp8_rows(codes, scales) -> np.ndarray:
+    """Rows of an FP8 cache: scale[j] * decode(codes[j])."""
+    return fp8_e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
 def index_scores(qi: np.ndarray, wi: np.ndarray, ki: np.ndarray) -> np.ndarray:

@@ -632,3 +632,38 @@ def test_shared_entries_when_values_are_omitted():
     keys = np.concatenate([kc[[1, 4]], kh[:2], raw[35:40]])
     ref = O.attend(q, keys, keys, 1 / math.sqrt(d))
     assert np.allclose(a[0], ref[0], rtol=0, atol=1e-12)
+
+
+def test_fp8_e4m3_decode_closed_forms_and_library():
+    # a few codes by hand: 1.0, the smallest subnormal and normal, the largest
+    # finite value, a negative one, zero and the NaN code
+    d = O.fp8_e4m3_decode([0x38, 0x01, 0x08, 0x7E, 0xB8, 0x00, 0x80, 0x7F, 0xFF, 0x3C, 0x07])
+    assert list(d[:7]) == [1.0, 2.0 ** -9, 2.0 ** -6, 448.0, -1.0, 0.0, -0.0]
+    assert np.isnan(d[7]) and np.isnan(d[8])
+    assert d[9] == 1.5 and d[10] == 7 * 2.0 ** -9
+    # every code against torch's float8_e4m3fn (the OCP E4M3 format)
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = O.fp8_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(lib), np.isnan(mine))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(lib[ok], mine[ok])
+    # positive finite codes are strictly increasing in value; sign is the top bit
+    pos = mine[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(mine[0x80:0xFF], -mine[:0x7F])
+
+
+def test_fp8_rows_scale_and_scores():
+    # rows are scale * decode(code); the indexer score of a scaled row is the scale
+    # times the score of its codes' values (the weights and the ReLU are positively
+    # homogeneous)
+    rng = np.random.default_rng(46)
+    codes = rng.integers(0, 0x7F, size=(5, 8)).astype(np.uint8) | (rng.integers(0, 2, size=(5, 8)) << 7).astype(np.uint8)
+    scales = rng.uniform(0.01, 2.0, 5)
+    rows = O.fp8_rows(codes, scales)
+    np.testing.assert_array_equal(rows, O.fp8_e4m3_decode(codes) * scales[:, None])
+    qi, wi = rng.standard_normal((3, 8)), rng.uniform(0, 1, 3)
+    s = O.index_scores(qi, wi, rows)
+    s0 = O.index_scores(qi, wi, O.fp8_e4m3_decode(codes))
+    np.testing.assert_allclose(s, s0 * scales, rtol=1e-14, atol=0)
