@@ -104,7 +104,7 @@ def step_bytes(cfg) -> dict:
     kv = 1 if cfg.shared_kv else 2     # shared entries are read once as key and value
     out = {}
     if cfg.branches & 1:
-        out["ki"] = B * n_vis * cfg.idx_dim * es
+        out["ki"] = B * n_vis * (cfg.idx_dim + 4 if cfg.ki_fp8 else cfg.idx_dim * es)   # FP8: codes + a scale per row
         out["qi_wi"] = B * cfg.idx_heads * (cfg.idx_dim * es + 4)
         out["idx"] = B * cfg.topk * 4 * 2
         out["csa_kv"] = B * min(cfg.topk, n_vis) * kv * d * es
@@ -149,7 +149,10 @@ def cpu_baseline(cfg, g, budget_s: float) -> dict:
     cores = len(os.sched_getaffinity(0))
     qi = O.as_f64(g["qi"], cfg.dtype) if "qi" in g else None
     wi = g["wi"].astype(np.float64) if "wi" in g else None
-    ki = O.as_f64(g["ki"], cfg.dtype) if "ki" in g else None
+    if "ki" in g:
+        ki = O.fp8_rows(g["ki"], g["ki_scale"]) if cfg.ki_fp8 else O.as_f64(g["ki"], cfg.dtype)
+    else:
+        ki = None
     q = O.as_f64(g["q"], cfg.dtype)
     caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
     for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):
@@ -336,7 +339,7 @@ def main():
 
     n_vis = (cfg.pos + 1) // cfg.m
     if dom == "index_score":
-        dom_bytes = cfg.batch * n_vis * cfg.idx_dim * (2 if cfg.dtype == "bf16" else 4)
+        dom_bytes = by["ki"]
         dom_name = "score_bf16_kernel (indexer keys streamed once)"
     else:
         dom_bytes = by.get("hca_kv", 0) + by.get("swa_kv", 0) + by.get("csa_kv", 0)
@@ -365,7 +368,8 @@ def main():
                    "step_form": "one_launch" if args.one_launch else "two_launch",
                    **({"shared_kv": True} if cfg.shared_kv else {}),
                    **({"rope_dims": cfg.rope_dims} if cfg.rope_dims else {}),
-                   **({"q_norm": True} if cfg.q_norm else {})},
+                   **({"q_norm": True} if cfg.q_norm else {}),
+                   **({"indexer_keys": "fp8_e4m3 codes + fp32 row scale"} if cfg.ki_fp8 else {})},
         "hbm_gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,

@@ -28,13 +28,13 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 CSA, HCA, SWA = 1, 2, 4
 BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ROPE_OUTPUT = 2       # v4a_attn_args.flags
 SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
-ABI_VERSION = 4
+ABI_VERSION = 5
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6, "qprep": 7}
 
@@ -62,7 +62,8 @@ class IndexArgs(ctypes.Structure):
                 ("tq", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
                 ("ratio", ctypes.c_int32), ("topk", ctypes.c_int32), ("pos0", ctypes.c_void_p),
                 ("pos_max", ctypes.c_int64), ("qi", Tensor), ("wi", Tensor), ("ki", Tensor),
-                ("idx", Tensor), ("sel_scores", Tensor)]
+                ("idx", Tensor), ("sel_scores", Tensor), ("ki_dtype", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("ki_scale", Tensor)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -194,21 +195,26 @@ def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, 
     _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
 
 
-def index_args(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max, sel_scores=None) -> IndexArgs:
+def index_args(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max, sel_scores=None, ki_scale=None) -> IndexArgs:
+    """ki as uint8 holds FP8 E4M3 codes, with ki_scale fp32 [B, N_cap] (one scale per row)."""
+    import torch
     B, Tq, HI, dI = qi.shape
+    fp8 = ki is not None and ki.dtype == torch.uint8
     return IndexArgs(ABI_VERSION, _dtype_code(qi), B, Tq, HI, dI, ratio, topk, _ptr(pos0), pos_max,
-                     _tensor(qi), _tensor(wi), _tensor(ki), _tensor(idx), _tensor(sel_scores))
+                     _tensor(qi), _tensor(wi), _tensor(ki), _tensor(idx), _tensor(sel_scores),
+                     FP8_E4M3 if fp8 else 0, 0, _tensor(ki_scale))
 
 
-def index_topk_workspace(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max) -> int:
-    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max)
+def index_topk_workspace(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max, ki_scale=None) -> int:
+    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max, ki_scale=ki_scale)
     return int(lib().v4attn_index_topk_workspace(ctypes.byref(a)))
 
 
 def index_topk(qi, wi, ki, pos0, idx, *, ratio: int, topk: int, pos_max: int, sel_scores=None,
-               workspace=None, stream=None):
+               workspace=None, stream=None, ki_scale=None):
     """v4attn_index_topk: indexer scores and per-query top-k ids into idx [B, Tq, k]."""
-    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max, sel_scores=sel_scores)
+    a = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max, sel_scores=sel_scores,
+                   ki_scale=ki_scale)
     if workspace is None:
         workspace = _alloc_ws(int(lib().v4attn_index_topk_workspace(ctypes.byref(a))), qi.device)
     p, n = _ws_ptr(workspace)
@@ -258,9 +264,11 @@ def prefill_chunk(q, pos0, o, *, workspace=None, stream=None, **kw):
 
 
 def _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw):
+    attn_kw = dict(attn_kw)
+    ki_scale = attn_kw.pop("ki_scale", None)
     ia = None
     if qi is not None:
-        ia = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max)
+        ia = index_args(qi, wi, ki, pos0, idx, ratio=ratio, topk=topk, pos_max=pos_max, ki_scale=ki_scale)
     aa = attn_args(q, pos0, o, idx=idx, csa_ratio=ratio, topk=topk, pos_max=pos_max, **attn_kw)
     return (ctypes.byref(ia) if ia is not None else None), ctypes.byref(aa)
 

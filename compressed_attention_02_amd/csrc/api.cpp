@@ -39,7 +39,7 @@ v4a_status ok() {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-size_t esize(int dtype) { return dtype == V4A_BF16 ? 2 : 4; }
+size_t esize(int dtype) { return dtype == V4A_FP8_E4M3 ? 1 : dtype == V4A_BF16 ? 2 : 4; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
@@ -265,10 +265,18 @@ v4a_status validate_index(const v4a_index_args* a) {
     if (a->dim % 4 != 0) return fail(V4A_ENOTSUP, "fp32 indexer: dim must be a multiple of 4");
     if ((int64_t)a->heads * a->dim + a->heads > 16384) return fail(V4A_ENOTSUP, "fp32 indexer: heads*dim too large");
   }
+  const int kdt = a->ki_dtype == 0 ? a->dtype : a->ki_dtype;
+  if (kdt != a->dtype && !(kdt == V4A_FP8_E4M3 && a->dtype == V4A_BF16))
+    return fail(V4A_EINVAL, "ki_dtype %d: 0, dtype, or FP8_E4M3 with a bf16 indexer", a->ki_dtype);
   if (a->batch == 0) return V4A_OK;
   if (!a->pos0) return fail(V4A_EINVAL, "pos0 is NULL");
   V4A_TRY(check_tensor("qi", a->qi, a->dtype, (int64_t)a->heads * a->dim, a->batch));
-  V4A_TRY(check_tensor("ki", a->ki, a->dtype, a->dim, a->batch));
+  V4A_TRY(check_tensor("ki", a->ki, kdt, a->dim, a->batch));
+  if (kdt == V4A_FP8_E4M3) {
+    if (!a->ki_scale.ptr || !aligned(a->ki_scale.ptr, 4)) return fail(V4A_EINVAL, "ki_scale: NULL or not 4-byte aligned");
+    if (a->ki_scale.row_stride != 1) return fail(V4A_EINVAL, "ki_scale: row_stride must be 1");
+    if (a->batch > 1 && a->ki_scale.batch_stride <= 0) return fail(V4A_EINVAL, "ki_scale: batch_stride must be positive");
+  }
   if (!a->wi.ptr || !aligned(a->wi.ptr, 4)) return fail(V4A_EINVAL, "wi: NULL or not 4-byte aligned");
   if (a->wi.row_stride < a->heads) return fail(V4A_EINVAL, "wi: row_stride < heads");
   if (a->batch > 1 && a->wi.batch_stride <= 0) return fail(V4A_EINVAL, "wi: batch_stride must be positive");
@@ -433,6 +441,10 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   char* base = (char*)ws;
   ScoreP& sp = L.sp;
   sp.qi = a->qi.ptr; sp.wi = (const float*)a->wi.ptr; sp.ki = a->ki.ptr; sp.pos0 = a->pos0;
+  if (a->ki_dtype == V4A_FP8_E4M3) {
+    sp.ki_scale = (const float*)a->ki_scale.ptr;
+    sp.ks_bs = a->ki_scale.batch_stride;
+  }
   sp.scores = (float*)base;
   sp.rep_key = (uint32_t*)(base + P.off_keys);
   sp.rep_info = (uint2*)(base + P.off_info);

@@ -48,16 +48,39 @@ namespace v4a {
 // current one is scored.  Each wave scores 64 keys: ReLU, w-weighted head sum (row
 // swaps across the 4 lane groups), then its top-4 report.
 template <int DI> __device__ __forceinline__ int swz_ki(int r) { return DI == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// FP8 key rows (DI bytes, DI/16 pieces): rows r that share a 256-byte bank offset
+// (r mod 256/DI) get distinct piece XORs, so the 8-byte fragment reads of 16 rows
+// at one logical piece are free of bank conflicts
+template <int DI> __device__ __forceinline__ int swz_k8(int r) { return (r / (256 / DI)) % (DI / 16); }
 
-template <int MT, int KS, int NB>
+// 8 FP8 E4M3 codes (bytes of v, low first) -> 8 bf16, exactly (every E4M3 value,
+// subnormals and NaN included, is a bf16 value): gfx950's packed conversion with a
+// unit scale, two codes per instruction
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1),
+                                                 __builtin_bit_cast(uint32_t, w2), __builtin_bit_cast(uint32_t, w3)));
+}
+
+// FP8: the key rows are FP8 E4M3 codes with one fp32 scale per row; they stay codes
+// in LDS (half the bytes), each fragment is decoded to bf16 exactly, and the row's
+// scale multiplies its 16 dot products before the ReLU.
+template <int MT, int KS, int NB, bool FP8>
 __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   constexpr int DI = KS * 32;
-  constexpr int ROWB = DI * 2;               // LDS bytes per key row
-  constexpr int CPR = DI * 2 / 16;           // 16-byte pieces per key row
-  constexpr int RPI = 64 / CPR;              // key rows per wave load
-  constexpr int IPW = kTile / RPI / 4;       // loads per wave per tile
+  constexpr int ROWB = DI * 2;               // LDS bytes per query row
+  constexpr int CPR = DI * 2 / 16;           // 16-byte pieces per query row
+  constexpr int RPI = 64 / CPR;              // query rows per wave load
+  constexpr int KROWB = FP8 ? DI : DI * 2;   // LDS bytes per key row
+  constexpr int KCPR = KROWB / 16;           // 16-byte pieces per key row
+  constexpr int KRPI = 64 / KCPR;            // key rows per wave load
+  constexpr int IPW = kTile / KRPI / 4;      // loads per wave per tile
   constexpr int QN = MT * 16 / RPI;         // wave loads of the query rows (heads)
-  __shared__ __align__(16) unsigned char sK[NB][kTile * ROWB];
+  __shared__ __align__(16) unsigned char sK[NB][kTile * KROWB];
   __shared__ __align__(16) unsigned char sQ[MT * 16 * ROWB];
   if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
     for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
@@ -76,16 +99,19 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   if (tile >= ntile_row) return;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint16_t* ki = reinterpret_cast<const uint16_t*>(p.ki) + (int64_t)b * p.ki_bs;
+  // key rows in bytes (row strides are in elements: 2 bytes for bf16, 1 for FP8)
+  const unsigned char* ki = reinterpret_cast<const unsigned char*>(p.ki) + (int64_t)b * p.ki_bs * (FP8 ? 1 : 2);
+  const int64_t ki_rb = p.ki_rs * (FP8 ? 1 : 2);
 
   // rows past n_vis re-read the last visible row; their scores are dropped
   auto issue = [&](int64_t t, unsigned char* buf) {
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      const int r0 = (wave * IPW + u) * RPI;
-      const int r = r0 + lane / CPR;
+      const int r0 = (wave * IPW + u) * KRPI;
+      const int r = r0 + lane / KCPR;
       const int64_t j = min(t * kTile + r, nvis - 1);
-      lds_load16(ki + j * p.ki_rs + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(buf + r0 * ROWB));
+      const int x = FP8 ? swz_k8<DI>(r) : swz_ki<DI>(r);
+      lds_load16(ki + j * ki_rb + ((lane % KCPR) ^ x) * 16, lds_addr(buf + r0 * KROWB));
     }
   };
   // the query rows go to LDS once per workgroup (laid out like the key rows), ahead
@@ -115,6 +141,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
 
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
   const int kx = swz_ki<DI>(col);          // rows 16u + col of a wave share col's XOR
+  const int kx8 = swz_k8<DI>(col);         // (the same holds for the FP8 layout)
   for (int c = 0; tile < ntile_row; tile += stride, ++c) {
     const unsigned char* buf = sK[NB == 2 ? (c & 1) : 0];
     const bool next = NB == 2 && tile + stride < ntile_row;
@@ -131,14 +158,24 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     }
     const int64_t tile0 = tile * kTile;
     float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
+    float kscale = 1.f;     // FP8: the scale of that key's row (rows past n_vis: the last row's)
+    if constexpr (FP8)
+      kscale = p.ki_scale[(int64_t)b * p.ks_bs + min(tile0 + wave * 64 + lane, nvis - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = wave * 64 + u * 16 + col;     // key row of this lane's column
       float part = 0.f;
       bf16x8_t Bv[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        Bv[s] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s * 4 + grp) ^ kx) * 16));
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (FP8)   // elements s*32 + grp*8: piece 2s + grp/2, half grp%2
+          Bv[s] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(buf + t * KROWB + (((2 * s + (grp >> 1)) ^ kx8) * 16) +
+                                                                (grp & 1) * 8));
+        else
+          Bv[s] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s * 4 + grp) ^ kx) * 16));
+      }
+      // FP8: the scale of this lane's key column (key u*16 + col of the wave)
+      const float cs = FP8 ? __shfl(kscale, u * 16 + col) : 1.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -146,7 +183,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
         for (int s = 0; s < KS; ++s)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[s], acc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(acc[e], 0.f), part);
+        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(FP8 ? acc[e] * cs : acc[e], 0.f), part);
       }
       part = col_sum4(part);
       if (grp == u) mine = part;
@@ -221,10 +258,16 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
   const dim3 pgrid((unsigned)(p.wgs_per_row + p.prep_x), (unsigned)nrows);
   // a second tile buffer only when workgroups walk several tiles
   const bool two = (int64_t)p.wgs_per_row < ntiles;
+  const bool f8 = p.ki_scale != nullptr;
 #define V4A_SCORE_CASE(M, K)                                                                             \
   if (mt == M && ks == K) {                                                                              \
-    if (two) V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 2>), pgrid, dim3(256), 0, s, q);                  \
-    else V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 1>), pgrid, dim3(256), 0, s, q);                      \
+    if (f8) {                                                                                            \
+      if (two) V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 2, true>), pgrid, dim3(256), 0, s, q);          \
+      else V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 1, true>), pgrid, dim3(256), 0, s, q);              \
+    } else {                                                                                             \
+      if (two) V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 2, false>), pgrid, dim3(256), 0, s, q);         \
+      else V4A_LAUNCH(tid, (score_bf16_kernel<M, K, 1, false>), pgrid, dim3(256), 0, s, q);             \
+    }                                                                                                    \
     return hipGetLastError();                                                                            \
   }
   V4A_SCORE_CASE(1, 1) V4A_SCORE_CASE(1, 2)

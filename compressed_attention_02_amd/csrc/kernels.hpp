@@ -51,6 +51,7 @@ inline int qprep_blocks(const QPrepP& p) { return (p.heads * (p.dim / 8) + 255) 
 
 struct ScoreP {
   const void* qi; const float* wi; const void* ki;
+  const float* ki_scale; int64_t ks_bs;   // FP8 keys: one scale per row (null: bf16 keys)
   const int64_t* pos0;
   float* scores;      // [rows][sc_rs]
   uint32_t* rep_key;  // [rows][key_rs]: per wave, the keys of its kWaveTop best, in id order

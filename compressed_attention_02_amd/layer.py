@@ -97,7 +97,8 @@ class LayerStep:
         if not s.branches & CSA:
             return
         self.ws_index = index_topk(t["qi"], t["wi"], t["ki"], t["pos"], self.idx, ratio=s.m, topk=s.topk,
-                                   pos_max=self.pos_max, workspace=self.ws_index, stream=stream)
+                                   pos_max=self.pos_max, workspace=self.ws_index, stream=stream,
+                                   ki_scale=t.get("ki_scale"))
 
     def attn_kwargs(self):
         s, t = self.s, self.t
@@ -122,6 +123,8 @@ class LayerStep:
             for k in ("idx", "csa_ratio", "topk", "pos_max"):
                 kw.pop(k)
             csa = bool(s.branches & CSA)
+            if t.get("ki_scale") is not None:
+                kw["ki_scale"] = t["ki_scale"]
             self._step_call = DecodeStepCall(t["qi"] if csa else None, t.get("wi"), t.get("ki"), t["q"], t["pos"],
                                              self.o, self.idx, ratio=s.m, topk=s.topk, pos_max=self.pos_max,
                                              workspace=getattr(self, "ws_step", None), **kw)

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 4u
+#define V4ATTN_ABI_VERSION 5u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -67,7 +67,9 @@ typedef enum v4a_status {
   V4A_EHIP = 4         /* a HIP runtime call failed at enqueue                  */
 } v4a_status;
 
-typedef enum v4a_dtype { V4A_F32 = 0, V4A_BF16 = 1 } v4a_dtype;
+/* V4A_FP8_E4M3: v4a_index_args.ki_dtype only (cache rows of FP8 codes with one
+ * fp32 scale per row) */
+typedef enum v4a_dtype { V4A_F32 = 0, V4A_BF16 = 1, V4A_FP8_E4M3 = 2 } v4a_dtype;
 
 /* branch_mask bits */
 #define V4A_CSA 1u
@@ -157,7 +159,16 @@ v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
  *   qi           [batch][tq][H_I][d_I] (row = query token, heads contiguous)
  *   wi           fp32 [batch][tq][H_I] (row = query token); weights should be
  *                >= 0 (the ReLU form assumes it; not checked)
- *   ki           [batch][N_cap][d_I] (row = block id)
+ *   ki           [batch][N_cap][d_I] (row = block id), of type ki_dtype
+ *   ki_dtype     0 (the same as dtype) or, with dtype BF16, V4A_FP8_E4M3:
+ *                ki holds FP8 E4M3 codes (bytes: sign, 4 exponent bits with
+ *                bias 7, 3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN)
+ *                and row j of block b stands for ki_scale[b][j] * decode(code),
+ *                so the score is s_j = sum_h wi[h] * max(0, ki_scale[b][j] *
+ *                (qi[h] . decode(ki[j]))).  [wiki] the quantization and
+ *                deployment section (attention kept in FP8, FP8 KV caches); the
+ *                E4M3 format and the per-row scale are readings.
+ *   ki_scale     fp32 [batch][N_cap], row_stride 1 (ki_dtype FP8 only)
  *   idx          int32 out [batch][tq][k] (row = query token), row_stride >= k
  *   sel_scores   fp32 out, same layout as idx, or ptr == NULL
  * Workspace: v4attn_index_topk_workspace(args) bytes.
@@ -176,6 +187,9 @@ typedef struct v4a_index_args {
   v4a_tensor qi, wi, ki;
   v4a_tensor idx;
   v4a_tensor sel_scores;
+  int32_t ki_dtype;     /* 0 (= dtype) or V4A_FP8_E4M3 */
+  int32_t reserved0;
+  v4a_tensor ki_scale;
 } v4a_index_args;
 
 size_t v4attn_index_topk_workspace(const v4a_index_args* args);

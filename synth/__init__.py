@@ -23,13 +23,16 @@ Recipe (the same for every configuration):
     span); the 1M-token history is never materialised, its compressed caches are
     drawn directly.  Caches hold at least one row even when no entry is visible;
   * shared K = V configurations draw no V tensor (each entry is its own value);
-    with a query RMSNorm its per-channel gain is U(0.5, 1.5) fp32.
+    with a query RMSNorm its per-channel gain is U(0.5, 1.5) fp32;
+  * FP8 indexer keys: each drawn row (needles planted as above) gets the scale
+    max|row| / 448 (1 for an all-zero row), stored in fp32, and its codes are
+    torch's round-to-nearest-even cast of row / scale to float8_e4m3fn.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .configs import C1, C2, C3, C4, C5, C6, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
+from .configs import C1, C2, C3, C4, C5, C6, C7, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
 
 # appending a stream leaves the earlier ones' draws unchanged
 _STREAMS = ("q", "qi", "wi", "ki", "kc", "vc", "kh", "vh", "k_raw", "v_raw",
@@ -55,6 +58,16 @@ def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
 
 def _load(stored: np.ndarray, dtype: str) -> np.ndarray:
     return (bf16_bits_to_f32(stored) if dtype == "bf16" else stored).astype(np.float64)
+
+
+def _fp8_rows(x64: np.ndarray):
+    """FP8 E4M3 codes (uint8) and fp32 per-row scales of the rows of x (last axis)."""
+    import torch
+    amax = np.abs(x64).max(axis=-1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    y = torch.from_numpy(x64 / scale.astype(np.float64)[..., None])
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -102,7 +115,10 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
                 u = (out["wi"][b, 0].astype(np.float64)[:, None] * _load(out["qi"][b, 0], cfg.dtype)).sum(axis=0)
             u /= np.linalg.norm(u)
             ki[b, needles[b]] += 3.0 * np.sqrt(dI) * u
-        out["ki"] = _store(ki, cfg.dtype)
+        if cfg.ki_fp8:
+            out["ki"], out["ki_scale"] = _fp8_rows(ki)
+        else:
+            out["ki"] = _store(ki, cfg.dtype)
         out["needles"] = needles
         kc = rngs["kc"].standard_normal((B, max(cfg.n_cap, 1), d))
         vc = None if cfg.shared_kv else rngs["vc"].standard_normal((B, max(cfg.n_cap, 1), d))

@@ -47,6 +47,7 @@ class LayerConfig:
     shared_kv: bool = False  # one tensor per branch: every entry is its own value
     rope_dims: int = 0    # partial RoPE on the last rope_dims channels (0: off)
     q_norm: bool = False  # RMSNorm of each head's query with a synthetic gain
+    ki_fp8: bool = False  # indexer keys stored as FP8 E4M3 codes with one fp32 scale per row
 
     # ---- derived shape helpers (pure bookkeeping, no method arithmetic) ----
     @property
@@ -132,4 +133,12 @@ C6 = LayerConfig(
     branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
     seed=20260006, timed="index_topk + decode", shared_kv=True, rope_dims=64, q_norm=True)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6)}
+# C3 with the indexer keys (the step's largest stream) kept in FP8 ([wiki]
+# quantization and deployment section: attention in FP8, FP8 caches).
+C7 = LayerConfig(
+    name="c7_fp8_indexer_decode_b1_1m", dtype="bf16", batch=1, pos=1048576, tq=1, heads=128,
+    dim=128, idx_heads=64, idx_dim=64, m=4, topk=1024, m_hca=128, window=128,
+    branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
+    seed=20260007, timed="index_topk + decode", ki_fp8=True)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7)}

@@ -145,7 +145,10 @@ class Run:
         p = int(self.g["pos"][b]) + i
         n = O.n_visible(p, cfg.m)
         qi = O.as_f64(self.g["qi"][b, i], cfg.dtype)
-        ki = O.as_f64(self.g["ki"][b, :n], cfg.dtype)
+        if cfg.ki_fp8:   # FP8 codes with one scale per row
+            ki = O.fp8_rows(self.g["ki"][b, :n], self.g["ki_scale"][b, :n])
+        else:
+            ki = O.as_f64(self.g["ki"][b, :n], cfg.dtype)
         return O.index_scores(qi, self.g["wi"][b, i].astype(np.float64), ki)
 
     def check_topk(self, rows=None):

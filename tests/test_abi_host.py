@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 13
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 4
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 5
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -274,3 +274,16 @@ def test_rope_argument_checks(field, value):
     assert rc == EINVAL and "rope" in msg
     assert _st(V.lib().v4attn_compress, good_compress(rope_dims=64, rope_base=1e4, rope_flags=4), None)[0] == EINVAL
     assert _st(V.lib().v4attn_compress, good_compress(rope_dims=128, rope_base=1e4, ratio=128), None)[0] == ENOTSUP
+
+
+def test_fp8_key_argument_checks():
+    L = V.lib()
+    f = L.v4attn_index_topk
+    # FP8 keys need a bf16 indexer and a scale tensor with unit row stride
+    r, msg = _st(f, good_index(ki_dtype=V.FP8_E4M3), None, 0, None)
+    assert r == EINVAL and "ki_scale" in msg
+    assert _st(f, good_index(ki_dtype=V.FP8_E4M3, dtype=V.F32), None, 0, None)[0] == EINVAL
+    assert _st(f, good_index(ki_dtype=7), None, 0, None)[0] == EINVAL
+    fp8 = dict(ki_dtype=V.FP8_E4M3, ki=_T(bs=64 * 32768, rs=64), ki_scale=_T(bs=32768, rs=1))
+    assert L.v4attn_index_topk_workspace(ctypes.byref(good_index(**fp8))) > 0
+    assert _st(f, good_index(**dict(fp8, ki_scale=_T(bs=32768, rs=2))), None, 0, None)[0] == EINVAL

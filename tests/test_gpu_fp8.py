@@ -1,0 +1,61 @@
+"""FP8 E4M3 indexer keys ([wiki] the quantization and deployment section: attention
+kept in FP8, FP8 caches) against the fp64 oracle, through the C ABI.
+
+Key rows are codes plus one fp32 scale; the oracle decodes every code exactly
+(oracle.fp8_e4m3_decode, pinned to torch's float8_e4m3fn) and scores the scaled
+rows; the GPU keeps the codes in LDS, decodes each fragment to bf16 and scales the
+dot products before the ReLU.  Top-k sets must match outside the tie band, in the
+stage-by-stage path, the decode step, prefill rows and launches whose workgroups
+walk several tiles; the codes cover every non-NaN value, subnormals and zero rows.
+"""
+import numpy as np
+import pytest
+
+from synth import configs as C
+import synth
+from tests.gpu_harness import Run, dev_to_np, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("batch,pos,fused", [(1, 70003, False), (1, 70003, True), (3, 40961, True),
+                                              (20, 131077, True)])
+def test_fp8_keys_decode(batch, pos, fused):
+    cfg = C.C7.small(name="f8d", batch=batch, pos=pos, needles=8, heads=64)
+    print(f"[case] fp8 decode B={batch} pos={pos} fused={fused}", flush=True)
+    r = Run(cfg).run(fused=fused).check_all()
+    idx = dev_to_np(r.step.idx)
+    for b in range(batch):
+        assert set(r.g["needles"][b].tolist()) <= set(idx[b, 0].tolist())
+
+
+def test_fp8_keys_prefill_rows():
+    cfg = C.C5.small(name="f85", pos=8192, tq=320, needles=8, ki_fp8=True)
+    print("[case] fp8 prefill", flush=True)
+    Run(cfg).run().check_all(rows=sample_rows(cfg))
+
+
+def test_fp8_every_code_subnormals_zero_rows_and_signs():
+    # rows built from all 254 non-NaN codes (in a seeded order), some all-zero rows,
+    # some scales negative (the definition scales before the ReLU) or zero
+    cfg = C.C7.small(name="f8c", pos=20483, needles=0, heads=64, topk=512)
+    g = synth.generate(cfg)
+    rng = np.random.default_rng(47)
+    n, d = g["ki"].shape[1], g["ki"].shape[2]
+    pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    g["ki"][0] = rng.choice(pool, size=(n, d))
+    g["ki"][0, ::97] = 0
+    sc = rng.uniform(0.001, 0.05, n).astype(np.float32)
+    sc[::31] *= -1
+    sc[::53] = 0
+    g["ki_scale"][0] = sc
+    print("[case] fp8 codes", flush=True)
+    Run(cfg, gen=g).run(fused=True).check_all()
+
+
+def test_full_c7_decode_step():
+    cfg = C.C7
+    print("[case] full c7", flush=True)
+    r = Run(cfg).run(fused=True).check_all()
+    idx = dev_to_np(r.step.idx)
+    assert set(r.g["needles"][0].tolist()) <= set(idx[0, 0].tolist())
