@@ -102,16 +102,17 @@ def step_bytes(cfg) -> dict:
     e_vis = (p + 1) // cfg.m_hca
     w = min(cfg.window, p + 1)
     kv = 1 if cfg.shared_kv else 2     # shared entries are read once as key and value
+    row = (d + 4) if cfg.kv_fp8 else d * es   # bytes of a cache row (FP8: codes + a 4-byte scale)
     out = {}
     if cfg.branches & 1:
         out["ki"] = B * n_vis * (cfg.idx_dim + 4 if cfg.ki_fp8 else cfg.idx_dim * es)   # FP8: codes + a scale per row
         out["qi_wi"] = B * cfg.idx_heads * (cfg.idx_dim * es + 4)
         out["idx"] = B * cfg.topk * 4 * 2
-        out["csa_kv"] = B * min(cfg.topk, n_vis) * kv * d * es
+        out["csa_kv"] = B * min(cfg.topk, n_vis) * kv * row
     if cfg.branches & 2:
-        out["hca_kv"] = B * e_vis * kv * d * es
+        out["hca_kv"] = B * e_vis * kv * row
     if cfg.branches & 4:
-        out["swa_kv"] = B * w * kv * d * es
+        out["swa_kv"] = B * w * kv * row
     if cfg.compress == "hca_newest":
         out["compress_rd"] = B * cfg.compress_tokens * (2 * d * es + 4)
         out["compress_wr"] = B * (cfg.compress_tokens // cfg.m_hca) * 2 * d * es
@@ -157,7 +158,7 @@ def cpu_baseline(cfg, g, budget_s: float) -> dict:
     caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
     for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):
         if nm in g:
-            caches[nm] = O.as_f64(g[nm], cfg.dtype)
+            caches[nm] = O.fp8_rows(g[nm], g[nm + "_scale"]) if cfg.kv_fp8 else O.as_f64(g[nm], cfg.dtype)
     arrays = (qi, wi, ki, q, caches)
     run_oracle_step(cfg, g, arrays)  # warm-up
     n, t0 = 0, time.perf_counter()
@@ -369,7 +370,8 @@ def main():
                    **({"shared_kv": True} if cfg.shared_kv else {}),
                    **({"rope_dims": cfg.rope_dims} if cfg.rope_dims else {}),
                    **({"q_norm": True} if cfg.q_norm else {}),
-                   **({"indexer_keys": "fp8_e4m3 codes + fp32 row scale"} if cfg.ki_fp8 else {})},
+                   **({"indexer_keys": "fp8_e4m3 codes + fp32 row scale"} if cfg.ki_fp8 else {}),
+                   **({"kv_caches": "fp8_e4m3 codes + fp32 row scale"} if cfg.kv_fp8 else {})},
         "hbm_gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,

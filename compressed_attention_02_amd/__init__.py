@@ -34,7 +34,7 @@ BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ROPE_OUTPUT = 2       # v4a_attn_args.flags
 SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
-ABI_VERSION = 5
+ABI_VERSION = 6
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6, "qprep": 7}
 
@@ -76,7 +76,9 @@ class AttnArgs(ctypes.Structure):
                 ("vc", Tensor), ("kh", Tensor), ("vh", Tensor), ("k_raw", Tensor), ("v_raw", Tensor),
                 ("raw_start", ctypes.c_void_p), ("sink", ctypes.c_void_p), ("o", Tensor), ("lse", Tensor),
                 ("q_norm", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32),
-                ("rope_base", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+                ("rope_base", ctypes.c_float), ("reserved1", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("reserved2", ctypes.c_int32), ("kc_scale", Tensor), ("vc_scale", Tensor), ("kh_scale", Tensor),
+                ("vh_scale", Tensor), ("kr_scale", Tensor), ("vr_scale", Tensor)]
 
 
 _lib = None
@@ -226,10 +228,15 @@ def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=N
               v_raw=None, raw_start=None, branch_mask=CSA | HCA | SWA, csa_ratio=4, hca_ratio=128,
               window=128, topk=1, pos_max=None, scale=0.0, sink=None, batch_invariant=False,
               q_norm=None, norm_eps=1e-6, rope_dims=0, rope_base=1e4, rope_out=False,
-              shared_kv=False) -> AttnArgs:
+              shared_kv=False, kc_scale=None, vc_scale=None, kh_scale=None, vh_scale=None, kr_scale=None,
+              vr_scale=None) -> AttnArgs:
+    """Caches given as uint8 hold FP8 E4M3 codes; each then comes with its fp32 [B, rows]
+    *_scale (one scale per row)."""
+    import torch
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
+    fp8 = any(t is not None and t.dtype == torch.uint8 for t in (kc, vc, kh, vh, k_raw, v_raw))
     return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
                     window, topk, scale,
                     (BATCH_INVARIANT if batch_invariant else 0) | (ROPE_OUTPUT if rope_out else 0) |
@@ -237,7 +244,8 @@ def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=N
                     _ptr(pos0), pos_max, _tensor(q), _tensor(idx), _tensor(kc),
                     _tensor(vc), _tensor(kh), _tensor(vh), _tensor(k_raw), _tensor(v_raw),
                     _ptr(raw_start), _ptr(sink), _tensor(o), _tensor(lse), _ptr(q_norm), norm_eps, rope_dims,
-                    rope_base, 0)
+                    rope_base, 0, FP8_E4M3 if fp8 else 0, 0, _tensor(kc_scale), _tensor(vc_scale),
+                    _tensor(kh_scale), _tensor(vh_scale), _tensor(kr_scale), _tensor(vr_scale))
 
 
 def _run_attn(fn, wsfn, q, pos0, o, workspace, stream, kw):

@@ -203,6 +203,14 @@ AttnPlan plan_attn(const v4a_attn_args* a) {
 }
 
 // ---------------------------------------------------------------- validation
+// A row-scale table of FP8 caches: fp32 [batch][rows], one word per row.
+v4a_status check_scale(const char* name, const v4a_tensor& t, int batch) {
+  if (!t.ptr || !aligned(t.ptr, 4)) return fail(V4A_EINVAL, "%s: NULL or not 4-byte aligned", name);
+  if (t.row_stride != 1) return fail(V4A_EINVAL, "%s: row_stride must be 1", name);
+  if (batch > 1 && t.batch_stride <= 0) return fail(V4A_EINVAL, "%s: batch_stride must be positive", name);
+  return V4A_OK;
+}
+
 v4a_status validate_compress(const v4a_compress_args* a) {
   if (!a) return fail(V4A_EINVAL, "args is NULL");
   if (a->abi_version != V4ATTN_ABI_VERSION) return fail(V4A_EINVAL, "abi_version %u != %u", a->abi_version, V4ATTN_ABI_VERSION);
@@ -302,6 +310,11 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (a->dim != 64 && a->dim != 128 && a->dim != 512) return fail(V4A_ENOTSUP, "dim must be 64, 128 or 512");
   if (a->dim == 512 && a->dtype == V4A_BF16 && !skv)
     return fail(V4A_ENOTSUP, "bf16 attention at dim 512 needs V4A_SHARED_KV");
+  const int kvt = a->kv_dtype == 0 ? a->dtype : a->kv_dtype;   // type of the caches
+  const bool f8 = kvt == V4A_FP8_E4M3;
+  if (kvt != a->dtype && !(f8 && a->dtype == V4A_BF16))
+    return fail(V4A_EINVAL, "kv_dtype %d: 0, dtype, or FP8_E4M3 with bf16 attention", a->kv_dtype);
+  if (f8 && (a->dim > 128 || skv)) return fail(V4A_ENOTSUP, "FP8 caches: dim <= 128 and separate K and V");
   if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
   if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
   if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
@@ -336,16 +349,19 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (a->branch_mask & V4A_CSA) {
     if (!a->idx.ptr || !aligned(a->idx.ptr, 4)) return fail(V4A_EINVAL, "idx: NULL or not 4-byte aligned");
     if (a->idx.row_stride < a->topk) return fail(V4A_EINVAL, "idx: row_stride < topk");
-    V4A_TRY(check_tensor("kc", a->kc, a->dtype, a->dim, bq));
-    if (!skv) V4A_TRY(check_tensor("vc", a->vc, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("kc", a->kc, kvt, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("vc", a->vc, kvt, a->dim, bq));
+    if (f8) { V4A_TRY(check_scale("kc_scale", a->kc_scale, bq)); V4A_TRY(check_scale("vc_scale", a->vc_scale, bq)); }
   }
   if (a->branch_mask & V4A_HCA) {
-    V4A_TRY(check_tensor("kh", a->kh, a->dtype, a->dim, bq));
-    if (!skv) V4A_TRY(check_tensor("vh", a->vh, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("kh", a->kh, kvt, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("vh", a->vh, kvt, a->dim, bq));
+    if (f8) { V4A_TRY(check_scale("kh_scale", a->kh_scale, bq)); V4A_TRY(check_scale("vh_scale", a->vh_scale, bq)); }
   }
   if ((a->branch_mask & V4A_SWA) && a->window > 0) {
-    V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, bq));
-    if (!skv) V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, bq));
+    V4A_TRY(check_tensor("k_raw", a->k_raw, kvt, a->dim, bq));
+    if (!skv) V4A_TRY(check_tensor("v_raw", a->v_raw, kvt, a->dim, bq));
+    if (f8) { V4A_TRY(check_scale("kr_scale", a->kr_scale, bq)); V4A_TRY(check_scale("vr_scale", a->vr_scale, bq)); }
     if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
   }
   if (a->sink && !aligned(a->sink, 4)) return fail(V4A_EINVAL, "sink: not 4-byte aligned");
@@ -386,6 +402,15 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
   p.kr = a->k_raw.ptr; p.kr_bs = a->k_raw.batch_stride; p.kr_rs = a->k_raw.row_stride;
   p.vr = a->v_raw.ptr; p.vr_bs = a->v_raw.batch_stride; p.vr_rs = a->v_raw.row_stride;
   p.skv = (a->flags & V4A_SHARED_KV) != 0;
+  p.f8 = a->kv_dtype == V4A_FP8_E4M3;
+  if (p.f8) {
+    p.kcs = (const float*)a->kc_scale.ptr; p.kcs_bs = a->kc_scale.batch_stride;
+    p.vcs = (const float*)a->vc_scale.ptr; p.vcs_bs = a->vc_scale.batch_stride;
+    p.khs = (const float*)a->kh_scale.ptr; p.khs_bs = a->kh_scale.batch_stride;
+    p.vhs = (const float*)a->vh_scale.ptr; p.vhs_bs = a->vh_scale.batch_stride;
+    p.krs = (const float*)a->kr_scale.ptr; p.krs_bs = a->kr_scale.batch_stride;
+    p.vrs = (const float*)a->vr_scale.ptr; p.vrs_bs = a->vr_scale.batch_stride;
+  }
   if (p.skv) {  // every entry is its own value
     p.vc = p.kc; p.vc_bs = p.kc_bs; p.vc_rs = p.kc_rs;
     p.vh = p.kh; p.vh_bs = p.kh_bs; p.vh_rs = p.kh_rs;

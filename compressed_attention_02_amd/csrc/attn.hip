@@ -36,16 +36,22 @@ template <int NW, int HT, int D, int KP>
 constexpr int attn_waves_per_eu() {
   return D == 512 ? 2 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
 }
-template <int NW, int HT, int D, int KP, bool QP, bool SKV>
+template <int NW, int HT, int D, int KP, bool QP, bool SKV, bool F8>
 __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
   __shared__ __align__(16) AttnSmem<D, SKV> sm;
-  attn_block<NW, HT, D, KP, false, QP, SKV>(p, blockIdx.x, blockIdx.y, sm);
+  attn_block<NW, HT, D, KP, false, QP, SKV, F8>(p, blockIdx.x, blockIdx.y, sm);
 }
 
-template <int NW, int HT, int D, int KP, bool SKV>
+template <int NW, int HT, int D, int KP, bool SKV, bool F8>
 static void launch_bf16(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
-  if (p.rope_out) V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, true, SKV>), grid, dim3(NW * 64), 0, s, p);
-  else V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, false, SKV>), grid, dim3(NW * 64), 0, s, p);
+  if (p.rope_out) V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, true, SKV, F8>), grid, dim3(NW * 64), 0, s, p);
+  else V4A_LAUNCH(tid, (attn_bf16_kernel<NW, HT, D, KP, false, SKV, F8>), grid, dim3(NW * 64), 0, s, p);
+}
+// rows of up to 128: bf16 or FP8 caches
+template <int NW, int HT, int D, int KP>
+static void launch_narrow(const AttnP& p, dim3 grid, hipStream_t s, int tid) {
+  if (p.f8) launch_bf16<NW, HT, D, KP, false, true>(p, grid, s, tid);
+  else launch_bf16<NW, HT, D, KP, false, false>(p, grid, s, tid);
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -194,18 +200,19 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
     // shared entries only: 8 waves, a wave pair per head tile, four tiles per
     // workgroup (more heads come in head groups)
     if (!p.skv || ntile > kWideTiles) return hipErrorInvalidValue;
-    launch_bf16<8, 1, 512, 1, true>(p, grid, s, tid);
+    if (p.f8) return hipErrorInvalidValue;
+    launch_bf16<8, 1, 512, 1, true, false>(p, grid, s, tid);
     return hipGetLastError();
   }
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
   // chunk's keys in half (four waves per SIMD); above, one wave per head tile
   // (shared entries at d <= 128 arrive with the value pointers aimed at the keys)
   if (ntile <= 4) {
-    if (p.dim == 64) launch_bf16<8, 1, 64, 2, false>(p, grid, s, tid);
-    else launch_bf16<8, 1, 128, 2, false>(p, grid, s, tid);
+    if (p.dim == 64) launch_narrow<8, 1, 64, 2>(p, grid, s, tid);
+    else launch_narrow<8, 1, 128, 2>(p, grid, s, tid);
   } else {
-    if (p.dim == 64) launch_bf16<8, 1, 64, 1, false>(p, grid, s, tid);
-    else launch_bf16<8, 1, 128, 1, false>(p, grid, s, tid);
+    if (p.dim == 64) launch_narrow<8, 1, 64, 1>(p, grid, s, tid);
+    else launch_narrow<8, 1, 128, 1>(p, grid, s, tid);
   }
   return hipGetLastError();
 }

@@ -339,7 +339,11 @@ struct RowKeys {
   const uint16_t *kc, *vc, *kh, *vh, *kr, *vr, *fallback;  // the row's sequence
   int64_t kc_rs, vc_rs, kh_rs, vh_rs, kr_rs, vr_rs;        // row strides (elements)
   int64_t n_csa, hca_end, raw_off, k_begin, k_end;
+  // FP8 caches: the row's scales (one per cache row); the code tables are the
+  // pointers above taken as bytes
+  const float *kcs, *vcs, *khs, *vhs, *krs, *vrs;
 };
+
 
 constexpr float kLazyRescale = 8.f; // running max moves only when exceeded by 2^8
 constexpr int kWideGroup = 4;        // fragment steps per scheduling group of rows wider than 128
@@ -453,6 +457,85 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
   }
 }
 
+// FP8 caches: where virtual key t's codes (bytes) and scales live; !ok keys read
+// the row's query bytes and a fallback scale word, always valid memory.
+__device__ __forceinline__ void key_src_f8(const RowKeys& R, const int* s_idx, int64_t t, bool want_v,
+                                           const unsigned char*& code, const float*& scale, bool& ok) {
+  const bool in = t < R.k_end;
+  const bool csa = t < R.n_csa, hca = t < R.hca_end;
+  const int64_t j = t - R.k_begin;
+  const int id = csa ? s_idx[j < 0 ? 0 : (j >= kMaxTopk ? kMaxTopk - 1 : j)] : 0;
+  ok = in && (!csa || id >= 0);
+  const int64_t r = ok ? (csa ? (int64_t)id : (hca ? t - R.n_csa : t + R.raw_off)) : 0;
+  const uint16_t* base = want_v ? (csa ? R.vc : (hca ? R.vh : R.vr)) : (csa ? R.kc : (hca ? R.kh : R.kr));
+  const int64_t rs = want_v ? (csa ? R.vc_rs : (hca ? R.vh_rs : R.vr_rs)) : (csa ? R.kc_rs : (hca ? R.kh_rs : R.kr_rs));
+  const float* sb = want_v ? (csa ? R.vcs : (hca ? R.vhs : R.vrs)) : (csa ? R.kcs : (hca ? R.khs : R.krs));
+  code = ok ? reinterpret_cast<const unsigned char*>(base) + r * rs : reinterpret_cast<const unsigned char*>(R.fallback);
+  scale = ok ? sb + r : reinterpret_cast<const float*>(R.fallback);
+}
+
+// Issues the loads of the FP8 chunk at virtual key kc0 into the staging buffers
+// (codes row-major, D bytes per row: lane l's 16 codes land at base + 16 l), the
+// rows' K and V scales (waves 0 and 1, lane l = row l, 4 bytes each) and writes the
+// mask.  Everything lands in LDS by direct loads; the caller waits for vmcnt(0).
+template <int NW, int D>
+__device__ __forceinline__ void issue_chunk_f8(const RowKeys& R, const int* s_idx, int64_t kc0, unsigned char* sKc,
+                                               unsigned char* sVc, float* sBias, float* sKs, float* sVs, int wave,
+                                               int lane) {
+  constexpr int PS = D / 16;              // 16-code pieces per row
+  constexpr int RPI = 64 / PS;            // rows per wave instruction
+  constexpr int NI = kAttnChunk / RPI;    // instructions per chunk, for K and for V
+  const int prow = lane / PS, ppiece = lane % PS;
+  for (int u = wave; u < NI; u += NW) {
+    const int r = u * RPI + prow;
+    const unsigned char *kp, *vp;
+    const float *ks, *vs;
+    bool ok;
+    key_src_f8(R, s_idx, kc0 + r, false, kp, ks, ok);
+    key_src_f8(R, s_idx, kc0 + r, true, vp, vs, ok);
+    lds_load16(kp + ppiece * 16, lds_addr(sKc + u * RPI * D));
+    lds_load16(vp + ppiece * 16, lds_addr(sVc + u * RPI * D));
+    if (ppiece == 0) sBias[r] = ok ? 0.f : -INFINITY;
+  }
+  if (wave < 2) {
+    const unsigned char* cp;
+    const float* sp;
+    bool ok;
+    key_src_f8(R, s_idx, kc0 + lane, wave == 1, cp, sp, ok);
+    lds_load4(sp, lds_addr(wave == 0 ? sKs : sVs));
+  }
+}
+
+// Staged FP8 codes -> the bf16 chunk layout (K with swz_k, V with swz_v), exactly:
+// thread item x takes 16 codes of one row (one staging piece) and writes two bf16
+// pieces.  Masked rows (sBias -inf) become zeros: their staged bytes are the query
+// row's, which may hold NaN codes, and a NaN times a zero weight would still reach
+// the sums.
+template <int NT, int D>
+__device__ __forceinline__ void convert_chunk_f8(const unsigned char* sKc, const unsigned char* sVc, uint16_t* sK,
+                                                 uint16_t* sV, const float* sBias) {
+  constexpr int PS = D / 16;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  for (int x = threadIdx.x; x < 2 * kAttnChunk * PS; x += NT) {
+    const bool v = x >= kAttnChunk * PS;
+    const int y = v ? x - kAttnChunk * PS : x;
+    const int r = y / PS, pc = y % PS;
+    uint4 c = *reinterpret_cast<const uint4*>((v ? sVc : sKc) + r * D + pc * 16);
+    if (sBias[r] != 0.f) c = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[k], 1.0f, false));
+      w[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[k], 1.0f, true));
+    }
+    uint16_t* dst = v ? sV : sK;
+    const int x0 = v ? swz_v<D>(r) : swz_k<D>(r);
+    *reinterpret_cast<uint4*>(dst + chunk_off<D>(r, 2 * pc, x0)) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + chunk_off<D>(r, 2 * pc + 1, x0)) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
 // S^T = K Q^T, online softmax and O^T += V^T P^T for one chunk of kAttnChunk keys
 // in LDS, for HT tiles of 16 heads.
 //   * S^T: keys on M, heads on N; lane (col, grp) ends up with head col and keys
@@ -467,11 +550,13 @@ __device__ __forceinline__ void issue_chunk(const RowKeys& R, const int* s_idx, 
 //     kLazyRescale (base 2); until then exp2(x - m) <= 2^8 and O, l need no
 //     rescaling.  (m, l, O) stay consistent, which is all that finishing and
 //     merging need.
-template <int D, int HT, int KP>
+// With F8, sKs / sVs hold the chunk's key and value scales: a key's scale joins its
+// logit, a value's its weight in the product (not the denominator l).
+template <int D, int HT, int KP, bool F8 = false>
 __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t* sV, const float* sBias,
                                              const bf16x8_t (&Qb)[HT][D / 32], f32x4 (&O)[HT][D / 16],
                                              float (&m_run)[HT], float (&l_run)[HT], float sl2, int col, int grp,
-                                             int kh) {
+                                             int kh, const float* sKs = nullptr, const float* sVs = nullptr) {
   constexpr int KS = D / 32, DT = D / 16;
   constexpr int NKT = 4 / KP;     // tiles of 16 keys of this wave: its part kh of the chunk
   f32x4 S[HT][NKT];
@@ -497,10 +582,16 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt) {
     const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * (NKT * kh + kt) + 4 * grp]);
+    f32x4 ksl = {sl2, sl2, sl2, sl2};
+    if constexpr (F8) {   // masked keys' scale words are whatever the fallback holds: zero them
+      ksl = *reinterpret_cast<const f32x4*>(&sKs[16 * (NKT * kh + kt) + 4 * grp]) * sl2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ksl[e] = bias[e] == 0.f ? ksl[e] : 0.f;
+    }
 #pragma unroll
     for (int t = 0; t < HT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][kt][e] = fmaf(S[t][kt][e], sl2, bias[e]);
+      for (int e = 0; e < 4; ++e) S[t][kt][e] = fmaf(S[t][kt][e], ksl[e], bias[e]);
   }
 #pragma unroll
   for (int t = 0; t < HT; ++t) {
@@ -537,6 +628,9 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
   for (int k2 = 0; k2 < 2 / KP; ++k2) {
     const int kk = (2 / KP) * kh + k2;   // 32-key half of the chunk
     // P^T of keys 32kk + {4grp+e, 16+4grp+e} (tiles 2kk, 2kk+1) as bf16 hi + lo
+    float vsc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vsc[e] = F8 ? sVs[32 * kk + 16 * (e >> 2) + 4 * grp + (e & 3)] : 1.f;
     bf16x8_t Bhi[HT], Blo[HT];
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
@@ -545,9 +639,10 @@ __device__ __forceinline__ void attend_chunk(const uint16_t* sK, const uint16_t*
       for (int e = 0; e < 8; ++e) {
         const float v = __builtin_amdgcn_exp2f(S[t][2 * k2 + (e >> 2)][e & 3] - mu[t]);
         ps += v;
-        const __bf16 h = (__bf16)v;
+        const float pv = F8 ? (v > 0.f ? v * vsc[e] : 0.f) : v;   // (masked keys: v = 0)
+        const __bf16 h = (__bf16)pv;
         Bhi[t][e] = h;
-        Blo[t][e] = (__bf16)(v - (float)h);
+        Blo[t][e] = (__bf16)(pv - (float)h);
       }
       l_run[t] += ps;
     }
@@ -598,6 +693,36 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
     if (active) attend_chunk<D, HT, KP>(Kc, Vc, Bc, Qb, O, m_run, l_run, sl2, col, grp, kh);
     __syncthreads();
     if (c + 2 < nch) issue_chunk<NW, D, SKV>(R, s_idx, R.k_begin + (c + 2) * CH, Kc, Vc, Bc, wave, lane);
+  }
+}
+
+// The chunk pipeline of FP8 caches: one staging buffer of codes and one bf16 chunk
+// buffer.  Each chunk's codes and scales land in staging, are converted into the
+// bf16 layout, and then the next chunk's loads are issued into staging while this
+// one is computed (the mask and scale arrays alternate by chunk parity).
+template <int NW, int D, int HT, int KP>
+__device__ __forceinline__ void run_chunks_f8(const RowKeys& R, const int* s_idx, uint16_t* sK, uint16_t* sV,
+                                              unsigned char* sKc, unsigned char* sVc, float* B0, float* B1,
+                                              float* sS, int64_t nch, bool active, const bf16x8_t (&Qb)[HT][D / 32],
+                                              f32x4 (&O)[HT][D / 16], float (&m_run)[HT], float (&l_run)[HT],
+                                              float sl2, int wave, int lane, int kh) {
+  constexpr int CH = kAttnChunk;
+  const int col = lane & 15, grp = lane >> 4;
+  // sS: [parity][K, V][64] scales
+  if (nch > 0) issue_chunk_f8<NW, D>(R, s_idx, R.k_begin, sKc, sVc, B0, sS, sS + CH, wave, lane);
+  for (int64_t c = 0; c < nch; ++c) {
+    const int par = (int)(c & 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    convert_chunk_f8<NW * 64, D>(sKc, sVc, sK, sV, par ? B1 : B0);
+    __syncthreads();
+    if (c + 1 < nch)
+      issue_chunk_f8<NW, D>(R, s_idx, R.k_begin + (c + 1) * CH, sKc, sVc, par ? B0 : B1, sS + (1 - par) * 2 * CH,
+                            sS + (1 - par) * 2 * CH + CH, wave, lane);
+    if (active)
+      attend_chunk<D, HT, KP, true>(sK, sV, par ? B1 : B0, Qb, O, m_run, l_run, sl2, col, grp, kh,
+                                    sS + par * 2 * CH, sS + par * 2 * CH + CH);
+    __syncthreads();
   }
 }
 
@@ -787,6 +912,7 @@ struct AttnSmem {
   // wide rows: the logits a wave pair hands over, [tile][key tile][lane] x 4
   float X[D > 128 ? kWideTiles * 4 * 64 * 4 : 1];
   float B0[kAttnChunk], B1[kAttnChunk];
+  float S8[4 * kAttnChunk];   // FP8 caches: [parity][K, V] row scales of a chunk
   int idx[kMaxTopk];
   int flag;
   __device__ uint16_t* K0() { return buf; }
@@ -808,8 +934,9 @@ struct AttnSmem {
 // QP: the output is rotated back at -pos (the query arrives normalised and rotated
 // from launch_qprep); without it the kernel carries none of that code.  SKV: every
 // entry is its own value (shared K = V rows, loaded once).
-template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false>
+template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false, bool F8 = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
+  static_assert(!F8 || (!SKV && D <= 128), "FP8 caches: separate K and V rows of up to 128");
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
   static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1), "wide rows: 8 waves, one tile per pair");
@@ -877,6 +1004,19 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   R.kr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.kr) + (int64_t)b * p.kr_bs : qrow;
   R.vr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.vr) + (int64_t)b * p.vr_bs : qrow;
   R.kc_rs = p.kc_rs; R.vc_rs = p.vc_rs; R.kh_rs = p.kh_rs; R.vh_rs = p.vh_rs; R.kr_rs = p.kr_rs; R.vr_rs = p.vr_rs;
+  if constexpr (F8) {
+    // codes are bytes (strides in elements = bytes); scales one fp32 per cache row
+    auto bytes = [&](const void* t, int64_t bs, bool on) {
+      return on ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(t) + (int64_t)b * bs) : qrow;
+    };
+    R.kc = bytes(p.kc, p.kc_bs, p.mask & 1u); R.vc = bytes(p.vc, p.vc_bs, p.mask & 1u);
+    R.kh = bytes(p.kh, p.kh_bs, p.mask & 2u); R.vh = bytes(p.vh, p.vh_bs, p.mask & 2u);
+    R.kr = bytes(p.kr, p.kr_bs, p.mask & 4u); R.vr = bytes(p.vr, p.vr_bs, p.mask & 4u);
+    const float* fb = reinterpret_cast<const float*>(qrow);
+    R.kcs = (p.mask & 1u) ? p.kcs + (int64_t)b * p.kcs_bs : fb; R.vcs = (p.mask & 1u) ? p.vcs + (int64_t)b * p.vcs_bs : fb;
+    R.khs = (p.mask & 2u) ? p.khs + (int64_t)b * p.khs_bs : fb; R.vhs = (p.mask & 2u) ? p.vhs + (int64_t)b * p.vhs_bs : fb;
+    R.krs = (p.mask & 4u) ? p.krs + (int64_t)b * p.krs_bs : fb; R.vrs = (p.mask & 4u) ? p.vrs + (int64_t)b * p.vrs_bs : fb;
+  }
   if (n_idx > 0) {
 #pragma unroll
     for (int u = 0; u < IDX_PER; ++u)
@@ -899,7 +1039,11 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  if constexpr (WIDE)
+  if constexpr (F8)
+    run_chunks_f8<NW, D, HT, KP>(R, s_idx, sm.K0(), sm.V0(), reinterpret_cast<unsigned char*>(sm.K1()),
+                                 reinterpret_cast<unsigned char*>(sm.V1()), sm.B0, sm.B1, sm.S8, nch, tv[0], Qb, O,
+                                 m_run, l_run, sl2, wave, lane, kh);
+  else if constexpr (WIDE)
     run_chunks_wide<NW, D, SKV>(R, s_idx, sm.K0(), sm.V0(), sm.B0, sm.K1(), sm.V1(), sm.B1, sm.X, nch, tv[0], Qb,
                                 O, m_run, l_run, sl2, wave, lane, wave % TW, kh);
   else

@@ -139,6 +139,10 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
 __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+// The 4-byte form: lane l's word lands at lds + 4 l.
+__device__ __forceinline__ void lds_load4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -103,6 +103,10 @@ struct AttnP {
   const float* q_norm; float norm_eps;  // RMSNorm gain of the queries (null: none)
   int rope; int rope_out; double rope_lb;  // query rotation (R channels), output rotation at -p
   int skv;             // shared entries: the value rows are the key rows (vc/vh/vr alias kc/kh/kr)
+  // FP8 caches (f8): every cache holds FP8 E4M3 codes; the row scales, [batch][rows]
+  int f8;
+  const float *kcs, *vcs, *khs, *vhs, *krs, *vrs;
+  int64_t kcs_bs, vcs_bs, khs_bs, vhs_bs, krs_bs, vrs_bs;
   // this launch covers the virtual keys [key_lo, key_hi) of every row, cut into
   // `splits` splits of keys_per_split keys; its partials go to slots
   // split_base .. split_base + splits - 1 of splits_total per row.  With

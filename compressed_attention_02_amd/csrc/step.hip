@@ -28,7 +28,7 @@ union StepSmem {
   SelShared sel;
 };
 
-template <int D, int KP, bool QP>
+template <int D, int KP, bool QP, bool F8>
 __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, AttnP ap, AttnP csa, int n_sel,
                                                                   int n_rest) {
   static_assert(kSelThreads == 8 * 64, "the attention workgroups run 8 waves");
@@ -42,10 +42,10 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   const int a = blk - n_sel;
   if (a < n_rest) {
     const int xw = ap.splits * ap.head_groups;   // (split, head group) workgroups per row
-    attn_block<8, 1, D, KP, true, QP, D == 512>(ap, a % xw, a / xw, sm.attn);
+    attn_block<8, 1, D, KP, true, QP, D == 512, F8>(ap, a % xw, a / xw, sm.attn);
   } else {
     const int c = a - n_rest;
-    attn_block<8, 1, D, KP, true, QP, D == 512>(csa, c % csa.splits, c / csa.splits, sm.attn);
+    attn_block<8, 1, D, KP, true, QP, D == 512, F8>(csa, c % csa.splits, c / csa.splits, sm.attn);
   }
 }
 
@@ -53,8 +53,14 @@ template <int D, int KP>
 static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int nr, dim3 g,
                       hipStream_t s, int tid) {
   const dim3 blk(kSelThreads);
-  if (ap.rope_out) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
-  else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+  constexpr bool CAN_F8 = D <= 128;
+  if (CAN_F8 && ap.f8) {
+    if (ap.rope_out) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true, CAN_F8>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false, CAN_F8>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+  } else {
+    if (ap.rope_out) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true, false>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+    else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false, false>), g, blk, 0, s, sp, ap, csa, n_sel, nr);
+  }
 }
 
 int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows) {

@@ -107,7 +107,9 @@ class LayerStep:
                     raw_start=t.get("raw_start"), branch_mask=s.branches, csa_ratio=s.m,
                     hca_ratio=s.m_hca, window=s.window, topk=s.topk, pos_max=self.pos_max,
                     shared_kv=s.shared_kv, rope_dims=s.rope_dims, rope_base=s.rope_base,
-                    rope_out=s.rope_dims > 0, q_norm=t.get("gq") if s.q_norm else None, norm_eps=s.norm_eps)
+                    rope_out=s.rope_dims > 0, q_norm=t.get("gq") if s.q_norm else None, norm_eps=s.norm_eps,
+                    kc_scale=t.get("kc_scale"), vc_scale=t.get("vc_scale"), kh_scale=t.get("kh_scale"),
+                    vh_scale=t.get("vh_scale"), kr_scale=t.get("k_raw_scale"), vr_scale=t.get("v_raw_scale"))
 
     def run_attn(self, stream=None):
         fn = decode if self.s.tq == 1 else prefill_chunk

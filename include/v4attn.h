@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 5u
+#define V4ATTN_ABI_VERSION 6u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -231,6 +231,14 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *                rotated at its position p like the entries (see
  *                v4attn_compress); rope_base > 0, finite.  The caches hold
  *                entries already rotated (compress, and the caller's raw rows).
+ *   kv_dtype     0 (the caches have type dtype) or, with dtype BF16, d <= 128
+ *                and no V4A_SHARED_KV, V4A_FP8_E4M3: every enabled cache (kc,
+ *                vc, kh, vh, k_raw, v_raw) holds FP8 E4M3 codes (as in
+ *                v4attn_index_topk) and its row r stands for scale[b][r] *
+ *                decode(code), the scale from the matching *_scale tensor (fp32
+ *                [batch][rows], row_stride 1).  Keys enter the logit and values
+ *                the output with their scale; the query stays bf16.  [wiki] the
+ *                quantization and deployment section (FP8 KV caches).
  *   flags        V4A_ROPE_OUTPUT (with rope_dims): o's last R channels are
  *                rotated at -p.
  *                V4A_BATCH_INVARIANT: a query's o and lse (and, through
@@ -293,6 +301,9 @@ typedef struct v4a_attn_args {
   int32_t rope_dims;
   float rope_base;
   int32_t reserved1;
+  int32_t kv_dtype;     /* 0 (= dtype) or V4A_FP8_E4M3 */
+  int32_t reserved2;
+  v4a_tensor kc_scale, vc_scale, kh_scale, vh_scale, kr_scale, vr_scale;
 } v4a_attn_args;
 
 size_t v4attn_decode_workspace(const v4a_attn_args* args);

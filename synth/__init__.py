@@ -26,13 +26,14 @@ Recipe (the same for every configuration):
     with a query RMSNorm its per-channel gain is U(0.5, 1.5) fp32;
   * FP8 indexer keys: each drawn row (needles planted as above) gets the scale
     max|row| / 448 (1 for an all-zero row), stored in fp32, and its codes are
-    torch's round-to-nearest-even cast of row / scale to float8_e4m3fn.
+    torch's round-to-nearest-even cast of row / scale to float8_e4m3fn; FP8 K/V
+    caches the same, each cache row from its N(0,1) draw (needle nudges included).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .configs import C1, C2, C3, C4, C5, C6, C7, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
+from .configs import C1, C2, C3, C4, C5, C6, C7, C8, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
 
 # appending a stream leaves the earlier ones' draws unchanged
 _STREAMS = ("q", "qi", "wi", "ki", "kc", "vc", "kh", "vh", "k_raw", "v_raw",
@@ -126,16 +127,25 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
             for b in range(B):
                 qm = _load(out["q"][b, 0], cfg.dtype).mean(axis=0)
                 kc[b, needles[b]] += 3.0 * qm / np.linalg.norm(qm)
-        out["kc"] = _store(kc, cfg.dtype)
-        if not cfg.shared_kv:
-            out["vc"] = _store(vc, cfg.dtype)
+        if cfg.kv_fp8:
+            out["kc"], out["kc_scale"] = _fp8_rows(kc)
+            out["vc"], out["vc_scale"] = _fp8_rows(vc)
+        else:
+            out["kc"] = _store(kc, cfg.dtype)
+            if not cfg.shared_kv:
+                out["vc"] = _store(vc, cfg.dtype)
+    def cache(name, shape):
+        if cfg.kv_fp8:
+            out[name], out[name + "_scale"] = _fp8_rows(rngs[name].standard_normal(shape))
+        else:
+            out[name] = _normal(rngs[name], shape, cfg.dtype)
     if use_hca:
-        out["kh"] = _normal(rngs["kh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
+        cache("kh", (B, max(cfg.e_cap, 1), d))
         if not cfg.shared_kv:
-            out["vh"] = _normal(rngs["vh"], (B, max(cfg.e_cap, 1), d), cfg.dtype)
-    out["k_raw"] = _normal(rngs["k_raw"], (B, cfg.raw_rows, d), cfg.dtype)
+            cache("vh", (B, max(cfg.e_cap, 1), d))
+    cache("k_raw", (B, cfg.raw_rows, d))
     if not cfg.shared_kv:
-        out["v_raw"] = _normal(rngs["v_raw"], (B, cfg.raw_rows, d), cfg.dtype)
+        cache("v_raw", (B, cfg.raw_rows, d))
     if cfg.q_norm:
         out["gq"] = rngs["gq"].uniform(0.5, 1.5, d).astype(np.float32)
     if cfg.compress != "none":

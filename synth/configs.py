@@ -48,6 +48,7 @@ class LayerConfig:
     rope_dims: int = 0    # partial RoPE on the last rope_dims channels (0: off)
     q_norm: bool = False  # RMSNorm of each head's query with a synthetic gain
     ki_fp8: bool = False  # indexer keys stored as FP8 E4M3 codes with one fp32 scale per row
+    kv_fp8: bool = False  # every K/V cache stored the same way (caches drawn directly)
 
     # ---- derived shape helpers (pure bookkeeping, no method arithmetic) ----
     @property
@@ -141,4 +142,12 @@ C7 = LayerConfig(
     branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
     seed=20260007, timed="index_topk + decode", ki_fp8=True)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7)}
+# C7 with every K/V cache in FP8 as well (compressed CSA and HCA entries and the
+# window's raw rows).
+C8 = LayerConfig(
+    name="c8_fp8_caches_decode_b1_1m", dtype="bf16", batch=1, pos=1048576, tq=1, heads=128,
+    dim=128, idx_heads=64, idx_dim=64, m=4, topk=1024, m_hca=128, window=128,
+    branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
+    seed=20260008, timed="index_topk + decode", ki_fp8=True, kv_fp8=True)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8)}

@@ -171,8 +171,8 @@ class Run:
         idx = dev_to_np(self.step.idx)
         caches = dict(branches=cfg.branches, m=cfg.m, m_hca=cfg.m_hca, window=cfg.window)
         for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):
-            if nm in self.t:
-                caches[nm] = self.f64(nm)
+            if nm in self.t:   # FP8 caches: codes with one scale per row
+                caches[nm] = (O.fp8_rows(self.host(nm), self.host(nm + "_scale")) if cfg.kv_fp8 else self.f64(nm))
         q = O.as_f64(self.g["q"], cfg.dtype)
         rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.tq)] if rows is None else rows
         out_o, out_l = [], []

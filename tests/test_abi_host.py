@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 13
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 5
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 6
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -287,3 +287,20 @@ def test_fp8_key_argument_checks():
     fp8 = dict(ki_dtype=V.FP8_E4M3, ki=_T(bs=64 * 32768, rs=64), ki_scale=_T(bs=32768, rs=1))
     assert L.v4attn_index_topk_workspace(ctypes.byref(good_index(**fp8))) > 0
     assert _st(f, good_index(**dict(fp8, ki_scale=_T(bs=32768, rs=2))), None, 0, None)[0] == EINVAL
+
+
+def test_fp8_cache_argument_checks():
+    L = V.lib()
+    none = V.Tensor(None, 0, 0)
+    f8 = dict(kv_dtype=V.FP8_E4M3, kc=_T(bs=128 * 32768, rs=128), vc=_T(bs=128 * 32768, rs=128),
+              kh=_T(bs=128 * 1024, rs=128), vh=_T(bs=128 * 1024, rs=128), k_raw=_T(bs=128 * 128, rs=128),
+              v_raw=_T(bs=128 * 128, rs=128))
+    scales = {n: _T(bs=32768, rs=1) for n in ("kc_scale", "vc_scale", "kh_scale", "vh_scale", "kr_scale", "vr_scale")}
+    assert L.v4attn_decode_workspace(ctypes.byref(good_attn(**f8, **scales))) > 0
+    r, msg = _st(L.v4attn_decode, good_attn(**f8), None, 0, None)
+    assert r == EINVAL and "scale" in msg
+    assert _st(L.v4attn_decode, good_attn(**f8, **dict(scales, kh_scale=_T(bs=1024, rs=4))), None, 0, None)[0] == EINVAL
+    assert _st(L.v4attn_decode, good_attn(**f8, **scales, dtype=V.F32), None, 0, None)[0] == EINVAL
+    r, msg = _st(L.v4attn_decode, good_attn(**dict(f8, flags=V.SHARED_KV, vc=none, vh=none, v_raw=none), **scales),
+                 None, 0, None)
+    assert r == ENOTSUP

@@ -59,3 +59,40 @@ def test_full_c7_decode_step():
     r = Run(cfg).run(fused=True).check_all()
     idx = dev_to_np(r.step.idx)
     assert set(r.g["needles"][0].tolist()) <= set(idx[0, 0].tolist())
+
+
+# ---- FP8 K/V caches (every branch): codes staged in LDS, converted to the bf16
+# chunk layout, key scales in the logits, value scales in the product weights
+@pytest.mark.parametrize("heads,batch,fused", [(128, 1, False), (128, 1, True), (64, 3, True), (16, 2, False)])
+def test_fp8_caches_decode(heads, batch, fused):
+    cfg = C.C8.small(name="f8kv", heads=heads, batch=batch, pos=70003, needles=8)
+    print(f"[case] fp8 caches H={heads} B={batch} fused={fused}", flush=True)
+    Run(cfg).run(fused=fused).check_all()
+
+
+def test_fp8_caches_prefill_rows():
+    cfg = C.C5.small(name="f8kv5", pos=8192, tq=320, needles=8, compress="none", ki_fp8=True, kv_fp8=True)
+    print("[case] fp8 caches prefill", flush=True)
+    Run(cfg).run().check_all(rows=sample_rows(cfg))
+
+
+def test_fp8_caches_every_code_and_signs():
+    cfg = C.C8.small(name="f8kvc", pos=20483, needles=0, heads=64, topk=512)
+    g = synth.generate(cfg)
+    rng = np.random.default_rng(48)
+    pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for nm in ("kc", "vc", "kh", "vh", "k_raw", "v_raw"):
+        g[nm][...] = rng.choice(pool, size=g[nm].shape)
+        sc = rng.uniform(0.001, 0.01, g[nm + "_scale"].shape).astype(np.float32)
+        sc[..., ::29] *= -1
+        sc[..., ::41] = 0
+        g[nm + "_scale"][...] = sc
+    print("[case] fp8 caches codes", flush=True)
+    Run(cfg, gen=g).run(fused=True).check_all()
+
+
+def test_full_c8_decode_step():
+    print("[case] full c8", flush=True)
+    r = Run(C.C8).run(fused=True).check_all()
+    idx = dev_to_np(r.step.idx)
+    assert set(r.g["needles"][0].tolist()) <= set(idx[0, 0].tolist())
