@@ -10,6 +10,7 @@ walk several tiles; the codes cover every non-NaN value, subnormals and zero row
 """
 import numpy as np
 import pytest
+import torch
 
 from synth import configs as C
 import synth
@@ -96,3 +97,31 @@ def test_full_c8_decode_step():
     r = Run(C.C8).run(fused=True).check_all()
     idx = dev_to_np(r.step.idx)
     assert set(r.g["needles"][0].tolist()) <= set(idx[0, 0].tolist())
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["stages", "decode_step"])
+def test_fp8_caches_with_query_prep_and_output_rotation(fused):
+    # FP8 keys and caches under the query RMSNorm, partial RoPE and the output rotation
+    cfg = C.C8.small(name="f8r", heads=64, batch=2, pos=70003, needles=8, rope_dims=64, q_norm=True)
+    print(f"[case] fp8 caches + rope/norm fused={fused}", flush=True)
+    Run(cfg).run(fused=fused).check_all()
+
+
+def test_fp8_caches_and_shared_rows_batch_invariant_mode():
+    # the batch-invariant split plan over FP8 caches, and over shared rows of 512
+    import compressed_attention_02_amd as V
+    for cfg in (C.C8.small(name="f8i", heads=64, batch=3, pos=40961, needles=8),
+                C.C6.small(name="s6i", heads=64, batch=2, pos=40961, needles=8)):
+        r = Run(cfg).run()
+        kw = r.step.attn_kwargs()
+        if cfg.ki_fp8:
+            kw["ki_scale"] = r.t["ki_scale"]
+        for k in ("idx", "csa_ratio", "topk", "pos_max"):
+            kw.pop(k)
+        kw["batch_invariant"] = True
+        print(f"[case] invariant mode {cfg.name}", flush=True)
+        V.decode_step(r.t["qi"], r.t["wi"], r.t["ki"], r.t["q"], r.t["pos"], r.step.o, r.step.idx, ratio=cfg.m,
+                      topk=cfg.topk, pos_max=r.step.pos_max, **kw)
+        torch.cuda.synchronize()
+        r.check_topk()
+        r.check_attn()
