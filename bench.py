@@ -11,8 +11,9 @@ launch stream between two synchronisations.  Inputs are resident in HBM; the ste
 cycles through R copies of the input set at distinct addresses (R * bytes touched
 per step >= 2.5x the 256 MB Infinity Cache) so that steps are not served from it.
 The dominant kernel (the indexer score kernel, which streams the indexer keys) is
-timed on every timed launch by a pair of HIP events that its dispatch records at the
-kernel's start and end (the library's timing hooks, hipExtLaunchKernel).
+timed on the first tenth of the timed steps by a pair of HIP events recorded on its
+launch stream right before and right after its launch (the library's timing hooks):
+the interval holds the kernel and its dispatch.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
 """
@@ -309,9 +310,9 @@ def main():
         one(k)
     torch.cuda.synchronize()
     dom = "index_score" if cfg.branches & 1 else "attn"
-    # the dominant kernel's duration comes from events its dispatch records; they
-    # hold the next kernel back by several microseconds, so only the first tenth of
-    # the timed steps carry them
+    # the dominant kernel's duration comes from events recorded on its stream right
+    # around its launch; they cost the step a little, so only the first tenth of the
+    # timed steps carry them
     n_ev = max(1, args.steps // 10)
     if not args.no_kernel_events:
         V.timing_reset()

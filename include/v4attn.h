@@ -365,9 +365,10 @@ uint32_t v4attn_abi_version(void);
 
 /* ---------------------------------------------------------------------------
  * Kernel timing for benchmarks.  v4attn_timing_enable(kernel, n) makes the
- * library launch each of the next n launches of that kernel with a pair of
- * events that the dispatch itself records at the kernel's start and end
- * (hipExtLaunchKernel; events created here, kept until v4attn_timing_reset).  v4attn_timing_read waits for the recorded events and
+ * library bracket each of the next n launches of that kernel with a pair of
+ * events recorded on the launch stream right before and right after it (so
+ * the interval holds the kernel and its dispatch; events created here, kept
+ * until v4attn_timing_reset).  v4attn_timing_read waits for the recorded events and
  * writes up to cap per-launch durations in milliseconds; it returns the count,
  * or -1 on error.  kernel: one of the V4A_K_* ids.
  * ------------------------------------------------------------------------- */
