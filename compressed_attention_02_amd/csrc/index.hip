@@ -190,8 +190,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     }
     const int64_t j = tile0 + wave * 64 + lane;
     if (j < nvis) sc[j] = mine;
-    wave_top(j < nvis ? pack_kid(score_key(mine), (uint32_t)j) : 0ull, (uint32_t)(tile0 + wave * 64),
-             p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
+    wave_top(score_key(mine), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
              p.rep_info + (int64_t)lr * p.info_rs + tile * 4 + wave);
     __syncthreads();       // the buffer is reloaded next
     if (NB == 2 && tile + 2 * stride < ntile_row)
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
   const float* ki = reinterpret_cast<const float*>(p.ki) + (int64_t)b * p.ki_bs;
   float* sc = p.scores + (int64_t)lr * p.sc_rs;
   const int64_t j = tile0 + threadIdx.x;
-  uint64_t v = 0;
+  uint32_t v = 0;
   if (j < nvis) {
     const float* kj = ki + j * p.ki_rs;
     float s = 0.f;
@@ -238,10 +237,9 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
       s = fmaf(s_q[HD + h], fmaxf(dot, 0.f), s);
     }
     sc[j] = s;
-    v = pack_kid(score_key(s), (uint32_t)j);
+    v = score_key(s);
   }
-  wave_top(v, (uint32_t)(tile0 + (threadIdx.x & ~63)),
-           p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop + (threadIdx.x >> 6) * kWaveTop,
+  wave_top(v, j < nvis, p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop + (threadIdx.x >> 6) * kWaveTop,
            p.rep_info + (int64_t)lr * p.info_rs + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 

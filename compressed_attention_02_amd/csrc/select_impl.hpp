@@ -14,69 +14,45 @@ __device__ __forceinline__ void row_coords(int row, int tq, const int64_t* pos0,
   pos = pos0[b] + i;
 }
 
-// (key, id) packed so that the larger value is the better element: higher key, then
-// lower id.  0 marks "no element".
-__device__ __forceinline__ uint64_t pack_kid(uint32_t key, uint32_t id) {
-  return ((uint64_t)key << 32) | (uint64_t)(~id);
-}
-
-template <int CTRL, int ROWMASK = 0xF>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWMASK, 0xF, false);
-}
-template <int CTRL, int ROWMASK = 0xF>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  return ((uint64_t)dpp32<CTRL, ROWMASK>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL, ROWMASK>((uint32_t)v);
-}
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Maximum over the wave, returned to every lane, with DPP moves only (quad swaps,
-// half-row and row mirrors, then the row_bcast15/31 steps that leave the total in
-// lane 63) and a readlane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp64<0xB1>(v));        // quad_perm [1,0,3,2]
-  v = umax64(v, dpp64<0x4E>(v));        // quad_perm [2,3,0,1]
-  v = umax64(v, dpp64<0x141>(v));       // row_half_mirror
-  v = umax64(v, dpp64<0x140>(v));       // row_mirror
-  v = umax64(v, dpp64<0x142, 0xA>(v));  // row_bcast15 into rows 1 and 3
-  v = umax64(v, dpp64<0x143, 0xC>(v));  // row_bcast31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// A wave's report on its 64 packed values (one per lane, 0 = no element; lane L
-// holds block wave_base + L): the keys of its kWaveTop best in ascending id order,
-// their ids as 8-bit offsets from wave_base (0xff = no element) packed in one word,
-// and the key of the next best, an upper bound on every key it leaves out (0 if
-// none).
-__device__ __forceinline__ void wave_top(uint64_t v, uint32_t wave_base, uint32_t* keys, uint2* info) {
+// A wave's report on its 64 elements (lane L holds block base + L with order key
+// `key` when `valid`): the keys of its kWaveTop best (higher key first, then lower
+// id) in ascending id order, their ids as 8-bit offsets from base (0xff = no
+// element) packed in one word, and the key of the next best, an upper bound on every
+// key it leaves out (0 if none).  Each round takes a 32-bit wave maximum (DPP) of
+// the keys not yet taken and gives it to the lowest lane that holds it (a ballot),
+// so ties go to the lower id; the taken lanes, in lane order, are the id order.
+__device__ __forceinline__ void wave_top(uint32_t key, bool valid, uint32_t* keys, uint2* info) {
   static_assert(kWaveTop == 4, "four offsets per info word");
-  uint64_t m[kWaveTop + 1];
+  const int lane = threadIdx.x & 63;
+  bool live = valid;
+  uint64_t won = 0;
 #pragma unroll
-  for (int r = 0; r <= kWaveTop; ++r) {
-    m[r] = wave_max_u64(v);
-    if (v == m[r]) v = 0;
+  for (int r = 0; r < kWaveTop; ++r) {
+    const uint32_t m = wave_max_u32(live ? key : 0u);
+    const uint64_t at = __ballot(live && key == m);
+    if (at) {
+      const int l = __builtin_ctzll(at);
+      won |= 1ull << l;
+      live = live && lane != l;
+    }
   }
-  if ((threadIdx.x & 63) == 0) {
-    uint32_t key[kWaveTop], id[kWaveTop];
+  const uint32_t bound = wave_max_u32(live ? key : 0u);
+  uint32_t k4[kWaveTop], offs = 0;
 #pragma unroll
-    for (int r = 0; r < kWaveTop; ++r) { key[r] = (uint32_t)(m[r] >> 32); id[r] = ~(uint32_t)m[r]; }
-#pragma unroll
-    for (int a = 0; a < kWaveTop; ++a)
-#pragma unroll
-      for (int c = 0; c + 1 < kWaveTop - a; ++c)
-        if (id[c + 1] < id[c]) {
-          const uint32_t tk = key[c], ti = id[c];
-          key[c] = key[c + 1]; id[c] = id[c + 1];
-          key[c + 1] = tk; id[c + 1] = ti;
-        }
-    uint32_t offs = 0;
-#pragma unroll
-    for (int r = 0; r < kWaveTop; ++r)
-      offs |= (id[r] == 0xffffffffu ? 0xffu : ((id[r] - wave_base) & 0x3fu)) << (8 * r);
-    *reinterpret_cast<uint4*>(keys) = make_uint4(key[0], key[1], key[2], key[3]);
-    *info = make_uint2(offs, (uint32_t)(m[kWaveTop] >> 32));
+  for (int r = 0; r < kWaveTop; ++r) {
+    if (won) {
+      const int l = __builtin_ctzll(won);
+      won &= won - 1;
+      k4[r] = __builtin_amdgcn_readlane(key, l);
+      offs |= (uint32_t)l << (8 * r);
+    } else {
+      k4[r] = 0u;
+      offs |= 0xffu << (8 * r);
+    }
+  }
+  if (lane == 0) {
+    *reinterpret_cast<uint4*>(keys) = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+    *info = make_uint2(offs, bound);
   }
 }
 
@@ -241,20 +217,6 @@ __device__ __forceinline__ uint32_t kth_key_floor(Each each, uint32_t r, SelShar
   uint32_t bin, before;
   find_rank(sh.hist, sh, nb, r, true, bin, before);
   return lo + (bin << shift);
-}
-
-// 64-bit minimum over the wave (DPP), wave-uniform
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-  auto umin64 = [](uint64_t a, uint64_t b) { return a < b ? a : b; };
-  v = umin64(v, dpp64<0xB1>(v));
-  v = umin64(v, dpp64<0x4E>(v));
-  v = umin64(v, dpp64<0x141>(v));
-  v = umin64(v, dpp64<0x140>(v));
-  v = umin64(v, dpp64<0x142, 0xA>(v));
-  v = umin64(v, dpp64<0x143, 0xC>(v));
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
 }
 
 // The key threshold T and the largest tie id of the exact top-k over the visited
