@@ -35,18 +35,23 @@ BF16_PEAK_TFLOPS = 2500.0
 
 # HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE, then
 # WRITE_SIZE) of this script, calibrated on a plain device copy of known size made in
-# the same runs (--calibration-copy).  The file records a hash of the kernel's sources;
-# once they change the figure no longer describes the kernel and is not reported.
+# the same runs (--calibration-copy).  The file records a hash of the kernel's sources
+# (their code, without comments or spacing); once the code changes the figure no longer
+# describes the kernel and is not reported.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_bf16_c3.json")
-SCORE_SOURCES = ("index.hip", "select_impl.hpp", "common.hpp", "kernels.hpp")
+SCORE_SOURCES = ("index.hip", "select_impl.hpp", "qprep_impl.hpp", "common.hpp", "kernels.hpp")
 
 
 def score_source_hash() -> str:
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in SCORE_SOURCES:
-        with open(os.path.join(ROOT, "compressed_attention_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_attention_02_amd", "csrc", f), encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)   # block comments
+        code = re.sub(r"//[^\n]*", " ", code)                  # line comments
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

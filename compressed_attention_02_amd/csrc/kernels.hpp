@@ -62,8 +62,8 @@ struct ScoreP {
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
   int nrows;          // rows of the launch (set by launch_score)
   int* zero; int n_zero;  // words workgroup (0, 0) clears before anything else (null: none)
-  // bf16 kernel: workgroups x >= wgs_per_row of row y prepare that row's attention
-  // queries instead (prep_x of them; 0: none)
+  // bf16 kernel: workgroups x < prep_x of row y prepare that row's attention queries
+  // instead (0: none); the score workgroups follow them
   QPrepP prep; int prep_x;
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
