@@ -306,6 +306,7 @@ def main():
     for st in steps[1:]:           # (one stream: steps never overlap)
         st.ws_index, st.ws_attn = steps[0].ws_index, steps[0].ws_attn
         st.ws_step = getattr(steps[0], "ws_step", None)
+        st.prepare()               # every set's call is marshalled before any timing
 
     def one(k):
         steps[k % R].step(stream)

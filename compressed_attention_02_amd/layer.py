@@ -118,7 +118,12 @@ class LayerStep:
 
     def run_decode_step(self, stream=None):
         """index_topk + decode as one v4attn_decode_step (decode only); the call's
-        arguments are marshalled on first use and reused."""
+        arguments are marshalled on first use (or by prepare()) and reused."""
+        self.prepare()
+        self._step_call(stream)
+
+    def prepare(self):
+        """Marshal the decode step's call without launching anything."""
         if getattr(self, "_step_call", None) is None:
             s, t = self.s, self.t
             kw = self.attn_kwargs()
@@ -131,7 +136,6 @@ class LayerStep:
                                              self.o, self.idx, ratio=s.m, topk=s.topk, pos_max=self.pos_max,
                                              workspace=getattr(self, "ws_step", None), **kw)
             self.ws_step = self._step_call.workspace
-        self._step_call(stream)
 
     def step(self, stream=None, fused=True):
         """The whole hot path of one step: compress (if the step compresses),
