@@ -395,9 +395,6 @@ template <int D> __device__ __forceinline__ int chunk_off(int r, int p, int x) {
   return ((p / PS) * kAttnChunk + r) * sub_cols<D>() + ((p % PS) ^ x) * 8;
 }
 
-// s_waitcnt immediate for vmcnt(n) (gfx9: low 4 bits at [3:0], high 2 at [15:14]),
-// every other counter left alone
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 // row r of a table at base with row stride rs (elements): 32 x 32 -> 64-bit product
 __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* base, uint32_t r, int64_t rs) {

@@ -136,6 +136,10 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
 // the vector-memory counter, then a workgroup barrier).  The instruction has no
 // register result, and the compiler's own waits can only get stricter for not
 // counting it, since vector-memory loads complete in issue order.
+// s_waitcnt immediate for vmcnt(n) (gfx9: low 4 bits at [3:0], high 2 at [15:14]),
+// every other counter left alone
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+
 __device__ __forceinline__ void lds_load16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }

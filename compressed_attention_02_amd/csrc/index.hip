@@ -124,9 +124,6 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
       lds_load16(qi + r * DI + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(sQ + u * RPI * ROWB));
     }
   }
-  issue(tile, sK[0]);
-  if (NB == 2 && tile + stride < ntile_row) issue(tile + stride, sK[NB - 1]);
-
   float w[MT][4];
   {
     const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
@@ -136,6 +133,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
       w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
     }
   }
+  // the tile loads go out last: the query rows and the weights are the oldest loads
+  issue(tile, sK[0]);
+  if (NB == 2 && tile + stride < ntile_row) issue(tile + stride, sK[NB - 1]);
   bf16x8_t A[MT][KS];
   bool have_q = false;
 
@@ -145,10 +145,13 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   for (int c = 0; tile < ntile_row; tile += stride, ++c) {
     const unsigned char* buf = sK[NB == 2 ? (c & 1) : 0];
     const bool next = NB == 2 && tile + stride < ntile_row;
-    if (next) __builtin_amdgcn_s_waitcnt(0x0F70 | IPW);  // vmcnt(IPW): the next tile may stay in flight
-    else __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
-    __syncthreads();
-    if (!have_q) {  // query fragments: row mt*16 + col, piece 4s + grp (the rows share col's XOR)
+    if (!have_q) {
+      // every wave's share of the query rows is in LDS once the loads issued before
+      // the tiles are done (vmcnt counts in issue order); then the query fragments:
+      // row mt*16 + col, piece 4s + grp (the rows share col's XOR)
+      if (next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+      __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -156,6 +159,10 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
           A[mt][s] = *reinterpret_cast<const bf16x8_t*>(sQ + (mt * 16 + col) * ROWB + (((s * 4 + grp) ^ kx) * 16));
       have_q = true;
     }
+    // a wave reads only the key rows it loaded itself, so its own loads are all it
+    // waits for (no barrier); the next tile may stay in flight
+    if (next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const int64_t tile0 = tile * kTile;
     float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
     float kscale = 1.f;     // FP8: the scale of that key's row (rows past n_vis: the last row's)
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
     if (j < nvis) sc[j] = mine;
     wave_top(score_key(mine), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop + wave * kWaveTop,
              p.rep_info + (int64_t)lr * p.info_rs + tile * 4 + wave);
-    __syncthreads();       // the buffer is reloaded next
+    // the buffer is reloaded next, each wave into the rows it has just read
     if (NB == 2 && tile + 2 * stride < ntile_row)
       issue(tile + 2 * stride, sK[NB == 2 ? (c & 1) : 0]);
   }
