@@ -448,7 +448,8 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
   V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
   if (P.splits > 1) {
-    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s, V4A_K_MERGE), "merge launch"));
+    const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, inv, s, V4A_K_MERGE), "merge launch"));
   }
   return ok();
 }
@@ -679,7 +680,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     V4A_TRY(attend(rest));
   }
   if (P.s_total > 1) {
-    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, s, V4A_K_MERGE), "merge launch"));
+    V4A_TRY(hip_check(launch_merge(p, (int)P.rows, inv, s, V4A_K_MERGE), "merge launch"));
   }
   return ok();
 }

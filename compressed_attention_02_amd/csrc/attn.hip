@@ -173,16 +173,22 @@ hipError_t launch_qprep(const QPrepP& p, int nrows, hipStream_t s, int tid) {
 }
 
 // ------------------------------------------------------------------ merge
-// One 256-thread workgroup per (row, head, 32 output columns): the merge reads every
+// One 256-thread workgroup per (row, head, DW output columns): the merge reads every
 // partial once, so it is spread over as many workgroups as there are column
-// slices to keep all CUs loading; merge_head holds the arithmetic.
+// slices to keep all CUs loading; merge_head holds the arithmetic.  DW = 32 by
+// default; with few splits a wider slice (64 or 128 columns) still loads all of a
+// thread's partials in its first batch and needs fewer, fuller workgroups (not in
+// batch-invariant plans, where the width, which sets how the splits are grouped in
+// the sum, must not follow the batch).
 constexpr int kMergeThreads = 256;
-constexpr int kMergeCols = 32;
+constexpr int kMergeCols = 32;          // the narrowest slice; every dim is a multiple
+constexpr int kMergeMinWorkgroups = 512;
 
+template <int DW>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnP p) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kMergeThreads];
-  merge_head<kMergeThreads, kMergeCols>(p, blockIdx.x, blockIdx.y, blockIdx.z * kMergeCols, s_w, s_red);
+  merge_head<kMergeThreads, DW>(p, blockIdx.x, blockIdx.y, blockIdx.z * DW, s_w, s_red);
 }
 
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid) {
@@ -217,11 +223,18 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid) {
+hipError_t launch_merge(const AttnP& p, int nrows, bool fixed_width, hipStream_t s, int tid) {
   if (p.splits_total > kMaxSplits) return hipErrorInvalidValue;
   if (p.dim % kMergeCols != 0 || p.merge_lo < 0 || p.merge_lo >= p.splits_total) return hipErrorInvalidValue;
-  V4A_LAUNCH(tid, merge_kernel, dim3((unsigned)nrows, (unsigned)p.heads, (unsigned)(p.dim / kMergeCols)),
-             dim3(kMergeThreads), 0, s, p);
+  const int S = p.splits_total - p.merge_lo;
+  auto fits = [&](int dw) {   // one batch of loads per thread, and enough workgroups
+    return !fixed_width && p.dim % dw == 0 && (kMergeThreads / dw) * kMergeBatch >= S &&
+           (int64_t)nrows * p.heads * (p.dim / dw) >= kMergeMinWorkgroups;
+  };
+  const dim3 blk(kMergeThreads);
+  if (fits(128)) V4A_LAUNCH(tid, merge_kernel<128>, dim3((unsigned)nrows, (unsigned)p.heads, (unsigned)(p.dim / 128)), blk, 0, s, p);
+  else if (fits(64)) V4A_LAUNCH(tid, merge_kernel<64>, dim3((unsigned)nrows, (unsigned)p.heads, (unsigned)(p.dim / 64)), blk, 0, s, p);
+  else V4A_LAUNCH(tid, merge_kernel<kMergeCols>, dim3((unsigned)nrows, (unsigned)p.heads, (unsigned)(p.dim / kMergeCols)), blk, 0, s, p);
   return hipGetLastError();
 }
 

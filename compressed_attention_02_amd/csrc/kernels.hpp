@@ -130,7 +130,9 @@ struct AttnP {
 constexpr int kRowWords = 4;
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
 
-hipError_t launch_merge(const AttnP& p, int nrows, hipStream_t s, int tid);
+// fixed_width: always 32 output columns per workgroup (batch-invariant plans: the
+// width sets how the splits are grouped in the sum)
+hipError_t launch_merge(const AttnP& p, int nrows, bool fixed_width, hipStream_t s, int tid);
 
 // selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
 // workgroups) in one launch; with csa (splits > 0, sync set) also the attention of
