@@ -9,11 +9,15 @@ step = index_topk + decode, the whole hot path of a decode token.
 Protocol: W untimed warm-up steps, then exactly K steps timed with events on the
 launch stream between two synchronisations.  Inputs are resident in HBM; the step
 cycles through R copies of the input set at distinct addresses (R * bytes touched
-per step >= 2.5x the 256 MB Infinity Cache) so that steps are not served from it.
-The dominant kernel (the indexer score kernel, which streams the indexer keys) is
-timed on the first tenth of the timed steps by a pair of HIP events recorded on its
-launch stream right before and right after its launch (the library's timing hooks):
-the interval holds the kernel and its dispatch.
+per step >= 1 GiB, four times the 256 MB Infinity Cache) so that steps are not
+served from it.  The dominant kernel (the indexer score kernel, which streams the
+indexer keys) is timed on the first tenth of the timed steps by a pair of HIP
+events recorded on its launch stream right before and right after its launch (the
+library's timing hooks): the interval holds the kernel and its dispatch.  A second
+pass of K steps over the same rotation records an event between every two steps
+for the median and the 10th / 90th percentiles of single steps; a read probe gives
+the rate at which this GPU streams a buffer read once (32 MiB cold, as the score
+kernel reads its keys, and 1 GiB), timed the same way as the dominant kernel.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
 """
@@ -32,6 +36,53 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn tokens/s + achieved HBM GB/s, CSA+HCA+SWA layer at 1M ctx"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+ROTATE_BYTES = 1 << 30   # bytes the rotating input sets touch together, at least
+
+# Kernel-trace averages (rocprofv3 --kernel-trace --stats) of the timed workloads,
+# recorded with the hash of the library's sources they were taken with.
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_{workload}.json")
+
+
+def library_source_hash() -> str:
+    """Hash of every source of the library (code only: comments and spacing are
+    ignored)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "compressed_attention_02_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if not f.endswith((".hip", ".hpp", ".cpp")):
+            continue
+        with open(os.path.join(src, f), encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(f.encode() + b"\0" + " ".join(code.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def parse_trace(stats_csv: str, workload: str, command: str) -> dict:
+    """Kernel-trace record from a rocprofv3 kernel_stats.csv: calls and average /
+    min / max duration (us) per kernel name."""
+    import csv
+    kernels = {}
+    with open(stats_csv, newline="") as fh:
+        for r in csv.DictReader(fh):
+            kernels[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": round(float(r["AverageNs"]) / 1e3, 3),
+                                  "min_us": round(float(r["MinNs"]) / 1e3, 3),
+                                  "max_us": round(float(r["MaxNs"]) / 1e3, 3)}
+    return {"workload": workload, "command": command, "kernels": kernels, "source_hash": library_source_hash()}
+
+
+def load_trace(workload: str):
+    try:
+        with open(TRACE_FILE.format(workload=workload)) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return d if d.get("source_hash") == library_source_hash() else None
+
 
 # HBM traffic of the dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE, then
 # WRITE_SIZE) of this script, calibrated on a plain device copy of known size made in
@@ -174,16 +225,17 @@ def cpu_baseline(cfg, g, budget_s: float) -> dict:
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    threads = cores
+    threads, vendor = cores, "unknown"
     try:
         from threadpoolctl import threadpool_info
         blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         if blas:
             threads = min(cores, int(blas[0]["num_threads"]))
+            vendor = f"{blas[0].get('internal_api', '?')} {blas[0].get('version', '')}".strip()
     except Exception:
         pass
     return {"value": round(n * cfg.batch / el, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "blas": vendor,
             "sample": f"{n} full decode steps (index_topk + decode, batch {cfg.batch}) of the same seeded "
                       f"input, fp64 NumPy oracle, {el:.1f} s"}
 
@@ -250,6 +302,35 @@ def bench_prefill(cfg, args):
     print(json.dumps(line), flush=True)
 
 
+def read_probe(dev) -> dict:
+    """Streaming read rate of this GPU: 32 MiB read once from a cold buffer (32
+    distinct windows of a 1 GiB buffer, the median), and 1 GiB read once (median of
+    3), each timed by events recorded on the stream right around the launch, like
+    the dominant kernel."""
+    import statistics
+    import torch
+    import compressed_attention_02_amd as V
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(8192 * 4, dtype=torch.int32, device=dev)
+    w = 32 << 20
+    V.timing_reset()
+    V.timing_enable("read_probe", 40)
+    torch.cuda.synchronize()
+    for k in range(32):   # 32 MiB: 1024 workgroups, eight 16-byte loads per thread
+        V.read_probe(buf[k * w:(k + 1) * w], sink, 1024)
+        torch.cuda.synchronize()
+    for _ in range(3):
+        V.read_probe(buf, sink, 8192)
+        torch.cuda.synchronize()
+    ms = V.timing_read("read_probe")
+    V.timing_reset()
+    small, big = statistics.median(ms[:32]), statistics.median(ms[32:35])
+    del buf, sink
+    return {"bytes_32mib_gbs": round(w / (small * 1e-3) / 1e9, 1), "bytes_32mib_us": round(small * 1e3, 3),
+            "bytes_1gib_gbs": round((1 << 30) / (big * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,14 +341,21 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
-    ap.add_argument("--one-launch", action="store_true",
-                    help="let the decode step run as one launch (workgroups wait for each other)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="BYTES",
                     help="after the timed region, three plain device copies of BYTES each "
                          "(reference dispatches for rocprofv3 --pmc byte counters)")
     ap.add_argument("--parse-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
                     help="turn the counter files of two --pmc runs into the traffic record")
+    ap.add_argument("--parse-trace", nargs=3, metavar=("STATS_CSV", "WORKLOAD", "COMMAND"),
+                    help="turn a rocprofv3 kernel_stats.csv into the kernel-trace record of WORKLOAD")
+    ap.add_argument("--no-probe", action="store_true")
     args = ap.parse_args()
+    if args.parse_trace:
+        rec = parse_trace(*args.parse_trace)
+        with open(TRACE_FILE.format(workload=args.parse_trace[1]), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return
     if args.parse_pmc:
         rec = parse_pmc(args.parse_pmc[0], args.parse_pmc[1], int(args.parse_pmc[2]))
         with open(TRAFFIC_FILE, "w") as fh:
@@ -289,15 +377,13 @@ def main():
     if cfg.tq != 1:
         bench_prefill(cfg, args)
         return
-    V.set_one_launch_step(args.one_launch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = synth.generate(cfg)
     base = to_device(g, dev)
     by = step_bytes(cfg)
     bytes_step = sum(by.values())
-    mall = 256 << 20
-    R = args.rotate or max(2, math.ceil(2.5 * mall / bytes_step))
+    R = args.rotate or max(2, math.ceil(ROTATE_BYTES / bytes_step))
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
     shape = LayerShape.of(cfg)
     steps = [LayerStep(shape, t) for t in sets]
@@ -334,6 +420,21 @@ def main():
     kern_ms = V.timing_read(dom) if not args.no_kernel_events else []
     V.timing_reset()
 
+    # single steps: a second pass over the same rotation, an event between every two
+    # steps (they cost the steps a little, so this pass does not give `value`)
+    import statistics
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        one(k)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    single = sorted(ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(args.steps))
+    q = statistics.quantiles(single, n=10, method="inclusive") if len(single) > 1 else single * 9
+    dist = {"median_us": round(statistics.median(single), 3), "p10_us": round(q[0], 3), "p90_us": round(q[-1], 3),
+            "steps": len(single), "note": "separate pass with an event between every two steps"}
+
     # warm (no rotation) figure, labelled separately
     for k in range(10):
         steps[0].step(stream)
@@ -352,6 +453,7 @@ def main():
     else:
         dom_bytes = by.get("hca_kv", 0) + by.get("swa_kv", 0) + by.get("csa_kv", 0)
         dom_name = "attn_bf16_kernel"
+    probe = None if args.no_probe else read_probe(dev)
     roof = None
     if kern_ms:
         avg = sum(kern_ms) / len(kern_ms)
@@ -363,6 +465,15 @@ def main():
                 "avg_launch_us": round(avg * 1e3, 3), "launches": len(kern_ms),
                 "timed_launches_note": "events on the first %d of the %d timed steps" % (len(kern_ms), args.steps),
                 "algorithmic_bytes_per_launch": dom_bytes}
+        if probe:
+            roof["frac_of_read_probe_32mib"] = round(ach / probe["bytes_32mib_gbs"], 4)
+        tr = load_trace(cfg.name)
+        if tr:   # the same kernel's duration in the committed kernel trace of this workload
+            hit = [v for k, v in tr["kernels"].items() if dom_name.split(" ")[0] in k]
+            if hit:
+                ktr = hit[0]["avg_us"]
+                roof["kernel_trace_avg_us"] = ktr
+                roof["frac_by_kernel_trace"] = round(dom_bytes / (ktr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     tok_s = cfg.batch / (ms * 1e-3)
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -373,7 +484,6 @@ def main():
                    "head_dim": cfg.dim, "csa_ratio": cfg.m, "topk": cfg.topk, "hca_ratio": cfg.m_hca,
                    "window": cfg.window, "indexer": f"{cfg.idx_heads}x{cfg.idx_dim}",
                    "step": cfg.timed, "rotating_input_sets": R,
-                   "step_form": "one_launch" if args.one_launch else "two_launch",
                    **({"shared_kv": True} if cfg.shared_kv else {}),
                    **({"rope_dims": cfg.rope_dims} if cfg.rope_dims else {}),
                    **({"q_norm": True} if cfg.q_norm else {}),
@@ -383,6 +493,9 @@ def main():
         "hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": bytes_step,
         "warm_ms_per_step_no_rotation": round(ms_warm, 5),
+        "single_step_us": dist,
+        "rotation_bytes": R * bytes_step,
+        "read_probe": probe,
         "roofline": roof,
     }
     if args.calibration_copy:

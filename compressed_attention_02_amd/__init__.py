@@ -34,9 +34,10 @@ BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ROPE_OUTPUT = 2       # v4a_attn_args.flags
 SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
-ABI_VERSION = 6
+ABI_VERSION = 7
+OP_COMPRESS, OP_INDEX_TOPK, OP_DECODE, OP_PREFILL_CHUNK, OP_DECODE_STEP = 0, 1, 2, 3, 4
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
-           "select_attn": 6, "qprep": 7}
+           "select_attn": 6, "qprep": 7, "read_probe": 8}
 
 
 class V4AttnError(RuntimeError):
@@ -81,6 +82,10 @@ class AttnArgs(ctypes.Structure):
                 ("vh_scale", Tensor), ("kr_scale", Tensor), ("vr_scale", Tensor)]
 
 
+class StepArgs(ctypes.Structure):
+    _fields_ = [("index", ctypes.c_void_p), ("attn", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -104,11 +109,10 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, ctypes.c_void_p]
         L.v4attn_decode_step_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs)]
         L.v4attn_decode_step_workspace.restype = ctypes.c_size_t
-        L.v4attn_set_wait_limit_us.argtypes = [ctypes.c_int64]
-        L.v4attn_set_one_launch_step.argtypes = [ctypes.c_int]
-        L.v4attn_set_one_launch_step.restype = None
+        L.v4attn_workspace_size.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.v4attn_workspace_size.restype = ctypes.c_size_t
         for name in ("v4attn_compress", "v4attn_index_topk", "v4attn_decode", "v4attn_prefill_chunk",
-                     "v4attn_decode_step", "v4attn_timing_enable", "v4attn_set_wait_limit_us"):
+                     "v4attn_decode_step", "v4attn_timing_enable"):
             getattr(L, name).restype = ctypes.c_int
         L.v4attn_status_string.argtypes = [ctypes.c_int]
         L.v4attn_status_string.restype = ctypes.c_char_p
@@ -120,6 +124,8 @@ def lib() -> ctypes.CDLL:
         L.v4attn_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.c_int]
         L.v4attn_timing_read.restype = ctypes.c_int
         L.v4attn_timing_reset.restype = None
+        L.v4attn_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.v4attn_read_probe.restype = ctypes.c_int
         if L.v4attn_abi_version() != ABI_VERSION:
             raise V4AttnError("libv4attn ABI version mismatch")
         _lib = L
@@ -231,13 +237,13 @@ def attn_args(q, pos0, o, *, lse=None, idx=None, kc=None, vc=None, kh=None, vh=N
               shared_kv=False, kc_scale=None, vc_scale=None, kh_scale=None, vh_scale=None, kr_scale=None,
               vr_scale=None) -> AttnArgs:
     """Caches given as uint8 hold FP8 E4M3 codes; each then comes with its fp32 [B, rows]
-    *_scale (one scale per row)."""
+    *_scale (one scale per row).  o may be fp32 or bf16 (out_dtype follows it)."""
     import torch
     B, Tq, H, d = q.shape
     if pos_max is None:
         raise V4AttnError("pos_max (host upper bound of the query positions) is required")
     fp8 = any(t is not None and t.dtype == torch.uint8 for t in (kc, vc, kh, vh, k_raw, v_raw))
-    return AttnArgs(ABI_VERSION, _dtype_code(q), F32, B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
+    return AttnArgs(ABI_VERSION, _dtype_code(q), _dtype_code(o), B, Tq, H, d, branch_mask, csa_ratio, hca_ratio,
                     window, topk, scale,
                     (BATCH_INVARIANT if batch_invariant else 0) | (ROPE_OUTPUT if rope_out else 0) |
                     (SHARED_KV if shared_kv else 0),
@@ -316,17 +322,13 @@ class DecodeStepCall:
         _check(self._fn(self._keep[0], self._keep[1], self._ws[0], self._ws[1], _stream(stream)))
 
 
+def workspace_size(op: int, args) -> int:
+    """v4attn_workspace_size: workspace bytes of an operation (OP_*) for its marshalled
+    arguments (CompressArgs, IndexArgs, AttnArgs, or StepArgs for OP_DECODE_STEP)."""
+    return int(lib().v4attn_workspace_size(int(op), ctypes.byref(args)))
+
+
 # ---------------------------------------------------------------- kernel timing
-def set_wait_limit_us(us: int) -> None:
-    """Bound of each wait between workgroups of the one-launch decode step."""
-    _check(lib().v4attn_set_wait_limit_us(int(us)))
-
-
-def set_one_launch_step(enable: bool) -> None:
-    """Let the decode step run as one launch when its grid fits the chip."""
-    lib().v4attn_set_one_launch_step(1 if enable else 0)
-
-
 def timing_enable(kernel: str, max_launches: int) -> None:
     _check(lib().v4attn_timing_enable(KERNELS[kernel], max_launches))
 
@@ -341,3 +343,9 @@ def timing_read(kernel: str, cap: int = 1 << 16) -> list:
 
 def timing_reset() -> None:
     lib().v4attn_timing_reset()
+
+
+def read_probe(buf, sink, workgroups: int, stream=None) -> None:
+    """v4attn_read_probe: read the device tensor buf once (HBM read-rate probe)."""
+    _check(lib().v4attn_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), int(workgroups),
+                                   _stream(stream)))

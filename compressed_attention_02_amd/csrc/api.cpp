@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -98,7 +97,7 @@ std::mutex g_tmu;
 Timing g_timing[V4A_K_COUNT];
 
 const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select", "attn", "merge",
-                                          "prefill", "select_attn", "qprep"};
+                                          "prefill", "select_attn", "qprep", "read_probe"};
 
 // ---------------------------------------------------------------- plans
 struct IndexPlan {
@@ -127,6 +126,7 @@ IndexPlan plan_index(const v4a_index_args* a) {
 struct AttnPlan {
   int64_t rows, n_keys, splits, kps;
   size_t off_q, ws_bytes;   // off_q: prepared bf16 queries (when qprep), after the partials
+  bool fits;                // the split count stays within what the merge takes
 };
 
 // bf16 queries with a norm gain or a rotation are prepared once per row
@@ -199,6 +199,7 @@ AttnPlan plan_attn(const v4a_attn_args* a) {
     P.ws_bytes = (size_t)(P.rows * P.splits * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
   }
   P.off_q = add_qprep(a, P.rows, P.ws_bytes);
+  P.fits = P.splits <= kAttnMaxSplits;
   return P;
 }
 
@@ -301,7 +302,7 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   if (!a) return fail(V4A_EINVAL, "args is NULL");
   if (a->abi_version != V4ATTN_ABI_VERSION) return fail(V4A_EINVAL, "abi_version %u != %u", a->abi_version, V4ATTN_ABI_VERSION);
   if (a->dtype != V4A_F32 && a->dtype != V4A_BF16) return fail(V4A_EINVAL, "dtype %d unknown", a->dtype);
-  if (a->out_dtype != V4A_F32) return fail(V4A_ENOTSUP, "out_dtype must be F32");
+  if (a->out_dtype != V4A_F32 && a->out_dtype != V4A_BF16) return fail(V4A_EINVAL, "out_dtype must be F32 or BF16");
   if (a->batch < 0) return fail(V4A_EINVAL, "batch < 0");
   if (prefill ? a->tq < 1 : a->tq != 1) return fail(V4A_EINVAL, prefill ? "tq must be >= 1" : "decode needs tq == 1");
   if (a->heads < 1 || a->heads > 128) return fail(V4A_ENOTSUP, "heads must be in 1..128");
@@ -341,7 +342,7 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   const int64_t hd = (int64_t)a->heads * a->dim;
   const int bq = a->batch;
   V4A_TRY(check_tensor("q", a->q, a->dtype, hd, bq));
-  V4A_TRY(check_tensor("o", a->o, V4A_F32, hd, bq));
+  V4A_TRY(check_tensor("o", a->o, a->out_dtype, hd, bq));
   if (a->lse.ptr) {
     if (!aligned(a->lse.ptr, 4)) return fail(V4A_EINVAL, "lse: not 4-byte aligned");
     if (a->lse.row_stride < a->heads) return fail(V4A_EINVAL, "lse: row_stride < heads");
@@ -417,7 +418,8 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
     p.vr = p.kr; p.vr_bs = p.kr_bs; p.vr_rs = p.kr_rs;
   }
   p.raw_start = a->raw_start; p.pos0 = a->pos0; p.sink = a->sink;
-  p.o = (float*)a->o.ptr; p.o_bs = a->o.batch_stride; p.o_rs = a->o.row_stride;
+  p.o = a->o.ptr; p.o_bs = a->o.batch_stride; p.o_rs = a->o.row_stride;
+  p.o_bf16 = a->out_dtype == V4A_BF16;
   p.lse = (float*)a->lse.ptr; p.lse_bs = a->lse.batch_stride; p.lse_rs = a->lse.row_stride;
   p.tq = a->tq; p.heads = a->heads; p.dim = a->dim;
   p.mask = a->branch_mask;
@@ -441,7 +443,10 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   V4A_TRY(validate_attn(a, prefill));
   if (a->batch == 0) return ok();
   const AttnPlan P = plan_attn(a);
-  if (P.splits > INT32_MAX || P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
+  if (!P.fits)
+    return fail(V4A_ENOTSUP, "%lld key splits per query exceed the merge's %d (batch-invariant plans split every 256 keys)",
+                (long long)P.splits, kAttnMaxSplits);
+  if (P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
   AttnP p = make_attn_params(a, P, ws);
   V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s, true));
@@ -523,13 +528,9 @@ struct StepPlan {
   bool csa;
   IndexPlan ix;
   int64_t rows, n_rest, kps_rest, s_rest, s_csa, s_total;
-  size_t off_attn, off_sync, off_q, ws_bytes;
+  size_t off_attn, off_q, ws_bytes;
+  bool fits;   // the split count stays within what the merge takes
 };
-
-// Bound of each wait of the one-launch step, in ticks of the 100 MHz clock.
-std::atomic<int64_t> g_wait_ticks{100 * 200000};  // 200 ms
-// Whether a decode step whose grid fits the chip runs as one launch.
-std::atomic<int> g_one_launch{0};
 
 StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
   StepPlan P{};
@@ -554,13 +555,11 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
     P.kps_rest = kAttnChunk;
   }
   P.s_total = P.s_rest + P.s_csa;
+  P.fits = P.s_total <= kAttnMaxSplits;
   if (P.csa) P.ix = plan_index(ix);
   P.off_attn = P.csa ? (size_t)round_up((int64_t)P.ix.ws_bytes, 256) : 0;
   P.ws_bytes = P.off_attn;
   if (P.s_total > 1) P.ws_bytes += (size_t)(P.rows * P.s_total * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
-  // per row {selection published, splits done} for the one-launch step
-  P.off_sync = (size_t)round_up((int64_t)P.ws_bytes, 256);
-  if (P.csa) P.ws_bytes = P.off_sync + (size_t)P.rows * kRowWords * sizeof(int);
   P.off_q = add_qprep(a, P.rows, P.ws_bytes);
   return P;
 }
@@ -585,6 +584,9 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   V4A_TRY(validate_step(ix, a));
   if (a->batch == 0) return ok();
   const StepPlan P = plan_step(ix, a);
+  if (!P.fits)
+    return fail(V4A_ENOTSUP, "%lld key splits per query exceed the merge's %d (batch-invariant plans split every 256 keys)",
+                (long long)P.s_total, kAttnMaxSplits);
   if (P.rows > 65535 * 1024LL) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(check_ws(ws, ws_bytes, P.ws_bytes));
   AttnPlan AP{};
@@ -631,46 +633,16 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     return V4A_OK;
   };
   if (P.csa) {
-    IndexLaunch IL = index_launch(ix, ws);
-    // selection and the selection-independent attention share one launch when the
-    // rows fit one score pass and the attention is bf16
-    // (rows of 512 join it too, but never in the one-launch form)
     if (combined) {
+      // selection and the selection-independent attention share one launch
+      IndexLaunch IL = index_launch(ix, ws);
       if (needs_qprep(a)) {
         IL.sp.prep = qprep_params(a, p, ws, P.off_q);
         IL.sp.prep_x = qprep_blocks(IL.sp.prep);
       }
-      // in the one-launch form (the whole grid resident at once, at most one
-      // workgroup per CU) the picks' attention and the merge join the launch; the
-      // rest of each row, done early, pre-merges in-kernel meanwhile
-      int* words = (int*)((char*)ws + P.off_sync);
-      AttnP csa_in = csa;
-      csa_in.head_groups = 1;   // the one-launch roles take every head
-      csa_in.sync = words;
-      const bool one_launch = !inv && a->dim <= 128 && g_one_launch.load() != 0 && P.s_rest >= 2 &&
-                              select_attn_grid((int)IL.P.rows, rest, csa_in, (int)P.rows) <= cu_count() &&
-                              P.s_total <= kStepMaxSplits;
-      const bool premerge = one_launch;
-      csa_in.sync = nullptr;
-      if (premerge) {
-        const int64_t ticks = g_wait_ticks.load();
-        rest.sync = words;
-        rest.wait_ticks = ticks;
-        rest.premerge = 1;
-        p.merge_lo = rest.merge_lo = csa.merge_lo = csa_in.merge_lo = (int)P.s_rest - 1;
-        IL.sp.zero = words;
-        IL.sp.n_zero = (int)(kRowWords * P.rows);
-        if (one_launch) {
-          csa_in.sync = words;
-          csa_in.wait_ticks = ticks;
-          csa_in.wait_idx = 1;
-          rest.final_merge = csa_in.final_merge = 1;
-        }
-      }
       V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
-      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, csa_in, (int)P.rows, s, V4A_K_SELECT_ATTN),
+      V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s, V4A_K_SELECT_ATTN),
                         "select+attention launch"));
-      if (one_launch) return ok();
     } else {
       V4A_TRY(run_index(ix, ws, P.ix.ws_bytes, s));
       if (P.s_rest > 0) V4A_TRY(attend(rest));
@@ -705,14 +677,6 @@ void timing_events(int k, hipEvent_t* start, hipEvent_t* stop) {
 extern "C" {
 
 uint32_t v4attn_abi_version(void) { return V4ATTN_ABI_VERSION; }
-
-void v4attn_set_one_launch_step(int enable) { g_one_launch.store(enable ? 1 : 0); }
-
-v4a_status v4attn_set_wait_limit_us(int64_t us) {
-  if (us < 0 || us > (int64_t)3600 * 1000000) return fail(V4A_EINVAL, "wait limit out of range");
-  g_wait_ticks.store(us * 100);
-  return V4A_OK;
-}
 
 const char* v4attn_status_string(v4a_status s) {
   switch (s) {
@@ -767,7 +731,8 @@ v4a_status v4attn_index_topk(const v4a_index_args* a, void* ws, size_t ws_bytes,
 
 size_t v4attn_decode_workspace(const v4a_attn_args* a) {
   if (validate_attn(a, false) != V4A_OK || a->batch == 0) return 0;
-  return plan_attn(a).ws_bytes;
+  const AttnPlan P = plan_attn(a);
+  return P.fits ? P.ws_bytes : 0;
 }
 
 v4a_status v4attn_decode(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -776,7 +741,8 @@ v4a_status v4attn_decode(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipS
 
 size_t v4attn_decode_step_workspace(const v4a_index_args* ix, const v4a_attn_args* a) {
   if (validate_step(ix, a) != V4A_OK || a->batch == 0) return 0;
-  return plan_step(ix, a).ws_bytes;
+  const StepPlan P = plan_step(ix, a);
+  return P.fits ? P.ws_bytes : 0;
 }
 
 v4a_status v4attn_decode_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, size_t ws_bytes,
@@ -786,11 +752,35 @@ v4a_status v4attn_decode_step(const v4a_index_args* ix, const v4a_attn_args* a, 
 
 size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* a) {
   if (validate_attn(a, true) != V4A_OK || a->batch == 0) return 0;
-  return plan_attn(a).ws_bytes;
+  const AttnPlan P = plan_attn(a);
+  return P.fits ? P.ws_bytes : 0;
+}
+
+size_t v4attn_workspace_size(int op, const void* args) {
+  if (!args) return 0;
+  switch (op) {
+    case V4A_OP_COMPRESS: return 0;
+    case V4A_OP_INDEX_TOPK: return v4attn_index_topk_workspace(static_cast<const v4a_index_args*>(args));
+    case V4A_OP_DECODE: return v4attn_decode_workspace(static_cast<const v4a_attn_args*>(args));
+    case V4A_OP_PREFILL_CHUNK: return v4attn_prefill_chunk_workspace(static_cast<const v4a_attn_args*>(args));
+    case V4A_OP_DECODE_STEP: {
+      const v4a_step_args* st = static_cast<const v4a_step_args*>(args);
+      return v4attn_decode_step_workspace(st->index, st->attn);
+    }
+  }
+  return 0;
 }
 
 v4a_status v4attn_prefill_chunk(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_attn(a, ws, ws_bytes, stream, true);
+}
+
+v4a_status v4attn_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4)) return fail(V4A_EINVAL, "buf / sink NULL or misaligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(V4A_EINVAL, "bytes must be a positive multiple of 16");
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(V4A_EINVAL, "workgroups out of range");
+  V4A_TRY(hip_check(launch_read_probe(buf, bytes, sink, workgroups, stream, V4A_K_READ_PROBE), "read probe launch"));
+  return ok();
 }
 
 v4a_status v4attn_timing_enable(int kernel, int max_launches) {

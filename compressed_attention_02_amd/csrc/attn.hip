@@ -39,7 +39,7 @@ constexpr int attn_waves_per_eu() {
 template <int NW, int HT, int D, int KP, bool QP, bool SKV, bool F8>
 __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
   __shared__ __align__(16) AttnSmem<D, SKV> sm;
-  attn_block<NW, HT, D, KP, false, QP, SKV, F8>(p, blockIdx.x, blockIdx.y, sm);
+  attn_block<NW, HT, D, KP, QP, SKV, F8>(p, blockIdx.x, blockIdx.y, sm);
 }
 
 template <int NW, int HT, int D, int KP, bool SKV, bool F8>
@@ -145,12 +145,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
     if (p.splits_total == 1) {
       float lse;
       const float f = finish_head(m_run, l_run, p.sink, head, &lse);
-      float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
+      const int64_t orow = (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         float a = acc[e] * f;
         if (p.rope_out) a = rope_back_pair(p, a, lane + 64 * e, pos);
-        orow[lane + 64 * e] = a;
+        store_out1(p.o, p.o_bf16, orow + lane + 64 * e, a);
       }
       if (lane == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
@@ -225,8 +225,8 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
 
 hipError_t launch_merge(const AttnP& p, int nrows, bool fixed_width, hipStream_t s, int tid) {
   if (p.splits_total > kMaxSplits) return hipErrorInvalidValue;
-  if (p.dim % kMergeCols != 0 || p.merge_lo < 0 || p.merge_lo >= p.splits_total) return hipErrorInvalidValue;
-  const int S = p.splits_total - p.merge_lo;
+  if (p.dim % kMergeCols != 0 || p.splits_total < 1) return hipErrorInvalidValue;
+  const int S = p.splits_total;
   auto fits = [&](int dw) {   // one batch of loads per thread, and enough workgroups
     return !fixed_width && p.dim % dw == 0 && (kMergeThreads / dw) * kMergeBatch >= S &&
            (int64_t)nrows * p.heads * (p.dim / dw) >= kMergeMinWorkgroups;

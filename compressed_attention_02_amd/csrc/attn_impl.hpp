@@ -79,8 +79,7 @@ __device__ __forceinline__ float rope_back_pair(const AttnP& p, float a, int ch,
 }
 
 // ------------------------------------------------------------------ merge
-// Combination of slots merge_lo .. splits_total - 1 of one (row, head)'s split
-// partials (U_s, m_s, l_s), m in base 2: weights exp2(m_s - max m), o = sum w_s U_s
+// Combination of the split partials of one (row, head) (U_s, m_s, l_s), m in base 2: weights exp2(m_s - max m), o = sum w_s U_s
 // / sum w_s l_s, for output columns [d0, d0 + DW).  NT threads; the statistics are
 // spread over the threads (kMaxSplits / NT each), the weighted sum over NT/DW thread
 // groups, each summing its splits in ascending order, and the groups are combined
@@ -94,10 +93,10 @@ __device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, in
   constexpr int G = NT / DW, NWV = NT / 64, KST = kMaxSplits / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = row / p.tq, i = row - b * p.tq;
-  const int ST = p.splits_total, lo = p.merge_lo, S = ST - lo, D = p.dim;
-  const float* ml = p.part_ml + (((int64_t)row * p.heads + head) * ST + lo) * 2;
+  const int S = p.splits_total, D = p.dim;
+  const float* ml = p.part_ml + ((int64_t)row * p.heads + head) * S * 2;
   const int c = tid % DW, g = tid / DW;
-  const float* po = p.part_o + (((int64_t)row * p.heads + head) * ST + lo) * D + d0 + c;
+  const float* po = p.part_o + ((int64_t)row * p.heads + head) * S * D + d0 + c;
   // this thread's first kMergeBatch partial values load together with the statistics
   float v[kMergeBatch];
 #pragma unroll
@@ -158,173 +157,8 @@ __device__ __forceinline__ void merge_head(const AttnP& p, int row, int head, in
     const float f = finish_head(M, l, p.sink, head, &lse);
     a *= f;
     if (p.rope_out) a = rope_back_pair(p, a, d0 + c, p.pos0[b] + i);
-    p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + d0 + c] = a;
+    store_out1(p.o, p.o_bf16, (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)head * D + d0 + c, a);
     if (c == 0 && d0 == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
-  }
-}
-
-// Merge of slots [lo, lo + n) of heads [h0, h0 + nh) of one row by one NT-thread
-// workgroup, with every load of a pass in flight at once: the workgroup's G = NT/D
-// column groups take up to G heads per pass, gph = G/heads groups per head, each
-// summing the slots lo + sub, lo + sub + gph, ... of its head in ascending order,
-// combined in LDS in group order.  The slot statistics of the pass load together
-// with the partials; the head maxima come from LDS integer maxima of
-// order-preserving keys (independent of order), the sums l from one wave per head
-// in a fixed lane order.  out_slot < 0 writes o and lse; otherwise the combination
-// (U relative to the new maximum, m, l) goes to slot out_slot.  With ok false
-// nothing is read and the outputs get NaN.  `lds` holds kMergeLds(NT, D, n) floats.
-constexpr int kMergeLoads = 48;     // partial values in flight per thread
-
-__host__ __device__ constexpr int kMergeLds(int nt, int d, int n) {
-  return 2 * (nt / d) + (nt / d) * n + ((nt / d) * n > nt ? (nt / d) * n : nt);
-}
-
-__device__ __forceinline__ uint32_t f2key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key2f(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-template <int NT>
-__device__ __forceinline__ void merge_heads(const AttnP& p, int row, int h0, int nh, int lo, int n, int out_slot,
-                                            bool ok, float* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = row / p.tq, i = row - b * p.tq;
-  const int ST = p.splits_total, D = p.dim, H = p.heads, G = NT / D;
-  const int g = tid / D, c = tid % D;
-  float* part_o = p.part_o + (int64_t)row * H * ST * D;
-  float* part_ml = p.part_ml + (int64_t)row * H * ST * 2;
-  if (!ok) {
-    for (int h = h0; h < h0 + nh; ++h) {
-      if (out_slot >= 0) {
-        if (tid == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)h * ST + out_slot) * 2) = make_float2(NAN, NAN);
-      } else if (tid < D) {
-        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + tid] = NAN;
-      }
-    }
-    return;
-  }
-  uint32_t* s_mk = reinterpret_cast<uint32_t*>(lds);
-  float* s_l = lds + G;
-  float* s_w = lds + 2 * G;
-  float* s_wl = s_w + G * n;   // w*l per item; later the group sums
-  constexpr int kStat = kStepMaxSplits * 8 / NT;  // statistics per thread (G <= 8)
-  for (int hb = 0; hb < nh; hb += G) {
-    const int nhp = min(G, nh - hb);
-    const int gph = G / nhp;
-    const int hs = min(g / gph, nhp - 1), sub = g % gph;
-    const bool act = g / gph < nhp;
-    const int h = h0 + hb + hs;
-    const int n_it = nhp * n;
-    const float* ph = part_o + ((int64_t)h * ST + lo) * D + c;
-    // 1) every load of the pass: this thread's partial values and slot statistics
-    const int nmine = (n - sub + gph - 1) / gph;
-    float v[kMergeLoads];
-#pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) v[u] = ph[(int64_t)min(sub + u * gph, n - 1) * D];
-    float2 ml[kStat];
-#pragma unroll
-    for (int u = 0; u < kStat; ++u) {
-      const int q = min(tid + u * NT, n_it - 1);
-      ml[u] = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(h0 + hb + q / n) * ST + lo + q % n) * 2);
-    }
-    if (tid < G) s_mk[tid] = 0u;
-    __syncthreads();
-    // 2) head maxima
-#pragma unroll
-    for (int u = 0; u < kStat; ++u) {
-      const int t = tid + u * NT;
-      if (t < n_it) atomicMax(&s_mk[t / n], f2key(ml[u].x));
-    }
-    __syncthreads();
-    // 3) slot weights and w*l per item, then l per head (wave hs, fixed order)
-#pragma unroll
-    for (int u = 0; u < kStat; ++u) {
-      const int t = tid + u * NT;
-      if (t < n_it) {
-        const float M = key2f(s_mk[t / n]);
-        const float w = (M == -INFINITY || ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
-        s_w[t] = w;
-        s_wl[t] = w * ml[u].y;
-      }
-    }
-    __syncthreads();
-    if (wave < nhp) {
-      float a = 0.f;
-      for (int sp = lane; sp < n; sp += 64) a += s_wl[wave * n + sp];
-      a = wave_sum(a);
-      if (lane == 0) s_l[wave] = a;
-    }
-    // 4) weighted sum of this thread's slots, ascending
-    float acc = 0.f;
-    for (int r0 = 0; r0 < nmine; r0 += kMergeLoads) {
-      if (r0 > 0) {
-#pragma unroll
-        for (int u = 0; u < kMergeLoads; ++u) v[u] = ph[(int64_t)min(sub + (r0 + u) * gph, n - 1) * D];
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeLoads; ++u)
-        if (r0 + u < nmine) acc = fmaf(s_w[hs * n + sub + (r0 + u) * gph], v[u], acc);
-    }
-    __syncthreads();
-    s_wl[tid] = acc;
-    __syncthreads();
-    if (act && sub == 0) {
-      float a = 0.f;
-      for (int q = 0; q < gph; ++q) a += s_wl[(g + q) * D + c];
-      const float M = key2f(s_mk[hs]), l = s_l[hs];
-      if (out_slot >= 0) {
-        part_o[((int64_t)h * ST + out_slot) * D + c] = a;
-        if (c == 0) *reinterpret_cast<float2*>(part_ml + ((int64_t)h * ST + out_slot) * 2) = make_float2(M, l);
-      } else {
-        float lse;
-        const float f = finish_head(M, l, p.sink, h, &lse);
-        a *= f;
-        if (p.rope_out) a = rope_back_pair(p, a, c, p.pos0[b] + i);
-        p.o[(int64_t)b * p.o_bs + (int64_t)i * p.o_rs + (int64_t)h * D + c] = a;
-        if (c == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + h] = lse;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------------ one-launch step sync
-// Thread 0 polls *w with relaxed agent-scope loads (no cache maintenance per poll)
-// until *w >= target, at most `ticks` of the 100 MHz clock, then takes one
-// agent-scope acquire; the workgroup learns the outcome through *flag.  After a
-// successful wait the workgroup's later loads see what the releasing workgroups
-// wrote before their release.
-__device__ __forceinline__ bool wg_wait_ge(const int* w, int target, int64_t ticks, int* flag) {
-  if (threadIdx.x == 0) {
-    const int64_t t0 = wall_clock64();
-    bool ok = true;
-    while (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (wall_clock64() - t0 > ticks) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *flag = ok;
-  }
-  __syncthreads();
-  const bool ok = *flag != 0;
-  __syncthreads();
-  return ok;
-}
-
-// Every wave waits for its own memory operations to complete, then thread 0
-// releases them at agent scope with its add to *w (or store of 1 when `set`).
-__device__ __forceinline__ void wg_release(int* w, bool set) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (set) __hip_atomic_store(w, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    else __hip_atomic_fetch_add(w, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -904,7 +738,6 @@ struct AttnSmem {
   float B0[kAttnChunk], B1[kAttnChunk];
   float S8[4 * kAttnChunk];   // FP8 caches: [parity][K, V] row scales of a chunk
   int idx[kMaxTopk];
-  int flag;
   __device__ uint16_t* K0() { return buf; }
   __device__ uint16_t* K1() { return buf + kRows; }
   __device__ uint16_t* V0() { return SKV ? buf : buf + 2 * kRows; }
@@ -924,7 +757,7 @@ struct AttnSmem {
 // QP: the output is rotated back at -pos (the query arrives normalised and rotated
 // from launch_qprep); without it the kernel carries none of that code.  SKV: every
 // entry is its own value (shared K = V rows, loaded once).
-template <int NW, int HT, int D, int KP, bool STEP = false, bool QP = false, bool SKV = false, bool F8 = false>
+template <int NW, int HT, int D, int KP, bool QP = false, bool SKV = false, bool F8 = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
   static_assert(!F8 || (!SKV && D <= 128), "FP8 caches: separate K and V rows of up to 128");
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
@@ -961,14 +794,9 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     for (int s = 0; s < KS; ++s)
       Qb[t][s] = *reinterpret_cast<const bf16x8_t*>(qrow + (tq * 16 + col) * D + s * 32 + grp * 8);
   }
-  // one-launch step: the picks are read only once the row's selection is published;
-  // if the wait gives up, the split attends nothing and reports NaN statistics
-  bool poison = false;
-  if constexpr (STEP)
-    if (p.sync && p.wait_idx) poison = !wg_wait_ge(p.sync + kRowWords * row, 1, p.wait_ticks, &sm.flag);
   const int64_t k_begin = p.key_lo + (int64_t)split * p.keys_per_split;
   const int64_t n_csa = (p.mask & 1u) ? p.topk : 0;
-  const int64_t n_idx = poison ? 0 : min(min(n_csa, p.key_hi), k_begin + (int64_t)p.keys_per_split) - k_begin;
+  const int64_t n_idx = min(min(n_csa, p.key_hi), k_begin + (int64_t)p.keys_per_split) - k_begin;
   const int32_t* ip = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs + k_begin;
   constexpr int IDX_PER = kMaxTopk / NT;  // ids per thread: n_idx <= topk <= kMaxTopk
   int ids[IDX_PER];
@@ -982,7 +810,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   const KeyList L = key_list(p, pos);
   RowKeys R;
   R.k_begin = k_begin;
-  R.k_end = poison ? R.k_begin : min(min(L.n_keys, p.key_hi), R.k_begin + (int64_t)p.keys_per_split);
+  R.k_end = min(min(L.n_keys, p.key_hi), R.k_begin + (int64_t)p.keys_per_split);
   R.n_csa = L.n_csa;
   R.hca_end = L.n_csa + L.e_vis;
   R.raw_off = L.w_lo - R.hca_end - raw0;
@@ -1075,7 +903,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     if (p.splits_total == 1) {
       float lse;
       const float f = finish_head(m_run[t], l, p.sink, head, &lse);
-      float* orow = p.o + (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
+      const int64_t orow = (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) {
         float ov[4] = {O[t][dt][0] * f, O[t][dt][1] * f, O[t][dt][2] * f, O[t][dt][3] * f};
@@ -1089,7 +917,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
             rot2(ov[2 * k2], ov[2 * k2 + 1], cs, sn, true);
           }
         }
-        *reinterpret_cast<float4*>(orow + (dt0 + dt) * 16 + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        store_out4(p.o, p.o_bf16, orow + (dt0 + dt) * 16 + 4 * grp, ov[0], ov[1], ov[2], ov[3]);
       }
       if (stats && grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
     } else {
@@ -1100,32 +928,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
         *reinterpret_cast<float4*>(po + (dt0 + dt) * 16 + 4 * grp) =
             make_float4(O[t][dt][0], O[t][dt][1], O[t][dt][2], O[t][dt][3]);
       if (stats && grp == 0)
-        *reinterpret_cast<float2*>(p.part_ml + slot * 2) = poison ? make_float2(NAN, NAN) : make_float2(m_run[t], l);
-    }
-  }
-
-  // (wide rows have no one-launch form: the host never sets sync for them)
-  if constexpr (STEP && !WIDE) if (p.sync) {
-    int* w = p.sync + kRowWords * row;
-    static_assert(kMergeLds(NT, D, kStepMaxSplits) <= 4 * 64 * (D / 4 + 2), "merge scratch fits the chunk buffers");
-    if (p.premerge) {
-      // the launch's splits of the row, done early, combine into its last slot
-      // while the rest of the step runs; heads are shared over the launch's splits
-      wg_release(w + 2, false);
-      const bool okr = wg_wait_ge(w + 2, p.splits, p.wait_ticks, &sm.flag);
-      const int hp = (p.heads + p.splits - 1) / p.splits;
-      const int hlo = min(p.heads, split * hp), h1 = min(p.heads, (split + 1) * hp);
-      merge_heads<NT>(p, row, hlo, h1 - hlo, p.split_base, p.splits, p.split_base + p.splits - 1, okr, sm.C);
-    }
-    if (p.final_merge) {
-      // count this split done, wait for all of the row's splits, then merge heads
-      // [j hp, (j + 1) hp) of the row from merge_lo on, j = this split's slot
-      wg_release(w + 1, false);
-      const bool ok = wg_wait_ge(w + 1, p.splits_total, p.wait_ticks, &sm.flag);
-      const int j = p.split_base + split;
-      const int hp = (p.heads + p.splits_total - 1) / p.splits_total;
-      const int hlo = min(p.heads, j * hp), h1 = min(p.heads, (j + 1) * hp);
-      merge_heads<NT>(p, row, hlo, h1 - hlo, p.merge_lo, p.splits_total - p.merge_lo, -1, ok, sm.C);
+        *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[t], l);
     }
   }
 }

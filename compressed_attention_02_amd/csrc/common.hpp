@@ -39,6 +39,19 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return r;
 }
 
+// Output stores: o is fp32, or bf16 rounded to nearest even (element offset off)
+__device__ __forceinline__ void store_out4(void* o, bool bf16, int64_t off, float a, float b, float c, float d) {
+  if (bf16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + off) =
+        make_uint2(f2bf(a) | (f2bf(b) << 16), f2bf(c) | (f2bf(d) << 16));
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + off) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store_out1(void* o, bool bf16, int64_t off, float a) {
+  if (bf16) reinterpret_cast<uint16_t*>(o)[off] = (uint16_t)f2bf(a);
+  else reinterpret_cast<float*>(o)[off] = a;
+}
+
 // ---- order-preserving key of an fp32 score ---------------------------------
 // Larger float -> larger unsigned key.  -0 is folded onto +0 so the two compare
 // equal, as they do as floats.

@@ -82,8 +82,6 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
   constexpr int QN = MT * 16 / RPI;         // wave loads of the query rows (heads)
   __shared__ __align__(16) unsigned char sK[NB][kTile * KROWB];
   __shared__ __align__(16) unsigned char sQ[MT * 16 * ROWB];
-  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
   if ((int)blockIdx.x < p.prep_x) {   // first (dispatched early): the attention queries of row y
     qprep_block(p.prep, p.row0 + blockIdx.y, blockIdx.x);
     return;
@@ -209,8 +207,6 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
 // One thread per block of the tile; the row's indexer queries and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
   extern __shared__ float s_q[];  // [heads*dim] then [heads]
-  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int t = threadIdx.x; t < p.n_zero; t += 256) p.zero[t] = 0;
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;

@@ -61,7 +61,6 @@ struct ScoreP {
   int heads, dim, ratio;
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
   int nrows;          // rows of the launch (set by launch_score)
-  int* zero; int n_zero;  // words workgroup (0, 0) clears before anything else (null: none)
   // bf16 kernel: workgroups x < prep_x of row y prepare that row's attention queries
   // instead (0: none); the score workgroups follow them
   QPrepP prep; int prep_x;
@@ -82,7 +81,6 @@ hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
 // ---------------------------------------------------------------- attention
 constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels
 constexpr int kWideTiles = 4;   // 16-head tiles per workgroup for rows wider than 128 (a wave pair each)
-constexpr int kStepMaxSplits = 256;  // splits per row the one-launch decode step merges in-kernel
 constexpr int kAttnMaxSplits = 1024;
 
 struct AttnP {
@@ -92,7 +90,8 @@ struct AttnP {
   const void* kh; const void* vh; int64_t kh_bs, kh_rs, vh_bs, vh_rs;
   const void* kr; const void* vr; int64_t kr_bs, kr_rs, vr_bs, vr_rs;
   const int64_t* raw_start; const int64_t* pos0; const float* sink;
-  float* o; int64_t o_bs, o_rs;
+  void* o; int64_t o_bs, o_rs;   // o: fp32, or bf16 (round to nearest even) with o_bf16
+  int o_bf16;
   float* lse; int64_t lse_bs, lse_rs;
   float* part_o;   // [rows][H][splits][d]: one head's splits contiguous for the merge
   float* part_ml;  // [rows][H][splits][2]
@@ -116,31 +115,20 @@ struct AttnP {
   // bf16 launches: heads split into head_groups groups of whole 16-head tiles, one
   // workgroup per (split, group); 1 = every workgroup takes all heads
   int head_groups;
-  // the merge (kernel or in-kernel) combines slots merge_lo .. splits_total - 1
-  int merge_lo;
-  // decode step only (null elsewhere): kRowWords words per row {idx ready, splits
-  // done, rest splits done}.  wait_idx: wait for the row's idx before reading it.
-  // premerge: the launch's workgroups count themselves done, wait for each other
-  // and combine the launch's slots of the row into its last slot.  final_merge:
-  // every workgroup of the row counts itself done, waits for all splits_total and
-  // merges its share of the heads from merge_lo on.  Each wait gives up after
-  // wait_ticks of the 100 MHz clock.
-  int* sync; int64_t wait_ticks; int wait_idx, premerge, final_merge;
 };
-constexpr int kRowWords = 4;
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
 
 // fixed_width: always 32 output columns per workgroup (batch-invariant plans: the
 // width sets how the splits are grouped in the sum)
 hipError_t launch_merge(const AttnP& p, int nrows, bool fixed_width, hipStream_t s, int tid);
 
-// selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x n_rows)
-// workgroups) in one launch; with csa (splits > 0, sync set) also the attention of
-// the picks and the merge, as one grid that must fit the chip at once
-hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, const AttnP& csa, int n_rows,
-                              hipStream_t s, int tid);
-// workgroups of the one-launch step; it needs every one resident at once
-int64_t select_attn_grid(int n_sel, const AttnP& ap, const AttnP& csa, int n_rows);
+// selection of rows [0, n_sel) of sp and bf16 attention of ap ((splits x head
+// groups x n_rows) workgroups) in one launch
+hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s, int tid);
+
+// ---------------------------------------------------------------- HBM read probe
+// reads bytes (a multiple of 16) of buf once; sink holds workgroups * 4 words
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- timing hooks
 // The next (start, stop) event pair of kernel id `tid` while timing is enabled for

@@ -50,6 +50,8 @@ class LayerShape:
     rope_base: float = 1e4
     q_norm: bool = False     # RMSNorm of the queries with the gain t["gq"]
     norm_eps: float = 1e-6
+    batch_invariant: bool = False  # V4A_BATCH_INVARIANT split plans
+    out_bf16: bool = False         # o stored in bf16 (round to nearest even) instead of fp32
 
     @classmethod
     def of(cls, cfg) -> "LayerShape":
@@ -70,7 +72,8 @@ class LayerStep:
         dev = t["q"].device
         self.B = B
         self.pos_max = shape.pos + shape.tq - 1
-        self.o = torch.empty((B, shape.tq, shape.heads, shape.dim), dtype=torch.float32, device=dev)
+        self.o = torch.empty((B, shape.tq, shape.heads, shape.dim),
+                             dtype=torch.bfloat16 if shape.out_bf16 else torch.float32, device=dev)
         self.lse = torch.empty((B, shape.tq, shape.heads), dtype=torch.float32, device=dev)
         self.idx = torch.full((B, shape.tq, shape.topk), -1, dtype=torch.int32, device=dev)
         self.ws_index = None
@@ -108,6 +111,7 @@ class LayerStep:
                     hca_ratio=s.m_hca, window=s.window, topk=s.topk, pos_max=self.pos_max,
                     shared_kv=s.shared_kv, rope_dims=s.rope_dims, rope_base=s.rope_base,
                     rope_out=s.rope_dims > 0, q_norm=t.get("gq") if s.q_norm else None, norm_eps=s.norm_eps,
+                    batch_invariant=s.batch_invariant,
                     kc_scale=t.get("kc_scale"), vc_scale=t.get("vc_scale"), kh_scale=t.get("kh_scale"),
                     vh_scale=t.get("vh_scale"), kr_scale=t.get("k_raw_scale"), vr_scale=t.get("v_raw_scale"))
 

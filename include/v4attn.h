@@ -34,7 +34,8 @@
  *    bytes (8 bf16 / 4 fp32 elements) except where a field says otherwise.
  *  * All pointers are device pointers unless the field says "host".
  *  * Ownership: the caller owns every buffer, including the workspace whose
- *    size the matching *_workspace() function returns.  The library allocates
+ *    size v4attn_workspace_size() (or the matching *_workspace() function)
+ *    returns.  The library allocates
  *    no device memory, keeps no pointer after a call returns, and holds no state
  *    between calls except a per-device property cache and the optional kernel
  *    timing events (v4attn_timing_*).
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 6u
+#define V4ATTN_ABI_VERSION 7u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -207,7 +208,8 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  * A query with no key and no sink gets o = 0, lse = -inf.  Disabled branches
  * (branch_mask) contribute nothing and their pointers may be NULL.
  *   dtype        F32 or BF16: q and every cache; BF16 needs heads % 16 == 0
- *   out_dtype    must be F32 (o and lse are fp32)
+ *   out_dtype    F32 or BF16: the type of o (bf16 rounds the fp32 result to
+ *                nearest even); lse is always fp32
  *   tq           query tokens per sequence: 1 for v4attn_decode, >= 1 for
  *                v4attn_prefill_chunk
  *   heads, dim   H <= 128; d = 64, 128 or 512 (bf16 at 512: V4A_SHARED_KV only)
@@ -221,7 +223,7 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *                NULL with V4A_SHARED_KV)
  *   k_raw, v_raw [batch][T_raw][d]; raw_start [batch] int64
  *   sink         fp32 [H] or NULL
- *   o            fp32 out [batch][tq][H][d] (row = query token)
+ *   o            out [batch][tq][H][d] (row = query token), of type out_dtype
  *   lse          fp32 out [batch][tq][H] (row = query token) or ptr == NULL
  *   q_norm       fp32 [d], 16-byte aligned: RMSNorm gain for every head's query, or NULL:
  *                q_h is used as g * q_h / sqrt(mean(q_h^2) + norm_eps) ([QbitAI]
@@ -245,9 +247,11 @@ v4a_status v4attn_index_topk(const v4a_index_args* args, void* workspace,
  *                v4attn_decode_step, its idx) depend only on its own sequence's
  *                inputs, bit for bit, not on the other sequences of the batch
  *                nor on pos_max.  Key splits then have a fixed size (256 keys;
- *                64 for the CSA picks of v4attn_decode_step), the CSA picks'
- *                attention takes one 16-head tile per workgroup and the step
- *                runs in two launches.
+ *                64 for the CSA picks of v4attn_decode_step) and the CSA picks'
+ *                attention takes one 16-head tile per workgroup.  A query may
+ *                then have at most 1024 splits (about 262k keys): larger
+ *                pos_max / hca_ratio give V4A_ENOTSUP before anything is
+ *                enqueued, and a zero workspace size.
  *                V4A_SHARED_KV: every entry is its own value (v = k in the
  *                formula above), read once; vc, vh and v_raw must be NULL.
  *                [QbitAI] 混合注意力机制, the partial RoPE paragraph (the KV
@@ -322,14 +326,8 @@ v4a_status v4attn_prefill_chunk(const v4a_attn_args* args, void* workspace,
  * CSA selection, so with a bf16 attention they are attended by the other
  * workgroups of the launch that runs the top-k selection (which needs one
  * workgroup per query row); the CSA keys are attended once the selection is
- * done, and one merge combines both.  Everything runs on `stream`, in order.
- * With v4attn_set_one_launch_step(1), when that launch, with one workgroup
- * per split of the CSA keys added, has no more workgroups than the device has
- * compute units, the CSA attention and the merge run inside it too: the
- * workgroups wait for each other on per-row words in the workspace (cleared
- * by the step's first kernel).  Each such wait is bounded
- * (v4attn_set_wait_limit_us); one that gives up leaves NaN in the o values
- * that depended on it instead of blocking the device.
+ * done, and one merge combines both.  Everything runs on `stream`, in order;
+ * no workgroup ever waits for another.
  *   index   arguments of v4attn_index_topk with tq == 1; its idx is read by
  *           the attention.  Ignored (may be NULL) when attn has no CSA branch.
  *   attn    arguments of v4attn_decode.  With CSA: batch, pos0 and pos_max
@@ -347,18 +345,35 @@ v4a_status v4attn_decode_step(const v4a_index_args* index,
                               size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * v4attn_workspace_size — workspace bytes of one call, by operation.
+ *   op    V4A_OP_*; args points to that operation's arguments:
+ *         V4A_OP_COMPRESS      v4a_compress_args   (always 0: no workspace)
+ *         V4A_OP_INDEX_TOPK    v4a_index_args
+ *         V4A_OP_DECODE        v4a_attn_args
+ *         V4A_OP_PREFILL_CHUNK v4a_attn_args
+ *         V4A_OP_DECODE_STEP   v4a_step_args (the pair v4attn_decode_step takes)
+ * Returns 0 for invalid or unsupported arguments, an unknown op or args NULL
+ * (the call itself then reports why), and for calls that need no workspace.  The
+ * buffer must be 256-byte aligned.  The same as the per-operation
+ * *_workspace() functions, which stay for callers that prefer them.
+ * ------------------------------------------------------------------------- */
+enum {
+  V4A_OP_COMPRESS = 0,
+  V4A_OP_INDEX_TOPK = 1,
+  V4A_OP_DECODE = 2,
+  V4A_OP_PREFILL_CHUNK = 3,
+  V4A_OP_DECODE_STEP = 4
+};
+typedef struct v4a_step_args {
+  const v4a_index_args* index;   /* may be NULL without the CSA branch */
+  const v4a_attn_args* attn;
+} v4a_step_args;
+size_t v4attn_workspace_size(int op, const void* args);
+
+/* ---------------------------------------------------------------------------
  * Status, version, diagnostics.
  * ------------------------------------------------------------------------- */
 const char* v4attn_status_string(v4a_status s);
-/* Whether v4attn_decode_step may run as one launch whose workgroups wait for
- * each other (default 0: two launches).  It needs every workgroup of the
- * launch resident at once, so leave it off where other work shares the GPU. */
-void v4attn_set_one_launch_step(int enable);
-/* Bound, in microseconds, of each wait between the workgroups of the one-launch
- * decode step (default 200000); applies to steps enqueued after the call.
- * V4A_EINVAL outside [0, 3600 s].  With 0, any wait not already satisfied gives
- * up, which is how the failure path is tested. */
-v4a_status v4attn_set_wait_limit_us(int64_t us);
 /* Thread-local text of the last error raised by this thread ("" if none). */
 const char* v4attn_last_error(void);
 uint32_t v4attn_abi_version(void);
@@ -381,9 +396,17 @@ enum {
   V4A_K_PREFILL = 5,
   V4A_K_SELECT_ATTN = 6, /* v4attn_decode_step: selection + HCA/window attention */
   V4A_K_QPREP = 7,       /* bf16 queries normalised / rotated once per row */
-  V4A_K_COUNT = 8
+  V4A_K_READ_PROBE = 8,  /* v4attn_read_probe */
+  V4A_K_COUNT = 9
 };
 v4a_status v4attn_timing_enable(int kernel, int max_launches);
+/* HBM read probe for benchmarks: reads `bytes` (a positive multiple of 16) of the
+ * device buffer `buf` (16-byte aligned) once with `workgroups` workgroups of 256
+ * threads (16-byte loads at a grid stride), and writes workgroups * 4 words of
+ * xor-folded data to `sink` so that no load is dropped.  Timed through
+ * V4A_K_READ_PROBE like the kernels above; it gives the streaming rate this GPU
+ * reaches, the ceiling the layer's kernels are compared with. */
+v4a_status v4attn_read_probe(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 int v4attn_timing_read(int kernel, float* ms, int cap);
 void v4attn_timing_reset(void);
 const char* v4attn_kernel_name(int kernel);

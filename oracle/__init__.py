@@ -46,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
-    "decode_keyset", "decode_query", "decode", "prefill", "lse_merge", "n_visible", "rms_norm",
+    "decode_keyset", "decode_query", "prefill", "lse_merge", "n_visible", "rms_norm",
     "rope", "compress_entries", "fp8_e4m3_decode", "fp8_rows",
 ]
 
@@ -295,23 +295,6 @@ def decode_query(q: np.ndarray, p: int, scale: float | None = None, sink=None, q
     if rope_out and rope_dims:
         o = rope(o, -p, rope_dims, rope_base)
     return o, lse
-
-
-def decode(q, pos, *, idx=None, scale=None, sink=None, raw_start=None, q_norm=None, norm_eps=1e-6, rope_dims=0,
-           rope_base=1e4, rope_out=False, **caches):
-    """Batched decode: q [B, H, d], pos [B], idx [B, k]; caches batched on axis 0.
-    Returns (o [B, H, d], lse [B, H])."""
-    B = q.shape[0]
-    os_, ls_ = [], []
-    for b in range(B):
-        kb = {k: (v[b] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in caches.items()}
-        o, lse = decode_query(q[b], int(pos[b]), scale=scale, sink=sink, q_norm=q_norm, norm_eps=norm_eps,
-                              rope_dims=rope_dims, rope_base=rope_base, rope_out=rope_out,
-                              idx=None if idx is None else idx[b],
-                              raw_start=0 if raw_start is None else int(raw_start[b]), **kb)
-        os_.append(o)
-        ls_.append(lse)
-    return np.stack(os_), np.stack(ls_)
 
 
 def prefill(q, pos0: int, idx, *, rows=None, scale=None, sink=None, raw_start: int = 0, q_norm=None,

@@ -22,6 +22,9 @@ Recipe (the same for every configuration):
   * raw K/V exist only for the positions the step touches (window + compressed
     span); the 1M-token history is never materialised, its compressed caches are
     drawn directly.  Caches hold at least one row even when no entry is visible;
+  * a ragged batch (decode without compression) puts sequence b's query at
+    pos - pos_back[b]; caches are sized for the longest sequence, raw buffers
+    start at each sequence's own window;
   * shared K = V configurations draw no V tensor (each entry is its own value);
     with a query RMSNorm its per-channel gain is U(0.5, 1.5) fp32;
   * FP8 indexer keys: each drawn row (needles planted as above) gets the scale
@@ -84,9 +87,11 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
                                for s in ss.spawn(len(_STREAMS)))))
     B, Tq, H, d = cfg.batch, cfg.tq, cfg.heads, cfg.dim
     HI, dI = cfg.idx_heads, cfg.idx_dim
+    if cfg.pos_back and (cfg.compress != "none" or Tq != 1 or min(cfg.pos_back) < 0):
+        raise ValueError("ragged positions: decode steps without compression, pos_back >= 0")
     out: dict = {}
-    out["pos"] = np.full(B, cfg.pos, dtype=np.int64)
-    out["raw_start"] = np.full(B, cfg.raw_start, dtype=np.int64)
+    out["pos"] = np.array([cfg.seq_pos(b) for b in range(B)], dtype=np.int64)
+    out["raw_start"] = np.array([cfg.seq_raw_start(b) for b in range(B)], dtype=np.int64)
     out["q"] = _normal(rngs["q"], (B, Tq, H, d), cfg.dtype)
 
     use_csa = bool(cfg.branches & CSA)
@@ -103,11 +108,11 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
         out["wi"] = rngs["wi"].uniform(0.0, 1.0, (B, Tq, HI)).astype(np.float32)
         ki = rngs["ki"].standard_normal((B, max(cfg.n_cap, 1), dI))
         needles = np.zeros((B, cfg.needles), dtype=np.int64)
-        # needles are planted among the blocks every query of the step can see
-        first_vis = (cfg.pos + 1) // cfg.m
+        # needles are planted among the blocks every query of the sequence can see
         for b in range(B):
             if cfg.needles == 0:
                 break
+            first_vis = (cfg.seq_pos(b) + 1) // cfg.m
             needles[b] = np.sort(rngs["needles"].choice(first_vis, cfg.needles, replace=False))
             if shared is not None:
                 wbar = out["wi"][b].astype(np.float64).mean(axis=0)

@@ -49,6 +49,9 @@ class LayerConfig:
     q_norm: bool = False  # RMSNorm of each head's query with a synthetic gain
     ki_fp8: bool = False  # indexer keys stored as FP8 E4M3 codes with one fp32 scale per row
     kv_fp8: bool = False  # every K/V cache stored the same way (caches drawn directly)
+    # ragged batch (decode steps without compression): sequence b's query sits at
+    # pos - pos_back[b % len(pos_back)] instead of pos; () keeps every query at pos
+    pos_back: tuple = ()
 
     # ---- derived shape helpers (pure bookkeeping, no method arithmetic) ----
     @property
@@ -64,6 +67,17 @@ class LayerConfig:
     @property
     def e_cap(self) -> int:
         return (self.last_pos + 1) // self.m_hca
+
+    def seq_pos(self, b: int) -> int:
+        """Position of sequence b's (first) query."""
+        return self.pos - (self.pos_back[b % len(self.pos_back)] if self.pos_back else 0)
+
+    def seq_raw_start(self, b: int) -> int:
+        """Absolute position of raw row 0 of sequence b (its own window start in a
+        ragged batch; raw_start otherwise)."""
+        if not self.pos_back:
+            return self.raw_start
+        return max(0, self.seq_pos(b) - self.window + 1)
 
     @property
     def raw_start(self) -> int:

@@ -27,9 +27,10 @@ def test_exports_every_declared_symbol():
     L = V.lib()
     names = _declared()
     assert len(names) >= 13
+    assert "v4attn_workspace_size" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 6
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 7
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -123,7 +124,7 @@ def test_index_rejects_tensors_and_workspace():
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("out_dtype", 1, ENOTSUP), ("tq", 2, EINVAL), ("heads", 40, ENOTSUP), ("dim", 96, ENOTSUP),
+    ("out_dtype", 2, EINVAL), ("tq", 2, EINVAL), ("heads", 40, ENOTSUP), ("dim", 96, ENOTSUP),
     ("branch_mask", 0, EINVAL), ("branch_mask", 9, EINVAL), ("csa_ratio", 0, EINVAL),
     ("window", -1, EINVAL), ("topk", 0, EINVAL), ("topk", 3000, ENOTSUP), ("scale", float("nan"), EINVAL),
     ("pos0", None, EINVAL), ("raw_start", None, EINVAL), ("sink", FAKE + 2, EINVAL),
@@ -213,24 +214,54 @@ def test_attention_rejects_huge_row_strides():
     assert r == ENOTSUP and msg
 
 
-def test_wait_limit_range():
-    L = V.lib()
-    assert L.v4attn_set_wait_limit_us(-1) == EINVAL
-    assert L.v4attn_set_wait_limit_us(3600 * 1000000 + 1) == EINVAL
-    assert L.v4attn_set_wait_limit_us(0) == 0
-    assert L.v4attn_set_wait_limit_us(200000) == 0
-    L.v4attn_set_one_launch_step(1)
-    L.v4attn_set_one_launch_step(0)
-
-
-def test_decode_step_workspace_holds_row_words():
-    # with CSA the step's workspace ends with four 32-bit words per row (selection
-    # published, splits done, rest splits done, spare) after the 256-byte aligned
-    # partials
+def test_workspace_size_by_operation():
+    # v4attn_workspace_size dispatches to the per-operation sizes
     L = V.lib()
     ix, a = good_index(), good_attn()
-    need = L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a))
-    assert need % 256 == a.batch * 16 % 256
+    ws = lambda op, x: V.workspace_size(op, x)
+    assert ws(V.OP_COMPRESS, good_compress()) == 0
+    assert ws(V.OP_INDEX_TOPK, ix) == L.v4attn_index_topk_workspace(ctypes.byref(ix)) > 0
+    assert ws(V.OP_DECODE, a) == L.v4attn_decode_workspace(ctypes.byref(a)) > 0
+    assert ws(V.OP_PREFILL_CHUNK, a) == L.v4attn_prefill_chunk_workspace(ctypes.byref(a)) > 0
+    st = V.StepArgs(ctypes.addressof(ix), ctypes.addressof(a))
+    assert ws(V.OP_DECODE_STEP, st) == L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a)) > 0
+    b = good_attn(branch_mask=6, kc=_T(None), vc=_T(None), idx=_T(None))
+    assert ws(V.OP_DECODE_STEP, V.StepArgs(None, ctypes.addressof(b))) > 0
+    assert ws(99, a) == 0
+    assert L.v4attn_workspace_size(V.OP_DECODE, None) == 0
+    assert ws(V.OP_DECODE, good_attn(dtype=9)) == 0
+
+
+def test_bf16_output_is_accepted_and_checked():
+    # out_dtype BF16: o holds bf16 (strides in bf16 elements, 16-byte multiples)
+    L = V.lib()
+    a = good_attn(out_dtype=V.BF16)
+    assert L.v4attn_decode_workspace(ctypes.byref(a)) > 0
+    assert _st(L.v4attn_decode, a, None, 0, None)[0] == EWORKSPACE   # past validation
+    r, msg = _st(L.v4attn_decode, good_attn(out_dtype=V.BF16, o=_T(FAKE, 8192 + 4, 8192)), None, 0, None)
+    assert r == EINVAL and "o" in msg
+    r, msg = _st(L.v4attn_decode, good_attn(out_dtype=3), None, 0, None)
+    assert r == EINVAL and "out_dtype" in msg
+
+
+def test_batch_invariant_split_limit_is_rejected_before_launch():
+    # batch-invariant plans split every 256 keys and the merge takes at most 1024
+    # splits: hca_ratio 1 at pos_max 300000 needs about 1173 splits.  The call must
+    # fail with ENOTSUP before anything is enqueued, and the workspace queries say 0.
+    L = V.lib()
+    a = good_attn(flags=V.BATCH_INVARIANT, hca_ratio=1, pos_max=300000)
+    ix = good_index(pos_max=300000)
+    assert L.v4attn_decode_workspace(ctypes.byref(a)) == 0
+    assert L.v4attn_prefill_chunk_workspace(ctypes.byref(a)) == 0
+    assert L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a)) == 0
+    r, msg = _st(L.v4attn_decode, a, FAKE, 1 << 40, None)
+    assert r == ENOTSUP and "splits" in msg
+    r, msg = _step(ix, a, FAKE, 1 << 40)
+    assert r == ENOTSUP and "splits" in msg
+    # the same shape without the flag is planned with longer splits
+    b = good_attn(hca_ratio=1, pos_max=300000)
+    assert L.v4attn_decode_workspace(ctypes.byref(b)) > 0
+    assert L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(b)) > 0
 
 
 def test_attention_rejects_unknown_flags():

@@ -134,24 +134,14 @@ def test_incremental_compress_bitwise():
         assert torch.equal(one_v[:, lo:hi], t[vn][:, lo:hi])
 
 
-@pytest.fixture(params=[False, True], ids=["two_launch", "one_launch"])
-def one_launch(request):
-    import compressed_attention_02_amd as V
-    V.set_one_launch_step(request.param)
-    yield request.param
-    V.set_one_launch_step(False)
-
-
 @pytest.mark.parametrize("name", ["c1_tiny_f32", "c2_small", "c3_small", "c4_small", "c2_b32"])
-def test_fused_decode_step(name, one_launch):
-    # v4attn_decode_step: the HCA + window attention shares the selection's launch
-    # (and in the one-launch form, when the grid fits the chip, so do the CSA
-    # attention and the merge: c2_b32 has too many workgroups for that and keeps
-    # the two-launch form); idx must equal the separate index_topk's bit for bit
+def test_fused_decode_step(name):
+    # v4attn_decode_step: the HCA + window attention shares the selection's launch;
+    # idx must equal the separate index_topk's bit for bit
     cfg = SMALL[name] if name != "c2_b32" else C.C2.small(name="c2_b32", batch=32, pos=4097, needles=4)
     if name == "c4_small":
         cfg = cfg.small(compress_tokens=1024 + (cfg.pos % cfg.m_hca))
-    print(f"[case] fused {name} one_launch={one_launch}", flush=True)
+    print(f"[case] fused {name}", flush=True)
     r = Run(cfg).run(fused=True).check_all()
     idx_fused = dev_to_np(r.step.idx).copy()
     o_fused = dev_to_np(r.step.o).copy()
@@ -161,41 +151,18 @@ def test_fused_decode_step(name, one_launch):
 
 
 @pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
-def test_fused_branch_subsets(mask, one_launch):
+def test_fused_branch_subsets(mask):
     cfg = C.C2.small(name=f"fmask{mask}", batch=2, pos=4097, branches=mask, needles=4)
-    print(f"[case] fused mask {mask} one_launch={one_launch}", flush=True)
+    print(f"[case] fused mask {mask}", flush=True)
     Run(cfg).run(fused=True).check_all()
 
 
-def test_fused_short_context_and_small_topk(one_launch):
+def test_fused_short_context_and_small_topk():
     # a row with no HCA entry yet and fewer visible blocks than k; k = 32 is a
     # single partial chunk
     cfg = C.C2.small(name="fshort", batch=2, pos=37, needles=0, topk=32, compress="all", compress_tokens=38)
-    print(f"[case] fused short one_launch={one_launch}", flush=True)
+    print("[case] fused short", flush=True)
     Run(cfg).run(fused=True).check_all()
-
-
-def test_step_wait_limit_gives_nan_then_recovers():
-    # the one-launch step's waits are bounded: with a zero bound the workgroups that
-    # wait for the selection or for the row's other splits give up at once and
-    # leave NaN in o (idx is unaffected); the default bound gives the normal result
-    import compressed_attention_02_amd as V
-    cfg = SMALL["c3_small"]
-    r = Run(cfg)
-    V.set_one_launch_step(True)
-    try:
-        V.set_wait_limit_us(0)
-        print("[case] wait limit 0", flush=True)
-        r.run(fused=True)
-        torch.cuda.synchronize()
-        assert np.isnan(dev_to_np(r.step.o)).any()
-    finally:
-        V.set_wait_limit_us(200000)
-    try:
-        print("[case] wait limit default", flush=True)
-        r.run(fused=True).check_all()
-    finally:
-        V.set_one_launch_step(False)
 
 
 @pytest.mark.parametrize("heads", [48, 80])

@@ -667,3 +667,43 @@ def test_fp8_rows_scale_and_scores():
     s = O.index_scores(qi, wi, rows)
     s0 = O.index_scores(qi, wi, O.fp8_e4m3_decode(codes))
     np.testing.assert_allclose(s, s0 * scales, rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------- bf16 decoding
+def test_bf16_to_f64_every_pattern():
+    """Every one of the 65536 bf16 patterns against two references that do not use the
+    oracle's "high half of a binary32 word" construction: the format's own field
+    decomposition (1 sign bit, 8 exponent bits with bias 127, 7 fraction bits;
+    exponent 0 subnormal, f * 2^-133; exponent 255 infinity or NaN), evaluated with
+    exact powers of two, and torch's bfloat16 -> float64 conversion.  NaN patterns
+    must decode to NaN (payloads are not compared)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    got = O.bf16_to_f64(bits.astype(np.uint16))
+    s = np.where(bits >> 15, -1.0, 1.0)
+    e = ((bits >> 7) & 0xFF).astype(np.int64)
+    f = (bits & 0x7F).astype(np.float64)
+    with np.errstate(over="ignore"):
+        mag = np.where(e == 0, f * 2.0 ** -133, (1.0 + f / 128.0) * np.exp2((e - 127).astype(np.float64)))
+    mag = np.where(e == 255, np.where(f == 0, np.inf, np.nan), mag)
+    ref = s * mag
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    tb = torch.from_numpy(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(tb), nan)
+    assert np.array_equal(got[~nan], tb[~nan])
+
+
+def test_bf16_to_f64_worked_values():
+    """A few patterns decoded by hand from the format definition."""
+    cases = {0x3F80: 1.0, 0xC040: -3.0, 0x4049: 3.140625, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x3C00: 2.0 ** -7, 0xBF00: -0.5, 0x7F80: math.inf,
+             0xFF80: -math.inf}
+    got = O.bf16_to_f64(np.array(list(cases), dtype=np.uint16))
+    assert got.tolist() == list(cases.values())
+    assert np.signbit(O.bf16_to_f64(np.array([0x8000], np.uint16)))[0]
+    assert np.isnan(O.bf16_to_f64(np.array([0x7FC0, 0xFF81], np.uint16))).all()
+    assert np.array_equal(O.as_f64(np.array([0x3F80], np.uint16), "bf16"), [1.0])
+    assert O.as_f64(np.array([0.1], np.float32), "f32")[0] == float(np.float32(0.1))

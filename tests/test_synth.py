@@ -1,5 +1,6 @@
 """The seeded input generator: shapes, determinism, rounding, planted structure."""
 import numpy as np
+import pytest
 import torch
 
 import oracle as O
@@ -48,3 +49,28 @@ def test_c1_needles_selected_by_oracle():
                        O.as_f64(g["ki"][0, :n], "f32"))
     sel = set(int(i) for i in O.topk_select(s, cfg.topk))
     assert set(int(i) for i in g["needles"][0]) <= sel
+
+
+def test_ragged_positions():
+    cfg = C.C2.small(name="rag", batch=3, pos=4097, needles=4, pos_back=(0, 1030, 3900))
+    g = synth.generate(cfg)
+    assert g["pos"].tolist() == [4097, 3067, 197]
+    assert g["raw_start"].tolist() == [4097 - 127, 3067 - 127, 197 - 127]
+    assert g["k_raw"].shape[1] == 128 and g["ki"].shape[1] == 4098 // 4
+    for b in range(3):   # needles only among the blocks the sequence's query sees
+        assert g["needles"][b].max() < (int(g["pos"][b]) + 1) // 4
+    with pytest.raises(ValueError):
+        synth.generate(C.C4.small(batch=2, pos_back=(0, 5)))   # compresses: uniform positions only
+
+
+def test_sample_rows_cover_the_chunk():
+    from tests.gpu_harness import sample_rows
+    cfg = C.C5
+    rows = [i for _, i in sample_rows(cfg)]
+    assert len(rows) == 256 == len(set(rows))
+    s = set(rows)
+    assert set(range(8)) <= s and set(range(cfg.tq - 8, cfg.tq)) <= s
+    csa = [i for i in range(cfg.tq) if (cfg.pos + i + 1) % cfg.m == 0]
+    assert set(csa[:16]) <= s and set(csa[-16:]) <= s
+    hca = [i for i in range(cfg.tq) if (cfg.pos + i + 1) % cfg.m_hca == 0]
+    assert len(hca) == 32 and set(hca) <= s and {i - 1 for i in hca} <= s
