@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_size_t
         L.v4attn_decode_step.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs), ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
+        L.v4attn_decode_step_noalloc.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+        L.v4attn_decode_step_noalloc.restype = ctypes.c_int
         L.v4attn_decode_step_workspace.argtypes = [ctypes.POINTER(IndexArgs), ctypes.POINTER(AttnArgs)]
         L.v4attn_decode_step_workspace.restype = ctypes.c_size_t
         L.v4attn_workspace_size.argtypes = [ctypes.c_int, ctypes.c_void_p]
@@ -302,6 +304,14 @@ def decode_step(qi, wi, ki, q, pos0, o, idx, *, ratio: int, topk: int, pos_max: 
     p, n = _ws_ptr(workspace)
     _check(lib().v4attn_decode_step(ia, aa, p, n, _stream(stream)))
     return workspace
+
+
+def decode_step_noalloc(qi, wi, ki, q, pos0, o, idx, *, ratio: int, topk: int, pos_max: int, stream=None,
+                        **attn_kw):
+    """v4attn_decode_step_noalloc: decode_step with the library's own static scratch
+    as workspace (nothing allocated; calls on one device must not overlap)."""
+    ia, aa = _step_args(qi, wi, ki, q, pos0, o, idx, ratio, topk, pos_max, attn_kw)
+    _check(lib().v4attn_decode_step_noalloc(ia, aa, _stream(stream)))
 
 
 class DecodeStepCall:

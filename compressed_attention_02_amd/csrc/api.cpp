@@ -659,6 +659,33 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
 
 }  // namespace
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of v4attn_decode_step_noalloc: one array per device, held from the
+// library's load until the process ends.  In host code its name is only a symbol;
+// its device address (per device) comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is what the kernels get.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+v4a_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = 0;
+  V4A_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    V4A_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(V4A_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return V4A_OK;
+}
+}  // namespace
+
 // ---------------------------------------------------------------- timing (namespace v4a)
 namespace v4a {
 void timing_events(int k, hipEvent_t* start, hipEvent_t* stop) {
@@ -748,6 +775,18 @@ size_t v4attn_decode_step_workspace(const v4a_index_args* ix, const v4a_attn_arg
 v4a_status v4attn_decode_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, size_t ws_bytes,
                               hipStream_t stream) {
   return run_step(ix, a, ws, ws_bytes, stream);
+}
+
+v4a_status v4attn_decode_step_noalloc(const v4a_index_args* ix, const v4a_attn_args* a, hipStream_t stream) {
+  V4A_TRY(validate_step(ix, a));
+  if (a->batch == 0) return ok();
+  const StepPlan P = plan_step(ix, a);
+  if (P.fits && P.ws_bytes > kScratchBytes)
+    return fail(V4A_ENOTSUP, "the step needs %zu bytes of scratch, more than the %zu this entry point holds",
+                P.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  V4A_TRY(scratch_ptr(&ws));
+  return run_step(ix, a, ws, kScratchBytes, stream);
 }
 
 size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* a) {

@@ -345,6 +345,23 @@ v4a_status v4attn_decode_step(const v4a_index_args* index,
                               size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * v4attn_decode_step_noalloc — v4attn_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same launches and results as
+ * v4attn_decode_step, bit for bit, with the workspace taken from a 64 MiB array
+ * the library holds in each device's memory (from its first use on that device
+ * until the process ends) instead of from the caller.  The call allocates and
+ * frees nothing.  Calls that need more than 64 MiB of workspace (what
+ * v4attn_decode_step_workspace returns) get V4A_ENOTSUP, before anything is
+ * enqueued.  Every call on a device shares that device's array and leaves its
+ * contents behind; no kernel expects it to hold anything on entry.  Calls whose
+ * work may overlap on one device (different streams, or different threads
+ * without ordering) race on the array and must not be issued.  Otherwise the
+ * arguments, errors and ordering are those of v4attn_decode_step.
+ * ------------------------------------------------------------------------- */
+v4a_status v4attn_decode_step_noalloc(const v4a_index_args* index, const v4a_attn_args* attn, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * v4attn_workspace_size — workspace bytes of one call, by operation.
  *   op    V4A_OP_*; args points to that operation's arguments:
  *         V4A_OP_COMPRESS      v4a_compress_args   (always 0: no workspace)

@@ -335,3 +335,16 @@ def test_fp8_cache_argument_checks():
     r, msg = _st(L.v4attn_decode, good_attn(**dict(f8, flags=V.SHARED_KV, vc=none, vh=none, v_raw=none), **scales),
                  None, 0, None)
     assert r == ENOTSUP
+
+
+def test_noalloc_step_validates_before_touching_the_device():
+    # invalid arguments are rejected on the host; a step whose workspace exceeds the
+    # 64 MiB static scratch gets ENOTSUP before any HIP call
+    L = V.lib()
+    r = L.v4attn_decode_step_noalloc(ctypes.byref(good_index(topk=256)), ctypes.byref(good_attn()), None)
+    assert r == EINVAL
+    a = good_attn(pos_max=1 << 26)      # 2^24 visible blocks: 64 MiB of scores per row
+    ix = good_index(pos_max=1 << 26)
+    assert L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a)) > 64 << 20
+    r = L.v4attn_decode_step_noalloc(ctypes.byref(ix), ctypes.byref(a), None)
+    assert r == ENOTSUP and "scratch" in L.v4attn_last_error().decode()
