@@ -39,7 +39,7 @@ constexpr int attn_waves_per_eu() {
 template <int NW, int HT, int D, int KP, bool QP, bool SKV, bool F8>
 __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
   __shared__ __align__(16) AttnSmem<D, SKV> sm;
-  attn_block<NW, HT, D, KP, QP, SKV, F8>(p, blockIdx.x, blockIdx.y, sm);
+  attn_block<NW, HT, D, KP, QP, SKV, F8>(p, blockIdx.x, blockIdx.y, sm, sm.idx);
 }
 
 template <int NW, int HT, int D, int KP, bool SKV, bool F8>

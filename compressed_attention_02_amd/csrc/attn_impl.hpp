@@ -723,9 +723,9 @@ __device__ __forceinline__ void run_chunks_wide(const RowKeys& R, const int* s_i
 }
 
 // LDS of one attention workgroup: two chunk buffers (K, V, mask; shared entries
-// (SKV) keep one row that serves as both) and the split's CSA ids.
+// (SKV) keep one row that serves as both); AttnSmem adds the split's CSA ids.
 template <int D, bool SKV = false>
-struct AttnSmem {
+struct AttnBuf {
   static constexpr int kRows = kAttnChunk * D;
   union {
     uint16_t buf[(SKV ? 2 : 4) * kRows];
@@ -737,11 +737,14 @@ struct AttnSmem {
   float X[D > 128 ? kWideTiles * 4 * 64 * 4 : 1];
   float B0[kAttnChunk], B1[kAttnChunk];
   float S8[4 * kAttnChunk];   // FP8 caches: [parity][K, V] row scales of a chunk
-  int idx[kMaxTopk];
   __device__ uint16_t* K0() { return buf; }
   __device__ uint16_t* K1() { return buf + kRows; }
   __device__ uint16_t* V0() { return SKV ? buf : buf + 2 * kRows; }
   __device__ uint16_t* V1() { return SKV ? buf + kRows : buf + 3 * kRows; }
+};
+template <int D, bool SKV = false>
+struct AttnSmem : AttnBuf<D, SKV> {
+  int idx[kMaxTopk];
 };
 
 // The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
@@ -757,8 +760,12 @@ struct AttnSmem {
 // QP: the output is rotated back at -pos (the query arrives normalised and rotated
 // from launch_qprep); without it the kernel carries none of that code.  SKV: every
 // entry is its own value (shared K = V rows, loaded once).
+// s_idx: the LDS array of the split's CSA ids (the split's slot t at s_idx[t]); with
+// ids_ready the caller has filled it already (and synchronised), else they are
+// loaded from p.idx here.
 template <int NW, int HT, int D, int KP, bool QP = false, bool SKV = false, bool F8 = false>
-__device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnSmem<D, SKV>& sm) {
+__device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnBuf<D, SKV>& sm, int* s_idx,
+                                           bool ids_ready = false) {
   static_assert(!F8 || (!SKV && D <= 128), "FP8 caches: separate K and V rows of up to 128");
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
@@ -767,7 +774,6 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   const int hgn = p.head_groups, split = xs / hgn, hgi = xs - split * hgn;
   constexpr int TW = WIDE ? kWideTiles : NW / KP;   // head tiles of one pass
   constexpr int NT = NW * 64, CH = kAttnChunk, KS = D / 32, DT = D / 16;
-  int* s_idx = sm.idx;
   const int b = row / p.tq, i = row - b * p.tq;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -800,7 +806,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   const int32_t* ip = p.idx + (int64_t)b * p.idx_bs + (int64_t)i * p.idx_rs + k_begin;
   constexpr int IDX_PER = kMaxTopk / NT;  // ids per thread: n_idx <= topk <= kMaxTopk
   int ids[IDX_PER];
-  if (n_idx > 0) {
+  if (!ids_ready && n_idx > 0) {
 #pragma unroll
     for (int u = 0; u < IDX_PER; ++u) ids[u] = ip[min((int64_t)(u * NT + tid), n_idx - 1)];
   }
@@ -835,7 +841,7 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     R.khs = (p.mask & 2u) ? p.khs + (int64_t)b * p.khs_bs : fb; R.vhs = (p.mask & 2u) ? p.vhs + (int64_t)b * p.vhs_bs : fb;
     R.krs = (p.mask & 4u) ? p.krs + (int64_t)b * p.krs_bs : fb; R.vrs = (p.mask & 4u) ? p.vrs + (int64_t)b * p.vrs_bs : fb;
   }
-  if (n_idx > 0) {
+  if (!ids_ready && n_idx > 0) {
 #pragma unroll
     for (int u = 0; u < IDX_PER; ++u)
       if (u * NT + tid < n_idx) s_idx[u * NT + tid] = ids[u];

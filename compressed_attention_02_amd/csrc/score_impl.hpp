@@ -1,0 +1,191 @@
+// Device code of the indexer score on MFMA (bf16 or FP8 keys), shared by the score
+// kernel of v4attn_index_topk and the decode step's first launch.  The design notes
+// are at the top of index.hip.
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+#include "select_impl.hpp"
+
+namespace v4a {
+
+// ------------------------------------------------------------------ score, bf16 MFMA
+// S = QI (heads x d_I) . KI^T (d_I x blocks) on v_mfma_f32_16x16x32_bf16.
+// Operand layout (wave64): lane l = 16*grp + col.  A (16 heads x 32 dims): lane holds
+// head col, 8 dims of group grp; B (32 dims x 16 blocks): lane holds block col, the
+// same 8 dims; C (16 heads x 16 blocks): lane holds block col, heads 4*grp + e.
+// The dims a lane group carries only have to agree between A and B.
+//
+// A workgroup of NW waves walks the tiles x, x + wgs_per_row, ... of its row (x its
+// index among the row's score workgroups), a tile being 64 * NW indexer keys, 64 per
+// wave.  A tile goes from HBM straight into LDS (16 bytes per lane per load; lane
+// l's piece lands at base + 16 l), unpadded, with the 16-byte pieces of row r
+// permuted by XOR with swz_ki(r) so that both the loads and the B-fragment reads
+// (16 rows, one piece column) are free of bank conflicts.  QI and the head weights
+// stay in registers.  With NB = 2 the next tile loads while the current one is
+// scored.  Each wave scores its 64 keys: ReLU, w-weighted head sum (row swaps across
+// the 4 lane groups), then its top-4 report, stored at the wave's global index
+// (block / 64), whatever NW is.
+template <int DI> __device__ __forceinline__ int swz_ki(int r) { return DI == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// FP8 key rows (DI bytes, DI/16 pieces): rows r that share a 256-byte bank offset
+// (r mod 256/DI) get distinct piece XORs, so the 8-byte fragment reads of 16 rows
+// at one logical piece are free of bank conflicts
+template <int DI> __device__ __forceinline__ int swz_k8(int r) { return (r / (256 / DI)) % (DI / 16); }
+
+// 8 FP8 E4M3 codes (bytes of v, low first) -> 8 bf16, exactly (every E4M3 value,
+// subnormals and NaN included, is a bf16 value): gfx950's packed conversion with a
+// unit scale, two codes per instruction
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1),
+                                                 __builtin_bit_cast(uint32_t, w2), __builtin_bit_cast(uint32_t, w3)));
+}
+
+// FP8: the key rows are FP8 E4M3 codes with one fp32 scale per row; they stay codes
+// in LDS (half the bytes), each fragment is decoded to bf16 exactly, and the row's
+// scale multiplies its 16 dot products before the ReLU.
+// LDS of a score workgroup
+template <int NW, int MT, int KS, int NB, bool FP8>
+struct ScoreSmem {
+  static constexpr int DI = KS * 32;
+  static constexpr int KROWB = FP8 ? DI : DI * 2;   // LDS bytes per key row
+  unsigned char sK[NB][64 * NW * KROWB];
+  unsigned char sQ[MT * 16 * DI * 2];
+};
+
+// Workgroup x (of the row's p.wgs_per_row) of launch row lr.
+template <int NW, int MT, int KS, int NB, bool FP8>
+__device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, ScoreSmem<NW, MT, KS, NB, FP8>& sm) {
+  constexpr int DI = KS * 32;
+  constexpr int TILE = 64 * NW;              // keys per workgroup tile
+  constexpr int ROWB = DI * 2;               // LDS bytes per query row
+  constexpr int CPR = DI * 2 / 16;           // 16-byte pieces per query row
+  constexpr int RPI = 64 / CPR;              // query rows per wave load
+  constexpr int KROWB = FP8 ? DI : DI * 2;   // LDS bytes per key row
+  constexpr int KCPR = KROWB / 16;           // 16-byte pieces per key row
+  constexpr int KRPI = 64 / KCPR;            // key rows per wave load
+  constexpr int IPW = 64 / KRPI;             // loads per wave per tile (its own 64 rows)
+  constexpr int QN = MT * 16 / RPI;         // wave loads of the query rows (heads)
+  auto& sK = sm.sK;
+  unsigned char* sQ = sm.sQ;
+  int b, i;
+  int64_t pos;
+  row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
+  const int64_t nvis = uniform_i64((pos + 1) / p.ratio);
+  const int64_t ntile_row = (nvis + TILE - 1) / TILE;
+  int64_t tile = x;
+  const int64_t stride = p.wgs_per_row;   // score workgroups of the row
+  if (tile >= ntile_row) return;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // key rows in bytes (row strides are in elements: 2 bytes for bf16, 1 for FP8)
+  const unsigned char* ki = reinterpret_cast<const unsigned char*>(p.ki) + (int64_t)b * p.ki_bs * (FP8 ? 1 : 2);
+  const int64_t ki_rb = p.ki_rs * (FP8 ? 1 : 2);
+
+  // rows past n_vis re-read the last visible row; their scores are dropped
+  auto issue = [&](int64_t t, unsigned char* buf) {
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int r0 = (wave * IPW + u) * KRPI;
+      const int r = r0 + lane / KCPR;
+      const int64_t j = min(t * TILE + r, nvis - 1);
+      const int x = FP8 ? swz_k8<DI>(r) : swz_ki<DI>(r);
+      lds_load16(ki + j * ki_rb + ((lane % KCPR) ^ x) * 16, lds_addr(buf + r0 * KROWB));
+    }
+  };
+  // the query rows go to LDS once per workgroup (laid out like the key rows), ahead
+  // of the first tile; the waves read their fragments from there
+  {
+    const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
+#pragma unroll
+    for (int u = wave; u < QN; u += NW) {
+      const int r = u * RPI + lane / CPR;
+      lds_load16(qi + r * DI + ((lane % CPR) ^ swz_ki<DI>(r)) * 8, lds_addr(sQ + u * RPI * ROWB));
+    }
+  }
+  float w[MT][4];
+  {
+    const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 wq = *reinterpret_cast<const f32x4*>(wi + mt * 16 + 4 * grp);
+      w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
+    }
+  }
+  // the tile loads go out last: the query rows and the weights are the oldest loads
+  issue(tile, sK[0]);
+  if (NB == 2 && tile + stride < ntile_row) issue(tile + stride, sK[NB - 1]);
+  bf16x8_t A[MT][KS];
+  bool have_q = false;
+
+  float* sc = p.scores + (int64_t)lr * p.sc_rs;
+  const int kx = swz_ki<DI>(col);          // rows 16u + col of a wave share col's XOR
+  const int kx8 = swz_k8<DI>(col);         // (the same holds for the FP8 layout)
+  for (int c = 0; tile < ntile_row; tile += stride, ++c) {
+    const unsigned char* buf = sK[NB == 2 ? (c & 1) : 0];
+    const bool next = NB == 2 && tile + stride < ntile_row;
+    if (!have_q) {
+      // every wave's share of the query rows is in LDS once the loads issued before
+      // the tiles are done (vmcnt counts in issue order); then the query fragments:
+      // row mt*16 + col, piece 4s + grp (the rows share col's XOR)
+      if (next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          A[mt][s] = *reinterpret_cast<const bf16x8_t*>(sQ + (mt * 16 + col) * ROWB + (((s * 4 + grp) ^ kx) * 16));
+      have_q = true;
+    }
+    // a wave reads only the key rows it loaded itself, so its own loads are all it
+    // waits for (no barrier); the next tile may stay in flight
+    if (next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int64_t tile0 = tile * TILE;
+    float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
+    float kscale = 1.f;     // FP8: the scale of that key's row (rows past n_vis: the last row's)
+    if constexpr (FP8)
+      kscale = p.ki_scale[(int64_t)b * p.ks_bs + min(tile0 + wave * 64 + lane, nvis - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = wave * 64 + u * 16 + col;     // key row of this lane's column
+      float part = 0.f;
+      bf16x8_t Bv[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (FP8)   // elements s*32 + grp*8: piece 2s + grp/2, half grp%2
+          Bv[s] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(buf + t * KROWB + (((2 * s + (grp >> 1)) ^ kx8) * 16) +
+                                                                (grp & 1) * 8));
+        else
+          Bv[s] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s * 4 + grp) ^ kx) * 16));
+      }
+      // FP8: the scale of this lane's key column (key u*16 + col of the wave)
+      const float cs = FP8 ? __shfl(kscale, u * 16 + col) : 1.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s], Bv[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(FP8 ? acc[e] * cs : acc[e], 0.f), part);
+      }
+      part = col_sum4(part);
+      if (grp == u) mine = part;
+    }
+    const int64_t j = tile0 + wave * 64 + lane;
+    if (j < nvis) sc[j] = mine;
+    const int64_t gw = tile * NW + wave;   // global wave: blocks 64 gw .. 64 gw + 63
+    wave_top(score_key(mine), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + gw * kWaveTop,
+             p.rep_info + (int64_t)lr * p.info_rs + gw);
+    // the buffer is reloaded next, each wave into the rows it has just read
+    if (NB == 2 && tile + 2 * stride < ntile_row)
+      issue(tile + 2 * stride, sK[NB == 2 ? (c & 1) : 0]);
+  }
+}
+
+}  // namespace v4a

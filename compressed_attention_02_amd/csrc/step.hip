@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
   }
   const int a = blk - n_sel;
   const int xw = ap.splits * ap.head_groups;   // (split, head group) workgroups per row
-  attn_block<8, 1, D, KP, QP, D == 512, F8>(ap, a % xw, a / xw, sm.attn);
+  attn_block<8, 1, D, KP, QP, D == 512, F8>(ap, a % xw, a / xw, sm.attn, sm.attn.idx);
 }
 
 template <int D, int KP>
@@ -49,17 +49,18 @@ static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, dim3 g, hip
 
 hipError_t launch_select_attn(const SelectP& sp, int n_sel, const AttnP& ap, int n_rows, hipStream_t s, int tid) {
   const int64_t n = (int64_t)n_sel + (int64_t)ap.splits * ap.head_groups * n_rows;
+  const int ntile = ap.heads / 16 / max(ap.head_groups, 1);   // head tiles per workgroup
   if (n > INT32_MAX || ap.splits < 1 || ap.heads < 16 || ap.heads > 128 || ap.heads % 16 != 0 ||
-      (ap.dim != 64 && ap.dim != 128 && !(ap.dim == 512 && ap.skv)) || (ap.dim != 512 && ap.head_groups != 1) ||
-      ap.head_groups < 1)
+      (ap.dim != 64 && ap.dim != 128 && !(ap.dim == 512 && ap.skv)) || ap.head_groups < 1 ||
+      ap.heads % (16 * ap.head_groups) != 0)
     return hipErrorInvalidValue;
   const dim3 g((unsigned)n);
   if (ap.dim == 512) {
     // shared rows of 512: a wave pair per head tile, head groups of kWideTiles tiles
-    if (ap.heads / 16 / ap.head_groups > kWideTiles) return hipErrorInvalidValue;
+    if (ntile > kWideTiles) return hipErrorInvalidValue;
     launch_sa<512, 1>(sp, n_sel, ap, g, s, tid);
-  } else if (ap.heads <= 64) {
-    // up to 64 heads, two waves per head tile take half of every chunk's keys each
+  } else if (ntile <= 4) {
+    // up to 4 head tiles, two waves per head tile take half of every chunk's keys each
     if (ap.dim == 64) launch_sa<64, 2>(sp, n_sel, ap, g, s, tid);
     else launch_sa<128, 2>(sp, n_sel, ap, g, s, tid);
   } else {

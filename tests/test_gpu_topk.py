@@ -88,3 +88,83 @@ def test_small_rows_and_padding():
         idx, _ = _run(qi, wi, kb, pos, k)
         s = _scores(qi, wi, kb[:, :n_vis])
         check_topk_row(idx[0, 0], s, k, f"n_vis={n_vis}")
+
+
+# ---------------------------------------------------------------- through the decode step
+def _run_step(qi, wi, ki, pos, k, heads=128, d=128, m=4, W=128):
+    """The same selection through v4attn_decode_step (its candidates per group of
+    waves, the exact top-k in the picks' launch, the full-report fallback)."""
+    B, n = qi.shape[0], ki.shape[1]
+    rng = np.random.default_rng(7)
+    e = (int(pos.max()) + 1) // 128 + 1
+
+    def bf(shape):
+        return synth.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+    g = {"qi": qi, "wi": wi, "ki": ki, "pos": pos, "q": bf((B, 1, heads, d)), "kc": bf((B, n, d)),
+         "vc": bf((B, n, d)), "kh": bf((B, e, d)), "vh": bf((B, e, d)), "k_raw": bf((B, W, d)),
+         "v_raw": bf((B, W, d)), "raw_start": (pos - W + 1).astype(np.int64)}
+    t = to_device(g)
+    idx = torch.full((B, 1, k), -7, dtype=torch.int32, device="cuda")
+    o = torch.empty((B, 1, heads, d), dtype=torch.float32, device="cuda")
+    V.decode_step(t["qi"], t["wi"], t["ki"], t["q"], t["pos"], o, idx, ratio=m, topk=k, pos_max=int(pos.max()),
+                  kc=t["kc"], vc=t["vc"], kh=t["kh"], vh=t["vh"], k_raw=t["k_raw"], v_raw=t["v_raw"],
+                  raw_start=t["raw_start"], hca_ratio=128, window=W)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(dev_to_np(o)))
+    return dev_to_np(idx)
+
+
+@pytest.mark.parametrize("distinct", [1, 3])
+def test_step_exact_ties(distinct):
+    # every group's bound equals the threshold: the picks' launch falls back to the
+    # selection over the reports (and, for one distinct row, over the scores)
+    n, k = 32768, 512
+    qi, wi, ki, pos, rng = _inputs(n)
+    rows = rng.standard_normal((distinct, ki.shape[2]))
+    ki[0] = rows[rng.integers(0, distinct, n)]
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    print(f"[case] step ties distinct={distinct}", flush=True)
+    idx = _run_step(qi, wi, kb, pos, k)
+    assert list(idx[0, 0]) == list(O.topk_select(_scores(qi, wi, kb), k))
+
+
+def test_step_clustered_winners():
+    # 900 winners in about four tiles: their group keeps 64 and its bound reaches T
+    n, k = 262144, 1024
+    qi, wi, ki, pos, rng = _inputs(n, seed=1)
+    u = (wi[0, 0].astype(np.float64)[:, None] * O.as_f64(qi[0, 0], "bf16")).sum(0)
+    u /= np.linalg.norm(u)
+    ki[0, 5000:5900] += 4.0 * 8.0 * u
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    print("[case] step clustered", flush=True)
+    idx = _run_step(qi, wi, kb, pos, k)
+    assert np.array_equal(idx, _run(qi, wi, kb, pos, k)[0])
+    check_topk_row(idx[0, 0], _scores(qi, wi, kb), k, "step clustered")
+
+
+@pytest.mark.parametrize("heads", [64, 128])
+def test_step_max_topk_and_batch(heads):
+    # k = 2048: 64 groups of candidates, a pool of 4096
+    n, k = 65536, 2048
+    qi, wi, ki, pos, rng = _inputs(n, B=3, seed=2)
+    pos[1] -= 4 * 777 + 2
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    print(f"[case] step k=2048 heads={heads}", flush=True)
+    idx = _run_step(qi, wi, kb, pos, k, heads=heads)
+    assert np.array_equal(idx, _run(qi, wi, kb, pos, k)[0])
+    for b in range(3):
+        nv = O.n_visible(int(pos[b]), 4)
+        s = O.index_scores(O.as_f64(qi[b, 0], "bf16"), wi[b, 0].astype(np.float64), O.as_f64(kb[b, :nv], "bf16"))
+        check_topk_row(idx[b, 0], s, k, f"step b={b}")
+
+
+def test_step_small_rows_and_padding():
+    for n_vis, k in ((100, 128), (128, 128), (129, 128), (3000, 1024), (2049, 128), (2051, 128)):
+        qi, wi, ki, pos, rng = _inputs(n_vis + 5, seed=n_vis)
+        pos[:] = 4 * n_vis + 2
+        kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+        print(f"[case] step n_vis={n_vis} k={k}", flush=True)
+        idx = _run_step(qi, wi, kb, pos, k)
+        assert np.array_equal(idx, _run(qi, wi, kb, pos, k)[0])
+        check_topk_row(idx[0, 0], _scores(qi, wi, kb[:, :n_vis]), k, f"step n_vis={n_vis}")
