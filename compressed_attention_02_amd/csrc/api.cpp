@@ -103,6 +103,7 @@ const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select
 struct IndexPlan {
   int64_t rows, n_cap, sc_rs, ntiles, key_rs, info_rs, chunk_rows;
   size_t off_keys, off_info, ws_bytes;
+  bool multi;   // score in workgroups of 8 query rows (prefill chunks of a 64 x 64 bf16 indexer)
 };
 
 IndexPlan plan_index(const v4a_index_args* a) {
@@ -116,6 +117,10 @@ IndexPlan plan_index(const v4a_index_args* a) {
   // rows are processed in chunks whose scores fit in 1 GiB
   const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 8;
   P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
+  // queries in groups of 8 share each key tile: a chunk of rows holds whole groups
+  P.multi = a->dtype == V4A_BF16 && a->heads == 64 && a->dim == 64 && a->ki_dtype != V4A_FP8_E4M3 &&
+            a->tq % 8 == 0 && P.chunk_rows >= 8;
+  if (P.multi) P.chunk_rows -= P.chunk_rows % 8;
 
   P.off_keys = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
   P.off_info = P.off_keys + (size_t)round_up(P.chunk_rows * P.key_rs * 4, 256);
@@ -499,9 +504,17 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   return L;
 }
 
-v4a_status launch_score_rows(const v4a_index_args* a, IndexLaunch& L, int64_t r0, int nr, hipStream_t stream) {
+v4a_status score_row_chunk(const v4a_index_args* a, IndexLaunch& L, int64_t r0, int nr, hipStream_t stream) {
   L.sp.row0 = (int)r0;
   L.tp.row0 = (int)r0;
+  if (L.P.multi) {
+    // enough workgroups to cover the chip about four times, each walking tiles
+    ScoreP sp = L.sp;
+    const int64_t groups = cdiv(nr, 8);
+    sp.wgs_per_row = (int)std::max<int64_t>(1, std::min<int64_t>(L.P.ntiles, cdiv(4 * (int64_t)cu_count(), groups)));
+    V4A_TRY(hip_check(launch_score_rows(sp, nr, (int)L.P.ntiles, stream, V4A_K_INDEX_SCORE), "index score launch"));
+    return V4A_OK;
+  }
   V4A_TRY(hip_check(launch_score(a->dtype, L.sp, nr, (int)L.P.ntiles, stream, V4A_K_INDEX_SCORE), "index score launch"));
   return V4A_OK;
 }
@@ -512,7 +525,7 @@ v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStre
   V4A_TRY(check_ws(ws, ws_bytes, L.P.ws_bytes));
   for (int64_t r0 = 0; r0 < L.P.rows; r0 += L.P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(L.P.chunk_rows, L.P.rows - r0);
-    V4A_TRY(launch_score_rows(a, L, r0, nr, stream));
+    V4A_TRY(score_row_chunk(a, L, r0, nr, stream));
     V4A_TRY(hip_check(launch_select(L.tp, nr, stream, V4A_K_TOPK_SELECT), "top-k select launch"));
   }
   return ok();
@@ -640,7 +653,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
         IL.sp.prep = qprep_params(a, p, ws, P.off_q);
         IL.sp.prep_x = qprep_blocks(IL.sp.prep);
       }
-      V4A_TRY(launch_score_rows(ix, IL, 0, (int)IL.P.rows, s));
+      V4A_TRY(score_row_chunk(ix, IL, 0, (int)IL.P.rows, s));
       V4A_TRY(hip_check(launch_select_attn(IL.tp, (int)IL.P.rows, rest, (int)P.rows, s, V4A_K_SELECT_ATTN),
                         "select+attention launch"));
     } else {

@@ -122,6 +122,18 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_score_rows(const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid) {
+  if (p.heads != 64 || p.dim != 64 || p.ki_scale || p.prep_x != 0 || p.tq % kScoreRowsQ != 0 ||
+      p.row0 % kScoreRowsQ != 0 || nrows < 1 || p.wgs_per_row < 1)
+    return hipErrorInvalidValue;
+  ScoreP q = p;
+  q.nrows = nrows;
+  // wgs_per_row workgroups per group of kScoreRowsQ queries, each walking tiles
+  const dim3 grid((unsigned)std::min(p.wgs_per_row, ntiles), (unsigned)((nrows + kScoreRowsQ - 1) / kScoreRowsQ));
+  V4A_LAUNCH(tid, score_rows_kernel, grid, dim3(kScoreRowsQ * 64), 0, s, q);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ selection
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectP p) {
   __shared__ SelShared sh;

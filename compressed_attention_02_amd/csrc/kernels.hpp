@@ -66,6 +66,10 @@ struct ScoreP {
   QPrepP prep; int prep_x;
 };
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
+// Prefill form (bf16 64 x 64 indexer, tq a multiple of 8, row0 too): workgroups of 8
+// query rows, each key tile read once for the 8; p.wgs_per_row workgroups per group
+// of 8 rows, walking the tiles (at most ntiles).  Same outputs as launch_score.
+hipError_t launch_score_rows(const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
 struct SelectP {
   const float* scores; const uint32_t* rep_key; const uint2* rep_info;

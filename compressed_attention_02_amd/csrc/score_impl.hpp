@@ -188,4 +188,150 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
   }
 }
 
+// ------------------------------------------------------------------ score, several queries
+// Prefill chunks: a workgroup of NQ waves takes NQ consecutive query rows of one
+// sequence, one per wave (its QI fragments and head weights in registers), and walks
+// the 256-key tiles x, x + gridDim.x, ... of the group's visible blocks.  Every tile
+// goes to LDS once (double-buffered) and serves all NQ queries, so the indexer keys
+// are read once per NQ queries instead of once per query.  A wave scores all 256
+// keys of the tile for its query, per 16-key group; lane l ends with the scores of
+// keys l, 64 + l, 128 + l and 192 + l, stores them and makes the four 64-block
+// reports, in the layout of score_block.  Launch rows lr >= p.nrows (a partial last
+// group) load and wait with the others but write nothing.
+//
+// The ReLU-weighted head sum is taken as s = (sum_h w_h x_h + sum_h w_h |x_h|) / 2
+// (max(x, 0) = (x + |x|) / 2, exactly, for any w), x_h = qi_h . k: the second sum is one
+// fused multiply-add per head with an absolute-value operand (half the vector work of
+// a maximum and a multiply-add), and the first is the single dot product u . k with
+// u = sum_h w_h qi_h, formed once per query in fp32 and split into three bf16 parts
+// (hi, mid, lo: about 24 significant bits) that fill three rows of a fifth MFMA head
+// tile.  The two sums agree with the per-head form to fp32 rounding of terms of the
+// size of sum_h w_h |x_h|.
+constexpr int kScoreRowsQ = 8;   // query rows per workgroup of score_rows_kernel
+
+__global__ __launch_bounds__(kScoreRowsQ * 64) void score_rows_kernel(ScoreP p) {
+  constexpr int NQ = kScoreRowsQ, DI = 64, MT = 4, KS = 2, ROWB = DI * 2, KCPR = ROWB / 16, KRPI = 64 / KCPR;
+  constexpr int IPW = kTile / KRPI / NQ;   // tile loads per wave
+  __shared__ __align__(16) unsigned char sK[2][kTile * ROWB];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr0 = blockIdx.y * NQ;                      // the group's first launch row
+  const int lr = lr0 + wave;                            // this wave's query
+  const bool have = lr < p.nrows;
+  const int last = min(lr0 + NQ, p.nrows) - 1;          // the group's last query: most visible blocks
+  int b, i, bl, il;
+  int64_t pos, pos_l;
+  row_coords(p.row0 + (have ? lr : last), p.tq, p.pos0, b, i, pos);
+  row_coords(p.row0 + last, p.tq, p.pos0, bl, il, pos_l);
+  const int64_t nvis = (pos + 1) / p.ratio;             // this query's
+  const int64_t nvis_g = uniform_i64((pos_l + 1) / p.ratio);
+  const int64_t ntile = (nvis_g + kTile - 1) / kTile;
+  int64_t tile = blockIdx.x;
+  const int64_t stride = gridDim.x;
+  if (tile >= ntile) return;
+  const unsigned char* ki = reinterpret_cast<const unsigned char*>(p.ki) + (int64_t)bl * p.ki_bs * 2;
+  const int64_t ki_rb = p.ki_rs * 2;
+  auto issue = [&](int64_t t, unsigned char* buf) {
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int r0 = (wave * IPW + u) * KRPI;
+      const int r = r0 + lane / KCPR;
+      const int64_t j = min(t * kTile + r, nvis_g - 1);
+      lds_load16(ki + j * ki_rb + ((lane % KCPR) ^ swz_ki<DI>(r)) * 16, lds_addr(buf + r0 * ROWB));
+    }
+  };
+  // the query's fragments (head mt*16 + col, dims s*32 + grp*8 .. + 8) and weights;
+  // U: rows 0, 1, 2 of the fifth head tile are the parts of u = sum_h w_h qi_h, the
+  // rest zero (lane (col, grp) holds row col, dims s*32 + grp*8 .. + 8 like A)
+  bf16x8_t A[MT][KS], U[KS];
+  float w[MT][4];
+  {
+    const uint16_t* qi = reinterpret_cast<const uint16_t*>(p.qi) + (int64_t)b * p.qi_bs + (int64_t)i * p.qi_rs;
+    const float* wi = p.wi + (int64_t)b * p.wi_bs + (int64_t)i * p.wi_rs;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        A[mt][s2] = *reinterpret_cast<const bf16x8_t*>(qi + (mt * 16 + col) * DI + s2 * 32 + grp * 8);
+      const f32x4 wq = *reinterpret_cast<const f32x4*>(wi + mt * 16 + 4 * grp);
+      w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
+    }
+    float u[KS][8];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[s2][e] = 0.f;
+    for (int h = 0; h < MT * 16; ++h) {   // in head order, the same in every lane of a row
+      const float wh = wi[h];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        float q8[8];
+        unpack8(*reinterpret_cast<const uint4*>(qi + h * DI + s2 * 32 + grp * 8), q8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[s2][e] = fmaf(wh, q8[e], u[s2][e]);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float hi = bf2f(f2bf(u[s2][e]));
+        const float mid = bf2f(f2bf(u[s2][e] - hi));
+        const float lo = u[s2][e] - hi - mid;
+        const float v = col == 0 ? hi : col == 1 ? mid : col == 2 ? lo : 0.f;
+        U[s2][e] = (__bf16)v;
+      }
+  }
+  // (the compiler does not count the tile loads below, so it would wait for them too
+  // at the fragments' first use: they are waited for here, before any tile load)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  issue(tile, sK[0]);
+  if (tile + stride < ntile) issue(tile + stride, sK[1]);
+  float* sc = p.scores + (int64_t)lr * p.sc_rs;
+  const int kx = swz_ki<DI>(col);   // rows 16u + col share col's XOR
+  for (int c = 0; tile < ntile; tile += stride, ++c) {
+    unsigned char* buf = sK[c & 1];
+    if (tile + stride < ntile) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();   // every wave's share of the tile is in LDS
+    float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kTile / 16; ++u) {
+      const int t = u * 16 + col;
+      bf16x8_t Bv[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        Bv[s2] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s2 * 4 + grp) ^ kx) * 16));
+      f32x4 lin = {0.f, 0.f, 0.f, 0.f};   // u . k in rows 0..2 (lane group 0)
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) lin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(U[s2], Bv[s2], lin, 0, 0, 0);
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s2], Bv[s2], acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fabsf(acc[e]), part);
+      }
+      part += (lin[0] + lin[1]) + lin[2];
+      part = 0.5f * col_sum4(part);
+      if (grp == (u & 3)) mine[u >> 2] = part;
+    }
+    if (have) {
+      const int64_t tile0 = tile * kTile;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int64_t j = tile0 + 64 * blk + lane;
+        if (j < nvis) sc[j] = mine[blk];
+        const int64_t gw = tile * 4 + blk;
+        wave_top(score_key(mine[blk]), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + gw * kWaveTop,
+                 p.rep_info + (int64_t)lr * p.info_rs + gw);
+      }
+    }
+    __syncthreads();   // every wave is done with this buffer
+    if (tile + 2 * stride < ntile) issue(tile + 2 * stride, buf);
+  }
+}
+
 }  // namespace v4a

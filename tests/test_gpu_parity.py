@@ -173,3 +173,17 @@ def test_step_odd_head_tile_counts(heads):
     print(f"[case] step heads={heads}", flush=True)
     Run(cfg).run(fused=True).check_all()
     Run(cfg).run(fused=False).check_all()
+
+
+@pytest.mark.parametrize("tq", [8, 24, 64])
+def test_prefill_index_two_sequences(tq):
+    # the prefill form of the indexer score (workgroups of 8 query rows sharing each
+    # key tile) over two sequences, checked row by row (the chunk starts on a block
+    # boundary, as compression needs; its rows cover every position in between)
+    cfg = C.C5.small(name=f"pf_ix{tq}", batch=2, pos=8192, tq=tq, needles=8)
+    print(f"[case] prefill index two sequences tq={tq}", flush=True)
+    r = Run(cfg)
+    r.step.run_compress()
+    r.step.run_index()
+    torch.cuda.synchronize()
+    r.check_topk()
