@@ -191,6 +191,15 @@ def _ws_ptr(ws):
 
 
 # ---------------------------------------------------------------- entry points
+def compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int,
+                  norm_k=None, norm_v=None, norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4,
+                  rope_v: bool = False) -> CompressArgs:
+    return CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
+                        _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
+                        _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, rope_dims, rope_base,
+                        ROPE_V if rope_v else 0)
+
+
 def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None,
              norm_k=None, norm_v=None, norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4,
              rope_v: bool = False):
@@ -198,11 +207,23 @@ def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, 
     (RMS-normalised with the fp32 gains norm_k / norm_v when given; with rope_dims,
     raw rows are rotated at their positions and entries at their block's last one).
     v_raw and v_out None: shared K = V entries, K alone is pooled."""
-    a = CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
-                     _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
-                     _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, rope_dims, rope_base,
-                     ROPE_V if rope_v else 0)
+    a = compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, t0=t0, n=n, ratio=ratio, norm_k=norm_k,
+                      norm_v=norm_v, norm_eps=norm_eps, rope_dims=rope_dims, rope_base=rope_base, rope_v=rope_v)
     _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
+
+
+class CompressCall:
+    """A v4attn_compress call whose arguments are marshalled once (same keywords as
+    compress); repeated calls on the same tensors pay only the C call."""
+
+    def __init__(self, k_raw, v_raw, logits, raw_start, k_out, v_out, **kw):
+        self._a = compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, **kw)
+        self._ref = ctypes.byref(self._a)
+        self._keep = (k_raw, v_raw, logits, raw_start, k_out, v_out, kw.get("norm_k"), kw.get("norm_v"))
+        self._fn = lib().v4attn_compress
+
+    def __call__(self, stream=None):
+        _check(self._fn(self._ref, _stream(stream)))
 
 
 def index_args(qi, wi, ki, pos0, idx, *, ratio, topk, pos_max, sel_scores=None, ki_scale=None) -> IndexArgs:

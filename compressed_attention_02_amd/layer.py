@@ -11,7 +11,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import CSA, HCA, SWA, DecodeStepCall, compress, decode, index_topk, prefill_chunk
+from . import CSA, HCA, SWA, CompressCall, DecodeStepCall, decode, index_topk, prefill_chunk
 
 
 def to_device(arrays: dict, device="cuda") -> dict:
@@ -81,19 +81,28 @@ class LayerStep:
 
     # -- stages -------------------------------------------------------------
     def run_compress(self, stream=None):
+        """The step's compress calls (CSA then HCA), marshalled on first use."""
+        if getattr(self, "_compress_calls", None) is None:
+            self._compress_calls = self._make_compress_calls()
+        for call in self._compress_calls:
+            call(stream)
+
+    def _make_compress_calls(self):
         s, t = self.s, self.t
         if s.compress == "none":
-            return
+            return []
         n = self.pos_max + 1 - s.compress_t0
         # with RoPE, raw rows arrive rotated at their positions and entries are stored
         # rotated at their block's last one (shared entries: the values are the keys)
-        rope = dict(rope_dims=s.rope_dims, rope_base=s.rope_base)
+        kw = dict(t0=s.compress_t0, n=n, rope_dims=s.rope_dims, rope_base=s.rope_base)
+        calls = []
         if s.branches & CSA and s.compress in ("all", "chunk"):
-            compress(t["k_raw"], t.get("v_raw"), t["logit_csa"], t["raw_start"], t["kc"], t.get("vc"),
-                     t0=s.compress_t0, n=n, ratio=s.m, stream=stream, **rope)
+            calls.append(CompressCall(t["k_raw"], t.get("v_raw"), t["logit_csa"], t["raw_start"], t["kc"],
+                                      t.get("vc"), ratio=s.m, **kw))
         if s.branches & HCA:
-            compress(t["k_raw"], t.get("v_raw"), t["logit_hca"], t["raw_start"], t["kh"], t.get("vh"),
-                     t0=s.compress_t0, n=n, ratio=s.m_hca, stream=stream, **rope)
+            calls.append(CompressCall(t["k_raw"], t.get("v_raw"), t["logit_hca"], t["raw_start"], t["kh"],
+                                      t.get("vh"), ratio=s.m_hca, **kw))
+        return calls
 
     def run_index(self, stream=None):
         s, t = self.s, self.t
@@ -127,7 +136,9 @@ class LayerStep:
         self._step_call(stream)
 
     def prepare(self):
-        """Marshal the decode step's call without launching anything."""
+        """Marshal the step's calls (compress, decode step) without launching anything."""
+        if getattr(self, "_compress_calls", None) is None:
+            self._compress_calls = self._make_compress_calls()
         if getattr(self, "_step_call", None) is None:
             s, t = self.s, self.t
             kw = self.attn_kwargs()
