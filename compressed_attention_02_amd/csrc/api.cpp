@@ -113,9 +113,9 @@ IndexPlan plan_index(const v4a_index_args* a) {
   P.sc_rs = round_up(std::max<int64_t>(P.n_cap, 1), 64);
   P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, kTile));
   P.key_rs = round_up(P.ntiles * kTileTop, 64);
-  P.info_rs = round_up(P.ntiles * 4, 32);
+  P.info_rs = round_up(P.ntiles, 16);
   // rows are processed in chunks whose scores fit in 1 GiB
-  const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 8;
+  const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 16;
   P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
   // queries in groups of 8 share each key tile: a chunk of rows holds whole groups
   P.multi = a->dtype == V4A_BF16 && a->heads == 64 && a->dim == 64 && a->ki_dtype != V4A_FP8_E4M3 &&
@@ -124,7 +124,7 @@ IndexPlan plan_index(const v4a_index_args* a) {
 
   P.off_keys = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
   P.off_info = P.off_keys + (size_t)round_up(P.chunk_rows * P.key_rs * 4, 256);
-  P.ws_bytes = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 8, 256);
+  P.ws_bytes = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 16, 256);
   return P;
 }
 
@@ -483,7 +483,7 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   }
   sp.scores = (float*)base;
   sp.rep_key = (uint32_t*)(base + P.off_keys);
-  sp.rep_info = (uint2*)(base + P.off_info);
+  sp.rep_info = (uint4*)(base + P.off_info);
   sp.key_rs = P.key_rs;
   sp.info_rs = P.info_rs;
   sp.qi_bs = a->qi.batch_stride; sp.qi_rs = a->qi.row_stride;
@@ -640,6 +640,10 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
     while (!inv && hg > hmin && (ntile % hg != 0 || P.rows * P.s_csa * hg > cu_count())) --hg;
     csa.head_groups = hg;
   }
+  // the rest's launch also hosts the selection: with eight or more head tiles its
+  // workgroups take half of them each, so that the rest's attention (every chunk
+  // read from LDS once per head tile) ends with the selection rather than after it
+  if (combined && a->dim <= 128 && a->heads >= 128 && (a->heads / 16) % 2 == 0) rest.head_groups = 2;
 
   auto attend = [&](const AttnP& ap) -> v4a_status {
     V4A_TRY(hip_check(launch_attn(a->dtype, ap, (int)P.rows, s, V4A_K_ATTN), "attention launch"));

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(ScoreP p) {
 // One thread per block of the tile; the row's indexer queries and weights sit in LDS.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
   extern __shared__ float s_q[];  // [heads*dim] then [heads]
+  __shared__ TileStage s_stage;
   const int lr = blockIdx.y;
   int b, i;
   int64_t pos;
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
     sc[j] = s;
     v = score_key(s);
   }
-  wave_top(v, j < nvis, p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop + (threadIdx.x >> 6) * kWaveTop,
-           p.rep_info + (int64_t)lr * p.info_rs + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+  tile_report_waves(v, j < nvis, 0, s_stage, p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop,
+                    p.rep_info + (int64_t)lr * p.info_rs + blockIdx.x);
 }
 
 hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid) {

@@ -28,8 +28,8 @@ hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t
 
 // ---------------------------------------------------------------- indexer
 constexpr int kTile = 256;        // blocks per score tile
-constexpr int kWaveTop = 4;       // (key, id) pairs each 64-block wave reports
-constexpr int kTileTop = 4 * kWaveTop;  // pairs per tile
+constexpr int kWaveTop = 4;       // (key, id) pairs each 64-block wave picks
+constexpr int kTileTop = 8;       // (key, id) pairs each tile reports, of its four waves' picks
 constexpr int kPoolCap = 4096;    // candidate pool of the per-row selection (LDS)
 constexpr int kMaxTopk = 2048;
 constexpr int kSelThreads = 512;
@@ -54,8 +54,8 @@ struct ScoreP {
   const float* ki_scale; int64_t ks_bs;   // FP8 keys: one scale per row (null: bf16 keys)
   const int64_t* pos0;
   float* scores;      // [rows][sc_rs]
-  uint32_t* rep_key;  // [rows][key_rs]: per wave, the keys of its kWaveTop best, in id order
-  uint2* rep_info;    // [rows][info_rs]: per wave, (4 packed 8-bit id offsets, bound key)
+  uint32_t* rep_key;  // [rows][key_rs]: per tile, the keys of its kTileTop best, in id order
+  uint4* rep_info;    // [rows][info_rs]: per tile, (offsets 0-3, offsets 4-7 as 8-bit fields, bound key, 0)
   int64_t qi_bs, qi_rs, wi_bs, wi_rs, ki_bs, ki_rs, sc_rs, key_rs, info_rs;
   int tq, row0;       // launch covers global rows row0 + blockIdx.y; row = b*tq + i
   int heads, dim, ratio;
@@ -72,7 +72,7 @@ hipError_t launch_score(int dtype, const ScoreP& p, int nrows, int ntiles, hipSt
 hipError_t launch_score_rows(const ScoreP& p, int nrows, int ntiles, hipStream_t s, int tid);
 
 struct SelectP {
-  const float* scores; const uint32_t* rep_key; const uint2* rep_info;
+  const float* scores; const uint32_t* rep_key; const uint4* rep_info;
   const int64_t* pos0;
   int32_t* idx; int64_t idx_bs, idx_rs;
   float* sel; int64_t sel_bs, sel_rs;

@@ -53,12 +53,18 @@ struct ScoreSmem {
   static constexpr int DI = KS * 32;
   static constexpr int KROWB = FP8 ? DI : DI * 2;   // LDS bytes per key row
   unsigned char sK[NB][64 * NW * KROWB];
-  unsigned char sQ[MT * 16 * DI * 2];
+  // the query rows until every wave holds its fragments, then the tiles' keys for
+  // the report (four waves of 64 blocks); a barrier separates the two uses
+  union {
+    unsigned char sQ[MT * 16 * DI * 2];
+    TileStage stage;
+  };
 };
 
 // Workgroup x (of the row's p.wgs_per_row) of launch row lr.
 template <int NW, int MT, int KS, int NB, bool FP8>
 __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, ScoreSmem<NW, MT, KS, NB, FP8>& sm) {
+  static_assert(NW == 4, "a workgroup tile is one report tile of four 64-block waves");
   constexpr int DI = KS * 32;
   constexpr int TILE = 64 * NW;              // keys per workgroup tile
   constexpr int ROWB = DI * 2;               // LDS bytes per query row
@@ -140,6 +146,7 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
         for (int s = 0; s < KS; ++s)
           A[mt][s] = *reinterpret_cast<const bf16x8_t*>(sQ + (mt * 16 + col) * ROWB + (((s * 4 + grp) ^ kx) * 16));
       have_q = true;
+      __syncthreads();   // the query rows are read: their LDS holds the wave picks from here on
     }
     // a wave reads only the key rows it loaded itself, so its own loads are all it
     // waits for (no barrier); the next tile may stay in flight
@@ -179,9 +186,8 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
     }
     const int64_t j = tile0 + wave * 64 + lane;
     if (j < nvis) sc[j] = mine;
-    const int64_t gw = tile * NW + wave;   // global wave: blocks 64 gw .. 64 gw + 63
-    wave_top(score_key(mine), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + gw * kWaveTop,
-             p.rep_info + (int64_t)lr * p.info_rs + gw);
+    tile_report_waves(score_key(mine), j < nvis, c & 1, sm.stage, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop,
+                      p.rep_info + (int64_t)lr * p.info_rs + tile);
     // the buffer is reloaded next, each wave into the rows it has just read
     if (NB == 2 && tile + 2 * stride < ntile_row)
       issue(tile + 2 * stride, sK[NB == 2 ? (c & 1) : 0]);
@@ -209,7 +215,7 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
 // size of sum_h w_h |x_h|.
 constexpr int kScoreRowsQ = 8;   // query rows per workgroup of score_rows_kernel
 
-__global__ __launch_bounds__(kScoreRowsQ * 64) void score_rows_kernel(ScoreP p) {
+__global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP p) {
   constexpr int NQ = kScoreRowsQ, DI = 64, MT = 4, KS = 2, ROWB = DI * 2, KCPR = ROWB / 16, KRPI = 64 / KCPR;
   constexpr int IPW = kTile / KRPI / NQ;   // tile loads per wave
   __shared__ __align__(16) unsigned char sK[2][kTile * ROWB];
@@ -320,14 +326,14 @@ __global__ __launch_bounds__(kScoreRowsQ * 64) void score_rows_kernel(ScoreP p) 
     }
     if (have) {
       const int64_t tile0 = tile * kTile;
+      uint32_t kb[4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const int64_t j = tile0 + 64 * blk + lane;
         if (j < nvis) sc[j] = mine[blk];
-        const int64_t gw = tile * 4 + blk;
-        wave_top(score_key(mine[blk]), j < nvis, p.rep_key + (int64_t)lr * p.key_rs + gw * kWaveTop,
-                 p.rep_info + (int64_t)lr * p.info_rs + gw);
+        kb[blk] = j < nvis ? score_key(mine[blk]) : 0u;
       }
+      tile_report(kb, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop, p.rep_info + (int64_t)lr * p.info_rs + tile);
     }
     __syncthreads();   // every wave is done with this buffer
     if (tile + 2 * stride < ntile) issue(tile + 2 * stride, buf);

@@ -4,6 +4,7 @@
 #pragma once
 #include "common.hpp"
 #include "kernels.hpp"
+#include <utility>
 
 namespace v4a {
 
@@ -14,45 +15,87 @@ __device__ __forceinline__ void row_coords(int row, int tq, const int64_t* pos0,
   pos = pos0[b] + i;
 }
 
-// A wave's report on its 64 elements (lane L holds block base + L with order key
-// `key` when `valid`): the keys of its kWaveTop best (higher key first, then lower
-// id) in ascending id order, their ids as 8-bit offsets from base (0xff = no
-// element) packed in one word, and the key of the next best, an upper bound on every
-// key it leaves out (0 if none).  Each round takes a 32-bit wave maximum (DPP) of
-// the keys not yet taken and gives it to the lowest lane that holds it (a ballot),
-// so ties go to the lower id; the taken lanes, in lane order, are the id order.
-__device__ __forceinline__ void wave_top(uint32_t key, bool valid, uint32_t* keys, uint2* info) {
-  static_assert(kWaveTop == 4, "four offsets per info word");
+// Reports of the score kernels, per tile of kTile = 256 blocks: the keys of the
+// tile's kTileTop best blocks (higher key first, then lower id) in ascending id
+// order (key 0 = no element), and an info word (offsets of entries 0-3, offsets of
+// entries 4-7, bound, 0): 8-bit offsets from the tile's first block, and the key of
+// the best block the report leaves out (0 if none), which bounds every other one.
+
+// Lane `dst` receives v (a forward permute); every lane sends, so lanes with nothing
+// to send aim at lane 63, which no caller reads.
+__device__ __forceinline__ uint32_t lane_send(uint32_t v, int dst) {
+  return (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)v);
+}
+// number of set bits of m below this lane
+__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The tile report made by one wave whose lane L holds the keys kb[q] of blocks
+// 64 q + L (0 for none).  Each of kTileTop rounds takes a 32-bit wave maximum (DPP)
+// of the keys not yet taken and gives it to the lowest id that holds it (the first
+// quarter q with a ballot hit, then its lowest lane), so ties go to the lower id;
+// one more maximum is the bound.  The winners then go to lanes 0..7 in id order (a
+// forward permute per quarter) and are written out: keys (8 words) and info.
+__device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* keys, uint4* info) {
+  static_assert(kTileTop == 8, "two offset words per tile");
   const int lane = threadIdx.x & 63;
-  bool live = valid;
-  uint64_t won = 0;
+  uint32_t k[4] = {kb[0], kb[1], kb[2], kb[3]};
+  uint64_t won[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll 1
+  for (int r = 0; r < kTileTop; ++r) {
+    const uint32_t m = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
+    if (m == 0u) break;
+    bool taken = false;
 #pragma unroll
-  for (int r = 0; r < kWaveTop; ++r) {
-    const uint32_t m = wave_max_u32(live ? key : 0u);
-    const uint64_t at = __ballot(live && key == m);
-    if (at) {
-      const int l = __builtin_ctzll(at);
-      won |= 1ull << l;
-      live = live && lane != l;
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t at = __ballot(k[q] == m);
+      if (!taken && at) {
+        const int l = __builtin_ctzll(at);
+        won[q] |= 1ull << l;
+        if (lane == l) k[q] = 0u;
+        taken = true;
+      }
     }
   }
-  const uint32_t bound = wave_max_u32(live ? key : 0u);
-  uint32_t k4[kWaveTop], offs = 0;
+  const uint32_t bound = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
+  uint32_t base = 0, rk = 0u, ro = 0u;
 #pragma unroll
-  for (int r = 0; r < kWaveTop; ++r) {
-    if (won) {
-      const int l = __builtin_ctzll(won);
-      won &= won - 1;
-      k4[r] = __builtin_amdgcn_readlane(key, l);
-      offs |= (uint32_t)l << (8 * r);
-    } else {
-      k4[r] = 0u;
-      offs |= 0xffu << (8 * r);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const bool w = (won[q] >> lane) & 1ull;
+    const int dst = w ? (int)(base + bits_below(won[q])) : 63;
+    const uint32_t gk = lane_send(kb[q], dst), go = lane_send(64u * q + lane, dst);
+    const uint32_t nq = (uint32_t)__popcll(won[q]);
+    if (lane >= (int)base && lane < (int)(base + nq)) { rk = gk; ro = go; }
+    base += nq;
   }
-  if (lane == 0) {
-    *reinterpret_cast<uint4*>(keys) = make_uint4(k4[0], k4[1], k4[2], k4[3]);
-    *info = make_uint2(offs, bound);
+  if (lane < kTileTop) keys[lane] = lane < (int)base ? rk : 0u;
+  // the offsets as bytes of two words (lanes 0..3 and 4..7): OR over each quad
+  uint32_t word = lane < (int)base ? (ro & 0xffu) << (8 * (lane & 3)) : 0u;
+  word |= dpp_u32<0xB1>(0u, word);   // quad_perm [1,0,3,2]
+  word |= dpp_u32<0x4E>(0u, word);   // quad_perm [2,3,0,1]
+  const uint32_t word1 = __builtin_amdgcn_readlane(word, 4);
+  if (lane == 0) *info = make_uint4(word, word1, bound, 0u);
+}
+
+// The tile's keys when its four 64-block quarters are four waves of a workgroup,
+// [parity] so that a tile's keys are read before the next tile's are written (a
+// barrier separates the two).
+struct TileStage {
+  uint32_t key[2][kTile];
+};
+// Every wave stages its keys (0 for no element); after the barrier wave 0 makes the
+// tile report.  Called by all four waves of the workgroup (it holds a barrier).
+__device__ __forceinline__ void tile_report_waves(uint32_t key, bool valid, int par, TileStage& st, uint32_t* keys,
+                                                  uint4* info) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  st.key[par][wave * 64 + lane] = valid ? key : 0u;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t kb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kb[q] = st.key[par][q * 64 + lane];
+    tile_report(kb, keys, info);
   }
 }
 
@@ -328,27 +371,25 @@ __device__ __forceinline__ void emit_pool(SelShared& sh, uint32_t np, uint32_t k
 __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t* RK = p.rep_key + (int64_t)lr * p.key_rs;
-  const uint2* RI = p.rep_info + (int64_t)lr * p.info_rs;
+  const uint4* RI = p.rep_info + (int64_t)lr * p.info_rs;
   // thread t owns tiles [t*tpt, t*tpt + tpt) of the longest row; the report loads do
   // not wait for the row's position (tiles past the row's own end are dropped below)
   const int64_t ntc = p.ntiles_cap;
   const int tpt = (int)min<int64_t>(kMaxTilesPerThread + 1, (ntc + kSelThreads - 1) / kSelThreads);
   bool ok = tpt <= kMaxTilesPerThread;
-  uint4 rk[kMaxTilesPerThread][kTileTop / 4], ri[kMaxTilesPerThread][2];
+  uint4 rk[kMaxTilesPerThread][kTileTop / 4], ri[kMaxTilesPerThread];
 #pragma unroll
   for (int q = 0; q < kMaxTilesPerThread; ++q) {
     if (ok && q < tpt) {
       const int64_t tl = min<int64_t>((int64_t)tid * tpt + q, ntc - 1);
       const uint4* ks = reinterpret_cast<const uint4*>(RK + tl * kTileTop);
-      const uint4* is = reinterpret_cast<const uint4*>(RI + tl * 4);
 #pragma unroll
       for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = ks[j];
-      ri[q][0] = is[0];
-      ri[q][1] = is[1];
+      ri[q] = RI[tl];
     } else {
 #pragma unroll
       for (int j = 0; j < kTileTop / 4; ++j) rk[q][j] = make_uint4(0u, 0u, 0u, 0u);
-      ri[q][0] = ri[q][1] = make_uint4(0xffffffffu, 0u, 0xffffffffu, 0u);
+      ri[q] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   // the two histogram levels of the register search start at zero (cleared while
@@ -379,8 +420,8 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
   const int64_t ntiles = (nvis + kTile - 1) / kTile;
   ok = ok && ntiles <= ntc;
 
-  // report keys, packed id offsets (the id of entry j of tile t is t*256 + (j/4)*64 +
-  // offset) and the largest wave bound of each owned tile
+  // report keys (0: no element), packed id offsets (the id of entry j of tile t is
+  // t*256 + its offset) and the bound of each owned tile
   uint32_t uk[kMaxTilesPerThread][kTileTop], uo[kMaxTilesPerThread][kTileTop / 4], ub[kMaxTilesPerThread];
   bool own[kMaxTilesPerThread];
   int64_t tbase[kMaxTilesPerThread];
@@ -394,31 +435,25 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
       uk[q][4 * w] = rk[q][w].x; uk[q][4 * w + 1] = rk[q][w].y;
       uk[q][4 * w + 2] = rk[q][w].z; uk[q][4 * w + 3] = rk[q][w].w;
     }
-    uo[q][0] = own[q] ? ri[q][0].x : 0xffffffffu;
-    uo[q][1] = own[q] ? ri[q][0].z : 0xffffffffu;
-    uo[q][2] = own[q] ? ri[q][1].x : 0xffffffffu;
-    uo[q][3] = own[q] ? ri[q][1].z : 0xffffffffu;
-    ub[q] = own[q] ? max(max(ri[q][0].y, ri[q][0].w), max(ri[q][1].y, ri[q][1].w)) : 0u;
-    // key 0 marks no element from here on
+    uo[q][0] = ri[q].x;
+    uo[q][1] = ri[q].y;
+    ub[q] = own[q] ? ri[q].z : 0u;
 #pragma unroll
-    for (int j = 0; j < kTileTop; ++j)
-      if (((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu) == 0xffu) uk[q][j] = 0u;
+    for (int j = 0; j < kTileTop; ++j) uk[q][j] = own[q] ? uk[q][j] : 0u;
   }
   auto rep_id = [&](int q, int j) -> uint32_t {
-    return (uint32_t)tbase[q] + 64u * (j / 4) + ((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu);
+    return (uint32_t)tbase[q] + ((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu);
   };
   auto eachOwn = [&](auto&& f) {
 #pragma unroll
     for (int q = 0; q < kMaxTilesPerThread; ++q)
 #pragma unroll
-      for (int j = 0; j < kTileTop; ++j) {
-        const uint32_t off = (uo[q][j / 4] >> (8 * (j % 4))) & 0xffu;
-        if (own[q] && off != 0xffu) f(uk[q][j], (uint32_t)tbase[q] + 64u * (j / 4) + off);
-      }
+      for (int j = 0; j < kTileTop; ++j)
+        if (uk[q][j] != 0u) f(uk[q][j], rep_id(q, j));
   };
-  // every wave of 64 visible blocks reports kWaveTop of them, a partial last wave
+  // every tile of 256 visible blocks reports kTileTop of them, a partial last tile
   // as many as it has
-  const int64_t n_rep = kWaveTop * (nvis / 64) + min<int64_t>(kWaveTop, nvis % 64);
+  const int64_t n_rep = kTileTop * (nvis / kTile) + min<int64_t>(kTileTop, nvis % kTile);
 
   if (ok && n_rep >= k) {
     // 1. the exact k-th key T of all the reports
@@ -449,13 +484,14 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
         while (mask) {
           const int j = __builtin_ctzll(mask);
           mask &= mask - 1;
+          constexpr int OW = kTileTop / 4;   // offset words per tile
           const int q = j / kTileTop, wv = (j % kTileTop) / 4, e = j % 4;
           uint32_t word = uo[0][0];
 #pragma unroll
           for (int qq = 0; qq < kMaxTilesPerThread; ++qq)
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) word = (q * 4 + wv == qq * 4 + ww) ? uo[qq][ww] : word;
-          const uint32_t id = (uint32_t)(((int64_t)tid * tpt + q) * kTile) + 64u * wv + ((word >> (8 * e)) & 0xffu);
+            for (int ww = 0; ww < OW; ++ww) word = (q * OW + wv == qq * OW + ww) ? uo[qq][ww] : word;
+          const uint32_t id = (uint32_t)(((int64_t)tid * tpt + q) * kTile) + ((word >> (8 * e)) & 0xffu);
           if (o < (uint32_t)k) sh.pool_id[o] = id;
           ++o;
         }
@@ -503,8 +539,7 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
         cnt[q] = 0;
         if (!own[q]) continue;
 #pragma unroll
-        for (int j = 0; j < kTileTop; ++j)
-          if (((uo[q][j / 4] >> (8 * (j % 4))) & 0xffu) != 0xffu) cnt[q] += uk[q][j] >= T ? 1u : 0u;
+        for (int j = 0; j < kTileTop; ++j) cnt[q] += (uk[q][j] != 0u && uk[q][j] >= T) ? 1u : 0u;
         if (ub[q] >= T) {
           const uint32_t slot = atomicAdd(&sh.n_fail, 1u);
           if (slot < 256u) { fslot[q] = (int)slot; sh.fail[slot] = (uint32_t)((int64_t)tid * tpt + q); }
@@ -549,10 +584,9 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
             } else if (own[q]) {
 #pragma unroll
               for (int j = 0; j < kTileTop; ++j) {
-                const uint32_t wo = (uo[q][j / 4] >> (8 * (j % 4))) & 0xffu;
-                if (wo != 0xffu && uk[q][j] >= T) {
+                if (uk[q][j] != 0u && uk[q][j] >= T) {
                   sh.pool_key[off] = uk[q][j];
-                  sh.pool_id[off] = (uint32_t)tbase[q] + 64u * (j / 4) + wo;
+                  sh.pool_id[off] = rep_id(q, j);
                   ++off;
                 }
               }

@@ -78,10 +78,11 @@ def test_max_topk_and_batch():
 
 
 def test_small_rows_and_padding():
-    # fewer visible blocks than k, exactly k, and one more than k; then rows whose
-    # last wave of 64 holds 1 or 3 blocks while the reports still cover k (the
-    # report of a wave with fewer than 4 elements)
-    for n_vis, k in ((100, 128), (128, 128), (129, 128), (3000, 1024), (2049, 128), (2051, 128)):
+    # fewer visible blocks than k, exactly k, and one more than k; rows whose last
+    # tile of 256 holds 1 or 3 blocks, with the tile reports short of k (the whole-row
+    # path) and covering k (the report of a tile with fewer than 8 elements)
+    for n_vis, k in ((100, 128), (128, 128), (129, 128), (3000, 1024), (2049, 128), (2051, 128), (4353, 128),
+                     (4355, 136)):
         qi, wi, ki, pos, rng = _inputs(n_vis + 5, seed=n_vis)
         pos[:] = 4 * n_vis + 2
         kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
@@ -160,7 +161,8 @@ def test_step_max_topk_and_batch(heads):
 
 
 def test_step_small_rows_and_padding():
-    for n_vis, k in ((100, 128), (128, 128), (129, 128), (3000, 1024), (2049, 128), (2051, 128)):
+    for n_vis, k in ((100, 128), (128, 128), (129, 128), (3000, 1024), (2049, 128), (2051, 128), (4353, 128),
+                     (4355, 136)):
         qi, wi, ki, pos, rng = _inputs(n_vis + 5, seed=n_vis)
         pos[:] = 4 * n_vis + 2
         kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
