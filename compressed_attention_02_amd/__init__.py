@@ -26,7 +26,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libv4attn.so")
+# V4ATTN_LIB names another build of the same library (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("V4ATTN_LIB") or os.path.join(PKG_DIR, "libv4attn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 CSA, HCA, SWA = 1, 2, 4

@@ -521,8 +521,8 @@ v4a_status score_row_chunk(const v4a_index_args* a, IndexLaunch& L, int64_t r0, 
 
 // Scores and selection of v4attn_index_topk on stream (arguments validated).
 v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  V4A_TRY(check_ws(ws, ws_bytes, plan_index(a).ws_bytes));   // before any pointer into ws is formed
   IndexLaunch L = index_launch(a, ws);
-  V4A_TRY(check_ws(ws, ws_bytes, L.P.ws_bytes));
   for (int64_t r0 = 0; r0 < L.P.rows; r0 += L.P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(L.P.chunk_rows, L.P.rows - r0);
     V4A_TRY(score_row_chunk(a, L, r0, nr, stream));
