@@ -24,10 +24,9 @@ namespace v4a {
 template <typename T> struct Chunk;
 template <> struct Chunk<float> {
   static constexpr int N = 4;
-  __device__ static u32x4 raw(const float* p) { return *reinterpret_cast<const u32x4*>(p); }
-  __device__ static void unpack(const u32x4 v, float* o) {
-    o[0] = __uint_as_float(v[0]); o[1] = __uint_as_float(v[1]);
-    o[2] = __uint_as_float(v[2]); o[3] = __uint_as_float(v[3]);
+  __device__ static void load(const float* p, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
   }
   __device__ static void store(float* p, const float* o) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
@@ -35,8 +34,7 @@ template <> struct Chunk<float> {
 };
 template <> struct Chunk<uint16_t> {
   static constexpr int N = 8;
-  __device__ static u32x4 raw(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-  __device__ static void unpack(const u32x4 v, float* o) { unpack8(make_uint4(v[0], v[1], v[2], v[3]), o); }
+  __device__ static void load(const uint16_t* p, float* o) { unpack8(*reinterpret_cast<const uint4*>(p), o); }
   __device__ static void store(uint16_t* p, const float* o) { *reinterpret_cast<uint4*>(p) = pack8(o); }
 };
 
@@ -64,36 +62,9 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   const int64_t row0 = j * p.r - p.raw_start[b];           // raw row of its first token
 
   const float* lg = p.logits + (int64_t)b * p.lg_bs + row0;
-  const T* kr = reinterpret_cast<const T*>(p.k_raw) + (int64_t)b * p.kr_bs + row0 * p.kr_rs + c * N;
-  const T* vr = reinterpret_cast<const T*>(p.v_raw) + (int64_t)b * p.vr_bs + row0 * p.vr_rs + c * N;
-  // The thread's rows are g, g + G, ...; they are taken in batches of PR whose raw
-  // chunks and logits sit in registers.  The first batch's loads go out before the
-  // logits' maximum is known, so that the block's reads overlap the max pass.
-  constexpr int PR = 8;
-  u32x4 rk[PR], rv[PR];
-  float lv[PR];
-  auto load_batch = [&](int u0) {
-#pragma unroll
-    for (int q = 0; q < PR; ++q) {
-      const int u = u0 + q * p.g;
-      if (u < p.r) {
-        rk[q] = Chunk<T>::raw(kr + (int64_t)u * p.kr_rs);
-        if (HV) rv[q] = Chunk<T>::raw(vr + (int64_t)u * p.vr_rs);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < PR; ++q) {
-      const int u = u0 + q * p.g;
-      lv[q] = u < p.r ? lg[u] : -INFINITY;
-    }
-  };
   float mx = -INFINITY;
-  if (active) {
-    load_batch(g);
-#pragma unroll
-    for (int q = 0; q < PR; ++q) mx = fmaxf(mx, lv[q]);
-    for (int u = g + PR * p.g; u < p.r; u += p.g) mx = fmaxf(mx, lg[u]);
-  }
+  if (active)
+    for (int u = g; u < p.r; u += p.g) mx = fmaxf(mx, lg[u]);
   s_max[tid] = mx;
   const int R = ROPE ? p.rope : 0, hr = R / 2, lo = p.d - R;
   if (R)
@@ -110,34 +81,31 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
 #pragma unroll
   for (int e = 0; e < N; ++e) { ak[e] = 0.f; av[e] = 0.f; }
   if (active) {
-    for (int u0 = g; u0 < p.r; u0 += PR * p.g) {
-      if (u0 != g) load_batch(u0);
+    const T* kr = reinterpret_cast<const T*>(p.k_raw) + (int64_t)b * p.kr_bs + row0 * p.kr_rs + c * N;
+    const T* vr = reinterpret_cast<const T*>(p.v_raw) + (int64_t)b * p.vr_bs + row0 * p.vr_rs + c * N;
+#pragma unroll 4
+    for (int u = g; u < p.r; u += p.g) {
+      const float w = __expf(lg[u] - mx);
+      float xk[N], xv[N];
+      Chunk<T>::load(kr + (int64_t)u * p.kr_rs, xk);
+      if (HV) Chunk<T>::load(vr + (int64_t)u * p.vr_rs, xv);
+      if (R) {
+        // raw rows are rotated at their positions j*r + u: undo the in-block part u
+        // here, the block part j*r once on the pooled entry
 #pragma unroll
-      for (int q = 0; q < PR; ++q) {
-        const int u = u0 + q * p.g;
-        if (u >= p.r) continue;
-        const float w = __expf(lv[q] - mx);
-        float xk[N], xv[N];
-        Chunk<T>::unpack(rk[q], xk);
-        if (HV) Chunk<T>::unpack(rv[q], xv);
-        if (R) {
-          // raw rows are rotated at their positions j*r + u: undo the in-block part u
-          // here, the block part j*r once on the pooled entry
-#pragma unroll
-          for (int k2 = 0; k2 < N / 2; ++k2) {
-            const int e0 = c * N + 2 * k2;
-            if (e0 < lo) continue;
-            const float2 cs = s_cs[u * hr + (e0 - lo) / 2];
-            rot2(xk[2 * k2], xk[2 * k2 + 1], cs.x, cs.y, true);
-            if (HV && p.rope_v) rot2(xv[2 * k2], xv[2 * k2 + 1], cs.x, cs.y, true);
-          }
+        for (int k2 = 0; k2 < N / 2; ++k2) {
+          const int e0 = c * N + 2 * k2;
+          if (e0 < lo) continue;
+          const float2 cs = s_cs[u * hr + (e0 - lo) / 2];
+          rot2(xk[2 * k2], xk[2 * k2 + 1], cs.x, cs.y, true);
+          if (HV && p.rope_v) rot2(xv[2 * k2], xv[2 * k2 + 1], cs.x, cs.y, true);
         }
-        ws += w;
+      }
+      ws += w;
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          ak[e] = fmaf(w, xk[e], ak[e]);
-          if (HV) av[e] = fmaf(w, xv[e], av[e]);
-        }
+      for (int e = 0; e < N; ++e) {
+        ak[e] = fmaf(w, xk[e], ak[e]);
+        if (HV) av[e] = fmaf(w, xv[e], av[e]);
       }
     }
   }
