@@ -132,7 +132,19 @@ struct AttnPlan {
   int64_t rows, n_keys, splits, kps;
   size_t off_q, ws_bytes;   // off_q: prepared bf16 queries (when qprep), after the partials
   bool fits;                // the split count stays within what the merge takes
+  bool qtile;               // prefill: CSA picks per row (slot 0) + HCA/window per query tile (slot 1)
 };
+
+// Prefill chunks whose queries share HCA entries and window rows: bf16, rows of up to
+// 128 with separate K and V, 32 to 128 heads (two 16-head tiles per wave, 256 / H
+// queries per workgroup), the CSA branch and at least one of the others on, no
+// batch-invariant plan (a tile's chunking depends on its neighbours' positions).
+bool qtile_ok(const v4a_attn_args* a, bool prefill) {
+  const int ntq = a->heads / 16;
+  return prefill && a->tq > 1 && a->dtype == V4A_BF16 && a->dim <= 128 && !(a->flags & V4A_SHARED_KV) &&
+         a->kv_dtype != V4A_FP8_E4M3 && !(a->flags & V4A_BATCH_INVARIANT) && a->heads % 32 == 0 && ntq >= 2 &&
+         ntq <= 8 && (a->branch_mask & V4A_CSA) && (a->branch_mask & (V4A_HCA | V4A_SWA));
+}
 
 // bf16 queries with a norm gain or a rotation are prepared once per row
 // (launch_qprep) into the workspace: rows * heads * dim bf16
@@ -175,9 +187,19 @@ constexpr int64_t kMinKeysPerSplit = 128;
 // keys per split of the batch-invariant plans
 constexpr int64_t kInvariantKeysPerSplit = 256;
 
-AttnPlan plan_attn(const v4a_attn_args* a) {
+AttnPlan plan_attn(const v4a_attn_args* a, bool prefill = false) {
   AttnPlan P{};
   P.rows = (int64_t)a->batch * a->tq;
+  if (qtile_ok(a, prefill)) {
+    P.qtile = true;
+    P.n_keys = a->topk;
+    P.splits = 2;   // slot 0 holds the CSA partial; the query-tile kernel writes o itself
+    P.kps = round_up(std::max<int64_t>(a->topk, 1), kAttnChunk);
+    P.ws_bytes = (size_t)(P.rows * P.splits * a->heads) * (size_t)(a->dim + 2) * 4 + 256;
+    P.off_q = add_qprep(a, P.rows, P.ws_bytes);
+    P.fits = true;
+    return P;
+  }
   const int64_t pmax = a->pos_max;
   P.n_keys = ((a->branch_mask & V4A_CSA) ? a->topk : 0) + ((a->branch_mask & V4A_HCA) ? (pmax + 1) / a->hca_ratio : 0) +
              ((a->branch_mask & V4A_SWA) ? std::min<int64_t>(a->window, pmax + 1) : 0);
@@ -447,7 +469,7 @@ AttnP make_attn_params(const v4a_attn_args* a, const AttnPlan& P, void* ws) {
 v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream_t s, bool prefill) {
   V4A_TRY(validate_attn(a, prefill));
   if (a->batch == 0) return ok();
-  const AttnPlan P = plan_attn(a);
+  const AttnPlan P = plan_attn(a, prefill);
   if (!P.fits)
     return fail(V4A_ENOTSUP, "%lld key splits per query exceed the merge's %d (batch-invariant plans split every 256 keys)",
                 (long long)P.splits, kAttnMaxSplits);
@@ -456,8 +478,20 @@ v4a_status run_attn(const v4a_attn_args* a, void* ws, size_t ws_bytes, hipStream
   AttnP p = make_attn_params(a, P, ws);
   V4A_TRY(prep_queries(a, p, P.rows, ws, P.off_q, s, true));
   const int kid = prefill ? V4A_K_PREFILL : V4A_K_ATTN;
-  V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
-  if (P.splits > 1) {
+  if (P.qtile) {
+    // the CSA picks of every row in one split (partials in slot 0 of 2), then the HCA
+    // entries and the window per query tile, which join that partial and write o
+    AttnP csa = p, rest = p;
+    csa.key_lo = 0;
+    csa.key_hi = a->topk;
+    csa.splits = 1;
+    rest.split_base = 1;
+    V4A_TRY(hip_check(launch_attn(a->dtype, csa, (int)P.rows, s, kid), "attention launch"));
+    V4A_TRY(hip_check(launch_attn_qtile(rest, a->batch, s, kid), "query-tile attention launch"));
+  } else {
+    V4A_TRY(hip_check(launch_attn(a->dtype, p, (int)P.rows, s, kid), "attention launch"));
+  }
+  if (P.splits > 1 && !P.qtile) {
     const bool inv = (a->flags & V4A_BATCH_INVARIANT) != 0;
     V4A_TRY(hip_check(launch_merge(p, (int)P.rows, inv, s, V4A_K_MERGE), "merge launch"));
   }
@@ -808,7 +842,7 @@ v4a_status v4attn_decode_step_noalloc(const v4a_index_args* ix, const v4a_attn_a
 
 size_t v4attn_prefill_chunk_workspace(const v4a_attn_args* a) {
   if (validate_attn(a, true) != V4A_OK || a->batch == 0) return 0;
-  const AttnPlan P = plan_attn(a);
+  const AttnPlan P = plan_attn(a, true);
   return P.fits ? P.ws_bytes : 0;
 }
 

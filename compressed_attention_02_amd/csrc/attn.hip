@@ -162,6 +162,31 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnP p) {
   }
 }
 
+// ------------------------------------------------------------------ prefill query tiles
+// One workgroup per (query tile, sequence), one per CU.  d = 128: sixteen waves of
+// one head tile each (four waves per SIMD); d = 64: eight waves of two.
+template <int D, int NW, int HT>
+__global__ __launch_bounds__(NW * 64, (NW / 4)) void attn_qtile_kernel(AttnP p) {
+  __shared__ __align__(16) QTileSmem<D> sm;
+  attn_qtile_block<D, NW, HT>(p, blockIdx.x, blockIdx.y, sm);
+}
+constexpr int kQTileNW128 = 16, kQTileHT128 = 1;
+
+hipError_t launch_attn_qtile(const AttnP& p, int batch, hipStream_t s, int tid) {
+  const int ntq = p.heads / 16;
+  if (p.heads % 32 != 0 || ntq < 2 || ntq > 8 || (p.dim != 64 && p.dim != 128) || p.f8 || p.skv ||
+      p.splits_total < 2)
+    return hipErrorInvalidValue;
+  const int nw = p.dim == 64 ? 8 : kQTileNW128, ht = p.dim == 64 ? 2 : kQTileHT128;
+  const int wpq = ntq / ht;
+  if (wpq < 1 || nw % wpq != 0 || nw / wpq > kMaxQTile) return hipErrorInvalidValue;
+  const int qt = nw / wpq;
+  const dim3 grid((unsigned)((p.tq + qt - 1) / qt), (unsigned)batch);
+  if (p.dim == 64) V4A_LAUNCH(tid, (attn_qtile_kernel<64, 8, 2>), grid, dim3(8 * 64), 0, s, p);
+  else V4A_LAUNCH(tid, (attn_qtile_kernel<128, kQTileNW128, kQTileHT128>), grid, dim3(kQTileNW128 * 64), 0, s, p);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ query prep
 // once per row, when no score launch of the same step carries it (qprep_impl.hpp)
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepP p) { qprep_block(p, blockIdx.x, blockIdx.y); }

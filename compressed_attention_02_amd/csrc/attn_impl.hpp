@@ -939,4 +939,176 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   }
 }
 
+// ------------------------------------------------------------------ prefill query tiles
+// [QbitAI] 混合注意力机制, HCA and window paragraphs: inside a prefill chunk the HCA
+// entries and raw window rows one query sees are, up to the causal edge, the ones its
+// neighbours see.  A workgroup of NW waves of HT head tiles each takes
+// QT = 16 NW HT / H consecutive queries of one sequence and streams the union of
+// their keys, HCA entries [0, e_vis(last)) then raw positions [w_lo(first), p(last)],
+// through LDS once for all of them; each query masks what it does not see (the
+// causal HCA edge, its own window bounds).  So every key row is read from L2 once
+// per QT queries instead of once per query.  The CSA picks differ per query and are
+// attended per row by the launch before this one, which leaves each row's partial
+// (O, m, l) in split slot 0; this kernel joins it to its own state and writes the
+// row's o and lse.  Rows past tq in a sequence's last tile are computed on the last
+// row's queries and not written.
+constexpr int kMaxQTile = 8;
+
+template <int D>
+struct QTileSmem {
+  uint16_t buf[4 * kAttnChunk * D];           // K0, K1, V0, V1
+  float bias[2][kMaxQTile][kAttnChunk];       // [chunk parity][query][key]
+  __device__ uint16_t* K(int c) { return buf + c * kAttnChunk * D; }
+  __device__ uint16_t* V(int c) { return buf + (2 + c) * kAttnChunk * D; }
+};
+
+// the tile's union key list and one query's view of it
+struct QTileKeys {
+  const uint16_t *kh, *vh, *kr, *vr, *fallback;
+  int64_t kh_rs, vh_rs, kr_rs, vr_rs;
+  int64_t n_h, n_u, w_lo0, raw0;     // HCA entries, all keys, first window position, raw_start
+  // query q (absent ones mirror the last present one) sees HCA entries [0, evis[q])
+  // and window keys with t - n_h in (hi[q] - W, hi[q]]
+  int evis[kMaxQTile], hi[kMaxQTile];
+  int W, qt;
+};
+
+// Loads chunk kc0 of the union list into (sK, sV) and writes every query's mask.
+template <int D, int NW>
+__device__ __forceinline__ void issue_qchunk(const QTileKeys& T, int64_t kc0, uint16_t* sK, uint16_t* sV,
+                                             float (*bias)[kAttnChunk], int wave, int lane) {
+  constexpr int PS = D / 8, RPI = 64 / PS, RBW = kAttnChunk / RPI / NW;
+  static_assert(D <= 128 && RBW >= 1 && RBW * RPI * NW == kAttnChunk, "rows of up to 128, spread over the waves");
+  const int prow = lane / PS, ppiece = lane % PS;
+#pragma unroll
+  for (int u = 0; u < RBW; ++u) {
+    const int r0 = (wave * RBW + u) * RPI;
+    const int r = r0 + prow;
+    const int64_t t = kc0 + r;
+    const bool in_h = t < T.n_h, in_w = !in_h && t < T.n_u;
+    const int64_t pt = T.w_lo0 + (t - T.n_h);          // window keys: their position
+    const uint16_t* kp = in_h ? row_ptr(T.kh, (uint32_t)t, T.kh_rs)
+                              : in_w ? row_ptr(T.kr, (uint32_t)(pt - T.raw0), T.kr_rs) : T.fallback;
+    const uint16_t* vp = in_h ? row_ptr(T.vh, (uint32_t)t, T.vh_rs)
+                              : in_w ? row_ptr(T.vr, (uint32_t)(pt - T.raw0), T.vr_rs) : T.fallback;
+    lds_load16(kp + (ppiece ^ swz_k<D>(r)) * 8, lds_addr(sK + r0 * D));
+    lds_load16(vp + (ppiece ^ swz_v<D>(r)) * 8, lds_addr(sV + r0 * D));
+    if (ppiece == 0) {
+      const int tw = (int)(t - T.n_h);
+#pragma unroll
+      for (int q = 0; q < kMaxQTile; ++q) {
+        if (q >= T.qt) break;
+        const bool ok = in_h ? t < T.evis[q] : in_w && tw <= T.hi[q] && tw > T.hi[q] - T.W;
+        bias[q][r] = ok ? 0.f : -INFINITY;
+      }
+    }
+  }
+}
+
+template <int D, int NW, int HT>
+__device__ __forceinline__ void attn_qtile_block(const AttnP& p, int tile, int b, QTileSmem<D>& sm) {
+  constexpr int KS = D / 32, DT = D / 16, CH = kAttnChunk;
+  constexpr int LPW = 2 * (CH * (D / 8) / 64 / NW);   // a chunk's direct loads per wave (K and V)
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntq = p.heads / 16;                 // head tiles per query
+  const int wpq = ntq / HT;                     // waves per query
+  const int QT = NW / wpq;                      // queries per workgroup tile
+  const int q = wave / wpq, t0 = (wave % wpq) * HT;
+  const int i0 = tile * QT;
+  const int nq = min(QT, p.tq - i0);            // queries of this tile that exist
+  const int i = i0 + min(q, nq - 1);            // the row this wave computes
+  const int64_t pos_ld = p.pos0[b];
+  const int64_t raw_ld = (p.mask & 4u) ? p.raw_start[b] : 0;
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_bs + (int64_t)i * p.q_rs;
+  bf16x8_t Qb[HT][KS];
+#pragma unroll
+  for (int t = 0; t < HT; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+      Qb[t][s2] = *reinterpret_cast<const bf16x8_t*>(qrow + ((t0 + t) * 16 + col) * D + s2 * 32 + grp * 8);
+
+  QTileKeys T;
+  const int64_t pos0 = uniform_i64(pos_ld) + i0;
+  T.qt = QT;
+  T.W = ((p.mask & 4u) && p.W > 0) ? p.W : 0;
+  const int64_t p_last = pos0 + nq - 1;
+  T.n_h = (p.mask & 2u) ? (p_last + 1) / p.mh : 0;
+  T.w_lo0 = pos0 - T.W + 1 > 0 ? pos0 - T.W + 1 : 0;
+#pragma unroll
+  for (int qq = 0; qq < kMaxQTile; ++qq) {
+    const int64_t pq = pos0 + min(qq, nq - 1);
+    T.evis[qq] = (p.mask & 2u) ? (int)((pq + 1) / p.mh) : 0;
+    T.hi[qq] = (int)(pq - T.w_lo0);
+  }
+  T.n_u = T.n_h + (T.W > 0 ? p_last - T.w_lo0 + 1 : 0);
+  T.raw0 = uniform_i64(raw_ld);
+  T.fallback = qrow;
+  T.kh = (p.mask & 2u) ? reinterpret_cast<const uint16_t*>(p.kh) + (int64_t)b * p.kh_bs : qrow;
+  T.vh = (p.mask & 2u) ? reinterpret_cast<const uint16_t*>(p.vh) + (int64_t)b * p.vh_bs : qrow;
+  T.kr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.kr) + (int64_t)b * p.kr_bs : qrow;
+  T.vr = (p.mask & 4u) ? reinterpret_cast<const uint16_t*>(p.vr) + (int64_t)b * p.vr_bs : qrow;
+  T.kh_rs = p.kh_rs; T.vh_rs = p.vh_rs; T.kr_rs = p.kr_rs; T.vr_rs = p.vr_rs;
+
+  const float sl2 = p.scale * kLog2e;
+  float m_run[HT], l_run[HT];
+  f32x4 O[HT][DT];
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int64_t nch = (T.n_u + CH - 1) / CH;
+  if (nch > 0) issue_qchunk<D, NW>(T, 0, sm.K(0), sm.V(0), sm.bias[0], wave, lane);
+  if (nch > 1) issue_qchunk<D, NW>(T, CH, sm.K(1), sm.V(1), sm.bias[1], wave, lane);
+  for (int64_t c = 0; c < nch; ++c) {
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    const int par = (int)(c & 1);
+    attend_chunk<D, HT, 1>(sm.K(par), sm.V(par), sm.bias[par][q], Qb, O, m_run, l_run, sl2, col, grp, 0);
+    __syncthreads();
+    if (c + 2 < nch) issue_qchunk<D, NW>(T, (c + 2) * CH, sm.K(par), sm.V(par), sm.bias[par], wave, lane);
+  }
+  if (q >= nq) return;
+  // the row's CSA partial (slot 0, written by the launch before this one) joins this
+  // state, and the row's output is written here: o, lse (no merge launch)
+  const int64_t row = (int64_t)b * p.tq + i;
+  const int64_t pos = pos0 + q;
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    const int head = (t0 + t) * 16 + col;
+    const int64_t slot = (row * p.heads + head) * p.splits_total;
+    const float2 mlc = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
+    const float* pc = p.part_o + slot * D;
+    const float m = fmaxf(m_run[t], mlc.x);
+    const float a = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - m);
+    const float ac = mlc.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlc.x - m);
+    const float l = col_sum4(l_run[t]) * a + mlc.y * ac;
+    float lse;
+    const float f = finish_head(m, l, p.sink, head, &lse);
+    const int64_t orow = (int64_t)b * p.o_bs + (int64_t)i * p.o_rs + head * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float4 oc = *reinterpret_cast<const float4*>(pc + dt * 16 + 4 * grp);
+      float ov[4] = {(O[t][dt][0] * a + oc.x * ac) * f, (O[t][dt][1] * a + oc.y * ac) * f,
+                     (O[t][dt][2] * a + oc.z * ac) * f, (O[t][dt][3] * a + oc.w * ac) * f};
+      if (p.rope_out) {  // back at -pos: channels dt*16 + 4*grp + e, pairs inside the lane
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int e0 = dt * 16 + 4 * grp + 2 * k2;
+          if (e0 < D - p.rope) continue;
+          float cs, sn;
+          rope_cs((double)pos, (e0 - (D - p.rope)) / 2, p.rope, p.rope_lb, cs, sn);
+          rot2(ov[2 * k2], ov[2 * k2 + 1], cs, sn, true);
+        }
+      }
+      store_out4(p.o, p.o_bf16, orow + dt * 16 + 4 * grp, ov[0], ov[1], ov[2], ov[3]);
+    }
+    if (grp == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)i * p.lse_rs + head] = lse;
+  }
+}
+
 }  // namespace v4a

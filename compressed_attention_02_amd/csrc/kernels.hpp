@@ -122,6 +122,12 @@ struct AttnP {
 };
 hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int tid);
 
+// Prefill (tq > 1, bf16, d <= 128, separate K and V): the HCA entries and the window
+// of 256 / H consecutive queries per workgroup, streamed once for all of them; each
+// row's CSA partial in split slot 0 of p.splits_total (>= 2) joins the result, and
+// the rows' o and lse are written.  Grid: (ceil(tq / (256 / H)), batch).
+hipError_t launch_attn_qtile(const AttnP& p, int batch, hipStream_t s, int tid);
+
 // fixed_width: always 32 output columns per workgroup (batch-invariant plans: the
 // width sets how the splits are grouped in the sum)
 hipError_t launch_merge(const AttnP& p, int nrows, bool fixed_width, hipStream_t s, int tid);
