@@ -90,7 +90,7 @@ def load_trace(workload: str):
 # (their code, without comments or spacing); once the code changes the figure no longer
 # describes the kernel and is not reported.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_bf16_c3.json")
-SCORE_SOURCES = ("index.hip", "select_impl.hpp", "qprep_impl.hpp", "common.hpp", "kernels.hpp")
+SCORE_SOURCES = ("index.hip", "score_impl.hpp", "select_impl.hpp", "qprep_impl.hpp", "common.hpp", "kernels.hpp")
 
 
 def score_source_hash() -> str:

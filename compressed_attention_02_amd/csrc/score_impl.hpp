@@ -153,7 +153,8 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
     if (next) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const int64_t tile0 = tile * TILE;
-    float mine = 0.f;       // score of key tile0 + 64*wave + lane after the loop
+    float mine;             // score of key tile0 + 64*wave + lane after the loop
+    float pu[4];            // this lane's part of key group u (keys 16 u .. 16 u + 15 of the wave)
     float kscale = 1.f;     // FP8: the scale of that key's row (rows past n_vis: the last row's)
     if constexpr (FP8)
       kscale = p.ki_scale[(int64_t)b * p.ks_bs + min(tile0 + wave * 64 + lane, nvis - 1)];
@@ -181,8 +182,19 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
 #pragma unroll
         for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fmaxf(FP8 ? acc[e] * cs : acc[e], 0.f), part);
       }
-      part = col_sum4(part);
-      if (grp == u) mine = part;
+      pu[u] = part;
+    }
+    // sum over the four lane groups, transposed: a row swap (groups 0<->1, 2<->3)
+    // leaves even groups the pair sum of key group 2v and odd groups that of 2v+1; a
+    // half swap (0<->2, 1<->3) completes group g's key group g (the additions of a
+    // row-then-half sum)
+    {
+      const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[0]), __float_as_uint(pu[1]), false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[2]), __float_as_uint(pu[3]), false, false);
+      const float a01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+      const float a23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+      const auto sh = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+      mine = __uint_as_float(sh[0]) + __uint_as_float(sh[1]);
     }
     const int64_t j = tile0 + wave * 64 + lane;
     if (j < nvis) sc[j] = mine;
@@ -260,7 +272,8 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
       for (int s2 = 0; s2 < KS; ++s2)
         A[mt][s2] = *reinterpret_cast<const bf16x8_t*>(qi + (mt * 16 + col) * DI + s2 * 32 + grp * 8);
       const f32x4 wq = *reinterpret_cast<const f32x4*>(wi + mt * 16 + 4 * grp);
-      w[mt][0] = wq[0]; w[mt][1] = wq[1]; w[mt][2] = wq[2]; w[mt][3] = wq[3];
+      // the halving of (u.k + sum_h w_h |x_h|) / 2 goes into w and u (exact)
+      w[mt][0] = 0.5f * wq[0]; w[mt][1] = 0.5f * wq[1]; w[mt][2] = 0.5f * wq[2]; w[mt][3] = 0.5f * wq[3];
     }
     float u[KS][8];
 #pragma unroll
@@ -281,10 +294,13 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
     for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float hi = bf2f(f2bf(u[s2][e]));
-        const float mid = bf2f(f2bf(u[s2][e] - hi));
-        const float lo = u[s2][e] - hi - mid;
-        const float v = col == 0 ? hi : col == 1 ? mid : col == 2 ? lo : 0.f;
+        const float uh = 0.5f * u[s2][e];
+        const float hi = bf2f(f2bf(uh));
+        const float mid = bf2f(f2bf(uh - hi));
+        const float lo = uh - hi - mid;
+        // rows 0, 4, 8: the parts land in lane groups 0, 1, 2 (output element 0),
+        // which the cross-lane sum of the score adds up
+        const float v = col == 0 ? hi : col == 4 ? mid : col == 8 ? lo : 0.f;
         U[s2][e] = (__bf16)v;
       }
   }
@@ -300,29 +316,42 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
     if (tile + stride < ntile) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPW));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's share of the tile is in LDS
-    float mine[4] = {0.f, 0.f, 0.f, 0.f};
+    // lane (col, grp) ends with the score of key 16 u + col for u = 4 q + grp in mine[q]
+    float mine[4];
 #pragma unroll
-    for (int u = 0; u < kTile / 16; ++u) {
-      const int t = u * 16 + col;
-      bf16x8_t Bv[KS];
+    for (int q4 = 0; q4 < kTile / 64; ++q4) {
+      float pu[4];   // this lane's part of key group u = 4 q4 + uu
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2)
-        Bv[s2] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s2 * 4 + grp) ^ kx) * 16));
-      f32x4 lin = {0.f, 0.f, 0.f, 0.f};   // u . k in rows 0..2 (lane group 0)
+      for (int uu = 0; uu < 4; ++uu) {
+        const int t = (4 * q4 + uu) * 16 + col;
+        bf16x8_t Bv[KS];
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) lin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(U[s2], Bv[s2], lin, 0, 0, 0);
-      float part = 0.f;
+        for (int s2 = 0; s2 < KS; ++s2)
+          Bv[s2] = *reinterpret_cast<const bf16x8_t*>(buf + t * ROWB + (((s2 * 4 + grp) ^ kx) * 16));
+        f32x4 lin = {0.f, 0.f, 0.f, 0.f};   // a part of u . k / 2 in element 0 of lane groups 0..2
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < KS; ++s2) lin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(U[s2], Bv[s2], lin, 0, 0, 0);
+        float part = lin[0];
 #pragma unroll
-        for (int s2 = 0; s2 < KS; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s2], Bv[s2], acc, 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fabsf(acc[e]), part);
+          for (int s2 = 0; s2 < KS; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][s2], Bv[s2], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = fmaf(w[mt][e], fabsf(acc[e]), part);
+        }
+        pu[uu] = part;
       }
-      part += (lin[0] + lin[1]) + lin[2];
-      part = 0.5f * col_sum4(part);
-      if (grp == (u & 3)) mine[u >> 2] = part;
+      // sum over the four lane groups, transposed: a row swap (groups 0<->1, 2<->3)
+      // pairs the parts of key groups 2v and 2v+1 so that even groups hold 2v's pair
+      // sum and odd groups 2v+1's; a half swap (0<->2, 1<->3) then completes group g's
+      // key group 4 q4 + g.  The additions are those of a row-then-half sum.
+      const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[0]), __float_as_uint(pu[1]), false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pu[2]), __float_as_uint(pu[3]), false, false);
+      const float a01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+      const float a23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+      const auto sh = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+      mine[q4] = __uint_as_float(sh[0]) + __uint_as_float(sh[1]);
     }
     if (have) {
       const int64_t tile0 = tile * kTile;
