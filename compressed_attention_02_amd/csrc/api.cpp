@@ -535,6 +535,7 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   tp.sel = (float*)a->sel_scores.ptr; tp.sel_bs = a->sel_scores.batch_stride; tp.sel_rs = a->sel_scores.row_stride;
   tp.sc_rs = P.sc_rs; tp.key_rs = P.key_rs; tp.info_rs = P.info_rs; tp.tq = a->tq; tp.ratio = a->ratio; tp.topk = a->topk;
   tp.ntiles_cap = (int)P.ntiles;
+  tp.rep_top = P.multi ? kPrefillTileTop : kTileTop;
   return L;
 }
 

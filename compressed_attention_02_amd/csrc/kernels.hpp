@@ -29,7 +29,8 @@ hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t
 // ---------------------------------------------------------------- indexer
 constexpr int kTile = 256;        // blocks per score tile
 constexpr int kWaveTop = 4;       // (key, id) pairs each 64-block wave picks
-constexpr int kTileTop = 8;       // (key, id) pairs each tile reports, of its four waves' picks
+constexpr int kTileTop = 8;       // (key, id) slots of a tile report
+constexpr int kPrefillTileTop = 4;  // slots the prefill score kernel fills (the rest are empty)
 constexpr int kPoolCap = 4096;    // candidate pool of the per-row selection (LDS)
 constexpr int kMaxTopk = 2048;
 constexpr int kSelThreads = 512;
@@ -79,6 +80,7 @@ struct SelectP {
   int64_t sc_rs, key_rs, info_rs;
   int tq, row0, ratio, topk;
   int ntiles_cap;     // score tiles of the longest row (pos_max): bounds the report loads
+  int rep_top;        // report slots per tile that the score kernel fills (kTileTop or kPrefillTileTop)
 };
 hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
 

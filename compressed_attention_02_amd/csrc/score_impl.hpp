@@ -362,7 +362,8 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
         if (j < nvis) sc[j] = mine[blk];
         kb[blk] = j < nvis ? score_key(mine[blk]) : 0u;
       }
-      tile_report(kb, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop, p.rep_info + (int64_t)lr * p.info_rs + tile);
+      tile_report<kPrefillTileTop>(kb, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop,
+                                   p.rep_info + (int64_t)lr * p.info_rs + tile);
     }
     __syncthreads();   // every wave is done with this buffer
     if (tile + 2 * stride < ntile) issue(tile + 2 * stride, buf);

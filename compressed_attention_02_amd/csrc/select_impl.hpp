@@ -16,10 +16,12 @@ __device__ __forceinline__ void row_coords(int row, int tq, const int64_t* pos0,
 }
 
 // Reports of the score kernels, per tile of kTile = 256 blocks: the keys of the
-// tile's kTileTop best blocks (higher key first, then lower id) in ascending id
-// order (key 0 = no element), and an info word (offsets of entries 0-3, offsets of
-// entries 4-7, bound, 0): 8-bit offsets from the tile's first block, and the key of
-// the best block the report leaves out (0 if none), which bounds every other one.
+// tile's best blocks, kTileTop of them in decode (the selection is on the step's
+// critical path, so its rescans should be rare) and 4 in prefill (about one block
+// per tile is picked there, and a rescan costs the selection little), in ascending
+// id order (key 0 = no element); and an info word (offsets of entries 0-3, offsets
+// of entries 4-7, bound, 0): 8-bit offsets from the tile's first block, and the key
+// of the best block the report leaves out (0 if none), which bounds every other one.
 
 // Lane `dst` receives v (a forward permute); every lane sends, so lanes with nothing
 // to send aim at lane 63, which no caller reads.
@@ -32,30 +34,31 @@ __device__ __forceinline__ uint32_t bits_below(uint64_t m) {
 }
 
 // The tile report made by one wave whose lane L holds the keys kb[q] of blocks
-// 64 q + L (0 for none).  Each of kTileTop rounds takes a 32-bit wave maximum (DPP)
-// of the keys not yet taken and gives it to the lowest id that holds it (the first
-// quarter q with a ballot hit, then its lowest lane), so ties go to the lower id;
-// one more maximum is the bound.  The winners then go to lanes 0..7 in id order (a
+// 64 q + L (0 for none), with the R <= kTileTop best (entries past R are empty).
+// Each of R rounds takes a 32-bit wave maximum (DPP) of the keys not yet taken and
+// takes one block holding it: the lowest lane with it, and that lane's first quarter.
+// Which of several equal keys is taken does not matter for the selection: if one
+// is left out, the bound (one more maximum) equals that key, so a threshold at it
+// sends the tile to a rescan.  The winners then go to lanes 0..R-1 in id order (a
 // forward permute per quarter) and are written out: keys (8 words) and info.
+template <int R>
 __device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* keys, uint4* info) {
-  static_assert(kTileTop == 8, "two offset words per tile");
+  static_assert(kTileTop == 8 && R >= 1 && R <= kTileTop, "two offset words per tile");
   const int lane = threadIdx.x & 63;
   uint32_t k[4] = {kb[0], kb[1], kb[2], kb[3]};
   uint64_t won[4] = {0ull, 0ull, 0ull, 0ull};
 #pragma unroll 1
-  for (int r = 0; r < kTileTop; ++r) {
-    const uint32_t m = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lm = max(max(k[0], k[1]), max(k[2], k[3]));
+    const uint32_t m = wave_max_u32(lm);
     if (m == 0u) break;
-    bool taken = false;
+    const int l = __builtin_ctzll(__ballot(lm == m));
+    const int qs = k[0] == m ? 0 : k[1] == m ? 1 : k[2] == m ? 2 : 3;   // lane-local
+    const int qw = __builtin_amdgcn_readlane(qs, l);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint64_t at = __ballot(k[q] == m);
-      if (!taken && at) {
-        const int l = __builtin_ctzll(at);
-        won[q] |= 1ull << l;
-        if (lane == l) k[q] = 0u;
-        taken = true;
-      }
+      if (q == qw) won[q] |= 1ull << l;
+      if (lane == l && q == qs) k[q] = 0u;
     }
   }
   const uint32_t bound = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
@@ -95,7 +98,7 @@ __device__ __forceinline__ void tile_report_waves(uint32_t key, bool valid, int 
     uint32_t kb[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) kb[q] = st.key[par][q * 64 + lane];
-    tile_report(kb, keys, info);
+    tile_report<kTileTop>(kb, keys, info);
   }
 }
 
@@ -146,6 +149,17 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelShared
   omx = sh.wmax[0];
   for (int w = 1; w < kNW; ++w) { omn = min(omn, sh.wmin[w]); omx = max(omx, sh.wmax[w]); }
   __syncthreads();
+}
+
+// Width (as a shift) of the power-of-two bins over [lo, hi] (lo <= hi): the
+// smallest one for which the bin of hi, (hi - lo) >> shift, is below kBins, so the
+// nb = ((hi - lo) >> shift) + 1 bins fit the histogram.  Bounding the rounded-up
+// count of bins rather than (hi - lo + 1) >> shift matters when that quotient is
+// exactly kBins with a remainder: that range needs kBins + 1 bins of that width.
+__device__ __forceinline__ int bin_shift(uint32_t lo, uint32_t hi) {
+  int shift = 0;
+  while (((hi - lo) >> shift) >= (uint32_t)kBins) ++shift;
+  return shift;
 }
 
 // Bin of sh.hist[0..nb) holding the r-th element (1-based) counted from the top
@@ -204,10 +218,8 @@ __device__ __forceinline__ uint32_t rank_search(Each each, Keep keep, Val val, u
   n_equal = 0;
   if (lo > hi) return lo;   // nothing accepted (callers never ask for that)
   while (true) {
-    const uint64_t range = (uint64_t)hi - lo + 1;
-    int shift = 0;
-    while ((range >> shift) > (uint64_t)kBins) ++shift;
-    const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+    const int shift = bin_shift(lo, hi);
+    const int nb = (int)((hi - lo) >> shift) + 1;
     for (int t = threadIdx.x; t < nb; t += kSelThreads) sh.hist[t] = 0;
     __syncthreads();
     each([&](uint32_t key, uint32_t id) {
@@ -249,10 +261,8 @@ __device__ __forceinline__ uint32_t kth_key_floor(Each each, uint32_t r, SelShar
   uint32_t lo, hi;
   block_minmax(mn, mx, sh, lo, hi);
   if (lo > hi) return 0;
-  const uint64_t range = (uint64_t)hi - lo + 1;
-  int shift = 0;
-  while ((range >> shift) > (uint64_t)kBins) ++shift;
-  const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+  const int shift = bin_shift(lo, hi);
+  const int nb = (int)((hi - lo) >> shift) + 1;
   for (int t = threadIdx.x; t < nb; t += kSelThreads) sh.hist[t] = 0;
   __syncthreads();
   each([&](uint32_t key, uint32_t) { atomicAdd(&sh.hist[(key - lo) >> shift], 1u); });
@@ -309,10 +319,8 @@ __device__ __forceinline__ uint32_t reg_rank_search(const uint32_t (&keys)[kMaxT
   n_equal = 0;
   if (lo > hi) return lo;
   for (int level = 0;; ++level) {
-    const uint64_t range = (uint64_t)hi - lo + 1;
-    int shift = 0;
-    while ((range >> shift) > (uint64_t)kBins) ++shift;
-    const int nb = (int)(((uint64_t)(hi - lo) >> shift) + 1);
+    const int shift = bin_shift(lo, hi);
+    const int nb = (int)((hi - lo) >> shift) + 1;
     // levels 0 and 1 count into sh.hist and sh.hist2, which the caller zeroed
     uint32_t* h = (level & 1) ? sh.hist2 : sh.hist;
     if (level >= 2) {
@@ -451,9 +459,9 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
       for (int j = 0; j < kTileTop; ++j)
         if (uk[q][j] != 0u) f(uk[q][j], rep_id(q, j));
   };
-  // every tile of 256 visible blocks reports kTileTop of them, a partial last tile
-  // as many as it has
-  const int64_t n_rep = kTileTop * (nvis / kTile) + min<int64_t>(kTileTop, nvis % kTile);
+  // every tile of 256 visible blocks reports rep_top of them, a partial last tile
+  // at most as many as it has
+  const int64_t n_rep = (int64_t)p.rep_top * (nvis / kTile) + min<int64_t>(p.rep_top, nvis % kTile);
 
   if (ok && n_rep >= k) {
     // 1. the exact k-th key T of all the reports

@@ -91,6 +91,31 @@ def test_small_rows_and_padding():
         check_topk_row(idx[0, 0], s, k, f"n_vis={n_vis}")
 
 
+@pytest.mark.parametrize("n_vis,k,zero_rows", [(3000, 1024, 1), (65536, 512, 256)])
+def test_key_range_one_bin_past_histogram(n_vis, k, zero_rows):
+    """Keys spanning [key(0.0), key(~2.0156)]: the order-preserving keys of positive
+    floats are their bits with the top bit set, so the span is 2^30 + ~2^16, which at
+    bins of 2^17 keys needs 8193 bins, one more than the histogram holds; the bin width
+    must grow to 2^18.  (3000, 1024): the tile reports fall short of k and the whole
+    row is ranked; (65536, 512): the reports cover k and tile 0, all zero scores,
+    reports key(0.0) into the ranking of reported keys."""
+    qi, wi, ki, pos, rng = _inputs(n_vis, seed=7)
+    ki[0, :zero_rows] = 0.0                          # scores exactly 0
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    s = _scores(qi, wi, kb)
+    top = n_vis // 2 + 3
+    ki[0] *= 1.0 / s.max()                           # scores are positively homogeneous in the key row
+    ki[0, top] *= 2.0156 * s.max() / s[top]
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    s = _scores(qi, wi, kb)
+    bits = np.sort(s).astype(np.float32).view(np.uint32)
+    assert s.min() == 0.0 and int(np.argmax(s)) == top
+    assert (1 << 30) + 4096 <= int(bits[-1]) < (1 << 30) + (1 << 17) - 4096   # the span the case is about
+    idx, sel = _run(qi, wi, kb, pos, k)
+    check_topk_row(idx[0, 0], s, k, f"n_vis={n_vis}")
+    np.testing.assert_allclose(sel[0, 0], s[idx[0, 0]], rtol=1e-5)
+
+
 # ---------------------------------------------------------------- through the decode step
 def _run_step(qi, wi, ki, pos, k, heads=128, d=128, m=4, W=128):
     """The same selection through v4attn_decode_step (its candidates per group of
