@@ -105,6 +105,7 @@ __device__ __forceinline__ void tile_report_waves(uint32_t key, bool valid, int 
 // ------------------------------------------------------------------ selection
 constexpr int kNW = kSelThreads / 64;
 constexpr int kBins = 8192;
+constexpr int kGatherMax = 64;   // a bin of at most this many keys is ranked by one wave
 
 struct SelShared {
   uint32_t hist[kBins + 64];   // + one slot per lane for branch-free passes to discard into
@@ -120,6 +121,8 @@ struct SelShared {
   uint32_t fail[256], fcount[256], fbase[256];
   uint32_t n_pool, n_fail, flag;
   uint32_t hit_bin, hit_before;
+  uint32_t n_gather, gres[3];
+  uint32_t gkey[kGatherMax];   // the few keys of one histogram bin (reg_rank_search)
 };
 
 // inclusive prefix sum over the workgroup (one value per thread)
@@ -314,6 +317,7 @@ __device__ __forceinline__ uint32_t reg_rank_search(const uint32_t (&keys)[kMaxT
       mn = min(mn, v ? v : 0xffffffffu);
     }
   }
+  if (threadIdx.x == 0) sh.n_gather = 0;   // (ordered before the gather by the barriers below)
   uint32_t lo, hi;
   block_minmax(mn, mx, sh, lo, hi);
   n_equal = 0;
@@ -348,6 +352,40 @@ __device__ __forceinline__ uint32_t reg_rank_search(const uint32_t (&keys)[kMaxT
     if (shift == 0 || r == in_bin) {   // one value left, or the bin is taken whole
       n_equal = in_bin;
       return nlo;
+    }
+    if (in_bin <= (uint32_t)kGatherMax) {
+      // few keys in the bin: gathered into LDS, and one wave ranks them by counting
+      // (lane i holds key i and counts the keys above it and equal to it); the r-th
+      // largest is the key of a lane with above < r <= above + equal
+#pragma unroll
+      for (int q = 0; q < kMaxTilesPerThread; ++q) {
+        if (q >= tpt) break;
+#pragma unroll
+        for (int j = 0; j < kTileTop; ++j) {
+          const uint32_t v = keys[q][j];
+          if (v >= nlo && v <= nhi) sh.gkey[atomicAdd(&sh.n_gather, 1u)] = v;
+        }
+      }
+      __syncthreads();
+      if ((threadIdx.x >> 6) == 0) {
+        const uint32_t mine = lane < (int)in_bin ? sh.gkey[lane] : 0u;
+        uint32_t above = 0, equal = 0;
+        for (uint32_t j = 0; j < in_bin; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)j);
+          above += kj > mine ? 1u : 0u;
+          equal += kj == mine ? 1u : 0u;
+        }
+        const bool hit = lane < (int)in_bin && above < r && r <= above + equal;
+        if (lane == (int)__builtin_ctzll(__ballot(hit))) {
+          sh.gres[0] = mine;
+          sh.gres[1] = r - above;
+          sh.gres[2] = equal;
+        }
+      }
+      __syncthreads();
+      r = sh.gres[1];
+      n_equal = sh.gres[2];
+      return sh.gres[0];
     }
     lo = nlo;
     hi = nhi;
@@ -487,6 +525,7 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
 #pragma unroll
           for (int j = 0; j < kTileTop; ++j) mask |= (uint64_t)(uk[q][j] >= T) << (q * kTileTop + j);
         }
+        // (written out directly: exactly k picks, in id order across threads)
         const uint32_t c = (uint32_t)__popcll(mask);
         uint32_t o = block_scan(c, sh) - c;
         while (mask) {
@@ -500,9 +539,13 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
 #pragma unroll
             for (int ww = 0; ww < OW; ++ww) word = (q * OW + wv == qq * OW + ww) ? uo[qq][ww] : word;
           const uint32_t id = (uint32_t)(((int64_t)tid * tpt + q) * kTile) + ((word >> (8 * e)) & 0xffu);
-          if (o < (uint32_t)k) sh.pool_id[o] = id;
+          if (o < (uint32_t)k) {
+            out[o] = (int32_t)id;
+            if (selp) selp[o] = sc[id];
+          }
           ++o;
         }
+        return;
       } else {
         // branch-free per entry
         uint32_t c = 0;
