@@ -272,8 +272,11 @@ def bench_prefill(cfg, args):
         steps[k % 2].step(stream)
     torch.cuda.synchronize()
     V.timing_reset()
+    # a step launches the score and select kernels once per row group (five at 4096
+    # queries): room for many more launches than that, checked below
+    ev_cap = 64 * K
     for name in ("index_score", "topk_select", "prefill", "compress", "merge"):
-        V.timing_enable(name, 4 * K)
+        V.timing_enable(name, ev_cap)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for k in range(K):
@@ -281,7 +284,12 @@ def bench_prefill(cfg, args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
-    kern = {n: sum(V.timing_read(n)) / K for n in ("index_score", "topk_select", "prefill", "compress", "merge")}
+    kern = {}
+    for n in ("index_score", "topk_select", "prefill", "compress", "merge"):
+        t = V.timing_read(n)
+        if len(t) >= ev_cap:
+            raise SystemExit(f"bench: every timing event of {n} was used; launches went untimed")
+        kern[n] = sum(t) / K
     V.timing_reset()
     fl = prefill_flops(cfg)
     sc = fl["indexer"] / (kern["index_score"] * 1e-3) / 1e12
