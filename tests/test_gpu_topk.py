@@ -116,6 +116,32 @@ def test_key_range_one_bin_past_histogram(n_vis, k, zero_rows):
     np.testing.assert_allclose(sel[0, 0], s[idx[0, 0]], rtol=1e-5)
 
 
+@pytest.mark.parametrize("n_tied", [30, 100])
+def test_cut_inside_ties_of_one_histogram_bin(n_tied):
+    """500 boosted blocks with distinct scores lead the row, then n_tied copies of one
+    key row (bit-identical scores) at ranks 501..500 + n_tied: k = 512 cuts inside the
+    ties, so the lowest-id 12 of them are picked.  30 ties rank inside one bin of the
+    first histogram level (at most 64 keys: one wave counts them); 100 take a second
+    level."""
+    n, k = 65536, 512
+    qi, wi, ki, pos, rng = _inputs(n, seed=11)
+    u = (wi[0, 0].astype(np.float64)[:, None] * O.as_f64(qi[0, 0], "bf16")).sum(0)
+    u /= np.linalg.norm(u)
+    rows = rng.choice(n, 500 + n_tied, replace=False)
+    lead, tied = rows[:500], np.sort(rows[500:])
+    ki[0, lead] += (40.0 + 0.05 * np.arange(500))[:, None] * u
+    ki[0, tied] = ki[0, tied[0]] + 30.0 * u
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    s = _scores(qi, wi, kb)
+    order = np.argsort(-s, kind="stable")
+    assert set(order[:500].tolist()) == set(lead.tolist())           # the leaders lead,
+    assert np.all(s[tied] == s[tied[0]]) and s[tied[0]] > np.delete(s, np.concatenate([lead, tied])).max()  # ties next
+    idx, _ = _run(qi, wi, kb, pos, k)
+    ref = O.topk_select(s, k)
+    assert set(tied[:12].tolist()) <= set(ref.tolist())
+    assert list(idx[0, 0]) == list(ref)
+
+
 # ---------------------------------------------------------------- through the decode step
 def _run_step(qi, wi, ki, pos, k, heads=128, d=128, m=4, W=128):
     """The same selection through v4attn_decode_step (its candidates per group of
