@@ -529,6 +529,11 @@ IndexLaunch index_launch(const v4a_index_args* a, void* ws) {
   // than its share has each workgroup walk several of them
   const int64_t per_row = cdiv(8 * (int64_t)cu_count(), std::min<int64_t>(P.rows, P.chunk_rows));
   sp.wgs_per_row = (int)std::max<int64_t>(1, std::min<int64_t>(P.ntiles, per_row));
+  // a 64-block wave of a decode tile report offers 4 candidates when it holds about a
+  // quarter of a pick or less (more than 4 of the row's top-k in one wave is then
+  // rare, and only costs a rescan), else kTileTop
+  const int64_t nvis_max = (a->pos_max + 1) / a->ratio;
+  sp.wave_top = (int64_t)a->topk * 64 * 4 <= std::max<int64_t>(nvis_max, 1) ? 4 : kTileTop;
   SelectP& tp = L.tp;
   tp.scores = sp.scores; tp.rep_key = sp.rep_key; tp.rep_info = sp.rep_info; tp.pos0 = a->pos0;
   tp.idx = (int32_t*)a->idx.ptr; tp.idx_bs = a->idx.batch_stride; tp.idx_rs = a->idx.row_stride;

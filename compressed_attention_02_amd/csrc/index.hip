@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreP p) {
     sc[j] = s;
     v = score_key(s);
   }
-  tile_report_waves(v, j < nvis, 0, s_stage, p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop,
+  tile_report_waves(v, j < nvis, 0, p.wave_top, s_stage, p.rep_key + (int64_t)lr * p.key_rs + (int64_t)blockIdx.x * kTileTop,
                     p.rep_info + (int64_t)lr * p.info_rs + blockIdx.x);
 }
 

@@ -61,6 +61,7 @@ struct ScoreP {
   int tq, row0;       // launch covers global rows row0 + blockIdx.y; row = b*tq + i
   int heads, dim, ratio;
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
+  int wave_top;       // decode forms: candidates per 64-block wave of a tile report (4 or kTileTop)
   int nrows;          // rows of the launch (set by launch_score)
   // bf16 kernel: workgroups x < prep_x of row y prepare that row's attention queries
   // instead (0: none); the score workgroups follow them

@@ -53,8 +53,8 @@ struct ScoreSmem {
   static constexpr int DI = KS * 32;
   static constexpr int KROWB = FP8 ? DI : DI * 2;   // LDS bytes per key row
   unsigned char sK[NB][64 * NW * KROWB];
-  // the query rows until every wave holds its fragments, then the tiles' keys for
-  // the report (four waves of 64 blocks); a barrier separates the two uses
+  // the query rows until every wave holds its fragments, then the tiles' report
+  // candidates (four waves of 64 blocks); a barrier separates the two uses
   union {
     unsigned char sQ[MT * 16 * DI * 2];
     TileStage stage;
@@ -198,7 +198,7 @@ __device__ __forceinline__ void score_block(const ScoreP& p, int x, int lr, Scor
     }
     const int64_t j = tile0 + wave * 64 + lane;
     if (j < nvis) sc[j] = mine;
-    tile_report_waves(score_key(mine), j < nvis, c & 1, sm.stage, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop,
+    tile_report_waves(score_key(mine), j < nvis, c & 1, p.wave_top, sm.stage, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop,
                       p.rep_info + (int64_t)lr * p.info_rs + tile);
     // the buffer is reloaded next, each wave into the rows it has just read
     if (NB == 2 && tile + 2 * stride < ntile_row)

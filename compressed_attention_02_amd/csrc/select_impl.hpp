@@ -81,24 +81,84 @@ __device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* k
   if (lane == 0) *info = make_uint4(word, word1, bound, 0u);
 }
 
-// The tile's keys when its four 64-block quarters are four waves of a workgroup,
-// [parity] so that a tile's keys are read before the next tile's are written (a
-// barrier separates the two).
+// Rounds of a wave maximum over one key per lane (0 = none): the lanes of the n <= R
+// best keys (the lowest lane among equal ones) and, through rest, the best key left.
+template <int R>
+__device__ __forceinline__ uint64_t wave_best(uint32_t k, int n, uint32_t& rest) {
+  const int lane = threadIdx.x & 63;
+  uint64_t won = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= n) break;
+    const uint32_t m = wave_max_u32(k);
+    if (m == 0u) break;
+    const int l = __builtin_ctzll(__ballot(k == m));
+    won |= 1ull << l;
+    if (lane == l) k = 0u;
+  }
+  rest = wave_max_u32(k);
+  return won;
+}
+
+// The report of a tile whose four 64-block quarters are the four waves of a
+// workgroup (lane L of wave w holds block 64 w + L).  Each wave first takes its own
+// wtop best keys (wtop <= kTileTop) as candidates, in lane order; then wave 0 ranks
+// the 4 wtop candidates, which are in id order, and the kTileTop best need only a
+// compaction.  Every block left out is either a candidate
+// that lost or a key a wave kept back, so the bound is the larger of the best losing
+// candidate and the waves' best kept-back keys.  (A wave holding more than wtop of
+// the tile's best makes the bound one of them: its tile is rescanned if that reaches
+// the threshold.)  [parity]: a tile's candidates are read before the next tile's are
+// written (a barrier separates the two).  Called by all four waves (holds a barrier).
 struct TileStage {
-  uint32_t key[2][kTile];
+  uint32_t key[2][4 * kTileTop];   // candidates, wave-major (key 0: none)
+  uint32_t off[2][4 * kTileTop];   // their offsets in the tile
+  uint32_t rest[2][4];             // each wave's best key past its candidates
 };
-// Every wave stages its keys (0 for no element); after the barrier wave 0 makes the
-// tile report.  Called by all four waves of the workgroup (it holds a barrier).
-__device__ __forceinline__ void tile_report_waves(uint32_t key, bool valid, int par, TileStage& st, uint32_t* keys,
-                                                  uint4* info) {
+__device__ __forceinline__ void tile_report_waves(uint32_t key, bool valid, int par, int wtop, TileStage& st,
+                                                  uint32_t* keys, uint4* info) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  st.key[par][wave * 64 + lane] = valid ? key : 0u;
+  const uint32_t k = valid ? key : 0u;
+  uint32_t rest;
+  const uint64_t won = wave_best<kTileTop>(k, wtop, rest);
+  const int cnt = __popcll(won);
+  if ((won >> lane) & 1ull) {
+    const int slot = wave * wtop + (int)bits_below(won);
+    st.key[par][slot] = k;
+    st.off[par][slot] = (uint32_t)(wave * 64 + lane);
+  }
+  if (lane >= cnt && lane < wtop) st.key[par][wave * wtop + lane] = 0u;
+  if (lane == 0) st.rest[par][wave] = rest;
   __syncthreads();
   if (wave == 0) {
-    uint32_t kb[4];
+    const int nc = 4 * wtop;
+    const uint32_t ck = lane < nc ? st.key[par][lane] : 0u;
+    const uint32_t co = lane < nc ? st.off[par][lane] : 0u;
+    const uint32_t kept = max(max(st.rest[par][0], st.rest[par][1]), max(st.rest[par][2], st.rest[par][3]));
+    // each candidate counts the candidates ahead of it (a larger key, or an equal one in
+    // a lower slot): independent steps, no chain of wave maxima.  The ranks are
+    // distinct, so the kTileTop best win and rank kTileTop is the best one lost.
+    uint32_t ahead = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) kb[q] = st.key[par][q * 64 + lane];
-    tile_report<kTileTop>(kb, keys, info);
+    for (int j = 0; j < 4 * kTileTop; ++j) {
+      if (j >= nc) break;
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+      ahead += (kj > ck || (kj == ck && j < lane)) ? 1u : 0u;
+    }
+    const uint64_t w2 = __ballot(ck != 0u && ahead < (uint32_t)kTileTop);
+    const uint64_t l2 = __ballot(ck != 0u && ahead == (uint32_t)kTileTop);
+    const uint32_t lost = l2 ? (uint32_t)__builtin_amdgcn_readlane((int)ck, (int)__builtin_ctzll(l2)) : 0u;
+    const uint32_t bound = max(lost, kept);
+    const int n = __popcll(w2);
+    const int dst = ((w2 >> lane) & 1ull) ? (int)bits_below(w2) : 63;
+    const uint32_t gk = lane_send(ck, dst), go = lane_send(co, dst);
+    if (lane < kTileTop) keys[lane] = lane < n ? gk : 0u;
+    // the offsets as bytes of two words (entries 0..3 and 4..7): OR over each quad
+    uint32_t word = lane < n ? (go & 0xffu) << (8 * (lane & 3)) : 0u;
+    word |= dpp_u32<0xB1>(0u, word);   // quad_perm [1,0,3,2]
+    word |= dpp_u32<0x4E>(0u, word);   // quad_perm [2,3,0,1]
+    const uint32_t word1 = __builtin_amdgcn_readlane(word, 4);
+    if (lane == 0) *info = make_uint4(word, word1, bound, 0u);
   }
 }
 
