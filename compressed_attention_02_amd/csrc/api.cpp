@@ -100,10 +100,17 @@ const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select
                                           "prefill", "select_attn", "qprep", "read_probe"};
 
 // ---------------------------------------------------------------- plans
+// Threshold mode (prefill form): every kThetaStride-th tile is scored first, and a
+// per-row threshold from those scores lets most tiles report without rounds and
+// store no scores; it needs rows of at least kThetaMinTiles tiles.
+constexpr int64_t kThetaStride = 64;
+constexpr int64_t kThetaMinTiles = 256;
+
 struct IndexPlan {
   int64_t rows, n_cap, sc_rs, ntiles, key_rs, info_rs, chunk_rows;
-  size_t off_keys, off_info, ws_bytes;
+  size_t off_keys, off_info, off_theta, off_flag, ws_bytes;
   bool multi;   // score in workgroups of 8 query rows (prefill chunks of a 64 x 64 bf16 indexer)
+  bool theta;   // multi, in threshold mode
 };
 
 IndexPlan plan_index(const v4a_index_args* a) {
@@ -122,9 +129,14 @@ IndexPlan plan_index(const v4a_index_args* a) {
             a->tq % 8 == 0 && P.chunk_rows >= 8;
   if (P.multi) P.chunk_rows -= P.chunk_rows % 8;
 
+  // (not when the selected scores are asked for: most tiles store none)
+  P.theta = P.multi && P.ntiles >= kThetaMinTiles && !a->sel_scores.ptr;
+
   P.off_keys = (size_t)round_up(P.chunk_rows * P.sc_rs * 4, 256);
   P.off_info = P.off_keys + (size_t)round_up(P.chunk_rows * P.key_rs * 4, 256);
-  P.ws_bytes = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 16, 256);
+  P.off_theta = P.off_info + (size_t)round_up(P.chunk_rows * P.info_rs * 16, 256);
+  P.off_flag = P.off_theta + (size_t)round_up(P.chunk_rows * 4, 256);
+  P.ws_bytes = P.theta ? P.off_flag + (size_t)round_up(P.chunk_rows * 4, 256) : P.off_theta;
   return P;
 }
 
@@ -559,12 +571,59 @@ v4a_status score_row_chunk(const v4a_index_args* a, IndexLaunch& L, int64_t r0, 
   return V4A_OK;
 }
 
+// Threshold mode for a group of rows: (1) the sampled tiles' scores, (2) each row's
+// threshold from them, (3) every tile, reporting its keys at or above the threshold
+// when there are at most kTileTop (else its exact best and its scores), (4) the
+// selection, which flags rows whose k-th key falls below their threshold, (5, 6) the
+// exact score and selection of the flagged rows' groups only.
+v4a_status theta_row_chunk(IndexLaunch& L, void* ws, int64_t r0, int nr, hipStream_t stream) {
+  ScoreP sp = L.sp;
+  SelectP tp = L.tp;
+  sp.row0 = tp.row0 = (int)r0;
+  uint32_t* theta = (uint32_t*)((char*)ws + L.P.off_theta);
+  uint32_t* flag = (uint32_t*)((char*)ws + L.P.off_flag);
+  const int64_t groups = cdiv(nr, 8);
+  auto wgs = [&](int64_t walk) {   // workgroups per group: the chip about four times over
+    return (int)std::max<int64_t>(1, std::min<int64_t>(walk, cdiv(4 * (int64_t)cu_count(), groups)));
+  };
+  const int64_t nsamp = cdiv(L.P.ntiles, kThetaStride);
+  ScoreP s1 = sp;
+  s1.sample_stride = (int)kThetaStride;
+  s1.wgs_per_row = wgs(nsamp);
+  V4A_TRY(hip_check(launch_score_rows(s1, nr, (int)nsamp, stream, V4A_K_INDEX_SCORE), "index sample launch"));
+  SelectP t2 = tp;
+  t2.sample_stride = (int)kThetaStride;
+  t2.theta_out = theta;
+  V4A_TRY(hip_check(launch_theta(t2, nr, stream, V4A_K_TOPK_SELECT), "threshold launch"));
+  ScoreP s3 = sp;
+  s3.theta = theta;
+  s3.wgs_per_row = wgs(L.P.ntiles);
+  V4A_TRY(hip_check(launch_score_rows(s3, nr, (int)L.P.ntiles, stream, V4A_K_INDEX_SCORE), "index score launch"));
+  SelectP t4 = tp;
+  t4.theta = theta;
+  t4.flag = flag;
+  t4.rep_top = kTileTop;
+  V4A_TRY(hip_check(launch_select(t4, nr, stream, V4A_K_TOPK_SELECT), "top-k select launch"));
+  ScoreP s5 = sp;
+  s5.repair = flag;
+  s5.wgs_per_row = wgs(L.P.ntiles);
+  V4A_TRY(hip_check(launch_score_rows(s5, nr, (int)L.P.ntiles, stream, V4A_K_INDEX_SCORE), "index repair launch"));
+  SelectP t6 = tp;
+  t6.repair = flag;
+  V4A_TRY(hip_check(launch_select(t6, nr, stream, V4A_K_TOPK_SELECT), "top-k repair launch"));
+  return V4A_OK;
+}
+
 // Scores and selection of v4attn_index_topk on stream (arguments validated).
 v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   V4A_TRY(check_ws(ws, ws_bytes, plan_index(a).ws_bytes));   // before any pointer into ws is formed
   IndexLaunch L = index_launch(a, ws);
   for (int64_t r0 = 0; r0 < L.P.rows; r0 += L.P.chunk_rows) {
     const int nr = (int)std::min<int64_t>(L.P.chunk_rows, L.P.rows - r0);
+    if (L.P.theta) {
+      V4A_TRY(theta_row_chunk(L, ws, r0, nr, stream));
+      continue;
+    }
     V4A_TRY(score_row_chunk(a, L, r0, nr, stream));
     V4A_TRY(hip_check(launch_select(L.tp, nr, stream, V4A_K_TOPK_SELECT), "top-k select launch"));
   }

@@ -146,4 +146,47 @@ hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ threshold
+// Threshold mode of the prefill form: from the scores of the sampled tiles (0, S,
+// 2S, ...; n_s keys), the r-th largest key with r = 3 k n_s / n_vis + 16, about three
+// times the sample's expected share of the row's top-k plus a margin: for keys in
+// random order it lies below the row's k-th key by a wide margin, and a row where it
+// does not is redone exactly (select_row flags it).  Rows whose sample holds fewer
+// than r keys (short rows) get 0, which makes every full tile report exactly.
+__global__ __launch_bounds__(kSelThreads) void theta_kernel(SelectP p) {
+  __shared__ SelShared sh;
+  const int lr = blockIdx.x;
+  int b, i;
+  int64_t pos;
+  row_coords(p.row0 + lr, p.tq, p.pos0, b, i, pos);
+  const int64_t nvis = (pos + 1) / p.ratio;
+  const int64_t S = p.sample_stride;
+  uint32_t th = 0u;
+  if (nvis >= kTile) {
+    const int64_t ns_t = ((nvis + kTile - 1) / kTile + S - 1) / S;   // sampled tiles
+    const int64_t last = (ns_t - 1) * S;                               // the last one's row tile
+    const int64_t n_s = (ns_t - 1) * kTile + min<int64_t>(kTile, nvis - last * kTile);
+    const uint64_t r = 3ull * (uint64_t)p.topk * (uint64_t)n_s / (uint64_t)nvis + 16ull;
+    if ((uint64_t)n_s >= r) {
+      const float* sc = p.scores + (int64_t)lr * p.sc_rs;
+      auto each = [&](auto&& f) {
+        for (int64_t t = threadIdx.x; t < n_s; t += kSelThreads) {
+          const int64_t j = (t / kTile) * S * kTile + t % kTile;
+          f(score_key(sc[j]), (uint32_t)j);
+        }
+      };
+      uint32_t rr = (uint32_t)r, n_eq;
+      th = rank_search(each, [](uint32_t, uint32_t) { return true; }, [](uint32_t key, uint32_t) { return key; }, rr,
+                       true, sh, n_eq);
+    }
+  }
+  if (threadIdx.x == 0) p.theta_out[lr] = th;
+}
+
+hipError_t launch_theta(const SelectP& p, int nrows, hipStream_t s, int tid) {
+  if (p.sample_stride < 1 || !p.theta_out) return hipErrorInvalidValue;
+  V4A_LAUNCH(tid, theta_kernel, dim3((unsigned)nrows), dim3(kSelThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace v4a

@@ -62,6 +62,11 @@ struct ScoreP {
   int heads, dim, ratio;
   int wgs_per_row;    // bf16 kernel: workgroups per row group, each walking tiles with that stride
   int wave_top;       // decode forms: candidates per 64-block wave of a tile report (4 or kTileTop)
+  // prefill form only:
+  int sample_stride;      // > 0: score tiles 0, s, 2s, ... only and store their scores (no reports)
+  const uint32_t* theta;  // [launch rows]: threshold mode, per row a key that bounds the row's k-th
+                          // from below (null: exact reports of kPrefillTileTop and every score stored)
+  const uint32_t* repair; // [launch rows]: only workgroups with a flagged row run (null: all)
   int nrows;          // rows of the launch (set by launch_score)
   // bf16 kernel: workgroups x < prep_x of row y prepare that row's attention queries
   // instead (0: none); the score workgroups follow them
@@ -82,8 +87,17 @@ struct SelectP {
   int tq, row0, ratio, topk;
   int ntiles_cap;     // score tiles of the longest row (pos_max): bounds the report loads
   int rep_top;        // report slots per tile that the score kernel fills (kTileTop or kPrefillTileTop)
+  // prefill threshold mode:
+  const uint32_t* theta;  // [launch rows]: the rows' thresholds (null: exact reports)
+  uint32_t* flag;         // [launch rows]: set to 1 where a row has to be redone exactly, else 0
+  const uint32_t* repair; // [launch rows]: only flagged rows are selected (null: all)
+  int sample_stride;      // theta_kernel: the sampled tiles (0, s, 2s, ...)
+  uint32_t* theta_out;    // theta_kernel: [launch rows]
 };
 hipError_t launch_select(const SelectP& p, int nrows, hipStream_t s, int tid);
+// Per row, a threshold key from the scores of the sampled tiles: the r-th largest
+// with r = 3 k n_s / n_vis + 16 (n_s sampled keys), or 0 when the sample holds fewer.
+hipError_t launch_theta(const SelectP& p, int nrows, hipStream_t s, int tid);
 
 // ---------------------------------------------------------------- attention
 constexpr int kAttnChunk = 64;  // keys per inner chunk of the attention kernels

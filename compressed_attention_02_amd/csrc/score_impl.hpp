@@ -243,10 +243,19 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
   row_coords(p.row0 + last, p.tq, p.pos0, bl, il, pos_l);
   const int64_t nvis = (pos + 1) / p.ratio;             // this query's
   const int64_t nvis_g = uniform_i64((pos_l + 1) / p.ratio);
-  const int64_t ntile = (nvis_g + kTile - 1) / kTile;
+  // the tiles walked: every one, or (sampling) 0, S, 2S, ...; tile v of the walk is
+  // tile v * S of the row
+  const int64_t S = p.sample_stride > 0 ? p.sample_stride : 1;
+  const int64_t ntile = ((nvis_g + kTile - 1) / kTile + S - 1) / S;
   int64_t tile = blockIdx.x;
   const int64_t stride = gridDim.x;
   if (tile >= ntile) return;
+  if (p.repair) {   // a repair pass: only groups holding a flagged row run
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) any |= lr0 + q < p.nrows && p.repair[lr0 + q] != 0u;
+    if (!any) return;
+  }
   const unsigned char* ki = reinterpret_cast<const unsigned char*>(p.ki) + (int64_t)bl * p.ki_bs * 2;
   const int64_t ki_rb = p.ki_rs * 2;
   auto issue = [&](int64_t t, unsigned char* buf) {
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
     for (int u = 0; u < IPW; ++u) {
       const int r0 = (wave * IPW + u) * KRPI;
       const int r = r0 + lane / KCPR;
-      const int64_t j = min(t * kTile + r, nvis_g - 1);
+      const int64_t j = min(t * S * kTile + r, nvis_g - 1);
       lds_load16(ki + j * ki_rb + ((lane % KCPR) ^ swz_ki<DI>(r)) * 16, lds_addr(buf + r0 * ROWB));
     }
   };
@@ -304,6 +313,8 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
         U[s2][e] = (__bf16)v;
       }
   }
+  // threshold mode: this query's threshold key
+  const uint32_t th = (p.theta && have) ? p.theta[lr] : 0u;
   // (the compiler does not count the tile loads below, so it would wait for them too
   // at the fragments' first use: they are waited for here, before any tile load)
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -354,16 +365,43 @@ __global__ __launch_bounds__(kScoreRowsQ * 64, 4) void score_rows_kernel(ScoreP 
       mine[q4] = __uint_as_float(sh[0]) + __uint_as_float(sh[1]);
     }
     if (have) {
-      const int64_t tile0 = tile * kTile;
+      const int64_t rt = tile * S;   // the row's tile
+      const int64_t tile0 = rt * kTile;
+      uint32_t* keys = p.rep_key + (int64_t)lr * p.key_rs + rt * kTileTop;
+      uint4* info = p.rep_info + (int64_t)lr * p.info_rs + rt;
       uint32_t kb[4];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int64_t j = tile0 + 64 * blk + lane;
-        if (j < nvis) sc[j] = mine[blk];
-        kb[blk] = j < nvis ? score_key(mine[blk]) : 0u;
+      for (int blk = 0; blk < 4; ++blk) kb[blk] = tile0 + 64 * blk + lane < nvis ? score_key(mine[blk]) : 0u;
+      auto store = [&]() {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+          if (tile0 + 64 * blk + lane < nvis) sc[tile0 + 64 * blk + lane] = mine[blk];
+      };
+      if (p.sample_stride > 0) {
+        store();   // a sampled tile: its scores are all the threshold needs
+      } else if (p.theta) {
+        // the keys at or above the row's threshold: when there are at most kTileTop,
+        // they are the report, every other key is below the threshold (the bound),
+        // and no score is stored; else the exact best kTileTop and the scores
+        uint64_t won[4];
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          won[q] = __ballot(kb[q] != 0u && kb[q] >= th);
+          c += (uint32_t)__popcll(won[q]);
+        }
+        if (c <= (uint32_t)kTileTop) {
+          tile_emit_few(kb, won, th ? th - 1u : 0u, keys, info);
+        } else {
+          store();
+          uint32_t bound;
+          tile_rounds<kTileTop>(kb, won, bound);
+          tile_emit(kb, won, bound, keys, info);
+        }
+      } else {
+        store();
+        tile_report<kPrefillTileTop>(kb, keys, info);
       }
-      tile_report<kPrefillTileTop>(kb, p.rep_key + (int64_t)lr * p.key_rs + tile * kTileTop,
-                                   p.rep_info + (int64_t)lr * p.info_rs + tile);
     }
     __syncthreads();   // every wave is done with this buffer
     if (tile + 2 * stride < ntile) issue(tile + 2 * stride, buf);

@@ -34,34 +34,12 @@ __device__ __forceinline__ uint32_t bits_below(uint64_t m) {
 }
 
 // The tile report made by one wave whose lane L holds the keys kb[q] of blocks
-// 64 q + L (0 for none), with the R <= kTileTop best (entries past R are empty).
-// Each of R rounds takes a 32-bit wave maximum (DPP) of the keys not yet taken and
-// takes one block holding it: the lowest lane with it, and that lane's first quarter.
-// Which of several equal keys is taken does not matter for the selection: if one
-// is left out, the bound (one more maximum) equals that key, so a threshold at it
-// sends the tile to a rescan.  The winners then go to lanes 0..R-1 in id order (a
-// forward permute per quarter) and are written out: keys (8 words) and info.
-template <int R>
-__device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* keys, uint4* info) {
-  static_assert(kTileTop == 8 && R >= 1 && R <= kTileTop, "two offset words per tile");
+// 64 q + L (0 for none): the entries won[q] (bit L: block 64 q + L) are written in
+// id order, keys (kTileTop words, empty ones 0) and info, with the bound given.
+// The winners go to lanes 0.. in id order (a forward permute per quarter).
+__device__ __forceinline__ void tile_emit(const uint32_t (&kb)[4], const uint64_t (&won)[4], uint32_t bound,
+                                          uint32_t* keys, uint4* info) {
   const int lane = threadIdx.x & 63;
-  uint32_t k[4] = {kb[0], kb[1], kb[2], kb[3]};
-  uint64_t won[4] = {0ull, 0ull, 0ull, 0ull};
-#pragma unroll 1
-  for (int r = 0; r < R; ++r) {
-    const uint32_t lm = max(max(k[0], k[1]), max(k[2], k[3]));
-    const uint32_t m = wave_max_u32(lm);
-    if (m == 0u) break;
-    const int l = __builtin_ctzll(__ballot(lm == m));
-    const int qs = k[0] == m ? 0 : k[1] == m ? 1 : k[2] == m ? 2 : 3;   // lane-local
-    const int qw = __builtin_amdgcn_readlane(qs, l);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == qw) won[q] |= 1ull << l;
-      if (lane == l && q == qs) k[q] = 0u;
-    }
-  }
-  const uint32_t bound = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
   uint32_t base = 0, rk = 0u, ro = 0u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -79,6 +57,66 @@ __device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* k
   word |= dpp_u32<0x4E>(0u, word);   // quad_perm [2,3,0,1]
   const uint32_t word1 = __builtin_amdgcn_readlane(word, 4);
   if (lane == 0) *info = make_uint4(word, word1, bound, 0u);
+}
+
+// The same report when the entries are known to be at most kTileTop: each winner
+// stores its own key and its offset byte at its rank in id order, the lanes past the
+// last entry clear the remaining key slots (an empty entry's offset byte is never
+// read), and no value crosses lanes.
+__device__ __forceinline__ void tile_emit_few(const uint32_t (&kb)[4], const uint64_t (&won)[4], uint32_t bound,
+                                              uint32_t* keys, uint4* info) {
+  const int lane = threadIdx.x & 63;
+  unsigned char* offs = reinterpret_cast<unsigned char*>(info);
+  uint32_t base = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if ((won[q] >> lane) & 1ull) {
+      const uint32_t at = base + bits_below(won[q]);
+      keys[at] = kb[q];
+      offs[at] = (unsigned char)(64 * q + lane);
+    }
+    base += (uint32_t)__popcll(won[q]);
+  }
+  if (lane >= (int)base && lane < kTileTop) keys[lane] = 0u;
+  if (lane == 0) reinterpret_cast<uint2*>(info)[1] = make_uint2(bound, 0u);
+}
+
+// The R <= kTileTop best of the wave's 256 keys (entries past R are empty).  Each of
+// R rounds takes a 32-bit wave maximum (DPP) of the keys not yet taken and takes one
+// block holding it: the lowest lane with it, and that lane's first quarter.  Which of
+// several equal keys is taken does not matter for the selection: if one is left out,
+// the bound (one more maximum) equals that key, so a threshold at it sends the tile
+// to a rescan.
+template <int R>
+__device__ __forceinline__ void tile_rounds(const uint32_t (&kb)[4], uint64_t (&won)[4], uint32_t& bound) {
+  static_assert(kTileTop == 8 && R >= 1 && R <= kTileTop, "two offset words per tile");
+  const int lane = threadIdx.x & 63;
+  uint32_t k[4] = {kb[0], kb[1], kb[2], kb[3]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) won[q] = 0ull;
+#pragma unroll 1
+  for (int r = 0; r < R; ++r) {
+    const uint32_t lm = max(max(k[0], k[1]), max(k[2], k[3]));
+    const uint32_t m = wave_max_u32(lm);
+    if (m == 0u) break;
+    const int l = __builtin_ctzll(__ballot(lm == m));
+    const int qs = k[0] == m ? 0 : k[1] == m ? 1 : k[2] == m ? 2 : 3;   // lane-local
+    const int qw = __builtin_amdgcn_readlane(qs, l);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q == qw) won[q] |= 1ull << l;
+      if (lane == l && q == qs) k[q] = 0u;
+    }
+  }
+  bound = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
+}
+
+template <int R>
+__device__ __forceinline__ void tile_report(const uint32_t (&kb)[4], uint32_t* keys, uint4* info) {
+  uint64_t won[4];
+  uint32_t bound;
+  tile_rounds<R>(kb, won, bound);
+  tile_emit(kb, won, bound, keys, info);
 }
 
 // Rounds of a wave maximum over one key per lane (0 = none): the lanes of the n <= R
@@ -476,6 +514,13 @@ __device__ __forceinline__ void emit_pool(SelShared& sh, uint32_t np, uint32_t k
 // The selection of row lr of the launch (one kSelThreads-thread workgroup).
 __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (p.repair && p.repair[lr] == 0u) return;   // a repair pass: flagged rows only
+  // threshold mode: the reports hold every key >= th of the tiles that stored no
+  // scores; a row whose k-th key turns out below th is flagged (and left to an exact
+  // repair pass) instead of selected.  thread 0 writes the flag, first clearing it.
+  const bool tmode = p.theta != nullptr;
+  const uint32_t th = tmode ? p.theta[lr] : 0u;
+  if (tmode && tid == 0) p.flag[lr] = 0u;
   const uint32_t* RK = p.rep_key + (int64_t)lr * p.key_rs;
   const uint4* RI = p.rep_info + (int64_t)lr * p.info_rs;
   // thread t owns tiles [t*tpt, t*tpt + tpt) of the longest row; the report loads do
@@ -558,13 +603,29 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
         if (uk[q][j] != 0u) f(uk[q][j], rep_id(q, j));
   };
   // every tile of 256 visible blocks reports rep_top of them, a partial last tile
-  // at most as many as it has
-  const int64_t n_rep = (int64_t)p.rep_top * (nvis / kTile) + min<int64_t>(p.rep_top, nvis % kTile);
+  // at most as many as it has; in threshold mode the count is the reports' own
+  int64_t n_rep = (int64_t)p.rep_top * (nvis / kTile) + min<int64_t>(p.rep_top, nvis % kTile);
+  if (tmode) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxTilesPerThread; ++q)
+#pragma unroll
+      for (int j = 0; j < kTileTop; ++j) c += uk[q][j] != 0u ? 1u : 0u;
+    const uint32_t incl = block_scan(c, sh);
+    if (tid == kSelThreads - 1) sh.n_pool = incl;
+    __syncthreads();
+    n_rep = sh.n_pool;
+    __syncthreads();
+  }
 
   if (ok && n_rep >= k) {
     // 1. the exact k-th key T of all the reports
     uint32_t r = (uint32_t)k, n_tie;
     const uint32_t T = reg_rank_search(uk, tpt, r, sh, n_tie);
+    if (tmode && T < th) {   // keys in [T, th) may sit in tiles that stored nothing
+      if (tid == 0) p.flag[lr] = 1u;
+      return;
+    }
     // 2. no tile hides a key >= T: the reports hold every element >= T and their top-k
     //    is the row's; compacted in id order from the registers through LDS
     bool hides = false;
@@ -732,7 +793,12 @@ __device__ __forceinline__ void select_row(const SelectP& p, int lr, SelShared& 
     }
   }
 
-  // whole-row path (ties everywhere, too many rescans, or more tiles than registers hold)
+  // whole-row path (ties everywhere, too many rescans, or more tiles than registers
+  // hold); in threshold mode not every score is stored: the row is flagged instead
+  if (tmode) {
+    if (tid == 0) p.flag[lr] = 1u;
+    return;
+  }
   uint32_t T, id_max;
   auto eachR = [&](auto&& f) {
     for (int64_t t = tid; t < nvis; t += kSelThreads) f(score_key(sc[t]), (uint32_t)t);

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle as O
+import synth
 from synth import configs as C
 from tests.gpu_harness import Run, assert_close, dev_to_np, sample_rows
 
@@ -187,3 +188,33 @@ def test_prefill_index_two_sequences(tq):
     r.step.run_index()
     torch.cuda.synchronize()
     r.check_topk()
+
+
+def test_prefill_index_threshold_mode_and_repair():
+    # rows of at least 256 score tiles take the threshold mode (a sampled pass sets
+    # each row's threshold; tiles with at most 8 keys above it report them without
+    # rounds or stores).  Sequence 0's sampled tiles (every 64th) are scaled up 8x, so
+    # its threshold lands above its true k-th score: its rows are flagged and redone
+    # exactly; sequence 1 takes the threshold path.  Both must match the oracle.
+    cfg = C.C5.small(name="pf_theta", batch=2, pos=262144, tq=16, needles=8)
+    print("[case] prefill index threshold mode and repair", flush=True)
+    g = synth.generate(cfg)
+    ki = synth.bf16_bits_to_f32(g["ki"]).astype(np.float64)
+    n = ki.shape[1]
+    sampled = (np.arange(n) // 256) % 64 == 0
+    ki[0, sampled] *= 8.0
+    g["ki"] = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    r = Run(cfg, gen=g)
+    r.step.run_compress()
+    r.step.run_index()
+    torch.cuda.synchronize()
+    r.check_topk()
+    # the premise, from the oracle's scores: each of sequence 0's rows has its
+    # threshold (the r-th largest sampled score, r = 3 k n_s / n_vis + 16) above its
+    # k-th score, so only the repair pass can have selected it; sequence 1's rows not
+    for b in range(2):
+        for i in (0, cfg.tq - 1):
+            s = r.oracle_scores(b, i)
+            smp = np.sort(s[sampled[:s.size]])[::-1]
+            rank = 3 * cfg.topk * smp.size // s.size + 16
+            assert (smp[rank - 1] > np.sort(s)[::-1][cfg.topk - 1]) == (b == 0)
