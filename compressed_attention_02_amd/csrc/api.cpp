@@ -354,7 +354,10 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
   const bool f8 = kvt == V4A_FP8_E4M3;
   if (kvt != a->dtype && !(f8 && a->dtype == V4A_BF16))
     return fail(V4A_EINVAL, "kv_dtype %d: 0, dtype, or FP8_E4M3 with bf16 attention", a->kv_dtype);
-  if (f8 && (a->dim > 128 || skv)) return fail(V4A_ENOTSUP, "FP8 caches: dim <= 128 and separate K and V");
+  if (f8 && !(a->dim <= 128 && !skv) && !(a->dim == 512 && skv))
+    return fail(V4A_ENOTSUP, "FP8 caches: separate K and V rows of dim <= 128, or shared entries (V4A_SHARED_KV) of 512");
+  if (f8 && skv && (a->vc_scale.ptr || a->vh_scale.ptr || a->vr_scale.ptr))
+    return fail(V4A_EINVAL, "V4A_SHARED_KV: vc_scale, vh_scale and vr_scale must be NULL (the key rows' scales serve)");
   if (a->branch_mask == 0 || a->branch_mask > 7) return fail(V4A_EINVAL, "branch_mask must be a non-empty subset of CSA|HCA|SWA");
   if (a->csa_ratio < 1 || a->hca_ratio < 1) return fail(V4A_EINVAL, "compression ratios must be >= 1");
   if (a->window < 0) return fail(V4A_EINVAL, "window must be >= 0");
@@ -391,17 +394,17 @@ v4a_status validate_attn(const v4a_attn_args* a, bool prefill) {
     if (a->idx.row_stride < a->topk) return fail(V4A_EINVAL, "idx: row_stride < topk");
     V4A_TRY(check_tensor("kc", a->kc, kvt, a->dim, bq));
     if (!skv) V4A_TRY(check_tensor("vc", a->vc, kvt, a->dim, bq));
-    if (f8) { V4A_TRY(check_scale("kc_scale", a->kc_scale, bq)); V4A_TRY(check_scale("vc_scale", a->vc_scale, bq)); }
+    if (f8) { V4A_TRY(check_scale("kc_scale", a->kc_scale, bq)); if (!skv) V4A_TRY(check_scale("vc_scale", a->vc_scale, bq)); }
   }
   if (a->branch_mask & V4A_HCA) {
     V4A_TRY(check_tensor("kh", a->kh, kvt, a->dim, bq));
     if (!skv) V4A_TRY(check_tensor("vh", a->vh, kvt, a->dim, bq));
-    if (f8) { V4A_TRY(check_scale("kh_scale", a->kh_scale, bq)); V4A_TRY(check_scale("vh_scale", a->vh_scale, bq)); }
+    if (f8) { V4A_TRY(check_scale("kh_scale", a->kh_scale, bq)); if (!skv) V4A_TRY(check_scale("vh_scale", a->vh_scale, bq)); }
   }
   if ((a->branch_mask & V4A_SWA) && a->window > 0) {
     V4A_TRY(check_tensor("k_raw", a->k_raw, kvt, a->dim, bq));
     if (!skv) V4A_TRY(check_tensor("v_raw", a->v_raw, kvt, a->dim, bq));
-    if (f8) { V4A_TRY(check_scale("kr_scale", a->kr_scale, bq)); V4A_TRY(check_scale("vr_scale", a->vr_scale, bq)); }
+    if (f8) { V4A_TRY(check_scale("kr_scale", a->kr_scale, bq)); if (!skv) V4A_TRY(check_scale("vr_scale", a->vr_scale, bq)); }
     if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
   }
   if (a->sink && !aligned(a->sink, 4)) return fail(V4A_EINVAL, "sink: not 4-byte aligned");

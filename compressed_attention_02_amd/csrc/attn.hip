@@ -231,8 +231,8 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
     // shared entries only: 8 waves, a wave pair per head tile, four tiles per
     // workgroup (more heads come in head groups)
     if (!p.skv || ntile > kWideTiles) return hipErrorInvalidValue;
-    if (p.f8) return hipErrorInvalidValue;
-    launch_bf16<8, 1, 512, 1, true, false>(p, grid, s, tid);
+    if (p.f8) launch_bf16<8, 1, 512, 1, true, true>(p, grid, s, tid);
+    else launch_bf16<8, 1, 512, 1, true, false>(p, grid, s, tid);
     return hipGetLastError();
   }
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every

@@ -334,18 +334,47 @@ __device__ __forceinline__ void issue_chunk_f8(const RowKeys& R, const int* s_id
   }
 }
 
+// FP8 shared entries (every row its own value, one scale per row serving as the
+// key's and the value's): the chunk's codes into staging (row-major, D bytes per
+// row), the rows' scales into sKs (wave 0, lane l = row l) and the mask.
+template <int NW, int D>
+__device__ __forceinline__ void issue_chunk_f8_shared(const RowKeys& R, const int* s_idx, int64_t kc0,
+                                                      unsigned char* sKc, float* sBias, float* sKs, int wave,
+                                                      int lane) {
+  constexpr int PS = D / 16;              // 16-code pieces per row
+  constexpr int RPI = 64 / PS;            // rows per wave instruction
+  constexpr int NI = kAttnChunk / RPI;    // instructions per chunk
+  const int prow = lane / PS, ppiece = lane % PS;
+  for (int u = wave; u < NI; u += NW) {
+    const int r = u * RPI + prow;
+    const unsigned char* kp;
+    const float* ks;
+    bool ok;
+    key_src_f8(R, s_idx, kc0 + r, false, kp, ks, ok);
+    lds_load16(kp + ppiece * 16, lds_addr(sKc + u * RPI * D));
+    if (ppiece == 0) sBias[r] = ok ? 0.f : -INFINITY;
+  }
+  if (wave == 0) {
+    const unsigned char* cp;
+    const float* sp;
+    bool ok;
+    key_src_f8(R, s_idx, kc0 + lane, false, cp, sp, ok);
+    lds_load4(sp, lds_addr(sKs));
+  }
+}
+
 // Staged FP8 codes -> the bf16 chunk layout (K with swz_k, V with swz_v), exactly:
 // thread item x takes 16 codes of one row (one staging piece) and writes two bf16
 // pieces.  Masked rows (sBias -inf) become zeros: their staged bytes are the query
 // row's, which may hold NaN codes, and a NaN times a zero weight would still reach
 // the sums.
-template <int NT, int D>
+template <int NT, int D, bool KONLY = false>
 __device__ __forceinline__ void convert_chunk_f8(const unsigned char* sKc, const unsigned char* sVc, uint16_t* sK,
                                                  uint16_t* sV, const float* sBias) {
   constexpr int PS = D / 16;
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  for (int x = threadIdx.x; x < 2 * kAttnChunk * PS; x += NT) {
-    const bool v = x >= kAttnChunk * PS;
+  for (int x = threadIdx.x; x < (KONLY ? 1 : 2) * kAttnChunk * PS; x += NT) {
+    const bool v = !KONLY && x >= kAttnChunk * PS;
     const int y = v ? x - kAttnChunk * PS : x;
     const int r = y / PS, pc = y % PS;
     uint4 c = *reinterpret_cast<const uint4*>((v ? sVc : sKc) + r * D + pc * 16);
@@ -564,9 +593,9 @@ __device__ __forceinline__ void run_chunks_f8(const RowKeys& R, const int* s_idx
 // (attend_wide_pv).  m and l are computed twice, identically.
 
 // logits (base 2, masked) of key tiles kt0 .. kt0 + NJ - 1 of the chunk over all of d
-template <int D, int NJ>
+template <int D, int NJ, bool F8 = false>
 __device__ __forceinline__ void wide_logits(const uint16_t* sK, const float* sBias, const bf16x8_t (&Qb)[1][D / 32],
-                                            float sl2, int kt0, int lane, f32x4 (&S)[NJ]) {
+                                            float sl2, int kt0, int lane, f32x4 (&S)[NJ], const float* sKs = nullptr) {
   constexpr int KS = D / 32;
   const int col = lane & 15, grp = lane >> 4;
   const int kx = swz_k<D>(col);
@@ -600,26 +629,34 @@ __device__ __forceinline__ void wide_logits(const uint16_t* sK, const float* sBi
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const f32x4 bias = *reinterpret_cast<const f32x4*>(&sBias[16 * (kt0 + j) + 4 * grp]);
+    f32x4 ksl = {sl2, sl2, sl2, sl2};
+    if constexpr (F8) {   // the rows' scales; masked keys' scale words are whatever the fallback holds
+      ksl = *reinterpret_cast<const f32x4*>(&sKs[16 * (kt0 + j) + 4 * grp]) * sl2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S[j][e] = fmaf(S[j][e], sl2, bias[e]);
+      for (int e = 0; e < 4; ++e) ksl[e] = bias[e] == 0.f ? ksl[e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[j][e] = fmaf(S[j][e], ksl[e], bias[e]);
   }
 }
 
 // the pair's hand-over: wave hh scores key tiles 2hh, 2hh + 1 into sX
-template <int D>
+template <int D, bool F8 = false>
 __device__ __forceinline__ void attend_wide_scores(const uint16_t* sK, const float* sBias, float* sX,
                                                    const bf16x8_t (&Qb)[1][D / 32], float sl2, int lt, int hh,
-                                                   int lane) {
+                                                   int lane, const float* sKs = nullptr) {
   f32x4 S[2];
-  wide_logits<D, 2>(sK, sBias, Qb, sl2, 2 * hh, lane, S);
+  wide_logits<D, 2, F8>(sK, sBias, Qb, sl2, 2 * hh, lane, S, sKs);
 #pragma unroll
   for (int j = 0; j < 2; ++j) reinterpret_cast<f32x4*>(sX)[(lt * 4 + 2 * hh + j) * 64 + lane] = S[j];
 }
 
 // softmax of the chunk's logits S (4 key tiles) and this wave's half of O^T += V^T P^T
-template <int D>
+// (F8: sVs holds the rows' scales, which weight the values in the product, not l)
+template <int D, bool F8 = false>
 __device__ __forceinline__ void attend_wide_pv(const uint16_t* sV, const f32x4 (&S)[4], f32x4 (&O)[1][D / 32],
-                                               float (&m_run)[1], float (&l_run)[1], int hh, int lane) {
+                                               float (&m_run)[1], float (&l_run)[1], int hh, int lane,
+                                               const float* sVs = nullptr) {
   constexpr int DH = D / 32;   // 16-column tiles of this wave's half
   const int col = lane & 15, grp = lane >> 4;
   float c = fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3]));
@@ -652,9 +689,11 @@ __device__ __forceinline__ void attend_wide_pv(const uint16_t* sV, const f32x4 (
     for (int e = 0; e < 8; ++e) {
       const float v = __builtin_amdgcn_exp2f(S[2 * kk + (e >> 2)][e & 3] - mu);
       ps += v;
-      const __bf16 h = (__bf16)v;
+      // (masked keys: v = 0, and their scale words are never multiplied)
+      const float pv = F8 ? (v > 0.f ? v * sVs[32 * kk + 16 * (e >> 2) + 4 * grp + (e & 3)] : 0.f) : v;
+      const __bf16 h = (__bf16)pv;
       Bhi[kk][e] = h;
-      Blo[kk][e] = (__bf16)(v - (float)h);
+      Blo[kk][e] = (__bf16)(pv - (float)h);
     }
     l_run[0] += ps;
   }
@@ -722,6 +761,41 @@ __device__ __forceinline__ void run_chunks_wide(const RowKeys& R, const int* s_i
   }
 }
 
+// The chunk pipeline of FP8 shared rows of 512: the codes of a chunk land in
+// staging (the second chunk buffer's space), are converted into the first, and the
+// next chunk's loads go out while this one is scored and its products taken (the
+// mask and scale arrays alternate by chunk parity).
+template <int NW, int D>
+__device__ __forceinline__ void run_chunks_wide_f8(const RowKeys& R, const int* s_idx, uint16_t* sK,
+                                                   unsigned char* sKc, float* B0, float* B1, float* sS, float* sX,
+                                                   int64_t nch, bool active, const bf16x8_t (&Qb)[1][D / 32],
+                                                   f32x4 (&O)[1][D / 32], float (&m_run)[1], float (&l_run)[1],
+                                                   float sl2, int wave, int lane, int lt, int hh) {
+  constexpr int CH = kAttnChunk;
+  if (nch > 0) issue_chunk_f8_shared<NW, D>(R, s_idx, R.k_begin, sKc, B0, sS, wave, lane);
+  for (int64_t c = 0; c < nch; ++c) {
+    const int par = (int)(c & 1);
+    float* Bc = par ? B1 : B0;
+    const float* Sc = sS + par * CH;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    convert_chunk_f8<NW * 64, D, true>(sKc, sKc, sK, sK, Bc);
+    __syncthreads();
+    if (c + 1 < nch)
+      issue_chunk_f8_shared<NW, D>(R, s_idx, R.k_begin + (c + 1) * CH, sKc, par ? B0 : B1, sS + (1 - par) * CH, wave,
+                                   lane);
+    if (active) attend_wide_scores<D, true>(sK, Bc, sX, Qb, sl2, lt, hh, lane, Sc);
+    __syncthreads();
+    if (active) {
+      f32x4 S[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) S[kt] = reinterpret_cast<const f32x4*>(sX)[(lt * 4 + kt) * 64 + lane];
+      attend_wide_pv<D, true>(sK, S, O, m_run, l_run, hh, lane, Sc);
+    }
+    __syncthreads();
+  }
+}
+
 // LDS of one attention workgroup: two chunk buffers (K, V, mask; shared entries
 // (SKV) keep one row that serves as both); AttnSmem adds the split's CSA ids.
 template <int D, bool SKV = false>
@@ -766,7 +840,8 @@ struct AttnSmem : AttnBuf<D, SKV> {
 template <int NW, int HT, int D, int KP, bool QP = false, bool SKV = false, bool F8 = false>
 __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, AttnBuf<D, SKV>& sm, int* s_idx,
                                            bool ids_ready = false) {
-  static_assert(!F8 || (!SKV && D <= 128), "FP8 caches: separate K and V rows of up to 128");
+  static_assert(!F8 || (!SKV && D <= 128) || (SKV && D == 512),
+                "FP8 caches: separate K and V rows of up to 128, or shared rows of 512");
   static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
   constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
   static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1), "wide rows: 8 waves, one tile per pair");
@@ -833,13 +908,24 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
     auto bytes = [&](const void* t, int64_t bs, bool on) {
       return on ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(t) + (int64_t)b * bs) : qrow;
     };
-    R.kc = bytes(p.kc, p.kc_bs, p.mask & 1u); R.vc = bytes(p.vc, p.vc_bs, p.mask & 1u);
-    R.kh = bytes(p.kh, p.kh_bs, p.mask & 2u); R.vh = bytes(p.vh, p.vh_bs, p.mask & 2u);
-    R.kr = bytes(p.kr, p.kr_bs, p.mask & 4u); R.vr = bytes(p.vr, p.vr_bs, p.mask & 4u);
+    R.kc = bytes(p.kc, p.kc_bs, p.mask & 1u);
+    R.kh = bytes(p.kh, p.kh_bs, p.mask & 2u);
+    R.kr = bytes(p.kr, p.kr_bs, p.mask & 4u);
     const float* fb = reinterpret_cast<const float*>(qrow);
-    R.kcs = (p.mask & 1u) ? p.kcs + (int64_t)b * p.kcs_bs : fb; R.vcs = (p.mask & 1u) ? p.vcs + (int64_t)b * p.vcs_bs : fb;
-    R.khs = (p.mask & 2u) ? p.khs + (int64_t)b * p.khs_bs : fb; R.vhs = (p.mask & 2u) ? p.vhs + (int64_t)b * p.vhs_bs : fb;
-    R.krs = (p.mask & 4u) ? p.krs + (int64_t)b * p.krs_bs : fb; R.vrs = (p.mask & 4u) ? p.vrs + (int64_t)b * p.vrs_bs : fb;
+    R.kcs = (p.mask & 1u) ? p.kcs + (int64_t)b * p.kcs_bs : fb;
+    R.khs = (p.mask & 2u) ? p.khs + (int64_t)b * p.khs_bs : fb;
+    R.krs = (p.mask & 4u) ? p.krs + (int64_t)b * p.krs_bs : fb;
+    if constexpr (SKV) {   // every row its own value: the value tables are the key tables
+      R.vc = R.kc; R.vh = R.kh; R.vr = R.kr;
+      R.vcs = R.kcs; R.vhs = R.khs; R.vrs = R.krs;
+    } else {
+      R.vc = bytes(p.vc, p.vc_bs, p.mask & 1u);
+      R.vh = bytes(p.vh, p.vh_bs, p.mask & 2u);
+      R.vr = bytes(p.vr, p.vr_bs, p.mask & 4u);
+      R.vcs = (p.mask & 1u) ? p.vcs + (int64_t)b * p.vcs_bs : fb;
+      R.vhs = (p.mask & 2u) ? p.vhs + (int64_t)b * p.vhs_bs : fb;
+      R.vrs = (p.mask & 4u) ? p.vrs + (int64_t)b * p.vrs_bs : fb;
+    }
   }
   if (!ids_ready && n_idx > 0) {
 #pragma unroll
@@ -863,7 +949,10 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
   }
 
   const int64_t nch = R.k_end > R.k_begin ? (R.k_end - R.k_begin + CH - 1) / CH : 0;
-  if constexpr (F8)
+  if constexpr (F8 && WIDE)
+    run_chunks_wide_f8<NW, D>(R, s_idx, sm.K0(), reinterpret_cast<unsigned char*>(sm.K1()), sm.B0, sm.B1, sm.S8, sm.X,
+                              nch, tv[0], Qb, O, m_run, l_run, sl2, wave, lane, wave % TW, kh);
+  else if constexpr (F8)
     run_chunks_f8<NW, D, HT, KP>(R, s_idx, sm.K0(), sm.V0(), reinterpret_cast<unsigned char*>(sm.K1()),
                                  reinterpret_cast<unsigned char*>(sm.V1()), sm.B0, sm.B1, sm.S8, nch, tv[0], Qb, O,
                                  m_run, l_run, sl2, wave, lane, kh);

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kSelThreads) void select_attn_kernel(SelectP sp, At
 template <int D, int KP>
 static void launch_sa(const SelectP& sp, int n_sel, const AttnP& ap, dim3 g, hipStream_t s, int tid) {
   const dim3 blk(kSelThreads);
-  constexpr bool CAN_F8 = D <= 128;
+  constexpr bool CAN_F8 = D <= 128 || D == 512;   // (rows of 512 are shared entries)
   if (CAN_F8 && ap.f8) {
     if (ap.rope_out) V4A_LAUNCH(tid, (select_attn_kernel<D, KP, true, CAN_F8>), g, blk, 0, s, sp, ap, n_sel);
     else V4A_LAUNCH(tid, (select_attn_kernel<D, KP, false, CAN_F8>), g, blk, 0, s, sp, ap, n_sel);

@@ -36,7 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import C1, C2, C3, C4, C5, C6, C7, C8, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
+from .configs import C1, C2, C3, C4, C5, C6, C7, C8, C9, CONFIGS, CSA, HCA, SWA, LayerConfig  # noqa: F401
 
 # appending a stream leaves the earlier ones' draws unchanged
 _STREAMS = ("q", "qi", "wi", "ki", "kc", "vc", "kh", "vh", "k_raw", "v_raw",
@@ -134,7 +134,8 @@ def generate(cfg: LayerConfig, seed: int | None = None) -> dict:
                 kc[b, needles[b]] += 3.0 * qm / np.linalg.norm(qm)
         if cfg.kv_fp8:
             out["kc"], out["kc_scale"] = _fp8_rows(kc)
-            out["vc"], out["vc_scale"] = _fp8_rows(vc)
+            if not cfg.shared_kv:
+                out["vc"], out["vc_scale"] = _fp8_rows(vc)
         else:
             out["kc"] = _store(kc, cfg.dtype)
             if not cfg.shared_kv:

@@ -164,4 +164,13 @@ C8 = LayerConfig(
     branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
     seed=20260008, timed="index_topk + decode", ki_fp8=True, kv_fp8=True)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8)}
+# The pages' layer shape (C6) with its caches in FP8 as well: the indexer keys and the
+# shared entries of 512, each row one scale that serves it as key and as value.
+C9 = LayerConfig(
+    name="c9_shared_kv_c512_fp8_decode_b1_1m", dtype="bf16", batch=1, pos=1048576, tq=1, heads=128,
+    dim=512, idx_heads=64, idx_dim=64, m=4, topk=1024, m_hca=128, window=128,
+    branches=CSA | HCA | SWA, needles=64, compress="none", compress_tokens=0,
+    seed=20260009, timed="index_topk + decode", shared_kv=True, rope_dims=64, q_norm=True, ki_fp8=True,
+    kv_fp8=True)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9)}

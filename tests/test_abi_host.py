@@ -335,6 +335,16 @@ def test_fp8_cache_argument_checks():
     r, msg = _st(L.v4attn_decode, good_attn(**dict(f8, flags=V.SHARED_KV, vc=none, vh=none, v_raw=none), **scales),
                  None, 0, None)
     assert r == ENOTSUP
+    # shared entries of 512 in FP8: the key rows' scales serve as the values' too
+    s512 = dict(kv_dtype=V.FP8_E4M3, dim=512, flags=V.SHARED_KV, q=_T(bs=64 * 512, rs=64 * 512),
+                o=_T(bs=64 * 512, rs=64 * 512), kc=_T(bs=512 * 32768, rs=512), vc=none,
+                kh=_T(bs=512 * 1024, rs=512), vh=none, k_raw=_T(bs=512 * 128, rs=512), v_raw=none)
+    kscales = {n: _T(bs=32768, rs=1) for n in ("kc_scale", "kh_scale", "kr_scale")}
+    assert L.v4attn_decode_workspace(ctypes.byref(good_attn(**s512, **kscales))) > 0
+    r, msg = _st(L.v4attn_decode, good_attn(**s512, **kscales, vh_scale=_T(bs=32768, rs=1)), None, 0, None)
+    assert r == EINVAL and "vc_scale" in msg
+    r, msg = _st(L.v4attn_decode, good_attn(**dict(s512, kv_dtype=0)), None, 0, None)   # bf16 rows of 512 still fine
+    assert r != ENOTSUP
 
 
 def test_noalloc_step_validates_before_touching_the_device():

@@ -108,10 +108,11 @@ def test_fp8_caches_with_query_prep_and_output_rotation(fused):
 
 
 def test_fp8_caches_and_shared_rows_batch_invariant_mode():
-    # the batch-invariant split plan over FP8 caches, and over shared rows of 512
+    # the batch-invariant split plan over FP8 caches, over shared rows of 512, and both
     import compressed_attention_02_amd as V
     for cfg in (C.C8.small(name="f8i", heads=64, batch=3, pos=40961, needles=8),
-                C.C6.small(name="s6i", heads=64, batch=2, pos=40961, needles=8)):
+                C.C6.small(name="s6i", heads=64, batch=2, pos=40961, needles=8),
+                C.C9.small(name="f8si", heads=64, batch=2, pos=40961, needles=8)):
         r = Run(cfg).run()
         kw = r.step.attn_kwargs()
         if cfg.ki_fp8:
@@ -125,3 +126,37 @@ def test_fp8_caches_and_shared_rows_batch_invariant_mode():
         torch.cuda.synchronize()
         r.check_topk()
         r.check_attn()
+
+
+# ---- FP8 shared entries of 512 (the pages' layer with FP8 caches): a row's codes
+# serve as its key and its value, one scale per row in both roles; each chunk's
+# codes are staged and converted in LDS for the wave-pair scoring of wide rows
+@pytest.mark.parametrize("heads,batch,branches,fused", [
+    (128, 1, 7, False), (128, 1, 7, True), (64, 3, 7, True), (16, 2, 7, False), (128, 2, 6, True), (64, 1, 4, False)])
+def test_fp8_shared_rows_decode(heads, batch, branches, fused):
+    cfg = C.C9.small(name="f8s", heads=heads, batch=batch, pos=70003, branches=branches,
+                     needles=8 if branches & 1 else 0, topk=1024 if branches & 1 else 0)
+    print(f"[case] fp8 shared rows H={heads} B={batch} br={branches} fused={fused}", flush=True)
+    Run(cfg).run(fused=fused).check_all()
+
+
+def test_fp8_shared_rows_every_code_and_signs():
+    cfg = C.C9.small(name="f8sc", pos=20483, needles=0, heads=64, topk=512)
+    g = synth.generate(cfg)
+    rng = np.random.default_rng(49)
+    pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for nm in ("kc", "kh", "k_raw"):
+        g[nm][...] = rng.choice(pool, size=g[nm].shape)
+        sc = rng.uniform(0.001, 0.01, g[nm + "_scale"].shape).astype(np.float32)
+        sc[..., ::29] *= -1
+        sc[..., ::41] = 0
+        g[nm + "_scale"][...] = sc
+    print("[case] fp8 shared rows codes", flush=True)
+    Run(cfg, gen=g).run(fused=True).check_all()
+
+
+def test_full_c9_decode_step():
+    print("[case] full c9", flush=True)
+    r = Run(C.C9).run(fused=True).check_all()
+    idx = dev_to_np(r.step.idx)
+    assert set(r.g["needles"][0].tolist()) <= set(idx[0, 0].tolist())
