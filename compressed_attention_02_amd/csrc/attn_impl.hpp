@@ -553,33 +553,62 @@ __device__ __forceinline__ void run_chunks(const RowKeys& R, const int* s_idx, u
   }
 }
 
-// The chunk pipeline of FP8 caches: one staging buffer of codes and one bf16 chunk
-// buffer.  Each chunk's codes and scales land in staging, are converted into the
-// bf16 layout, and then the next chunk's loads are issued into staging while this
-// one is computed (the mask and scale arrays alternate by chunk parity).
+// Loads that issue_chunk_f8 (shared: issue_chunk_f8_shared) gives wave `wave` for
+// one chunk: its code pieces (K and V, or K alone) and its scale word.
+template <int NW, int D, bool SHARED>
+__device__ __forceinline__ int f8_chunk_loads(int wave) {
+  constexpr int PS = D / 16, RPI = 64 / PS, NI = kAttnChunk / RPI;
+  const int nu = wave < NI ? (NI - 1 - wave) / NW + 1 : 0;
+  return SHARED ? nu + (wave == 0 ? 1 : 0) : 2 * nu + (wave < 2 ? 1 : 0);
+}
+// Waits until at most n (wave-uniform) of the wave's vector memory operations are
+// outstanding; n above 7 waits for 7.
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7)); break;
+  }
+}
+
+// The chunk pipeline of FP8 caches: two staging halves of codes and one bf16 chunk
+// buffer.  Chunks 0 and 1 are issued together; chunk c lands in staging half c & 1,
+// is converted into the bf16 layout and computed while chunk c + 1 is in flight, and
+// chunk c + 2 is issued into its half once it is done (the mask and scale arrays
+// alternate by chunk parity as well).
 template <int NW, int D, int HT, int KP>
 __device__ __forceinline__ void run_chunks_f8(const RowKeys& R, const int* s_idx, uint16_t* sK, uint16_t* sV,
                                               unsigned char* sKc, unsigned char* sVc, float* B0, float* B1,
                                               float* sS, int64_t nch, bool active, const bf16x8_t (&Qb)[HT][D / 32],
                                               f32x4 (&O)[HT][D / 16], float (&m_run)[HT], float (&l_run)[HT],
                                               float sl2, int wave, int lane, int kh) {
-  constexpr int CH = kAttnChunk;
+  constexpr int CH = kAttnChunk, SB = kAttnChunk * D;   // staging bytes per chunk (K codes; V codes)
   const int col = lane & 15, grp = lane >> 4;
+  const int nl = f8_chunk_loads<NW, D, false>(wave);
   // sS: [parity][K, V][64] scales
-  if (nch > 0) issue_chunk_f8<NW, D>(R, s_idx, R.k_begin, sKc, sVc, B0, sS, sS + CH, wave, lane);
+  auto issue = [&](int64_t c) {
+    const int par = __builtin_amdgcn_readfirstlane((int)(c & 1));   // (the staging address must be scalar)
+    issue_chunk_f8<NW, D>(R, s_idx, R.k_begin + c * CH, sKc + par * SB, sVc + par * SB, par ? B1 : B0,
+                          sS + par * 2 * CH, sS + par * 2 * CH + CH, wave, lane);
+  };
+  if (nch > 0) issue(0);
+  if (nch > 1) issue(1);
   for (int64_t c = 0; c < nch; ++c) {
     const int par = (int)(c & 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wait_vm_at_most(c + 1 < nch ? nl : 0);   // chunk c landed (chunk c + 1 may be in flight)
     __syncthreads();
-    convert_chunk_f8<NW * 64, D>(sKc, sVc, sK, sV, par ? B1 : B0);
+    convert_chunk_f8<NW * 64, D>(sKc + par * SB, sVc + par * SB, sK, sV, par ? B1 : B0);
     __syncthreads();
-    if (c + 1 < nch)
-      issue_chunk_f8<NW, D>(R, s_idx, R.k_begin + (c + 1) * CH, sKc, sVc, par ? B0 : B1, sS + (1 - par) * 2 * CH,
-                            sS + (1 - par) * 2 * CH + CH, wave, lane);
     if (active)
       attend_chunk<D, HT, KP, true>(sK, sV, par ? B1 : B0, Qb, O, m_run, l_run, sl2, col, grp, kh,
                                     sS + par * 2 * CH, sS + par * 2 * CH + CH);
     __syncthreads();
+    if (c + 2 < nch) issue(c + 2);
   }
 }
 
@@ -761,29 +790,32 @@ __device__ __forceinline__ void run_chunks_wide(const RowKeys& R, const int* s_i
   }
 }
 
-// The chunk pipeline of FP8 shared rows of 512: the codes of a chunk land in
-// staging (the second chunk buffer's space), are converted into the first, and the
-// next chunk's loads go out while this one is scored and its products taken (the
-// mask and scale arrays alternate by chunk parity).
+// The chunk pipeline of FP8 shared rows of 512, as run_chunks_f8: two staging halves
+// in the second chunk buffer's space (32 KB of codes each), converted into the first;
+// chunks 0 and 1 go out together, chunk c + 2 once chunk c is done.
 template <int NW, int D>
 __device__ __forceinline__ void run_chunks_wide_f8(const RowKeys& R, const int* s_idx, uint16_t* sK,
                                                    unsigned char* sKc, float* B0, float* B1, float* sS, float* sX,
                                                    int64_t nch, bool active, const bf16x8_t (&Qb)[1][D / 32],
                                                    f32x4 (&O)[1][D / 32], float (&m_run)[1], float (&l_run)[1],
                                                    float sl2, int wave, int lane, int lt, int hh) {
-  constexpr int CH = kAttnChunk;
-  if (nch > 0) issue_chunk_f8_shared<NW, D>(R, s_idx, R.k_begin, sKc, B0, sS, wave, lane);
+  constexpr int CH = kAttnChunk, SB = kAttnChunk * D;   // staging bytes per chunk
+  const int nl = f8_chunk_loads<NW, D, true>(wave);
+  auto issue = [&](int64_t c) {
+    const int par = __builtin_amdgcn_readfirstlane((int)(c & 1));   // (the staging address must be scalar)
+    issue_chunk_f8_shared<NW, D>(R, s_idx, R.k_begin + c * CH, sKc + par * SB, par ? B1 : B0, sS + par * CH, wave,
+                                 lane);
+  };
+  if (nch > 0) issue(0);
+  if (nch > 1) issue(1);
   for (int64_t c = 0; c < nch; ++c) {
     const int par = (int)(c & 1);
     float* Bc = par ? B1 : B0;
     const float* Sc = sS + par * CH;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wait_vm_at_most(c + 1 < nch ? nl : 0);   // chunk c landed (chunk c + 1 may be in flight)
     __syncthreads();
-    convert_chunk_f8<NW * 64, D, true>(sKc, sKc, sK, sK, Bc);
+    convert_chunk_f8<NW * 64, D, true>(sKc + par * SB, sKc + par * SB, sK, sK, Bc);
     __syncthreads();
-    if (c + 1 < nch)
-      issue_chunk_f8_shared<NW, D>(R, s_idx, R.k_begin + (c + 1) * CH, sKc, par ? B0 : B1, sS + (1 - par) * CH, wave,
-                                   lane);
     if (active) attend_wide_scores<D, true>(sK, Bc, sX, Qb, sl2, lt, hh, lane, Sc);
     __syncthreads();
     if (active) {
@@ -793,6 +825,7 @@ __device__ __forceinline__ void run_chunks_wide_f8(const RowKeys& R, const int* 
       attend_wide_pv<D, true>(sK, S, O, m_run, l_run, hh, lane, Sc);
     }
     __syncthreads();
+    if (c + 2 < nch) issue(c + 2);
   }
 }
 
