@@ -6,26 +6,40 @@
 // section: k = 1024 for Pro, 512 for Flash).  Score form fixed by the layer
 // configuration: s_j = sum_h w_h * ReLU(qi_h . ki_j).
 //
-// Two launches per group of query rows, with no global atomics and no state that
-// has to be cleared between calls:
-//   score   bf16 MFMA 16x16x32 (indexer heads on M, blocks on N) or fp32 VALU over
-//           tiles of 256 blocks.  Writes the fp32 scores; each wave (64 consecutive
-//           blocks) also reports its 4 best (key, id) pairs and the key of its 5th
-//           best, which bounds every key it leaves out.
-//   select  one 512-thread workgroup per row.  The k-th largest of the wave maxima
-//           bounds the row's k-th key from below (the k-th largest of any subset
-//           does), so the reports at or above it (an LDS pool, about k entries)
-//           contain the reports' top-k, whose exact k-th key T a rank search over
-//           power-of-two slices of the live key range finds (then over the ids, for
-//           ties: the lower id wins).  If no wave's bound reaches T, nothing left
-//           unreported can beat T and the pool's top-k is the row's.  Otherwise the
-//           waves that may hide elements >= T are rescanned into the pool first.
-//           Reports come in id order and pools are built by order-preserving
-//           compaction, so the k ids come out ascending without a sort.  Too many
-//           rescans, an LDS overflow or more than 2048 tiles send the row to the same
-//           search over all of its scores.  Rows with n_vis < k are padded with -1.
-// Keys are the order-preserving uint32 image of the fp32 scores, so "larger key" is
-// "larger score"; the result does not depend on launch shape or timing.
+// The keys are the order-preserving uint32 image of the fp32 scores, so "larger key"
+// is "larger score"; the result does not depend on launch shape or timing.
+//
+// score   bf16 / FP8 MFMA 16x16x32 (indexer heads on M, blocks on N) or fp32 VALU,
+//         over tiles of 256 blocks.  Every tile leaves a report: the keys of its 8
+//         best blocks in id order with their offsets, and a bound, the key of the
+//         best block the report leaves out (it bounds every other one).  Decode
+//         builds the report in two phases: each 64-block wave keeps its 4 (or 8)
+//         best as candidates, then one wave ranks the tile's candidates by counting
+//         and keeps the 8 ahead of the rest (bound: the best candidate or wave
+//         remainder not kept).  Prefill keeps the tile's exact best 4 (rounds of
+//         wave maxima).  The fp32 scores are stored too, for rescans.
+// select  one 512-thread workgroup per row, the reports of the row's tiles in its
+//         registers.  (1) The exact k-th key T of all the reports: a rank search
+//         over a histogram of the live key range (8192 bins, two levels); when the
+//         bin holding T has at most 64 keys, those keys are gathered and ranked
+//         directly.  (2) If no tile's bound reaches T, the reports hold every key
+//         >= T and their top-k is the row's, written in id order.  (3) Otherwise
+//         the few tiles whose bound reaches T are rescanned from their stored
+//         scores: their keys >= T join the other tiles' reports >= T, and T is
+//         searched again in that pool.  Ties at T go to the lower ids; rows with
+//         n_vis < k are padded with -1.  Too many rescans, or more tiles than the
+//         registers hold, send the row to the same search over all its scores.
+//
+// Threshold mode (prefill chunks on long contexts, where most tiles hold no pick):
+// a first score pass over every 64th tile stores those scores; each row takes
+// from them a key theta below its k-th key (the sample's rank 3k n_s / n_vis + 16
+// key), which holds for all but rare rows.  The full pass then reports, for every
+// tile with at most 8 keys >= theta, exactly those keys (the bound is theta - 1:
+// no other key of the tile reaches theta) and stores no scores; only the denser
+// tiles store scores and report their exact best 8.  The selection flags a row
+// whose k-th key falls below theta (its reports may miss keys); a repair pass
+// scores and selects the flagged rows' groups again, exactly.  No global atomics,
+// and every buffer a launch reads is written earlier in the same call.
 #include "qprep_impl.hpp"
 #include "score_impl.hpp"
 #include "select_impl.hpp"

@@ -23,8 +23,8 @@ namespace v4a {
 // (16 rows, one piece column) are free of bank conflicts.  QI and the head weights
 // stay in registers.  With NB = 2 the next tile loads while the current one is
 // scored.  Each wave scores its 64 keys: ReLU, w-weighted head sum (row swaps across
-// the 4 lane groups), then its top-4 report, stored at the wave's global index
-// (block / 64), whatever NW is.
+// the 4 lane groups); the tile's report (its 8 best keys and the bound of the rest)
+// comes from the waves' candidates, ranked by one wave.
 template <int DI> __device__ __forceinline__ int swz_ki(int r) { return DI == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 // FP8 key rows (DI bytes, DI/16 pieces): rows r that share a 256-byte bank offset
 // (r mod 256/DI) get distinct piece XORs, so the 8-byte fragment reads of 16 rows
