@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "as_f64", "compress", "index_scores", "topk_select", "attend",
     "decode_keyset", "decode_query", "prefill", "lse_merge", "n_visible", "rms_norm",
-    "rope", "compress_entries", "fp8_e4m3_decode", "fp8_rows",
+    "rope", "compress_entries", "fp8_e4m3_decode", "fp8_rows", "fp8_e4m3_encode", "fp8_quantize_rows",
 ]
 
 
@@ -176,6 +176,46 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
 def fp8_rows(codes, scales) -> np.ndarray:
     """Rows of an FP8 cache: scale[j] * decode(codes[j])."""
     return fp8_e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """The E4M3 code whose value is nearest to each x (|x| <= 448), and of two equally
+    near the one with an even mantissa (last code bit 0): round to nearest even,
+    taken as a search over the 127 finite magnitudes that ``fp8_e4m3_decode``
+    defines.  The sign bit is x's own (so -0.0 gives 0x80).
+
+    [wiki] the quantization and deployment section (FP8 caches); writing a cache row
+    in FP8 is the inverse of reading it, and nearest-even rounding is a reading.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 448.0) or np.any(np.isnan(a)):
+        raise ValueError("E4M3 encoding takes finite |x| <= 448")
+    mags = fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))   # codes 0..126, ascending
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == mags[hi], hi, pick)
+    return (pick | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_rows(rows) -> tuple[np.ndarray, np.ndarray]:
+    """Rows as an FP8 cache stores them: per row the scale max|row| / 448 (the row's
+    largest magnitude lands on the largest finite E4M3 value) and the codes of
+    row / scale; a row of zeros gets scale 0 and zero codes.  Returns (codes
+    [..., d] uint8, scales [...] fp64); ``fp8_rows`` reads them back.
+
+    The pages give no scale rule for their FP8 caches; one scale per row at its
+    maximum magnitude is the reading taken.
+    """
+    x = np.asarray(rows, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = amax / 448.0
+    safe = np.where(scale > 0, scale, 1.0)
+    codes = fp8_e4m3_encode(np.clip(x / safe[..., None], -448.0, 448.0))
+    codes = np.where((scale > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
 
 
 def index_scores(qi: np.ndarray, wi: np.ndarray, ki: np.ndarray) -> np.ndarray:

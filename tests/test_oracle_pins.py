@@ -669,6 +669,52 @@ def test_fp8_rows_scale_and_scores():
     np.testing.assert_allclose(s, s0 * scales, rtol=1e-14, atol=0)
 
 
+def test_fp8_e4m3_encode_closed_forms_and_library():
+    # closed forms: zero, the largest finite value, the smallest subnormal; ties go to
+    # the even code: 2^-10 (between 0 and 2^-9) to 0, 3*2^-10 (between codes 1 and 2)
+    # to 2, 1.0625 (between 1.0 = 0x38 and 1.125 = 0x39) to 0x38, 1.1875 (between 0x39
+    # and 0x3A) to 0x3A; the sign is the value's own
+    got = O.fp8_e4m3_encode([0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875, -0.0,
+                             -1.0, 440.0, 0.99])
+    assert list(got) == [0x00, 0x7E, 0xFE, 0x01, 0x00, 0x02, 0x38, 0x3A, 0x80, 0xB8, 0x7E, 0x38]
+    # every finite code is its own value's code
+    codes = np.arange(256, dtype=np.uint8)
+    fin = (codes & 0x7F) != 0x7F
+    assert np.array_equal(O.fp8_e4m3_encode(O.fp8_e4m3_decode(codes[fin])), codes[fin])
+    # torch's float8_e4m3fn cast (round to nearest even) on random values and on every
+    # midpoint between neighbouring magnitudes, both signs
+    rng = np.random.default_rng(47)
+    mags = O.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[1:] + mags[:-1]) / 2
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000), 0.01 * rng.standard_normal(5000),
+                        mids, -mids]).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x.astype(np.float64)), lib)
+    with pytest.raises(ValueError):
+        O.fp8_e4m3_encode([449.0])
+
+
+def test_fp8_quantize_rows():
+    rng = np.random.default_rng(48)
+    x = rng.standard_normal((6, 64)) * rng.uniform(0.01, 10, (6, 1))
+    x[2] = 0.0
+    codes, scales = O.fp8_quantize_rows(x)
+    # the scale puts each row's largest magnitude on 448, which decodes exactly
+    assert np.array_equal(scales, np.max(np.abs(x), axis=-1) / 448.0)
+    back = O.fp8_rows(codes, scales)
+    top = np.argmax(np.abs(x), axis=-1)
+    for r in (0, 1, 3, 4, 5):
+        assert abs(back[r, top[r]]) == pytest.approx(abs(x[r, top[r]]), rel=1e-15)
+    # a zero row: scale 0, codes 0, read back as zeros
+    assert scales[2] == 0 and not codes[2].any() and not back[2].any()
+    # nearest rounding: within half a step of the value; a step is 2^-3 of the
+    # magnitude's binade above 2^-6 and 2^-9 below, in units of the scale
+    q = np.abs(x) / np.where(scales > 0, scales, 1)[:, None]
+    step = np.where(q >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(q, 2.0 ** -6))) - 3), 2.0 ** -9)
+    err = np.abs(back - x) / np.where(scales > 0, scales, 1)[:, None]
+    assert np.all(err <= step / 2 * (1 + 1e-12))
+
+
 # ----------------------------------------------------------------- bf16 decoding
 def test_bf16_to_f64_every_pattern():
     """Every one of the 65536 bf16 patterns against two references that do not use the
