@@ -35,7 +35,7 @@ BATCH_INVARIANT = 1   # v4a_attn_args.flags
 ROPE_OUTPUT = 2       # v4a_attn_args.flags
 SHARED_KV = 4         # v4a_attn_args.flags
 ROPE_V = 1            # v4a_compress_args.rope_flags
-ABI_VERSION = 7
+ABI_VERSION = 8
 OP_COMPRESS, OP_INDEX_TOPK, OP_DECODE, OP_PREFILL_CHUNK, OP_DECODE_STEP = 0, 1, 2, 3, 4
 KERNELS = {"compress": 0, "index_score": 1, "topk_select": 2, "attn": 3, "merge": 4, "prefill": 5,
            "select_attn": 6, "qprep": 7, "read_probe": 8}
@@ -56,7 +56,8 @@ class CompressArgs(ctypes.Structure):
                 ("k_raw", Tensor), ("v_raw", Tensor), ("logits", Tensor), ("k_out", Tensor),
                 ("v_out", Tensor), ("norm_k", ctypes.c_void_p), ("norm_v", ctypes.c_void_p),
                 ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("rope_flags", ctypes.c_uint32)]
+                ("rope_flags", ctypes.c_uint32), ("out_dtype", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+                ("k_scale", Tensor), ("v_scale", Tensor)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -194,22 +195,28 @@ def _ws_ptr(ws):
 # ---------------------------------------------------------------- entry points
 def compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int,
                   norm_k=None, norm_v=None, norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4,
-                  rope_v: bool = False) -> CompressArgs:
+                  rope_v: bool = False, k_scale=None, v_scale=None) -> CompressArgs:
+    """k_out / v_out as uint8 receive the entries as FP8 E4M3 codes, with their fp32
+    row scales in k_scale / v_scale [B, N_cap]."""
+    import torch
+    fp8 = k_out is not None and k_out.dtype == torch.uint8
     return CompressArgs(ABI_VERSION, _dtype_code(k_raw), k_raw.shape[0], k_raw.shape[-1], ratio, 0, t0, n,
                         _ptr(raw_start), _tensor(k_raw), _tensor(v_raw), _tensor(logits), _tensor(k_out),
                         _tensor(v_out), _ptr(norm_k), _ptr(norm_v), norm_eps, rope_dims, rope_base,
-                        ROPE_V if rope_v else 0)
+                        ROPE_V if rope_v else 0, FP8_E4M3 if fp8 else 0, 0, _tensor(k_scale), _tensor(v_scale))
 
 
 def compress(k_raw, v_raw, logits, raw_start, k_out, v_out, *, t0: int, n: int, ratio: int, stream=None,
              norm_k=None, norm_v=None, norm_eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 1e4,
-             rope_v: bool = False):
+             rope_v: bool = False, k_scale=None, v_scale=None):
     """v4attn_compress: pool the complete ratio-blocks of [t0, t0+n) into k_out/v_out
     (RMS-normalised with the fp32 gains norm_k / norm_v when given; with rope_dims,
     raw rows are rotated at their positions and entries at their block's last one).
-    v_raw and v_out None: shared K = V entries, K alone is pooled."""
+    v_raw and v_out None: shared K = V entries, K alone is pooled.  uint8 k_out / v_out:
+    FP8 E4M3 entries with fp32 row scales in k_scale / v_scale."""
     a = compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, t0=t0, n=n, ratio=ratio, norm_k=norm_k,
-                      norm_v=norm_v, norm_eps=norm_eps, rope_dims=rope_dims, rope_base=rope_base, rope_v=rope_v)
+                      norm_v=norm_v, norm_eps=norm_eps, rope_dims=rope_dims, rope_base=rope_base, rope_v=rope_v,
+                      k_scale=k_scale, v_scale=v_scale)
     _check(lib().v4attn_compress(ctypes.byref(a), _stream(stream)))
 
 
@@ -220,7 +227,8 @@ class CompressCall:
     def __init__(self, k_raw, v_raw, logits, raw_start, k_out, v_out, **kw):
         self._a = compress_args(k_raw, v_raw, logits, raw_start, k_out, v_out, **kw)
         self._ref = ctypes.byref(self._a)
-        self._keep = (k_raw, v_raw, logits, raw_start, k_out, v_out, kw.get("norm_k"), kw.get("norm_v"))
+        self._keep = (k_raw, v_raw, logits, raw_start, k_out, v_out, kw.get("norm_k"), kw.get("norm_v"),
+                      kw.get("k_scale"), kw.get("v_scale"))
         self._fn = lib().v4attn_compress
 
     def __call__(self, stream=None):

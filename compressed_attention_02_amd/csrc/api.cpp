@@ -277,13 +277,28 @@ v4a_status validate_compress(const v4a_compress_args* a) {
   if (hv && !(a->v_raw.ptr && a->v_out.ptr)) return fail(V4A_EINVAL, "v_raw and v_out must both be set or both be NULL");
   if (!hv && (a->norm_v || (a->rope_flags & V4A_ROPE_V)))
     return fail(V4A_EINVAL, "K-only compression: norm_v must be NULL and rope_flags 0");
+  if (a->out_dtype != 0 && a->out_dtype != a->dtype && a->out_dtype != V4A_FP8_E4M3)
+    return fail(V4A_EINVAL, "out_dtype %d: 0, dtype or V4A_FP8_E4M3", a->out_dtype);
+  const bool f8 = a->out_dtype == V4A_FP8_E4M3;
+  if (!f8 && (a->k_scale.ptr || a->v_scale.ptr)) return fail(V4A_EINVAL, "k_scale / v_scale are for an FP8 output only");
+  if (f8 && a->dim % 16 != 0) return fail(V4A_ENOTSUP, "FP8 entries: dim must be a multiple of 16");
+  if (f8 && !hv && a->v_scale.ptr) return fail(V4A_EINVAL, "K-only compression: v_scale must be NULL");
   if (a->batch == 0 || a->n / a->ratio == 0) return V4A_OK;
   if (!a->raw_start) return fail(V4A_EINVAL, "raw_start is NULL");
+  const int odt = f8 ? V4A_FP8_E4M3 : a->dtype;
   V4A_TRY(check_tensor("k_raw", a->k_raw, a->dtype, a->dim, a->batch));
-  V4A_TRY(check_tensor("k_out", a->k_out, a->dtype, a->dim, a->batch));
+  V4A_TRY(check_tensor("k_out", a->k_out, odt, a->dim, a->batch));
   if (hv) {
     V4A_TRY(check_tensor("v_raw", a->v_raw, a->dtype, a->dim, a->batch));
-    V4A_TRY(check_tensor("v_out", a->v_out, a->dtype, a->dim, a->batch));
+    V4A_TRY(check_tensor("v_out", a->v_out, odt, a->dim, a->batch));
+  }
+  if (f8) {
+    V4A_TRY(check_tensor("k_scale", a->k_scale, V4A_F32, 1, a->batch, 4));
+    if (a->k_scale.row_stride != 1) return fail(V4A_EINVAL, "k_scale: row_stride must be 1");
+    if (hv) {
+      V4A_TRY(check_tensor("v_scale", a->v_scale, V4A_F32, 1, a->batch, 4));
+      if (a->v_scale.row_stride != 1) return fail(V4A_EINVAL, "v_scale: row_stride must be 1");
+    }
   }
   if (!a->logits.ptr) return fail(V4A_EINVAL, "logits: NULL pointer");
   if (!aligned(a->logits.ptr, 4)) return fail(V4A_EINVAL, "logits: pointer not 4-byte aligned");
@@ -860,6 +875,9 @@ v4a_status v4attn_compress(const v4a_compress_args* a, hipStream_t stream) {
   p.gk = a->norm_k; p.gv = a->norm_v; p.eps = a->norm_eps;
   p.rope = a->rope_dims; p.rope_v = (a->rope_flags & V4A_ROPE_V) != 0;
   p.rope_lb = a->rope_dims > 0 ? std::log2((double)a->rope_base) : 0.0;
+  p.f8out = a->out_dtype == V4A_FP8_E4M3;
+  p.ks_out = (float*)a->k_scale.ptr; p.vs_out = (float*)a->v_scale.ptr;
+  p.kso_bs = a->k_scale.batch_stride; p.vso_bs = a->v_scale.batch_stride;
   if (cdiv(nb, p.bpw) > INT32_MAX || a->batch > 65535) return fail(V4A_ENOTSUP, "launch too large");
   V4A_TRY(hip_check(launch_compress(a->dtype, p, a->batch, stream, V4A_K_COMPRESS), "compress launch"));
   return ok();

@@ -15,7 +15,9 @@
 // is g * y / sqrt(mean(y^2) + eps).  Optional partial RoPE (the partial RoPE
 // paragraph of the same section): raw rows are rotated at their own positions; the
 // entry is pooled and normalised in the unrotated frame and stored rotated at the
-// position of its block's last token.
+// position of its block's last token.  Optional FP8 entries ([wiki] quantization and
+// deployment section: FP8 KV caches): one fp32 scale max|y| / 448 per entry and the
+// E4M3 codes of y / scale, nearest with ties to even.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,7 +44,25 @@ template <> struct Chunk<uint16_t> {
 constexpr int kRopeTab = 4096;
 
 // HV: the block has V rows too (else the entries are shared K = V: K alone is pooled)
-template <typename T, bool ROPE, bool HV>
+// The E4M3 code of x, |x| <= 448 (larger magnitudes are taken as 448): the nearest
+// finite E4M3 value, ties to the even code.  Below 2^-6 the values are the multiples
+// of 2^-9 (codes 0..8, 8 being 2^-6 itself); above, the fp32 mantissa is rounded to 3
+// bits (nearest, ties to even: add 2^19 - 1 plus the lowest kept bit, carrying into
+// the exponent), and the exponent is rebased from bias 127 to bias 7.
+__device__ __forceinline__ uint32_t e4m3_nearest(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t m;
+  if (a < 0.015625f) {
+    m = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    m = ((bits + 0x7FFFFu + ((bits >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+  }
+  return sign | m;
+}
+
+template <typename T, bool ROPE, bool HV, bool F8O>
 __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   constexpr int N = Chunk<T>::N;
   __shared__ float s_max[256];
@@ -169,18 +189,64 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
       }
     }
   }
-  if (active && g == 0) {
-    if (R) {  // the entry's own rotation, at its block's last position
+  if (active && g == 0 && R) {  // the entry's own rotation, at its block's last position
 #pragma unroll
-      for (int k2 = 0; k2 < N / 2; ++k2) {
-        const int e0 = c * N + 2 * k2;
-        if (e0 < lo) continue;
-        float cs, sn;
-        rope_cs((double)((j + 1) * p.r - 1), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
-        rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, false);
-        if (HV && p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, false);
+    for (int k2 = 0; k2 < N / 2; ++k2) {
+      const int e0 = c * N + 2 * k2;
+      if (e0 < lo) continue;
+      float cs, sn;
+      rope_cs((double)((j + 1) * p.r - 1), (e0 - lo) / 2, R, p.rope_lb, cs, sn);
+      rot2(ak[2 * k2], ak[2 * k2 + 1], cs, sn, false);
+      if (HV && p.rope_v) rot2(av[2 * k2], av[2 * k2 + 1], cs, sn, false);
+    }
+  }
+  if constexpr (F8O) {
+    // FP8 entries: the row's scale s = max |y| / 448 (its ch chunk threads meet in
+    // LDS, in chunk order), then the codes of y / s and, from chunk thread 0, s
+    float mk = 0.f, mv = 0.f;
+    if (active && g == 0) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        mk = fmaxf(mk, fabsf(ak[e]));
+        if (HV) mv = fmaxf(mv, fabsf(av[e]));
       }
     }
+    __syncthreads();   // the combine or the norm above may still read s_acc
+    s_acc[tid][0] = mk;
+    s_acc[tid][1] = mv;
+    __syncthreads();
+    if (active && g == 0) {
+      for (int cc = 0; cc < p.ch; ++cc) {
+        mk = fmaxf(mk, s_acc[slot * per_block + cc][0]);
+        mv = fmaxf(mv, s_acc[slot * per_block + cc][1]);
+      }
+      const float sk = mk / 448.f, sv = mv / 448.f;
+      uint32_t wk[N / 4], wv[N / 4];
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        wk[q] = 0u;
+        wv[q] = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[q] |= e4m3_nearest(sk > 0.f ? ak[4 * q + e] / sk : 0.f) << (8 * e);
+          if (HV) wv[q] |= e4m3_nearest(sv > 0.f ? av[4 * q + e] / sv : 0.f) << (8 * e);
+        }
+      }
+      unsigned char* ko = reinterpret_cast<unsigned char*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
+      unsigned char* vo = reinterpret_cast<unsigned char*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
+      if constexpr (N == 8) {
+        *reinterpret_cast<uint2*>(ko) = make_uint2(wk[0], wk[1]);
+        if (HV) *reinterpret_cast<uint2*>(vo) = make_uint2(wv[0], wv[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(ko) = wk[0];
+        if (HV) *reinterpret_cast<uint32_t*>(vo) = wv[0];
+      }
+      if (c == 0) {
+        p.ks_out[(int64_t)b * p.kso_bs + j] = sk;
+        if (HV) p.vs_out[(int64_t)b * p.vso_bs + j] = sv;
+      }
+    }
+  } else if (active && g == 0) {
     T* ko = reinterpret_cast<T*>(p.k_out) + (int64_t)b * p.ko_bs + j * p.ko_rs + c * N;
     T* vo = reinterpret_cast<T*>(p.v_out) + (int64_t)b * p.vo_bs + j * p.vo_rs + c * N;
     Chunk<T>::store(ko, ak);
@@ -188,21 +254,27 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressP p) {
   }
 }
 
-template <typename T, bool HV>
+template <typename T, bool HV, bool F8O>
 static void launch_variant(const CompressP& p, dim3 grid, hipStream_t s, int tid) {
-  if (p.rope) V4A_LAUNCH(tid, (compress_kernel<T, true, HV>), grid, dim3(256), 0, s, p);
-  else V4A_LAUNCH(tid, (compress_kernel<T, false, HV>), grid, dim3(256), 0, s, p);
+  if (p.rope) V4A_LAUNCH(tid, (compress_kernel<T, true, HV, F8O>), grid, dim3(256), 0, s, p);
+  else V4A_LAUNCH(tid, (compress_kernel<T, false, HV, F8O>), grid, dim3(256), 0, s, p);
+}
+
+template <typename T, bool HV>
+static void launch_out(const CompressP& p, dim3 grid, hipStream_t s, int tid) {
+  if (p.f8out) launch_variant<T, HV, true>(p, grid, s, tid);
+  else launch_variant<T, HV, false>(p, grid, s, tid);
 }
 
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid) {
   const dim3 grid((unsigned)((p.nb + p.bpw - 1) / p.bpw), (unsigned)batch);
   const bool hv = p.v_raw != nullptr;
   if (dtype == 0) {
-    if (hv) launch_variant<float, true>(p, grid, s, tid);
-    else launch_variant<float, false>(p, grid, s, tid);
+    if (hv) launch_out<float, true>(p, grid, s, tid);
+    else launch_out<float, false>(p, grid, s, tid);
   } else {
-    if (hv) launch_variant<uint16_t, true>(p, grid, s, tid);
-    else launch_variant<uint16_t, false>(p, grid, s, tid);
+    if (hv) launch_out<uint16_t, true>(p, grid, s, tid);
+    else launch_out<uint16_t, false>(p, grid, s, tid);
   }
   return hipGetLastError();
 }

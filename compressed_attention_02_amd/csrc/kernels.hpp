@@ -23,6 +23,8 @@ struct CompressP {
   int rope;            // rotated channels R (0: off), the last R of each row
   int rope_v;          // raw V rows are rotated too
   double rope_lb;      // log2 of the RoPE base
+  int f8out;           // entries stored as FP8 E4M3 codes (k_out / v_out bytes) with fp32 row scales
+  float* ks_out; float* vs_out; int64_t kso_bs, vso_bs;
 };
 hipError_t launch_compress(int dtype, const CompressP& p, int batch, hipStream_t s, int tid);
 

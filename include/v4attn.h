@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define V4ATTN_ABI_VERSION 7u
+#define V4ATTN_ABI_VERSION 8u
 
 typedef enum v4a_status {
   V4A_OK = 0,
@@ -118,6 +118,19 @@ typedef struct v4a_tensor {
  *                frame, normalised there, and stored rotated at the position of
  *                its block's last token, (j+1)*r - 1.  Angles are reduced in
  *                fp64.  rope_base > 0, finite.
+ *   out_dtype    0 (entries stored in dtype) or V4A_FP8_E4M3: FP8 caches
+ *                ([wiki] the quantization and deployment section: FP8 KV caches;
+ *                the pages give no scale rule).  Each stored entry y (fp32, after
+ *                the pooling, the norm and the rotation) becomes one fp32 scale
+ *                s = max_c |y_c| / 448 and the E4M3 codes of y / s, each the
+ *                nearest finite E4M3 value, ties to the even code; an all-zero
+ *                entry gets s = 0 and zero codes.  k_out / v_out then hold uint8
+ *                codes [batch][N_cap][d] (strides in bytes, rows 16-byte
+ *                aligned, dim a multiple of 16) and k_scale / v_scale the fp32
+ *                scales [batch][N_cap] (row_stride 1): the layout the attention
+ *                reads with kv_dtype V4A_FP8_E4M3 (value = s * decode(code)).
+ *   k_scale/v_scale  fp32 row scales of an FP8 output; v_scale set iff v_out
+ *                is; both NULL unless out_dtype is V4A_FP8_E4M3
  * ------------------------------------------------------------------------- */
 typedef struct v4a_compress_args {
   uint32_t abi_version;
@@ -138,6 +151,9 @@ typedef struct v4a_compress_args {
   int32_t rope_dims;
   float rope_base;
   uint32_t rope_flags;  /* V4A_ROPE_V or 0 */
+  int32_t out_dtype;    /* 0 (= dtype) or V4A_FP8_E4M3 */
+  int32_t reserved1;
+  v4a_tensor k_scale, v_scale;
 } v4a_compress_args;
 
 v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);

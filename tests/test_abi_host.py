@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     assert "v4attn_workspace_size" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.v4attn_abi_version() == V.ABI_VERSION == 7
+    assert L.v4attn_abi_version() == V.ABI_VERSION == 8
     assert L.v4attn_status_string(0) == b"ok"
     assert L.v4attn_kernel_name(1) == b"index_score"
 
@@ -93,6 +93,27 @@ def test_compress_rejects_tensors():
     # nothing to do is not an error, even with NULL buffers
     assert _st(L.v4attn_compress, good_compress(n=3, k_raw=_T(None)), None)[0] == 0
     assert _st(L.v4attn_compress, good_compress(batch=0), None)[0] == 0
+
+
+def test_compress_rejects_fp8_output():
+    L = V.lib()
+    ks = _T(FAKE, 1024, 1)
+    f8 = dict(out_dtype=V.FP8_E4M3, k_out=_T(FAKE, 128 * 1024, 128), v_out=_T(FAKE, 128 * 1024, 128))
+    assert _st(L.v4attn_compress, good_compress(out_dtype=7), None)[0] == EINVAL
+    # scales belong to an FP8 output only
+    assert _st(L.v4attn_compress, good_compress(k_scale=ks), None)[0] == EINVAL
+    # an FP8 output needs its scales: present, 4-byte aligned, one per row (row_stride 1)
+    assert _st(L.v4attn_compress, good_compress(**f8), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(**f8, k_scale=ks), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(**f8, k_scale=ks, v_scale=_T(FAKE, 1024, 2)), None)[0] == EINVAL
+    assert _st(L.v4attn_compress, good_compress(**f8, k_scale=_T(FAKE + 2, 1024, 1), v_scale=ks), None)[0] == EINVAL
+    # code rows of 16-byte multiples: dim a multiple of 16, row_stride a multiple of 16 bytes
+    assert _st(L.v4attn_compress, good_compress(**f8, dim=120, k_scale=ks, v_scale=ks), None)[0] == ENOTSUP
+    bad_rows = dict(f8, k_out=_T(FAKE, 128 * 1024, 136))
+    assert _st(L.v4attn_compress, good_compress(**bad_rows, k_scale=ks, v_scale=ks), None)[0] == EINVAL
+    # K-only pooling takes no v_scale
+    konly = dict(f8, v_out=_T(None))
+    assert _st(L.v4attn_compress, good_compress(**konly, v_raw=_T(None), k_scale=ks, v_scale=ks), None)[0] == EINVAL
 
 
 @pytest.mark.parametrize("field,value,code", [
