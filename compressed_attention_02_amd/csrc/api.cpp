@@ -650,10 +650,10 @@ v4a_status run_index(const v4a_index_args* a, void* ws, size_t ws_bytes, hipStre
 
 // ---------------------------------------------------------------- fused decode step
 // Key list of a decode row = [CSA picks | HCA entries + window].  The second part
-// does not depend on the selection: it is attended on the side stream while the
-// indexer runs, in splits of kps_rest keys; the CSA picks are attended afterwards
-// in one-chunk splits (they sit on the critical path).  Both write partials into
-// one [rows][s_rest + s_csa] table, merged once.
+// does not depend on the selection: its splits of kps_rest keys are workgroups of
+// the selection's own launch, attended while the selection runs; the CSA picks are
+// attended afterwards in one-chunk splits (they sit on the critical path).  Both
+// write partials into one [rows][s_rest + s_csa] table, merged once.
 struct StepPlan {
   bool csa;
   IndexPlan ix;
