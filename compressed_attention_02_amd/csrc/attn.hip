@@ -34,7 +34,7 @@ namespace v4a {
 // per CU, two waves per SIMD, a wave pair per head tile (attend_wide_*).
 template <int NW, int HT, int D, int KP>
 constexpr int attn_waves_per_eu() {
-  return D == 512 ? 2 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
+  return D == 512 ? 2 : (KP == 2 && HT == 2) ? 2 : KP == 2 ? 4 : NW * HT <= 4 ? 2 : 1;
 }
 template <int NW, int HT, int D, int KP, bool QP, bool SKV, bool F8>
 __global__ __launch_bounds__(NW * 64, (attn_waves_per_eu<NW, HT, D, KP>())) void attn_bf16_kernel(AttnP p) {
@@ -238,7 +238,13 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
   // chunk's keys in half (four waves per SIMD); above, one wave per head tile
   // (shared entries at d <= 128 arrive with the value pointers aimed at the keys)
-  if (ntile <= 4) {
+  if (ntile == 4 && !p.f8) {
+    // four tiles: four waves of two head tiles each, two waves per key half, so a
+    // wave's K and V fragment reads from LDS serve two tiles (half the LDS reads of
+    // one tile per wave); two workgroups per CU
+    if (p.dim == 64) launch_bf16<4, 2, 64, 2, false, false>(p, grid, s, tid);
+    else launch_bf16<4, 2, 128, 2, false, false>(p, grid, s, tid);
+  } else if (ntile <= 4) {
     if (p.dim == 64) launch_narrow<8, 1, 64, 2>(p, grid, s, tid);
     else launch_narrow<8, 1, 128, 2>(p, grid, s, tid);
   } else {

@@ -855,9 +855,9 @@ struct AttnSmem : AttnBuf<D, SKV> {
 };
 
 // The work of one workgroup of NW waves on (split, row).  With KP = 1, wave w computes
-// head tiles w, w + NW, ... (HT of them); with KP = 2 (HT = 1), waves w and
-// w + NW/2 share head tile w and take one half of every chunk's keys each, and
-// combine their softmax states through LDS at the end.  With head_groups > 1 the
+// head tiles w, w + NW, ... (HT of them); with KP = 2, waves w and w + NW/2 share
+// head tiles w, w + NW/2, ... (HT of them) and take one half of every chunk's keys
+// each, and combine their softmax states through LDS at the end.  With head_groups > 1 the
 // launch's x index is split * head_groups + group and the workgroup takes only the
 // group's head tiles (fewer queries read and partials written per workgroup).  A
 // tile past the group's is computed on a copy of the group's first tile's queries
@@ -875,7 +875,8 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
                                            bool ids_ready = false) {
   static_assert(!F8 || (!SKV && D <= 128) || (SKV && D == 512),
                 "FP8 caches: separate K and V rows of up to 128, or shared rows of 512");
-  static_assert(KP == 1 || (KP == 2 && HT == 1 && NW % 2 == 0), "key halves pair waves on one head tile");
+  static_assert(KP == 1 || (KP == 2 && NW % 2 == 0 && (NW / 2) * HT <= 4),
+                "key halves pair waves on their head tiles; the combine buffer holds 4 (wave, tile) states");
   constexpr bool WIDE = D > 128;   // wave pairs per head tile (attend_wide_*)
   static_assert(!WIDE || (NW == 8 && HT == 1 && KP == 1), "wide rows: 8 waves, one tile per pair");
   // xs = split * head_groups + group: the workgroup takes group's head tiles
@@ -997,28 +998,36 @@ __device__ __forceinline__ void attn_block(const AttnP& p, int xs, int row, Attn
                                    m_run, l_run, sl2, wave, lane, kh);
 
   if constexpr (KP == 2) {
-    // the second key half hands (O, m, l) to the first through LDS; the chunk
-    // buffers are free (every chunk's reads ended at a barrier, no load in flight)
-    static_assert(TW <= 4, "combine buffer holds 4 waves");
+    // the second key half hands (O, m, l) of each of its tiles to the first through
+    // LDS; the chunk buffers are free (every chunk's reads ended at a barrier, no
+    // load in flight)
     f32x4* sO = reinterpret_cast<f32x4*>(sm.C);
     float* sM = sm.C + 4 * 64 * (D / 4);
-    const int slot = (wave % TW) * 64 + lane;
+    constexpr int NS = TW * HT * 64;   // (wave, tile) state slots
     if (kh == 1) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) sO[dt * TW * 64 + slot] = O[0][dt];
-      sM[slot] = m_run[0];
-      sM[TW * 64 + slot] = l_run[0];
+      for (int t = 0; t < HT; ++t) {
+        const int slot = (t * TW + wave % TW) * 64 + lane;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) sO[dt * NS + slot] = O[t][dt];
+        sM[slot] = m_run[t];
+        sM[NS + slot] = l_run[t];
+      }
     }
     __syncthreads();
     if (kh == 0) {
-      const float m1 = sM[slot], l1 = sM[TW * 64 + slot];
-      const float m = fmaxf(m_run[0], m1);
-      const float a0 = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m);
-      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-      m_run[0] = m;
-      l_run[0] = l_run[0] * a0 + l1 * a1;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[0][dt] = O[0][dt] * a0 + sO[dt * TW * 64 + slot] * a1;
+      for (int t = 0; t < HT; ++t) {
+        const int slot = (t * TW + wave % TW) * 64 + lane;
+        const float m1 = sM[slot], l1 = sM[NS + slot];
+        const float m = fmaxf(m_run[t], m1);
+        const float a0 = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - m);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+        m_run[t] = m;
+        l_run[t] = l_run[t] * a0 + l1 * a1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[t][dt] = O[t][dt] * a0 + sO[dt * NS + slot] * a1;
+      }
     }
   }
 
