@@ -658,6 +658,7 @@ struct StepPlan {
   bool csa;
   IndexPlan ix;
   int64_t rows, n_rest, kps_rest, s_rest, s_csa, s_total;
+  int hg_rest;   // head groups of the rest's launch (0: the attention's default)
   size_t off_attn, off_q, ws_bytes;
   bool fits;   // the split count stays within what the merge takes
 };
@@ -675,7 +676,18 @@ StepPlan plan_step(const v4a_index_args* ix, const v4a_attn_args* a) {
     P.kps_rest = kInvariantKeysPerSplit;
     P.s_rest = cdiv(P.n_rest, P.kps_rest);
   } else if (P.n_rest > 0) {
-    const int64_t per_row = cdiv(2 * (int64_t)cu_count(), P.rows);
+    int64_t per_row = cdiv(2 * (int64_t)cu_count(), P.rows);
+    // shared bf16 rows of 512 (one workgroup per CU): workgroups of two head tiles,
+    // half what one takes at most, so each reads every chunk from LDS for fewer tiles
+    // and writes fewer partials (heads * 514 floats a split: 131 KB at 64 heads), and
+    // about one split per CU and head group (a 128-head step at 1M context: 51.0
+    // against 52.1 us; with FP8 rows the extra rows each CU then loads cost more than
+    // that saves: 71.5 against 67.4 us)
+    const int ntile = std::max(1, a->heads / 16);
+    if (a->dtype == V4A_BF16 && a->dim == 512 && a->kv_dtype != V4A_FP8_E4M3 && ntile % 2 == 0 && ntile >= 4) {
+      P.hg_rest = ntile / 2;
+      per_row = std::max<int64_t>(1, (int64_t)cu_count() / (P.rows * P.hg_rest));
+    }
     P.kps_rest = std::max<int64_t>(round_up(cdiv(P.n_rest, per_row), kAttnChunk), kMinKeysPerSplit);
     P.kps_rest = std::max<int64_t>(P.kps_rest, round_up(cdiv(P.n_rest, kAttnMaxSplits - P.s_csa), kAttnChunk));
     P.s_rest = cdiv(P.n_rest, P.kps_rest);
@@ -741,6 +753,7 @@ v4a_status run_step(const v4a_index_args* ix, const v4a_attn_args* a, void* ws, 
   rest.key_hi = INT64_MAX;
   rest.splits = (int)P.s_rest;
   rest.keys_per_split = (int)P.kps_rest;
+  if (P.hg_rest > 0) rest.head_groups = P.hg_rest;
   rest.split_base = inv ? (int)P.s_csa : 0;
   csa.key_lo = 0;
   csa.key_hi = a->topk;
