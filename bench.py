@@ -272,8 +272,8 @@ def bench_prefill(cfg, args):
         steps[k % 2].step(stream)
     torch.cuda.synchronize()
     V.timing_reset()
-    # a step launches the score and select kernels once per row group (five at 4096
-    # queries): room for many more launches than that, checked below
+    # a step launches the score and select kernels a few times per row group (one
+    # group at 4096 queries): room for many more launches than that, checked below
     ev_cap = 64 * K
     for name in ("index_score", "topk_select", "prefill", "compress", "merge"):
         V.timing_enable(name, ev_cap)

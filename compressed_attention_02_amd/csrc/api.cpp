@@ -105,6 +105,8 @@ const char* kKernelNames[V4A_K_COUNT] = {"compress", "index_score", "topk_select
 // store no scores; it needs rows of at least kThetaMinTiles tiles.
 constexpr int64_t kThetaStride = 64;
 constexpr int64_t kThetaMinTiles = 256;
+// workspace bytes of scores and tile reports for one chunk of index rows
+constexpr int64_t kScoreBudget = (int64_t)8 << 30;
 
 struct IndexPlan {
   int64_t rows, n_cap, sc_rs, ntiles, key_rs, info_rs, chunk_rows;
@@ -121,9 +123,11 @@ IndexPlan plan_index(const v4a_index_args* a) {
   P.ntiles = std::max<int64_t>(1, cdiv(P.n_cap, kTile));
   P.key_rs = round_up(P.ntiles * kTileTop, 64);
   P.info_rs = round_up(P.ntiles, 16);
-  // rows are processed in chunks whose scores fit in 1 GiB
+  // rows are processed in chunks whose scores fit in kScoreBudget (a prefill chunk of
+  // 4096 queries at 1M context takes 4.5 GB, one chunk: each chunk's launches, the
+  // threshold mode's six among them, are paid once)
   const int64_t row_bytes = P.sc_rs * 4 + P.key_rs * 4 + P.info_rs * 16;
-  P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, ((int64_t)1 << 30) / row_bytes));
+  P.chunk_rows = std::max<int64_t>(1, std::min<int64_t>(P.rows, kScoreBudget / row_bytes));
   // queries in groups of 8 share each key tile: a chunk of rows holds whole groups
   P.multi = a->dtype == V4A_BF16 && a->heads == 64 && a->dim == 64 && a->ki_dtype != V4A_FP8_E4M3 &&
             a->tq % 8 == 0 && P.chunk_rows >= 8;
