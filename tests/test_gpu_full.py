@@ -5,6 +5,8 @@ on 256 sampled rows (the first and last rows, rows where a CSA block completes n
 both ends of the chunk, every row where an HCA entry completes and the row before
 it, random rows), which the oracle computes one by one.
 """
+from dataclasses import replace
+
 import pytest
 
 from synth import configs as C
@@ -44,3 +46,19 @@ def test_full_prefill_sampled():
     assert len(rows) == 256
     r.check_topk(rows)
     r.check_attn(rows)
+
+
+@pytest.mark.timeout(900)
+def test_full_prefill_two_row_groups():
+    # A chunk of 8192 queries at 1M context: its index scores and tile reports (about
+    # 1.1 MB a row) exceed what the index call takes at a time, so its rows run in two
+    # groups (the second from about row 7760), whose launches carry a row offset.
+    # Sampled rows of both groups: every 128th row, the rows around the boundary and
+    # the last 8.
+    cfg = replace(C.C5, name="c5_prefill_8192_on_1m", tq=8192, compress_tokens=8192)
+    print("[case] full prefill 8192 on 1M (two index row groups)", flush=True)
+    r = Run(cfg).run()
+    rows = sorted(set(range(0, cfg.tq, 128)) | set(range(7744, 7776)) | set(range(cfg.tq - 8, cfg.tq)))
+    pairs = [(0, i) for i in rows]
+    r.check_topk(pairs)
+    r.check_attn(pairs)
