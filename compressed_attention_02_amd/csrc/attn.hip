@@ -29,7 +29,9 @@
 namespace v4a {
 
 // One workgroup of NW waves per (split, row); two workgroups per CU when each wave
-// computes one head tile over half the keys (KP = 2) or NW <= 4.  Shared entries of
+// computes one head tile over half the keys (KP = 2; four waves per SIMD), two head
+// tiles over half the keys (KP = 2, HT = 2, four waves: two waves per SIMD, up to 256
+// registers each), or NW <= 4.  Shared entries of
 // D = 512 take most of the LDS (two 64 KB chunk buffers): one workgroup of 8 waves
 // per CU, two waves per SIMD, a wave pair per head tile (attend_wide_*).
 template <int NW, int HT, int D, int KP>
@@ -236,8 +238,9 @@ hipError_t launch_attn(int dtype, const AttnP& p, int nrows, hipStream_t s, int 
     return hipGetLastError();
   }
   // 8 waves of 16 heads each: up to 64 heads, two waves per head tile split every
-  // chunk's keys in half (four waves per SIMD); above, one wave per head tile
-  // (shared entries at d <= 128 arrive with the value pointers aimed at the keys)
+  // chunk's keys in half (four waves per SIMD); exactly four tiles with bf16 caches
+  // take four waves of two tiles instead (below); above 64 heads, one wave per head
+  // tile (shared entries at d <= 128 arrive with the value pointers aimed at the keys)
   if (ntile == 4 && !p.f8) {
     // four tiles: four waves of two head tiles each, two waves per key half, so a
     // wave's K and V fragment reads from LDS serve two tiles (half the LDS reads of
