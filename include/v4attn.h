@@ -188,7 +188,11 @@ v4a_status v4attn_compress(const v4a_compress_args* args, hipStream_t stream);
  *   ki_scale     fp32 [batch][N_cap], row_stride 1 (ki_dtype FP8 only)
  *   idx          int32 out [batch][tq][k] (row = query token), row_stride >= k
  *   sel_scores   fp32 out, same layout as idx, or ptr == NULL
- * Workspace: v4attn_index_topk_workspace(args) bytes.
+ * Workspace: v4attn_index_topk_workspace(args) bytes: per query row about
+ * 4 * N_cap + 48 * N_cap / 256 bytes of scores and tile reports, for as many
+ * rows as fit in 8 GiB at once (larger calls take their rows in groups of that
+ * size).  A 4096-query prefill chunk at 1M context needs 4.5 GB, a decode step
+ * at 1M context 1.1 MB per row.
  * ------------------------------------------------------------------------- */
 typedef struct v4a_index_args {
   uint32_t abi_version;
