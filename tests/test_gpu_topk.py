@@ -221,3 +221,20 @@ def test_step_small_rows_and_padding():
         idx = _run_step(qi, wi, kb, pos, k)
         assert np.array_equal(idx, _run(qi, wi, kb, pos, k)[0])
         check_topk_row(idx[0, 0], _scores(qi, wi, kb[:, :n_vis]), k, f"step n_vis={n_vis}")
+
+
+def test_rows_with_more_tiles_than_the_selection_holds():
+    # 524288 visible blocks (a 2M-token context at m = 4): 2048 tiles of reports, more
+    # than the selection's 512 threads keep in registers (3 tiles each), so the row
+    # is selected by the whole-row path over its stored scores
+    n, k = 524288, 1024
+    qi, wi, ki, pos, rng = _inputs(n, seed=7)
+    kb = synth.f32_to_bf16_bits(ki.astype(np.float32))
+    print("[case] 2M-token row, whole-row path", flush=True)
+    idx, sel = _run(qi, wi, kb, pos, k)
+    s = _scores(qi, wi, kb)
+    check_topk_row(idx[0, 0], s, k, "2M")
+    np.testing.assert_allclose(sel[0, 0], s[idx[0, 0]], rtol=1e-5)
+    # and inside the decode step (the selection hosted by the HCA/window launch)
+    print("[case] step 2M-token row", flush=True)
+    assert np.array_equal(_run_step(qi, wi, kb, pos, k), idx)
