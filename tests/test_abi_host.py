@@ -379,3 +379,16 @@ def test_noalloc_step_validates_before_touching_the_device():
     assert L.v4attn_decode_step_workspace(ctypes.byref(ix), ctypes.byref(a)) > 64 << 20
     r = L.v4attn_decode_step_noalloc(ctypes.byref(ix), ctypes.byref(a), None)
     assert r == ENOTSUP and "scratch" in L.v4attn_last_error().decode()
+
+
+def test_index_workspace_row_groups():
+    # scores and tile reports of about 1.1 MB a row at 1M context, taken in groups of
+    # rows within 8 GiB: a 4096-query chunk is one group, an 8192-query chunk two, so
+    # its workspace holds fewer rows than the chunk has
+    L = V.lib()
+    per_row = 262144 * 4 + 1024 * (8 * 4 + 16)   # fp32 scores + 8 report keys and an info word a tile
+    w4 = L.v4attn_index_topk_workspace(ctypes.byref(good_index(batch=1, tq=4096, pos_max=1048576 + 4095)))
+    w8 = L.v4attn_index_topk_workspace(ctypes.byref(good_index(batch=1, tq=8192, pos_max=1048576 + 8191)))
+    assert 4096 * per_row <= w4 < 4200 * per_row
+    assert w8 <= 8 << 30
+    assert 4096 * per_row < w8 < 8192 * per_row
